@@ -1,0 +1,324 @@
+"""TriAttention KV-pruning oracle: a plain, slow, fp64 CPU implementation.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module; only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` use it.  It shares
+no code with the HIP library and imports nothing from it.
+
+Sources (cited by page title and the section or equation on that page):
+
+* [RoPE-eq]   qingkeai.online, talk page "聊聊 TriAttention: 面向长上下文推理的
+              三角级数式 KV Cache 压缩" -- the RoPE rotation equation (band f,
+              frequency omega_f = theta^(-2f/d), theta = 10000, 2x2 rotation).
+* [logit-eq]  same page -- "RoPE 注意力 logit 的一般形式": logit(q,k) =
+              sum_f |q_f||k_f| cos(omega_f*Delta + phi_f), Delta = p_q - p_k.
+* [Strig-eq]  same page -- "三角级数分数" S_trig equation.
+* [Snorm-eq]  same page -- "范数分数" S_norm equation and the definition of R_f.
+* [avg-eq]    same page -- "综合打分并跨未来偏移平均": S = S_trig + S_norm and the
+              mean over the offset set D = {1, 2, 4, ..., 2^16}.
+* [topB]      same page -- the closing step: rank keys by the averaged score
+              and keep the top B.
+* [gqa]       hyper.ai summary of arXiv 2604.04921, section "方法": average over
+              future query positions, then for grouped-query attention
+              "normalise then aggregate": z-score per query head, max over the
+              group.
+* [calib]     hyper.ai summary, section "方法" (R = |E[q]| / E[|q|]) and the
+              shibing624 blog review, section "具体操作分三步" step 1 (offline
+              calibration on ~10K tokens, done once).
+* [evict]     jaedaily.cn KV-cache compression tutorial, eviction step: the
+              ``evict_kv_cache`` snippet (top-k, then sort the kept indices so
+              the time order is preserved, then gather keys and values).
+
+Readings where the pages are silent or disagree (each is a choice, listed
+again in the design notes):
+
+* RoPE pairs are interleaved (x_{2f}, x_{2f+1}) as the rotation equation
+  writes them; band f is the complex number x_{2f} + i x_{2f+1}, and the
+  printed matrix multiplies it by exp(+i omega_f p).
+* phi_f in S_trig is arg E[q_f] - arg k_f with k_f the pre-RoPE key.
+* The offsets are averaged (formula page), not max-reduced (the blog review).
+* (1 - R_f) weights S_norm only.
+* R_f := 1 when E|q_f| = 0 (both terms of that band vanish anyway).
+* z-score uses the population standard deviation over all n keys of the
+  unit; sigma = 0 gives z = 0.  Query heads [gG, (g+1)G) belong to KV head g.
+* Ties in the top-B are broken by the lower position (= lower index, since
+  positions increase within a unit); -0.0 equals +0.0; NaN ranks below -inf.
+"""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+# D = {2^0, 2^1, ..., 2^16}  [avg-eq]
+OFFSETS = tuple(float(2 ** m) for m in range(17))
+
+
+# --------------------------------------------------------------------------
+# bf16 decoding (exact)
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode raw bf16 bit patterns (uint16) to fp64 exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# RoPE  [RoPE-eq]
+# --------------------------------------------------------------------------
+def rope_omega(d: int, theta: float) -> np.ndarray:
+    """omega_f = theta^(-2f/d) for f = 0 .. d/2-1."""
+    if d % 2:
+        raise ValueError("head_dim must be even")
+    f = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * f / d)
+
+
+def rope_rotate(x: np.ndarray, pos, omega: np.ndarray) -> np.ndarray:
+    """Apply the printed 2x2 rotation to every band of x at position pos.
+
+    x: [..., d] (pre-RoPE).  pos broadcasts against x[..., 0].
+    (x'_{2f}, x'_{2f+1}) = [[cos, -sin], [sin, cos]] (x_{2f}, x_{2f+1}),
+    angle omega_f * pos.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * omega
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = c * xe - s * xo
+    out[..., 1::2] = s * xe + c * xo
+    return out
+
+
+def rope_derotate(x: np.ndarray, pos, omega: np.ndarray) -> np.ndarray:
+    """Inverse of rope_rotate (rotation by -omega_f * pos)."""
+    return rope_rotate(x, -np.asarray(pos, dtype=np.float64), omega)
+
+
+def bands(x: np.ndarray) -> np.ndarray:
+    """View band f of x as the complex number x_{2f} + i x_{2f+1}."""
+    x = np.asarray(x, dtype=np.float64)
+    return x[..., 0::2] + 1j * x[..., 1::2]
+
+
+# --------------------------------------------------------------------------
+# Logit decomposition  [logit-eq]
+# --------------------------------------------------------------------------
+def logit_decomposed(q_pre: np.ndarray, k_pre: np.ndarray, delta, omega) -> np.ndarray:
+    """sum_f |q_f| |k_f| cos(omega_f * Delta + phi_f), phi_f = arg q_f - arg k_f.
+
+    q_pre, k_pre: [..., d] pre-RoPE vectors; delta = p_q - p_k.
+    """
+    qf, kf = bands(q_pre), bands(k_pre)
+    phi = np.angle(qf) - np.angle(kf)
+    ang = np.asarray(delta, dtype=np.float64)[..., None] * omega + phi
+    return np.sum(np.abs(qf) * np.abs(kf) * np.cos(ang), axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Calibration  [calib], [Snorm-eq]
+# --------------------------------------------------------------------------
+def calibrate(q: np.ndarray, q_pos, omega: np.ndarray):
+    """Per-band query statistics from sample queries of one layer.
+
+    q: [N, H, d] fp64 sample queries, post-RoPE at q_pos[N]; pass
+       q_pos=None when the samples are already pre-RoPE.
+    Returns (centre [H, F] complex = E[q_f],
+             absmean [H, F] = E[|q_f|],
+             R [H, F] = |E[q_f]| / E[|q_f|], with R := 1 where E|q_f| = 0).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if q_pos is not None:
+        pos = np.asarray(q_pos, dtype=np.float64)[:, None]       # [N, 1]
+        q = rope_derotate(q, pos, omega)                          # pre-RoPE
+    qf = bands(q)                                                 # [N, H, F]
+    centre = qf.mean(axis=0)
+    absmean = np.abs(qf).mean(axis=0)
+    R = np.ones_like(absmean)
+    nz = absmean > 0
+    R[nz] = np.abs(centre[nz]) / absmean[nz]
+    return centre, absmean, R
+
+
+# --------------------------------------------------------------------------
+# Scores, term by term  [Strig-eq], [Snorm-eq], [avg-eq]
+# --------------------------------------------------------------------------
+def score_terms(k_post: np.ndarray, k_pos, p_q: float,
+                centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
+                omega: np.ndarray, offsets=OFFSETS):
+    """Offset-averaged TriAttention score of every key, for each query head.
+
+    k_post: [n, d] post-RoPE keys (fp64); k_pos: [n] their positions.
+    centre/absmean/R: [G, F] statistics of the G query heads that read
+    this KV head.  Returns (S_tilde [G, n], S_trig_avg [G, n], S_norm [G, n]).
+
+    The trig term is summed band by band and offset by offset exactly as the
+    equations write it; nothing is factored.
+    """
+    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega)
+    kf = bands(k_pre)                                   # [n, F]
+    k_abs = np.abs(kf)
+    k_arg = np.angle(kf)
+    delta = p_q - np.asarray(k_pos, dtype=np.float64)   # [n]
+
+    G = centre.shape[0]
+    n = k_post.shape[0]
+    s_trig = np.zeros((G, n))
+    s_norm = np.zeros((G, n))
+    for h in range(G):
+        amp_q = np.abs(centre[h])                       # |E[q_f]|  [F]
+        phi = np.angle(centre[h])[None, :] - k_arg      # [n, F]
+        acc = np.zeros(n)
+        for dlt in offsets:                             # mean over D
+            ang = (delta[:, None] + dlt) * omega[None, :] + phi
+            acc += np.sum(amp_q[None, :] * k_abs * np.cos(ang), axis=1)
+        s_trig[h] = acc / len(offsets)
+        # S_norm(k) = sum_f (1 - R_f) E|q_f| |k_f|; independent of Delta,
+        # so the offset mean leaves it unchanged.
+        s_norm[h] = np.sum(((1.0 - R[h]) * absmean[h])[None, :] * k_abs, axis=1)
+    return s_trig + s_norm, s_trig, s_norm
+
+
+def offset_phasor_mean(omega: np.ndarray, offsets=OFFSETS) -> np.ndarray:
+    """C_f = mean over delta in D of exp(i omega_f delta)."""
+    d = np.asarray(offsets, dtype=np.float64)
+    return np.exp(1j * omega[:, None] * d[None, :]).mean(axis=1)
+
+
+def score_factored(k_post: np.ndarray, p_q: float,
+                   centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
+                   omega: np.ndarray, offsets=OFFSETS) -> np.ndarray:
+    """The same S_tilde as score_terms, written as one dot product per head.
+
+    Band f of a query at p_q + delta contributes
+    Re(E[q_f] conj(k_f) exp(i omega_f (Delta + delta))); with the stored key
+    k'_f = k_f exp(i omega_f p_k) the key position cancels and the offset mean
+    folds into C_f:  S_trig = sum_f Re(E[q_f] C_f exp(i omega_f p_q) conj(k'_f)).
+    Used to check that identity and to evaluate large units quickly.
+    Returns S_tilde [G, n].
+    """
+    C = offset_phasor_mean(omega, offsets)                       # [F]
+    A = centre * C[None, :] * np.exp(1j * omega * p_q)[None, :]  # [G, F]
+    kf = bands(k_post)                                           # [n, F]
+    trig = np.real(A[:, None, :] * np.conj(kf)[None, :, :]).sum(axis=2)
+    w = (1.0 - R) * absmean                                      # [G, F]
+    norm = w @ np.abs(kf).T
+    return trig + norm
+
+
+# --------------------------------------------------------------------------
+# GQA: normalise, then aggregate  [gqa]
+# --------------------------------------------------------------------------
+def zscore_rows(S: np.ndarray):
+    """Per row (query head): z = (S - mean) / population std; std 0 -> z 0.
+
+    Two passes (mean, then mean squared deviation).  Returns (z, mu, sigma).
+    """
+    S = np.asarray(S, dtype=np.float64)
+    mu = S.mean(axis=1)
+    sigma = np.sqrt(((S - mu[:, None]) ** 2).mean(axis=1))
+    z = np.zeros_like(S)
+    ok = sigma > 0
+    z[ok] = (S[ok] - mu[ok, None]) / sigma[ok, None]
+    return z, mu, sigma
+
+
+def gqa_max(z: np.ndarray) -> np.ndarray:
+    """Max over the query heads of one GQA group: [G, n] -> [n]."""
+    return np.max(z, axis=0)
+
+
+def unit_scores(k_post, k_pos, p_q, centre, absmean, R, omega,
+                offsets=OFFSETS, factored=False):
+    """Final fp64 score of each key of one unit (one sequence/layer/KV head).
+
+    Returns (score [n], S_tilde [G, n], mu [G], sigma [G]).
+    """
+    if factored:
+        S = score_factored(k_post, p_q, centre, absmean, R, omega, offsets)
+    else:
+        S = score_terms(k_post, k_pos, p_q, centre, absmean, R, omega, offsets)[0]
+    z, mu, sigma = zscore_rows(S)
+    return gqa_max(z), S, mu, sigma
+
+
+# --------------------------------------------------------------------------
+# Top-B selection and order-preserving compaction  [topB], [evict]
+# --------------------------------------------------------------------------
+def select_topb(scores: np.ndarray, budget: int) -> np.ndarray:
+    """Kept indices of one unit, ascending.
+
+    b = min(budget, n).  Keys are ranked by score, higher first; equal
+    scores go to the lower index (lower position); -0.0 equals +0.0; NaN
+    ranks below every number.  The first b of that ranking are kept and
+    returned in ascending index order (the time order).
+    """
+    s = np.asarray(scores)
+    n = s.shape[0]
+    b = max(0, min(int(budget), n))
+    if b == 0:
+        return np.zeros(0, dtype=np.int64)
+    s64 = s.astype(np.float64)
+    nan = np.isnan(s64)
+    neg = np.where(nan, 0.0, -s64)            # -0.0 and +0.0 compare equal
+    idx = np.arange(n)
+    order = np.lexsort((idx, neg, nan.astype(np.int8)))  # last key sorts first
+    return np.sort(order[:b])
+
+
+def select_topb_bruteforce(scores: np.ndarray, budget: int) -> np.ndarray:
+    """Definition by enumeration (tiny n only): the unique b-subset S such
+    that every kept key beats every dropped one, where i beats j if
+    score_i > score_j, or the scores are equal and i < j (NaN below all,
+    -0 == +0)."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    b = max(0, min(int(budget), n))
+
+    def beats(i, j):
+        si, sj = s[i], s[j]
+        if np.isnan(si) and np.isnan(sj):
+            return i < j
+        if np.isnan(si):
+            return False
+        if np.isnan(sj):
+            return True
+        if si != sj:
+            return si > sj
+        return i < j
+
+    found = []
+    for sub in itertools.combinations(range(n), b):
+        kept = set(sub)
+        if all(beats(i, j) for i in kept for j in range(n) if j not in kept):
+            found.append(np.array(sub, dtype=np.int64))
+    if len(found) != 1:
+        raise AssertionError(f"expected one valid subset, found {len(found)}")
+    return found[0]
+
+
+def compact_rows(rows: np.ndarray, kept: np.ndarray) -> np.ndarray:
+    """Gather rows[kept] (keys, values or positions) in the given order."""
+    return np.asarray(rows)[np.asarray(kept, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# Whole-batch helpers over the unit-major packed layout
+# --------------------------------------------------------------------------
+def unit_rows(cu_len, L: int, Hkv: int, s: int, l: int, g: int):
+    """Row range [start, start+n) of unit (s, l, g) in the packed cache:
+    sequence s starts at L*Hkv*cu_len[s]; unit (l, g) holds n_s rows."""
+    n = int(cu_len[s + 1] - cu_len[s])
+    start = L * Hkv * int(cu_len[s]) + (l * Hkv + g) * n
+    return start, n
+
+
+def out_rows(cu_len, budget, L: int, Hkv: int, s: int, l: int, g: int):
+    """Output row range of unit (s, l, g): as unit_rows with b_s = min(B_s, n_s)."""
+    b = [max(0, min(int(budget[i]), int(cu_len[i + 1] - cu_len[i])))
+         for i in range(len(cu_len) - 1)]
+    cu_b = np.concatenate([[0], np.cumsum(b)]).astype(np.int64)
+    start = L * Hkv * int(cu_b[s]) + (l * Hkv + g) * b[s]
+    return start, b[s]

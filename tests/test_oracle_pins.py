@@ -1,0 +1,364 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+Each test ties the oracle to something other than itself: a hand-derived
+closed form (tests/golden/hand_cases.json), an independent computation path
+(the explicit RoPE dot product instead of the cosine series), an invariant,
+or brute-force enumeration.  None of these needs a GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def _direct_logit(q_pre, p_q, k_post):
+    """Attention logit the plain way: rotate the query to p_q, dot with the
+    stored (already rotated) key.  No cosine series involved."""
+    om = O.rope_omega(q_pre.shape[-1], _direct_logit.theta)
+    return O.rope_rotate(q_pre, p_q, om) @ k_post
+
+
+_direct_logit.theta = 10000.0
+
+
+# ---------------------------------------------------------------- RoPE ----
+def test_omega_closed_forms():
+    g = GOLD["omega_closed_forms"]
+    om = O.rope_omega(g["d"], g["theta"])
+    for f, w in zip(g["f"], g["omega"]):
+        assert om[f] == pytest.approx(w, rel=1e-14)
+
+
+def test_rope_quarter_turn_matches_printed_matrix():
+    g = GOLD["rope_quarter_turn"]
+    om = O.rope_omega(g["d"], g["theta"])
+    for x, y in zip(g["inputs"], g["outputs"]):
+        out = O.rope_rotate(np.array(x), g["pos"], om)
+        np.testing.assert_allclose(out, y, atol=1e-15)
+
+
+def test_rope_group_properties():
+    rng = np.random.default_rng(1)
+    om = O.rope_omega(64, 1e4)
+    x = rng.normal(size=(5, 64))
+    p1, p2 = 1234.0, 98765.0
+    a = O.rope_rotate(O.rope_rotate(x, p1, om), p2, om)
+    b = O.rope_rotate(x, p1 + p2, om)
+    np.testing.assert_allclose(a, b, atol=1e-11)
+    np.testing.assert_allclose(O.rope_derotate(O.rope_rotate(x, p2, om), p2, om), x, atol=1e-11)
+    # norms of every band are preserved
+    np.testing.assert_allclose(np.abs(O.bands(O.rope_rotate(x, p2, om))), np.abs(O.bands(x)), rtol=1e-13)
+
+
+def test_rope_relative_position_property():
+    """q_i^T k_j depends only on i - j (tutorial page, RoPE paragraph)."""
+    rng = np.random.default_rng(2)
+    om = O.rope_omega(128, 1e4)
+    q, k = rng.normal(size=128), rng.normal(size=128)
+    a = O.rope_rotate(q, 5000.0, om) @ O.rope_rotate(k, 1000.0, om)
+    b = O.rope_rotate(q, 104000.0, om) @ O.rope_rotate(k, 100000.0, om)
+    assert a == pytest.approx(b, rel=1e-9, abs=1e-9)
+
+
+# ---------------------------------------------------- logit decomposition ----
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_logit_decomposition_vs_direct_dot(seed):
+    rng = np.random.default_rng(seed)
+    d = 128
+    om = O.rope_omega(d, 1e4)
+    q = rng.normal(size=(50, d))
+    k = rng.normal(size=(50, d))
+    pq = rng.integers(0, 200000, size=50).astype(float)
+    pk = rng.integers(0, 200000, size=50).astype(float)
+    direct = np.einsum("nd,nd->n", O.rope_rotate(q, pq, om), O.rope_rotate(k, pk, om))
+    series = O.logit_decomposed(q, k, pq - pk, om)
+    scale = np.sum(np.abs(O.bands(q)) * np.abs(O.bands(k)), axis=1)
+    assert np.max(np.abs(direct - series) / scale) < 1e-12
+
+
+# ------------------------------------------------------------- S_trig ----
+def _unit(rng, n, d, p_q_max=70000):
+    om = O.rope_omega(d, 1e4)
+    pos = np.sort(rng.choice(p_q_max - 1, size=n, replace=False)).astype(float)
+    k_pre = rng.normal(size=(n, d)) + 1.5
+    k_post = O.rope_rotate(k_pre, pos, om)
+    return om, pos, k_post
+
+
+def test_strig_equals_mean_logit_when_queries_equal_centre():
+    """Every query equals its centre: R_f = 1, S_norm = 0, and the averaged
+    score equals the mean over D of the direct logit at distance Delta + delta."""
+    rng = np.random.default_rng(3)
+    d, n = 32, 40
+    om, pos, k_post = _unit(rng, n, d)
+    c = rng.normal(size=d)
+    qpos = np.arange(16, dtype=float) * 37.0
+    q_post = O.rope_rotate(np.tile(c, (16, 1))[:, None, :], qpos[:, None], om)  # [N,1,d]
+    centre, absmean, R = O.calibrate(q_post, qpos, om)
+    np.testing.assert_allclose(R, 1.0, atol=1e-13)
+    p_q = 70000.0
+    S, s_trig, s_norm = O.score_terms(k_post, pos, p_q, centre, absmean, R, om)
+    assert np.max(np.abs(s_norm)) < 1e-10
+    ref = np.mean([_direct_logit(c, p_q + dl, k_post.T) for dl in O.OFFSETS], axis=0)
+    assert np.max(np.abs(S[0] - ref)) < 1e-11 * np.max(np.abs(ref))
+
+
+def test_score_linearity_for_any_concentration():
+    """S_trig is linear in the query: the averaged trig term equals the mean
+    over the calibration set and over D of the direct logit, for any R; and
+    S_norm = sum_f (E|q_f| - |E q_f|) |k_f|."""
+    rng = np.random.default_rng(4)
+    d, n, N = 32, 30, 200
+    om, pos, k_post = _unit(rng, n, d)
+    q_pre = rng.normal(size=(N, d)) * 0.8 + rng.normal(size=d)
+    qpos = rng.integers(0, 5000, size=N).astype(float)
+    q_post = O.rope_rotate(q_pre[:, None, :], qpos[:, None], om)
+    centre, absmean, R = O.calibrate(q_post, qpos, om)
+    assert np.all(R < 1.0) and np.all(R > 0.0)
+    p_q = 70000.0
+    S, s_trig, s_norm = O.score_terms(k_post, pos, p_q, centre, absmean, R, om)
+    ref_trig = np.zeros(n)
+    for dl in O.OFFSETS:
+        ref_trig += np.mean(O.rope_rotate(q_pre, p_q + dl, om) @ k_post.T, axis=0)
+    ref_trig /= len(O.OFFSETS)
+    assert np.max(np.abs(s_trig[0] - ref_trig)) < 1e-11 * np.max(np.abs(ref_trig))
+    qf = q_pre[:, 0::2] + 1j * q_pre[:, 1::2]
+    k_abs = np.abs(k_post[:, 0::2] + 1j * k_post[:, 1::2])   # rotation keeps |k_f|
+    gap = np.mean(np.abs(qf), axis=0) - np.abs(np.mean(qf, axis=0))
+    ref_norm = k_abs @ gap
+    np.testing.assert_allclose(s_norm[0], ref_norm, rtol=1e-11)
+
+
+@pytest.mark.parametrize("case", ["offset_mean_omega_pi", "offset_mean_omega_half_pi"])
+def test_offset_average_closed_form(case):
+    """d = 4 with theta chosen so omega_1 is pi or pi/2: the 17-offset mean has
+    a closed form, which pins the offset set (2^0..2^16, 17 items)."""
+    g = GOLD[case]
+    omega1 = math.pi if case.endswith("_pi") and "half" not in case else math.pi / 2
+    theta = omega1 ** -2.0
+    om = O.rope_omega(4, theta)
+    assert om[1] == pytest.approx(omega1, rel=1e-14)
+    rng = np.random.default_rng(5)
+    n = 12
+    pos = np.arange(n, dtype=float) * 3.0
+    k_pre = np.zeros((n, 4))
+    k_pre[:, 2:] = rng.normal(size=(n, 2))
+    k_post = O.rope_rotate(k_pre, pos, om)
+    cq = np.array([0.0, 0.0, 0.7, -1.3])
+    centre = O.bands(cq)[None, :]
+    absmean = np.abs(centre) * 1.25
+    R = np.abs(centre) / np.where(absmean > 0, absmean, 1.0)
+    R[absmean == 0] = 1.0
+    p_q = 1000.0
+    _, s_trig, _ = O.score_terms(k_post, pos, p_q, centre, absmean, R, om)
+    kf = O.bands(k_pre)[:, 1]
+    qf = O.bands(cq)[1]
+    psi = omega1 * (p_q - pos) + np.angle(qf) - np.angle(kf)
+    amp = abs(qf) * np.abs(kf)
+    if "half" in case:
+        expect = amp * (14.0 * np.cos(psi) - np.sin(psi)) / 17.0
+        C = O.offset_phasor_mean(om)[1]
+        # omega_1 * 2^16 carries ~1e-11 rad of fp64 rounding of pi
+        assert C.real == pytest.approx(g["C_re"], abs=1e-10)
+        assert C.imag == pytest.approx(g["C_im"], abs=1e-10)
+    else:
+        expect = g["ratio"] * amp * np.cos(psi)
+    np.testing.assert_allclose(s_trig[0], expect, atol=1e-9 * np.max(amp))
+
+
+def test_factored_equals_term_by_term():
+    rng = np.random.default_rng(6)
+    d, n, G = 128, 64, 3
+    om, pos, k_post = _unit(rng, n, d, p_q_max=131072)
+    F = d // 2
+    centre = rng.uniform(0.5, 2, size=(G, F)) * np.exp(1j * rng.uniform(0, 2 * np.pi, size=(G, F)))
+    R = rng.uniform(0.3, 0.99, size=(G, F))
+    absmean = np.abs(centre) / R
+    p_q = 131072.0
+    S_terms = O.score_terms(k_post, pos, p_q, centre, absmean, R, om)[0]
+    S_fact = O.score_factored(k_post, p_q, centre, absmean, R, om)
+    assert np.max(np.abs(S_terms - S_fact)) < 1e-12 * np.max(np.abs(S_terms))
+
+
+def test_offset_phasor_limits():
+    om = np.array([1e-12, 1e-3, 0.1, 1.0])
+    C = O.offset_phasor_mean(om)
+    assert np.all(np.abs(C) <= 1.0 + 1e-15)
+    assert abs(C[0] - 1.0) < 1e-6
+
+
+def test_key_position_cancels():
+    """The same stored (post-RoPE) key at two positions scores the same, and
+    shifting every position and p_q by t (keys re-rotated) changes nothing."""
+    rng = np.random.default_rng(7)
+    d, n, G = 64, 20, 2
+    om, pos, k_post = _unit(rng, n, d)
+    F = d // 2
+    centre = rng.normal(size=(G, F)) + 1j * rng.normal(size=(G, F))
+    R = rng.uniform(0.5, 1.0, size=(G, F))
+    absmean = np.abs(centre) / R
+    k2 = np.concatenate([k_post, k_post[:5]])
+    pos2 = np.concatenate([pos, pos[:5] + 77.0])
+    S = O.score_terms(k2, pos2, 80000.0, centre, absmean, R, om)[0]
+    np.testing.assert_allclose(S[:, n:], S[:, :5], rtol=1e-11, atol=1e-11)
+    k_pre = O.rope_derotate(k_post, pos, om)
+    t = 12345.0
+    S_a = O.score_terms(k_post, pos, 80000.0, centre, absmean, R, om)[0]
+    S_b = O.score_terms(O.rope_rotate(k_pre, pos + t, om), pos + t, 80000.0 + t,
+                        centre, absmean, R, om)[0]
+    np.testing.assert_allclose(S_a, S_b, rtol=1e-9, atol=1e-9)
+
+
+# --------------------------------------------------------- S_norm / R ----
+def test_antipodal_queries_zero_trig():
+    """Samples (q, -q) at the same position: E[q_f] = 0, R_f = 0, S_trig = 0
+    and S = sum_f E|q_f| |k_f|."""
+    rng = np.random.default_rng(8)
+    d = 16
+    om = O.rope_omega(d, 1e4)
+    q = rng.normal(size=(10, d))
+    qq = np.concatenate([q, -q])[:, None, :]
+    qpos = np.concatenate([np.arange(10.0), np.arange(10.0)])
+    centre, absmean, R = O.calibrate(O.rope_rotate(qq, qpos[:, None], om), qpos, om)
+    assert np.max(np.abs(centre)) < 1e-13
+    np.testing.assert_allclose(R, 0.0, atol=1e-13)
+    _, pos, k_post = _unit(rng, 8, d)
+    S, s_trig, s_norm = O.score_terms(k_post, pos, 9000.0, centre, absmean, R, om)
+    assert np.max(np.abs(s_trig)) < 1e-12
+    kabs = np.abs(O.bands(k_post))
+    np.testing.assert_allclose(S[0], kabs @ absmean[0], rtol=1e-12)
+
+
+def test_calibration_hand_example():
+    g = GOLD["calibration_two_samples"]
+    om = O.rope_omega(2, g["theta"])
+    q_post = np.array([[[3.0, 4.0]], [[-5.0 * math.sin(1.0), 5.0 * math.cos(1.0)]]])
+    centre, absmean, R = O.calibrate(q_post, np.array([0.0, 1.0]), om)
+    assert centre[0, 0].real == pytest.approx(g["centre"][0], abs=1e-14)
+    assert centre[0, 0].imag == pytest.approx(g["centre"][1], abs=1e-14)
+    assert absmean[0, 0] == pytest.approx(g["absmean"], rel=1e-15)
+    assert R[0, 0] == pytest.approx(g["R"], rel=1e-14)
+
+
+def test_calibration_identical_samples():
+    rng = np.random.default_rng(9)
+    d = 8
+    om = O.rope_omega(d, 1e4)
+    c = rng.normal(size=d)
+    qpos = np.arange(7, dtype=float) * 1001
+    q_post = O.rope_rotate(np.tile(c, (7, 1))[:, None, :], qpos[:, None], om)
+    centre, absmean, R = O.calibrate(q_post, qpos, om)
+    np.testing.assert_allclose(R, 1.0, atol=1e-12)
+    np.testing.assert_allclose(absmean, np.abs(centre), rtol=1e-12)
+    np.testing.assert_allclose(centre[0], O.bands(c), atol=1e-12)
+    # pre-RoPE samples (q_pos None) skip the de-rotation
+    c2, a2, R2 = O.calibrate(np.tile(c, (3, 1))[:, None, :], None, om)
+    np.testing.assert_allclose(c2[0], O.bands(c), atol=1e-15)
+
+
+def test_calibration_zero_band_reads_R_one():
+    q = np.zeros((4, 1, 4))
+    q[:, 0, 2:] = [1.0, 0.5]
+    c, a, R = O.calibrate(q, None, O.rope_omega(4, 1e4))
+    assert R[0, 0] == 1.0 and a[0, 0] == 0.0
+
+
+# ---------------------------------------------------------- z and max ----
+def test_zscore_hand_example():
+    g = GOLD["zscore_1234"]
+    z, mu, sigma = O.zscore_rows(np.array([g["raw"]]))
+    np.testing.assert_allclose(z[0], g["z"], rtol=1e-14)
+
+
+def test_zscore_invariants_and_max():
+    rng = np.random.default_rng(10)
+    S = rng.normal(size=(5, 300)) * rng.uniform(0.1, 5, size=(5, 1)) + rng.normal(size=(5, 1)) * 10
+    z, mu, sigma = O.zscore_rows(S)
+    np.testing.assert_allclose(z.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(np.sqrt((z ** 2).mean(axis=1)), 1.0, rtol=1e-12)
+    z2, _, _ = O.zscore_rows(S * 3.7 + 11.0)
+    np.testing.assert_allclose(z2, z, atol=1e-11)
+    m = O.gqa_max(z)
+    assert np.all(m[None, :] >= z - 0.0)
+    assert np.all(np.any(z == m[None, :], axis=0))
+    z1, _, _ = O.zscore_rows(S[:1])
+    np.testing.assert_array_equal(O.gqa_max(z1), z1[0])
+    zc, _, sc = O.zscore_rows(np.full((1, 9), 4.2))
+    assert sc[0] == 0.0 and np.all(zc == 0.0)
+
+
+def test_unit_scores_scale_invariance():
+    """Scaling (E[q], E|q|) of every head by c > 0 leaves the final scores unchanged."""
+    rng = np.random.default_rng(11)
+    d, n, G = 32, 50, 4
+    om, pos, k_post = _unit(rng, n, d)
+    F = d // 2
+    centre = rng.normal(size=(G, F)) + 1j * rng.normal(size=(G, F))
+    R = rng.uniform(0.5, 1.0, size=(G, F))
+    absmean = np.abs(centre) / R
+    a = O.unit_scores(k_post, pos, 1e5, centre, absmean, R, om)[0]
+    b = O.unit_scores(k_post, pos, 1e5, centre * 2.5, absmean * 2.5, R, om)[0]
+    np.testing.assert_allclose(a, b, atol=1e-10)
+
+
+# ------------------------------------------------------------- select ----
+@pytest.mark.parametrize("seed", range(12))
+def test_select_matches_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 10))
+    pool = np.array([0.5, -0.5, 1.0, 0.0, -0.0, np.inf, -np.inf, np.nan, 2.0], dtype=np.float32)
+    s = rng.choice(pool, size=n) if seed % 2 else rng.normal(size=n).astype(np.float32)
+    for B in range(0, n + 2):
+        np.testing.assert_array_equal(O.select_topb(s, B), O.select_topb_bruteforce(s, B))
+
+
+def test_select_edge_cases():
+    s = np.full(10, 3.0, dtype=np.float32)
+    np.testing.assert_array_equal(O.select_topb(s, 4), [0, 1, 2, 3])
+    np.testing.assert_array_equal(O.select_topb(s, 50), np.arange(10))
+    assert O.select_topb(s, 0).size == 0
+    assert O.select_topb(np.zeros(0, np.float32), 5).size == 0
+    s = np.array([0.0, -0.0, 0.0, -0.0], dtype=np.float32)
+    np.testing.assert_array_equal(O.select_topb(s, 2), [0, 1])
+    s = np.array([np.nan, -np.inf, np.nan, 1.0], dtype=np.float32)
+    np.testing.assert_array_equal(O.select_topb(s, 2), [1, 3])
+    np.testing.assert_array_equal(O.select_topb(s, 3), [0, 1, 3])
+
+
+def test_select_permutation_invariance():
+    rng = np.random.default_rng(12)
+    s = rng.normal(size=200)
+    perm = rng.permutation(200)
+    a = set(O.select_topb(s, 37).tolist())
+    b = set(perm[O.select_topb(s[perm], 37)].tolist())
+    assert a == b
+
+
+def test_compact_rows_bytes():
+    rng = np.random.default_rng(13)
+    rows = rng.integers(0, 65535, size=(20, 8), dtype=np.uint16)
+    kept = O.select_topb(rng.normal(size=20), 7)
+    out = O.compact_rows(rows, kept)
+    assert np.all(np.diff(kept) > 0)
+    for j, i in enumerate(kept):
+        assert out[j].tobytes() == rows[i].tobytes()
+
+
+def test_bf16_decode_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F80, 0x4049], dtype=np.uint16)
+    v = O.bf16_bits_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -1.0 and v[2] == 0.0 and np.signbit(v[3])
+    assert np.isinf(v[4]) and v[5] == 3.140625
+
+
+def test_packed_unit_rows():
+    cu = np.array([0, 5, 12])
+    assert O.unit_rows(cu, 2, 3, 0, 1, 2) == ((1 * 3 + 2) * 5, 5)
+    assert O.unit_rows(cu, 2, 3, 1, 0, 1) == (2 * 3 * 5 + 1 * 7, 7)
+    assert O.out_rows(cu, [3, 10], 2, 3, 1, 1, 0) == (2 * 3 * 3 + 1 * 3 * 7, 7)
