@@ -1,0 +1,197 @@
+"""Throughput of the TriAttention pruning path on one MI355X.
+
+One step = tri_score + tri_select_compact over the whole batch of the
+long-reasoning compression workload (28 layers, 4 KV heads, 28 query heads,
+head_dim 128, batch 8, 32768 keys per head pruned to 2048, K and V bf16),
+inputs resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "keys scored+compacted/sec and achieved HBM GB/s (% of peak), 1 MI355X"
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {
+    # name: (config id, overrides, label)
+    "c3": (3, {}, "long_reasoning_32k_to_2048"),
+    "c2": (2, {}, "decode_window_3200_to_3072"),
+    "c4": (4, {}, "ragged_256seq_one_layer"),
+    "c5": (5, {}, "stress_ties_131072_to_4096"),
+}
+
+
+def algorithmic_bytes(case):
+    """Bytes the method must move (no design intermediates):
+    score:   n*d*2 (K read) + n*4 (score write)
+    select:  n*4 (score read) + b*4 (index write)
+    compact: 2*b*d*2 (K, V rows read) + 2*b*d*2 (rows written) + 2*b*4 (positions)."""
+    d = case.shape.head_dim
+    LH = case.shape.num_layers * case.shape.num_kv_heads
+    score = sel = 0
+    keys = 0
+    for s in range(case.num_seqs):
+        n, b = case.seq_len(s), case.kept(s)
+        keys += LH * n
+        score += LH * (n * d * 2 + n * 4)
+        sel += LH * (n * 4 + b * 4 + 4 * b * d * 2 + 2 * b * 4)
+    return keys, score, sel
+
+
+def cpu_baseline(case, max_seconds=30.0):
+    """The oracle as it stands (fp64, term by term) on whole units of the same
+    workload, one after another, on one host thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    om = O.rope_omega(case.shape.head_dim, case.shape.rope_theta)
+    G = case.shape.group
+    keys = 0
+    units = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for g in range(case.shape.num_kv_heads):
+            start, n = case.unit_rows(0, 0, g)
+            kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
+            pos = case.k_pos[start:start + n].cpu().numpy().astype(np.float64)
+            vrows = case.v[start:start + n].cpu().numpy()
+            qc = case.q_centre[0, g * G:(g + 1) * G].cpu().double().numpy()
+            t_unit = time.perf_counter()
+            score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, float(case.cur_pos[0]),
+                                  qc[..., 0] + 1j * qc[..., 1],
+                                  case.q_absmean[0, g * G:(g + 1) * G].cpu().double().numpy(),
+                                  case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy(), om)[0]
+            kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
+            O.compact_rows(kbits, kept)
+            O.compact_rows(vrows, kept)
+            O.compact_rows(pos, kept)
+            keys += n
+            units += 1
+            if time.perf_counter() - t0 > max_seconds or time.perf_counter() - t_unit > max_seconds / 2:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": keys / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} unit(s) (sequence 0, layer 0, KV heads 0..{units - 1}) of "
+                      f"{n} keys, G={G}: term-by-term fp64 score, z-score, max, top-B, gather; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path shards over (sequence, layer, KV head) "
+              "units with no exchange, so N GPUs run N independent copies of this step.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rope_aware_key_amd as R
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cid, over, label = WORKLOADS[args.workload]
+    print(f"[bench] building workload {label}", file=sys.stderr, flush=True)
+    case = synth.config_case(cid, device=dev, **over)
+    sh = R.make_shape(case.shape.head_dim, case.shape.num_q_heads, case.shape.num_kv_heads,
+                      case.shape.num_layers, case.shape.rope_theta)
+    rows, out_rows, d = case.total_rows(), case.total_out_rows(), case.shape.head_dim
+    cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
+    cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
+    bu = torch.as_tensor(case.budget).pin_memory().numpy()
+    ws = torch.empty(max(1, R.tri_workspace_bytes(sh, cu)), dtype=torch.uint8, device=dev)
+    scores = torch.empty(rows, dtype=torch.float32, device=dev)
+    kept = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
+    k_out = torch.empty(max(1, out_rows), d, dtype=torch.int16, device=dev)
+    v_out = torch.empty(max(1, out_rows), d, dtype=torch.int16, device=dev)
+    pos_out = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def score():
+        R.tri_score(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean, case.q_R,
+                    scores, workspace=ws, stream=stream)
+
+    def select():
+        R.tri_select_compact(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept, k_out, v_out,
+                             pos_out, workspace=ws, stream=stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        score()
+        select()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        score()
+        e1.record(stream)
+        select()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_score = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
+    t_sel = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    t_step = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e-3
+    print(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    keys, b_score, b_sel = algorithmic_bytes(case)
+    step = float(t_step.mean())
+    value = keys / step
+    gbps = (b_score + b_sel) / step / 1e9
+    score_gbps = b_score / float(t_score.mean()) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded concentrated bf16 K cache, N(0,1) V)",
+        "config": {"workload": label, "batch": case.num_seqs, "layers": case.shape.num_layers,
+                   "kv_heads": case.shape.num_kv_heads, "q_heads": case.shape.num_q_heads,
+                   "head_dim": d, "keys_per_head": int(case.seq_len(0)),
+                   "budget": int(case.budget[0]), "units": case.num_units},
+        "hbm_gbps": gbps,
+        "hbm_frac_of_peak": gbps / PEAK_HBM_GBPS,
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "breakdown_ms": {"tri_score": float(t_score.mean()) * 1e3,
+                         "tri_select_compact": float(t_sel.mean()) * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "tri_score",
+                     "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": score_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": b_score},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * triattn.h -- C ABI of the TriAttention KV-cache pruning library (gfx950).
+ *
+ * The library scores every cached key with the TriAttention importance
+ * estimate, keeps the top-B keys of each (sequence, layer, KV head) and
+ * compacts K, V and positions in their original order.  All work runs as
+ * hand-written HIP kernels on the stream the caller passes.
+ *
+ * Sources of the definitions (page title, then section or equation):
+ *  - qingkeai.online talk page "聊聊 TriAttention: 面向长上下文推理的三角级数式
+ *    KV Cache 压缩": RoPE rotation equation; RoPE logit decomposition;
+ *    S_trig equation; S_norm equation with R_f = |E[q_f]| / E[|q_f|];
+ *    S = S_trig + S_norm and its mean over the offsets D = {1, 2, ..., 2^16};
+ *    keep the top-B keys.
+ *  - hyper.ai summary of arXiv 2604.04921, section "方法": average over
+ *    future query positions; for grouped-query attention, z-score each query
+ *    head's scores, then take the max over the group; prune every 128
+ *    generated tokens.
+ *  - shibing624 blog review of TriAttention, section "具体操作分三步",
+ *    step 1: statistics are calibrated offline, once, from ~10K tokens.
+ *  - jaedaily.cn KV-cache compression tutorial, eviction step: the
+ *    evict_kv_cache snippet keeps the top-k indices, sorts them to keep the
+ *    time order, and gathers keys and values with them.
+ *
+ * Conventions shared by every call
+ *  - d = head_dim, F = d/2 RoPE bands.  Band f of a vector x is the pair
+ *    (x[2f], x[2f+1]) (interleaved), rotated at position p by omega_f * p,
+ *    omega_f = rope_theta^(-2f/d).
+ *  - G = num_q_heads / num_kv_heads; query heads [g*G, (g+1)*G) read KV
+ *    head g.
+ *  - A "unit" is one (sequence s, layer l, KV head g).  Packed unit-major
+ *    layout: with n_s = cu_len[s+1] - cu_len[s], the rows of sequence s
+ *    start at row L*Hkv*cu_len[s]; unit (l, g) holds the n_s consecutive rows
+ *    starting (l*Hkv + g)*n_s after that.  Within a unit, positions must
+ *    increase strictly (row order == time order).
+ *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *  - Pointers marked [host] are host memory, read before the call returns.
+ *    Every other pointer is device memory on the current HIP device.
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on it; outputs are ready once the stream reaches the end
+ *    of the call.
+ *  - The caller owns every buffer.  Outputs must not alias inputs.  K/V row
+ *    pointers must be 16-byte aligned and d*2 a multiple of 16.
+ *  - Argument errors return before any device work is queued.  A HIP error
+ *    during launch returns TRI_ERR_HIP.  tri_last_error() gives a message
+ *    for the last failing call of the calling thread.
+ */
+#ifndef TRIATTN_H
+#define TRIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRI_OK = 0,
+  TRI_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad alignment   */
+  TRI_ERR_UNSUPPORTED = 2,      /* shape outside what the kernels handle   */
+  TRI_ERR_WORKSPACE = 3,        /* workspace missing or too small          */
+  TRI_ERR_HIP = 4               /* HIP runtime error while queueing work   */
+} tri_status;
+
+typedef struct {
+  int32_t head_dim;     /* d: even, multiple of 8, 8..256                 */
+  int32_t num_q_heads;  /* H_q                                            */
+  int32_t num_kv_heads; /* H_kv; H_q % H_kv == 0 and G = H_q/H_kv <= 16   */
+  int32_t num_layers;   /* L                                              */
+  double rope_theta;    /* theta > 0 (10000 in the pages)                 */
+} tri_shape;
+
+/*
+ * tri_calibrate -- per-band query statistics (offline, once per model).
+ *
+ * Defined by the talk page's S_norm paragraph (R_f = |E[q_f]| / E[|q_f|])
+ * and the hyper.ai summary, section "方法"; calibration runs once on a small
+ * batch (blog review, step 1).
+ *
+ *  q         [L][n_samples][H_q][d] bf16 sample queries.  If q_pos != NULL
+ *            they are post-RoPE at positions q_pos[n_samples] (int32,
+ *            device) and are de-rotated first; if q_pos == NULL they are
+ *            taken as pre-RoPE.
+ *  q_centre  out [L][H_q][F][2] fp32: E[q_f] (real, imaginary) pre-RoPE.
+ *  q_absmean out [L][H_q][F] fp32: E[|q_f|].
+ *  q_R       out [L][H_q][F] fp32: R_f = |E[q_f]| / E[|q_f|]; 1 where
+ *            E[|q_f|] = 0.
+ * Sums are taken in fp64 in sample order (deterministic).  n_samples >= 1.
+ */
+tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q,
+                         const int32_t* q_pos, int64_t n_samples,
+                         float* q_centre, float* q_absmean, float* q_R,
+                         void* stream);
+
+/*
+ * tri_workspace_bytes -- device workspace that tri_score and
+ * tri_select_compact need for this batch (the larger of the two).
+ * cu_len [host][num_seqs+1].  Returns 0 on invalid arguments.
+ */
+size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs,
+                           const int64_t* cu_len);
+
+/*
+ * tri_score -- TriAttention importance of every cached key.
+ *
+ * For query head h of unit (s, l, g) and key i, the offset-averaged score
+ *   S~_h(i) = mean_{delta in D} [ S_trig(k_i, Delta_i + delta) ] + S_norm(k_i)
+ *   S_trig(k, Delta) = sum_f |E q_f| |k_f| cos(omega_f Delta + arg E q_f - arg k_f)
+ *   S_norm(k)        = sum_f (1 - R_f) E|q_f| |k_f|
+ * with k_f the pre-RoPE key band, Delta_i = cur_pos[s] - pos_i and
+ * D = {2^0, ..., 2^16} (talk page, S_trig / S_norm / averaged-score
+ * equations).  Then, per unit and query head, z_h(i) = (S~_h(i) - mu_h) /
+ * sigma_h over the unit's n_s keys (population sigma; sigma = 0 gives z = 0)
+ * and scores[i] = max over the G heads of z_h(i) (hyper.ai summary,
+ * section "方法").
+ *
+ * The stored key is k'_f = k_f exp(i omega_f pos_i), so the key position
+ * cancels from the score: only k' and cur_pos enter.  k_pos may be NULL and
+ * is not read.
+ *
+ *  cu_len     [host][num_seqs+1] non-decreasing row offsets (see layout).
+ *  cur_pos    [host][num_seqs] current query position p_q of each sequence.
+ *  k          post-RoPE bf16 keys, rows of d, packed unit-major.
+ *  q_centre, q_absmean, q_R   statistics as tri_calibrate writes them.
+ *  scores     out fp32, one per row (same packing, no d).
+ *  raw_scores optional out fp32 [rows][G]: S~_h(i) before the z-score.
+ *  head_stats optional out fp64 [units][G][2]: (mu_h, sigma_h); unit index
+ *             = (s*L + l)*Hkv + g.
+ *  workspace  device scratch of at least tri_workspace_bytes().
+ */
+tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
+                     const int64_t* cu_len, const int32_t* cur_pos,
+                     const uint16_t* k, const int32_t* k_pos,
+                     const float* q_centre, const float* q_absmean,
+                     const float* q_R, float* scores, float* raw_scores,
+                     double* head_stats, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * tri_select_compact -- keep the top-B keys of every unit, in time order,
+ * and gather their K, V rows and positions.
+ *
+ * Per unit, b_s = min(budget[s], n_s) keys are kept: the highest scores,
+ * equal scores resolved toward the lower index (= lower position); -0.0
+ * equals +0.0 and NaN ranks below every number (talk page, closing top-B
+ * step; tutorial page, evict_kv_cache snippet, which sorts the kept indices
+ * to keep the time order).
+ *
+ *  budget    [host][num_seqs] B_s >= 0.
+ *  scores    fp32 per row (as tri_score writes them).
+ *  kept_idx  out int32, b_s per unit, ascending indices in [0, n_s);
+ *            packed unit-major like the input with b_s in place of n_s.
+ *  k, k_out  optional pair (both NULL or both set): K rows in / gathered out.
+ *  v, v_out  optional pair: V rows in / gathered out.
+ *  k_pos, pos_out  optional pair: int32 positions in / gathered out.
+ *  Output rows use the same packing as kept_idx.
+ */
+tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs,
+                              const int64_t* cu_len, const int32_t* budget,
+                              const float* scores, const uint16_t* k,
+                              const uint16_t* v, const int32_t* k_pos,
+                              int32_t* kept_idx, uint16_t* k_out,
+                              uint16_t* v_out, int32_t* pos_out,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* tri_status_string(tri_status status);
+
+/* Message describing the calling thread's last failing call ("" if none). */
+const char* tri_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIATTN_H */

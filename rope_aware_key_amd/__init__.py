@@ -1,0 +1,10 @@
+"""MI355X-native TriAttention KV-cache pruning: Python face of libtriattn.so.
+
+The hot path (score, top-B select, compaction) and the calibration run as
+HIP kernels for gfx950 behind the C ABI in include/triattn.h; this package
+only marshals arguments to it.  Importing raises if the library is not built.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, TriError, TriShape, last_error, make_shape, status_string,
+    tri_calibrate, tri_score, tri_select_compact, tri_workspace_bytes,
+)

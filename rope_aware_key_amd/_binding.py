@@ -1,0 +1,139 @@
+"""ctypes binding of libtriattn.so: argument marshalling only.
+
+Every call forwards device pointers (torch tensors' data_ptr), host arrays
+and the current HIP stream to the C ABI in include/triattn.h.  Nothing here
+computes any part of the path; if the library is missing, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+# One HIP runtime per process: torch ships its own libamdhip64 with the same
+# soname as the system one this library links.  Loading torch first makes the
+# library bind to torch's runtime instead of pulling in a second copy, which
+# would leave the two runtimes fighting over the device.
+import torch  # noqa: F401,E402
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtriattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+TRI_OK = 0
+STATUS = {0: "TRI_OK", 1: "TRI_ERR_INVALID_ARGUMENT", 2: "TRI_ERR_UNSUPPORTED",
+          3: "TRI_ERR_WORKSPACE", 4: "TRI_ERR_HIP"}
+
+
+class TriShape(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_lib.tri_calibrate.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c_int64, _P, _P, _P, _P]
+_lib.tri_calibrate.restype = ctypes.c_int
+_lib.tri_workspace_bytes.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P]
+_lib.tri_workspace_bytes.restype = ctypes.c_size_t
+_lib.tri_score.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                           _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.tri_score.restype = ctypes.c_int
+_lib.tri_select_compact.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.tri_select_compact.restype = ctypes.c_int
+_lib.tri_status_string.argtypes = [ctypes.c_int]
+_lib.tri_status_string.restype = ctypes.c_char_p
+_lib.tri_last_error.argtypes = []
+_lib.tri_last_error.restype = ctypes.c_char_p
+
+EXPORTS = ("tri_calibrate", "tri_workspace_bytes", "tri_score", "tri_select_compact",
+           "tri_status_string", "tri_last_error")
+
+
+class TriError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.tri_last_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _check(st, where):
+    if st != TRI_OK:
+        raise TriError(st, where)
+
+
+def make_shape(head_dim, num_q_heads, num_kv_heads, num_layers, rope_theta=10000.0) -> TriShape:
+    return TriShape(head_dim, num_q_heads, num_kv_heads, num_layers, float(rope_theta))
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or NULL for None."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host(a, dtype):
+    """Contiguous host numpy array (kept alive by the caller's reference)."""
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=dtype))
+    return arr, ctypes.c_void_p(arr.ctypes.data)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def status_string(st: int) -> str:
+    return _lib.tri_status_string(st).decode()
+
+
+def last_error() -> str:
+    return _lib.tri_last_error().decode()
+
+
+def tri_calibrate(shape: TriShape, q, q_pos, n_samples, q_centre, q_absmean, q_R, stream=None):
+    st = _lib.tri_calibrate(ctypes.byref(shape), _ptr(q), _ptr(q_pos), int(n_samples),
+                            _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), _stream(stream))
+    _check(st, "tri_calibrate")
+
+
+def tri_workspace_bytes(shape: TriShape, cu_len) -> int:
+    arr, p = _host(cu_len, np.int64)
+    return int(_lib.tri_workspace_bytes(ctypes.byref(shape), len(arr) - 1, p))
+
+
+def tri_score(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_absmean, q_R, scores,
+              raw_scores=None, head_stats=None, workspace=None, workspace_bytes=None, stream=None):
+    cu, pcu = _host(cu_len, np.int64)
+    cp, pcp = _host(cur_pos, np.int32)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_score(ctypes.byref(shape), len(cu) - 1, pcu, pcp, _ptr(k), _ptr(k_pos),
+                        _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), _ptr(scores),
+                        _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
+                        _stream(stream))
+    _check(st, "tri_score")
+
+
+def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx, k_out,
+                       v_out, pos_out, workspace=None, workspace_bytes=None, stream=None):
+    cu, pcu = _host(cu_len, np.int64)
+    bu, pbu = _host(budget, np.int32)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_select_compact(ctypes.byref(shape), len(cu) - 1, pcu, pbu, _ptr(scores), _ptr(k),
+                                 _ptr(v), _ptr(k_pos), _ptr(kept_idx), _ptr(k_out), _ptr(v_out),
+                                 _ptr(pos_out), _ptr(workspace), int(wsb), _stream(stream))
+    _check(st, "tri_select_compact")

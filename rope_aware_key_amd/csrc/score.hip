@@ -1,0 +1,238 @@
+// Per-key TriAttention score: raw offset-averaged scores per query head,
+// per-head z-score over the unit, max over the GQA group.
+//
+// Math (talk page "聊聊 TriAttention", S_trig / S_norm / averaged-score
+// equations; hyper.ai summary, section "方法" for the z-score and the max):
+// with the per-(sequence, head, band) coefficient A_f = E[q_f] C_f
+// exp(i omega_f p_q) prepared by the prologue,
+//   S~_h(i) = sum_f [ Re(A_f) x_f + Im(A_f) y_f ] + sum_f w_f sqrt(x_f^2 + y_f^2)
+// where (x_f, y_f) is band f of the stored post-RoPE key and
+// w_f = (1 - R_f) E|q_f|.  One read of a key serves all G query heads.
+//
+// Work split: a "ticket" is one chunk of kScoreChunk keys of one unit.
+// Tickets of a unit are consecutive; each records (count, mean, M2) per head
+// in fp64, and the z pass merges them in ticket order (Chan's update), so
+// the result is deterministic.
+#include "tri_internal.hpp"
+
+namespace tri {
+
+__device__ __forceinline__ float bf16_lo_s(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_s(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the 256 threads of a block; every thread gets the total.
+__device__ __forceinline__ double block_sum256(double v, double* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const double t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+struct Ticket {
+  int s, lg, c, nch, nkeys, key0;
+  int64_t row0;
+};
+
+__device__ __forceinline__ Ticket decode_ticket(const SeqInfo* seqs, int S, int t) {
+  Ticket k;
+  k.s = find_seq_by_ticket(seqs, S, t);
+  const SeqInfo si = seqs[k.s];
+  k.nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+  const int local = t - si.chunk_base;
+  k.lg = local / k.nch;
+  k.c = local % k.nch;
+  k.key0 = k.c * kScoreChunk;
+  k.nkeys = min(kScoreChunk, si.n - k.key0);
+  k.row0 = si.row_base + (int64_t)k.lg * si.n;
+  return k;
+}
+
+template <int GT>
+__global__ __launch_bounds__(256) void score_raw_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int Hkv, int Hq, int G, int d,
+    const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
+    const uint16_t* __restrict__ k, float* __restrict__ raw, double* __restrict__ chunk_stats) {
+  constexpr int KPT = kScoreChunk / 256;
+  __shared__ float a_s[GT * kMaxHeadDim];
+  __shared__ float w_s[GT * (kMaxHeadDim / 2)];
+  __shared__ double red[4];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const Ticket tk = decode_ticket(seqs, S, t);
+  const int l = tk.lg / Hkv, g = tk.lg % Hkv;
+  const int F = d >> 1;
+
+  for (int idx = tid; idx < GT * F; idx += 256) {
+    const int h = idx / F, f = idx % F;
+    float ar = 0.f, ai = 0.f, wv = 0.f;
+    if (h < G) {
+      const int64_t o = ((int64_t)l * Hq + g * G + h) * F + f;
+      const double2 pv = P[o];
+      const double2 ev = E[(int64_t)tk.s * F + f];
+      ar = (float)(pv.x * ev.x - pv.y * ev.y);
+      ai = (float)(pv.x * ev.y + pv.y * ev.x);
+      wv = W[o];
+    }
+    a_s[h * d + 2 * f] = ar;
+    a_s[h * d + 2 * f + 1] = ai;
+    w_s[h * F + f] = wv;
+  }
+  __syncthreads();
+
+  float vals[KPT][GT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int key = tid + j * 256;
+    float acc[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) acc[h] = 0.f;
+    if (key < tk.nkeys) {
+      const uint4* rp = reinterpret_cast<const uint4*>(k + (tk.row0 + tk.key0 + key) * d);
+      for (int c8 = 0; c8 < (d >> 3); ++c8) {
+        const uint4 q = rp[c8];
+        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = c8 * 4 + u;
+          const float x = bf16_lo_s(wd[u]), y = bf16_hi_s(wd[u]);
+          const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            float a = acc[h];
+            a = fmaf(a_s[h * d + 2 * f], x, a);
+            a = fmaf(a_s[h * d + 2 * f + 1], y, a);
+            a = fmaf(w_s[h * F + f], r, a);
+            acc[h] = a;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GT; ++h) vals[j][h] = acc[h];
+  }
+
+  // Chunk statistics per head: count, mean, sum of squared deviations.
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    if (h >= G) break;
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (tid + j * 256 < tk.nkeys) sum += (double)vals[j][h];
+    sum = block_sum256(sum, red);
+    const double mean = sum / (double)tk.nkeys;
+    double m2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (tid + j * 256 < tk.nkeys) {
+        const double dv = (double)vals[j][h] - mean;
+        m2 += dv * dv;
+      }
+    m2 = block_sum256(m2, red);
+    if (tid == 0) {
+      double* cs = chunk_stats + ((int64_t)t * kMaxGroup + h) * 3;
+      cs[0] = (double)tk.nkeys;
+      cs[1] = mean;
+      cs[2] = m2;
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int key = tid + j * 256;
+    if (key < tk.nkeys) {
+      float* rp = raw + (tk.row0 + tk.key0 + key) * G;
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+        if (h < G) rp[h] = vals[j][h];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zmax_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G,
+    const float* __restrict__ raw, const double* __restrict__ chunk_stats,
+    float* __restrict__ scores, double* __restrict__ head_stats) {
+  __shared__ double mu_s[kMaxGroup], inv_s[kMaxGroup];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const Ticket tk = decode_ticket(seqs, S, t);
+  if (tid < G) {
+    const int t0 = seqs[tk.s].chunk_base + tk.lg * tk.nch;
+    double cnt = 0.0, mean = 0.0, m2 = 0.0;
+    for (int cc = 0; cc < tk.nch; ++cc) {
+      const double* cs = chunk_stats + ((int64_t)(t0 + cc) * kMaxGroup + tid) * 3;
+      const double nb = cs[0], mb = cs[1], m2b = cs[2];
+      if (cc == 0) {
+        cnt = nb; mean = mb; m2 = m2b;
+      } else {
+        const double tot = cnt + nb;
+        const double dl = mb - mean;
+        mean += dl * (nb / tot);
+        m2 += m2b + dl * dl * (cnt * nb / tot);
+        cnt = tot;
+      }
+    }
+    const double sigma = sqrt(m2 / cnt);
+    mu_s[tid] = mean;
+    inv_s[tid] = sigma > 0.0 ? 1.0 / sigma : 0.0;
+    if (tk.c == 0 && head_stats) {
+      const int64_t unit = (int64_t)tk.s * L * Hkv + tk.lg;
+      head_stats[(unit * G + tid) * 2] = mean;
+      head_stats[(unit * G + tid) * 2 + 1] = sigma;
+    }
+  }
+  __syncthreads();
+  for (int key = tid; key < tk.nkeys; key += 256) {
+    const int64_t row = tk.row0 + tk.key0 + key;
+    const float* rp = raw + row * G;
+    double best = -__builtin_huge_val();
+    for (int h = 0; h < G; ++h) {
+      const double z = ((double)rp[h] - mu_s[h]) * inv_s[h];
+      best = fmax(best, z);
+    }
+    scores[row] = (float)best;
+  }
+}
+
+template <int GT>
+static void launch_raw(int grid, hipStream_t st, const SeqInfo* seqs, int S, int Hkv, int Hq,
+                       int G, int d, const double2* P, const float* W, const double2* E,
+                       const uint16_t* k, float* raw, double* cs) {
+  hipLaunchKernelGGL(score_raw_kernel<GT>, dim3(grid), dim3(256), 0, st, seqs, S, Hkv, Hq, G, d,
+                     P, W, E, k, raw, cs);
+}
+
+hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
+                        int total_tickets, const double2* P, const float* W, const double2* E,
+                        const uint16_t* k, float* raw, double* chunk_stats, float* scores,
+                        double* head_stats, hipStream_t st) {
+  if (total_tickets == 0) return hipSuccess;
+  const int Hq = Hkv * G;
+  if (G <= 1)
+    launch_raw<1>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+  else if (G <= 2)
+    launch_raw<2>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+  else if (G <= 4)
+    launch_raw<4>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+  else if (G <= 8)
+    launch_raw<8>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+  else
+    launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zmax_kernel, dim3(total_tickets), dim3(256), 0, st, seqs, S, L, Hkv, G, raw,
+                     chunk_stats, scores, head_stats);
+  return hipGetLastError();
+}
+
+}  // namespace tri

@@ -1,0 +1,72 @@
+// Internal types shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+// Per-sequence plan entry, built on the host from cu_len / cur_pos / budget
+// and uploaded once per call.
+struct SeqInfo {
+  int64_t row_base;    // first input row of the sequence: L*Hkv*cu_len[s]
+  int64_t out_base;    // first output row: L*Hkv*cu_b[s], cu_b = prefix of b
+  int32_t n;           // keys per unit
+  int32_t b;           // kept keys per unit, min(budget, n)
+  int32_t p_q;         // current query position
+  int32_t chunk_base;  // first score ticket of the sequence
+};
+static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
+
+// Keys per score work-group ticket.
+constexpr int kScoreChunk = 1024;
+constexpr int kMaxGroup = 16;
+constexpr int kMaxHeadDim = 256;
+
+// Largest s with seqs[s].chunk_base <= t (sequences with no tickets share
+// chunk_base with their successor, so the search lands on the owner).
+__device__ __forceinline__ int find_seq_by_ticket(const SeqInfo* seqs, int S, int t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seqs[mid].chunk_base <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Largest s with seqs[s].out_base <= r among sequences that have output rows.
+__device__ __forceinline__ int find_seq_by_out_row(const SeqInfo* seqs, int S, int64_t r) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seqs[mid].out_base <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Launchers (defined in the .hip files).  Each returns the hipError_t of the
+// launch.
+hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* q,
+                            const int32_t* q_pos, int64_t n_samples, float* centre,
+                            float* absmean, float* R, hipStream_t st);
+
+hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
+                           const SeqInfo* seqs, const float* q_centre,
+                           const float* q_absmean, const float* q_R, double2* P,
+                           float* W, double2* E, hipStream_t st);
+
+hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
+                        int total_tickets, const double2* P, const float* W,
+                        const double2* E, const uint16_t* k, float* raw,
+                        double* chunk_stats, float* scores, double* head_stats,
+                        hipStream_t st);
+
+hipError_t launch_select(const SeqInfo* seqs, int S, int LH, const float* scores,
+                         int32_t* kept_idx, hipStream_t st);
+
+hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int64_t total_out,
+                          const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,
+                          const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
+                          int32_t* pos_out, hipStream_t st);
+
+}  // namespace tri

@@ -1,0 +1,147 @@
+"""Shared helpers for the parity tests: run a synthetic case through the HIP
+library (via the binding) and evaluate units with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from synth import Case
+
+
+def shape_of(case: Case):
+    import rope_aware_key_amd as R
+    sh = case.shape
+    return R.make_shape(sh.head_dim, sh.num_q_heads, sh.num_kv_heads, sh.num_layers, sh.rope_theta)
+
+
+def pinned(a, dtype):
+    """Page-locked host copy (the library reads host arrays during the call)."""
+    t = torch.as_tensor(np.asarray(a, dtype=dtype))
+    return t.pin_memory().numpy()
+
+
+def gpu_calibrate(case: Case):
+    """Fill case.q_centre/q_absmean/q_R from case.calib_q on the GPU."""
+    import rope_aware_key_amd as R
+    n = case.calib_q.shape[1]
+    R.tri_calibrate(shape_of(case), case.calib_q, case.calib_pos, n, case.q_centre, case.q_absmean,
+                    case.q_R)
+    torch.cuda.synchronize()
+
+
+def gpu_run(case: Case, raw=True, stats=True, compact=True, scores_in=None):
+    """Score + select/compact one case on the GPU.  Returns a dict of tensors."""
+    import rope_aware_key_amd as R
+    dev = case.k.device
+    sh = shape_of(case)
+    G = case.shape.group
+    rows = case.total_rows()
+    out_rows = case.total_out_rows()
+    d = case.shape.head_dim
+    cu = pinned(case.cu_len, np.int64)
+    cp = pinned(case.cur_pos, np.int32)
+    bu = pinned(case.budget, np.int32)
+    wsb = R.tri_workspace_bytes(sh, cu)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    res = {}
+    if scores_in is None:
+        scores = torch.full((rows,), float("nan"), dtype=torch.float32, device=dev)
+        raw_t = torch.full((rows, G), float("nan"), dtype=torch.float32, device=dev) if raw else None
+        hs = torch.full((case.num_units, G, 2), float("nan"), dtype=torch.float64, device=dev) if stats else None
+        R.tri_score(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean, case.q_R, scores,
+                    raw_scores=raw_t, head_stats=hs, workspace=ws)
+        res.update(scores=scores, raw=raw_t, head_stats=hs)
+    else:
+        scores = scores_in
+        res["scores"] = scores
+    kept = torch.full((max(out_rows, 1),), -1, dtype=torch.int32, device=dev)
+    k_out = v_out = pos_out = None
+    if compact:
+        k_out = torch.zeros((max(out_rows, 1), d), dtype=torch.int16, device=dev)
+        v_out = torch.zeros((max(out_rows, 1), d), dtype=torch.int16, device=dev) if case.v is not None else None
+        pos_out = torch.full((max(out_rows, 1),), -1, dtype=torch.int32, device=dev)
+    R.tri_select_compact(sh, cu, bu, scores, case.k if compact else None,
+                         case.v if compact else None, case.k_pos if compact else None, kept,
+                         k_out, v_out, pos_out, workspace=ws)
+    torch.cuda.synchronize()
+    res.update(kept=kept[:out_rows], k_out=None if k_out is None else k_out[:out_rows],
+               v_out=None if v_out is None else v_out[:out_rows],
+               pos_out=None if pos_out is None else pos_out[:out_rows])
+    return res
+
+
+def unit_inputs(case: Case, s, l, g):
+    start, n = case.unit_rows(s, l, g)
+    kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
+    pos = case.k_pos[start:start + n].cpu().numpy().astype(np.float64)
+    G = case.shape.group
+    hq = slice(g * G, (g + 1) * G)
+    qc = case.q_centre[l, hq].cpu().double().numpy()
+    centre = qc[..., 0] + 1j * qc[..., 1]
+    absmean = case.q_absmean[l, hq].cpu().double().numpy()
+    Rr = case.q_R[l, hq].cpu().double().numpy()
+    return start, n, kbits, pos, centre, absmean, Rr
+
+
+def oracle_unit(case: Case, s, l, g, factored=False, stats=None):
+    """fp64 oracle scores of one unit. stats: optional (centre, absmean, R)
+    overriding the case's fp32 statistics for this KV head's group."""
+    start, n, kbits, pos, centre, absmean, Rr = unit_inputs(case, s, l, g)
+    if stats is not None:
+        centre, absmean, Rr = stats
+    om = O.rope_omega(case.shape.head_dim, case.shape.rope_theta)
+    kpost = O.bf16_bits_to_f64(kbits)
+    score, S, mu, sigma = O.unit_scores(kpost, pos, float(case.cur_pos[s]), centre, absmean, Rr,
+                                        om, factored=factored)
+    return start, n, score, S, mu, sigma
+
+
+def check_scores(gpu_scores: np.ndarray, ref: np.ndarray, what=""):
+    """|gpu - ref| <= 1e-4 * max(1, |ref|): z-scores are in units of sigma."""
+    err = np.abs(gpu_scores.astype(np.float64) - ref) / np.maximum(1.0, np.abs(ref))
+    worst = float(np.max(err)) if err.size else 0.0
+    assert worst <= 1e-4, f"{what}: worst scaled score error {worst:.3e}"
+    return worst
+
+
+def check_raw(gpu_raw: np.ndarray, S_ref: np.ndarray, sigma_ref: np.ndarray, what=""):
+    """Raw S~_h(i): |gpu - ref| <= 1e-4 * max(|ref|, sigma_h)."""
+    scale = np.maximum(np.abs(S_ref), sigma_ref[:, None])
+    err = np.abs(gpu_raw.T.astype(np.float64) - S_ref) / scale
+    worst = float(np.max(err)) if err.size else 0.0
+    assert worst <= 1e-4, f"{what}: worst scaled raw error {worst:.3e}"
+    return worst
+
+
+def units_of(case: Case):
+    L, H = case.shape.num_layers, case.shape.num_kv_heads
+    return [(s, l, g) for s in range(case.num_seqs) for l in range(L) for g in range(H)]
+
+
+def check_selection_exact(case: Case, res, units=None, rows_units=None):
+    """kept_idx must equal the oracle's selection run on the GPU's own fp32
+    scores (every unit in `units`, default all), and the compacted K, V and
+    position rows must equal the input rows at those indices (units in
+    `rows_units`, default the same units)."""
+    scores = res["scores"].cpu().numpy()
+    kept = res["kept"].cpu().numpy()
+    units = units_of(case) if units is None else units
+    rows_units = units if rows_units is None else rows_units
+    for (s, l, g) in units:
+        start, n = case.unit_rows(s, l, g)
+        ostart, b = case.unit_out_rows(s, l, g)
+        ref = O.select_topb(scores[start:start + n], int(case.budget[s]))
+        assert len(ref) == b
+        np.testing.assert_array_equal(kept[ostart:ostart + b], ref, err_msg=f"unit {(s, l, g)}")
+    for (s, l, g) in rows_units:
+        start, n = case.unit_rows(s, l, g)
+        ostart, b = case.unit_out_rows(s, l, g)
+        ref = O.select_topb(scores[start:start + n], int(case.budget[s]))
+        for name, src_t in (("k_out", case.k), ("v_out", case.v), ("pos_out", case.k_pos)):
+            out_t = res.get(name)
+            if out_t is None or src_t is None:
+                continue
+            src = src_t[start:start + n].cpu().numpy()
+            got = out_t[ostart:ostart + b].cpu().numpy()
+            assert np.array_equal(got, O.compact_rows(src, ref)), f"{name} rows of unit {(s, l, g)}"

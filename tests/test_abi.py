@@ -1,0 +1,139 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol the header declares, and rejects bad arguments before queueing any
+device work (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "triattn.h")
+
+R = pytest.importorskip("rope_aware_key_amd", reason="libtriattn.so not built")
+
+ST = {"OK": 0, "INVALID": 1, "UNSUPPORTED": 2, "WORKSPACE": 3, "HIP": 4}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = ctypes.CDLL(R.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == {"tri_calibrate", "tri_workspace_bytes", "tri_score",
+                          "tri_select_compact", "tri_status_string", "tri_last_error"}
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(R.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    assert R.status_string(0) == "TRI_OK"
+    assert R.status_string(3) == "TRI_ERR_WORKSPACE"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+class _Fake:
+    def __init__(self, addr=FAKE):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _score(shape, cu, cp, **kw):
+    args = dict(k=_Fake(), k_pos=None, q_centre=_Fake(), q_absmean=_Fake(), q_R=_Fake(),
+                scores=_Fake(), workspace=None, workspace_bytes=0)
+    args.update(kw)
+    return R.tri_score(shape, cu, cp, args["k"], args["k_pos"], args["q_centre"],
+                       args["q_absmean"], args["q_R"], args["scores"],
+                       workspace=args["workspace"], workspace_bytes=args["workspace_bytes"],
+                       stream=0)
+
+
+def _status(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+        return 0
+    except R.TriError as e:
+        return e.status
+
+
+@pytest.mark.parametrize("d,hq,hkv,L,theta,expect", [
+    (127, 4, 4, 1, 1e4, "INVALID"), (0, 4, 4, 1, 1e4, "INVALID"), (260, 4, 4, 1, 1e4, "INVALID"),
+    (12, 4, 4, 1, 1e4, "INVALID"), (128, 6, 4, 1, 1e4, "INVALID"), (128, 34, 2, 1, 1e4, "UNSUPPORTED"),
+    (128, 4, 4, 0, 1e4, "INVALID"), (128, 4, 4, 1, 0.0, "INVALID"), (128, 4, 0, 1, 1e4, "INVALID"),
+])
+def test_shape_validation(d, hq, hkv, L, theta, expect):
+    sh = R.make_shape(d, hq, hkv, L, theta)
+    assert _status(_score, sh, [0, 8], [8]) == ST[expect]
+    assert R.tri_workspace_bytes(sh, [0, 8]) == 0
+
+
+def test_score_argument_checks():
+    sh = R.make_shape(128, 8, 2, 2)
+    cu = [0, 100, 250]
+    need = R.tri_workspace_bytes(sh, cu)
+    assert need > 0
+    assert _status(_score, sh, [0, 100, 90], [1, 2]) == ST["INVALID"]          # decreasing
+    assert _status(_score, sh, cu, None) == ST["INVALID"]                      # no cur_pos
+    assert _status(_score, sh, cu, [1, 2], k=None) == ST["INVALID"]
+    assert _status(_score, sh, cu, [1, 2], scores=None) == ST["INVALID"]
+    assert _status(_score, sh, cu, [1, 2], k=_Fake(FAKE + 2)) == ST["INVALID"]  # misaligned
+    assert _status(_score, sh, cu, [1, 2], workspace=_Fake(), workspace_bytes=need - 1) == ST["WORKSPACE"]
+    assert _status(_score, sh, cu, [1, 2]) == ST["WORKSPACE"]
+    # an empty batch queues nothing and succeeds
+    assert _status(_score, sh, [0, 0, 0], [1, 2]) == 0
+    assert _status(_score, sh, [0], []) == 0                                   # no sequences
+    assert _status(_score, sh, [], []) == ST["INVALID"]                        # num_seqs = -1
+    assert "num_seqs" in R.last_error()
+
+
+def _sel(shape, cu, budget, **kw):
+    args = dict(scores=_Fake(), k=_Fake(), v=_Fake(), k_pos=_Fake(), kept=_Fake(),
+                k_out=_Fake(FAKE * 2), v_out=_Fake(FAKE * 3), pos_out=_Fake(FAKE * 4),
+                workspace=None, workspace_bytes=0)
+    args.update(kw)
+    return R.tri_select_compact(shape, cu, budget, args["scores"], args["k"], args["v"],
+                                args["k_pos"], args["kept"], args["k_out"], args["v_out"],
+                                args["pos_out"], workspace=args["workspace"],
+                                workspace_bytes=args["workspace_bytes"], stream=0)
+
+
+def test_select_argument_checks():
+    sh = R.make_shape(64, 4, 2, 1)
+    cu = [0, 50, 80]
+    assert _status(_sel, sh, cu, [10, -1]) == ST["INVALID"]
+    assert _status(_sel, sh, cu, None) == ST["INVALID"]
+    assert _status(_sel, sh, cu, [10, 10], v_out=None) == ST["INVALID"]          # unpaired
+    assert _status(_sel, sh, cu, [10, 10], kept=None) == ST["INVALID"]
+    assert _status(_sel, sh, cu, [10, 10], k=_Fake(FAKE + 8)) == ST["INVALID"]   # misaligned
+    assert _status(_sel, sh, cu, [10, 10]) == ST["WORKSPACE"]
+    assert _status(_sel, sh, cu, [0, 0]) == 0                                    # nothing kept
+    assert _status(_sel, sh, [0, 0, 0], [5, 5]) == 0
+
+
+def test_calibrate_argument_checks():
+    sh = R.make_shape(64, 4, 2, 1)
+
+    def cal(q=_Fake(), n=10, c=_Fake(), a=_Fake(), r=_Fake()):
+        return R.tri_calibrate(sh, q, None, n, c, a, r, stream=0)
+
+    assert _status(cal, n=0) == ST["INVALID"]
+    assert _status(cal, q=None) == ST["INVALID"]
+    assert _status(cal, r=None) == ST["INVALID"]
+    assert _status(cal, q=_Fake(FAKE + 2)) == ST["INVALID"]
+
+
+def test_workspace_grows_with_batch():
+    sh = R.make_shape(128, 28, 4, 28)
+    small = R.tri_workspace_bytes(sh, [0, 1024])
+    big = R.tri_workspace_bytes(sh, np.arange(9) * 32768)
+    assert 0 < small < big

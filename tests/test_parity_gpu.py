@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (scores are z-scores, in units of the per-head sigma):
+  scores      |gpu - ref| <= 1e-4 * max(1, |ref|)
+  raw S~_h    |gpu - ref| <= 1e-4 * max(|ref|, sigma_h)
+  statistics  relative 1e-5 (calibration), mu/sigma relative 1e-5 of sigma
+  selection   bit-exact against the oracle's selection on the GPU's own scores
+  compaction  byte-exact
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from harness import (check_raw, check_scores, check_selection_exact, gpu_calibrate, gpu_run,
+                     oracle_unit, units_of)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _compare_units(case, res, units, factored):
+    scores = res["scores"].cpu().numpy()
+    raw = res["raw"].cpu().numpy() if res.get("raw") is not None else None
+    hs = res["head_stats"].cpu().numpy() if res.get("head_stats") is not None else None
+    L, H = case.shape.num_layers, case.shape.num_kv_heads
+    worst = 0.0
+    for (s, l, g) in units:
+        start, n, ref, S, mu, sigma = oracle_unit(case, s, l, g, factored=factored)
+        worst = max(worst, check_scores(scores[start:start + n], ref, f"unit {(s, l, g)}"))
+        if raw is not None:
+            check_raw(raw[start:start + n], S, sigma, f"raw unit {(s, l, g)}")
+        if hs is not None:
+            u = (s * L + l) * H + g
+            np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * np.max(sigma))
+            np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5)
+    return worst
+
+
+# ------------------------------------------------------------- calibration
+def test_calibrate_c1_matches_oracle():
+    case = synth.config_case(1, device=DEV)
+    gpu_calibrate(case)
+    q = O.bf16_bits_to_f64(case.calib_q[0].cpu().numpy().view(np.uint16))   # [N, Hq, d]
+    om = O.rope_omega(128, 1e4)
+    centre, absmean, Rr = O.calibrate(q, case.calib_pos.cpu().numpy(), om)
+    qc = case.q_centre[0].cpu().double().numpy()
+    np.testing.assert_allclose(qc[..., 0], centre.real, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(qc[..., 1], centre.imag, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(case.q_absmean[0].cpu().double().numpy(), absmean, rtol=1e-5)
+    np.testing.assert_allclose(case.q_R[0].cpu().double().numpy(), Rr, rtol=1e-5)
+    assert 0.9 < float(Rr.mean()) < 0.99     # the synthetic queries are concentrated
+
+
+def test_calibrate_pre_rope_and_multi_layer():
+    torch.manual_seed(0)
+    L, N, Hq, d = 2, 257, 3, 16
+    q = (torch.randn(L, N, Hq, d, device=DEV) + 0.7).to(torch.bfloat16).view(torch.int16)
+    import rope_aware_key_amd as R
+    sh = R.make_shape(d, Hq, 1, L)
+    c = torch.empty(L, Hq, d // 2, 2, device=DEV)
+    a = torch.empty(L, Hq, d // 2, device=DEV)
+    r = torch.empty(L, Hq, d // 2, device=DEV)
+    R.tri_calibrate(sh, q, None, N, c, a, r)
+    torch.cuda.synchronize()
+    qq = O.bf16_bits_to_f64(q.cpu().numpy().view(np.uint16))
+    om = O.rope_omega(d, 1e4)
+    for l in range(L):
+        centre, absmean, Rr = O.calibrate(qq[l], None, om)
+        np.testing.assert_allclose(c[l, ..., 0].cpu().numpy(), centre.real, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(c[l, ..., 1].cpu().numpy(), centre.imag, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(a[l].cpu().numpy(), absmean, rtol=1e-5)
+        np.testing.assert_allclose(r[l].cpu().numpy(), Rr, rtol=1e-5)
+
+
+# ----------------------------------------------------------- c1 end to end
+def test_c1_end_to_end_term_by_term():
+    """Smallest workload in full: GPU calibration -> score -> select/compact,
+    against the oracle's own calibration and term-by-term scores."""
+    case = synth.config_case(1, device=DEV)
+    gpu_calibrate(case)
+    res = gpu_run(case)
+    q = O.bf16_bits_to_f64(case.calib_q[0].cpu().numpy().view(np.uint16))
+    om = O.rope_omega(128, 1e4)
+    stats = O.calibrate(q, case.calib_pos.cpu().numpy(), om)
+    start, n, ref, S, mu, sigma = oracle_unit(case, 0, 0, 0, factored=False, stats=stats)
+    check_scores(res["scores"].cpu().numpy(), ref, "c1")
+    check_raw(res["raw"].cpu().numpy(), S, sigma, "c1 raw")
+    check_selection_exact(case, res)
+    # end-to-end kept set vs the oracle's own selection on fp64 scores
+    b = case.kept(0)
+    ref_kept = set(O.select_topb(ref, b).tolist())
+    got = set(res["kept"].cpu().numpy().tolist())
+    thr = np.sort(ref)[::-1][b - 1]
+    diff = ref_kept ^ got
+    assert all(abs(ref[i] - thr) <= 1e-4 * max(1.0, abs(thr)) for i in diff), sorted(diff)[:10]
+
+
+# ------------------------------------------- reduced configs, many tiles
+REDUCED = {
+    "c2": dict(cid=2, S=2, L=1),                 # 16 units, n = 3200 (3 tiles + tail)
+    "c3": dict(cid=3, S=1, L=1, n=5000, B=2048),  # G = 7, 4 tiles + ragged tail
+    "c4": dict(cid=4, S=6, L=1, n_range=(100, 3000)),  # ragged lengths, some B >= n
+    "c5": dict(cid=5, n=5000, B=1024),           # d = 64, G = 8, duplicated blocks
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_config_parity(name):
+    kw = dict(REDUCED[name])
+    cid = kw.pop("cid")
+    case = synth.config_case(cid, device=DEV, **kw)
+    res = gpu_run(case)
+    units = units_of(case)
+    # every unit against the factored oracle path, two against term-by-term
+    _compare_units(case, res, units, factored=True)
+    _compare_units(case, res, units[:1] + units[-1:], factored=False)
+    check_selection_exact(case, res)
+
+
+def test_duplicate_keys_score_bitwise_equal():
+    case = synth.config_case(5, device=DEV, n=4096, B=512)
+    res = gpu_run(case, raw=False, stats=False, compact=False)
+    sc = res["scores"].cpu().numpy()
+    for (s, l, g) in units_of(case):
+        start, n = case.unit_rows(s, l, g)
+        u = sc[start:start + n].reshape(-1, 128)
+        assert np.array_equal(u[:, 64:].view(np.uint32), u[:, :64].view(np.uint32))
+    check_selection_exact(case, res)
+
+
+def test_determinism_bitwise():
+    case = synth.config_case(3, device=DEV, S=1, L=2, n=3000, B=700)
+    a = gpu_run(case)
+    b = gpu_run(case)
+    for key in ("scores", "raw", "head_stats", "kept", "k_out", "v_out", "pos_out"):
+        assert torch.equal(a[key].view(torch.uint8) if a[key].dtype.is_floating_point else a[key],
+                           b[key].view(torch.uint8) if b[key].dtype.is_floating_point else b[key]), key
+
+
+# ----------------------------------------------- hand-built selection cases
+def _hand_case(lens, budgets, d=64, L=1, Hkv=2, G=1):
+    shape = synth.Shape(d, Hkv * G, Hkv, L)
+    return synth.build_case("hand", shape, lens, budgets, device=DEV, seed=3)
+
+
+def test_select_edge_cases_exact():
+    lens = [0, 1, 5, 1025, 3000, 700, 2049]
+    budgets = [4, 0, 9, 1025, 17, 3, 2048]
+    case = _hand_case(lens, budgets)
+    rows = case.total_rows()
+    g = np.random.default_rng(7)
+    pool = np.array([0.0, -0.0, 1.5, -1.5, np.inf, -np.inf, np.nan, 3.25, 1e-38, -1e-38], np.float32)
+    sc = g.choice(pool, size=rows).astype(np.float32)
+    # one unit with all-equal scores, one with random normals
+    s0, n0 = case.unit_rows(4, 0, 1)
+    sc[s0:s0 + n0] = 2.0
+    s1, n1 = case.unit_rows(6, 0, 0)
+    sc[s1:s1 + n1] = g.normal(size=n1).astype(np.float32)
+    scores = torch.as_tensor(sc, device=DEV)
+    res = gpu_run(case, scores_in=scores)
+    check_selection_exact(case, res)
+    ostart, b = case.unit_out_rows(4, 0, 1)
+    np.testing.assert_array_equal(res["kept"][ostart:ostart + b].cpu().numpy(), np.arange(17))
+
+
+@pytest.mark.parametrize("n,B", [(4096, 4095), (4096, 1), (20000, 10000), (33000, 2048)])
+def test_select_many_ties(n, B):
+    case = _hand_case([n], [B], Hkv=1)
+    g = np.random.default_rng(n + B)
+    sc = g.integers(-3, 4, size=n).astype(np.float32) * 0.5    # 7 distinct values
+    res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
+    check_selection_exact(case, res)
+
+
+# ---------------------------------------------- full sizes (bench launch)
+def _sample(units, k, seed=0):
+    g = np.random.default_rng(seed)
+    idx = sorted(g.choice(len(units), size=min(k, len(units)), replace=False).tolist())
+    return [units[i] for i in idx]
+
+
+@pytest.mark.timeout(600)
+def test_c3_full_size_sampled():
+    """32K -> 2048 long-reasoning workload at full size: sampled units against
+    the oracle, selection bit-exact on every unit, rows on sampled units."""
+    case = synth.config_case(3, device=DEV)
+    res = gpu_run(case, raw=False, stats=True)
+    units = units_of(case)
+    samp = _sample(units, 6, seed=3)
+    _compare_units(case, res, samp, factored=True)
+    _compare_units(case, res, samp[:1], factored=False)
+    check_selection_exact(case, res, units=units, rows_units=samp)
+
+
+@pytest.mark.timeout(600)
+def test_c2_full_size_sampled():
+    case = synth.config_case(2, device=DEV)
+    res = gpu_run(case, raw=False, stats=True)
+    units = units_of(case)
+    samp = _sample(units, 6, seed=2)
+    _compare_units(case, res, samp, factored=True)
+    check_selection_exact(case, res, units=_sample(units, 2000, seed=5), rows_units=samp)
+
+
+@pytest.mark.timeout(600)
+def test_c4_full_layer_sampled():
+    case = synth.config_case(4, device=DEV)
+    res = gpu_run(case, raw=False, stats=True)
+    units = units_of(case)
+    samp = _sample(units, 6, seed=4)
+    _compare_units(case, res, samp, factored=True)
+    check_selection_exact(case, res, units=units, rows_units=samp)
+
+
+@pytest.mark.timeout(600)
+def test_c5_full_size():
+    case = synth.config_case(5, device=DEV)
+    res = gpu_run(case, raw=False, stats=True)
+    units = units_of(case)
+    _compare_units(case, res, units, factored=True)
+    check_selection_exact(case, res, units=units, rows_units=units[:2])
+    sc = res["scores"].cpu().numpy()
+    for (s, l, g) in units:
+        start, n = case.unit_rows(s, l, g)
+        u = sc[start:start + n].reshape(-1, 128)
+        assert np.array_equal(u[:, 64:].view(np.uint32), u[:, :64].view(np.uint32))
