@@ -115,7 +115,10 @@ struct Plan {
   int64_t total_rows = 0, total_out = 0;
   int64_t tickets = 0;
   // workspace offsets (bytes)
-  size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_raw = 0;
+  size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ustats = 0,
+         off_ctrl = 0, off_raw = 0;
+  int64_t n_units = 0;
+  bool fused = false;
   size_t score_bytes = 0, select_bytes = 0;
 };
 
@@ -174,7 +177,13 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.off_W = take((size_t)p.L * p.Hq * p.F * sizeof(float));
   p.off_E = take((size_t)S * p.F * sizeof(double2));
   p.off_stats = take((size_t)p.tickets * tri::kMaxGroup * 3 * sizeof(double));
-  p.off_raw = take((size_t)p.total_rows * p.G * sizeof(float));
+  p.n_units = (int64_t)S * LH;
+  p.off_ustats = take((size_t)p.n_units * tri::kMaxGroup * 2 * sizeof(double));
+  p.off_ctrl = take(((size_t)tri::kCtrlHeader + (size_t)p.n_units * tri::kUnitCtrlStride) *
+                    sizeof(uint32_t));
+  // The fused path keeps raw scores on chip; the generic path spills them.
+  p.fused = tri::fused_supported(p.d);
+  p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
   p.select_bytes = after_seq;
   return TRI_OK;
@@ -235,7 +244,7 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   if (!k || !q_centre || !q_absmean || !q_R || !scores)
     return fail(TRI_ERR_INVALID_ARGUMENT, "k, statistics and scores must be non-NULL");
   if (!aligned16(k)) return fail(TRI_ERR_INVALID_ARGUMENT, "k must be 16-byte aligned");
-  const size_t need = raw_scores ? p.off_raw : p.score_bytes;
+  const size_t need = (raw_scores || p.fused) ? p.off_raw : p.score_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
   hipStream_t s = (hipStream_t)stream;
@@ -245,8 +254,14 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   if (e == hipSuccess)
     e = tri::launch_prologue(p.L, p.Hq, p.d, shape->rope_theta, p.S, dseq, q_centre, q_absmean,
                              q_R, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
-                             (double2*)(ws + p.off_E), s);
-  if (e == hipSuccess)
+                             (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl), p.n_units, s);
+  if (e == hipSuccess && p.fused)
+    e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
+                                (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
+                                (const double2*)(ws + p.off_E), k, (double*)(ws + p.off_stats),
+                                (double*)(ws + p.off_ustats), (uint32_t*)(ws + p.off_ctrl),
+                                scores, raw_scores, head_stats, s);
+  else if (e == hipSuccess)
     e = tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                           (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                           (const double2*)(ws + p.off_E), k,

@@ -1,0 +1,445 @@
+// Fused TriAttention score kernel for head_dim a multiple of 32 (gfx950).
+//
+// Per key i of a unit and query head h (talk page "聊聊 TriAttention", S_trig,
+// S_norm and averaged-score equations; the offset mean and current position
+// are folded into A_f = E[q_f] C_f exp(i omega_f p_q) by the prologue):
+//   S~_h(i) = sum_j a_h[j] k'_i[j] + sum_f w_h[f] |k'_i,f|
+// with a_h[2f] = Re A_f, a_h[2f+1] = Im A_f and w_h[f] = (1 - R_f) E|q_f|.
+// Then z_h(i) = (S~_h(i) - mu_h) / sigma_h over the unit and the score is the
+// max over the G heads of the group (hyper.ai summary, section "方法").
+//
+// Mapping onto CDNA4:
+//  * The dot product with the post-RoPE key is a (16 heads x d) x (d x 16
+//    keys) product per block of 16 keys: v_mfma_f32_16x16x32_bf16.  The keys
+//    are bf16 already; the fp64 coefficient a_h is split into three bf16
+//    terms (hi + mid + lo, ~25 significant bits), so three MFMAs per 32-wide
+//    step reproduce an fp32-accurate dot product with exact bf16 x bf16
+//    products and fp32 accumulation.
+//  * The norm term sum_f w_f |k_f| uses v_mfma_f32_16x16x4_f32 on the fp32
+//    magnitudes (computed once per key band on the VALU, shared by all G
+//    heads).
+//  * Each lane loads 16 bytes of one key per step (4 lanes cover 64
+//    contiguous bytes of a row); the 4 waves of a work-group take
+//    interleaved blocks so the group streams one contiguous span of K.
+//  * Work is cut into "tickets": one chunk of kScoreChunk keys of one unit.
+//    The kernel is persistent: each work-group claims tickets in order from
+//    an atomic counter and keeps two chunks' raw per-head scores in LDS.  It
+//    computes chunk i, publishes its per-head (count, mean, M2) in fp64, then
+//    computes chunk i+1 before it finalizes chunk i, so the wait for the
+//    rest of chunk i's unit overlaps useful streaming.  The last chunk of a
+//    unit to publish merges the unit's chunks in chunk order (Chan's update)
+//    and publishes (mu, sigma) per head; everyone reads those, so every
+//    chunk z-scores with identical numbers (deterministic; equal keys score
+//    equally).
+//  * Waits cannot deadlock: tickets are claimed in order and a work-group
+//    claims its next ticket (and publishes it) before it waits on its
+//    previous one, so a unit's missing chunks are always claimable while the
+//    resident work-groups outnumber the chunks of one unit (a few hundred
+//    resident groups against at most 2^31 / kScoreChunk chunks of a unit
+//    that fits in one call).  A spin bound turns a broken invariant into an
+//    error flag instead of a hang.
+//  * Cross-work-group data (chunk statistics, unit statistics, flags) move
+//    through agent-scope atomics, which are coherent across the XCDs' L2
+//    caches; an s_waitcnt orders the data stores before the flag update.
+#include "tri_internal.hpp"
+
+namespace tri {
+
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo_m(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_m(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x ~= hi + mid + lo with each term a bf16 (relative residual ~2^-25).
+__device__ __forceinline__ void split3(double x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_rne((float)x);
+  const double r1 = x - (double)__uint_as_float(hi << 16);
+  mid = bf16_rne((float)r1);
+  const double r2 = r1 - (double)__uint_as_float(mid << 16);
+  lo = bf16_rne((float)r2);
+}
+
+constexpr int kFusedThreads = 256;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kRawStride = kScoreChunk + 4;  // LDS row stride (floats) per head
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ double wave_sum_f(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ double ld_agent(const double* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return __longlong_as_double((long long)u);
+}
+__device__ __forceinline__ void st_agent(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's earlier memory operations have completed, so that
+// data stored before a flag update is visible before the flag.
+__device__ __forceinline__ void drain_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
+
+struct Chunk {
+  int t, s, lg, l, g, c, nch, nkeys;
+  int64_t row0, unit;
+};
+
+__device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L, int Hkv, int t) {
+  Chunk ck;
+  ck.t = t;
+  ck.s = find_seq_by_ticket(seqs, S, t);
+  const SeqInfo si = seqs[ck.s];
+  ck.nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+  const int local = t - si.chunk_base;
+  ck.lg = local / ck.nch;
+  ck.c = local % ck.nch;
+  ck.l = ck.lg / Hkv;
+  ck.g = ck.lg % Hkv;
+  const int key0 = ck.c * kScoreChunk;
+  ck.nkeys = min(kScoreChunk, si.n - key0);
+  ck.row0 = si.row_base + (int64_t)ck.lg * si.n + key0;
+  ck.unit = (int64_t)ck.s * L * Hkv + ck.lg;
+  return ck;
+}
+
+struct Shared {
+  double red[kFusedWaves][kMaxGroup];
+  double mean[kMaxGroup];
+  float zmul[kMaxGroup], zadd[kMaxGroup];
+  int ticket;
+  int last;
+};
+
+// Raw scores of one chunk into raw (LDS, [G][kRawStride]).
+template <int STEPS>
+__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int Hq,
+                                          const double2* __restrict__ P,
+                                          const float* __restrict__ W,
+                                          const double2* __restrict__ E,
+                                          const uint16_t* __restrict__ k, float* raw) {
+  constexpr int D = STEPS * 32;
+  constexpr int F = D / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, q = lane >> 4;
+
+  // MFMA A operands: lane holds head m, d-range of lane group q.
+  bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];
+  float wn[STEPS][4];
+  {
+    const bool live = m < G;
+    const int64_t pbase = ((int64_t)ck.l * Hq + ck.g * G + (live ? m : 0)) * F;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      uint32_t h3[8], m3[8], l3[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = 4 * (4 * st + q) + u;
+        double re = 0.0, im = 0.0;
+        float wv = 0.f;
+        if (live) {
+          const double2 pv = P[pbase + f];
+          const double2 ev = E[(int64_t)ck.s * F + f];
+          re = pv.x * ev.x - pv.y * ev.y;
+          im = pv.x * ev.y + pv.y * ev.x;
+          wv = W[pbase + f];
+        }
+        split3(re, h3[2 * u], m3[2 * u], l3[2 * u]);
+        split3(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+        wn[st][u] = wv;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a_hi[st][j] = (short)h3[j];
+        a_mid[st][j] = (short)m3[j];
+        a_lo[st][j] = (short)l3[j];
+      }
+    }
+  }
+
+  // Stream the chunk: wave w takes blocks of 16 keys w, w+4, ...
+  const int nkeys = ck.nkeys;
+  const int nblk = (nkeys + 15) >> 4;
+  const uint4* kbase = reinterpret_cast<const uint4*>(k + ck.row0 * D);
+  auto load_block = [&](int b, uint4 (&bv)[STEPS]) {
+    int key = b * 16 + m;
+    key = key < nkeys ? key : nkeys - 1;  // padding lanes re-read a valid row
+    const uint4* rp = kbase + (int64_t)key * (D / 8);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
+  };
+  uint4 cur[STEPS], nxt[STEPS];
+  int b = wave;
+  if (b < nblk) load_block(b, cur);
+  for (; b < nblk; b += kFusedWaves) {
+    const int bn = b + kFusedWaves;
+    if (bn < nblk) load_block(bn, nxt);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      bf16x8_t bk;
+      __builtin_memcpy(&bk, &cur[st], 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[st], bk, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[st], bk, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[st], bk, acc, 0, 0, 0);
+      const uint32_t wd[4] = {cur[st].x, cur[st].y, cur[st].z, cur[st].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x = bf16_lo_m(wd[u]), y = bf16_hi_m(wd[u]);
+        const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc, 0, 0, 0);
+      }
+    }
+    // D layout: lane holds heads 4q..4q+3 of key b*16 + m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q + i;
+      if (h < G) raw[h * kRawStride + b * 16 + m] = acc[i];
+    }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) cur[st] = nxt[st];
+  }
+}
+
+// Per-head (count, mean, M2) of the chunk in fp64; publish them; the last
+// chunk of the unit to arrive merges all chunks and publishes (mu, sigma).
+__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, const float* raw,
+                                              Shared& sh, double* __restrict__ chunk_stats,
+                                              double* __restrict__ unit_stats,
+                                              uint32_t* __restrict__ unit_ctrl) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nkeys = ck.nkeys;
+  double acc_h[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) acc_h[h] = 0.0;
+  for (int i = tid; i < nkeys; i += kFusedThreads) {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) acc_h[h] += (double)raw[h * kRawStride + i];
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    if (h < G) {
+      const double v = wave_sum_f(acc_h[h]);
+      if (lane == 0) sh.red[wave][h] = v;
+    }
+  __syncthreads();
+  if (tid < G)
+    sh.mean[tid] = (sh.red[0][tid] + sh.red[1][tid] + sh.red[2][tid] + sh.red[3][tid]) /
+                   (double)nkeys;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) acc_h[h] = 0.0;
+  for (int i = tid; i < nkeys; i += kFusedThreads) {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) {
+        const double dv = (double)raw[h * kRawStride + i] - sh.mean[h];
+        acc_h[h] += dv * dv;
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    if (h < G) {
+      const double v = wave_sum_f(acc_h[h]);
+      if (lane == 0) sh.red[wave][h] = v;
+    }
+  __syncthreads();
+
+  uint32_t* arrive = unit_ctrl + ck.unit * kUnitCtrlStride;
+  uint32_t* ready = arrive + kUnitCtrlStride / 2;
+  if (tid == 0) {
+    double* cs = chunk_stats + (int64_t)ck.t * kMaxGroup * 3;
+    for (int h = 0; h < G; ++h) {
+      st_agent(cs + 3 * h, (double)nkeys);
+      st_agent(cs + 3 * h + 1, sh.mean[h]);
+      st_agent(cs + 3 * h + 2, sh.red[0][h] + sh.red[1][h] + sh.red[2][h] + sh.red[3][h]);
+    }
+    drain_memory_ops();
+    const uint32_t before =
+        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.last = before + 1 == (uint32_t)ck.nch;
+  }
+  __syncthreads();
+  if (sh.last) {
+    // Every chunk has published; merge them in chunk order.
+    if (tid < G) {
+      const int t0 = ck.t - ck.c;
+      double cnt = 0.0, mu = 0.0, m2 = 0.0;
+      for (int cc = 0; cc < ck.nch; ++cc) {
+        const double* cs = chunk_stats + ((int64_t)(t0 + cc) * kMaxGroup + tid) * 3;
+        const double nb = ld_agent(cs), mb = ld_agent(cs + 1), m2b = ld_agent(cs + 2);
+        if (cc == 0) {
+          cnt = nb; mu = mb; m2 = m2b;
+        } else {
+          const double tot = cnt + nb;
+          const double dl = mb - mu;
+          mu += dl * (nb / tot);
+          m2 += m2b + dl * dl * (cnt * nb / tot);
+          cnt = tot;
+        }
+      }
+      double* us = unit_stats + (ck.unit * kMaxGroup + tid) * 2;
+      st_agent(us, mu);
+      st_agent(us + 1, sqrt(m2 / cnt));
+      drain_memory_ops();
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait for the unit's statistics, then z-score the chunk, take the max over
+// the group and write the scores (and the optional debug outputs).
+__device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, const float* raw,
+                                               Shared& sh, const double* __restrict__ unit_stats,
+                                               const uint32_t* __restrict__ unit_ctrl,
+                                               uint32_t* __restrict__ err_flag,
+                                               float* __restrict__ scores,
+                                               float* __restrict__ raw_out,
+                                               double* __restrict__ head_stats) {
+  const int tid = threadIdx.x;
+  const uint32_t* ready = unit_ctrl + ck.unit * kUnitCtrlStride + kUnitCtrlStride / 2;
+  if (tid == 0) {
+    uint32_t spins = 0;
+    while (ld_agent_u32(ready) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    const double* us = unit_stats + (ck.unit * kMaxGroup + tid) * 2;
+    const double mu = ld_agent(us), sigma = ld_agent(us + 1);
+    const double inv = sigma > 0.0 ? 1.0 / sigma : 0.0;
+    sh.zmul[tid] = (float)inv;
+    sh.zadd[tid] = (float)(-mu * inv);
+    if (ck.c == 0 && head_stats) {
+      head_stats[(ck.unit * G + tid) * 2] = mu;
+      head_stats[(ck.unit * G + tid) * 2 + 1] = sigma;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < ck.nkeys; i += kFusedThreads) {
+    float best = -__builtin_inff();
+    for (int h = 0; h < G; ++h)
+      best = fmaxf(best, fmaf(raw[h * kRawStride + i], sh.zmul[h], sh.zadd[h]));
+    scores[ck.row0 + i] = best;
+    if (raw_out)
+      for (int h = 0; h < G; ++h) raw_out[(ck.row0 + i) * G + h] = raw[h * kRawStride + i];
+  }
+}
+
+// STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
+// tickets.
+template <int STEPS>
+__global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int total_tickets,
+    const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
+    const uint16_t* __restrict__ k, double* __restrict__ chunk_stats,
+    double* __restrict__ unit_stats, uint32_t* __restrict__ ctrl, float* __restrict__ scores,
+    float* __restrict__ raw_out, double* __restrict__ head_stats) {
+  extern __shared__ float raw_s[];  // 2 buffers of [G][kRawStride]
+  __shared__ Shared sh;
+  uint32_t* ticket_ctr = ctrl;
+  uint32_t* err_flag = ctrl + 1;
+  uint32_t* unit_ctrl = ctrl + kCtrlHeader;
+  const int Hq = Hkv * G;
+
+  Chunk prev;
+  bool have_prev = false;
+  int cur = 0;
+  for (;;) {
+    if (threadIdx.x == 0)
+      sh.ticket = (int)__hip_atomic_fetch_add(ticket_ctr, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = sh.ticket;
+    __syncthreads();
+    const bool have = t < total_tickets;
+    float* buf_cur = raw_s + cur * G * kRawStride;
+    float* buf_prev = raw_s + (cur ^ 1) * G * kRawStride;
+    Chunk ck;
+    if (have) {
+      ck = decode_chunk(seqs, S, L, Hkv, t);
+      chunk_raw<STEPS>(ck, G, Hq, P, W, E, k, buf_cur);
+      __syncthreads();
+      chunk_publish(ck, G, buf_cur, sh, chunk_stats, unit_stats, unit_ctrl);
+      __syncthreads();
+    }
+    if (have_prev) {
+      chunk_finalize(prev, G, buf_prev, sh, unit_stats, unit_ctrl, err_flag, scores, raw_out,
+                     head_stats);
+      __syncthreads();
+    }
+    if (!have) break;
+    prev = ck;
+    have_prev = true;
+    cur ^= 1;
+  }
+}
+
+template <int STEPS>
+static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
+                                 const SeqInfo* seqs, int S, int L, int Hkv, int G,
+                                 const double2* P, const float* W, const double2* E,
+                                 const uint16_t* k, double* cs, double* us, uint32_t* ctrl,
+                                 float* scores, float* raw, double* hs) {
+  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS>);
+  // Two 16-head buffers need more than 64 KB of LDS: raise the limit once.
+  static const hipError_t attr = hipFuncSetAttribute(
+      kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+      2 * kMaxGroup * kRawStride * (int)sizeof(float));
+  if (attr != hipSuccess) return attr;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  int grid = cus * per_cu;
+  if (grid > total_tickets) grid = total_tickets;
+  hipLaunchKernelGGL(score_fused_kernel<STEPS>, dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
+                     L, Hkv, G, total_tickets, P, W, E, k, cs, us, ctrl, scores, raw, hs);
+  return hipGetLastError();
+}
+
+bool fused_supported(int d) { return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim; }
+
+hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
+                              int total_tickets, const double2* P, const float* W,
+                              const double2* E, const uint16_t* k, double* chunk_stats,
+                              double* unit_stats, uint32_t* ctrl, float* scores, float* raw,
+                              double* head_stats, hipStream_t st) {
+  if (total_tickets == 0) return hipSuccess;
+  const size_t lds = 2 * (size_t)G * kRawStride * sizeof(float);
+  switch (d / 32) {
+#define TRI_CASE(n)                                                                  \
+  case n:                                                                            \
+    return launch_fused_t<n>(total_tickets, lds, st, seqs, S, L, Hkv, G, P, W, E, k, \
+                             chunk_stats, unit_stats, ctrl, scores, raw, head_stats);
+    TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7) TRI_CASE(8)
+#undef TRI_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tri
