@@ -113,10 +113,11 @@ struct Plan {
   std::vector<SeqInfo> seqs;
   int S = 0, L = 0, Hkv = 0, Hq = 0, G = 0, d = 0, F = 0;
   int64_t total_rows = 0, total_out = 0;
+  int max_n = 0, max_b = 0;
   int64_t tickets = 0;
   // workspace offsets (bytes)
   size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ustats = 0,
-         off_ctrl = 0, off_raw = 0;
+         off_ctrl = 0, off_apack = 0, off_raw = 0;
   int64_t n_units = 0;
   bool fused = false;
   size_t score_bytes = 0, select_bytes = 0;
@@ -154,6 +155,8 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
       b = budget[s] < n ? budget[s] : n;
     }
     si.b = (int32_t)b;
+    if (n > p.max_n) p.max_n = (int)n;
+    if (b > p.max_b) p.max_b = (int)b;
     si.out_base = LH * out_acc;
     out_acc += b;
     si.p_q = cur_pos ? cur_pos[s] : 0;
@@ -183,6 +186,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
                     sizeof(uint32_t));
   // The fused path keeps raw scores on chip; the generic path spills them.
   p.fused = tri::fused_supported(p.d);
+  p.off_apack = take(tri::fused_operand_bytes(p.d, p.n_units));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
   p.select_bytes = after_seq;
@@ -258,7 +262,8 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   if (e == hipSuccess && p.fused)
     e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                                 (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
-                                (const double2*)(ws + p.off_E), k, (double*)(ws + p.off_stats),
+                                (const double2*)(ws + p.off_E), ws + p.off_apack, k,
+                                (double*)(ws + p.off_stats),
                                 (double*)(ws + p.off_ustats), (uint32_t*)(ws + p.off_ctrl),
                                 scores, raw_scores, head_stats, s);
   else if (e == hipSuccess)
@@ -295,9 +300,9 @@ tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs, const in
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
   hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   const int LH = p.L * p.Hkv;
-  if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, scores, kept_idx, s);
+  if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, s);
   if (e == hipSuccess && (k_out || v_out || pos_out))
-    e = tri::launch_compact(dseq, p.S, LH, p.d, p.total_out, kept_idx, k, v, k_pos, k_out, v_out,
+    e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
                             pos_out, s);
   if (e != hipSuccess)
     return fail(TRI_ERR_HIP, std::string("select_compact: ") + hipGetErrorString(e));

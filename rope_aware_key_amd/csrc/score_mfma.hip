@@ -70,6 +70,7 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kRawStride = kScoreChunk + 4;  // LDS row stride (floats) per head
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kPrefetch = 4;  // blocks of 16 keys in flight per wave
 
 __device__ __forceinline__ double wave_sum_f(double v) {
 #pragma unroll
@@ -117,60 +118,53 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
 }
 
 struct Shared {
-  double red[kFusedWaves][kMaxGroup];
-  double mean[kMaxGroup];
+  double red1[kFusedWaves][kMaxGroup];
+  double red2[kFusedWaves][kMaxGroup];
   float zmul[kMaxGroup], zadd[kMaxGroup];
   int ticket;
   int last;
 };
 
-// Raw scores of one chunk into raw (LDS, [G][kRawStride]).
+// MFMA operands of one unit, packed by pack_operands_kernel in lane order:
+// vector 4*st + 0/1/2 is the bf16 hi/mid/lo split of a_h over the lane's
+// eight d-elements of step st, vector 4*st + 3 the four fp32 norm weights.
 template <int STEPS>
-__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int Hq,
-                                          const double2* __restrict__ P,
-                                          const float* __restrict__ W,
-                                          const double2* __restrict__ E,
-                                          const uint16_t* __restrict__ k, float* raw) {
+__device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ apack,
+                                                      int64_t unit) {
+  return apack + unit * (4 * STEPS) * 64;
+}
+
+// Raw scores of one chunk into raw (LDS, [G][kRawStride]); per-head
+// sum and sum of squares of the chunk's raw scores in fp64 into sh.s1/s2.
+template <int STEPS>
+__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, const uint4* __restrict__ apack,
+                                          const uint16_t* __restrict__ k, float* raw,
+                                          Shared& sh) {
   constexpr int D = STEPS * 32;
-  constexpr int F = D / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
 
-  // MFMA A operands: lane holds head m, d-range of lane group q.
+  // A operands: lane holds head m (zero rows beyond G), d-range of group q.
   bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];
   float wn[STEPS][4];
   {
-    const bool live = m < G;
-    const int64_t pbase = ((int64_t)ck.l * Hq + ck.g * G + (live ? m : 0)) * F;
+    const uint4* op = unit_operands<STEPS>(apack, ck.unit) + lane;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-      uint32_t h3[8], m3[8], l3[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int f = 4 * (4 * st + q) + u;
-        double re = 0.0, im = 0.0;
-        float wv = 0.f;
-        if (live) {
-          const double2 pv = P[pbase + f];
-          const double2 ev = E[(int64_t)ck.s * F + f];
-          re = pv.x * ev.x - pv.y * ev.y;
-          im = pv.x * ev.y + pv.y * ev.x;
-          wv = W[pbase + f];
-        }
-        split3(re, h3[2 * u], m3[2 * u], l3[2 * u]);
-        split3(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
-        wn[st][u] = wv;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        a_hi[st][j] = (short)h3[j];
-        a_mid[st][j] = (short)m3[j];
-        a_lo[st][j] = (short)l3[j];
-      }
+      const uint4 vh = op[(4 * st + 0) * 64], vm = op[(4 * st + 1) * 64];
+      const uint4 vl = op[(4 * st + 2) * 64], vw = op[(4 * st + 3) * 64];
+      __builtin_memcpy(&a_hi[st], &vh, 16);
+      __builtin_memcpy(&a_mid[st], &vm, 16);
+      __builtin_memcpy(&a_lo[st], &vl, 16);
+      wn[st][0] = __uint_as_float(vw.x);
+      wn[st][1] = __uint_as_float(vw.y);
+      wn[st][2] = __uint_as_float(vw.z);
+      wn[st][3] = __uint_as_float(vw.w);
     }
   }
 
-  // Stream the chunk: wave w takes blocks of 16 keys w, w+4, ...
+  // Stream the chunk: wave w takes blocks of 16 keys w, w+4, ...  A ring of
+  // kPrefetch register buffers keeps that many blocks in flight per wave.
   const int nkeys = ck.nkeys;
   const int nblk = (nkeys + 15) >> 4;
   const uint4* kbase = reinterpret_cast<const uint4*>(k + ck.row0 * D);
@@ -181,92 +175,92 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int Hq,
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
   };
-  uint4 cur[STEPS], nxt[STEPS];
-  int b = wave;
-  if (b < nblk) load_block(b, cur);
-  for (; b < nblk; b += kFusedWaves) {
-    const int bn = b + kFusedWaves;
-    if (bn < nblk) load_block(bn, nxt);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
+  uint4 ring[kPrefetch][STEPS];
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      bf16x8_t bk;
-      __builtin_memcpy(&bk, &cur[st], 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[st], bk, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[st], bk, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[st], bk, acc, 0, 0, 0);
-      const uint32_t wd[4] = {cur[st].x, cur[st].y, cur[st].z, cur[st].w};
+  for (int j = 0; j < kPrefetch; ++j) {
+    const int b = wave + kFusedWaves * j;
+    if (b < nblk) load_block(b, ring[j]);
+  }
+  for (int base = wave; base < nblk; base += kFusedWaves * kPrefetch) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x = bf16_lo_m(wd[u]), y = bf16_hi_m(wd[u]);
-        const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc, 0, 0, 0);
+    for (int j = 0; j < kPrefetch; ++j) {
+      const int b = base + kFusedWaves * j;
+      if (b < nblk) {
+        f32x4_t acc_t = {0.f, 0.f, 0.f, 0.f}, acc_n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+          bf16x8_t bk;
+          __builtin_memcpy(&bk, &ring[j][st], 16);
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[st], bk, acc_t, 0, 0, 0);
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[st], bk, acc_t, 0, 0, 0);
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[st], bk, acc_t, 0, 0, 0);
+          const uint32_t wd[4] = {ring[j][st].x, ring[j][st].y, ring[j][st].z, ring[j][st].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float x = bf16_lo_m(wd[u]), y = bf16_hi_m(wd[u]);
+            const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+            acc_n = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc_n, 0, 0, 0);
+          }
+        }
+        const int bn = b + kFusedWaves * kPrefetch;
+        if (bn < nblk) load_block(bn, ring[j]);
+        // D layout: lane holds heads 4q..4q+3 of key b*16 + m
+        const bool valid = b * 16 + m < nkeys;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 4 * q + i;
+          const float v = acc_t[i] + acc_n[i];
+          if (h < G) raw[h * kRawStride + b * 16 + m] = v;
+          const double dv = valid ? (double)v : 0.0;
+          s1[i] += dv;
+          s2[i] = fma(dv, dv, s2[i]);
+        }
       }
     }
-    // D layout: lane holds heads 4q..4q+3 of key b*16 + m
+  }
+  // Sum over the 16 keys of each lane group, then over the waves.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      s1[i] += __shfl_xor(s1[i], o, 64);
+      s2[i] += __shfl_xor(s2[i], o, 64);
+    }
+  }
+  if (m == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * q + i;
-      if (h < G) raw[h * kRawStride + b * 16 + m] = acc[i];
+      sh.red1[wave][4 * q + i] = s1[i];
+      sh.red2[wave][4 * q + i] = s2[i];
     }
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) cur[st] = nxt[st];
   }
 }
 
-// Per-head (count, mean, M2) of the chunk in fp64; publish them; the last
-// chunk of the unit to arrive merges all chunks and publishes (mu, sigma).
-__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, const float* raw,
-                                              Shared& sh, double* __restrict__ chunk_stats,
+// Publish the chunk's per-head (count, mean, M2) (fp64; M2 = sum x^2 -
+// (sum x)^2 / n, whose cancellation costs a few digits of fp64 only); the
+// last chunk of the unit to arrive merges all chunks and publishes
+// (mu, sigma).  Call after a barrier that follows chunk_raw.
+__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, Shared& sh,
+                                              double* __restrict__ chunk_stats,
                                               double* __restrict__ unit_stats,
                                               uint32_t* __restrict__ unit_ctrl) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nkeys = ck.nkeys;
-  double acc_h[kMaxGroup];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) acc_h[h] = 0.0;
-  for (int i = tid; i < nkeys; i += kFusedThreads) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) acc_h[h] += (double)raw[h * kRawStride + i];
-  }
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-    if (h < G) {
-      const double v = wave_sum_f(acc_h[h]);
-      if (lane == 0) sh.red[wave][h] = v;
-    }
-  __syncthreads();
-  if (tid < G)
-    sh.mean[tid] = (sh.red[0][tid] + sh.red[1][tid] + sh.red[2][tid] + sh.red[3][tid]) /
-                   (double)nkeys;
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) acc_h[h] = 0.0;
-  for (int i = tid; i < nkeys; i += kFusedThreads) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) {
-        const double dv = (double)raw[h * kRawStride + i] - sh.mean[h];
-        acc_h[h] += dv * dv;
-      }
-  }
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-    if (h < G) {
-      const double v = wave_sum_f(acc_h[h]);
-      if (lane == 0) sh.red[wave][h] = v;
-    }
-  __syncthreads();
-
+  const int tid = threadIdx.x;
   uint32_t* arrive = unit_ctrl + ck.unit * kUnitCtrlStride;
   uint32_t* ready = arrive + kUnitCtrlStride / 2;
   if (tid == 0) {
     double* cs = chunk_stats + (int64_t)ck.t * kMaxGroup * 3;
+    const double n = (double)ck.nkeys;
     for (int h = 0; h < G; ++h) {
-      st_agent(cs + 3 * h, (double)nkeys);
-      st_agent(cs + 3 * h + 1, sh.mean[h]);
-      st_agent(cs + 3 * h + 2, sh.red[0][h] + sh.red[1][h] + sh.red[2][h] + sh.red[3][h]);
+      double a = 0.0, b2 = 0.0;
+      for (int w = 0; w < kFusedWaves; ++w) {
+        a += sh.red1[w][h];
+        b2 += sh.red2[w][h];
+      }
+      const double mean = a / n;
+      st_agent(cs + 3 * h, n);
+      st_agent(cs + 3 * h + 1, mean);
+      st_agent(cs + 3 * h + 2, fmax(b2 - a * mean, 0.0));
     }
     drain_memory_ops();
     const uint32_t before =
@@ -351,16 +345,14 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, const flo
 template <int STEPS>
 __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int total_tickets,
-    const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
-    const uint16_t* __restrict__ k, double* __restrict__ chunk_stats,
-    double* __restrict__ unit_stats, uint32_t* __restrict__ ctrl, float* __restrict__ scores,
-    float* __restrict__ raw_out, double* __restrict__ head_stats) {
+    const uint4* __restrict__ apack, const uint16_t* __restrict__ k,
+    double* __restrict__ chunk_stats, double* __restrict__ unit_stats, uint32_t* __restrict__ ctrl,
+    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats) {
   extern __shared__ float raw_s[];  // 2 buffers of [G][kRawStride]
   __shared__ Shared sh;
   uint32_t* ticket_ctr = ctrl;
   uint32_t* err_flag = ctrl + 1;
   uint32_t* unit_ctrl = ctrl + kCtrlHeader;
-  const int Hq = Hkv * G;
 
   Chunk prev;
   bool have_prev = false;
@@ -378,9 +370,9 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     Chunk ck;
     if (have) {
       ck = decode_chunk(seqs, S, L, Hkv, t);
-      chunk_raw<STEPS>(ck, G, Hq, P, W, E, k, buf_cur);
+      chunk_raw<STEPS>(ck, G, apack, k, buf_cur, sh);
       __syncthreads();
-      chunk_publish(ck, G, buf_cur, sh, chunk_stats, unit_stats, unit_ctrl);
+      chunk_publish(ck, G, sh, chunk_stats, unit_stats, unit_ctrl);
       __syncthreads();
     }
     if (have_prev) {
@@ -395,12 +387,69 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   }
 }
 
+// MFMA operand pack of every unit (s, l, g): thread (unit, st, lane) forms
+// A_f = P[l][h][f] * E[s][f] (fp64) for the lane's head h = g*G + lane%16
+// and its four bands of step st, splits Re/Im into bf16 hi/mid/lo and
+// stores them with the fp32 norm weights W[l][h][f] (zeros for lanes
+// beyond G).
+template <int STEPS>
+__global__ __launch_bounds__(256) void pack_operands_kernel(
+    int S, int L, int Hkv, int G, const double2* __restrict__ P, const float* __restrict__ W,
+    const double2* __restrict__ E, uint4* __restrict__ apack) {
+  constexpr int F = STEPS * 16;
+  const int64_t units = (int64_t)S * L * Hkv;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= units * STEPS * 64) return;
+  const int lane = (int)(idx & 63);
+  const int st = (int)((idx >> 6) % STEPS);
+  const int64_t unit = idx / (64 * STEPS);
+  const int lg = (int)(unit % ((int64_t)L * Hkv));
+  const int s = (int)(unit / ((int64_t)L * Hkv));
+  const int l = lg / Hkv, g = lg % Hkv;
+  const int m = lane & 15, q = lane >> 4;
+  const int Hq = Hkv * G;
+  uint32_t h3[8], m3[8], l3[8];
+  float wv[4];
+  const bool live = m < G;
+  const int64_t pbase = ((int64_t)l * Hq + g * G + (live ? m : 0)) * F;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int f = 4 * (4 * st + q) + u;
+    double re = 0.0, im = 0.0;
+    wv[u] = 0.f;
+    if (live) {
+      const double2 pv = P[pbase + f];
+      const double2 ev = E[(int64_t)s * F + f];
+      re = pv.x * ev.x - pv.y * ev.y;
+      im = pv.x * ev.y + pv.y * ev.x;
+      wv[u] = W[pbase + f];
+    }
+    split3(re, h3[2 * u], m3[2 * u], l3[2 * u]);
+    split3(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+  }
+  auto pack8 = [](const uint32_t (&v)[8]) {
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                      v[6] | (v[7] << 16));
+  };
+  uint4* op = apack + unit * (4 * STEPS) * 64 + lane;
+  op[(4 * st + 0) * 64] = pack8(h3);
+  op[(4 * st + 1) * 64] = pack8(m3);
+  op[(4 * st + 2) * 64] = pack8(l3);
+  op[(4 * st + 3) * 64] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
+                                     __float_as_uint(wv[2]), __float_as_uint(wv[3]));
+}
+
 template <int STEPS>
 static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
                                  const double2* P, const float* W, const double2* E,
-                                 const uint16_t* k, double* cs, double* us, uint32_t* ctrl,
-                                 float* scores, float* raw, double* hs) {
+                                 uint4* apack, const uint16_t* k, double* cs, double* us,
+                                 uint32_t* ctrl, float* scores, float* raw, double* hs) {
+  const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
+  hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
+                     dim3(256), 0, st, S, L, Hkv, G, P, W, E, apack);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS>);
   // Two 16-head buffers need more than 64 KB of LDS: raise the limit once.
   static const hipError_t attr = hipFuncSetAttribute(
@@ -408,7 +457,7 @@ static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
       2 * kMaxGroup * kRawStride * (int)sizeof(float));
   if (attr != hipSuccess) return attr;
   int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds);
@@ -417,23 +466,28 @@ static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
   int grid = cus * per_cu;
   if (grid > total_tickets) grid = total_tickets;
   hipLaunchKernelGGL(score_fused_kernel<STEPS>, dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
-                     L, Hkv, G, total_tickets, P, W, E, k, cs, us, ctrl, scores, raw, hs);
+                     L, Hkv, G, total_tickets, apack, k, cs, us, ctrl, scores, raw, hs);
   return hipGetLastError();
 }
 
 bool fused_supported(int d) { return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim; }
 
+size_t fused_operand_bytes(int d, int64_t units) {
+  return fused_supported(d) ? (size_t)units * (4 * (d / 32)) * 64 * sizeof(uint4) : 0;
+}
+
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                               int total_tickets, const double2* P, const float* W,
-                              const double2* E, const uint16_t* k, double* chunk_stats,
-                              double* unit_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, hipStream_t st) {
+                              const double2* E, void* apack, const uint16_t* k,
+                              double* chunk_stats, double* unit_stats, uint32_t* ctrl,
+                              float* scores, float* raw, double* head_stats, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)G * kRawStride * sizeof(float);
+  uint4* ap = reinterpret_cast<uint4*>(apack);
   switch (d / 32) {
-#define TRI_CASE(n)                                                                  \
-  case n:                                                                            \
-    return launch_fused_t<n>(total_tickets, lds, st, seqs, S, L, Hkv, G, P, W, E, k, \
+#define TRI_CASE(n)                                                                      \
+  case n:                                                                                \
+    return launch_fused_t<n>(total_tickets, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, k, \
                              chunk_stats, unit_stats, ctrl, scores, raw, head_stats);
     TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7) TRI_CASE(8)
 #undef TRI_CASE

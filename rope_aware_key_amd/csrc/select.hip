@@ -25,7 +25,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+__global__ __launch_bounds__(kSelThreads) void select_global_kernel(
     const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
     int32_t* __restrict__ kept) {
   __shared__ uint32_t hist[kSelWaves][256];
@@ -128,51 +128,229 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
-hipError_t launch_select(const SeqInfo* seqs, int S, int LH, const float* scores,
-                         int32_t* kept_idx, hipStream_t st) {
-  const int64_t units = (int64_t)S * LH;
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, st, seqs, LH,
+// ---------------------------------------------------------------------------
+// LDS-staged select: the unit's order keys are loaded once (coalesced) into
+// LDS; the radix passes and the ordered scan then run on LDS.  Digits are
+// 12, 12 and 8 bits wide: z-scores crowd a few exponent values, and 12-bit
+// first digits (sign, exponent, 3 mantissa bits) spread them over enough
+// bins that LDS atomics rarely collide.  NT threads per unit: 1024 for long
+// units, 256 so that many short units share a CU.
+// ---------------------------------------------------------------------------
+constexpr int kHistBins = 4096;
+constexpr int kScanItems = 8;  // consecutive keys per thread in the ordered scan
+
+// Exclusive prefix sum over a block of NT threads; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = wsum[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_lds_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
+    int32_t* __restrict__ kept) {
+  constexpr int NW = NT / 64;
+  constexpr int BPT = kHistBins / NT;  // histogram bins per thread
+  extern __shared__ uint32_t keys_s[];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t wsum[NW];
+
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int s = unit / LH, lg = unit % LH;
+  const SeqInfo si = seqs[s];
+  const int n = si.n, b = si.b;
+  if (b <= 0) return;
+  const float* in = scores + si.row_base + (int64_t)lg * n;
+  int32_t* out = kept + si.out_base + (int64_t)lg * b;
+  if (b >= n) {
+    for (int i = tid; i < n; i += NT) out[i] = i;
+    return;
+  }
+#pragma unroll 8
+  for (int i = tid; i < n; i += NT) keys_s[i] = order_key(in[i]);
+  __syncthreads();
+
+  uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)b;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const uint32_t dmask = pass == 2 ? 0xffu : 0xfffu;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = keys_s[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // Thread t owns bins [t*BPT, (t+1)*BPT); find the bin holding rank kk
+    // counted from the top.
+    uint32_t c[BPT], mine = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[tid * BPT + j];
+      mine += c[j];
+    }
+    uint32_t all = 0;
+    const uint32_t below = block_excl_scan<NT>(mine, wsum, &all);
+    uint32_t above = all - below - mine;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (above < kk && kk <= above + c[j]) {
+        sel[0] = (uint32_t)(tid * BPT + j);
+        sel[1] = above;
+      }
+      above += c[j];
+    }
+    __syncthreads();
+    kk -= sel[1];
+    prefix |= sel[0] << shift;
+    mask |= dmask << shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix, quota = kk;
+
+  // Ordered emission: each thread owns kScanItems consecutive keys of a tile.
+  uint32_t base_out = 0, base_eq = 0;
+  constexpr int kTile = NT * kScanItems;
+  for (int tile = 0; tile < n && base_out < (uint32_t)b; tile += kTile) {
+    const int i0 = tile + tid * kScanItems;
+    uint32_t kv[kScanItems];
+    uint32_t neq = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      kv[j] = (i0 + j < n) ? keys_s[i0 + j] : 0u;
+      neq += (i0 + j < n && kv[j] == T) ? 1u : 0u;
+    }
+    uint32_t eq_tile = 0;
+    const uint32_t eq_before = base_eq + block_excl_scan<NT>(neq, wsum, &eq_tile);
+    uint32_t nkeep = 0;
+    uint32_t e = eq_before;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const bool valid = i0 + j < n;
+      const bool gt = valid && kv[j] > T;
+      const bool eq = valid && kv[j] == T;
+      nkeep += (gt || (eq && e < quota)) ? 1u : 0u;
+      e += eq ? 1u : 0u;
+    }
+    uint32_t keep_tile = 0;
+    uint32_t pos = base_out + block_excl_scan<NT>(nkeep, wsum, &keep_tile);
+    e = eq_before;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const bool valid = i0 + j < n;
+      const bool gt = valid && kv[j] > T;
+      const bool eq = valid && kv[j] == T;
+      if (gt || (eq && e < quota)) {
+        if (pos < (uint32_t)b) out[pos] = i0 + j;
+        ++pos;
+      }
+      e += eq ? 1u : 0u;
+    }
+    base_out += keep_tile;
+    base_eq += eq_tile;
+  }
+}
+
+// Longest unit whose keys the LDS-staged select holds (140 KB of keys next
+// to the 16 KB histogram).
+constexpr int kSelLdsMaxKeys = 35840;
+constexpr int kSelSmallUnit = 4096;  // up to here 256 threads per unit
+
+template <int NT>
+static hipError_t launch_select_lds(int64_t units, int max_n, hipStream_t st, const SeqInfo* seqs,
+                                    int LH, const float* scores, int32_t* kept_idx) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&select_lds_kernel<NT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMaxKeys * (int)sizeof(uint32_t));
+  if (attr != hipSuccess) return attr;
+  const size_t lds = (size_t)(max_n > 0 ? max_n : 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL(select_lds_kernel<NT>, dim3((unsigned)units), dim3(NT), lds, st, seqs, LH,
                      scores, kept_idx);
   return hipGetLastError();
 }
 
-// Gather kept rows.  One group of d/8 lanes copies one 16-byte slice each of
-// a K row and a V row; the first lane of the group copies the position.
-__global__ __launch_bounds__(256) void compact_kernel(
-    const SeqInfo* __restrict__ seqs, int S, int LH, int d, int64_t total_out,
-    const int32_t* __restrict__ kept, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ k_pos,
-    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, int32_t* __restrict__ pos_out) {
-  const int lpr = d >> 3;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r = gid / lpr;
-  const int part = (int)(gid - r * lpr);
-  if (r >= total_out) return;
-  const int s = find_seq_by_out_row(seqs, S, r);
-  const SeqInfo si = seqs[s];
-  const int64_t local = r - si.out_base;
-  const int64_t lg = local / si.b;
-  const int32_t idx = kept[r];
-  if ((uint32_t)idx >= (uint32_t)si.n) return;  // never read outside the unit
-  const int64_t src = si.row_base + lg * si.n + idx;
-  if (k_out)
-    reinterpret_cast<uint4*>(k_out + r * d)[part] = reinterpret_cast<const uint4*>(k + src * d)[part];
-  if (v_out)
-    reinterpret_cast<uint4*>(v_out + r * d)[part] = reinterpret_cast<const uint4*>(v + src * d)[part];
-  if (pos_out && part == 0) pos_out[r] = k_pos[src];
+hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
+                         int32_t* kept_idx, hipStream_t st) {
+  const int64_t units = (int64_t)S * LH;
+  if (units == 0) return hipSuccess;
+  if (max_n <= kSelSmallUnit)
+    return launch_select_lds<256>(units, max_n, st, seqs, LH, scores, kept_idx);
+  if (max_n <= kSelLdsMaxKeys)
+    return launch_select_lds<1024>(units, max_n, st, seqs, LH, scores, kept_idx);
+  hipLaunchKernelGGL(select_global_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, st, seqs,
+                     LH, scores, kept_idx);
+  return hipGetLastError();
 }
 
-hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int64_t total_out,
+// Gather kept rows.  Work-group (unit, tile) copies kCompactRows output rows;
+// a group of d/8 lanes moves one row (16 bytes per lane) of K and of V, the
+// first lane of the group the position.
+constexpr int kCompactRows = 64;
+
+__global__ __launch_bounds__(256) void compact_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, int d, const int32_t* __restrict__ kept,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ k_pos, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
+    int32_t* __restrict__ pos_out) {
+  const int unit = blockIdx.x;
+  const int s = unit / LH, lg = unit % LH;
+  const SeqInfo si = seqs[s];
+  const int b = si.b;
+  const int r0 = blockIdx.y * kCompactRows;
+  if (r0 >= b) return;
+  const int r1 = min(b, r0 + kCompactRows);
+  const int lpr = d >> 3;
+  const int rows_per_pass = 256 / lpr;
+  const int tid = threadIdx.x;
+  const int sub = tid / lpr, part = tid - sub * lpr;
+  if (sub >= rows_per_pass) return;
+  const int64_t out0 = si.out_base + (int64_t)lg * b;
+  const int64_t in0 = si.row_base + (int64_t)lg * si.n;
+#pragma unroll 4
+  for (int r = r0 + sub; r < r1; r += rows_per_pass) {
+    const int32_t idx = kept[out0 + r];
+    if ((uint32_t)idx >= (uint32_t)si.n) continue;  // never read outside the unit
+    const int64_t src = in0 + idx, dst = out0 + r;
+    if (k_out)
+      reinterpret_cast<uint4*>(k_out + dst * d)[part] = reinterpret_cast<const uint4*>(k + src * d)[part];
+    if (v_out)
+      reinterpret_cast<uint4*>(v_out + dst * d)[part] = reinterpret_cast<const uint4*>(v + src * d)[part];
+    if (pos_out && part == 0) pos_out[dst] = k_pos[src];
+  }
+}
+
+hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,
                           const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
                           int32_t* pos_out, hipStream_t st) {
-  (void)LH;
-  if (total_out == 0) return hipSuccess;
-  const int64_t threads = total_out * (d >> 3);
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, st, seqs, S, LH, d,
-                     total_out, kept_idx, k, v, k_pos, k_out, v_out, pos_out);
+  const int64_t units = (int64_t)S * LH;
+  if (units == 0 || max_b <= 0) return hipSuccess;
+  const dim3 grid((unsigned)units, (unsigned)((max_b + kCompactRows - 1) / kCompactRows));
+  hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, seqs, LH, d, kept_idx, k, v, k_pos,
+                     k_out, v_out, pos_out);
   return hipGetLastError();
 }
 

@@ -64,14 +64,16 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
                            hipStream_t st);
 
 bool fused_supported(int d);
+// Workspace bytes of the fused path's packed MFMA operands.
+size_t fused_operand_bytes(int d, int64_t units);
 
 // Fused MFMA score path (head_dim % 32 == 0); ctrl as above, zeroed by the
 // prologue.  unit_stats: [units][kMaxGroup][2] (mu, sigma).
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                               int total_tickets, const double2* P, const float* W,
-                              const double2* E, const uint16_t* k, double* chunk_stats,
-                              double* unit_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, hipStream_t st);
+                              const double2* E, void* apack, const uint16_t* k,
+                              double* chunk_stats, double* unit_stats, uint32_t* ctrl,
+                              float* scores, float* raw, double* head_stats, hipStream_t st);
 
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W,
@@ -79,10 +81,10 @@ hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d
                         double* chunk_stats, float* scores, double* head_stats,
                         hipStream_t st);
 
-hipError_t launch_select(const SeqInfo* seqs, int S, int LH, const float* scores,
+hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
                          int32_t* kept_idx, hipStream_t st);
 
-hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int64_t total_out,
+hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,
                           const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
                           int32_t* pos_out, hipStream_t st);
