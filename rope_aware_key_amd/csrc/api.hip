@@ -116,9 +116,10 @@ struct Plan {
   int max_n = 0, max_b = 0;
   int64_t tickets = 0;
   // workspace offsets (bytes)
-  size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ustats = 0,
-         off_ctrl = 0, off_apack = 0, off_raw = 0;
-  int64_t n_units = 0;
+  size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ctrl = 0,
+         off_apack = 0, off_raw = 0;
+  int64_t n_units = 0, n_stat_slots = 0;
+  int chunk = 0;  // keys per score ticket
   bool fused = false;
   size_t score_bytes = 0, select_bytes = 0;
 };
@@ -142,6 +143,8 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.seqs.resize(S);
   if (S > 0 && cu_len[0] < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len[0] must be >= 0");
   int64_t out_acc = 0, ticket_acc = 0;
+  p.fused = tri::fused_supported(p.d);
+  p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
   for (int s = 0; s < S; ++s) {
     const int64_t n = cu_len[s + 1] - cu_len[s];
     if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");
@@ -161,7 +164,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     out_acc += b;
     si.p_q = cur_pos ? cur_pos[s] : 0;
     si.chunk_base = (int32_t)ticket_acc;
-    ticket_acc += LH * ((n + tri::kScoreChunk - 1) / tri::kScoreChunk);
+    ticket_acc += LH * ((n + p.chunk - 1) / p.chunk);
     if (ticket_acc > 0x7fffffff) return fail(TRI_ERR_UNSUPPORTED, "batch too large for one call");
   }
   p.total_rows = S > 0 ? LH * cu_len[S] : 0;
@@ -179,13 +182,13 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.off_P = take((size_t)p.L * p.Hq * p.F * sizeof(double2));
   p.off_W = take((size_t)p.L * p.Hq * p.F * sizeof(float));
   p.off_E = take((size_t)S * p.F * sizeof(double2));
+  // generic path: (count, mean, M2) per ticket and head; fused path: (sum,
+  // sum of squares) per ticket and head, reset to a sentinel per call
+  p.n_stat_slots = p.fused ? p.tickets * p.G * 2 : 0;
   p.off_stats = take((size_t)p.tickets * tri::kMaxGroup * 3 * sizeof(double));
   p.n_units = (int64_t)S * LH;
-  p.off_ustats = take((size_t)p.n_units * tri::kMaxGroup * 2 * sizeof(double));
-  p.off_ctrl = take(((size_t)tri::kCtrlHeader + (size_t)p.n_units * tri::kUnitCtrlStride) *
-                    sizeof(uint32_t));
+  p.off_ctrl = take((size_t)tri::kCtrlHeader * sizeof(uint32_t));
   // The fused path keeps raw scores on chip; the generic path spills them.
-  p.fused = tri::fused_supported(p.d);
   p.off_apack = take(tri::fused_operand_bytes(p.d, p.n_units));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
@@ -258,13 +261,13 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   if (e == hipSuccess)
     e = tri::launch_prologue(p.L, p.Hq, p.d, shape->rope_theta, p.S, dseq, q_centre, q_absmean,
                              q_R, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
-                             (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl), p.n_units, s);
+                             (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl), (double*)(ws + p.off_stats),
+                             p.n_stat_slots, s);
   if (e == hipSuccess && p.fused)
-    e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
+    e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                 (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                                 (const double2*)(ws + p.off_E), ws + p.off_apack, k,
-                                (double*)(ws + p.off_stats),
-                                (double*)(ws + p.off_ustats), (uint32_t*)(ws + p.off_ctrl),
+                                (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
                                 scores, raw_scores, head_stats, s);
   else if (e == hipSuccess)
     e = tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,

@@ -76,17 +76,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     int L, int Hq, int d, double theta, int S, const SeqInfo* __restrict__ seqs,
     const float* __restrict__ q_centre, const float* __restrict__ q_absmean,
     const float* __restrict__ q_R, double2* __restrict__ P, float* __restrict__ W,
-    double2* __restrict__ E, uint32_t* __restrict__ ctrl, int64_t n_units) {
+    double2* __restrict__ E, uint32_t* __restrict__ ctrl, double* __restrict__ stat_slots,
+    int64_t n_stat_slots) {
   const int F = d >> 1;
   const int64_t n_stat = (int64_t)L * Hq * F;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // score control block: header words, then each unit's arrival counter and
-  // ready flag
+  // score control block and published-statistics slots of this call
   if (idx < kCtrlHeader) ctrl[idx] = 0u;
-  if (idx < n_units) {
-    ctrl[kCtrlHeader + idx * kUnitCtrlStride] = 0u;
-    ctrl[kCtrlHeader + idx * kUnitCtrlStride + kUnitCtrlStride / 2] = 0u;
-  }
+  if (idx < n_stat_slots)
+    reinterpret_cast<unsigned long long*>(stat_slots)[idx] = kStatSentinel;
   if (idx < n_stat) {
     const int f = (int)(idx % F);
     const double omega = pow(theta, -2.0 * (double)f / (double)d);
@@ -115,14 +113,14 @@ __global__ __launch_bounds__(256) void prologue_kernel(
 
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqInfo* seqs,
                            const float* q_centre, const float* q_absmean, const float* q_R,
-                           double2* P, float* W, double2* E, uint32_t* ctrl, int64_t n_units,
-                           hipStream_t st) {
+                           double2* P, float* W, double2* E, uint32_t* ctrl, double* stat_slots,
+                           int64_t n_stat_slots, hipStream_t st) {
   int64_t total = (int64_t)L * Hq * (d / 2) + (int64_t)S * (d / 2);
-  if (n_units > total) total = n_units;
+  if (n_stat_slots > total) total = n_stat_slots;
   if (kCtrlHeader > total) total = kCtrlHeader;
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, st, L, Hq, d, theta, S,
-                     seqs, q_centre, q_absmean, q_R, P, W, E, ctrl, n_units);
+                     seqs, q_centre, q_absmean, q_R, P, W, E, ctrl, stat_slots, n_stat_slots);
   return hipGetLastError();
 }
 

@@ -14,33 +14,35 @@
 //    are bf16 already; the fp64 coefficient a_h is split into three bf16
 //    terms (hi + mid + lo, ~25 significant bits), so three MFMAs per 32-wide
 //    step reproduce an fp32-accurate dot product with exact bf16 x bf16
-//    products and fp32 accumulation.
+//    products and fp32 accumulation.  The split operands of every unit are
+//    packed once per call, in MFMA lane order, by pack_operands_kernel.
 //  * The norm term sum_f w_f |k_f| uses v_mfma_f32_16x16x4_f32 on the fp32
 //    magnitudes (computed once per key band on the VALU, shared by all G
 //    heads).
 //  * Each lane loads 16 bytes of one key per step (4 lanes cover 64
 //    contiguous bytes of a row); the 4 waves of a work-group take
 //    interleaved blocks so the group streams one contiguous span of K.
-//  * Work is cut into "tickets": one chunk of kScoreChunk keys of one unit.
-//    The kernel is persistent: each work-group claims tickets in order from
-//    an atomic counter and keeps two chunks' raw per-head scores in LDS.  It
-//    computes chunk i, publishes its per-head (count, mean, M2) in fp64, then
-//    computes chunk i+1 before it finalizes chunk i, so the wait for the
-//    rest of chunk i's unit overlaps useful streaming.  The last chunk of a
-//    unit to publish merges the unit's chunks in chunk order (Chan's update)
-//    and publishes (mu, sigma) per head; everyone reads those, so every
-//    chunk z-scores with identical numbers (deterministic; equal keys score
-//    equally).
-//  * Waits cannot deadlock: tickets are claimed in order and a work-group
-//    claims its next ticket (and publishes it) before it waits on its
-//    previous one, so a unit's missing chunks are always claimable while the
-//    resident work-groups outnumber the chunks of one unit (a few hundred
-//    resident groups against at most 2^31 / kScoreChunk chunks of a unit
-//    that fits in one call).  A spin bound turns a broken invariant into an
-//    error flag instead of a hang.
-//  * Cross-work-group data (chunk statistics, unit statistics, flags) move
-//    through agent-scope atomics, which are coherent across the XCDs' L2
-//    caches; an s_waitcnt orders the data stores before the flag update.
+//  * Work is cut into "tickets": one chunk of `ch` keys of one unit, with ch
+//    chosen per call so that three work-groups fit in a CU's LDS.  The
+//    kernel is persistent: each work-group claims tickets in order from an
+//    atomic counter and keeps two chunks' raw per-head scores in LDS.  It
+//    streams chunk i, publishes the chunk's per-head fp64 sum and sum of
+//    squares, streams chunk i+1, and only then finalizes chunk i, so the
+//    wait for the rest of chunk i's unit overlaps useful streaming.
+//  * Publishing needs no flag and no ordering wait: every published slot
+//    holds a sentinel NaN (set by the prologue) until its value lands, and
+//    values are written once with coherent (agent-scope) stores.  A
+//    finalizing work-group reads all chunk slots of its unit (re-reading any
+//    that still hold the sentinel), sums them in chunk order and derives
+//    (mu, sigma); every chunk of the unit does the same arithmetic on the
+//    same numbers, so results are deterministic and equal keys score
+//    equally.
+//  * Waits cannot deadlock: tickets are claimed in order, and a work-group
+//    publishes each ticket it claims before it waits on an earlier one, so
+//    the chunks a waiter needs are claimed by running work-groups that will
+//    publish them without waiting, as long as the resident work-groups
+//    outnumber the chunks of one unit.  A spin bound turns a broken
+//    invariant into an error flag instead of a hang.
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -68,9 +70,12 @@ __device__ __forceinline__ void split3(double x, uint32_t& hi, uint32_t& mid, ui
 
 constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / 64;
-constexpr int kRawStride = kScoreChunk + 4;  // LDS row stride (floats) per head
+constexpr int kRawPad = 4;  // LDS row stride (floats) per head = ch + kRawPad
 constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr int kPrefetch = 4;  // blocks of 16 keys in flight per wave
+constexpr int kPrefetch = 2;  // blocks of 16 keys in flight per wave
+constexpr int kStatGroups = kFusedThreads / kMaxGroup;  // finalize reduction fan-in
+constexpr int kFusedLdsPerCu = 160 * 1024;
+constexpr int kFusedMaxLds = 96 * 1024;  // dynamic LDS ceiling of one work-group
 
 __device__ __forceinline__ double wave_sum_f(double v) {
 #pragma unroll
@@ -87,42 +92,40 @@ __device__ __forceinline__ void st_agent(double* p, double v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t ld_agent_u64(const double* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until this wave's earlier memory operations have completed, so that
-// data stored before a flag update is visible before the flag.
-__device__ __forceinline__ void drain_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
 
 struct Chunk {
   int t, s, lg, l, g, c, nch, nkeys;
   int64_t row0, unit;
 };
 
-__device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L, int Hkv, int t) {
+__device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L, int Hkv, int ch,
+                                              int t) {
   Chunk ck;
   ck.t = t;
   ck.s = find_seq_by_ticket(seqs, S, t);
   const SeqInfo si = seqs[ck.s];
-  ck.nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+  ck.nch = (si.n + ch - 1) / ch;
   const int local = t - si.chunk_base;
   ck.lg = local / ck.nch;
   ck.c = local % ck.nch;
   ck.l = ck.lg / Hkv;
   ck.g = ck.lg % Hkv;
-  const int key0 = ck.c * kScoreChunk;
-  ck.nkeys = min(kScoreChunk, si.n - key0);
+  const int key0 = ck.c * ch;
+  ck.nkeys = min(ch, si.n - key0);
   ck.row0 = si.row_base + (int64_t)ck.lg * si.n + key0;
   ck.unit = (int64_t)ck.s * L * Hkv + ck.lg;
   return ck;
 }
 
 struct Shared {
-  double red1[kFusedWaves][kMaxGroup];
-  double red2[kFusedWaves][kMaxGroup];
+  double red1[kStatGroups][kMaxGroup];
+  double red2[kStatGroups][kMaxGroup];
   float zmul[kMaxGroup], zadd[kMaxGroup];
   int ticket;
-  int last;
 };
 
 // MFMA operands of one unit, packed by pack_operands_kernel in lane order:
@@ -137,7 +140,8 @@ __device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ 
 // Raw scores of one chunk into raw (LDS, [G][kRawStride]); per-head
 // sum and sum of squares of the chunk's raw scores in fp64 into sh.s1/s2.
 template <int STEPS>
-__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, const uint4* __restrict__ apack,
+__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
+                                          const uint4* __restrict__ apack,
                                           const uint16_t* __restrict__ k, float* raw,
                                           Shared& sh) {
   constexpr int D = STEPS * 32;
@@ -211,7 +215,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, const uint4* _
         for (int i = 0; i < 4; ++i) {
           const int h = 4 * q + i;
           const float v = acc_t[i] + acc_n[i];
-          if (h < G) raw[h * kRawStride + b * 16 + m] = v;
+          if (h < G) raw[h * rs + b * 16 + m] = v;
           const double dv = valid ? (double)v : 0.0;
           s1[i] += dv;
           s2[i] = fma(dv, dv, s2[i]);
@@ -237,90 +241,72 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, const uint4* _
   }
 }
 
-// Publish the chunk's per-head (count, mean, M2) (fp64; M2 = sum x^2 -
-// (sum x)^2 / n, whose cancellation costs a few digits of fp64 only); the
-// last chunk of the unit to arrive merges all chunks and publishes
-// (mu, sigma).  Call after a barrier that follows chunk_raw.
+// Publish the chunk's per-head fp64 (sum, sum of squares) with coherent
+// stores; call after a barrier that follows chunk_raw.  No wait: readers
+// recognise slots not yet written by their sentinel.
 __device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, Shared& sh,
-                                              double* __restrict__ chunk_stats,
-                                              double* __restrict__ unit_stats,
-                                              uint32_t* __restrict__ unit_ctrl) {
+                                              double* __restrict__ chunk_stats) {
   const int tid = threadIdx.x;
-  uint32_t* arrive = unit_ctrl + ck.unit * kUnitCtrlStride;
-  uint32_t* ready = arrive + kUnitCtrlStride / 2;
-  if (tid == 0) {
-    double* cs = chunk_stats + (int64_t)ck.t * kMaxGroup * 3;
-    const double n = (double)ck.nkeys;
-    for (int h = 0; h < G; ++h) {
-      double a = 0.0, b2 = 0.0;
-      for (int w = 0; w < kFusedWaves; ++w) {
-        a += sh.red1[w][h];
-        b2 += sh.red2[w][h];
-      }
-      const double mean = a / n;
-      st_agent(cs + 3 * h, n);
-      st_agent(cs + 3 * h + 1, mean);
-      st_agent(cs + 3 * h + 2, fmax(b2 - a * mean, 0.0));
+  if (tid < G) {
+    double a = 0.0, b2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < kFusedWaves; ++w) {
+      a += sh.red1[w][tid];
+      b2 += sh.red2[w][tid];
     }
-    drain_memory_ops();
-    const uint32_t before =
-        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.last = before + 1 == (uint32_t)ck.nch;
-  }
-  __syncthreads();
-  if (sh.last) {
-    // Every chunk has published; merge them in chunk order.
-    if (tid < G) {
-      const int t0 = ck.t - ck.c;
-      double cnt = 0.0, mu = 0.0, m2 = 0.0;
-      for (int cc = 0; cc < ck.nch; ++cc) {
-        const double* cs = chunk_stats + ((int64_t)(t0 + cc) * kMaxGroup + tid) * 3;
-        const double nb = ld_agent(cs), mb = ld_agent(cs + 1), m2b = ld_agent(cs + 2);
-        if (cc == 0) {
-          cnt = nb; mu = mb; m2 = m2b;
-        } else {
-          const double tot = cnt + nb;
-          const double dl = mb - mu;
-          mu += dl * (nb / tot);
-          m2 += m2b + dl * dl * (cnt * nb / tot);
-          cnt = tot;
-        }
-      }
-      double* us = unit_stats + (ck.unit * kMaxGroup + tid) * 2;
-      st_agent(us, mu);
-      st_agent(us + 1, sqrt(m2 / cnt));
-      drain_memory_ops();
-    }
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    double* cs = chunk_stats + ((int64_t)ck.t * G + tid) * 2;
+    st_agent(cs, a);
+    st_agent(cs + 1, b2);
   }
 }
 
-// Wait for the unit's statistics, then z-score the chunk, take the max over
-// the group and write the scores (and the optional debug outputs).
-__device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, const float* raw,
-                                               Shared& sh, const double* __restrict__ unit_stats,
-                                               const uint32_t* __restrict__ unit_ctrl,
+// Read every chunk slot of the unit (waiting for any still holding the
+// sentinel), derive (mu, sigma) per head, z-score the chunk, take the max
+// over the group and write the scores (and the optional debug outputs).
+__device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, const float* raw,
+                                               Shared& sh, const double* __restrict__ chunk_stats,
                                                uint32_t* __restrict__ err_flag,
                                                float* __restrict__ scores,
                                                float* __restrict__ raw_out,
-                                               double* __restrict__ head_stats) {
+                                               double* __restrict__ head_stats, int unit_n) {
   const int tid = threadIdx.x;
-  const uint32_t* ready = unit_ctrl + ck.unit * kUnitCtrlStride + kUnitCtrlStride / 2;
-  if (tid == 0) {
-    uint32_t spins = 0;
-    while (ld_agent_u32(ready) == 0u) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+  const int h = tid % kMaxGroup, j = tid / kMaxGroup;  // head, reduction group
+  double a = 0.0, b2 = 0.0;
+  if (h < G) {
+    const int t0 = ck.t - ck.c;
+    for (int cc = j; cc < ck.nch; cc += kStatGroups) {
+      const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
+      uint64_t u0 = ld_agent_u64(cs), u1 = ld_agent_u64(cs + 1);
+      uint32_t spins = 0;
+      while (u0 == kStatSentinel || u1 == kStatSentinel) {
+        __builtin_amdgcn_s_sleep(2);
+        u0 = ld_agent_u64(cs);
+        u1 = ld_agent_u64(cs + 1);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
       }
+      a += __longlong_as_double((long long)u0);
+      b2 += __longlong_as_double((long long)u1);
     }
   }
+  sh.red1[j][h] = a;
+  sh.red2[j][h] = b2;
   __syncthreads();
   if (tid < G) {
-    const double* us = unit_stats + (ck.unit * kMaxGroup + tid) * 2;
-    const double mu = ld_agent(us), sigma = ld_agent(us + 1);
+    double sa = 0.0, sb = 0.0;
+#pragma unroll
+    for (int g2 = 0; g2 < kStatGroups; ++g2) {
+      sa += sh.red1[g2][tid];
+      sb += sh.red2[g2][tid];
+    }
+    // population moments over the unit's keys; fp64 keeps the cancellation
+    // in sum x^2 - n mu^2 far below the fp32 resolution of the raw scores
+    const double n = (double)unit_n;
+    const double mu = sa / n;
+    const double var = fmax(sb / n - mu * mu, 0.0);
+    const double sigma = sqrt(var);
     const double inv = sigma > 0.0 ? 1.0 / sigma : 0.0;
     sh.zmul[tid] = (float)inv;
     sh.zadd[tid] = (float)(-mu * inv);
@@ -332,29 +318,30 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, const flo
   __syncthreads();
   for (int i = tid; i < ck.nkeys; i += kFusedThreads) {
     float best = -__builtin_inff();
-    for (int h = 0; h < G; ++h)
-      best = fmaxf(best, fmaf(raw[h * kRawStride + i], sh.zmul[h], sh.zadd[h]));
+    for (int hh = 0; hh < G; ++hh)
+      best = fmaxf(best, fmaf(raw[hh * rs + i], sh.zmul[hh], sh.zadd[hh]));
     scores[ck.row0 + i] = best;
     if (raw_out)
-      for (int h = 0; h < G; ++h) raw_out[(ck.row0 + i) * G + h] = raw[h * kRawStride + i];
+      for (int hh = 0; hh < G; ++hh) raw_out[(ck.row0 + i) * G + hh] = raw[hh * rs + i];
   }
 }
 
 // STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
-// tickets.
+// tickets.  ch = keys per ticket.
 template <int STEPS>
 __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
-    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int total_tickets,
+    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
     const uint4* __restrict__ apack, const uint16_t* __restrict__ k,
-    double* __restrict__ chunk_stats, double* __restrict__ unit_stats, uint32_t* __restrict__ ctrl,
-    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats) {
-  extern __shared__ float raw_s[];  // 2 buffers of [G][kRawStride]
+    double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, float* __restrict__ scores,
+    float* __restrict__ raw_out, double* __restrict__ head_stats) {
+  extern __shared__ float raw_s[];  // 2 buffers of [G][ch + kRawPad]
   __shared__ Shared sh;
   uint32_t* ticket_ctr = ctrl;
   uint32_t* err_flag = ctrl + 1;
-  uint32_t* unit_ctrl = ctrl + kCtrlHeader;
+  const int rs = ch + kRawPad;
 
   Chunk prev;
+  int prev_n = 0;
   bool have_prev = false;
   int cur = 0;
   for (;;) {
@@ -365,23 +352,24 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const int t = sh.ticket;
     __syncthreads();
     const bool have = t < total_tickets;
-    float* buf_cur = raw_s + cur * G * kRawStride;
-    float* buf_prev = raw_s + (cur ^ 1) * G * kRawStride;
+    float* buf_cur = raw_s + cur * G * rs;
+    float* buf_prev = raw_s + (cur ^ 1) * G * rs;
     Chunk ck;
     if (have) {
-      ck = decode_chunk(seqs, S, L, Hkv, t);
-      chunk_raw<STEPS>(ck, G, apack, k, buf_cur, sh);
+      ck = decode_chunk(seqs, S, L, Hkv, ch, t);
+      chunk_raw<STEPS>(ck, G, rs, apack, k, buf_cur, sh);
       __syncthreads();
-      chunk_publish(ck, G, sh, chunk_stats, unit_stats, unit_ctrl);
+      chunk_publish(ck, G, sh, chunk_stats);
       __syncthreads();
     }
     if (have_prev) {
-      chunk_finalize(prev, G, buf_prev, sh, unit_stats, unit_ctrl, err_flag, scores, raw_out,
-                     head_stats);
+      chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, scores, raw_out,
+                     head_stats, prev_n);
       __syncthreads();
     }
     if (!have) break;
     prev = ck;
+    prev_n = seqs[ck.s].n;
     have_prev = true;
     cur ^= 1;
   }
@@ -440,21 +428,19 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
 }
 
 template <int STEPS>
-static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
+static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
                                  const double2* P, const float* W, const double2* E,
-                                 uint4* apack, const uint16_t* k, double* cs, double* us,
-                                 uint32_t* ctrl, float* scores, float* raw, double* hs) {
+                                 uint4* apack, const uint16_t* k, double* cs, uint32_t* ctrl,
+                                 float* scores, float* raw, double* hs) {
   const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
   hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
                      dim3(256), 0, st, S, L, Hkv, G, P, W, E, apack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS>);
-  // Two 16-head buffers need more than 64 KB of LDS: raise the limit once.
   static const hipError_t attr = hipFuncSetAttribute(
-      kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-      2 * kMaxGroup * kRawStride * (int)sizeof(float));
+      kern, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds);
   if (attr != hipSuccess) return attr;
   int dev = 0, cus = 0, per_cu = 0;
   e = hipGetDevice(&dev);
@@ -466,29 +452,40 @@ static hipError_t launch_fused_t(int total_tickets, size_t lds, hipStream_t st,
   int grid = cus * per_cu;
   if (grid > total_tickets) grid = total_tickets;
   hipLaunchKernelGGL(score_fused_kernel<STEPS>, dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
-                     L, Hkv, G, total_tickets, apack, k, cs, us, ctrl, scores, raw, hs);
+                     L, Hkv, G, ch, total_tickets, apack, k, cs, ctrl, scores, raw, hs);
   return hipGetLastError();
 }
 
 bool fused_supported(int d) { return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim; }
 
+// Keys per ticket: as many as let three work-groups (two raw buffers of G
+// heads each) share a CU's LDS, in multiples of 64, at most 1024.
+int fused_chunk_keys(int G) {
+  const int per_wg = kFusedLdsPerCu / 3 - 4608;  // leave room for static LDS (Shared)
+  int ch = (per_wg / (2 * G * (int)sizeof(float)) - kRawPad) / 64 * 64;
+  if (ch > 1024) ch = 1024;
+  if (ch < 64) ch = 64;
+  return ch;
+}
+
 size_t fused_operand_bytes(int d, int64_t units) {
   return fused_supported(d) ? (size_t)units * (4 * (d / 32)) * 64 * sizeof(uint4) : 0;
 }
 
-hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
+hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
-                              double* chunk_stats, double* unit_stats, uint32_t* ctrl,
-                              float* scores, float* raw, double* head_stats, hipStream_t st) {
+                              double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
+                              double* head_stats, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
-  const size_t lds = 2 * (size_t)G * kRawStride * sizeof(float);
+  const size_t lds = 2 * (size_t)G * (ch + kRawPad) * sizeof(float);
+  if (lds > (size_t)kFusedMaxLds) return hipErrorInvalidValue;
   uint4* ap = reinterpret_cast<uint4*>(apack);
   switch (d / 32) {
-#define TRI_CASE(n)                                                                      \
-  case n:                                                                                \
-    return launch_fused_t<n>(total_tickets, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, k, \
-                             chunk_stats, unit_stats, ctrl, scores, raw, head_stats);
+#define TRI_CASE(n)                                                                          \
+  case n:                                                                                    \
+    return launch_fused_t<n>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, k, \
+                             chunk_stats, ctrl, scores, raw, head_stats);
     TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7) TRI_CASE(8)
 #undef TRI_CASE
     default:

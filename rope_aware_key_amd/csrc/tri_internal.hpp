@@ -21,12 +21,12 @@ static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
 // Keys per score work-group ticket.
 constexpr int kScoreChunk = 1024;
 
-// Score control block (uint32 words): [0] ticket counter, [1] error flag,
-// then from word kCtrlHeader one kUnitCtrlStride-word slot per unit holding
-// its arrival counter (word 0) and ready flag (word kUnitCtrlStride/2), kept
-// on separate cache lines.
+// Score control block (uint32 words): [0] ticket counter, [1] error flag.
 constexpr int kCtrlHeader = 64;
-constexpr int kUnitCtrlStride = 64;
+
+// Bit pattern (a NaN no arithmetic produces) that marks a published
+// statistics slot as not yet written.
+constexpr uint64_t kStatSentinel = 0x7ff4dead0000beefull;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxHeadDim = 256;
 
@@ -60,20 +60,23 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* 
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
                            const SeqInfo* seqs, const float* q_centre,
                            const float* q_absmean, const float* q_R, double2* P,
-                           float* W, double2* E, uint32_t* ctrl, int64_t n_units,
-                           hipStream_t st);
+                           float* W, double2* E, uint32_t* ctrl, double* stat_slots,
+                           int64_t n_stat_slots, hipStream_t st);
 
 bool fused_supported(int d);
+// Keys per ticket of the fused path for a GQA group of G heads.
+int fused_chunk_keys(int G);
 // Workspace bytes of the fused path's packed MFMA operands.
 size_t fused_operand_bytes(int d, int64_t units);
 
-// Fused MFMA score path (head_dim % 32 == 0); ctrl as above, zeroed by the
-// prologue.  unit_stats: [units][kMaxGroup][2] (mu, sigma).
-hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
+// Fused MFMA score path (head_dim % 32 == 0).  ctrl as above, zeroed by the
+// prologue; chunk_stats: [tickets][G][2] fp64 (sum, sum of squares), reset
+// to kStatSentinel by the prologue.
+hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
-                              double* chunk_stats, double* unit_stats, uint32_t* ctrl,
-                              float* scores, float* raw, double* head_stats, hipStream_t st);
+                              double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
+                              double* head_stats, hipStream_t st);
 
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W,
