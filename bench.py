@@ -6,8 +6,12 @@ head_dim 128, batch 8, 32768 keys per head pruned to 2048, K and V bf16),
 inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
+  python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -19,6 +23,82 @@ if ROOT not in sys.path:
 
 METRIC = "keys scored+compacted/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_c3.json")
+KERNEL_SOURCES = ["score_mfma.hip", "calib.hip", "api.hip", "tri_internal.hpp"]
+
+
+def kernel_source_hash():
+    """Hash of the sources that define the tri_score kernels: counter
+    readings taken on other sources do not describe this build."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rope_aware_key_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per tri_score call from the committed counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_call")
+
+
+def copy_probe(reps=10):
+    """A plain device copy of COPY_PROBE_BYTES, for scaling FETCH_SIZE and
+    WRITE_SIZE (each copy reads and writes exactly that many bytes)."""
+    import torch
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "reps": reps}))
+
+
+def summarize(prof_dir, out, cmd):
+    """Turn a rocprofv3 --stats / --pmc CSV directory into a short text summary."""
+    import csv
+    lines = [f"# rocprofv3 summary: {os.path.basename(out)}", "", f"command: `{cmd}`", ""]
+    for path in sorted(glob.glob(os.path.join(prof_dir, "**", "*kernel_stats.csv"), recursive=True)):
+        lines += ["kernel stats (durations in microseconds):", "",
+                  "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
+        rows = list(csv.DictReader(open(path)))
+        ours = any(r["Name"].replace("void ", "").startswith("tri::") for r in rows)
+        for r in rows:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            if ours and not name.startswith("tri::"):
+                continue
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        lines.append("")
+    for path in sorted(glob.glob(os.path.join(prof_dir, "**", "*counter_collection.csv"), recursive=True)):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"].split("(")[0].replace("void ", ""), r["Counter_Name"])
+            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        lines += ["counters (mean per dispatch over the dispatches seen):", "",
+                  "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+        ours = any(kn.startswith("tri::") for kn, _ in per)
+        for (kname, cname), d in sorted(per.items()):
+            if ours and not kname.startswith("tri::"):
+                continue
+            vals = list(d.values())
+            lines.append(f"| {kname[:60]} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} |")
+        lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
 
 WORKLOADS = {
     # name: (config id, overrides, label)
@@ -92,7 +172,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize", default=None)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--cmd", default="")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.out, args.cmd)
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path shards over (sequence, layer, KV head) "
               "units with no exchange, so N GPUs run N independent copies of this step.",
@@ -184,8 +274,10 @@ def main():
                          "tri_select_compact": float(t_sel.mean()) * 1e3},
         "roofline": {"bound": "hbm", "kernel": "tri_score",
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": score_gbps / PEAK_HBM_GBPS, "traffic": None,
-                     "algorithmic_bytes_per_launch": b_score},
+                     "frac": score_gbps / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic() if args.workload == "c3" else None,
+                     "algorithmic_bytes_per_launch": b_score,
+                     "launch": "tri_score call: prologue + operand pack + fused score kernel"},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -49,9 +49,7 @@ namespace tri {
 
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_lo_m(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi_m(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 bits, round to nearest even (inputs are finite).
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -202,8 +200,11 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           const uint32_t wd[4] = {ring[j][st].x, ring[j][st].y, ring[j][st].z, ring[j][st].w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float x = bf16_lo_m(wd[u]), y = bf16_hi_m(wd[u]);
-            const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+            // |k_f|^2 = x^2 + y^2 straight from the packed bf16 pair (exact
+            // bf16 products, one fp32 rounding)
+            bf16x2_t pr;
+            __builtin_memcpy(&pr, &wd[u], 4);
+            const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fdot2_f32_bf16(pr, pr, 0.0f, false));
             acc_n = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc_n, 0, 0, 0);
           }
         }
