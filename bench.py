@@ -8,6 +8,8 @@ inputs resident in HBM.  Prints one JSON line.
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
   python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
   python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
+  python bench.py --traffic DIR --out FILE   # counter runs (DIR/fetch, write, copy_fetch,
+                                             # copy_write) -> HBM bytes per tri_score call
 """
 import argparse
 import glob
@@ -100,6 +102,81 @@ def summarize(prof_dir, out, cmd):
         f.write("\n".join(lines))
     print(out)
 
+TRAFFIC_RUNS = {
+    # subdirectory of --traffic: (counter, command that fills it; OUT = that subdirectory)
+    "fetch": ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- "
+                            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
+    "write": ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- "
+                            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
+    "copy_fetch": ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- "
+                                 "python3 bench.py --copy-probe"),
+    "copy_write": ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- "
+                                 "python3 bench.py --copy-probe"),
+}
+SCORE_KERNELS = ("tri::prologue_kernel", "tri::pack_operands_kernel", "tri::score_fused_kernel")
+
+
+def counter_means(run_dir, counter):
+    """Mean per dispatch (KiB) of one counter, per kernel name, over a run."""
+    import csv
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            d = per.setdefault(name, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def write_traffic(run_root, out):
+    """HBM bytes per tri_score call from the four counter runs of
+    TRAFFIC_RUNS under run_root.  FETCH_SIZE and WRITE_SIZE are scaled by
+    what they read for the copy probe, which moves exactly COPY_PROBE_BYTES
+    each way per dispatch."""
+    means = {sub: counter_means(os.path.join(run_root, sub), c) for sub, (c, _) in TRAFFIC_RUNS.items()}
+    true_kib = COPY_PROBE_BYTES / 1024.0
+    # the copy probe's copies are the dispatches with the largest reading
+    fetch_scale = true_kib / max(means["copy_fetch"].values())
+    write_scale = true_kib / max(means["copy_write"].values())
+    raw = {}
+    fetch = write = 0.0
+    for name in set(means["fetch"]) | set(means["write"]):
+        if name.startswith(SCORE_KERNELS):
+            f, w = means["fetch"].get(name, 0.0), means["write"].get(name, 0.0)
+            raw[name] = {"FETCH_SIZE": f, "WRITE_SIZE": w}
+            fetch += f * 1024.0 * fetch_scale
+            write += w * 1024.0 * write_scale
+    cfg = synth_config_bytes("c3")
+    t = {
+        "what": "HBM bytes per tri_score call on the 32K->2048 long-reasoning workload (28 layers, "
+                "4 KV heads, 28 q heads, d 128, batch 8): prologue + operand pack + fused score kernel",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "copy_probe_kib": {"FETCH_SIZE": max(means["copy_fetch"].values()),
+                           "WRITE_SIZE": max(means["copy_write"].values()), "true_each": true_kib},
+        "raw_kib_per_dispatch": raw,
+        "fetch_bytes_per_call": fetch,
+        "write_bytes_per_call": write,
+        "bytes_per_call": fetch + write,
+        "algorithmic_bytes_per_call": cfg,
+        "ratio_to_algorithmic": (fetch + write) / cfg,
+        "commands": [cmd for _, cmd in TRAFFIC_RUNS.values()],
+    }
+    with open(out, "w") as f:
+        json.dump(t, f, indent=1)
+    print(out)
+
+
+def synth_config_bytes(name):
+    """Algorithmic tri_score bytes of a fixed-length workload, from its sizes
+    alone (no tensors): units * n * (d*2 + 4)."""
+    sizes = {"c3": dict(S=8, L=28, Hkv=4, n=32768, d=128)}[name]
+    return sizes["S"] * sizes["L"] * sizes["Hkv"] * sizes["n"] * (sizes["d"] * 2 + 4)
+
+
 WORKLOADS = {
     # name: (config id, overrides, label)
     "c3": (3, {}, "long_reasoning_32k_to_2048"),
@@ -176,7 +253,12 @@ def main():
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--cmd", default="")
+    ap.add_argument("--traffic", default=None, metavar="DIR",
+                    help="write the tri_score traffic JSON (--out) from the counter runs under DIR")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.traffic, args.out)
+        return
     if args.summarize:
         summarize(args.summarize, args.out, args.cmd)
         return

@@ -8,6 +8,8 @@
 #include <string>
 #include <vector>
 
+#include <algorithm>
+
 #include "tri_internal.hpp"
 #include "triattn.h"
 
@@ -143,7 +145,13 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.seqs.resize(S);
   if (S > 0 && cu_len[0] < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len[0] must be >= 0");
   int64_t out_acc = 0, ticket_acc = 0;
-  p.fused = tri::fused_supported(p.d);
+  // The fused path bounds the chunks of one unit; longer sequences take the
+  // generic path, which never waits on other work-groups.
+  int64_t longest = 0;
+  for (int s = 0; s < S; ++s) longest = std::max<int64_t>(longest, cu_len[s + 1] - cu_len[s]);
+  p.fused = tri::fused_supported(p.d) &&
+            (longest + tri::fused_chunk_keys(p.G) - 1) / tri::fused_chunk_keys(p.G) <=
+                tri::kFusedMaxUnitChunks;
   p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
   for (int s = 0; s < S; ++s) {
     const int64_t n = cu_len[s + 1] - cu_len[s];

@@ -27,8 +27,15 @@
 //    kernel is persistent: each work-group claims tickets in order from an
 //    atomic counter and keeps two chunks' raw per-head scores in LDS.  It
 //    streams chunk i, publishes the chunk's per-head fp64 sum and sum of
-//    squares, streams chunk i+1, and only then finalizes chunk i, so the
+//    squares, and finalizes chunk i only after streaming chunk i+1, so the
 //    wait for the rest of chunk i's unit overlaps useful streaming.
+//  * No work-group idles between chunks: while streaming chunk i+1 it has
+//    already claimed chunk i+2 (an atomic whose result it reads afterwards),
+//    so it requests chunk i+2's first K blocks and operands, then finalizes
+//    chunk i and publishes chunk i+1 while they land.  This holds whenever
+//    chunk i+1 starts past the end of chunk i's unit; otherwise (rare: one
+//    group took two chunks of a unit) it publishes chunk i+1, finalizes
+//    chunk i, and only then claims and requests the next chunk.
 //  * Publishing needs no flag and no ordering wait: every published slot
 //    holds a sentinel NaN (set by the prologue) until its value lands, and
 //    values are written once with coherent (agent-scope) stores.  A
@@ -37,12 +44,19 @@
 //    (mu, sigma); every chunk of the unit does the same arithmetic on the
 //    same numbers, so results are deterministic and equal keys score
 //    equally.
-//  * Waits cannot deadlock: tickets are claimed in order, and a work-group
-//    publishes each ticket it claims before it waits on an earlier one, so
-//    the chunks a waiter needs are claimed by running work-groups that will
-//    publish them without waiting, as long as the resident work-groups
-//    outnumber the chunks of one unit.  A spin bound turns a broken
-//    invariant into an error flag instead of a hang.
+//  * Waits cannot deadlock.  A work-group waits only to finalize, and then
+//    holds claimed, unpublished chunks (at most two) only of later units
+//    than the one it waits on.  Following "waits on a chunk held by" from
+//    any waiter therefore passes through strictly earlier units and ends at
+//    a work-group that is streaming (and will publish) or at an unclaimed
+//    chunk.  Tickets are claimed in order, so an unclaimed chunk a waiter
+//    needs lies in the unit holding the claim frontier; a waiter on that
+//    unit holds no unpublished chunk and two published ones of it, so such
+//    a chunk stays unclaimed only if every resident work-group waits with
+//    two chunks of one unit, i.e. with twice the resident work-groups no
+//    more than the unit's chunks.  The planner caps chunks per unit well
+//    below that.  A spin bound turns a broken invariant into an error flag
+//    instead of a hang.
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -72,6 +86,7 @@ constexpr int kRawPad = 4;  // LDS row stride (floats) per head = ch + kRawPad
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kPrefetch = 2;  // blocks of 16 keys in flight per wave
 constexpr int kStatGroups = kFusedThreads / kMaxGroup;  // finalize reduction fan-in
+constexpr int kPollBatch = 4;  // chunk-stat slots a finalizing thread loads at once
 constexpr int kFusedLdsPerCu = 160 * 1024;
 constexpr int kFusedMaxLds = 96 * 1024;  // dynamic LDS ceiling of one work-group
 
@@ -79,6 +94,14 @@ __device__ __forceinline__ double wave_sum_f(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// |k_f|^2 = x^2 + y^2 of a packed bf16 pair (x low, y high): exact bf16
+// products, one fp32 rounding.
+__device__ __forceinline__ float band_sq(uint32_t w) {
+  bf16x2_t pr;
+  __builtin_memcpy(&pr, &w, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(pr, pr, 0.0f, false);
 }
 
 __device__ __forceinline__ double ld_agent(const double* p) {
@@ -96,7 +119,7 @@ __device__ __forceinline__ uint64_t ld_agent_u64(const double* p) {
 }
 
 struct Chunk {
-  int t, s, lg, l, g, c, nch, nkeys;
+  int t, s, lg, l, g, c, nch, nkeys, nkeys_unit;
   int64_t row0, unit;
 };
 
@@ -112,6 +135,7 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
   ck.c = local % ck.nch;
   ck.l = ck.lg / Hkv;
   ck.g = ck.lg % Hkv;
+  ck.nkeys_unit = si.n;
   const int key0 = ck.c * ch;
   ck.nkeys = min(ch, si.n - key0);
   ck.row0 = si.row_base + (int64_t)ck.lg * si.n + key0;
@@ -122,6 +146,7 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
 struct Shared {
   double red1[kStatGroups][kMaxGroup];
   double red2[kStatGroups][kMaxGroup];
+  double pub[kMaxGroup][2];  // a chunk's moments, summed, until published
   float zmul[kMaxGroup], zadd[kMaxGroup];
   int ticket;
 };
@@ -135,55 +160,76 @@ __device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ 
   return apack + unit * (4 * STEPS) * 64;
 }
 
-// Raw scores of one chunk into raw (LDS, [G][kRawStride]); per-head
-// sum and sum of squares of the chunk's raw scores in fp64 into sh.s1/s2.
+// Block b (16 keys) of a chunk into bv: lane (m, q) takes 16 bytes of key
+// b*16 + m per step st (4 lanes cover 64 contiguous bytes of the row).
 template <int STEPS>
-__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
-                                          const uint4* __restrict__ apack,
-                                          const uint16_t* __restrict__ k, float* raw,
-                                          Shared& sh) {
+__device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __restrict__ k,
+                                           int b, uint4 (&bv)[STEPS]) {
   constexpr int D = STEPS * 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-
-  // A operands: lane holds head m (zero rows beyond G), d-range of group q.
-  bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];
-  float wn[STEPS][4];
-  {
-    const uint4* op = unit_operands<STEPS>(apack, ck.unit) + lane;
+  int key = b * 16 + m;
+  key = key < ck.nkeys ? key : ck.nkeys - 1;  // padding lanes re-read a valid row
+  const uint4* rp = reinterpret_cast<const uint4*>(k + (ck.row0 + key) * D);
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const uint4 vh = op[(4 * st + 0) * 64], vm = op[(4 * st + 1) * 64];
-      const uint4 vl = op[(4 * st + 2) * 64], vw = op[(4 * st + 3) * 64];
-      __builtin_memcpy(&a_hi[st], &vh, 16);
-      __builtin_memcpy(&a_mid[st], &vm, 16);
-      __builtin_memcpy(&a_lo[st], &vl, 16);
-      wn[st][0] = __uint_as_float(vw.x);
-      wn[st][1] = __uint_as_float(vw.y);
-      wn[st][2] = __uint_as_float(vw.z);
-      wn[st][3] = __uint_as_float(vw.w);
-    }
-  }
+  for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
+}
 
-  // Stream the chunk: wave w takes blocks of 16 keys w, w+4, ...  A ring of
-  // kPrefetch register buffers keeps that many blocks in flight per wave.
-  const int nkeys = ck.nkeys;
-  const int nblk = (nkeys + 15) >> 4;
-  const uint4* kbase = reinterpret_cast<const uint4*>(k + ck.row0 * D);
-  auto load_block = [&](int b, uint4 (&bv)[STEPS]) {
-    int key = b * 16 + m;
-    key = key < nkeys ? key : nkeys - 1;  // padding lanes re-read a valid row
-    const uint4* rp = kbase + (int64_t)key * (D / 8);
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
-  };
-  double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
-  uint4 ring[kPrefetch][STEPS];
+// Request the first kPrefetch blocks of each wave of a chunk (wave w takes
+// blocks w, w + 4, ...).  chunk_raw consumes them.  Unconditional (blocks
+// past the chunk's end re-read its last block) so that no earlier ring
+// contents stay live across the caller's code.
+template <int STEPS>
+__device__ __forceinline__ void ring_prime(const Chunk& ck, const uint16_t* __restrict__ k,
+                                           uint4 (&ring)[kPrefetch][STEPS]) {
+  const int wave = threadIdx.x >> 6;
+  const int nblk = (ck.nkeys + 15) >> 4;
 #pragma unroll
   for (int j = 0; j < kPrefetch; ++j) {
     const int b = wave + kFusedWaves * j;
-    if (b < nblk) load_block(b, ring[j]);
+    load_block<STEPS>(ck, k, b < nblk ? b : nblk - 1, ring[j]);
   }
+}
+
+// Raw scores of one chunk into raw (LDS, [G][ch + kRawPad]) and the per-wave,
+// per-head fp64 sum and sum of squares of them into sh.red1/red2.  The ring
+// holds the chunk's first blocks (ring_prime); a ring of kPrefetch register
+// buffers keeps that many blocks in flight per wave.
+template <int STEPS>
+struct UnitOperands {
+  bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];  // trig coefficients, bf16 split
+  float wn[STEPS][4];                                // norm weights
+};
+
+// The MFMA A operands of a chunk's unit (L2-resident): lane holds head m
+// (zero rows beyond G), d-range of group q.
+template <int STEPS>
+__device__ __forceinline__ void load_operands(const Chunk& ck, const uint4* __restrict__ apack,
+                                              UnitOperands<STEPS>& op) {
+  const uint4* src = unit_operands<STEPS>(apack, ck.unit) + (threadIdx.x & 63);
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const uint4 vh = src[(4 * st + 0) * 64], vm = src[(4 * st + 1) * 64];
+    const uint4 vl = src[(4 * st + 2) * 64], vw = src[(4 * st + 3) * 64];
+    __builtin_memcpy(&op.a_hi[st], &vh, 16);
+    __builtin_memcpy(&op.a_mid[st], &vm, 16);
+    __builtin_memcpy(&op.a_lo[st], &vl, 16);
+    op.wn[st][0] = __uint_as_float(vw.x);
+    op.wn[st][1] = __uint_as_float(vw.y);
+    op.wn[st][2] = __uint_as_float(vw.z);
+    op.wn[st][3] = __uint_as_float(vw.w);
+  }
+}
+
+template <int STEPS>
+__device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
+                                          const UnitOperands<STEPS>& op,
+                                          const uint16_t* __restrict__ k, float* raw,
+                                          uint4 (&ring)[kPrefetch][STEPS]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int nblk = (ck.nkeys + 15) >> 4;
+
   for (int base = wave; base < nblk; base += kFusedWaves * kPrefetch) {
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
@@ -192,78 +238,115 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
         f32x4_t acc_t = {0.f, 0.f, 0.f, 0.f}, acc_n = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
+          // band magnitudes first (independent VALU work), then the trig
+          // MFMAs, then the norm MFMAs that consume the magnitudes
+          const uint32_t wd[4] = {ring[j][st].x, ring[j][st].y, ring[j][st].z, ring[j][st].w};
+          float r[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) r[u] = band_sq(wd[u]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) r[u] = __builtin_amdgcn_sqrtf(r[u]);
           bf16x8_t bk;
           __builtin_memcpy(&bk, &ring[j][st], 16);
-          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[st], bk, acc_t, 0, 0, 0);
-          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[st], bk, acc_t, 0, 0, 0);
-          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[st], bk, acc_t, 0, 0, 0);
-          const uint32_t wd[4] = {ring[j][st].x, ring[j][st].y, ring[j][st].z, ring[j][st].w};
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_hi[st], bk, acc_t, 0, 0, 0);
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_mid[st], bk, acc_t, 0, 0, 0);
+          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_lo[st], bk, acc_t, 0, 0, 0);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // |k_f|^2 = x^2 + y^2 straight from the packed bf16 pair (exact
-            // bf16 products, one fp32 rounding)
-            bf16x2_t pr;
-            __builtin_memcpy(&pr, &wd[u], 4);
-            const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fdot2_f32_bf16(pr, pr, 0.0f, false));
-            acc_n = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc_n, 0, 0, 0);
-          }
+          for (int u = 0; u < 4; ++u)
+            acc_n = __builtin_amdgcn_mfma_f32_16x16x4f32(op.wn[st][u], r[u], acc_n, 0, 0, 0);
+          // Keep the four bands' dot2 -> sqrt -> MFMA chains overlapped
+          // (left alone, the scheduler funnels them through one register and
+          // pads every step with wait states): the dot2s and their operand
+          // clears, the trig MFMAs, the square roots, the norm MFMAs.
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         const int bn = b + kFusedWaves * kPrefetch;
-        if (bn < nblk) load_block(bn, ring[j]);
-        // D layout: lane holds heads 4q..4q+3 of key b*16 + m
-        const bool valid = b * 16 + m < nkeys;
+        if (bn < nblk) load_block<STEPS>(ck, k, bn, ring[j]);
+        // D layout: lane holds heads 4q..4q+3 of key b*16 + m (rows past
+        // the chunk's end land in the buffer's padding and are never read)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int h = 4 * q + i;
-          const float v = acc_t[i] + acc_n[i];
-          if (h < G) raw[h * rs + b * 16 + m] = v;
-          const double dv = valid ? (double)v : 0.0;
-          s1[i] += dv;
-          s2[i] = fma(dv, dv, s2[i]);
+          if (h < G) raw[h * rs + b * 16 + m] = acc_t[i] + acc_n[i];
         }
       }
     }
   }
-  // Sum over the 16 keys of each lane group, then over the waves.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      s1[i] += __shfl_xor(s1[i], o, 64);
-      s2[i] += __shfl_xor(s2[i], o, 64);
-    }
-  }
-  if (m == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sh.red1[wave][4 * q + i] = s1[i];
-      sh.red2[wave][4 * q + i] = s2[i];
-    }
-  }
 }
 
-// Publish the chunk's per-head fp64 (sum, sum of squares) with coherent
-// stores; call after a barrier that follows chunk_raw.  No wait: readers
-// recognise slots not yet written by their sentinel.
-__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, Shared& sh,
-                                              double* __restrict__ chunk_stats) {
+// Per-head fp64 sum and sum of squares of a chunk's raw scores, read back
+// from LDS (call after a barrier that follows chunk_raw): thread (h, j)
+// takes keys 4j.. of every 64, then the tail, into sh.red1/red2[j][h].
+__device__ __forceinline__ void chunk_moments(const Chunk& ck, int G, int rs, const float* raw,
+                                              Shared& sh) {
+  const int tid = threadIdx.x;
+  const int h = tid % kMaxGroup, j = tid / kMaxGroup;
+  double a = 0.0, b2 = 0.0;
+  if (h < G) {
+    const float* row = raw + h * rs;
+    const int nk4 = ck.nkeys & ~3;
+    for (int i = 4 * j; i < nk4; i += 4 * kStatGroups) {
+      const f32x4_t r = *reinterpret_cast<const f32x4_t*>(row + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double v = (double)r[e];
+        a += v;
+        b2 = fma(v, v, b2);
+      }
+    }
+    for (int i = nk4 + j; i < ck.nkeys; i += kStatGroups) {
+      const double v = (double)row[i];
+      a += v;
+      b2 = fma(v, v, b2);
+    }
+  }
+  sh.red1[j][h] = a;
+  sh.red2[j][h] = b2;
+}
+
+// Sum the chunk's per-group moments (call after a barrier that follows
+// chunk_moments); thread h < G keeps head h's (sum, sum of squares) in
+// sh.pub for chunk_publish.
+__device__ __forceinline__ void chunk_moment_sums(int G, Shared& sh) {
   const int tid = threadIdx.x;
   if (tid < G) {
     double a = 0.0, b2 = 0.0;
 #pragma unroll
-    for (int w = 0; w < kFusedWaves; ++w) {
-      a += sh.red1[w][tid];
-      b2 += sh.red2[w][tid];
+    for (int g2 = 0; g2 < kStatGroups; ++g2) {
+      a += sh.red1[g2][tid];
+      b2 += sh.red2[g2][tid];
     }
+    sh.pub[tid][0] = a;
+    sh.pub[tid][1] = b2;
+  }
+}
+
+// Publish the sums with coherent stores, by the threads that formed them.
+// No wait: readers recognise slots not yet written by their sentinel.
+__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, const Shared& sh,
+                                              double* __restrict__ chunk_stats) {
+  const int tid = threadIdx.x;
+  if (tid < G) {
     double* cs = chunk_stats + ((int64_t)ck.t * G + tid) * 2;
-    st_agent(cs, a);
-    st_agent(cs + 1, b2);
+    st_agent(cs, sh.pub[tid][0]);
+    st_agent(cs + 1, sh.pub[tid][1]);
   }
 }
 
 // Read every chunk slot of the unit (waiting for any still holding the
-// sentinel), derive (mu, sigma) per head, z-score the chunk, take the max
-// over the group and write the scores (and the optional debug outputs).
+// sentinel), derive (mu, sigma) per head, z-score the chunk and take the
+// max over the group, into row 0 of raw (each key's score overwrites its
+// head-0 raw value, by the thread that read the key's raw values).
+// chunk_store_scores copies them out; the debug outputs are written here.
+// Whether a chunk's scores move as 16-byte vectors (see chunk_finalize).
+__device__ __forceinline__ bool vector_scores(const Chunk& ck, const float* scores,
+                                              const float* raw_out) {
+  return (reinterpret_cast<uintptr_t>(scores + ck.row0) & 15u) == 0 && !raw_out;
+}
+
 __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, const float* raw,
                                                Shared& sh, const double* __restrict__ chunk_stats,
                                                uint32_t* __restrict__ err_flag,
@@ -274,22 +357,38 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
   const int h = tid % kMaxGroup, j = tid / kMaxGroup;  // head, reduction group
   double a = 0.0, b2 = 0.0;
   if (h < G) {
+    // Thread (h, j) sums chunks j, j + kStatGroups, ... in that order.  The
+    // loads of a batch are all issued before any is examined, so a unit of
+    // up to kStatGroups * kPollBatch chunks costs one round trip.
     const int t0 = ck.t - ck.c;
-    for (int cc = j; cc < ck.nch; cc += kStatGroups) {
-      const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
-      uint64_t u0 = ld_agent_u64(cs), u1 = ld_agent_u64(cs + 1);
-      uint32_t spins = 0;
-      while (u0 == kStatSentinel || u1 == kStatSentinel) {
-        __builtin_amdgcn_s_sleep(2);
-        u0 = ld_agent_u64(cs);
-        u1 = ld_agent_u64(cs + 1);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+    for (int cc0 = j; cc0 < ck.nch; cc0 += kStatGroups * kPollBatch) {
+      uint64_t u[kPollBatch][2];
+#pragma unroll
+      for (int r = 0; r < kPollBatch; ++r) {
+        const int cc = min(cc0 + r * kStatGroups, ck.nch - 1);
+        const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
+        u[r][0] = ld_agent_u64(cs);
+        u[r][1] = ld_agent_u64(cs + 1);
+      }
+#pragma unroll
+      for (int r = 0; r < kPollBatch; ++r) {
+        const int cc = cc0 + r * kStatGroups;
+        if (cc < ck.nch) {
+          const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
+          uint32_t spins = 0;
+          while (u[r][0] == kStatSentinel || u[r][1] == kStatSentinel) {
+            __builtin_amdgcn_s_sleep(2);
+            u[r][0] = ld_agent_u64(cs);
+            u[r][1] = ld_agent_u64(cs + 1);
+            if (++spins > kSpinLimit) {
+              __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+          a += __longlong_as_double((long long)u[r][0]);
+          b2 += __longlong_as_double((long long)u[r][1]);
         }
       }
-      a += __longlong_as_double((long long)u0);
-      b2 += __longlong_as_double((long long)u1);
     }
   }
   sh.red1[j][h] = a;
@@ -317,14 +416,51 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
     }
   }
   __syncthreads();
-  for (int i = tid; i < ck.nkeys; i += kFusedThreads) {
+  // Four keys per thread with 16-byte LDS accesses where the chunk's first
+  // score is 16-byte aligned in global memory (rs and the buffers are
+  // multiples of four floats); the same fmaf/fmaxf per key as the scalar
+  // loop below.
+  float* out = const_cast<float*>(raw);
+  int i0 = 0;
+  if (vector_scores(ck, scores, raw_out)) {
+    const int nk4 = ck.nkeys & ~3;
+    for (int i = 4 * tid; i < nk4; i += 4 * kFusedThreads) {
+      f32x4_t best = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      for (int hh = 0; hh < G; ++hh) {
+        const f32x4_t r = *reinterpret_cast<const f32x4_t*>(raw + hh * rs + i);
+        const float zm = sh.zmul[hh], za = sh.zadd[hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) best[e] = fmaxf(best[e], fmaf(r[e], zm, za));
+      }
+      *reinterpret_cast<f32x4_t*>(out + i) = best;
+    }
+    i0 = nk4;
+  }
+  for (int i = i0 + tid; i < ck.nkeys; i += kFusedThreads) {
     float best = -__builtin_inff();
     for (int hh = 0; hh < G; ++hh)
       best = fmaxf(best, fmaf(raw[hh * rs + i], sh.zmul[hh], sh.zadd[hh]));
-    scores[ck.row0 + i] = best;
     if (raw_out)
       for (int hh = 0; hh < G; ++hh) raw_out[(ck.row0 + i) * G + hh] = raw[hh * rs + i];
+    out[i] = best;
   }
+}
+
+// Copy a finalized chunk's scores (row 0 of raw) to global memory, each key
+// by the thread that computed it in chunk_finalize.
+__device__ __forceinline__ void chunk_store_scores(const Chunk& ck, const float* raw,
+                                                   float* __restrict__ scores,
+                                                   const float* raw_out) {
+  const int tid = threadIdx.x;
+  int i0 = 0;
+  if (vector_scores(ck, scores, raw_out)) {
+    const int nk4 = ck.nkeys & ~3;
+    for (int i = 4 * tid; i < nk4; i += 4 * kFusedThreads)
+      *reinterpret_cast<f32x4_t*>(scores + ck.row0 + i) =
+          *reinterpret_cast<const f32x4_t*>(raw + i);
+    i0 = nk4;
+  }
+  for (int i = i0 + tid; i < ck.nkeys; i += kFusedThreads) scores[ck.row0 + i] = raw[i];
 }
 
 // STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
@@ -341,37 +477,81 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   uint32_t* err_flag = ctrl + 1;
   const int rs = ch + kRawPad;
 
-  Chunk prev;
-  int prev_n = 0;
+  auto claim = [&]() {
+    return __hip_atomic_fetch_add(ticket_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // One vector-memory counter covers loads and stores, so a wait for a load
+  // also waits for every store issued before it.  The next chunk's K ring and
+  // operands are therefore requested before this chunk's stores (scores,
+  // published moments) and the streaming loop never waits on a store.
+  uint4 ring[kPrefetch][STEPS];
+  UnitOperands<STEPS> op;
+  Chunk prev, ck;
+  int prev_last = 0;  // last ticket of prev's unit
   bool have_prev = false;
   int cur = 0;
+  if (threadIdx.x == 0) sh.ticket = (int)claim();
+  __syncthreads();
+  int t = __builtin_amdgcn_readfirstlane(sh.ticket);  // uniform: chunk fields in SGPRs
+  if (t < total_tickets) {
+    ck = decode_chunk(seqs, S, L, Hkv, ch, t);
+    ring_prime<STEPS>(ck, k, ring);
+    load_operands<STEPS>(ck, apack, op);
+  }
+  // Each pass streams chunk ck (if any) and finalizes prev (if any).  Every
+  // step below has one call site, so their per-lane constants exist once.
   for (;;) {
-    if (threadIdx.x == 0)
-      sh.ticket = (int)__hip_atomic_fetch_add(ticket_ctr, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int t = sh.ticket;
-    __syncthreads();
     const bool have = t < total_tickets;
+    if (!have && !have_prev) break;
     float* buf_cur = raw_s + cur * G * rs;
     float* buf_prev = raw_s + (cur ^ 1) * G * rs;
-    Chunk ck;
+    // Claim the next ticket now (its result is read after streaming) when it
+    // is bound to lie in a later unit than prev.  Then prev's finalize and
+    // this chunk's publish both run under the next chunk's first loads with
+    // this chunk and the next held unpublished, both of later units than the
+    // one waited on.  Otherwise this chunk is published before prev's
+    // finalize and the next ticket claimed after it.
+    const bool ahead = have && (!have_prev || prev_last < t);
+    uint32_t next = 0;  // thread 0
+    if (ahead && threadIdx.x == 0) next = claim();
+    if (have) chunk_raw<STEPS>(ck, G, rs, op, k, buf_cur, ring);
+    if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
+    __syncthreads();
+    // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
+    // go unused.  The ring and operands are reloaded on every path so their
+    // old contents are dead from here on.
+    Chunk nk = ck;
+    if (ahead) {
+      t = __builtin_amdgcn_readfirstlane(sh.ticket);
+      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
+    }
+    if (ahead || !have) ring_prime<STEPS>(nk, k, ring);
     if (have) {
-      ck = decode_chunk(seqs, S, L, Hkv, ch, t);
-      chunk_raw<STEPS>(ck, G, rs, apack, k, buf_cur, sh);
+      chunk_moments(ck, G, rs, buf_cur, sh);
       __syncthreads();
-      chunk_publish(ck, G, sh, chunk_stats);
-      __syncthreads();
+      chunk_moment_sums(G, sh);
+      if (!ahead) chunk_publish(ck, G, sh, chunk_stats);
+      __syncthreads();  // sh.red1/red2 are free again
     }
-    if (have_prev) {
+    if (have_prev)
       chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, scores, raw_out,
-                     head_stats, prev_n);
+                     head_stats, prev.nkeys_unit);
+    if (have && !ahead) {
+      if (threadIdx.x == 0) sh.ticket = (int)claim();
       __syncthreads();
+      t = __builtin_amdgcn_readfirstlane(sh.ticket);
+      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
+      ring_prime<STEPS>(nk, k, ring);
     }
+    load_operands<STEPS>(nk, apack, op);
+    if (have_prev) chunk_store_scores(prev, buf_prev, scores, raw_out);
+    if (ahead) chunk_publish(ck, G, sh, chunk_stats);
+    __syncthreads();
     if (!have) break;
     prev = ck;
-    prev_n = seqs[ck.s].n;
+    prev_last = ck.t - ck.c + ck.nch - 1;
     have_prev = true;
+    ck = nk;
     cur ^= 1;
   }
 }

@@ -66,6 +66,9 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
 bool fused_supported(int d);
 // Keys per ticket of the fused path for a GQA group of G heads.
 int fused_chunk_keys(int G);
+// Most chunks one unit may have on the fused path.  Its waits need more
+// than half that many work-groups resident (every CU holds at least one).
+constexpr int kFusedMaxUnitChunks = 384;
 // Workspace bytes of the fused path's packed MFMA operands.
 size_t fused_operand_bytes(int d, int64_t units);
 

@@ -137,3 +137,16 @@ def test_workspace_grows_with_batch():
     small = R.tri_workspace_bytes(sh, [0, 1024])
     big = R.tri_workspace_bytes(sh, np.arange(9) * 32768)
     assert 0 < small < big
+
+
+def test_long_units_leave_the_fused_path():
+    """Units of more than 384 fused chunks (832 keys each at G = 7) take the
+    generic path, whose workspace holds the raw per-head scores; one chunk
+    fewer stays fused and needs no such spill."""
+    sh = R.make_shape(128, 7, 1, 1)
+    ch, cap = 832, 384
+    fused_n = ch * cap
+    long_n = ch * cap + 1
+    w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
+    w_long = R.tri_workspace_bytes(sh, [0, long_n])
+    assert w_long >= long_n * 7 * 4 > w_fused

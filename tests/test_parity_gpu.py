@@ -241,3 +241,15 @@ def test_c5_full_size():
         start, n = case.unit_rows(s, l, g)
         u = sc[start:start + n].reshape(-1, 128)
         assert np.array_equal(u[:, 64:].view(np.uint32), u[:, :64].view(np.uint32))
+
+
+@pytest.mark.timeout(600)
+def test_unit_past_fused_chunk_cap():
+    """A unit of more than 384 fused chunks (here 320488 keys at G = 7) is
+    scored by the generic path; scores against the oracle, selection exact."""
+    shape = synth.Shape(128, 7, 1, 1)
+    case = synth.build_case("long_unit", shape, [832 * 384 + 1000], [4096], device=DEV, seed=11)
+    res = gpu_run(case, raw=False, stats=True)
+    units = units_of(case)
+    _compare_units(case, res, units, factored=True)
+    check_selection_exact(case, res, units=units, rows_units=units)
