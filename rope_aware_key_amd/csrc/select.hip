@@ -309,6 +309,7 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
 // a group of d/8 lanes moves one row (16 bytes per lane) of K and of V, the
 // first lane of the group the position.
 constexpr int kCompactRows = 64;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void compact_kernel(
     const SeqInfo* __restrict__ seqs, int LH, int d, const int32_t* __restrict__ kept,
@@ -334,10 +335,14 @@ __global__ __launch_bounds__(256) void compact_kernel(
     const int32_t idx = kept[out0 + r];
     if ((uint32_t)idx >= (uint32_t)si.n) continue;  // never read outside the unit
     const int64_t src = in0 + idx, dst = out0 + r;
+    // rows move whole (d/8 lanes x 16 bytes), read once and written once:
+    // non-temporal on both sides
     if (k_out)
-      reinterpret_cast<uint4*>(k_out + dst * d)[part] = reinterpret_cast<const uint4*>(k + src * d)[part];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(k + src * d) + part),
+                                  reinterpret_cast<v4u*>(k_out + dst * d) + part);
     if (v_out)
-      reinterpret_cast<uint4*>(v_out + dst * d)[part] = reinterpret_cast<const uint4*>(v + src * d)[part];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(v + src * d) + part),
+                                  reinterpret_cast<v4u*>(v_out + dst * d) + part);
     if (pos_out && part == 0) pos_out[dst] = k_pos[src];
   }
 }
