@@ -274,6 +274,139 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(
   }
 }
 
+// Find the bin of hist (kHistBins bins, counts) that holds rank kk counted
+// from the top: thread t owns bins [t*BPT, (t+1)*BPT).  Returns the bin and
+// sets *above_out to the count in higher bins (all threads get both).
+template <int NT>
+__device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, uint32_t kk, uint32_t* sel,
+                                             uint32_t* wsum, uint32_t* above_out) {
+  constexpr int BPT = kHistBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t c[BPT], mine = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    c[j] = hist[tid * BPT + j];
+    mine += c[j];
+  }
+  uint32_t all = 0;
+  const uint32_t below = block_excl_scan<NT>(mine, wsum, &all);
+  uint32_t above = all - below - mine;
+#pragma unroll
+  for (int j = BPT - 1; j >= 0; --j) {
+    if (above < kk && kk <= above + c[j]) {
+      sel[0] = (uint32_t)(tid * BPT + j);
+      sel[1] = above;
+    }
+    above += c[j];
+  }
+  __syncthreads();
+  const uint32_t bin = sel[0];
+  *above_out = sel[1];
+  __syncthreads();
+  return bin;
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident select for units of up to NT*KPT keys: thread t holds
+// keys [t*KPT, (t+1)*KPT) in registers, so LDS holds only the histogram and
+// two work-groups share a CU.  Same digits and passes as select_lds_kernel;
+// since each thread's keys are one contiguous index range, the ordered
+// emission needs a single pair of block scans over per-thread counts.
+// ---------------------------------------------------------------------------
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void select_reg_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
+    int32_t* __restrict__ kept) {
+  constexpr int NW = NT / 64;
+  static_assert(KPT % 4 == 0, "keys load as float4");
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t wsum[NW];
+
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int s = unit / LH, lg = unit % LH;
+  const SeqInfo si = seqs[s];
+  const int n = si.n, b = si.b;
+  if (b <= 0) return;
+  const float* in = scores + si.row_base + (int64_t)lg * n;
+  int32_t* out = kept + si.out_base + (int64_t)lg * b;
+  if (b >= n) {
+    for (int i = tid; i < n; i += NT) out[i] = i;
+    return;
+  }
+  const int i0 = tid * KPT;
+  uint32_t key[KPT];
+  if ((reinterpret_cast<uintptr_t>(in) & 15u) == 0 && i0 + KPT <= n) {
+#pragma unroll
+    for (int j = 0; j < KPT; j += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(in + i0 + j);
+      key[j] = order_key(f.x);
+      key[j + 1] = order_key(f.y);
+      key[j + 2] = order_key(f.z);
+      key[j + 3] = order_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? order_key(in[i0 + j]) : 0u;
+  }
+  // keys past n are 0 (the NaN key) and are excluded by index below
+  const int mine = max(0, min(KPT, n - i0));
+
+  uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)b;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const uint32_t dmask = pass == 2 ? 0xffu : 0xfffu;
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j < mine && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+    __syncthreads();
+    uint32_t above = 0;
+    const uint32_t bin = pick_bin<NT>(hist, kk, sel, wsum, &above);
+    kk -= above;
+    prefix |= bin << shift;
+    mask |= dmask << shift;
+  }
+  const uint32_t T = prefix, quota = kk;
+
+  // Keys are blocked per thread, so a thread's counts cover a contiguous
+  // index range: one scan of the per-thread totals orders the whole unit.
+  uint32_t neq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) neq += (j < mine && key[j] == T) ? 1u : 0u;
+  uint32_t eq_all = 0;
+  const uint32_t eq_before = block_excl_scan<NT>(neq, wsum, &eq_all);
+  uint32_t nkeep = 0;
+  {
+    uint32_t e = eq_before;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool valid = j < mine;
+      const bool gt = valid && key[j] > T;
+      const bool eq = valid && key[j] == T;
+      nkeep += (gt || (eq && e < quota)) ? 1u : 0u;
+      e += eq ? 1u : 0u;
+    }
+  }
+  uint32_t keep_all = 0;
+  uint32_t pos = block_excl_scan<NT>(nkeep, wsum, &keep_all);
+  uint32_t e = eq_before;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool valid = j < mine;
+    const bool gt = valid && key[j] > T;
+    const bool eq = valid && key[j] == T;
+    if (gt || (eq && e < quota)) {
+      if (pos < (uint32_t)b) out[pos] = i0 + j;
+      ++pos;
+    }
+    e += eq ? 1u : 0u;
+  }
+}
+
 // Longest unit whose keys the LDS-staged select holds (140 KB of keys next
 // to the 16 KB histogram).
 constexpr int kSelLdsMaxKeys = 35840;
@@ -298,6 +431,16 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
   if (units == 0) return hipSuccess;
   if (max_n <= kSelSmallUnit)
     return launch_select_lds<256>(units, max_n, st, seqs, LH, scores, kept_idx);
+  if (max_n <= 1024 * 16) {
+    hipLaunchKernelGGL((select_reg_kernel<1024, 16>), dim3((unsigned)units), dim3(1024), 0, st,
+                       seqs, LH, scores, kept_idx);
+    return hipGetLastError();
+  }
+  if (max_n <= 1024 * 32) {
+    hipLaunchKernelGGL((select_reg_kernel<1024, 32>), dim3((unsigned)units), dim3(1024), 0, st,
+                       seqs, LH, scores, kept_idx);
+    return hipGetLastError();
+  }
   if (max_n <= kSelLdsMaxKeys)
     return launch_select_lds<1024>(units, max_n, st, seqs, LH, scores, kept_idx);
   hipLaunchKernelGGL(select_global_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, st, seqs,
