@@ -36,7 +36,8 @@ again in the design notes):
   writes them; band f is the complex number x_{2f} + i x_{2f+1}, and the
   printed matrix multiplies it by exp(+i omega_f p).
 * phi_f in S_trig is arg E[q_f] - arg k_f with k_f the pre-RoPE key.
-* The offsets are averaged (formula page), not max-reduced (the blog review).
+* The offsets are averaged (formula page) by default; the blog review's
+  maximum over D is available as reduce="max" (a variant, not the default).
 * (1 - R_f) weights S_norm only.
 * R_f := 1 when E|q_f| = 0 (both terms of that band vanish anyway).
 * z-score uses the population standard deviation over all n keys of the
@@ -147,15 +148,18 @@ def calibrate(q: np.ndarray, q_pos, omega: np.ndarray):
 # --------------------------------------------------------------------------
 def score_terms(k_post: np.ndarray, k_pos, p_q: float,
                 centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
-                omega: np.ndarray, offsets=OFFSETS):
-    """Offset-averaged TriAttention score of every key, for each query head.
+                omega: np.ndarray, offsets=OFFSETS, reduce="mean"):
+    """Offset-reduced TriAttention score of every key, for each query head.
 
     k_post: [n, d] post-RoPE keys (fp64); k_pos: [n] their positions.
     centre/absmean/R: [G, F] statistics of the G query heads that read
-    this KV head.  Returns (S_tilde [G, n], S_trig_avg [G, n], S_norm [G, n]).
+    this KV head.  reduce: "mean" (the formula page's average over D) or
+    "max" (the blog review's maximum over D).  Returns
+    (S_tilde [G, n], S_trig_reduced [G, n], S_norm [G, n]).
 
     The trig term is summed band by band and offset by offset exactly as the
-    equations write it; nothing is factored.
+    equations write it; nothing is factored.  S_norm does not depend on the
+    offset, so either reduction of S_trig + S_norm leaves it unchanged.
     """
     k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega)
     kf = bands(k_pre)                                   # [n, F]
@@ -170,11 +174,16 @@ def score_terms(k_post: np.ndarray, k_pos, p_q: float,
     for h in range(G):
         amp_q = np.abs(centre[h])                       # |E[q_f]|  [F]
         phi = np.angle(centre[h])[None, :] - k_arg      # [n, F]
-        acc = np.zeros(n)
-        for dlt in offsets:                             # mean over D
+        per = []
+        for dlt in offsets:                             # S_trig at Delta + delta
             ang = (delta[:, None] + dlt) * omega[None, :] + phi
-            acc += np.sum(amp_q[None, :] * k_abs * np.cos(ang), axis=1)
-        s_trig[h] = acc / len(offsets)
+            per.append(np.sum(amp_q[None, :] * k_abs * np.cos(ang), axis=1))
+        if reduce == "mean":
+            s_trig[h] = np.sum(per, axis=0) / len(offsets)
+        elif reduce == "max":
+            s_trig[h] = np.max(per, axis=0)
+        else:
+            raise ValueError(reduce)
         # S_norm(k) = sum_f (1 - R_f) E|q_f| |k_f|; independent of Delta,
         # so the offset mean leaves it unchanged.
         s_norm[h] = np.sum(((1.0 - R[h]) * absmean[h])[None, :] * k_abs, axis=1)
@@ -189,20 +198,31 @@ def offset_phasor_mean(omega: np.ndarray, offsets=OFFSETS) -> np.ndarray:
 
 def score_factored(k_post: np.ndarray, p_q: float,
                    centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
-                   omega: np.ndarray, offsets=OFFSETS) -> np.ndarray:
+                   omega: np.ndarray, offsets=OFFSETS, reduce="mean") -> np.ndarray:
     """The same S_tilde as score_terms, written as one dot product per head.
 
     Band f of a query at p_q + delta contributes
     Re(E[q_f] conj(k_f) exp(i omega_f (Delta + delta))); with the stored key
     k'_f = k_f exp(i omega_f p_k) the key position cancels and the offset mean
     folds into C_f:  S_trig = sum_f Re(E[q_f] C_f exp(i omega_f p_q) conj(k'_f)).
-    Used to check that identity and to evaluate large units quickly.
+    Used to check that identity and to evaluate large units quickly.  With
+    reduce="max" the offsets cannot be folded: the dot product is taken per
+    offset (A_f = E[q_f] exp(i omega_f (p_q + delta))) and the maximum kept.
     Returns S_tilde [G, n].
     """
-    C = offset_phasor_mean(omega, offsets)                       # [F]
-    A = centre * C[None, :] * np.exp(1j * omega * p_q)[None, :]  # [G, F]
     kf = bands(k_post)                                           # [n, F]
-    trig = np.real(A[:, None, :] * np.conj(kf)[None, :, :]).sum(axis=2)
+    if reduce == "mean":
+        C = offset_phasor_mean(omega, offsets)                   # [F]
+        A = centre * C[None, :] * np.exp(1j * omega * p_q)[None, :]  # [G, F]
+        trig = np.real(A[:, None, :] * np.conj(kf)[None, :, :]).sum(axis=2)
+    elif reduce == "max":
+        trig = None
+        for dlt in offsets:
+            A = centre * np.exp(1j * omega * (p_q + dlt))[None, :]
+            t = np.real(A[:, None, :] * np.conj(kf)[None, :, :]).sum(axis=2)
+            trig = t if trig is None else np.maximum(trig, t)
+    else:
+        raise ValueError(reduce)
     w = (1.0 - R) * absmean                                      # [G, F]
     norm = w @ np.abs(kf).T
     return trig + norm
@@ -231,15 +251,15 @@ def gqa_max(z: np.ndarray) -> np.ndarray:
 
 
 def unit_scores(k_post, k_pos, p_q, centre, absmean, R, omega,
-                offsets=OFFSETS, factored=False):
+                offsets=OFFSETS, factored=False, reduce="mean"):
     """Final fp64 score of each key of one unit (one sequence/layer/KV head).
 
     Returns (score [n], S_tilde [G, n], mu [G], sigma [G]).
     """
     if factored:
-        S = score_factored(k_post, p_q, centre, absmean, R, omega, offsets)
+        S = score_factored(k_post, p_q, centre, absmean, R, omega, offsets, reduce)
     else:
-        S = score_terms(k_post, k_pos, p_q, centre, absmean, R, omega, offsets)[0]
+        S = score_terms(k_post, k_pos, p_q, centre, absmean, R, omega, offsets, reduce)[0]
     z, mu, sigma = zscore_rows(S)
     return gqa_max(z), S, mu, sigma
 

@@ -362,3 +362,83 @@ def test_packed_unit_rows():
     assert O.unit_rows(cu, 2, 3, 0, 1, 2) == ((1 * 3 + 2) * 5, 5)
     assert O.unit_rows(cu, 2, 3, 1, 0, 1) == (2 * 3 * 5 + 1 * 7, 7)
     assert O.out_rows(cu, [3, 10], 2, 3, 1, 1, 0) == (2 * 3 * 3 + 1 * 3 * 7, 7)
+
+
+# ------------------------------------------------ offset-set variants ----
+LINEAR_OFFSETS = tuple(float(x) for x in range(1, 129, 8))       # 16 evenly spaced
+SHORT_OFFSETS = tuple(float(2 ** m) for m in range(9))            # max distance 256
+
+
+@pytest.mark.parametrize("offsets", [O.OFFSETS, LINEAR_OFFSETS, SHORT_OFFSETS, (5.0,)])
+def test_max_over_offsets_equals_max_logit_when_queries_equal_centre(offsets):
+    """Every query equals its centre (R = 1, S_norm = 0): the max-reduced score
+    is the largest direct RoPE logit over the offsets (q rotated to
+    p_q + delta, dotted with the stored key), for any offset set."""
+    rng = np.random.default_rng(31)
+    d, n = 32, 40
+    om, pos, k_post = _unit(rng, n, d)
+    c = rng.normal(size=d)
+    qpos = np.arange(16, dtype=float) * 37.0
+    q_post = O.rope_rotate(np.tile(c, (16, 1))[:, None, :], qpos[:, None], om)
+    centre, absmean, R = O.calibrate(q_post, qpos, om)
+    p_q = 70000.0
+    S, s_trig, s_norm = O.score_terms(k_post, pos, p_q, centre, absmean, R, om, offsets, "max")
+    assert np.max(np.abs(s_norm)) < 1e-10
+    ref = np.max([_direct_logit(c, p_q + dl, k_post.T) for dl in offsets], axis=0)
+    assert np.max(np.abs(S[0] - ref)) < 1e-11 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("offsets", [LINEAR_OFFSETS, SHORT_OFFSETS])
+def test_mean_over_other_offset_sets_is_mean_logit(offsets):
+    """The mean over any offset set equals the mean over the calibration set
+    and over that set of direct logits (linearity in q), the same pin as the
+    default set with another D."""
+    rng = np.random.default_rng(32)
+    d, n, N = 32, 30, 100
+    om, pos, k_post = _unit(rng, n, d)
+    q_pre = rng.normal(size=(N, d)) * 0.8 + rng.normal(size=d)
+    qpos = rng.integers(0, 5000, size=N).astype(float)
+    q_post = O.rope_rotate(q_pre[:, None, :], qpos[:, None], om)
+    centre, absmean, R = O.calibrate(q_post, qpos, om)
+    p_q = 70000.0
+    _, s_trig, _ = O.score_terms(k_post, pos, p_q, centre, absmean, R, om, offsets, "mean")
+    ref = np.mean([np.mean(O.rope_rotate(q_pre, p_q + dl, om) @ k_post.T, axis=0)
+                   for dl in offsets], axis=0)
+    assert np.max(np.abs(s_trig[0] - ref)) < 1e-11 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("reduce", ["mean", "max"])
+@pytest.mark.parametrize("offsets", [O.OFFSETS, LINEAR_OFFSETS])
+def test_factored_equals_term_by_term_for_offset_variants(reduce, offsets):
+    rng = np.random.default_rng(33)
+    d, n, G = 64, 48, 3
+    om, pos, k_post = _unit(rng, n, d, p_q_max=131072)
+    F = d // 2
+    centre = rng.uniform(0.5, 2, size=(G, F)) * np.exp(1j * rng.uniform(0, 2 * np.pi, size=(G, F)))
+    R = rng.uniform(0.3, 0.99, size=(G, F))
+    absmean = np.abs(centre) / R
+    p_q = 131072.0
+    S_terms = O.score_terms(k_post, pos, p_q, centre, absmean, R, om, offsets, reduce)[0]
+    S_fact = O.score_factored(k_post, p_q, centre, absmean, R, om, offsets, reduce)
+    assert np.max(np.abs(S_terms - S_fact)) < 1e-12 * np.max(np.abs(S_terms))
+
+
+def test_max_reduction_invariants():
+    """max over D >= mean over D key by key; one offset makes them equal;
+    repeating offsets changes neither (the GPU pads with repeats)."""
+    rng = np.random.default_rng(34)
+    d, n, G = 32, 25, 2
+    om, pos, k_post = _unit(rng, n, d)
+    F = d // 2
+    centre = rng.normal(size=(G, F)) + 1j * rng.normal(size=(G, F))
+    R = rng.uniform(0.2, 0.9, size=(G, F))
+    absmean = np.abs(centre) / R
+    p_q = 9000.0
+    mx = O.score_factored(k_post, p_q, centre, absmean, R, om, O.OFFSETS, "max")
+    mn = O.score_factored(k_post, p_q, centre, absmean, R, om, O.OFFSETS, "mean")
+    assert np.all(mx >= mn - 1e-12 * np.max(np.abs(mn)))
+    one_max = O.score_factored(k_post, p_q, centre, absmean, R, om, (64.0,), "max")
+    one_mean = O.score_factored(k_post, p_q, centre, absmean, R, om, (64.0,), "mean")
+    np.testing.assert_allclose(one_max, one_mean, rtol=1e-12, atol=1e-12)
+    rep = O.OFFSETS + O.OFFSETS[:3]
+    np.testing.assert_array_equal(O.score_factored(k_post, p_q, centre, absmean, R, om, rep, "max"), mx)
