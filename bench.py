@@ -6,6 +6,7 @@ head_dim 128, batch 8, 32768 keys per head pruned to 2048, K and V bf16),
 inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py --offsets linear --reduce max   # offset-set variant (tri_score_offsets)
   python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
   python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
   python bench.py --traffic DIR --out FILE   # counter runs (DIR/fetch, write, copy_fetch,
@@ -186,6 +187,24 @@ WORKLOADS = {
 }
 
 
+OFFSET_SETS = {
+    "default": [2.0 ** j for j in range(17)],           # {2^0..2^16}
+    "linear": [float(x) for x in range(1, 129, 8)],     # 16 offsets, spacing 8
+    "short": [2.0 ** j for j in range(9)],              # {2^0..2^8}
+}
+
+
+def max_mode_flops(case, n_offsets):
+    """Per-key MFMA work of the max-over-offsets kernel: the method's dot
+    products (2*G*|D|*d flops, fp32-equivalent) and the bf16 MFMA flops the
+    kernel issues for them (rows padded to 4 per head and 16 per tile, three
+    bf16 terms per coefficient)."""
+    G, d = case.shape.group, case.shape.head_dim
+    dp = (n_offsets + 3) // 4 * 4
+    rows = (G * dp + 15) // 16 * 16
+    return 2 * G * n_offsets * d, 3 * 2 * rows * d
+
+
 def algorithmic_bytes(case):
     """Bytes the method must move (no design intermediates):
     score:   n*d*2 (K read) + n*4 (score write)
@@ -248,6 +267,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
+    ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
+    ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", default=None)
@@ -288,7 +309,14 @@ def main():
     cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
     cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
     bu = torch.as_tensor(case.budget).pin_memory().numpy()
-    ws = torch.empty(max(1, R.tri_workspace_bytes(sh, cu)), dtype=torch.uint8, device=dev)
+    variant = args.offsets != "default" or args.reduce != "mean"
+    offs = torch.as_tensor(OFFSET_SETS[args.offsets], dtype=torch.float64).pin_memory().numpy()
+    if variant:
+        label = f"{label}+{args.reduce}_over_{args.offsets}_offsets"
+        wsb = R.tri_workspace_bytes_offsets(sh, cu, len(offs), args.reduce)
+    else:
+        wsb = R.tri_workspace_bytes(sh, cu)
+    ws = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
     scores = torch.empty(rows, dtype=torch.float32, device=dev)
     kept = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
     k_out = torch.empty(max(1, out_rows), d, dtype=torch.int16, device=dev)
@@ -297,8 +325,12 @@ def main():
     stream = torch.cuda.current_stream()
 
     def score():
-        R.tri_score(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean, case.q_R,
-                    scores, workspace=ws, stream=stream)
+        if variant:
+            R.tri_score_offsets(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean,
+                                case.q_R, offs, args.reduce, scores, workspace=ws, stream=stream)
+        else:
+            R.tri_score(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean, case.q_R,
+                        scores, workspace=ws, stream=stream)
 
     def select():
         R.tri_select_compact(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept, k_out, v_out,
@@ -357,10 +389,24 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "tri_score",
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": score_gbps / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic() if args.workload == "c3" else None,
+                     "traffic": measured_traffic() if args.workload == "c3" and not variant
+                     else None,
                      "algorithmic_bytes_per_launch": b_score,
                      "launch": "tri_score call: prologue + operand pack + fused score kernel"},
     }
+    if variant:
+        out["offsets"] = {"set": args.offsets, "values": OFFSET_SETS[args.offsets],
+                          "reduce": args.reduce}
+        out["roofline"]["kernel"] = "tri_score_offsets"
+        out["roofline"]["launch"] = "tri_score_offsets call: prologue + " + (
+            "operand pack + max-over-offsets MFMA kernel + z pass" if args.reduce == "max"
+            else "operand pack + score kernels")
+        if args.reduce == "max":
+            f_alg, f_issued = max_mode_flops(case, len(offs))
+            t = float(t_score.mean())
+            out["mfma"] = {"method_tflops": keys * f_alg / t / 1e12,
+                           "issued_bf16_tflops": keys * f_issued / t / 1e12,
+                           "issued_frac_of_bf16_peak": keys * f_issued / t / 1e12 / 2500.0}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case)

@@ -138,6 +138,59 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Offset-set variants of tri_score.
+ *
+ * The hyper.ai summary, section "实验", reports an ablation over the future
+ * offsets (maximum distance, number of offsets, geometric against linear
+ * spacing); the shibing624 blog review, section "一个细节：未来位置的处理",
+ * combines the offsets with a maximum where the talk page's averaged-score
+ * equation takes their mean.  tri_score_offsets runs either reduction over
+ * a caller-given set D:
+ *   TRI_REDUCE_MEAN  S~_h(i) = mean_{delta in D} S_trig(k_i, Delta_i + delta) + S_norm(k_i)
+ *   TRI_REDUCE_MAX   S~_h(i) = max_{delta in D}  S_trig(k_i, Delta_i + delta) + S_norm(k_i)
+ * followed by the same z-score and max over the GQA group as tri_score.
+ * With TRI_REDUCE_MEAN and D = {2^0, ..., 2^16} in that order the outputs
+ * equal tri_score's bit for bit.
+ */
+typedef enum {
+  TRI_REDUCE_MEAN = 0, /* average over the offsets (folds into one term)  */
+  TRI_REDUCE_MAX = 1   /* maximum over the offsets (one row per offset)   */
+} tri_reduce;
+
+/*
+ * tri_workspace_bytes_offsets -- workspace of tri_score_offsets and
+ * tri_select_compact for this batch, n_offsets offsets and this reduction.
+ * Returns 0 on invalid or unsupported arguments (tri_last_error() says
+ * which).
+ */
+size_t tri_workspace_bytes_offsets(const tri_shape* shape, int32_t num_seqs,
+                                   const int64_t* cu_len, int32_t n_offsets,
+                                   int32_t reduce);
+
+/*
+ * tri_score_offsets -- tri_score over the offset set offsets[n_offsets]
+ * [host] (distances in positions, any finite doubles, used in the order
+ * given; 1 <= n_offsets <= 4096) combined by `reduce` (a tri_reduce).
+ * Every other argument is as for tri_score.
+ *
+ * TRI_REDUCE_MAX needs head_dim % 32 == 0; its per-head rows of
+ * ceil(n_offsets/4)*4 offsets must fit the kernel's LDS budget (up to 160
+ * offsets at d = 128, 80 at d = 256); heads are processed in as many passes
+ * over the keys as that budget needs.  Shapes outside this return
+ * TRI_ERR_UNSUPPORTED.  TRI_REDUCE_MAX spills raw scores to the workspace
+ * (or to raw_scores when given).
+ */
+tri_status tri_score_offsets(const tri_shape* shape, int32_t num_seqs,
+                             const int64_t* cu_len, const int32_t* cur_pos,
+                             const uint16_t* k, const int32_t* k_pos,
+                             const float* q_centre, const float* q_absmean,
+                             const float* q_R, const double* offsets,
+                             int32_t n_offsets, int32_t reduce, float* scores,
+                             float* raw_scores, double* head_stats,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * tri_select_compact -- keep the top-B keys of every unit, in time order,
  * and gather their K, V rows and positions.
  *

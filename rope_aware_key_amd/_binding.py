@@ -45,6 +45,13 @@ _lib.tri_workspace_bytes.restype = ctypes.c_size_t
 _lib.tri_score.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                            _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_score.restype = ctypes.c_int
+_lib.tri_workspace_bytes_offsets.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P,
+                                             ctypes.c_int32, ctypes.c_int32]
+_lib.tri_workspace_bytes_offsets.restype = ctypes.c_size_t
+_lib.tri_score_offsets.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]
+_lib.tri_score_offsets.restype = ctypes.c_int
 _lib.tri_select_compact.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P,
                                     _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_select_compact.restype = ctypes.c_int
@@ -54,7 +61,12 @@ _lib.tri_last_error.argtypes = []
 _lib.tri_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("tri_calibrate", "tri_workspace_bytes", "tri_score", "tri_select_compact",
-           "tri_status_string", "tri_last_error")
+           "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
+           "tri_score_offsets")
+
+TRI_REDUCE_MEAN = 0
+TRI_REDUCE_MAX = 1
+REDUCE = {"mean": TRI_REDUCE_MEAN, "max": TRI_REDUCE_MAX}
 
 
 class TriError(RuntimeError):
@@ -125,6 +137,29 @@ def tri_score(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_absmean, q
                         _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
                         _stream(stream))
     _check(st, "tri_score")
+
+
+def tri_workspace_bytes_offsets(shape: TriShape, cu_len, n_offsets, reduce="mean") -> int:
+    arr, p = _host(cu_len, np.int64)
+    return int(_lib.tri_workspace_bytes_offsets(ctypes.byref(shape), len(arr) - 1, p,
+                                                int(n_offsets), REDUCE[reduce]))
+
+
+def tri_score_offsets(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_absmean, q_R,
+                      offsets, reduce, scores, raw_scores=None, head_stats=None, workspace=None,
+                      workspace_bytes=None, stream=None):
+    """tri_score over a caller-given offset set; reduce is "mean" or "max"."""
+    cu, pcu = _host(cu_len, np.int64)
+    cp, pcp = _host(cur_pos, np.int32)
+    off, poff = _host(offsets, np.float64)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_score_offsets(ctypes.byref(shape), len(cu) - 1, pcu, pcp, _ptr(k), _ptr(k_pos),
+                                _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), poff,
+                                0 if off is None else len(off), REDUCE[reduce], _ptr(scores),
+                                _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
+                                _stream(stream))
+    _check(st, "tri_score_offsets")
 
 
 def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx, k_out,

@@ -2,6 +2,7 @@
 // the per-call sequence plan, workspace layout and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -111,6 +112,14 @@ tri_status check_shape(const tri_shape* sh) {
   return TRI_OK;
 }
 
+// How the offsets enter the score: the built-in set {2^0..2^16} averaged
+// (tri_score), or a caller-given set averaged or maximised.
+struct OffsetMode {
+  const double* host = nullptr;  // NULL: built-in set, nothing uploaded
+  int n = 0;
+  bool max = false;
+};
+
 struct Plan {
   std::vector<SeqInfo> seqs;
   int S = 0, L = 0, Hkv = 0, Hq = 0, G = 0, d = 0, F = 0;
@@ -119,17 +128,35 @@ struct Plan {
   int64_t tickets = 0;
   // workspace offsets (bytes)
   size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ctrl = 0,
-         off_apack = 0, off_raw = 0;
+         off_apack = 0, off_raw = 0, off_offsets = 0;
   int64_t n_units = 0, n_stat_slots = 0;
   int chunk = 0;  // keys per score ticket
   bool fused = false;
+  OffsetMode om;
+  tri::MaxOffsetsPlan mp;  // max-over-offsets path
   size_t score_bytes = 0, select_bytes = 0;
 };
 
+tri_status check_offsets(const tri_shape* sh, const OffsetMode& om) {
+  if (!om.host) return TRI_OK;
+  if (om.n < 1 || om.n > tri::kMaxOffsets)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "n_offsets must be in [1, 4096]");
+  for (int j = 0; j < om.n; ++j)
+    if (!std::isfinite(om.host[j]))
+      return fail(TRI_ERR_INVALID_ARGUMENT, "offsets must be finite");
+  if (om.max && sh->head_dim % 32 != 0)
+    return fail(TRI_ERR_UNSUPPORTED, "the max over offsets needs head_dim % 32 == 0");
+  return TRI_OK;
+}
+
 tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
-                     const int32_t* cur_pos, const int32_t* budget, Plan& p) {
+                     const int32_t* cur_pos, const int32_t* budget, Plan& p,
+                     const OffsetMode& om = OffsetMode()) {
   tri_status st = check_shape(sh);
   if (st != TRI_OK) return st;
+  st = check_offsets(sh, om);
+  if (st != TRI_OK) return st;
+  p.om = om;
   if (S < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
   if (S > 0 && !cu_len) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len is NULL");
   if ((size_t)S * sizeof(SeqInfo) > kSlotBytes)
@@ -149,7 +176,13 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   // generic path, which never waits on other work-groups.
   int64_t longest = 0;
   for (int s = 0; s < S; ++s) longest = std::max<int64_t>(longest, cu_len[s + 1] - cu_len[s]);
-  p.fused = tri::fused_supported(p.d) &&
+  if (om.max) {
+    p.mp = tri::plan_max_offsets(p.d, p.G, om.n);
+    if (!p.mp.ok)
+      return fail(TRI_ERR_UNSUPPORTED,
+                  "the max over offsets: one head's offset rows exceed the LDS budget");
+  }
+  p.fused = !om.max && tri::fused_supported(p.d) &&
             (longest + tri::fused_chunk_keys(p.G) - 1) / tri::fused_chunk_keys(p.G) <=
                 tri::kFusedMaxUnitChunks;
   p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
@@ -187,6 +220,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   };
   p.off_seq = take((size_t)S * sizeof(SeqInfo));
   const size_t after_seq = off;
+  p.off_offsets = take(om.host ? (size_t)om.n * sizeof(double) : 0);
   p.off_P = take((size_t)p.L * p.Hq * p.F * sizeof(double2));
   p.off_W = take((size_t)p.L * p.Hq * p.F * sizeof(float));
   p.off_E = take((size_t)S * p.F * sizeof(double2));
@@ -197,7 +231,8 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.n_units = (int64_t)S * LH;
   p.off_ctrl = take((size_t)tri::kCtrlHeader * sizeof(uint32_t));
   // The fused path keeps raw scores on chip; the generic path spills them.
-  p.off_apack = take(tri::fused_operand_bytes(p.d, p.n_units));
+  p.off_apack = take(om.max ? tri::max_offsets_operand_bytes(p.d, p.mp, p.n_units)
+                            : tri::fused_operand_bytes(p.d, p.n_units));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
   p.select_bytes = after_seq;
@@ -229,6 +264,27 @@ size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs, const int64
   return p.score_bytes > p.select_bytes ? p.score_bytes : p.select_bytes;
 }
 
+size_t tri_workspace_bytes_offsets(const tri_shape* shape, int32_t num_seqs,
+                                   const int64_t* cu_len, int32_t n_offsets, int32_t reduce) {
+  if (reduce != TRI_REDUCE_MEAN && reduce != TRI_REDUCE_MAX) {
+    fail(TRI_ERR_INVALID_ARGUMENT, "reduce must be TRI_REDUCE_MEAN or TRI_REDUCE_MAX");
+    return 0;
+  }
+  // offsets are only counted here; their values are checked by the call
+  std::vector<double> zeros(n_offsets > 0 && n_offsets <= tri::kMaxOffsets ? n_offsets : 0, 0.0);
+  OffsetMode om;
+  om.host = zeros.data();
+  om.n = n_offsets;
+  om.max = reduce == TRI_REDUCE_MAX;
+  if (zeros.empty()) {
+    fail(TRI_ERR_INVALID_ARGUMENT, "n_offsets must be in [1, 4096]");
+    return 0;
+  }
+  Plan p;
+  if (make_plan(shape, num_seqs, cu_len, nullptr, nullptr, p, om) != TRI_OK) return 0;
+  return p.score_bytes > p.select_bytes ? p.score_bytes : p.select_bytes;
+}
+
 tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_t* q_pos,
                          int64_t n_samples, float* q_centre, float* q_absmean, float* q_R,
                          void* stream) {
@@ -245,14 +301,17 @@ tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_
   return TRI_OK;
 }
 
-tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
-                     const int32_t* cur_pos, const uint16_t* k, const int32_t* k_pos,
-                     const float* q_centre, const float* q_absmean, const float* q_R,
-                     float* scores, float* raw_scores, double* head_stats, void* workspace,
-                     size_t workspace_bytes, void* stream) {
-  (void)k_pos;
+}  // extern "C"
+
+namespace {
+
+tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                      const int32_t* cur_pos, const uint16_t* k, const float* q_centre,
+                      const float* q_absmean, const float* q_R, const OffsetMode& om,
+                      float* scores, float* raw_scores, double* head_stats, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   Plan p;
-  tri_status st = make_plan(shape, num_seqs, cu_len, cur_pos, nullptr, p);
+  tri_status st = make_plan(shape, num_seqs, cu_len, cur_pos, nullptr, p, om);
   if (st != TRI_OK) return st;
   if (num_seqs > 0 && !cur_pos) return fail(TRI_ERR_INVALID_ARGUMENT, "cur_pos is NULL");
   if (p.total_rows == 0) return TRI_OK;
@@ -265,26 +324,70 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
+  double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
   hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
   if (e == hipSuccess)
     e = tri::launch_prologue(p.L, p.Hq, p.d, shape->rope_theta, p.S, dseq, q_centre, q_absmean,
-                             q_R, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
-                             (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl), (double*)(ws + p.off_stats),
+                             q_R, doff, om.n, !om.max, (double2*)(ws + p.off_P),
+                             (float*)(ws + p.off_W), (double2*)(ws + p.off_E),
+                             (uint32_t*)(ws + p.off_ctrl), (double*)(ws + p.off_stats),
                              p.n_stat_slots, s);
-  if (e == hipSuccess && p.fused)
+  float* raw = raw_scores ? raw_scores : (float*)(ws + p.off_raw);
+  if (e != hipSuccess) {
+  } else if (om.max) {
+    e = tri::launch_score_max(dseq, p.S, p.L, p.Hkv, p.G, p.d, om.n, p.mp, shape->rope_theta,
+                              (int)p.tickets, (const double2*)(ws + p.off_P),
+                              (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E), doff,
+                              ws + p.off_apack, k, raw, (double*)(ws + p.off_stats), scores,
+                              head_stats, s);
+  } else if (p.fused) {
     e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                 (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                                 (const double2*)(ws + p.off_E), ws + p.off_apack, k,
                                 (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
                                 scores, raw_scores, head_stats, s);
-  else if (e == hipSuccess)
+  } else {
     e = tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                           (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
-                          (const double2*)(ws + p.off_E), k,
-                          raw_scores ? raw_scores : (float*)(ws + p.off_raw),
-                          (double*)(ws + p.off_stats), scores, head_stats, s);
+                          (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
+                          scores, head_stats, s);
+  }
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score: ") + hipGetErrorString(e));
   return TRI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                     const int32_t* cur_pos, const uint16_t* k, const int32_t* k_pos,
+                     const float* q_centre, const float* q_absmean, const float* q_R,
+                     float* scores, float* raw_scores, double* head_stats, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  (void)k_pos;
+  return score_impl(shape, num_seqs, cu_len, cur_pos, k, q_centre, q_absmean, q_R,
+                    OffsetMode(), scores, raw_scores, head_stats, workspace, workspace_bytes,
+                    stream);
+}
+
+tri_status tri_score_offsets(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                             const int32_t* cur_pos, const uint16_t* k, const int32_t* k_pos,
+                             const float* q_centre, const float* q_absmean, const float* q_R,
+                             const double* offsets, int32_t n_offsets, int32_t reduce,
+                             float* scores, float* raw_scores, double* head_stats,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  (void)k_pos;
+  if (!offsets) return fail(TRI_ERR_INVALID_ARGUMENT, "offsets is NULL");
+  if (reduce != TRI_REDUCE_MEAN && reduce != TRI_REDUCE_MAX)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "reduce must be TRI_REDUCE_MEAN or TRI_REDUCE_MAX");
+  OffsetMode om;
+  om.host = offsets;
+  om.n = n_offsets;
+  om.max = reduce == TRI_REDUCE_MAX;
+  return score_impl(shape, num_seqs, cu_len, cur_pos, k, q_centre, q_absmean, q_R, om, scores,
+                    raw_scores, head_stats, workspace, workspace_bytes, stream);
 }
 
 tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,

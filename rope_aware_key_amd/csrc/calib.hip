@@ -71,13 +71,15 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* 
 
 // P[l][h][f] = E[q_f] * C_f and W[l][h][f] = (1 - R_f) E|q_f| for every
 // (layer, query head, band); E[s][f] = exp(i omega_f p_q(s)) per sequence.
+// C_f is the mean of exp(i omega_f delta) over the offsets, summed in their
+// order (the default set is {2^0, ..., 2^16}); without folding C_f = 1.
 // All in fp64 (W is stored as fp32: it multiplies fp32 magnitudes).
 __global__ __launch_bounds__(256) void prologue_kernel(
     int L, int Hq, int d, double theta, int S, const SeqInfo* __restrict__ seqs,
     const float* __restrict__ q_centre, const float* __restrict__ q_absmean,
-    const float* __restrict__ q_R, double2* __restrict__ P, float* __restrict__ W,
-    double2* __restrict__ E, uint32_t* __restrict__ ctrl, double* __restrict__ stat_slots,
-    int64_t n_stat_slots) {
+    const float* __restrict__ q_R, const double* __restrict__ offsets, int nD, int fold,
+    double2* __restrict__ P, float* __restrict__ W, double2* __restrict__ E,
+    uint32_t* __restrict__ ctrl, double* __restrict__ stat_slots, int64_t n_stat_slots) {
   const int F = d >> 1;
   const int64_t n_stat = (int64_t)L * Hq * F;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -88,16 +90,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(
   if (idx < n_stat) {
     const int f = (int)(idx % F);
     const double omega = pow(theta, -2.0 * (double)f / (double)d);
-    double cr = 0.0, ci = 0.0;
-    double delta = 1.0;
-    for (int m = 0; m <= 16; ++m, delta *= 2.0) {
-      double sn, cs;
-      sincos(omega * delta, &sn, &cs);
-      cr += cs;
-      ci += sn;
+    double cr = 1.0, ci = 0.0;
+    if (fold) {
+      cr = 0.0;
+      for (int j = 0; j < nD; ++j) {
+        const double delta = offsets ? offsets[j] : ldexp(1.0, j);
+        double sn, cs;
+        sincos(omega * delta, &sn, &cs);
+        cr += cs;
+        ci += sn;
+      }
+      const double inv = 1.0 / (double)nD;
+      cr *= inv;
+      ci *= inv;
     }
-    cr *= (1.0 / 17.0);
-    ci *= (1.0 / 17.0);
     const double qr = (double)q_centre[2 * idx], qi = (double)q_centre[2 * idx + 1];
     P[idx] = make_double2(qr * cr - qi * ci, qr * ci + qi * cr);
     W[idx] = (float)((1.0 - (double)q_R[idx]) * (double)q_absmean[idx]);
@@ -113,14 +119,17 @@ __global__ __launch_bounds__(256) void prologue_kernel(
 
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqInfo* seqs,
                            const float* q_centre, const float* q_absmean, const float* q_R,
-                           double2* P, float* W, double2* E, uint32_t* ctrl, double* stat_slots,
+                           const double* offsets, int n_offsets, bool fold, double2* P,
+                           float* W, double2* E, uint32_t* ctrl, double* stat_slots,
                            int64_t n_stat_slots, hipStream_t st) {
   int64_t total = (int64_t)L * Hq * (d / 2) + (int64_t)S * (d / 2);
   if (n_stat_slots > total) total = n_stat_slots;
   if (kCtrlHeader > total) total = kCtrlHeader;
+  const int nD = offsets ? n_offsets : 17;
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, st, L, Hq, d, theta, S,
-                     seqs, q_centre, q_absmean, q_R, P, W, E, ctrl, stat_slots, n_stat_slots);
+                     seqs, q_centre, q_absmean, q_R, offsets, nD, fold ? 1 : 0, P, W, E, ctrl,
+                     stat_slots, n_stat_slots);
   return hipGetLastError();
 }
 

@@ -230,6 +230,13 @@ hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d
     launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, scores, head_stats, st);
+}
+
+hipError_t launch_zmax(const SeqInfo* seqs, int S, int L, int Hkv, int G, int total_tickets,
+                       const float* raw, const double* chunk_stats, float* scores,
+                       double* head_stats, hipStream_t st) {
+  if (total_tickets == 0) return hipSuccess;
   hipLaunchKernelGGL(zmax_kernel, dim3(total_tickets), dim3(256), 0, st, seqs, S, L, Hkv, G, raw,
                      chunk_stats, scores, head_stats);
   return hipGetLastError();

@@ -29,6 +29,10 @@ constexpr int kCtrlHeader = 64;
 constexpr uint64_t kStatSentinel = 0x7ff4dead0000beefull;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxHeadDim = 256;
+// Most offsets in a caller-given offset set.
+constexpr int kMaxOffsets = 4096;
+// Dynamic LDS of the max-over-offsets score kernel (its static LDS is 34 KB).
+constexpr size_t kMaxOffsetsLds = 120 * 1024;
 
 // Largest s with seqs[s].chunk_base <= t (sequences with no tickets share
 // chunk_base with their successor, so the search lands on the owner).
@@ -57,9 +61,13 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* 
                             const int32_t* q_pos, int64_t n_samples, float* centre,
                             float* absmean, float* R, hipStream_t st);
 
+// offsets: device array of n_offsets distances, or NULL for the default set
+// {2^0, ..., 2^16}.  fold: P = E[q] * mean_delta exp(i omega delta) when
+// true, P = E[q] when false (the offsets are applied later, per row).
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
                            const SeqInfo* seqs, const float* q_centre,
-                           const float* q_absmean, const float* q_R, double2* P,
+                           const float* q_absmean, const float* q_R,
+                           const double* offsets, int n_offsets, bool fold, double2* P,
                            float* W, double2* E, uint32_t* ctrl, double* stat_slots,
                            int64_t n_stat_slots, hipStream_t st);
 
@@ -86,6 +94,29 @@ hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d
                         const double2* E, const uint16_t* k, float* raw,
                         double* chunk_stats, float* scores, double* head_stats,
                         hipStream_t st);
+
+// z pass of the generic path: merges the (count, mean, M2) tickets of each
+// unit, writes max_h z and the per-head (mu, sigma).
+hipError_t launch_zmax(const SeqInfo* seqs, int S, int L, int Hkv, int G, int total_tickets,
+                       const float* raw, const double* chunk_stats, float* scores,
+                       double* head_stats, hipStream_t st);
+
+// Max-over-offsets score path: rows (head, offset) padded to Dp per head,
+// taken hp heads per pass in npass passes of ptiles 16-row tiles.
+struct MaxOffsetsPlan {
+  bool ok = false;
+  int Dp = 0, hp = 0, npass = 0, ptiles = 0;
+};
+MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets);
+size_t max_offsets_operand_bytes(int d, const MaxOffsetsPlan& mp, int64_t units);
+// Generic tickets (kScoreChunk keys); raw: [rows][G] fp32 spill; chunk_stats
+// as the generic path; P from the prologue with fold = false.
+hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int nD,
+                            const MaxOffsetsPlan& mp, double theta, int total_tickets,
+                            const double2* P, const float* W, const double2* E,
+                            const double* offsets, void* operands, const uint16_t* k,
+                            float* raw, double* chunk_stats, float* scores, double* head_stats,
+                            hipStream_t st);
 
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
                          int32_t* kept_idx, hipStream_t st);

@@ -71,6 +71,31 @@ def gpu_run(case: Case, raw=True, stats=True, compact=True, scores_in=None):
     return res
 
 
+def gpu_score_offsets(case: Case, offsets, reduce, raw=True, stats=True, raw_in_ws=False):
+    """tri_score_offsets on one case.  raw_in_ws: let the library spill the
+    raw scores into its workspace (raw output not requested)."""
+    import rope_aware_key_amd as R
+    dev = case.k.device
+    sh = shape_of(case)
+    G = case.shape.group
+    rows = case.total_rows()
+    cu = pinned(case.cu_len, np.int64)
+    cp = pinned(case.cur_pos, np.int32)
+    off = pinned(offsets, np.float64)
+    wsb = R.tri_workspace_bytes_offsets(sh, cu, len(off), reduce)
+    assert wsb > 0, R.last_error()
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    scores = torch.full((rows,), float("nan"), dtype=torch.float32, device=dev)
+    raw_t = None
+    if raw and not raw_in_ws:
+        raw_t = torch.full((rows, G), float("nan"), dtype=torch.float32, device=dev)
+    hs = torch.full((case.num_units, G, 2), float("nan"), dtype=torch.float64, device=dev) if stats else None
+    R.tri_score_offsets(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean, case.q_R,
+                        off, reduce, scores, raw_scores=raw_t, head_stats=hs, workspace=ws)
+    torch.cuda.synchronize()
+    return dict(scores=scores, raw=raw_t, head_stats=hs)
+
+
 def unit_inputs(case: Case, s, l, g):
     start, n = case.unit_rows(s, l, g)
     kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
@@ -84,16 +109,19 @@ def unit_inputs(case: Case, s, l, g):
     return start, n, kbits, pos, centre, absmean, Rr
 
 
-def oracle_unit(case: Case, s, l, g, factored=False, stats=None):
+def oracle_unit(case: Case, s, l, g, factored=False, stats=None, offsets=None,
+                reduce="mean"):
     """fp64 oracle scores of one unit. stats: optional (centre, absmean, R)
-    overriding the case's fp32 statistics for this KV head's group."""
+    overriding the case's fp32 statistics for this KV head's group;
+    offsets/reduce: the offset set (default {2^0..2^16}) and its reduction."""
     start, n, kbits, pos, centre, absmean, Rr = unit_inputs(case, s, l, g)
     if stats is not None:
         centre, absmean, Rr = stats
     om = O.rope_omega(case.shape.head_dim, case.shape.rope_theta)
     kpost = O.bf16_bits_to_f64(kbits)
+    extra = {} if offsets is None else dict(offsets=np.asarray(offsets, np.float64))
     score, S, mu, sigma = O.unit_scores(kpost, pos, float(case.cur_pos[s]), centre, absmean, Rr,
-                                        om, factored=factored)
+                                        om, factored=factored, reduce=reduce, **extra)
     return start, n, score, S, mu, sigma
 
 

@@ -26,7 +26,8 @@ def test_header_symbols_exported():
     lib = ctypes.CDLL(R.LIB_PATH)
     names = declared_functions()
     assert set(names) == {"tri_calibrate", "tri_workspace_bytes", "tri_score",
-                          "tri_select_compact", "tri_status_string", "tri_last_error"}
+                          "tri_select_compact", "tri_status_string", "tri_last_error",
+                          "tri_workspace_bytes_offsets", "tri_score_offsets"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -150,3 +151,80 @@ def test_long_units_leave_the_fused_path():
     w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
     w_long = R.tri_workspace_bytes(sh, [0, long_n])
     assert w_long >= long_n * 7 * 4 > w_fused
+
+
+DEFAULT_OFFSETS = [2.0 ** j for j in range(17)]
+
+
+def _score_off(shape, cu, cp, offsets=DEFAULT_OFFSETS, reduce="mean", **kw):
+    args = dict(k=_Fake(), k_pos=None, q_centre=_Fake(), q_absmean=_Fake(), q_R=_Fake(),
+                scores=_Fake(), workspace=None, workspace_bytes=0)
+    args.update(kw)
+    return R.tri_score_offsets(shape, cu, cp, args["k"], args["k_pos"], args["q_centre"],
+                               args["q_absmean"], args["q_R"], offsets, reduce, args["scores"],
+                               workspace=args["workspace"],
+                               workspace_bytes=args["workspace_bytes"], stream=0)
+
+
+def test_score_offsets_argument_checks():
+    sh = R.make_shape(128, 8, 2, 2)
+    cu, cp = [0, 100, 250], [1, 2]
+    for red in ("mean", "max"):
+        need = R.tri_workspace_bytes_offsets(sh, cu, 17, red)
+        assert need > 0
+        assert _status(_score_off, sh, cu, cp, reduce=red) == ST["WORKSPACE"]
+        assert _status(_score_off, sh, cu, cp, reduce=red, workspace=_Fake(),
+                       workspace_bytes=need - 1) == ST["WORKSPACE"]
+        assert _status(_score_off, sh, cu, cp, offsets=None, reduce=red) == ST["INVALID"]
+        assert _status(_score_off, sh, cu, cp, offsets=[], reduce=red) == ST["INVALID"]
+        assert _status(_score_off, sh, cu, cp, offsets=[1.0, float("nan")],
+                       reduce=red) == ST["INVALID"]
+        assert _status(_score_off, sh, cu, cp, offsets=[1.0, float("inf")],
+                       reduce=red) == ST["INVALID"]
+        assert _status(_score_off, sh, cu, cp, offsets=np.ones(4097),
+                       reduce=red) == ST["INVALID"]
+        assert R.tri_workspace_bytes_offsets(sh, cu, 0, red) == 0
+        assert R.tri_workspace_bytes_offsets(sh, cu, 4097, red) == 0
+        # an empty batch queues nothing and succeeds
+        assert _status(_score_off, sh, [0, 0, 0], cp, reduce=red) == 0
+    # an unknown reduction code is rejected by the library itself
+    lib = R._binding._lib
+    st = lib.tri_score_offsets(ctypes.byref(sh), 2, np.array(cu, np.int64).ctypes.data,
+                               np.array(cp, np.int32).ctypes.data, FAKE, None, FAKE, FAKE, FAKE,
+                               np.array(DEFAULT_OFFSETS).ctypes.data, 17, 7, FAKE, None, None,
+                               None, 0, None)
+    assert st == ST["INVALID"] and "reduce" in R.last_error()
+    assert lib.tri_workspace_bytes_offsets(ctypes.byref(sh), 2,
+                                           np.array(cu, np.int64).ctypes.data, 17, 7) == 0
+
+
+def test_max_over_offsets_shape_limits():
+    cu, cp = [0, 64], [64]
+    # head_dim must be a multiple of 32 for the MFMA rows
+    sh = R.make_shape(72, 4, 2, 1)
+    assert _status(_score_off, sh, cu, cp, reduce="max") == ST["UNSUPPORTED"]
+    assert R.tri_workspace_bytes_offsets(sh, cu, 17, "max") == 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 17, "mean") > 0
+    # one head's rows must fit the LDS budget: 160 offsets at d = 128, 80 at d = 256
+    sh = R.make_shape(128, 8, 2, 1)
+    assert R.tri_workspace_bytes_offsets(sh, cu, 160, "max") > 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 161, "max") == 0
+    assert _status(_score_off, sh, cu, cp, offsets=np.arange(1.0, 162.0),
+                   reduce="max") == ST["UNSUPPORTED"]
+    sh = R.make_shape(256, 8, 2, 1)
+    assert R.tri_workspace_bytes_offsets(sh, cu, 80, "max") > 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 81, "max") == 0
+
+
+def test_offset_workspaces():
+    """The mean over any set needs the tri_score layout plus room for the
+    offsets; the max adds the per-offset operand rows and the raw spill."""
+    sh = R.make_shape(128, 7, 1, 4)
+    cu = [0, 32768, 40000]
+    base = R.tri_workspace_bytes(sh, cu)
+    mean = R.tri_workspace_bytes_offsets(sh, cu, 17, "mean")
+    mx = R.tri_workspace_bytes_offsets(sh, cu, 17, "max")
+    rows = 4 * cu[-1]
+    assert base < mean <= base + 17 * 8 + 256
+    assert mx >= rows * 7 * 4 > base
+    assert R.tri_workspace_bytes_offsets(sh, cu, 64, "max") > mx
