@@ -173,10 +173,10 @@ size_t tri_workspace_bytes_offsets(const tri_shape* shape, int32_t num_seqs,
  * given; 1 <= n_offsets <= 4096) combined by `reduce` (a tri_reduce).
  * Every other argument is as for tri_score.
  *
- * TRI_REDUCE_MAX needs head_dim % 32 == 0; its per-head rows of
- * ceil(n_offsets/4)*4 offsets must fit the kernel's LDS budget (up to 160
- * offsets at d = 128, 80 at d = 256); heads are processed in as many passes
- * over the keys as that budget needs.  Shapes outside this return
+ * TRI_REDUCE_MAX needs head_dim % 32 == 0, and one head's offset rows
+ * must fit the kernel's LDS budget: up to 400 offsets at d = 64, 192 at
+ * d = 128, 80 at d = 256.  Heads are processed in as many
+ * passes over the keys as that budget needs.  Shapes outside this return
  * TRI_ERR_UNSUPPORTED.  TRI_REDUCE_MAX spills raw scores to the workspace
  * (or to raw_scores when given).
  */

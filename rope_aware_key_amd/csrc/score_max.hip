@@ -8,25 +8,36 @@
 // own, so per unit the trig term is a (G*|D| x d) by (d x n) product.
 //
 // Mapping onto CDNA4:
-//  * Rows are (head h, offset slot j), row = h*Dp + j with Dp = |D| rounded
-//    up to a multiple of 4; slots past |D| repeat the first offset (a repeat
-//    leaves the maximum unchanged).  The 4 accumulator rows one lane holds
-//    (4q..4q+3 of a 16-row tile) therefore always belong to one head.
 //  * v_mfma_f32_16x16x32_bf16 with each fp64 coefficient split into three
 //    bf16 terms (hi, mid, lo), the same fp32-accurate scheme as the averaged
-//    path.  The split rows live in LDS and each A-operand read serves GB
-//    blocks of 16 keys held in registers.
+//    path.  The split rows of one unit live in LDS; each A-operand read
+//    serves GB blocks of 16 keys held in registers.
+//  * Lane (m, q) of an MFMA holds accumulator rows 4q..4q+3 of key m, so the
+//    rows are dealt to the four lane slots q.  Normally head h of a pass
+//    owns slot h % 4: its Dp rows (|D| rounded up to 4) fill Dp/4
+//    consecutive tiles of that slot, every lane takes the running maximum of
+//    its own rows in registers and ends holding heads q, q+4, q+8, q+12 of
+//    its key.  When one head's rows exceed the LDS budget the head is spread
+//    over all four slots and two cross-lane maxima merge them.  No LDS
+//    traffic is spent on the reduction.
 //  * When the rows of all G heads do not fit in LDS, the heads are taken in
-//    passes of whole heads (each pass re-reads the keys); a head's maximum
-//    is always complete within one pass.
-//  * A lane reduces its 4 rows and merges the result into a per-(key, head)
-//    maximum in LDS with an integer atomic max on an order-preserving map;
-//    the norm term is a v_mfma_f32_16x16x4_f32 product with heads as rows.
-//  * Raw scores are spilled in the generic path's layout with per-ticket
-//    (count, mean, M2) per head; the generic z pass (zmax_kernel) then merges
-//    the tickets of each unit and writes the z-score maxima.
+//    passes (each pass re-reads the keys); a head's maximum is always
+//    complete within one pass.
+//  * The norm term runs on the same bf16 MFMA with heads as rows (weights
+//    and band magnitudes split exactly into three bf16 terms each), the rows
+//    permuted so that lane q's accumulator entry i is head 4i + q of the
+//    pass, the same heads the lane holds maxima for.
+//  * Raw scores are spilled in the generic path's layout.  Each wave writes
+//    its sums (S1, S2) per (ticket, head); a merge kernel turns them into
+//    per-ticket (count, mean, M2) in wave order and the generic z pass
+//    (zmax_kernel) merges the tickets of each unit and writes the z-score
+//    maxima.
 //  * A work-group takes kTicketsPerGroup consecutive tickets and stages the
-//    split rows again only when the unit (or pass) changes.
+//    split rows again only when the unit (or pass) changes; otherwise its
+//    waves run independently, each loading the keys of its next group while
+//    it computes the current one.
+#include <algorithm>
+
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -34,17 +45,13 @@ namespace tri {
 typedef short bf16x8m_t __attribute__((ext_vector_type(8)));
 typedef float f32x4m_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2m_t __attribute__((ext_vector_type(2)));
+typedef float f32x2m_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTicketsPerGroup = 8;
-
-struct MaxLds {
-  uint32_t smax[kWaves][64][kMaxGroup];
-  double red_s[kWaves][kMaxGroup], red_q[kWaves][kMaxGroup];
-};
 
 __device__ __forceinline__ uint32_t bf16_rne_m(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -59,13 +66,25 @@ __device__ __forceinline__ void split3_m(double x, uint32_t& hi, uint32_t& mid, 
   lo = bf16_rne_m((float)r2);
 }
 
-// Order-preserving map of finite floats to uint32 (0 is below every image).
-__device__ __forceinline__ uint32_t ord(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// Two floats to a bf16 pair (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
+  const bf16x2m_t v = __builtin_convertvector((f32x2m_t){a, b}, bf16x2m_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
 }
-__device__ __forceinline__ float unord(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+
+// Exact three-term bf16 split of two floats: x = t1 + t2 + t3 for each,
+// returned as bf16 pairs (x_a in the low half).
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& t1, uint32_t& t2,
+                                            uint32_t& t3) {
+  t1 = cvt_pair(a, b);
+  a -= __uint_as_float(t1 << 16);
+  b -= __uint_as_float(t1 & 0xffff0000u);
+  t2 = cvt_pair(a, b);
+  a -= __uint_as_float(t2 << 16);
+  b -= __uint_as_float(t2 & 0xffff0000u);
+  t3 = cvt_pair(a, b);
 }
 
 __device__ __forceinline__ float band_sq_m(uint32_t w) {
@@ -101,23 +120,34 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&v)[8]) {
 
 }  // namespace
 
-// Split coefficient rows: thread (unit, pass, tile, step, lane) forms, for
-// row r = 16*tile + lane%16 of the pass (local head r / Dp, slot r % Dp),
-// the fp64 coefficients of the lane's four bands of the step,
-//   a_f = P[l][h][f] E[s][f] exp(i omega_f delta_slot),
-// and stores their bf16 hi/mid/lo splits in MFMA A-operand lane order.
-// The norm weights (heads as rows, one set per unit) go to wpack.
+// Split coefficient rows: thread (unit, pass, tile, step, lane) forms the
+// fp64 coefficients of the row the lane feeds at tile position m = lane%16
+// (slot m/4, entry m%4; head and offset from the slot layout above),
+//   a_f = P[l][h][f] E[s][f] exp(i omega_f delta),
+// for the lane's four bands of the step, and stores their bf16 hi/mid/lo
+// splits in MFMA A-operand lane order.  Rows past |D| repeat the first
+// offset; rows of heads outside the pass are zero.
+//
+// The norm term sum_f w_f |k_f| runs on the same bf16 MFMA: with
+// w = w1 + w2 + w3 and r = |k_f| = r1 + r2 + r3 split exactly into bf16
+// terms, three products per 16 bands,
+//   [w1 w1].[r1 r2] + [w2 w2].[r1 r2] + [w1 w3].[r3 r1],
+// keep every term down to 2^-24 of w r.  Lane (m, q) of step st feeds
+// bands b_u = 16 st + 4q + u as k = 8q + {r(b0) r(b1) r'(b0) r'(b1)
+// r(b2) r(b3) r'(b2) r'(b3)}, the order in which bf16 pairs come out of
+// the key words.  wpack holds the three A operands per (unit, pass, step),
+// row r = 4q' + i carrying the pass's local head 4i + q'.
 template <int STEPS>
 __global__ __launch_bounds__(256) void pack_max_operands_kernel(
-    int S, int L, int Hkv, int G, int Dp, int nD, int hp, int npass, int ptiles, double theta,
+    int S, int L, int Hkv, int G, MaxOffsetsPlan mp, int nD, double theta,
     const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
     const double* __restrict__ offsets, uint4* __restrict__ apack, uint4* __restrict__ wpack) {
   constexpr int F = STEPS * 16;
   constexpr int D = STEPS * 32;
   const int64_t units = (int64_t)S * L * Hkv;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n_a = units * npass * ptiles * STEPS * 64;
-  const int64_t n_w = units * STEPS * 64;
+  const int64_t n_a = units * mp.npass * mp.ptiles * STEPS * 64;
+  const int64_t n_w = units * mp.npass * STEPS * 64;  // one thread: 3 operands
   if (idx >= n_a + n_w) return;
   const int lane = (int)(idx & 63);
   const int m = lane & 15, q = lane >> 4;
@@ -126,18 +156,26 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
     int64_t r = idx >> 6;
     const int st = (int)(r % STEPS);
     r /= STEPS;
-    const int tile = (int)(r % ptiles);
-    r /= ptiles;
-    const int pass = (int)(r % npass);
-    const int64_t unit = r / npass;
+    const int tile = (int)(r % mp.ptiles);
+    r /= mp.ptiles;
+    const int pass = (int)(r % mp.npass);
+    const int64_t unit = r / mp.npass;
     const int lg = (int)(unit % ((int64_t)L * Hkv));
     const int s = (int)(unit / ((int64_t)L * Hkv));
     const int l = lg / Hkv, g = lg % Hkv;
-    const int row = tile * 16 + m;
-    const int hl = row / Dp, slot = row % Dp;
-    const int h = pass * hp + hl;
-    const bool live = hl < hp && h < G;
-    const double delta = offsets[slot < nD ? slot : 0];
+    const int slot = m >> 2, entry = m & 3;
+    const int k = tile / mp.tiles_per_head, tt = tile % mp.tiles_per_head;
+    int hl, j;
+    if (mp.spread == 1) {
+      hl = 4 * k + slot;
+      j = 4 * tt + entry;
+    } else {
+      hl = k;
+      j = 16 * tt + 4 * slot + entry;
+    }
+    const int h = pass * mp.hp + hl;
+    const bool live = hl < mp.hp && h < G;
+    const double delta = offsets[j < nD ? j : 0];
     uint32_t h3[8], m3[8], l3[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -163,193 +201,305 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
   } else {
     const int64_t j = idx - n_a;
     const int st = (int)((j >> 6) % STEPS);
-    const int64_t unit = (j >> 6) / STEPS;
+    const int64_t r = (j >> 6) / STEPS;
+    const int pass = (int)(r % mp.npass);
+    const int64_t unit = r / mp.npass;
     const int lg = (int)(unit % ((int64_t)L * Hkv));
     const int l = lg / Hkv, g = lg % Hkv;
+    // row m = 4q' + i carries local head 4i + q' of the pass
+    const int hl = 4 * (m & 3) + (m >> 2);
+    const int h = pass * mp.hp + hl;
     float wv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m < G) {
+    if (hl < mp.hp && h < G) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        wv[u] = W[((int64_t)l * Hq + g * G + m) * F + 4 * (4 * st + q) + u];
+        wv[u] = W[((int64_t)l * Hq + g * G + h) * F + 4 * (4 * st + q) + u];
     }
-    wpack[j] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
-                          __float_as_uint(wv[2]), __float_as_uint(wv[3]));
+    uint32_t a1, a2, a3, c1, c2, c3;  // splits of (w_b0, w_b1) and (w_b2, w_b3)
+    split3_pair(wv[0], wv[1], a1, a2, a3);
+    split3_pair(wv[2], wv[3], c1, c2, c3);
+    uint4* op = wpack + (j >> 6) * 3 * 64 + lane;
+    op[0] = make_uint4(a1, a1, c1, c1);    // [w1 w1] against [r1 r2]
+    op[64] = make_uint4(a2, a2, c2, c2);   // [w2 w2] against [r1 r2]
+    op[128] = make_uint4(a1, a3, c1, c3);  // [w1 w3] against [r3 r1]
+  }
+}
+
+// One work item of a wave: group grp (KG keys) of ticket t in pass `pass`.
+// A wave takes the groups grp = wave, wave + kWaves, ... of every ticket of
+// its work-group, pass by pass.
+struct MaxItem {
+  int pass, t, grp;
+  bool valid;
+};
+
+// First item of the wave at or after (pass, t), or an invalid item.
+__device__ __forceinline__ MaxItem first_item(const SeqInfo* seqs, int S, int npass, int t_begin,
+                                              int t_end, int pass, int t, int wave, int KG) {
+  for (; pass < npass; ++pass, t = t_begin) {
+    for (; t < t_end; ++t) {
+      const SeqInfo si = seqs[find_seq_by_ticket(seqs, S, t)];
+      const int nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+      const int c = (t - si.chunk_base) % nch;
+      const int nkeys = min(kScoreChunk, si.n - c * kScoreChunk);
+      if (wave * KG < nkeys) return MaxItem{pass, t, wave, true};
+    }
+  }
+  return MaxItem{0, 0, 0, false};
+}
+
+// Key rows of one item into registers: block bb, key 16*bb + m of the
+// group, dims 32*st + 8q .. +7 (the MFMA B-operand layout).  Rows past the
+// ticket's keys re-read its last row.
+template <int STEPS, int GB>
+__device__ __forceinline__ void load_item_keys(const SeqInfo* seqs, int S, int LH,
+                                               const uint16_t* __restrict__ k, const MaxItem& it,
+                                               int m, int q, uint4 (&kb)[GB][STEPS]) {
+  constexpr int D = STEPS * 32;
+  const MaxTicket tk = decode_max_ticket(seqs, S, LH, it.t);
+  const uint16_t* base = k + (tk.row0 + tk.key0) * (int64_t)D;
+#pragma unroll
+  for (int bb = 0; bb < GB; ++bb) {
+    int key = it.grp * 16 * GB + bb * 16 + m;
+    key = key < tk.nkeys ? key : tk.nkeys - 1;
+    const uint4* rp = reinterpret_cast<const uint4*>(base + (int64_t)key * D);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) kb[bb][st] = rp[4 * st + q];
   }
 }
 
 // kTicketsPerGroup consecutive tickets (kScoreChunk keys of one unit each)
-// per work-group.  Dynamic LDS: the split rows of one (unit, pass),
-// [ptiles][STEPS][3][64] uint4.
-template <int STEPS, int GB>
+// per work-group.  Dynamic LDS: the norm operands of one (unit, pass),
+// [STEPS][3][64] uint4, then its split rows, [ptiles][STEPS][3][64] uint4.
+// Each wave keeps the keys of its next item loading while it computes the
+// current one.  NE = ceil(hp/4) head entries per lane; every lane issues
+// the same GB*NE raw stores per group (rows past the ticket or heads past
+// the pass go to `sink`), so the load/store counter waits for the
+// prefetched keys stay exact.
+template <int STEPS, int GB, int NE>
 __global__ __launch_bounds__(kThreads) void score_max_kernel(
-    const SeqInfo* __restrict__ seqs, int S, int LH, int G, int Dp, int hp, int npass,
-    int ptiles, int total_tickets, const uint4* __restrict__ apack,
-    const uint4* __restrict__ wpack, const uint16_t* __restrict__ k, float* __restrict__ raw,
-    double* __restrict__ chunk_stats) {
-  constexpr int D = STEPS * 32;
+    const SeqInfo* __restrict__ seqs, int S, int LH, int G, MaxOffsetsPlan mp, int total_tickets,
+    const uint4* __restrict__ apack, const uint4* __restrict__ wpack,
+    const uint16_t* __restrict__ k, float* __restrict__ raw, double* __restrict__ wsum,
+    float* __restrict__ sink) {
   constexpr int KG = 16 * GB;  // keys per wave group
-  extern __shared__ uint4 a_s[];
-  __shared__ MaxLds sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ uint4 lds[];
+  uint4* w_s = lds;
+  uint4* a_s = lds + STEPS * 3 * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: the work list and ticket lookups stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, q = lane >> 4;
-  const int rows_per_head = Dp >> 2;  // row groups of 4 per head
-  const int n_a = ptiles * STEPS * 3 * 64;
+  const int n_a = mp.ptiles * STEPS * 3 * 64;
   const int t_begin = blockIdx.x * kTicketsPerGroup;
   const int t_end = min(t_begin + kTicketsPerGroup, total_tickets);
+  const bool spread = mp.spread != 1;
   int64_t staged = -1;
-  float wn[STEPS][4];
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const MaxTicket tk = decode_max_ticket(seqs, S, LH, t);
-    double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
-    const uint16_t* kbase = k + (tk.row0 + tk.key0) * (int64_t)D;
-    const int ngroups = (tk.nkeys + KG - 1) / KG;
-    for (int pass = 0; pass < npass; ++pass) {
-      const int64_t tag = tk.unit * npass + pass;
+  MaxItem cur = first_item(seqs, S, mp.npass, t_begin, t_end, 0, t_begin, wave, KG);
+  uint4 kb[GB][STEPS];
+  if (cur.valid) load_item_keys<STEPS, GB>(seqs, S, LH, k, cur, m, q, kb);
+
+  // Waves run through the tickets independently; the block meets only
+  // where the staged rows change (a new unit or pass).
+  for (int pass = 0; pass < mp.npass; ++pass) {
+    const int h0 = pass * mp.hp, h1 = min(G, h0 + mp.hp);
+    for (int t = t_begin; t < t_end; ++t) {
+      const MaxTicket tk = decode_max_ticket(seqs, S, LH, t);
+      double s1[NE], s2[NE];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) s1[i] = s2[i] = 0.0;
+      const int ngroups = (tk.nkeys + KG - 1) / KG;
+      const int64_t tag = tk.unit * mp.npass + pass;
       if (tag != staged) {
         __syncthreads();  // every wave is done with the previous rows
         const uint4* src = apack + tag * (int64_t)n_a;
         for (int i = tid; i < n_a; i += kThreads) a_s[i] = src[i];
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-          const uint4 w = wpack[(tk.unit * STEPS + st) * 64 + lane];
-          wn[st][0] = __uint_as_float(w.x);
-          wn[st][1] = __uint_as_float(w.y);
-          wn[st][2] = __uint_as_float(w.z);
-          wn[st][3] = __uint_as_float(w.w);
-        }
+        for (int i = tid; i < STEPS * 3 * 64; i += kThreads)
+          w_s[i] = wpack[tag * STEPS * 3 * 64 + i];
         __syncthreads();
         staged = tag;
       }
-      const int h0 = pass * hp, h1 = min(G, h0 + hp);
       for (int grp = wave; grp < ngroups; grp += kWaves) {
+        // this item is `cur`, its keys are in kb; start loading the next
+        // item's keys (the current item again when there is none)
+        const MaxItem nx = grp + kWaves < ngroups
+                               ? MaxItem{pass, t, grp + kWaves, true}
+                               : first_item(seqs, S, mp.npass, t_begin, t_end, pass, t + 1, wave, KG);
+        uint4 kn[GB][STEPS];
+        load_item_keys<STEPS, GB>(seqs, S, LH, k, nx.valid ? nx : cur, m, q, kn);
         const int key_g = grp * KG;
-        uint4 kb[GB][STEPS];
-#pragma unroll
-        for (int bb = 0; bb < GB; ++bb) {
-          int key = key_g + bb * 16 + m;
-          key = key < tk.nkeys ? key : tk.nkeys - 1;  // padding lanes re-read a valid row
-          const uint4* rp = reinterpret_cast<const uint4*>(kbase + (int64_t)key * D);
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st) kb[bb][st] = rp[4 * st + q];
-        }
-        // lane (m, q) owns keys m of each block, heads 4q..4q+3
+        // trig term: running maximum over each head's tiles
+        float hm[GB][NE];
 #pragma unroll
         for (int bb = 0; bb < GB; ++bb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sh.smax[wave][bb * 16 + m][4 * q + i] = 0u;
-        // Other lanes' atomics below touch these words: keep the three LDS
-        // phases (reset, max, read) in program order; one wave's LDS
-        // operations complete in issue order.
-        __builtin_amdgcn_wave_barrier();
-        // norm term, heads as rows: D[head][key] = sum_f w_f |k_f|
+          for (int i = 0; i < NE; ++i) hm[bb][i] = 0.f;
+        // A operands run one MFMA step ahead of their use (tiles in order
+        // over all rounds); past the last tile the last step is re-read.
+        const uint4* ap = a_s + lane;
+        uint4 va[3] = {ap[0], ap[64], ap[128]};
+        for (int kk = 0; kk < mp.nk; ++kk) {
+          float run[GB];
+#pragma unroll
+          for (int bb = 0; bb < GB; ++bb) run[bb] = -__builtin_huge_valf();
+          const int tile0 = kk * mp.tiles_per_head;
+          for (int tile = tile0; tile < tile0 + mp.tiles_per_head; ++tile) {
+            f32x4m_t acc[GB];
+#pragma unroll
+            for (int bb = 0; bb < GB; ++bb) acc[bb] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
+            const bool more = tile + 1 < mp.ptiles;
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+              const uint4* np = ap + ((st + 1 < STEPS || more) ? 192 : 0);
+              const uint4 vn[3] = {np[0], np[64], np[128]};
+              bf16x8m_t ah, am, al;
+              __builtin_memcpy(&ah, &va[0], 16);
+              __builtin_memcpy(&am, &va[1], 16);
+              __builtin_memcpy(&al, &va[2], 16);
+#pragma unroll
+              for (int bb = 0; bb < GB; ++bb) {
+                bf16x8m_t bk;
+                __builtin_memcpy(&bk, &kb[bb][st], 16);
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bk, acc[bb], 0, 0, 0);
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bk, acc[bb], 0, 0, 0);
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bk, acc[bb], 0, 0, 0);
+              }
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);       // next operands
+              __builtin_amdgcn_sched_group_barrier(0x008, 3 * GB, 0);  // this step
+              va[0] = vn[0];
+              va[1] = vn[1];
+              va[2] = vn[2];
+              ap = np;
+            }
+#pragma unroll
+            for (int bb = 0; bb < GB; ++bb)
+              run[bb] = fmaxf(run[bb], fmaxf(fmaxf(acc[bb][0], acc[bb][1]),
+                                             fmaxf(acc[bb][2], acc[bb][3])));
+          }
+          // head of this round: 4*kk + q (own slot), or kk spread over all
+          // slots (merge the four, lane kk % 4 keeps it as entry kk / 4)
+          int ent = kk;
+          bool own = true;
+          if (spread) {
+#pragma unroll
+            for (int bb = 0; bb < GB; ++bb) {
+              run[bb] = fmaxf(run[bb], __shfl_xor(run[bb], 16, 64));
+              run[bb] = fmaxf(run[bb], __shfl_xor(run[bb], 32, 64));
+            }
+            ent = kk >> 2;
+            own = q == (kk & 3);
+          }
+#pragma unroll
+          for (int i = 0; i < NE; ++i) {
+            if (own && i == ent) {
+#pragma unroll
+              for (int bb = 0; bb < GB; ++bb) hm[bb][i] = run[bb];
+            }
+          }
+        }
+        // norm term, heads as (permuted) rows: entry i of lane q is local
+        // head 4i + q of the pass
         f32x4m_t acc_n[GB];
 #pragma unroll
-        for (int bb = 0; bb < GB; ++bb) {
-          acc_n[bb] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
+        for (int bb = 0; bb < GB; ++bb) acc_n[bb] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int st = 0; st < STEPS; ++st) {
-            const uint32_t wd[4] = {kb[bb][st].x, kb[bb][st].y, kb[bb][st].z, kb[bb][st].w};
+        for (int st = 0; st < STEPS; ++st) {
+          const uint4* wp = w_s + st * 3 * 64 + lane;
+          const uint4 w1 = wp[0], w2 = wp[64], w3 = wp[128];
+          bf16x8m_t aw1, aw2, aw3;
+          __builtin_memcpy(&aw1, &w1, 16);
+          __builtin_memcpy(&aw2, &w2, 16);
+          __builtin_memcpy(&aw3, &w3, 16);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float r = __builtin_amdgcn_sqrtf(band_sq_m(wd[u]));
-              acc_n[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wn[st][u], r, acc_n[bb], 0, 0, 0);
-            }
+          for (int bb = 0; bb < GB; ++bb) {
+            const uint4 kw = kb[bb][st];
+            uint32_t r1a, r2a, r3a, r1b, r2b, r3b;
+            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(kw.x)),
+                        __builtin_amdgcn_sqrtf(band_sq_m(kw.y)), r1a, r2a, r3a);
+            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(kw.z)),
+                        __builtin_amdgcn_sqrtf(band_sq_m(kw.w)), r1b, r2b, r3b);
+            const uint4 b12 = make_uint4(r1a, r2a, r1b, r2b);
+            const uint4 b31 = make_uint4(r3a, r1a, r3b, r1b);
+            bf16x8m_t bx, by;
+            __builtin_memcpy(&bx, &b12, 16);
+            __builtin_memcpy(&by, &b31, 16);
+            acc_n[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw1, bx, acc_n[bb], 0, 0, 0);
+            acc_n[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw2, bx, acc_n[bb], 0, 0, 0);
+            acc_n[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw3, by, acc_n[bb], 0, 0, 0);
           }
         }
-        // trig term per (head, offset) row, reduced to a maximum per head
-        for (int tile = 0; tile < ptiles; ++tile) {
-          f32x4m_t acc[GB];
-#pragma unroll
-          for (int bb = 0; bb < GB; ++bb) acc[bb] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st) {
-            const uint4* ap = a_s + (tile * STEPS + st) * 3 * 64 + lane;
-            const uint4 vh = ap[0], vm = ap[64], vl = ap[128];
-            bf16x8m_t ah, am, al;
-            __builtin_memcpy(&ah, &vh, 16);
-            __builtin_memcpy(&am, &vm, 16);
-            __builtin_memcpy(&al, &vl, 16);
-#pragma unroll
-            for (int bb = 0; bb < GB; ++bb) {
-              bf16x8m_t bk;
-              __builtin_memcpy(&bk, &kb[bb][st], 16);
-              acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bk, acc[bb], 0, 0, 0);
-              acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bk, acc[bb], 0, 0, 0);
-              acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bk, acc[bb], 0, 0, 0);
-            }
-          }
-          // accumulator rows 4q..4q+3 of the tile: row group 4*tile + q
-          const int hl = (4 * tile + q) / rows_per_head;
-          const int h = h0 + hl;
-          if (hl < hp && h < h1) {
-#pragma unroll
-            for (int bb = 0; bb < GB; ++bb) {
-              const float v =
-                  fmaxf(fmaxf(acc[bb][0], acc[bb][1]), fmaxf(acc[bb][2], acc[bb][3]));
-              __hip_atomic_fetch_max(&sh.smax[wave][bb * 16 + m][h], ord(v), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // raw = max over offsets + norm, for the heads of this pass
+        // raw = max over offsets + norm, for the lane's heads 4i + q of this pass
 #pragma unroll
         for (int bb = 0; bb < GB; ++bb) {
           const int key = key_g + bb * 16 + m;
-          if (key < tk.nkeys) {
-            float* rp = raw + (tk.row0 + tk.key0 + key) * G;
+          float* rp = raw + (tk.row0 + tk.key0 + key) * G;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int h = 4 * q + i;
-              if (h >= h0 && h < h1) {
-                const float v = unord(__hip_atomic_load(&sh.smax[wave][bb * 16 + m][h],
-                                                        __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_WORKGROUP)) +
-                                acc_n[bb][i];
-                rp[h] = v;
-                const double dv = (double)v;
-                s1[i] += dv;
-                s2[i] = fma(dv, dv, s2[i]);
-              }
-            }
+          for (int i = 0; i < NE; ++i) {
+            const int h = h0 + 4 * i + q;
+            const bool ok = key < tk.nkeys && h < h1;
+            const float v = hm[bb][i] + acc_n[bb][i];
+            *(ok ? rp + h : sink + lane) = v;
+            const double dv = ok ? (double)v : 0.0;
+            s1[i] += dv;
+            s2[i] = fma(dv, dv, s2[i]);
+          }
+        }
+#pragma unroll
+        for (int bb = 0; bb < GB; ++bb)
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st) kb[bb][st] = kn[bb][st];
+        cur = nx;
+      }
+      // this wave's sums over its keys of ticket t for the pass's heads
+      // (entry i of lane q is head h0 + 4i + q): wsum[t][wave][h] = (S1, S2)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          s1[i] += __shfl_xor(s1[i], o, 64);
+          s2[i] += __shfl_xor(s2[i], o, 64);
+        }
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+          const int h = h0 + 4 * i + q;
+          if (h < h1) {
+            double* ws = wsum + (((int64_t)t * kWaves + wave) * G + h) * 2;
+            ws[0] = s1[i];
+            ws[1] = s2[i];
           }
         }
       }
     }
-    // per-ticket statistics per head: count, mean, M2 (from fp64 sums)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        s1[i] += __shfl_xor(s1[i], o, 64);
-        s2[i] += __shfl_xor(s2[i], o, 64);
-      }
-    }
-    if (m == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sh.red_s[wave][4 * q + i] = s1[i];
-        sh.red_q[wave][4 * q + i] = s2[i];
-      }
-    }
-    __syncthreads();
-    if (tid < G) {
-      double a = 0.0, b2 = 0.0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        a += sh.red_s[w][tid];
-        b2 += sh.red_q[w][tid];
-      }
-      const double cnt = (double)tk.nkeys;
-      const double mean = a / cnt;
-      double* cs = chunk_stats + ((int64_t)t * kMaxGroup + tid) * 3;
-      cs[0] = cnt;
-      cs[1] = mean;
-      cs[2] = fmax(b2 - cnt * mean * mean, 0.0);
-    }
-    __syncthreads();  // red_s / red_q are rewritten by the next ticket
   }
+}
+
+// Per-ticket statistics from the per-wave sums, in wave order:
+// chunk_stats[t][h] = (count, mean, M2) as the z pass reads them.
+__global__ __launch_bounds__(256) void max_stats_merge_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int G, int total_tickets,
+    const double* __restrict__ wsum, double* __restrict__ chunk_stats) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)total_tickets * G) return;
+  const int t = (int)(idx / G), h = (int)(idx % G);
+  const SeqInfo si = seqs[find_seq_by_ticket(seqs, S, t)];
+  const int nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+  const int c = (t - si.chunk_base) % nch;
+  const double cnt = (double)min(kScoreChunk, si.n - c * kScoreChunk);
+  double a = 0.0, b2 = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const double* ws = wsum + (((int64_t)t * kWaves + w) * G + h) * 2;
+    a += ws[0];
+    b2 += ws[1];
+  }
+  const double mean = a / cnt;
+  double* cs = chunk_stats + ((int64_t)t * kMaxGroup + h) * 3;
+  cs[0] = cnt;
+  cs[1] = mean;
+  cs[2] = fmax(b2 - cnt * mean * mean, 0.0);
 }
 
 MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets) {
@@ -358,25 +508,42 @@ MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets) {
       n_offsets > kMaxOffsets)
     return mp;
   const int steps = d / 32;
-  mp.Dp = (n_offsets + 3) / 4 * 4;
   const size_t tile_bytes = (size_t)steps * 3 * 64 * sizeof(uint4);
-  const int max_tiles = (int)(kMaxOffsetsLds / tile_bytes);
-  // most heads whose rows fit in LDS, then balanced over the passes
-  int hp = 0;
-  while (hp < G && ((hp + 1) * mp.Dp + 15) / 16 <= max_tiles) ++hp;
-  if (hp == 0) return mp;
-  mp.npass = (G + hp - 1) / hp;
-  mp.hp = (G + mp.npass - 1) / mp.npass;
-  mp.ptiles = (mp.hp * mp.Dp + 15) / 16;
+  // the norm operands take one tile's worth of the LDS budget
+  const int max_tiles = (int)(kMaxOffsetsLds / tile_bytes) - 1;
+  // one slot per head: Dp/4 tiles per head, four heads per round of tiles
+  int tph = (n_offsets + 3) / 4;
+  if (tph <= max_tiles) {
+    mp.spread = 1;
+    mp.Dp = 4 * tph;
+    const int hp_max = std::min(G, 4 * (max_tiles / tph));
+    mp.npass = (G + hp_max - 1) / hp_max;
+    mp.hp = (G + mp.npass - 1) / mp.npass;
+    mp.nk = (mp.hp + 3) / 4;
+  } else {
+    // one head over all four slots: Dp/16 tiles per head, one head per round
+    tph = (n_offsets + 15) / 16;
+    if (tph > max_tiles) return mp;
+    mp.spread = 4;
+    mp.Dp = 16 * tph;
+    const int hp_max = std::min(G, max_tiles / tph);
+    mp.npass = (G + hp_max - 1) / hp_max;
+    mp.hp = (G + mp.npass - 1) / mp.npass;
+    mp.nk = mp.hp;
+  }
+  mp.tiles_per_head = tph;
+  mp.ptiles = mp.nk * tph;
   mp.ok = true;
   return mp;
 }
 
-size_t max_offsets_operand_bytes(int d, const MaxOffsetsPlan& mp, int64_t units) {
+size_t max_offsets_operand_bytes(int d, int G, const MaxOffsetsPlan& mp, int64_t units,
+                                 int64_t tickets) {
   if (!mp.ok) return 0;
   const int steps = d / 32;
-  return (size_t)units *
-         ((size_t)mp.npass * mp.ptiles * steps * 3 * 64 + (size_t)steps * 64) * sizeof(uint4);
+  const size_t ops = (size_t)units * mp.npass *
+                     ((size_t)mp.ptiles * steps * 3 * 64 + (size_t)steps * 3 * 64) * sizeof(uint4);
+  return ops + (size_t)tickets * kWaves * G * 2 * sizeof(double) + 64 * sizeof(float);
 }
 
 template <int STEPS>
@@ -388,22 +555,33 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
   const int64_t units = (int64_t)S * L * Hkv;
   uint4* apack = reinterpret_cast<uint4*>(operands);
   uint4* wpack = apack + units * mp.npass * mp.ptiles * STEPS * 3 * 64;
-  const int64_t threads = units * mp.npass * mp.ptiles * STEPS * 64 + units * STEPS * 64;
+  double* wsum = reinterpret_cast<double*>(wpack + units * mp.npass * STEPS * 3 * 64);
+  const int64_t threads = units * mp.npass * mp.ptiles * STEPS * 64 + units * mp.npass * STEPS * 64;
   hipLaunchKernelGGL(pack_max_operands_kernel<STEPS>, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, st, S, L, Hkv, G, mp.Dp, nD, mp.hp, mp.npass, mp.ptiles,
-                     theta, P, W, E, offsets, apack, wpack);
+                     dim3(256), 0, st, S, L, Hkv, G, mp, nD, theta, P, W, E, offsets, apack,
+                     wpack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)mp.ptiles * STEPS * 3 * 64 * sizeof(uint4);
+  const size_t lds = ((size_t)mp.ptiles + 1) * STEPS * 3 * 64 * sizeof(uint4);
   const int grid = (total_tickets + kTicketsPerGroup - 1) / kTicketsPerGroup;
-  if constexpr (STEPS <= 4)
-    hipLaunchKernelGGL((score_max_kernel<STEPS, 4>), dim3(grid), dim3(kThreads), lds, st, seqs,
-                       S, L * Hkv, G, mp.Dp, mp.hp, mp.npass, mp.ptiles, total_tickets, apack,
-                       wpack, k, raw, chunk_stats);
+  constexpr int GB = STEPS <= 4 ? 4 : 2;
+  float* sink = reinterpret_cast<float*>(wsum + (int64_t)total_tickets * kWaves * G * 2);
+  const int ne = (mp.hp + 3) / 4;
+#define TRI_LAUNCH(NE)                                                                         \
+  hipLaunchKernelGGL((score_max_kernel<STEPS, GB, NE>), dim3(grid), dim3(kThreads), lds, st,   \
+                     seqs, S, L * Hkv, G, mp, total_tickets, apack, wpack, k, raw, wsum, sink)
+  if (ne == 1)
+    TRI_LAUNCH(1);
+  else if (ne == 2)
+    TRI_LAUNCH(2);
   else
-    hipLaunchKernelGGL((score_max_kernel<STEPS, 2>), dim3(grid), dim3(kThreads), lds, st, seqs,
-                       S, L * Hkv, G, mp.Dp, mp.hp, mp.npass, mp.ptiles, total_tickets, apack,
-                       wpack, k, raw, chunk_stats);
+    TRI_LAUNCH(4);
+#undef TRI_LAUNCH
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t merge = (int64_t)total_tickets * G;
+  hipLaunchKernelGGL(max_stats_merge_kernel, dim3((unsigned)((merge + 255) / 256)), dim3(256), 0,
+                     st, seqs, S, G, total_tickets, wsum, chunk_stats);
   return hipGetLastError();
 }
 

@@ -31,8 +31,9 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxHeadDim = 256;
 // Most offsets in a caller-given offset set.
 constexpr int kMaxOffsets = 4096;
-// Dynamic LDS of the max-over-offsets score kernel (its static LDS is 34 KB).
-constexpr size_t kMaxOffsetsLds = 120 * 1024;
+// Dynamic LDS of the max-over-offsets score kernel (it has no static LDS):
+// the whole 160 KB of a gfx950 CU.
+constexpr size_t kMaxOffsetsLds = 160 * 1024;
 
 // Largest s with seqs[s].chunk_base <= t (sequences with no tickets share
 // chunk_base with their successor, so the search lands on the owner).
@@ -101,14 +102,23 @@ hipError_t launch_zmax(const SeqInfo* seqs, int S, int L, int Hkv, int G, int to
                        const float* raw, const double* chunk_stats, float* scores,
                        double* head_stats, hipStream_t st);
 
-// Max-over-offsets score path: rows (head, offset) padded to Dp per head,
-// taken hp heads per pass in npass passes of ptiles 16-row tiles.
+// Max-over-offsets score path.  Accumulator row 4q+i of a 16-row tile is
+// held by lanes q (MFMA layout), so rows are assigned to the four lane
+// slots q: with spread == 1 head h of a pass lives in slot h % 4 (its Dp
+// rows, Dp = |D| rounded up to 4, take Dp/4 consecutive tiles of that
+// slot); with spread == 4 (one head's rows exceed the LDS budget) a head
+// takes all four slots of Dp/16 tiles (Dp rounded up to 16) and the slots
+// are merged with two cross-lane maxima.  hp heads per pass, npass passes
+// over the keys, ptiles = nk * tiles_per_head tiles per pass with nk the
+// number of head rounds (hp/4 rounded up, or hp).
 struct MaxOffsetsPlan {
   bool ok = false;
-  int Dp = 0, hp = 0, npass = 0, ptiles = 0;
+  int spread = 1, Dp = 0, tiles_per_head = 0, hp = 0, nk = 0, npass = 0, ptiles = 0;
 };
 MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets);
-size_t max_offsets_operand_bytes(int d, const MaxOffsetsPlan& mp, int64_t units);
+// Operand rows, norm weights and per-wave moment sums of the max path.
+size_t max_offsets_operand_bytes(int d, int G, const MaxOffsetsPlan& mp, int64_t units,
+                                 int64_t tickets);
 // Generic tickets (kScoreChunk keys); raw: [rows][G] fp32 spill; chunk_stats
 // as the generic path; P from the prologue with fold = false.
 hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int nD,

@@ -93,13 +93,15 @@ def test_max_c3_shape(name):
 
 
 @pytest.mark.parametrize("d,G,offsets", [
-    (64, 8, DEFAULT),        # two A tiles per step pair, GB = 4
+    (64, 8, DEFAULT),        # two head rounds of 5 tiles, GB = 4
     (256, 2, DEFAULT),       # eight MFMA steps, GB = 2
-    (32, 16, SHORT),         # one step, 16 heads in one pass
-    (96, 5, LINEAR),         # three steps
-    (128, 16, DEFAULT),      # 16 heads x 20 rows: two passes over the keys
-    (256, 8, LINEAR),        # 8 heads x 16 rows at 24 KB a tile: two passes
-    (128, 1, [float(x) for x in range(1, 161)]),   # one head of 160 rows, 10 tiles
+    (32, 16, SHORT),         # one step, 16 heads (four rounds) in one pass
+    (96, 5, LINEAR),         # three steps, five heads: the second round holds one
+    (128, 16, DEFAULT),      # 16 heads of 5 tiles at 12 per pass: two passes
+    (256, 8, LINEAR),        # 24 KB tiles, 4 tiles a head: two passes of 4 heads
+    (128, 1, [float(x) for x in range(1, 161)]),   # 160 rows: one head over all slots
+    (128, 4, [0.5 * x for x in range(100)]),       # spread heads, one per pass: four passes
+    (64, 3, [float(x) for x in range(1, 384, 2)]), # spread, 12 tiles a head: passes of 2 + 1 heads
 ])
 def test_max_shapes_and_passes(d, G, offsets):
     shape = synth.Shape(d, 2 * G, 2, 2)
