@@ -128,7 +128,7 @@ struct Plan {
   int64_t tickets = 0;
   // workspace offsets (bytes)
   size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ctrl = 0,
-         off_apack = 0, off_raw = 0, off_offsets = 0;
+         off_apack = 0, off_raw = 0, off_offsets = 0, off_ustats = 0;
   int64_t n_units = 0, n_stat_slots = 0;
   int chunk = 0;  // keys per score ticket
   bool fused = false;
@@ -233,6 +233,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   // The fused path keeps raw scores on chip; the generic path spills them.
   p.off_apack = take(om.max ? tri::max_offsets_operand_bytes(p.d, p.G, p.mp, p.n_units, p.tickets)
                             : tri::fused_operand_bytes(p.d, p.n_units));
+  p.off_ustats = take(p.fused ? 0 : (size_t)p.n_units * p.G * 2 * sizeof(double));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
   p.select_bytes = after_seq;
@@ -339,8 +340,8 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
     e = tri::launch_score_max(dseq, p.S, p.L, p.Hkv, p.G, p.d, om.n, p.mp, shape->rope_theta,
                               (int)p.tickets, (const double2*)(ws + p.off_P),
                               (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E), doff,
-                              ws + p.off_apack, k, raw, (double*)(ws + p.off_stats), scores,
-                              head_stats, s);
+                              ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
+                              (double*)(ws + p.off_ustats), scores, head_stats, s);
   } else if (p.fused) {
     e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                 (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
@@ -351,7 +352,7 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
     e = tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                           (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                           (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
-                          scores, head_stats, s);
+                          (double*)(ws + p.off_ustats), scores, head_stats, s);
   }
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score: ") + hipGetErrorString(e));
   return TRI_OK;

@@ -158,49 +158,91 @@ __global__ __launch_bounds__(256) void score_raw_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void zmax_kernel(
-    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G,
-    const float* __restrict__ raw, const double* __restrict__ chunk_stats,
-    float* __restrict__ scores, double* __restrict__ head_stats) {
-  __shared__ double mu_s[kMaxGroup], inv_s[kMaxGroup];
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x;
-  const Ticket tk = decode_ticket(seqs, S, t);
-  if (tid < G) {
-    const int t0 = seqs[tk.s].chunk_base + tk.lg * tk.nch;
-    double cnt = 0.0, mean = 0.0, m2 = 0.0;
-    for (int cc = 0; cc < tk.nch; ++cc) {
-      const double* cs = chunk_stats + ((int64_t)(t0 + cc) * kMaxGroup + tid) * 3;
-      const double nb = cs[0], mb = cs[1], m2b = cs[2];
-      if (cc == 0) {
-        cnt = nb; mean = mb; m2 = m2b;
-      } else {
-        const double tot = cnt + nb;
-        const double dl = mb - mean;
-        mean += dl * (nb / tot);
-        m2 += m2b + dl * dl * (cnt * nb / tot);
-        cnt = tot;
-      }
+// Per-(unit, head) statistics: the unit's tickets merged in ticket order
+// (Chan's update), once per unit.  unit_stats[unit][h] = (mu, 1/sigma), with
+// 1/sigma = 0 where sigma = 0; head_stats (optional) gets (mu, sigma).
+__global__ __launch_bounds__(256) void unit_stats_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int LH, int G, const double* __restrict__ chunk_stats,
+    double* __restrict__ unit_stats, double* __restrict__ head_stats) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)S * LH * G) return;
+  const int64_t unit = idx / G;
+  const int h = (int)(idx % G);
+  const SeqInfo si = seqs[unit / LH];
+  if (si.n == 0) return;
+  const int lg = (int)(unit % LH);
+  const int nch = (si.n + kScoreChunk - 1) / kScoreChunk;
+  const int t0 = si.chunk_base + lg * nch;
+  double cnt = 0.0, mean = 0.0, m2 = 0.0;
+#pragma unroll 4
+  for (int cc = 0; cc < nch; ++cc) {
+    const double* cs = chunk_stats + ((int64_t)(t0 + cc) * kMaxGroup + h) * 3;
+    const double nb = cs[0], mb = cs[1], m2b = cs[2];
+    if (cc == 0) {
+      cnt = nb; mean = mb; m2 = m2b;
+    } else {
+      const double tot = cnt + nb;
+      const double dl = mb - mean;
+      mean += dl * (nb / tot);
+      m2 += m2b + dl * dl * (cnt * nb / tot);
+      cnt = tot;
     }
-    const double sigma = sqrt(m2 / cnt);
-    mu_s[tid] = mean;
-    inv_s[tid] = sigma > 0.0 ? 1.0 / sigma : 0.0;
-    if (tk.c == 0 && head_stats) {
-      const int64_t unit = (int64_t)tk.s * L * Hkv + tk.lg;
-      head_stats[(unit * G + tid) * 2] = mean;
-      head_stats[(unit * G + tid) * 2 + 1] = sigma;
+  }
+  const double sigma = sqrt(m2 / cnt);
+  unit_stats[(unit * G + h) * 2] = mean;
+  unit_stats[(unit * G + h) * 2 + 1] = sigma > 0.0 ? 1.0 / sigma : 0.0;
+  if (head_stats) {
+    head_stats[(unit * G + h) * 2] = mean;
+    head_stats[(unit * G + h) * 2 + 1] = sigma;
+  }
+}
+
+// scores = max_h (raw_h - mu_h) / sigma_h, one ticket per work-group.  The
+// ticket's raw block (nkeys * G contiguous floats) is copied to LDS with
+// coalesced loads, into rows of odd stride GT|1 (conflict-free row reads).
+template <int GT>
+__global__ __launch_bounds__(256) void zmax_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int LH, int G, const float* __restrict__ raw,
+    const double* __restrict__ unit_stats, float* __restrict__ scores) {
+  constexpr int GP = GT | 1;
+  __shared__ float blk[kScoreChunk * GP];
+  __shared__ double mu_s[GT], inv_s[GT];
+  const int tid = threadIdx.x;
+  const Ticket tk = decode_ticket(seqs, S, blockIdx.x);
+  const int64_t unit = (int64_t)tk.s * LH + tk.lg;
+  if (tid < GT) {
+    mu_s[tid] = tid < G ? unit_stats[(unit * G + tid) * 2] : 0.0;
+    inv_s[tid] = tid < G ? unit_stats[(unit * G + tid) * 2 + 1] : 0.0;
+  }
+  const float* base = raw + (tk.row0 + tk.key0) * G;
+  const int total = tk.nkeys * G;
+  const float invG = 1.0f / (float)G;
+  constexpr int kUnroll = 4;
+  for (int i0 = tid; i0 < total; i0 += 256 * kUnroll) {
+    float v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int i = i0 + 256 * j;
+      v[j] = i < total ? base[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int i = i0 + 256 * j;
+      if (i < total) {
+        int key = (int)((float)i * invG);  // i < 2^14: off by at most one
+        key += (key + 1) * G <= i;
+        key -= key * G > i;
+        blk[key * GP + (i - key * G)] = v[j];
+      }
     }
   }
   __syncthreads();
   for (int key = tid; key < tk.nkeys; key += 256) {
-    const int64_t row = tk.row0 + tk.key0 + key;
-    const float* rp = raw + row * G;
     double best = -__builtin_huge_val();
-    for (int h = 0; h < G; ++h) {
-      const double z = ((double)rp[h] - mu_s[h]) * inv_s[h];
-      best = fmax(best, z);
-    }
-    scores[row] = (float)best;
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+      if (h < G) best = fmax(best, ((double)blk[key * GP + h] - mu_s[h]) * inv_s[h]);
+    scores[tk.row0 + tk.key0 + key] = (float)best;
   }
 }
 
@@ -214,8 +256,8 @@ static void launch_raw(int grid, hipStream_t st, const SeqInfo* seqs, int S, int
 
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W, const double2* E,
-                        const uint16_t* k, float* raw, double* chunk_stats, float* scores,
-                        double* head_stats, hipStream_t st) {
+                        const uint16_t* k, float* raw, double* chunk_stats, double* unit_stats,
+                        float* scores, double* head_stats, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const int Hq = Hkv * G;
   if (G <= 1)
@@ -230,15 +272,34 @@ hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d
     launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, scores, head_stats, st);
+  return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, unit_stats, scores,
+                     head_stats, st);
 }
 
 hipError_t launch_zmax(const SeqInfo* seqs, int S, int L, int Hkv, int G, int total_tickets,
-                       const float* raw, const double* chunk_stats, float* scores,
-                       double* head_stats, hipStream_t st) {
+                       const float* raw, const double* chunk_stats, double* unit_stats,
+                       float* scores, double* head_stats, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
-  hipLaunchKernelGGL(zmax_kernel, dim3(total_tickets), dim3(256), 0, st, seqs, S, L, Hkv, G, raw,
-                     chunk_stats, scores, head_stats);
+  const int LH = L * Hkv;
+  const int64_t n_us = (int64_t)S * LH * G;
+  hipLaunchKernelGGL(unit_stats_kernel, dim3((unsigned)((n_us + 255) / 256)), dim3(256), 0, st,
+                     seqs, S, LH, G, chunk_stats, unit_stats, head_stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define TRI_Z(GT)                                                                              \
+  hipLaunchKernelGGL(zmax_kernel<GT>, dim3(total_tickets), dim3(256), 0, st, seqs, S, LH, G, raw, \
+                     unit_stats, scores)
+  if (G <= 1)
+    TRI_Z(1);
+  else if (G <= 2)
+    TRI_Z(2);
+  else if (G <= 4)
+    TRI_Z(4);
+  else if (G <= 8)
+    TRI_Z(8);
+  else
+    TRI_Z(16);
+#undef TRI_Z
   return hipGetLastError();
 }
 

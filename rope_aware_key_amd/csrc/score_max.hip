@@ -589,8 +589,8 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const MaxOffsetsPlan& mp, double theta, int total_tickets,
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
-                            float* raw, double* chunk_stats, float* scores, double* head_stats,
-                            hipStream_t st) {
+                            float* raw, double* chunk_stats, double* unit_stats, float* scores,
+                            double* head_stats, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   if (!mp.ok) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
@@ -607,7 +607,8 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
       return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, scores, head_stats, st);
+  return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, unit_stats, scores,
+                     head_stats, st);
 }
 
 }  // namespace tri

@@ -90,17 +90,19 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
                               double* head_stats, hipStream_t st);
 
+// unit_stats: [units][G][2] fp64 scratch for the per-unit (mu, 1/sigma).
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W,
                         const double2* E, const uint16_t* k, float* raw,
-                        double* chunk_stats, float* scores, double* head_stats,
-                        hipStream_t st);
+                        double* chunk_stats, double* unit_stats, float* scores,
+                        double* head_stats, hipStream_t st);
 
 // z pass of the generic path: merges the (count, mean, M2) tickets of each
-// unit, writes max_h z and the per-head (mu, sigma).
+// unit into unit_stats ([units][G][2]: mu, 1/sigma; head_stats gets mu,
+// sigma), then writes max_h z per key.
 hipError_t launch_zmax(const SeqInfo* seqs, int S, int L, int Hkv, int G, int total_tickets,
-                       const float* raw, const double* chunk_stats, float* scores,
-                       double* head_stats, hipStream_t st);
+                       const float* raw, const double* chunk_stats, double* unit_stats,
+                       float* scores, double* head_stats, hipStream_t st);
 
 // Max-over-offsets score path.  Accumulator row 4q+i of a 16-row tile is
 // held by lanes q (MFMA layout), so rows are assigned to the four lane
@@ -125,8 +127,8 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const MaxOffsetsPlan& mp, double theta, int total_tickets,
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
-                            float* raw, double* chunk_stats, float* scores, double* head_stats,
-                            hipStream_t st);
+                            float* raw, double* chunk_stats, double* unit_stats, float* scores,
+                            double* head_stats, hipStream_t st);
 
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
                          int32_t* kept_idx, hipStream_t st);
