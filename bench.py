@@ -26,9 +26,13 @@ if ROOT not in sys.path:
 
 METRIC = "keys scored+compacted/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_c3.json")
-KERNEL_SOURCES = ["score_mfma.hip", "calib.hip", "api.hip", "tri_internal.hpp"]
+# The fused score kernel, its operand pack and launch shape (score_mfma.hip)
+# and the prologue (calib.hip): the kernels one tri_score call runs on the
+# 32K->2048 workload.
+KERNEL_SOURCES = ["score_mfma.hip", "calib.hip"]
 
 
 def kernel_source_hash():
@@ -197,12 +201,28 @@ OFFSET_SETS = {
 def max_mode_flops(case, n_offsets):
     """Per-key MFMA work of the max-over-offsets kernel: the method's dot
     products (2*G*|D|*d flops, fp32-equivalent) and the bf16 MFMA flops the
-    kernel issues for them (rows padded to 4 per head and 16 per tile, three
-    bf16 terms per coefficient)."""
+    kernel issues for them.  Issued work follows the library's plan: per 16
+    keys and pass, tiles*d/32*3 trig MFMAs (three bf16 terms per
+    coefficient) and d/32*3 norm MFMAs, 16*16*32*2 flops each; tiles hold the
+    (head, offset) rows with each head's rows rounded up to 4 (one lane
+    slot) or, when one head exceeds the LDS budget, to 16 (all four)."""
     G, d = case.shape.group, case.shape.head_dim
-    dp = (n_offsets + 3) // 4 * 4
-    rows = (G * dp + 15) // 16 * 16
-    return 2 * G * n_offsets * d, 3 * 2 * rows * d
+    steps = d // 32
+    max_tiles = (160 * 1024) // (steps * 3 * 64 * 16) - 1
+    tph = (n_offsets + 3) // 4
+    if tph <= max_tiles:
+        hp_max = min(G, 4 * (max_tiles // tph))
+        npass = -(-G // hp_max)
+        hp = -(-G // npass)
+        tiles = -(-hp // 4) * tph
+    else:
+        tph = (n_offsets + 15) // 16
+        hp_max = min(G, max_tiles // tph)
+        npass = -(-G // hp_max)
+        hp = -(-G // npass)
+        tiles = hp * tph
+    mfma_per_16_keys = npass * (tiles * steps * 3 + steps * 3)
+    return 2 * G * n_offsets * d, mfma_per_16_keys * 16 * 16 * 32 * 2 // 16
 
 
 def algorithmic_bytes(case):
@@ -222,9 +242,10 @@ def algorithmic_bytes(case):
     return keys, score, sel
 
 
-def cpu_baseline(case, max_seconds=30.0):
+def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean"):
     """The oracle as it stands (fp64, term by term) on whole units of the same
-    workload, one after another, on one host thread."""
+    workload, one after another, on one host thread (with the same offset
+    set and reduction as the GPU line)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -245,7 +266,9 @@ def cpu_baseline(case, max_seconds=30.0):
             score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, float(case.cur_pos[0]),
                                   qc[..., 0] + 1j * qc[..., 1],
                                   case.q_absmean[0, g * G:(g + 1) * G].cpu().double().numpy(),
-                                  case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy(), om)[0]
+                                  case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy(), om,
+                                  reduce=reduce,
+                                  **({} if offsets is None else {"offsets": offsets}))[0]
             kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
             O.compact_rows(kbits, kept)
             O.compact_rows(vrows, kept)
@@ -257,7 +280,9 @@ def cpu_baseline(case, max_seconds=30.0):
     dt = time.perf_counter() - t0
     return {"value": keys / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} unit(s) (sequence 0, layer 0, KV heads 0..{units - 1}) of "
-                      f"{n} keys, G={G}: term-by-term fp64 score, z-score, max, top-B, gather; "
+                      f"{n} keys, G={G}: term-by-term fp64 score ({reduce} over "
+                      f"{len(offsets) if offsets is not None else 17} offsets), z-score, max, "
+                      f"top-B, gather; "
                       f"{dt:.1f} s"}
 
 
@@ -402,14 +427,24 @@ def main():
             "operand pack + max-over-offsets MFMA kernel + z pass" if args.reduce == "max"
             else "operand pack + score kernels")
         if args.reduce == "max":
+            # One row per (head, offset): a dense contraction on the bf16
+            # MFMA.  `achieved` counts the method's dot products once
+            # (2*G*|D|*d per key); the kernel issues more (three bf16 terms
+            # per coefficient, padded rows, the norm term).
             f_alg, f_issued = max_mode_flops(case, len(offs))
             t = float(t_score.mean())
-            out["mfma"] = {"method_tflops": keys * f_alg / t / 1e12,
-                           "issued_bf16_tflops": keys * f_issued / t / 1e12,
-                           "issued_frac_of_bf16_peak": keys * f_issued / t / 1e12 / 2500.0}
+            alg, issued = keys * f_alg / t / 1e12, keys * f_issued / t / 1e12
+            out["roofline"].update({
+                "bound": "mfma", "achieved": alg, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": alg / PEAK_BF16_TFLOPS,
+                "algorithmic_flops_per_launch": keys * f_alg,
+                "issued_bf16_tflops": issued, "issued_frac": issued / PEAK_BF16_TFLOPS,
+                "hbm_gbps": score_gbps})
+            out["roofline"].pop("algorithmic_bytes_per_launch", None)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(case)
+        out["cpu_baseline"] = cpu_baseline(case, offsets=OFFSET_SETS[args.offsets],
+                                           reduce=args.reduce)
     print(json.dumps(out), flush=True)
 
 
