@@ -33,7 +33,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // read it has completed (its event).
 // ---------------------------------------------------------------------------
 constexpr int kSlots = 16;
-constexpr size_t kSlotBytes = 256 * 1024;
+constexpr size_t kSlotBytes = 320 * 1024;  // 8192 sequences of 40-byte plan entries
 
 struct Staging {
   std::mutex mu;
@@ -120,10 +120,22 @@ struct OffsetMode {
   bool max = false;
 };
 
+// Where each unit's rows live.  Packed (stride 0): units of n_s (input) or
+// b_s (output) rows back to back, sequence s from row L*Hkv*cu_len[s] (or
+// its output prefix); this is the public layout.  Strided: every unit of
+// sequence s at row0[s] + (l*Hkv + g)*stride, so units can grow in place
+// (the decode cache).
+struct PlanLayout {
+  int64_t in_stride = 0, out_stride = 0;
+  const int64_t* in_row0 = nullptr;   // [S] host, strided input only
+  const int64_t* out_row0 = nullptr;  // [S] host, strided output only
+};
+
 struct Plan {
   std::vector<SeqInfo> seqs;
   int S = 0, L = 0, Hkv = 0, Hq = 0, G = 0, d = 0, F = 0;
-  int64_t total_rows = 0, total_out = 0;
+  int64_t total_rows = 0, total_out = 0;  // rows spanned by the input / output layout
+  int64_t keys = 0, kept = 0;             // rows that hold keys / kept keys
   int max_n = 0, max_b = 0;
   int64_t tickets = 0;
   // workspace offsets (bytes)
@@ -151,7 +163,7 @@ tri_status check_offsets(const tri_shape* sh, const OffsetMode& om) {
 
 tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
                      const int32_t* cur_pos, const int32_t* budget, Plan& p,
-                     const OffsetMode& om = OffsetMode()) {
+                     const OffsetMode& om = OffsetMode(), const PlanLayout& lay = PlanLayout()) {
   tri_status st = check_shape(sh);
   if (st != TRI_OK) return st;
   st = check_offsets(sh, om);
@@ -191,8 +203,10 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");
     if (n > (int64_t)0x7fffffff / 2) return fail(TRI_ERR_UNSUPPORTED, "sequence too long");
     SeqInfo& si = p.seqs[s];
-    si.row_base = LH * cu_len[s];
+    si.row_base = lay.in_stride ? lay.in_row0[s] : LH * cu_len[s];
     si.n = (int32_t)n;
+    si.in_stride = (int32_t)(lay.in_stride ? lay.in_stride : n);
+    if (n > si.in_stride) return fail(TRI_ERR_INVALID_ARGUMENT, "unit longer than its stride");
     int64_t b = 0;
     if (budget) {
       if (budget[s] < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "budget must be >= 0");
@@ -201,15 +215,19 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     si.b = (int32_t)b;
     if (n > p.max_n) p.max_n = (int)n;
     if (b > p.max_b) p.max_b = (int)b;
-    si.out_base = LH * out_acc;
+    si.out_base = lay.out_stride ? lay.out_row0[s] : LH * out_acc;
+    si.out_stride = (int32_t)(lay.out_stride ? lay.out_stride : b);
+    if (b > si.out_stride) return fail(TRI_ERR_INVALID_ARGUMENT, "budget above the output stride");
+    p.total_rows = std::max(p.total_rows, si.row_base + LH * si.in_stride);
+    p.total_out = std::max(p.total_out, si.out_base + LH * si.out_stride);
+    p.keys += LH * n;
+    p.kept += LH * b;
     out_acc += b;
     si.p_q = cur_pos ? cur_pos[s] : 0;
     si.chunk_base = (int32_t)ticket_acc;
     ticket_acc += LH * ((n + p.chunk - 1) / p.chunk);
     if (ticket_acc > 0x7fffffff) return fail(TRI_ERR_UNSUPPORTED, "batch too large for one call");
   }
-  p.total_rows = S > 0 ? LH * cu_len[S] : 0;
-  p.total_out = LH * out_acc;
   p.tickets = ticket_acc;
 
   size_t off = 0;
@@ -315,7 +333,7 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
   tri_status st = make_plan(shape, num_seqs, cu_len, cur_pos, nullptr, p, om);
   if (st != TRI_OK) return st;
   if (num_seqs > 0 && !cur_pos) return fail(TRI_ERR_INVALID_ARGUMENT, "cur_pos is NULL");
-  if (p.total_rows == 0) return TRI_OK;
+  if (p.keys == 0) return TRI_OK;
   if (!k || !q_centre || !q_absmean || !q_R || !scores)
     return fail(TRI_ERR_INVALID_ARGUMENT, "k, statistics and scores must be non-NULL");
   if (!aligned16(k)) return fail(TRI_ERR_INVALID_ARGUMENT, "k must be 16-byte aligned");
@@ -403,7 +421,7 @@ tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs, const in
   if ((k == nullptr) != (k_out == nullptr) || (v == nullptr) != (v_out == nullptr) ||
       (k_pos == nullptr) != (pos_out == nullptr))
     return fail(TRI_ERR_INVALID_ARGUMENT, "k/k_out, v/v_out and k_pos/pos_out come in pairs");
-  if (p.total_out == 0) return TRI_OK;
+  if (p.kept == 0) return TRI_OK;
   if (!scores || !kept_idx)
     return fail(TRI_ERR_INVALID_ARGUMENT, "scores and kept_idx must be non-NULL");
   if ((k && (!aligned16(k) || !aligned16(k_out))) || (v && (!aligned16(v) || !aligned16(v_out))))

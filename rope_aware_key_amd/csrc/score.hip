@@ -52,7 +52,7 @@ __device__ __forceinline__ Ticket decode_ticket(const SeqInfo* seqs, int S, int 
   k.c = local % k.nch;
   k.key0 = k.c * kScoreChunk;
   k.nkeys = min(kScoreChunk, si.n - k.key0);
-  k.row0 = si.row_base + (int64_t)k.lg * si.n;
+  k.row0 = si.row_base + (int64_t)k.lg * si.in_stride;
   return k;
 }
 

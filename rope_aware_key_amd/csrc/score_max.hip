@@ -108,7 +108,7 @@ __device__ __forceinline__ MaxTicket decode_max_ticket(const SeqInfo* seqs, int 
   const int c = local % nch;
   k.key0 = c * kScoreChunk;
   k.nkeys = min(kScoreChunk, si.n - k.key0);
-  k.row0 = si.row_base + (int64_t)k.lg * si.n;
+  k.row0 = si.row_base + (int64_t)k.lg * si.in_stride;
   k.unit = (int64_t)k.s * LH + k.lg;
   return k;
 }

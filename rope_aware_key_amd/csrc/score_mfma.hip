@@ -138,7 +138,7 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
   ck.nkeys_unit = si.n;
   const int key0 = ck.c * ch;
   ck.nkeys = min(ch, si.n - key0);
-  ck.row0 = si.row_base + (int64_t)ck.lg * si.n + key0;
+  ck.row0 = si.row_base + (int64_t)ck.lg * si.in_stride + key0;
   ck.unit = (int64_t)ck.s * L * Hkv + ck.lg;
   return ck;
 }

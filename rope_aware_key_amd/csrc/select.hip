@@ -38,8 +38,8 @@ __global__ __launch_bounds__(kSelThreads) void select_global_kernel(
   const SeqInfo si = seqs[s];
   const int n = si.n, b = si.b;
   if (b <= 0) return;
-  const float* in = scores + si.row_base + (int64_t)lg * n;
-  int32_t* out = kept + si.out_base + (int64_t)lg * b;
+  const float* in = scores + si.row_base + (int64_t)lg * si.in_stride;
+  int32_t* out = kept + si.out_base + (int64_t)lg * si.out_stride;
   if (b >= n) {
     for (int i = tid; i < n; i += kSelThreads) out[i] = i;
     return;
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(NT) void select_lds_kernel(
   const SeqInfo si = seqs[s];
   const int n = si.n, b = si.b;
   if (b <= 0) return;
-  const float* in = scores + si.row_base + (int64_t)lg * n;
-  int32_t* out = kept + si.out_base + (int64_t)lg * b;
+  const float* in = scores + si.row_base + (int64_t)lg * si.in_stride;
+  int32_t* out = kept + si.out_base + (int64_t)lg * si.out_stride;
   if (b >= n) {
     for (int i = tid; i < n; i += NT) out[i] = i;
     return;
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(
   const SeqInfo si = seqs[s];
   const int n = si.n, b = si.b;
   if (b <= 0) return;
-  const float* in = scores + si.row_base + (int64_t)lg * n;
-  int32_t* out = kept + si.out_base + (int64_t)lg * b;
+  const float* in = scores + si.row_base + (int64_t)lg * si.in_stride;
+  int32_t* out = kept + si.out_base + (int64_t)lg * si.out_stride;
   if (b >= n) {
     for (int i = tid; i < n; i += NT) out[i] = i;
     return;
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(256) void compact_kernel(
   const int tid = threadIdx.x;
   const int sub = tid / lpr, part = tid - sub * lpr;
   if (sub >= rows_per_pass) return;
-  const int64_t out0 = si.out_base + (int64_t)lg * b;
-  const int64_t in0 = si.row_base + (int64_t)lg * si.n;
+  const int64_t out0 = si.out_base + (int64_t)lg * si.out_stride;
+  const int64_t in0 = si.row_base + (int64_t)lg * si.in_stride;
 #pragma unroll 4
   for (int r = r0 + sub; r < r1; r += rows_per_pass) {
     const int32_t idx = kept[out0 + r];

@@ -9,14 +9,16 @@ namespace tri {
 // Per-sequence plan entry, built on the host from cu_len / cur_pos / budget
 // and uploaded once per call.
 struct SeqInfo {
-  int64_t row_base;    // first input row of the sequence: L*Hkv*cu_len[s]
-  int64_t out_base;    // first output row: L*Hkv*cu_b[s], cu_b = prefix of b
+  int64_t row_base;    // first input row of the sequence (packed: L*Hkv*cu_len[s])
+  int64_t out_base;    // first output row (packed: L*Hkv*cu_b[s], cu_b = prefix of b)
   int32_t n;           // keys per unit
   int32_t b;           // kept keys per unit, min(budget, n)
   int32_t p_q;         // current query position
   int32_t chunk_base;  // first score ticket of the sequence
+  int32_t in_stride;   // input rows from one unit of the sequence to the next (packed: n)
+  int32_t out_stride;  // output rows from one unit to the next (packed: b)
 };
-static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
+static_assert(sizeof(SeqInfo) == 40, "SeqInfo layout");
 
 // Keys per score work-group ticket.
 constexpr int kScoreChunk = 1024;
