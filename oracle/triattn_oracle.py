@@ -28,6 +28,13 @@ Sources (cited by page title and the section or equation on that page):
 * [evict]     jaedaily.cn KV-cache compression tutorial, eviction step: the
               ``evict_kv_cache`` snippet (top-k, then sort the kept indices so
               the time order is preserved, then gather keys and values).
+* [stream]    same tutorial page, streaming-generation paragraph: each decode
+              step appends the new token's K and V, eviction runs when the
+              cache exceeds the budget, and the most recent r tokens are
+              protected; its renormalisation paragraph keeps attention-sink
+              tokens (e.g. [BOS]).
+* [trigger]   hyper.ai summary, section "方法": scoring and pruning run once
+              every 128 generated tokens.
 
 Readings where the pages are silent or disagree (each is a choice, listed
 again in the design notes):
@@ -44,6 +51,11 @@ again in the design notes):
   unit; sigma = 0 gives z = 0.  Query heads [gG, (g+1)G) belong to KV head g.
 * Ties in the top-B are broken by the lower position (= lower index, since
   positions increase within a unit); -0.0 equals +0.0; NaN ranks below -inf.
+* Decode loop: a unit is pruned to B when it reaches B + interval keys
+  (interval 128), scored at the position of its newest key; the first
+  `sink` and the last `recent` keys are kept whatever their score and count
+  against B; the other B - sink - recent are the top of the remaining keys
+  by the same ranking as the top-B.
 """
 
 from __future__ import annotations
@@ -342,3 +354,72 @@ def out_rows(cu_len, budget, L: int, Hkv: int, s: int, l: int, g: int):
     cu_b = np.concatenate([[0], np.cumsum(b)]).astype(np.int64)
     start = L * Hkv * int(cu_b[s]) + (l * Hkv + g) * b[s]
     return start, b[s]
+
+
+# --------------------------------------------------------------------------
+# Decode loop: append, prune every `interval` tokens, keep sink and recent
+# keys  [stream], [trigger]
+# --------------------------------------------------------------------------
+def protected_mask(n: int, sink: int, recent: int) -> np.ndarray:
+    """Keys that are always kept: the first `sink` and the last `recent`."""
+    i = np.arange(n)
+    return (i < sink) | (i >= n - recent)
+
+
+def select_protected(scores: np.ndarray, budget: int, sink: int, recent: int) -> np.ndarray:
+    """Kept indices (ascending): every protected key, plus the top
+    b - (#protected) of the other keys ranked as in select_topb, with
+    b = min(budget, n) and #protected <= b."""
+    s = np.asarray(scores)
+    n = s.shape[0]
+    b = max(0, min(int(budget), n))
+    prot = protected_mask(n, sink, recent)
+    n_prot = int(prot.sum())
+    if n_prot > b:
+        raise ValueError("more protected keys than the budget")
+    free = np.nonzero(~prot)[0]
+    chosen = free[select_topb(s[free], b - n_prot)]
+    return np.sort(np.concatenate([np.nonzero(prot)[0], chosen]))
+
+
+class DecodeUnit:
+    """One (sequence, layer, KV head) cache in the decode loop: bf16 key and
+    value rows (raw 16-bit patterns) and int positions, in time order."""
+
+    def __init__(self, k_bits, v_bits, pos):
+        self.k = np.asarray(k_bits, dtype=np.uint16).reshape(len(pos), -1)
+        self.v = np.asarray(v_bits, dtype=np.uint16).reshape(len(pos), -1)
+        self.pos = np.asarray(pos, dtype=np.int64)
+
+    def __len__(self):
+        return len(self.pos)
+
+    def append(self, k_row, v_row, p):
+        self.k = np.vstack([self.k, np.asarray(k_row, dtype=np.uint16)[None]])
+        self.v = np.vstack([self.v, np.asarray(v_row, dtype=np.uint16)[None]])
+        self.pos = np.append(self.pos, int(p))
+
+    def scores(self, centre, absmean, R, omega, offsets=OFFSETS, reduce="mean"):
+        """Final scores of every key, the query at the newest key's position."""
+        return unit_scores(bf16_bits_to_f64(self.k), self.pos.astype(np.float64),
+                           float(self.pos[-1]), centre, absmean, R, omega, offsets,
+                           reduce=reduce)[0]
+
+    def prune(self, kept):
+        kept = np.asarray(kept, dtype=np.int64)
+        self.k, self.v, self.pos = (compact_rows(self.k, kept), compact_rows(self.v, kept),
+                                    compact_rows(self.pos, kept))
+
+
+def decode_step(unit: DecodeUnit, k_row, v_row, p, budget, interval, sink, recent,
+                score_fn):
+    """Append one token; if the unit now holds budget + interval keys, score
+    it (score_fn(unit) -> scores) and keep select_protected of them.
+    Returns the scores used, or None when no prune ran."""
+    unit.append(k_row, v_row, p)
+    if len(unit) < budget + interval:
+        return None
+    sc = score_fn(unit)
+    unit.prune(select_protected(sc, budget, sink, recent))
+    return sc
+

@@ -9,6 +9,8 @@ import json
 import math
 import os
 
+import itertools
+
 import numpy as np
 import pytest
 
@@ -442,3 +444,118 @@ def test_max_reduction_invariants():
     np.testing.assert_allclose(one_max, one_mean, rtol=1e-12, atol=1e-12)
     rep = O.OFFSETS + O.OFFSETS[:3]
     np.testing.assert_array_equal(O.score_factored(k_post, p_q, centre, absmean, R, om, rep, "max"), mx)
+
+
+# ---------------------------------------------------------------- decode loop
+def _select_protected_bruteforce(scores, budget, sink, recent):
+    """Every b-subset that holds all protected keys and in which each kept
+    unprotected key beats each dropped key (same ranking as the top-B)."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = len(s)
+    b = min(budget, n)
+    prot = {i for i in range(n) if i < sink or i >= n - recent}
+
+    def beats(i, j):
+        if np.isnan(s[i]) and np.isnan(s[j]):
+            return i < j
+        if np.isnan(s[i]):
+            return False
+        if np.isnan(s[j]):
+            return True
+        return s[i] > s[j] or (s[i] == s[j] and i < j)
+
+    found = []
+    for sub in itertools.combinations(range(n), b):
+        kept = set(sub)
+        if not prot <= kept:
+            continue
+        free_kept = kept - prot
+        dropped = set(range(n)) - kept
+        if all(beats(i, j) for i in free_kept for j in dropped):
+            found.append(np.array(sub))
+    assert len(found) == 1
+    return found[0]
+
+
+def test_select_protected_matches_enumeration():
+    g = np.random.default_rng(21)
+    pool = np.array([0.0, -0.0, 1.0, 1.0, -2.0, np.inf, -np.inf, np.nan, 3.5])
+    for _ in range(300):
+        n = int(g.integers(1, 9))
+        sink = int(g.integers(0, 3))
+        recent = int(g.integers(0, 3))
+        prot = len({i for i in range(n) if i < sink or i >= n - recent})
+        budget = int(g.integers(prot, n + 2))
+        sc = g.choice(pool, size=n)
+        np.testing.assert_array_equal(O.select_protected(sc, budget, sink, recent),
+                                      _select_protected_bruteforce(sc, budget, sink, recent))
+
+
+def test_select_protected_reduces_to_topb_and_to_the_protected_set():
+    g = np.random.default_rng(22)
+    for _ in range(50):
+        n = int(g.integers(5, 60))
+        sc = g.normal(size=n)
+        b = int(g.integers(0, n + 3))
+        np.testing.assert_array_equal(O.select_protected(sc, b, 0, 0), O.select_topb(sc, b))
+        sink, recent = 2, 3
+        if n >= 6:
+            kept = O.select_protected(sc, sink + recent, sink, recent)
+            np.testing.assert_array_equal(kept, np.r_[0:sink, n - recent:n])
+    with pytest.raises(ValueError):
+        O.select_protected(np.zeros(10), 3, 2, 2)
+
+
+def _tiny_unit(n, d=8, seed=0):
+    g = np.random.default_rng(seed)
+    return O.DecodeUnit(g.integers(0, 2 ** 16, size=(n, d)), g.integers(0, 2 ** 16, size=(n, d)),
+                        np.arange(n) * 3)
+
+
+def test_decode_loop_keeps_oldest_and_recent_when_older_scores_higher():
+    """score = -position: the oldest keys win, so after every prune the cache
+    holds the first B - r positions ever seen plus the r newest."""
+    B, I, r = 12, 5, 3
+    u = _tiny_unit(B)
+    seen = list(u.pos)
+    prunes = 0
+    for step in range(23):
+        p = int(u.pos[-1]) + 2
+        seen.append(p)
+        sc = O.decode_step(u, np.full(8, step), np.full(8, step), p, B, I, 0, r,
+                           lambda unit: -unit.pos.astype(float))
+        if sc is not None:
+            prunes += 1
+            assert len(u) == B
+            np.testing.assert_array_equal(u.pos, np.r_[seen[:B - r], seen[-r:]])
+    assert prunes == 23 // I
+
+
+def test_decode_loop_invariants():
+    """Random scores: length sawtooth, prune count, time order, sink keys
+    kept forever, the newest `recent` kept at every prune, kept rows are
+    rows that were in the cache."""
+    B, I, sink, recent = 20, 7, 2, 4
+    u = _tiny_unit(B + 3, seed=5)
+    g = np.random.default_rng(6)
+    first = u.pos[:sink].copy()
+    prunes = 0
+    # prefill longer than B + I - 1 prunes at once in the driver; here the
+    # unit starts below B + I
+    for step in range(60):
+        before = {int(x) for x in u.pos}
+        p = int(u.pos[-1]) + 1 + int(g.integers(0, 3))
+        before.add(p)
+        newest = sorted(before)[-recent:]
+        sc = O.decode_step(u, g.integers(0, 2 ** 16, 8), g.integers(0, 2 ** 16, 8), p, B, I,
+                           sink, recent, lambda unit: g.normal(size=len(unit)))
+        assert np.all(np.diff(u.pos) > 0)
+        np.testing.assert_array_equal(u.pos[:sink], first)
+        if sc is not None:
+            prunes += 1
+            assert len(u) == B
+            assert set(newest) <= {int(x) for x in u.pos}
+            assert {int(x) for x in u.pos} <= before
+        else:
+            assert len(u) < B + I
+    assert prunes == (60 + 3) // I
