@@ -218,6 +218,96 @@ tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Decode-loop driver.
+ *
+ * Keeps the pruned K/V cache of a batch across decode steps.
+ *  - tutorial page, streaming-generation paragraph: every decode step
+ *    appends the new token's K and V to the cache and evicts once the
+ *    cache is over budget; the most recent r tokens are protected.
+ *  - the same page's renormalisation paragraph: attention-sink tokens
+ *    (e.g. [BOS]) are kept.
+ *  - hyper.ai summary, section "方法": score and prune once every 128
+ *    generated tokens.
+ *
+ * Every unit of a sequence holds the same number of keys.  When a
+ * sequence's units reach budget + interval keys (after an append, or at
+ * prefill), the driver prunes them to `budget`:
+ *  - scores come from tri_score, at the position of the newest key (at
+ *    prefill: cur_pos);
+ *  - the first protect_sink and last protect_recent keys are kept
+ *    whatever their score;
+ *  - the other keys compete as in tri_select_compact.
+ * The kept rows are compacted, in time order, into the sequence's other
+ * buffer: each sequence has two ping-pong buffers of budget + interval
+ * rows per unit.
+ *
+ * Memory: the driver allocates with hipMalloc on the current device,
+ * 2 * units * (budget + interval) rows of K, V (bf16) and positions
+ * (int32), plus scores, indices and a score workspace.  A prefill of
+ * sequences longer than budget + interval grows its own scratch.  The
+ * statistics pointers given to tri_decode_create are borrowed and must
+ * outlive the driver.
+ *
+ * Calls on one driver are not thread-safe and must be ordered, normally
+ * on one stream.  All work is queued on `stream`; lengths are tracked on
+ * the host, so no call waits on the device except tri_decode_destroy.
+ */
+typedef struct tri_decode tri_decode; /* opaque */
+
+typedef struct {
+  int32_t budget;         /* B >= 1: keys per unit after a prune            */
+  int32_t interval;       /* >= 1: appends between prunes (128 in the pages) */
+  int32_t protect_sink;   /* >= 0: first keys of a unit always kept         */
+  int32_t protect_recent; /* >= 0: last keys of a unit always kept          */
+} tri_decode_config;      /* protect_sink + protect_recent <= budget        */
+
+typedef struct {
+  int64_t unit_stride;         /* rows from one unit of a sequence to the next
+                                  (budget + interval)                          */
+  const uint16_t* const* k;    /* [num_seqs] device: row 0 of unit 0; unit
+                                  (l, g) at + (l*Hkv + g)*unit_stride rows     */
+  const uint16_t* const* v;    /* [num_seqs] device, same layout               */
+  const int32_t* const* pos;   /* [num_seqs] device positions, same layout     */
+  const int32_t* len;          /* [num_seqs] keys per unit now                 */
+  const float* const* scores;  /* [num_seqs] device scores the sequence's last
+                                  prune used (protected keys read +inf), or
+                                  NULL before its first prune                  */
+  const int64_t* scores_stride;/* [num_seqs] rows between units in `scores`    */
+  int64_t prunes;              /* sequence prunes run so far                   */
+} tri_decode_view;             /* host arrays owned by the driver, valid until
+                                  its next call                                */
+
+/* Create a driver for num_seqs sequences.  q_centre/q_absmean/q_R as for
+ * tri_score (device, borrowed).  Returns TRI_ERR_HIP if allocation fails. */
+tri_status tri_decode_create(const tri_shape* shape, int32_t num_seqs,
+                             const tri_decode_config* config,
+                             const float* q_centre, const float* q_absmean,
+                             const float* q_R, tri_decode** out);
+
+/* Load the caches from packed K, V and positions (the tri_score layout;
+ * cu_len [host][num_seqs+1], cur_pos [host][num_seqs]).  Sequences of at
+ * least budget + interval keys are pruned to budget at once (scored at
+ * cur_pos); the others are copied whole.  Replaces any earlier contents. */
+tri_status tri_decode_prefill(tri_decode* dec, const int64_t* cu_len,
+                              const int32_t* cur_pos, const uint16_t* k,
+                              const uint16_t* v, const int32_t* k_pos,
+                              void* stream);
+
+/* Append one token to every sequence: k_new, v_new [num_seqs][L][Hkv][d]
+ * bf16 (device), pos_new [host][num_seqs] its position (above the
+ * sequence's last one).  Sequences that reach budget + interval keys are
+ * pruned in the same call. */
+tri_status tri_decode_append(tri_decode* dec, const uint16_t* k_new,
+                             const uint16_t* v_new, const int32_t* pos_new,
+                             void* stream);
+
+/* Where the caches are now. */
+tri_status tri_decode_get_view(const tri_decode* dec, tri_decode_view* view);
+
+/* Wait for the device, then free everything the driver allocated. */
+tri_status tri_decode_destroy(tri_decode* dec);
+
 /* Human-readable name of a status code (static string). */
 const char* tri_status_string(tri_status status);
 

@@ -387,9 +387,11 @@ class DecodeUnit:
     value rows (raw 16-bit patterns) and int positions, in time order."""
 
     def __init__(self, k_bits, v_bits, pos):
-        self.k = np.asarray(k_bits, dtype=np.uint16).reshape(len(pos), -1)
-        self.v = np.asarray(v_bits, dtype=np.uint16).reshape(len(pos), -1)
+        """k_bits, v_bits: [n, d] raw bf16 patterns; pos: [n]."""
+        self.k = np.asarray(k_bits, dtype=np.uint16)
+        self.v = np.asarray(v_bits, dtype=np.uint16)
         self.pos = np.asarray(pos, dtype=np.int64)
+        assert self.k.ndim == 2 and self.k.shape == self.v.shape and len(self.k) == len(self.pos)
 
     def __len__(self):
         return len(self.pos)
@@ -399,11 +401,13 @@ class DecodeUnit:
         self.v = np.vstack([self.v, np.asarray(v_row, dtype=np.uint16)[None]])
         self.pos = np.append(self.pos, int(p))
 
-    def scores(self, centre, absmean, R, omega, offsets=OFFSETS, reduce="mean"):
-        """Final scores of every key, the query at the newest key's position."""
-        return unit_scores(bf16_bits_to_f64(self.k), self.pos.astype(np.float64),
-                           float(self.pos[-1]), centre, absmean, R, omega, offsets,
-                           reduce=reduce)[0]
+    def scores(self, centre, absmean, R, omega, offsets=OFFSETS, reduce="mean",
+               factored=False, p_q=None):
+        """Final scores of every key, the query at the newest key's position
+        (or at p_q)."""
+        p = float(self.pos[-1]) if p_q is None else float(p_q)
+        return unit_scores(bf16_bits_to_f64(self.k), self.pos.astype(np.float64), p, centre,
+                           absmean, R, omega, offsets, factored=factored, reduce=reduce)[0]
 
     def prune(self, kept):
         kept = np.asarray(kept, dtype=np.int64)

@@ -60,9 +60,36 @@ _lib.tri_status_string.restype = ctypes.c_char_p
 _lib.tri_last_error.argtypes = []
 _lib.tri_last_error.restype = ctypes.c_char_p
 
+class TriDecodeConfig(ctypes.Structure):
+    _fields_ = [("budget", ctypes.c_int32), ("interval", ctypes.c_int32),
+                ("protect_sink", ctypes.c_int32), ("protect_recent", ctypes.c_int32)]
+
+
+class TriDecodeView(ctypes.Structure):
+    _fields_ = [("unit_stride", ctypes.c_int64), ("k", ctypes.POINTER(ctypes.c_void_p)),
+                ("v", ctypes.POINTER(ctypes.c_void_p)), ("pos", ctypes.POINTER(ctypes.c_void_p)),
+                ("len", ctypes.POINTER(ctypes.c_int32)),
+                ("scores", ctypes.POINTER(ctypes.c_void_p)),
+                ("scores_stride", ctypes.POINTER(ctypes.c_int64)), ("prunes", ctypes.c_int64)]
+
+
+_lib.tri_decode_create.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32,
+                                   ctypes.POINTER(TriDecodeConfig), _P, _P, _P,
+                                   ctypes.POINTER(ctypes.c_void_p)]
+_lib.tri_decode_create.restype = ctypes.c_int
+_lib.tri_decode_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _P]
+_lib.tri_decode_prefill.restype = ctypes.c_int
+_lib.tri_decode_append.argtypes = [_P, _P, _P, _P, _P]
+_lib.tri_decode_append.restype = ctypes.c_int
+_lib.tri_decode_get_view.argtypes = [_P, ctypes.POINTER(TriDecodeView)]
+_lib.tri_decode_get_view.restype = ctypes.c_int
+_lib.tri_decode_destroy.argtypes = [_P]
+_lib.tri_decode_destroy.restype = ctypes.c_int
+
 EXPORTS = ("tri_calibrate", "tri_workspace_bytes", "tri_score", "tri_select_compact",
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
-           "tri_score_offsets")
+           "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
+           "tri_decode_get_view", "tri_decode_destroy")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -172,3 +199,51 @@ def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kep
                                  _ptr(v), _ptr(k_pos), _ptr(kept_idx), _ptr(k_out), _ptr(v_out),
                                  _ptr(pos_out), _ptr(workspace), int(wsb), _stream(stream))
     _check(st, "tri_select_compact")
+
+
+class Decode:
+    """The decode-loop driver (tri_decode_* in include/triattn.h)."""
+
+    def __init__(self, shape: TriShape, num_seqs, budget, interval, q_centre, q_absmean, q_R,
+                 protect_sink=0, protect_recent=0):
+        self.num_seqs = int(num_seqs)
+        cfg = TriDecodeConfig(int(budget), int(interval), int(protect_sink), int(protect_recent))
+        h = ctypes.c_void_p()
+        _check(_lib.tri_decode_create(ctypes.byref(shape), self.num_seqs, ctypes.byref(cfg),
+                                      _ptr(q_centre), _ptr(q_absmean), _ptr(q_R),
+                                      ctypes.byref(h)), "tri_decode_create")
+        self._h = h
+
+    def prefill(self, cu_len, cur_pos, k, v, k_pos, stream=None):
+        self._cu, pcu = _host(cu_len, np.int64)
+        self._cp, pcp = _host(cur_pos, np.int32)
+        _check(_lib.tri_decode_prefill(self._h, pcu, pcp, _ptr(k), _ptr(v), _ptr(k_pos),
+                                       _stream(stream)), "tri_decode_prefill")
+
+    def append(self, k_new, v_new, pos_new, stream=None):
+        self._pn, ppn = _host(pos_new, np.int32)
+        _check(_lib.tri_decode_append(self._h, _ptr(k_new), _ptr(v_new), ppn, _stream(stream)),
+               "tri_decode_append")
+
+    def view(self) -> dict:
+        vw = TriDecodeView()
+        _check(_lib.tri_decode_get_view(self._h, ctypes.byref(vw)), "tri_decode_get_view")
+        n = self.num_seqs
+        return {"unit_stride": int(vw.unit_stride), "k": [vw.k[i] for i in range(n)],
+                "v": [vw.v[i] for i in range(n)], "pos": [vw.pos[i] for i in range(n)],
+                "len": [int(vw.len[i]) for i in range(n)],
+                "scores": [vw.scores[i] for i in range(n)],
+                "scores_stride": [int(vw.scores_stride[i]) for i in range(n)],
+                "prunes": int(vw.prunes)}
+
+    def close(self):
+        if self._h:
+            _check(_lib.tri_decode_destroy(self._h), "tri_decode_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

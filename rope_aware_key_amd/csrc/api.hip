@@ -324,6 +324,58 @@ tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_
 
 namespace {
 
+// Queue the score kernels of a ready plan: upload its sequence table (and
+// offsets), the prologue, then the score path the plan chose.
+hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const uint16_t* k,
+                     const float* q_centre, const float* q_absmean, const float* q_R,
+                     float* scores, float* raw_scores, double* head_stats, char* ws,
+                     hipStream_t s) {
+  SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
+  double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
+  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
+  if (e == hipSuccess)
+    e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq, q_centre, q_absmean, q_R, doff,
+                             om.n, !om.max, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
+                             (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl),
+                             (double*)(ws + p.off_stats), p.n_stat_slots, s);
+  if (e != hipSuccess) return e;
+  float* raw = raw_scores ? raw_scores : (float*)(ws + p.off_raw);
+  if (om.max)
+    return tri::launch_score_max(dseq, p.S, p.L, p.Hkv, p.G, p.d, om.n, p.mp, theta,
+                                 (int)p.tickets, (const double2*)(ws + p.off_P),
+                                 (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E),
+                                 doff, ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
+                                 (double*)(ws + p.off_ustats), scores, head_stats, s);
+  if (p.fused)
+    return tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
+                                   (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
+                                   (const double2*)(ws + p.off_E), ws + p.off_apack, k,
+                                   (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
+                                   scores, raw_scores, head_stats, s);
+  return tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
+                           (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
+                           (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
+                           (double*)(ws + p.off_ustats), scores, head_stats, s);
+}
+
+// Queue select (and the gathers asked for) of a ready plan; the sequence
+// table is uploaded unless the caller already did on this stream.
+hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t* k,
+                              const uint16_t* v, const int32_t* k_pos, int32_t* kept_idx,
+                              uint16_t* k_out, uint16_t* v_out, int32_t* pos_out, char* ws,
+                              hipStream_t s, bool upload_seqs = true) {
+  SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
+  hipError_t e = hipSuccess;
+  if (upload_seqs) e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  const int LH = p.L * p.Hkv;
+  if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, s);
+  if (e == hipSuccess && (k_out || v_out || pos_out))
+    e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
+                            pos_out, s);
+  return e;
+}
+
 tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
                       const int32_t* cur_pos, const uint16_t* k, const float* q_centre,
                       const float* q_absmean, const float* q_R, const OffsetMode& om,
@@ -340,38 +392,8 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
   const size_t need = (raw_scores || p.fused) ? p.off_raw : p.score_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
-  double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
-  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
-  if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
-  if (e == hipSuccess)
-    e = tri::launch_prologue(p.L, p.Hq, p.d, shape->rope_theta, p.S, dseq, q_centre, q_absmean,
-                             q_R, doff, om.n, !om.max, (double2*)(ws + p.off_P),
-                             (float*)(ws + p.off_W), (double2*)(ws + p.off_E),
-                             (uint32_t*)(ws + p.off_ctrl), (double*)(ws + p.off_stats),
-                             p.n_stat_slots, s);
-  float* raw = raw_scores ? raw_scores : (float*)(ws + p.off_raw);
-  if (e != hipSuccess) {
-  } else if (om.max) {
-    e = tri::launch_score_max(dseq, p.S, p.L, p.Hkv, p.G, p.d, om.n, p.mp, shape->rope_theta,
-                              (int)p.tickets, (const double2*)(ws + p.off_P),
-                              (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E), doff,
-                              ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
-                              (double*)(ws + p.off_ustats), scores, head_stats, s);
-  } else if (p.fused) {
-    e = tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
-                                (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
-                                (const double2*)(ws + p.off_E), ws + p.off_apack, k,
-                                (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
-                                scores, raw_scores, head_stats, s);
-  } else {
-    e = tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
-                          (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
-                          (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
-                          (double*)(ws + p.off_ustats), scores, head_stats, s);
-  }
+  const hipError_t e = run_score(p, shape->rope_theta, om, k, q_centre, q_absmean, q_R, scores,
+                                 raw_scores, head_stats, (char*)workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score: ") + hipGetErrorString(e));
   return TRI_OK;
 }
@@ -428,17 +450,300 @@ tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs, const in
     return fail(TRI_ERR_INVALID_ARGUMENT, "K/V buffers must be 16-byte aligned");
   if (!workspace || workspace_bytes < p.select_bytes)
     return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
-  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
-  const int LH = p.L * p.Hkv;
-  if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, s);
-  if (e == hipSuccess && (k_out || v_out || pos_out))
-    e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
-                            pos_out, s);
+  const hipError_t e = run_select_compact(p, scores, k, v, k_pos, kept_idx, k_out, v_out, pos_out,
+                                          (char*)workspace, (hipStream_t)stream);
   if (e != hipSuccess)
     return fail(TRI_ERR_HIP, std::string("select_compact: ") + hipGetErrorString(e));
+  return TRI_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode-loop driver (declared in triattn.h).  Lengths, buffer choice and
+// the prune trigger live on the host; every prune is one plan over the
+// sequences that reached budget + interval keys: tri_score's kernels on the
+// strided cache, the protect pass, then select and compaction into each
+// sequence's other buffer.  Both ping-pong buffers are halves of one
+// allocation, so one plan can read sequences from either half.
+// ---------------------------------------------------------------------------
+struct tri_decode {
+  tri_shape shape{};
+  tri_decode_config cfg{};
+  int S = 0, LH = 0, d = 0;
+  int64_t C = 0;      // unit stride: budget + interval
+  int64_t half = 0;   // rows of one buffer: S * LH * C
+  const float *qc = nullptr, *qa = nullptr, *qr = nullptr;
+  uint16_t *k = nullptr, *v = nullptr;  // [2 * half][d]
+  int32_t* pos = nullptr;               // [2 * half]
+  float* scores = nullptr;              // [2 * half]
+  int32_t* kept = nullptr;              // [2 * half]
+  char* ws = nullptr;                   // score/select workspace
+  size_t ws_bytes = 0;
+  tri::DecodeItem* items = nullptr;     // [S] per-append targets
+  float* pre_scores = nullptr;          // prefill scores (packed input rows)
+  size_t pre_rows = 0;
+  std::vector<int32_t> len;
+  std::vector<uint8_t> cur;             // buffer index per sequence
+  std::vector<const uint16_t*> vk, vv;
+  std::vector<const int32_t*> vpos;
+  std::vector<const float*> vsc;
+  std::vector<int64_t> vsc_stride;
+  int64_t prunes = 0;
+};
+
+namespace {
+
+hipError_t grow(void** p, size_t* have, size_t need) {
+  if (need <= *have) return hipSuccess;
+  if (*p) {
+    hipError_t e = hipFree(*p);
+    if (e != hipSuccess) return e;
+    *p = nullptr;
+    *have = 0;
+  }
+  hipError_t e = hipMalloc(p, need);
+  if (e == hipSuccess) *have = need;
+  return e;
+}
+
+void refresh_view(tri_decode* dec) {
+  for (int s = 0; s < dec->S; ++s) {
+    const int64_t row0 = dec->cur[s] * dec->half + (int64_t)s * dec->LH * dec->C;
+    dec->vk[s] = dec->k + row0 * dec->d;
+    dec->vv[s] = dec->v + row0 * dec->d;
+    dec->vpos[s] = dec->pos + row0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+tri_status tri_decode_create(const tri_shape* shape, int32_t num_seqs,
+                             const tri_decode_config* config, const float* q_centre,
+                             const float* q_absmean, const float* q_R, tri_decode** out) {
+  if (!out) return fail(TRI_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  tri_status st = check_shape(shape);
+  if (st != TRI_OK) return st;
+  if (!config) return fail(TRI_ERR_INVALID_ARGUMENT, "config is NULL");
+  const tri_decode_config c = *config;
+  if (num_seqs < 1) return fail(TRI_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+  if (c.budget < 1 || c.interval < 1 || c.protect_sink < 0 || c.protect_recent < 0)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "budget and interval must be >= 1, protections >= 0");
+  if ((int64_t)c.protect_sink + c.protect_recent > c.budget)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "protect_sink + protect_recent must be <= budget");
+  if ((int64_t)c.budget + c.interval > (int64_t)0x7fffffff / 2)
+    return fail(TRI_ERR_UNSUPPORTED, "budget + interval too large");
+  if (!q_centre || !q_absmean || !q_R)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "statistics must be non-NULL");
+  tri_decode* dec = new tri_decode();
+  dec->shape = *shape;
+  dec->cfg = c;
+  dec->S = num_seqs;
+  dec->LH = shape->num_layers * shape->num_kv_heads;
+  dec->d = shape->head_dim;
+  dec->C = (int64_t)c.budget + c.interval;
+  dec->half = (int64_t)num_seqs * dec->LH * dec->C;
+  dec->qc = q_centre;
+  dec->qa = q_absmean;
+  dec->qr = q_R;
+  dec->len.assign(num_seqs, 0);
+  dec->cur.assign(num_seqs, 0);
+  dec->vk.assign(num_seqs, nullptr);
+  dec->vv.assign(num_seqs, nullptr);
+  dec->vpos.assign(num_seqs, nullptr);
+  dec->vsc.assign(num_seqs, nullptr);
+  dec->vsc_stride.assign(num_seqs, 0);
+  // workspace of a prune of every sequence at once (either half)
+  std::vector<int64_t> cu(num_seqs + 1), r_in(num_seqs), r_out(num_seqs);
+  std::vector<int32_t> bud(num_seqs, c.budget);
+  for (int s = 0; s <= num_seqs; ++s) cu[s] = (int64_t)s * dec->C;
+  for (int s = 0; s < num_seqs; ++s) {
+    r_in[s] = dec->half + (int64_t)s * dec->LH * dec->C;
+    r_out[s] = r_in[s];
+  }
+  PlanLayout lay;
+  lay.in_stride = lay.out_stride = dec->C;
+  lay.in_row0 = r_in.data();
+  lay.out_row0 = r_out.data();
+  Plan p;
+  st = make_plan(shape, num_seqs, cu.data(), nullptr, bud.data(), p, OffsetMode(), lay);
+  if (st != TRI_OK) {
+    delete dec;
+    return st;
+  }
+  const size_t rows = 2 * (size_t)dec->half;
+  const size_t d = (size_t)dec->d;
+  hipError_t e = hipMalloc((void**)&dec->k, rows * d * 2);
+  if (e == hipSuccess) e = hipMalloc((void**)&dec->v, rows * d * 2);
+  if (e == hipSuccess) e = hipMalloc((void**)&dec->pos, rows * 4);
+  if (e == hipSuccess) e = hipMalloc((void**)&dec->scores, rows * 4);
+  if (e == hipSuccess) e = hipMalloc((void**)&dec->kept, rows * 4);
+  if (e == hipSuccess)
+    e = grow((void**)&dec->ws, &dec->ws_bytes, std::max(p.score_bytes, p.select_bytes));
+  if (e == hipSuccess) e = hipMalloc((void**)&dec->items, (size_t)num_seqs * sizeof(tri::DecodeItem));
+  if (e != hipSuccess) {
+    tri_decode_destroy(dec);
+    return fail(TRI_ERR_HIP, std::string("decode create: ") + hipGetErrorString(e));
+  }
+  refresh_view(dec);
+  *out = dec;
+  return TRI_OK;
+}
+
+tri_status tri_decode_prefill(tri_decode* dec, const int64_t* cu_len, const int32_t* cur_pos,
+                              const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
+                              void* stream) {
+  if (!dec) return fail(TRI_ERR_INVALID_ARGUMENT, "driver is NULL");
+  if (!cu_len || !cur_pos) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len and cur_pos are required");
+  const int S = dec->S;
+  std::vector<int32_t> bud(S);
+  std::vector<int64_t> r_out(S);
+  bool any_prune = false;
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = cu_len[s + 1] - cu_len[s];
+    if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");
+    const bool prune = n >= dec->C;
+    any_prune |= prune;
+    bud[s] = prune ? dec->cfg.budget : (int32_t)n;
+    r_out[s] = (int64_t)s * dec->LH * dec->C;  // buffer 0
+  }
+  PlanLayout lay;
+  lay.out_stride = dec->C;
+  lay.out_row0 = r_out.data();
+  Plan p;
+  tri_status st = make_plan(&dec->shape, S, cu_len, cur_pos, bud.data(), p, OffsetMode(), lay);
+  if (st != TRI_OK) return st;
+  if (p.keys > 0 && (!k || !v || !k_pos))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "k, v and k_pos are required");
+  if ((k && !aligned16(k)) || (v && !aligned16(v)))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "K/V buffers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = grow((void**)&dec->ws, &dec->ws_bytes, std::max(p.score_bytes, p.select_bytes));
+  if (e == hipSuccess && any_prune)
+    e = grow((void**)&dec->pre_scores, &dec->pre_rows, (size_t)p.total_rows * sizeof(float));
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode prefill: ") + hipGetErrorString(e));
+  if (p.keys > 0) {
+    float* sc = any_prune ? dec->pre_scores : dec->scores;
+    if (any_prune) {
+      e = run_score(p, dec->shape.rope_theta, OffsetMode(), k, dec->qc, dec->qa, dec->qr, sc,
+                    nullptr, nullptr, dec->ws, s);
+      if (e == hipSuccess)
+        e = tri::launch_protect((const SeqInfo*)(dec->ws + p.off_seq), S, dec->LH,
+                                dec->cfg.protect_sink, dec->cfg.protect_recent, sc, s);
+    }
+    // sequences below the trigger keep every key (b = n: the identity)
+    if (e == hipSuccess)
+      e = run_select_compact(p, sc, k, v, k_pos, dec->kept, dec->k, dec->v, dec->pos, dec->ws, s,
+                             !any_prune);
+    if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode prefill: ") + hipGetErrorString(e));
+  }
+  for (int i = 0; i < S; ++i) {
+    const int64_t n = cu_len[i + 1] - cu_len[i];
+    dec->len[i] = bud[i];
+    dec->cur[i] = 0;
+    dec->vsc[i] = n >= dec->C ? dec->pre_scores + p.seqs[i].row_base : nullptr;
+    dec->vsc_stride[i] = n >= dec->C ? n : 0;
+    if (n >= dec->C) ++dec->prunes;
+  }
+  refresh_view(dec);
+  return TRI_OK;
+}
+
+tri_status tri_decode_append(tri_decode* dec, const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* pos_new, void* stream) {
+  if (!dec) return fail(TRI_ERR_INVALID_ARGUMENT, "driver is NULL");
+  if (!k_new || !v_new || !pos_new)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "k_new, v_new and pos_new are required");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "K/V buffers must be 16-byte aligned");
+  const int S = dec->S;
+  std::vector<tri::DecodeItem> it(S);
+  std::vector<int> hit;
+  for (int s = 0; s < S; ++s) {
+    it[s].row0 = dec->cur[s] * dec->half + (int64_t)s * dec->LH * dec->C + dec->len[s];
+    it[s].pos = pos_new[s];
+    it[s].pad = 0;
+    if (dec->len[s] + 1 == dec->C) hit.push_back(s);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = upload(dec->items, it.data(), it.size() * sizeof(tri::DecodeItem), st);
+  if (e == hipSuccess)
+    e = tri::launch_append(dec->items, S, dec->LH, dec->d, dec->C, k_new, v_new, dec->k, dec->v,
+                           dec->pos, st);
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode append: ") + hipGetErrorString(e));
+  for (int s = 0; s < S; ++s) ++dec->len[s];
+  if (hit.empty()) return TRI_OK;
+
+  // prune the sequences that reached budget + interval keys
+  const int P = (int)hit.size();
+  std::vector<int64_t> cu(P + 1), r_in(P), r_out(P);
+  std::vector<int32_t> cp(P), bud(P, dec->cfg.budget);
+  for (int i = 0; i <= P; ++i) cu[i] = (int64_t)i * dec->C;
+  for (int i = 0; i < P; ++i) {
+    const int s = hit[i];
+    const int64_t off = (int64_t)s * dec->LH * dec->C;
+    r_in[i] = dec->cur[s] * dec->half + off;
+    r_out[i] = (1 - dec->cur[s]) * dec->half + off;
+    cp[i] = pos_new[s];
+  }
+  PlanLayout lay;
+  lay.in_stride = lay.out_stride = dec->C;
+  lay.in_row0 = r_in.data();
+  lay.out_row0 = r_out.data();
+  Plan p;
+  tri_status rs = make_plan(&dec->shape, P, cu.data(), cp.data(), bud.data(), p, OffsetMode(), lay);
+  if (rs != TRI_OK) return rs;
+  // the two halves share one allocation: rows read and rows written never
+  // overlap (input and output halves differ for every sequence)
+  e = run_score(p, dec->shape.rope_theta, OffsetMode(), dec->k, dec->qc, dec->qa, dec->qr,
+                dec->scores, nullptr, nullptr, dec->ws, st);
+  if (e == hipSuccess)
+    e = tri::launch_protect((const SeqInfo*)(dec->ws + p.off_seq), P, dec->LH,
+                            dec->cfg.protect_sink, dec->cfg.protect_recent, dec->scores, st);
+  if (e == hipSuccess)
+    e = run_select_compact(p, dec->scores, dec->k, dec->v, dec->pos, dec->kept, dec->k, dec->v,
+                           dec->pos, dec->ws, st, false);
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode prune: ") + hipGetErrorString(e));
+  for (int i = 0; i < P; ++i) {
+    const int s = hit[i];
+    dec->vsc[s] = dec->scores + r_in[i];
+    dec->vsc_stride[s] = dec->C;
+    dec->cur[s] ^= 1;
+    dec->len[s] = dec->cfg.budget;
+  }
+  dec->prunes += P;
+  refresh_view(dec);
+  return TRI_OK;
+}
+
+tri_status tri_decode_get_view(const tri_decode* dec, tri_decode_view* view) {
+  if (!dec || !view) return fail(TRI_ERR_INVALID_ARGUMENT, "driver and view must be non-NULL");
+  view->unit_stride = dec->C;
+  view->k = dec->vk.data();
+  view->v = dec->vv.data();
+  view->pos = dec->vpos.data();
+  view->len = dec->len.data();
+  view->scores = dec->vsc.data();
+  view->scores_stride = dec->vsc_stride.data();
+  view->prunes = dec->prunes;
+  return TRI_OK;
+}
+
+tri_status tri_decode_destroy(tri_decode* dec) {
+  if (!dec) return TRI_OK;
+  hipError_t e = hipDeviceSynchronize();
+  void* bufs[] = {dec->k, dec->v, dec->pos, dec->scores, dec->kept, dec->ws, dec->items,
+                  dec->pre_scores};
+  for (void* b : bufs)
+    if (b) {
+      const hipError_t f = hipFree(b);
+      if (e == hipSuccess) e = f;
+    }
+  delete dec;
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode destroy: ") + hipGetErrorString(e));
   return TRI_OK;
 }
 

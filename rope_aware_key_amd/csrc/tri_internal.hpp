@@ -132,6 +132,22 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             float* raw, double* chunk_stats, double* unit_stats, float* scores,
                             double* head_stats, hipStream_t st);
 
+// Decode-loop driver: where one appended token of sequence s goes (row of
+// unit 0; unit lg at row0 + lg*stride) and its position.
+struct DecodeItem {
+  int64_t row0;
+  int32_t pos;
+  int32_t pad;
+};
+static_assert(sizeof(DecodeItem) == 16, "DecodeItem layout");
+hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t stride,
+                         const uint16_t* k_new, const uint16_t* v_new, uint16_t* k, uint16_t* v,
+                         int32_t* pos, hipStream_t st);
+// Scores of the first `sink` and last `recent` keys of every pruned unit
+// (b < n) of the plan's sequences -> +inf.
+hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
+                          float* scores, hipStream_t st);
+
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
                          int32_t* kept_idx, hipStream_t st);
 

@@ -9,6 +9,27 @@ import oracle as O
 from synth import Case
 
 
+_HIP = None
+
+
+def dev_read(ptr: int, count: int, dtype) -> np.ndarray:
+    """Copy `count` elements at a raw device address to a host array (after
+    the device is idle), through the HIP runtime torch has loaded."""
+    global _HIP
+    import ctypes
+    import os
+    if _HIP is None:
+        _HIP = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        _HIP.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _HIP.hipMemcpy.restype = ctypes.c_int
+    torch.cuda.synchronize()
+    out = np.empty(count, dtype=dtype)
+    if count:
+        rc = _HIP.hipMemcpy(out.ctypes.data, ptr, out.nbytes, 2)  # device to host
+        assert rc == 0, f"hipMemcpy failed: {rc}"
+    return out
+
+
 def shape_of(case: Case):
     import rope_aware_key_amd as R
     sh = case.shape

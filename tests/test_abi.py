@@ -27,7 +27,9 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert set(names) == {"tri_calibrate", "tri_workspace_bytes", "tri_score",
                           "tri_select_compact", "tri_status_string", "tri_last_error",
-                          "tri_workspace_bytes_offsets", "tri_score_offsets"}
+                          "tri_workspace_bytes_offsets", "tri_score_offsets",
+                          "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
+                          "tri_decode_get_view", "tri_decode_destroy"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -232,3 +234,37 @@ def test_offset_workspaces():
     assert base < mean <= base + 17 * 8 + 256
     assert mx >= rows * 7 * 4 > base
     assert R.tri_workspace_bytes_offsets(sh, cu, 64, "max") > mx
+
+
+
+def test_decode_argument_checks():
+    """Every failing create is rejected before any device allocation."""
+    lib = R._binding._lib
+    sh = R.make_shape(128, 8, 2, 2)
+    h = ctypes.c_void_p()
+
+    def create(budget=64, interval=16, sink=0, recent=0, n=2, stats=FAKE, shape=sh):
+        cfg = R._binding.TriDecodeConfig(budget, interval, sink, recent)
+        return lib.tri_decode_create(ctypes.byref(shape) if shape is not None else None, n,
+                                     ctypes.byref(cfg), stats, stats, stats, ctypes.byref(h))
+
+    assert create(budget=0) == ST["INVALID"]
+    assert create(interval=0) == ST["INVALID"]
+    assert create(sink=-1) == ST["INVALID"]
+    assert create(sink=40, recent=25) == ST["INVALID"]
+    assert "protect" in R.last_error()
+    assert create(n=0) == ST["INVALID"]
+    assert create(stats=None) == ST["INVALID"]
+    assert create(shape=R.make_shape(127, 8, 2, 2)) == ST["INVALID"]
+    assert create(budget=2 ** 30, interval=2 ** 30) == ST["UNSUPPORTED"]
+    assert h.value is None
+    assert lib.tri_decode_create(ctypes.byref(sh), 2, None, FAKE, FAKE, FAKE,
+                                 ctypes.byref(h)) == ST["INVALID"]
+    # calls on a NULL driver
+    assert lib.tri_decode_append(None, FAKE, FAKE, np.zeros(2, np.int32).ctypes.data,
+                                 None) == ST["INVALID"]
+    assert lib.tri_decode_prefill(None, np.zeros(3, np.int64).ctypes.data,
+                                  np.zeros(2, np.int32).ctypes.data, FAKE, FAKE, FAKE,
+                                  None) == ST["INVALID"]
+    assert lib.tri_decode_get_view(None, None) == ST["INVALID"]
+    assert lib.tri_decode_destroy(None) == ST["OK"]
