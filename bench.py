@@ -286,11 +286,158 @@ def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean"):
                       f"{dt:.1f} s"}
 
 
+def decode_cpu_baseline(case, tokens_k, tokens_v, B, interval, sink, recent, max_seconds=30.0):
+    """The oracle's decode loop (term by term, one host thread) on whole units
+    of the same run: each unit starts from its pruned prompt and takes
+    `interval` appends, the last of which prunes.  Returns ms of host time
+    per generated token for the whole batch (per-unit time x units)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    sh = case.shape
+    LH, G = sh.num_layers * sh.num_kv_heads, sh.group
+    om = O.rope_omega(sh.head_dim, sh.rope_theta)
+    done, t_sum = 0, 0.0
+    with threadpool_limits(limits=1):
+        for g in range(sh.num_kv_heads):
+            start, n = case.unit_rows(0, 0, g)
+            qc = case.q_centre[0, g * G:(g + 1) * G].cpu().double().numpy()
+            stats = (qc[..., 0] + 1j * qc[..., 1],
+                     case.q_absmean[0, g * G:(g + 1) * G].cpu().double().numpy(),
+                     case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy())
+            u = O.DecodeUnit(case.k[start:start + n].cpu().numpy().view(np.uint16),
+                             case.v[start:start + n].cpu().numpy().view(np.uint16),
+                             case.k_pos[start:start + n].cpu().numpy())
+            sc = u.scores(*stats, om, p_q=int(case.cur_pos[0]))
+            u.prune(O.select_protected(sc, B, sink, recent))
+            p = int(case.cur_pos[0])
+            t0 = time.perf_counter()
+            for t in range(interval):
+                O.decode_step(u, tokens_k[t, g].cpu().numpy().view(np.uint16),
+                              tokens_v[t, g].cpu().numpy().view(np.uint16), p + t, B, interval,
+                              sink, recent, lambda unit: unit.scores(*stats, om))
+            t_sum += time.perf_counter() - t0
+            done += 1
+            if t_sum > max_seconds:
+                break
+    per_unit_token = t_sum / done / interval
+    units = case.num_units
+    return {"value": per_unit_token * units * 1e3, "unit": "ms/token", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} unit(s) (sequence 0, layer 0, KV heads 0..{done - 1}), each "
+                      f"after its prompt prune: {interval} appends and the prune they trigger, "
+                      f"term-by-term fp64; per-unit time x {units} units; {t_sum:.1f} s"}
+
+
+def run_decode(args):
+    """Decode-loop driver at the decode-window shape: 64 sequences, 32 layers,
+    8 KV heads, G = 4, d = 128; prompts of 3200 keys pruned to 3072 at
+    prefill, then one token per sequence per step, a prune every 128."""
+    import numpy as np
+    import torch
+
+    import rope_aware_key_amd as R
+    import synth
+
+    B, interval, sink, recent = 3072, 128, 4, 64
+    steps = args.steps if args.steps_given else 256
+    warm = args.warmup if args.warmup_given else 0
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print("[bench] building the decode-window prompts", file=sys.stderr, flush=True)
+    case = synth.config_case(2, device=dev)
+    sh = case.shape
+    S, LH, d = case.num_seqs, sh.num_layers * sh.num_kv_heads, sh.head_dim
+    T = warm + steps
+    pos_tok = [torch.arange(T, device=dev, dtype=torch.int64) + int(case.cur_pos[s])
+               for s in range(S)]
+    tok = synth.build_case("decode_tokens", sh, [T] * S, [1] * S, device=dev, seed=0,
+                           positions=pos_tok)
+    # [T][S*LH][d]: token t of unit (s, l, g)
+    idx = (torch.arange(S * LH, device=dev)[None, :] * T + torch.arange(T, device=dev)[:, None])
+    tokens_k, tokens_v = tok.k[idx].contiguous(), tok.v[idx].contiguous()
+    del tok
+    dec = R.Decode(R.make_shape(d, sh.num_q_heads, sh.num_kv_heads, sh.num_layers, sh.rope_theta),
+                   S, B, interval, case.q_centre, case.q_absmean, case.q_R,
+                   protect_sink=sink, protect_recent=recent)
+    stream = torch.cuda.current_stream()
+    cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
+    cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
+    dec.prefill(cu, cp, case.k, case.v, case.k_pos, stream=stream)
+    pos_host = [torch.as_tensor(case.cur_pos.astype(np.int64) + t, dtype=torch.int32)
+                .pin_memory().numpy() for t in range(T)]
+    for t in range(warm):
+        dec.append(tokens_k[t], tokens_v[t], pos_host[t], stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    prunes0 = dec.view()["prunes"]
+    pruning = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        before = dec.view()["len"][0]
+        ev[i][0].record(stream)
+        dec.append(tokens_k[warm + i], tokens_v[warm + i], pos_host[warm + i], stream=stream)
+        ev[i][1].record(stream)
+        pruning.append(dec.view()["len"][0] < before + 1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pr = np.array(pruning)
+    prunes = dec.view()["prunes"] - prunes0
+    dec.close()
+    total = float(ms.sum())
+    prune_ms = float(ms[pr].mean()) if pr.any() else None
+    append_ms = float(ms[~pr].mean()) if (~pr).any() else None
+    units = S * LH
+    # algorithmic bytes of one prune of every sequence: K read by the score,
+    # scores written and read, K and V rows of the kept keys read and
+    # written, positions read and written, indices written
+    C = B + interval
+    prune_bytes = units * (C * d * 2 + 2 * C * 4 + 4 * B * d * 2 + 2 * B * 4 + B * 4)
+    out = {
+        "metric": "decode-loop cache upkeep per generated token (append + amortised prune), 1 MI355X",
+        "value": total / steps,
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": total / steps,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (decode-window prompts: steady-state positions; generated keys drawn "
+                "at the following positions)",
+        "config": {"workload": "decode_loop_3072_plus_128", "batch": S, "layers": sh.num_layers,
+                   "kv_heads": sh.num_kv_heads, "q_heads": sh.num_q_heads, "head_dim": d,
+                   "budget": B, "interval": interval, "protect_sink": sink,
+                   "protect_recent": recent, "units": units},
+        "wall_ms_per_step": wall / steps * 1e3,
+        "breakdown_ms": {"append_step": append_ms, "pruning_step": prune_ms,
+                         "prunes_in_timed_steps": int(prunes)},
+        "roofline": {"bound": "hbm", "kernel": "pruning step (score + protect + select + gather)",
+                     "achieved": prune_bytes / (prune_ms * 1e-3) / 1e9 if prune_ms else None,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": prune_bytes / (prune_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS
+                     if prune_ms else None,
+                     "traffic": None, "algorithmic_bytes_per_launch": prune_bytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle decode loop)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = decode_cpu_baseline(case, tokens_k[:, :LH], tokens_v[:, :LH], B,
+                                                  interval, sink, recent)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode-loop driver at the decode-window shape")
     ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
     ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
@@ -302,6 +449,9 @@ def main():
     ap.add_argument("--traffic", default=None, metavar="DIR",
                     help="write the tri_score traffic JSON (--out) from the counter runs under DIR")
     args = ap.parse_args()
+    args.steps_given, args.warmup_given = args.steps is not None, args.warmup is not None
+    args.steps = 20 if args.steps is None else args.steps
+    args.warmup = 3 if args.warmup is None else args.warmup
     if args.traffic:
         write_traffic(args.traffic, args.out)
         return
@@ -316,6 +466,10 @@ def main():
               "units with no exchange, so N GPUs run N independent copies of this step.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        run_decode(args)
+        return
 
     import numpy as np
     import torch
