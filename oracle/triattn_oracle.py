@@ -35,6 +35,9 @@ Sources (cited by page title and the section or equation on that page):
               tokens (e.g. [BOS]).
 * [trigger]   hyper.ai summary, section "方法": scoring and pruning run once
               every 128 generated tokens.
+* [recon]     shibing624 blog review, Fig. 1(D) (the trig series built from
+              the centres against the real attention logits) and Fig. 7
+              (per-head Pearson correlation of that reconstruction).
 
 Readings where the pages are silent or disagree (each is a choice, listed
 again in the design notes):
@@ -51,6 +54,10 @@ again in the design notes):
   unit; sigma = 0 gives z = 0.  Query heads [gG, (g+1)G) belong to KV head g.
 * Ties in the top-B are broken by the lower position (= lower index, since
   positions increase within a unit); -0.0 equals +0.0; NaN ranks below -inf.
+* Reconstruction diagnostic: per (layer, query head), the Pearson
+  correlation over every (sample query, key) pair of the direct post-RoPE
+  logit q'.k' and S_trig(k, p_q - p_k) built from the query centre; 0 when
+  either side is constant.
 * Decode loop: a unit is pruned to B when it reaches B + interval keys
   (interval 128), scored at the position of its newest key; the first
   `sink` and the last `recent` keys are kept whatever their score and count
@@ -426,4 +433,42 @@ def decode_step(unit: DecodeUnit, k_row, v_row, p, budget, interval, sink, recen
     sc = score_fn(unit)
     unit.prune(select_protected(sc, budget, sink, recent))
     return sc
+
+
+# --------------------------------------------------------------------------
+# Reconstruction diagnostic  [recon], [logit-eq], [Strig-eq]
+# --------------------------------------------------------------------------
+def pearson(x, y) -> float:
+    """Pearson correlation of two equal-length samples from centred fp64
+    sums; 0 when either sample is constant."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    dx, dy = x - x.mean(), y - y.mean()
+    sxx, syy = float(np.sum(dx * dx)), float(np.sum(dy * dy))
+    if sxx == 0.0 or syy == 0.0:
+        return 0.0
+    return float(np.sum(dx * dy)) / np.sqrt(sxx * syy)
+
+
+def trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega):
+    """For one (layer, query head): the direct logits [n_q, n_k], q'_j . k'_i
+    of the post-RoPE vectors, and the reconstruction S_trig(k_i, p_j - p_i)
+    = sum_f |E q_f| |k_f| cos(omega_f Delta + arg E q_f - arg k_f) with k_f
+    the pre-RoPE key band and E q_f = centre [F] complex."""
+    q_post = np.asarray(q_post, dtype=np.float64)
+    k_post = np.asarray(k_post, dtype=np.float64)
+    direct = q_post @ k_post.T
+    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega)
+    c_vec = np.empty(2 * len(centre))
+    c_vec[0::2], c_vec[1::2] = np.real(centre), np.imag(centre)
+    delta = np.asarray(q_pos, dtype=np.float64)[:, None] - np.asarray(k_pos, dtype=np.float64)[None, :]
+    recon = logit_decomposed(c_vec[None, None, :], k_pre[None, :, :], delta, omega)
+    return direct, recon
+
+
+def trig_reconstruction_r(q_post, q_pos, k_post, k_pos, centre, omega) -> float:
+    """Pearson r of the reconstruction against the direct logits, over all
+    (query, key) pairs."""
+    direct, recon = trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega)
+    return pearson(recon, direct)
 

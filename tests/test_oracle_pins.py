@@ -559,3 +559,49 @@ def test_decode_loop_invariants():
         else:
             assert len(u) < B + I
     assert prunes == (60 + 3) // I
+
+
+# ------------------------------------------------- reconstruction diagnostic
+def test_pearson_textbook_values():
+    assert O.pearson([1, 2, 3], [2, 4, 6]) == pytest.approx(1.0, abs=1e-15)
+    assert O.pearson([1, 2, 3], [3, 2, 1]) == pytest.approx(-1.0, abs=1e-15)
+    # dx = dy-permuted (-1.5, -.5, .5, 1.5): sxy = 4, sxx = syy = 5
+    assert O.pearson([1, 2, 3, 4], [1, 3, 2, 4]) == pytest.approx(0.8, abs=1e-15)
+    assert O.pearson([2, 2, 2], [1, 5, 3]) == 0.0
+    g = np.random.default_rng(31)
+    x, y = g.normal(size=500), g.normal(size=500)
+    assert O.pearson(x, y) == pytest.approx(np.corrcoef(x, y)[0, 1], abs=1e-12)
+    assert O.pearson(3 * x + 1, -2 * y + 7) == pytest.approx(-O.pearson(x, y), abs=1e-12)
+
+
+def _diag_case(noise, seed=0, nq=40, nk=60, d=16):
+    g = np.random.default_rng(seed)
+    om = O.rope_omega(d, 1e4)
+    v = g.normal(size=d) + 1.0                      # one pre-RoPE direction
+    q_pre = v[None, :] + noise * g.normal(size=(nq, d))
+    q_pos = g.integers(0, 5000, size=nq).astype(np.float64)
+    k_pos = np.sort(g.choice(4000, size=nk, replace=False)).astype(np.float64)
+    k_pre = g.normal(size=(nk, d)) + 0.5
+    q_post = O.rope_rotate(q_pre, q_pos, om)
+    k_post = O.rope_rotate(k_pre, k_pos, om)
+    centre, _, _ = O.calibrate(q_post[:, None, :], q_pos, om)
+    return q_post, q_pos, k_post, k_pos, centre[0], om
+
+
+def test_reconstruction_is_exact_when_queries_sit_on_their_centre():
+    """Every sample query the same pre-RoPE vector: the centre is that vector
+    and S_trig(k, Delta) is the logit itself (talk page, logit decomposition),
+    so the two arrays agree entry by entry and r = 1."""
+    q_post, q_pos, k_post, k_pos, centre, om = _diag_case(0.0)
+    direct, recon = O.trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, om)
+    np.testing.assert_allclose(recon, direct, rtol=1e-11, atol=1e-11)
+    assert O.trig_reconstruction_r(q_post, q_pos, k_post, k_pos, centre, om) == pytest.approx(1.0, abs=1e-12)
+
+
+def test_reconstruction_degrades_with_query_spread():
+    """Controlled concentration: the more the sample queries scatter around
+    their centre, the lower the correlation (fixed seeds)."""
+    rs = [O.trig_reconstruction_r(*_diag_case(noise, seed=4)) for noise in (0.02, 0.3, 1.0, 4.0)]
+    assert rs[0] > 0.99
+    assert all(a > b for a, b in zip(rs, rs[1:])), rs
+    assert rs[-1] < 0.6
