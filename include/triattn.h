@@ -219,6 +219,37 @@ tri_status tri_select_compact(const tri_shape* shape, int32_t num_seqs,
                               void* stream);
 
 /*
+ * tri_trig_correlation -- reconstruction diagnostic (shibing624 blog
+ * review, Fig. 1(D) and Fig. 7): how well the trig series built from the
+ * query centres follows the real attention logits.  For layer l and query
+ * head h (KV head g = h / G), over every pair of a sample query j and a
+ * key i,
+ *   x_ji = S_trig(k_i, p_j - p_i) = sum_f |E q_f| |k_f| cos(omega_f (p_j - p_i) + arg E q_f - arg k_f)
+ *   y_ji = <q'_j, k'_i>   (post-RoPE logit, unscaled)
+ * (talk page, logit decomposition and S_trig equation), and
+ *   r[l][h] = Pearson(x, y) over all n_q * n_k pairs; 0 if either is constant.
+ *
+ *  q         [L][n_q][H_q][d] bf16 post-RoPE sample queries (tri_calibrate's
+ *            layout) at positions q_pos [n_q] (int32, device).
+ *  k         [L][H_kv][n_k][d] bf16 post-RoPE keys: one sequence in the
+ *            packed layout.  k_pos may be NULL and is not read (the key
+ *            position cancels as in tri_score).
+ *  q_centre  [L][H_q][F][2] as tri_calibrate writes it.
+ *  r         out fp64 [L][H_q].
+ *  workspace at least tri_trig_correlation_workspace_bytes().
+ * head_dim must be a multiple of 32 (TRI_ERR_UNSUPPORTED otherwise).
+ * Sums are fp64 in a fixed order (deterministic).
+ */
+size_t tri_trig_correlation_workspace_bytes(const tri_shape* shape, int64_t n_q);
+
+tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q,
+                                const int32_t* q_pos, int64_t n_q,
+                                const uint16_t* k, const int32_t* k_pos,
+                                int64_t n_k, const float* q_centre, double* r,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * Decode-loop driver.
  *
  * Keeps the pruned K/V cache of a batch across decode steps.

@@ -86,10 +86,17 @@ _lib.tri_decode_get_view.restype = ctypes.c_int
 _lib.tri_decode_destroy.argtypes = [_P]
 _lib.tri_decode_destroy.restype = ctypes.c_int
 
+_lib.tri_trig_correlation_workspace_bytes.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int64]
+_lib.tri_trig_correlation_workspace_bytes.restype = ctypes.c_size_t
+_lib.tri_trig_correlation.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c_int64, _P, _P,
+                                      ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.tri_trig_correlation.restype = ctypes.c_int
+
 EXPORTS = ("tri_calibrate", "tri_workspace_bytes", "tri_score", "tri_select_compact",
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
-           "tri_decode_get_view", "tri_decode_destroy")
+           "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
+           "tri_trig_correlation")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -187,6 +194,22 @@ def tri_score_offsets(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_ab
                                 _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
                                 _stream(stream))
     _check(st, "tri_score_offsets")
+
+
+def tri_trig_correlation_workspace_bytes(shape: TriShape, n_q) -> int:
+    return int(_lib.tri_trig_correlation_workspace_bytes(ctypes.byref(shape), int(n_q)))
+
+
+def tri_trig_correlation(shape: TriShape, q, q_pos, n_q, k, k_pos, n_k, q_centre, r,
+                         workspace=None, workspace_bytes=None, stream=None):
+    """Per-(layer, query head) Pearson r of the trig reconstruction against
+    the direct logits (include/triattn.h)."""
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_trig_correlation(ctypes.byref(shape), _ptr(q), _ptr(q_pos), int(n_q), _ptr(k),
+                                   _ptr(k_pos), int(n_k), _ptr(q_centre), _ptr(r), _ptr(workspace),
+                                   int(wsb), _stream(stream))
+    _check(st, "tri_trig_correlation")
 
 
 def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx, k_out,

@@ -5,8 +5,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libtriattn.so")
-SOURCES = ["api.hip", "calib.hip", "decode.hip", "score.hip", "score_max.hip", "score_mfma.hip",
-           "select.hip"]
+SOURCES = ["api.hip", "calib.hip", "decode.hip", "diag.hip", "score.hip", "score_max.hip",
+           "score_mfma.hip", "select.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

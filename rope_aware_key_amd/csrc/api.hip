@@ -304,6 +304,41 @@ size_t tri_workspace_bytes_offsets(const tri_shape* shape, int32_t num_seqs,
   return p.score_bytes > p.select_bytes ? p.score_bytes : p.select_bytes;
 }
 
+size_t tri_trig_correlation_workspace_bytes(const tri_shape* shape, int64_t n_q) {
+  if (check_shape(shape) != TRI_OK) return 0;
+  if (n_q < 1) {
+    fail(TRI_ERR_INVALID_ARGUMENT, "n_q must be >= 1");
+    return 0;
+  }
+  return tri::trig_corr_workspace_bytes(shape->num_layers, shape->num_q_heads, n_q);
+}
+
+tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q, const int32_t* q_pos,
+                                int64_t n_q, const uint16_t* k, const int32_t* k_pos, int64_t n_k,
+                                const float* q_centre, double* r, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  tri_status st = check_shape(shape);
+  if (st != TRI_OK) return st;
+  if (shape->head_dim % 32 != 0)
+    return fail(TRI_ERR_UNSUPPORTED, "the reconstruction diagnostic needs head_dim % 32 == 0");
+  if (n_q < 1 || n_k < 1) return fail(TRI_ERR_INVALID_ARGUMENT, "n_q and n_k must be >= 1");
+  if (n_q > (int64_t)0x7fffffff / 16 || n_k > (int64_t)0x7fffffff)
+    return fail(TRI_ERR_UNSUPPORTED, "too many samples");
+  if (!q || !q_pos || !k || !q_centre || !r)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "q, q_pos, k, q_centre and r must be non-NULL");
+  if (!aligned16(q) || !aligned16(k))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
+  const size_t need = tri::trig_corr_workspace_bytes(shape->num_layers, shape->num_q_heads, n_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(TRI_ERR_WORKSPACE,
+                "workspace missing or smaller than tri_trig_correlation_workspace_bytes()");
+  hipError_t e = tri::launch_trig_corr(shape->num_layers, shape->num_q_heads, shape->num_kv_heads,
+                                       shape->head_dim, n_q, n_k, shape->rope_theta, q, q_pos, k,
+                                       k_pos, q_centre, (double*)workspace, r, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("trig_correlation: ") + hipGetErrorString(e));
+  return TRI_OK;
+}
+
 tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_t* q_pos,
                          int64_t n_samples, float* q_centre, float* q_absmean, float* q_R,
                          void* stream) {

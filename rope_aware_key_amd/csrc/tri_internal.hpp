@@ -148,6 +148,15 @@ hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t 
 hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
                           float* scores, hipStream_t st);
 
+// Reconstruction diagnostic (d % 32 == 0): per-(layer, query head) Pearson
+// r of the trig series against the direct logits; partial is
+// trig_corr_workspace_bytes() of scratch.
+size_t trig_corr_workspace_bytes(int L, int Hq, int64_t n_q);
+hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t n_k, double theta,
+                            const uint16_t* q, const int32_t* q_pos, const uint16_t* k,
+                            const int32_t* k_pos, const float* q_centre, double* partial,
+                            double* r, hipStream_t st);
+
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
                          int32_t* kept_idx, hipStream_t st);
 

@@ -29,7 +29,8 @@ def test_header_symbols_exported():
                           "tri_select_compact", "tri_status_string", "tri_last_error",
                           "tri_workspace_bytes_offsets", "tri_score_offsets",
                           "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
-                          "tri_decode_get_view", "tri_decode_destroy"}
+                          "tri_decode_get_view", "tri_decode_destroy",
+                          "tri_trig_correlation_workspace_bytes", "tri_trig_correlation"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -268,3 +269,25 @@ def test_decode_argument_checks():
                                   None) == ST["INVALID"]
     assert lib.tri_decode_get_view(None, None) == ST["INVALID"]
     assert lib.tri_decode_destroy(None) == ST["OK"]
+
+
+
+def test_trig_correlation_argument_checks():
+    sh = R.make_shape(128, 8, 2, 2)
+    need = R.tri_trig_correlation_workspace_bytes(sh, 100)
+    assert need == 2 * 8 * 7 * 5 * 8          # L * Hq * ceil(100/16) tiles * 5 sums
+    assert R.tri_trig_correlation_workspace_bytes(sh, 0) == 0
+
+    def call(shape=sh, q=_Fake(), qp=_Fake(), nq=100, k=_Fake(), nk=50, c=_Fake(), r=_Fake(),
+             ws=None, wsb=0):
+        return R.tri_trig_correlation(shape, q, qp, nq, k, None, nk, c, r, workspace=ws,
+                                      workspace_bytes=wsb, stream=0)
+
+    assert _status(call, shape=R.make_shape(48, 8, 2, 2)) == ST["UNSUPPORTED"]
+    assert _status(call, nq=0) == ST["INVALID"]
+    assert _status(call, nk=0) == ST["INVALID"]
+    assert _status(call, q=None) == ST["INVALID"]
+    assert _status(call, r=None) == ST["INVALID"]
+    assert _status(call, k=_Fake(FAKE + 4)) == ST["INVALID"]
+    assert _status(call) == ST["WORKSPACE"]
+    assert _status(call, ws=_Fake(), wsb=need - 1) == ST["WORKSPACE"]

@@ -1,0 +1,73 @@
+"""tri_trig_correlation (reconstruction diagnostic) against the oracle.
+
+Both sides get the same fp32 query centres (the oracle's calibration of the
+sample queries, rounded to fp32) and the same bf16 queries and keys.  r is
+a ratio of fp64 sums of fp32-accurate products: |r_gpu - r_ref| <= 2e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth.cases import _calibration_queries
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(shape, n_q, n_k, R_Q, seed):
+    import rope_aware_key_amd as R
+    q, q_pos = _calibration_queries(shape, n_q, DEV, seed, R_Q=R_Q)
+    case = synth.build_case("diag", shape, (n_k,), (1,), device=DEV, seed=seed, with_values=False)
+    L, Hq, Hkv, d = shape.num_layers, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    om = O.rope_omega(d, shape.rope_theta)
+    qb = O.bf16_bits_to_f64(q.cpu().numpy().view(np.uint16))           # [L, n_q, Hq, d]
+    qp = q_pos.cpu().numpy().astype(np.float64)
+    centre = np.zeros((L, Hq, d // 2, 2), np.float32)
+    for l in range(L):
+        c, _, _ = O.calibrate(qb[l], qp, om)
+        centre[l, ..., 0], centre[l, ..., 1] = c.real, c.imag
+    qc = torch.as_tensor(centre, device=DEV)
+    sh = R.make_shape(d, Hq, Hkv, L, shape.rope_theta)
+    ws = torch.empty(R.tri_trig_correlation_workspace_bytes(sh, n_q), dtype=torch.uint8, device=DEV)
+    r = torch.full((L, Hq), float("nan"), dtype=torch.float64, device=DEV)
+    R.tri_trig_correlation(sh, q, q_pos, n_q, case.k, case.k_pos, n_k, qc, r, workspace=ws)
+    torch.cuda.synchronize()
+    r = r.cpu().numpy()
+    kb = O.bf16_bits_to_f64(case.k.cpu().numpy().view(np.uint16))
+    kp = case.k_pos.cpu().numpy().astype(np.float64)
+    G = shape.group
+    ref = np.zeros((L, Hq))
+    for l in range(L):
+        for h in range(Hq):
+            u = l * Hkv + h // G
+            c = centre[l, h, :, 0].astype(np.float64) + 1j * centre[l, h, :, 1].astype(np.float64)
+            ref[l, h] = O.trig_reconstruction_r(qb[l, :, h, :], qp, kb[u * n_k:(u + 1) * n_k],
+                                                kp[u * n_k:(u + 1) * n_k], c, om)
+    return r, ref
+
+
+@pytest.mark.parametrize("R_Q", [0.99, 0.8, 0.5])
+def test_trig_correlation_matches_oracle(R_Q):
+    """d = 128, G = 4, two layers; 100 queries and 300 keys (ragged tiles)."""
+    shape = synth.Shape(128, 8, 2, 2)
+    r, ref = _run(shape, 100, 300, R_Q, seed=int(R_Q * 100))
+    np.testing.assert_allclose(r, ref, rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("d,G,n_q,n_k", [(64, 2, 17, 33), (256, 1, 64, 64), (32, 8, 130, 15)])
+def test_trig_correlation_shapes(d, G, n_q, n_k):
+    shape = synth.Shape(d, 2 * G, 2, 1)
+    r, ref = _run(shape, n_q, n_k, 0.9, seed=d)
+    np.testing.assert_allclose(r, ref, rtol=0, atol=2e-5)
+
+
+def test_trig_correlation_tracks_concentration():
+    """Tighter query concentration, better reconstruction (per head)."""
+    shape = synth.Shape(128, 4, 1, 1)
+    hi, _ = _run(shape, 200, 500, 0.98, seed=1)
+    lo, _ = _run(shape, 200, 500, 0.6, seed=1)
+    assert np.all(hi > lo)
+    assert np.all(hi > 0.9)
