@@ -86,11 +86,17 @@ typedef struct {
  *  q_absmean out [L][H_q][F] fp32: E[|q_f|].
  *  q_R       out [L][H_q][F] fp32: R_f = |E[q_f]| / E[|q_f|]; 1 where
  *            E[|q_f|] = 0.
- * Sums are taken in fp64 in sample order (deterministic).  n_samples >= 1.
+ *  workspace device scratch of at least tri_calibrate_workspace_bytes(),
+ *            16-byte aligned.
+ * Sums are fp64: in sample order within chunks of 256 samples, then over
+ * the chunks in order (deterministic).  n_samples >= 1.
  */
+size_t tri_calibrate_workspace_bytes(const tri_shape* shape, int64_t n_samples);
+
 tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q,
                          const int32_t* q_pos, int64_t n_samples,
                          float* q_centre, float* q_absmean, float* q_R,
+                         void* workspace, size_t workspace_bytes,
                          void* stream);
 
 /*

@@ -38,7 +38,10 @@ class TriShape(ctypes.Structure):
 
 
 _P = ctypes.c_void_p
-_lib.tri_calibrate.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c_int64, _P, _P, _P, _P]
+_lib.tri_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int64]
+_lib.tri_calibrate_workspace_bytes.restype = ctypes.c_size_t
+_lib.tri_calibrate.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c_int64, _P, _P, _P, _P,
+                               ctypes.c_size_t, _P]
 _lib.tri_calibrate.restype = ctypes.c_int
 _lib.tri_workspace_bytes.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P]
 _lib.tri_workspace_bytes.restype = ctypes.c_size_t
@@ -92,7 +95,7 @@ _lib.tri_trig_correlation.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c
                                       ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_trig_correlation.restype = ctypes.c_int
 
-EXPORTS = ("tri_calibrate", "tri_workspace_bytes", "tri_score", "tri_select_compact",
+EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_bytes", "tri_score", "tri_select_compact",
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
@@ -149,9 +152,23 @@ def last_error() -> str:
     return _lib.tri_last_error().decode()
 
 
-def tri_calibrate(shape: TriShape, q, q_pos, n_samples, q_centre, q_absmean, q_R, stream=None):
+def tri_calibrate_workspace_bytes(shape: TriShape, n_samples) -> int:
+    return int(_lib.tri_calibrate_workspace_bytes(ctypes.byref(shape), int(n_samples)))
+
+
+def tri_calibrate(shape: TriShape, q, q_pos, n_samples, q_centre, q_absmean, q_R, workspace=None,
+                  workspace_bytes=None, stream=None):
+    """workspace: device tensor of tri_calibrate_workspace_bytes(); when None
+    one is allocated through torch on q's device."""
+    if workspace is None and workspace_bytes is None and hasattr(q, "device"):
+        import torch
+        need = tri_calibrate_workspace_bytes(shape, n_samples)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
     st = _lib.tri_calibrate(ctypes.byref(shape), _ptr(q), _ptr(q_pos), int(n_samples),
-                            _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), _stream(stream))
+                            _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), _ptr(workspace), int(wsb),
+                            _stream(stream))
     _check(st, "tri_calibrate")
 
 

@@ -339,18 +339,34 @@ tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q, const
   return TRI_OK;
 }
 
+size_t tri_calibrate_workspace_bytes(const tri_shape* shape, int64_t n_samples) {
+  if (check_shape(shape) != TRI_OK) return 0;
+  if (n_samples < 1) {
+    fail(TRI_ERR_INVALID_ARGUMENT, "n_samples must be >= 1");
+    return 0;
+  }
+  return tri::calibrate_workspace_bytes(shape->num_layers, shape->num_q_heads, shape->head_dim,
+                                        n_samples);
+}
+
 tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_t* q_pos,
                          int64_t n_samples, float* q_centre, float* q_absmean, float* q_R,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   tri_status st = check_shape(shape);
   if (st != TRI_OK) return st;
   if (n_samples < 1) return fail(TRI_ERR_INVALID_ARGUMENT, "n_samples must be >= 1");
   if (!q || !q_centre || !q_absmean || !q_R)
     return fail(TRI_ERR_INVALID_ARGUMENT, "q and every output must be non-NULL");
   if (((uintptr_t)q & 3u) != 0) return fail(TRI_ERR_INVALID_ARGUMENT, "q must be 4-byte aligned");
+  const size_t need = tri::calibrate_workspace_bytes(shape->num_layers, shape->num_q_heads,
+                                                     shape->head_dim, n_samples);
+  if (!workspace || workspace_bytes < need)
+    return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_calibrate_workspace_bytes()");
+  if (((uintptr_t)workspace & 15u) != 0)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   hipError_t e = tri::launch_calibrate(shape->num_layers, shape->num_q_heads, shape->head_dim,
                                        shape->rope_theta, q, q_pos, n_samples, q_centre,
-                                       q_absmean, q_R, (hipStream_t)stream);
+                                       q_absmean, q_R, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("calibrate: ") + hipGetErrorString(e));
   return TRI_OK;
 }

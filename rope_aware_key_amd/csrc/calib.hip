@@ -19,53 +19,115 @@ namespace tri {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// One thread per (layer, query head, band); samples are summed in order in
-// fp64, so the result does not depend on the launch shape.
-__global__ __launch_bounds__(256) void calibrate_kernel(
-    int L, int Hq, int d, double theta, const uint16_t* __restrict__ q,
-    const int32_t* __restrict__ q_pos, int64_t N, float* __restrict__ centre,
-    float* __restrict__ absmean, float* __restrict__ R) {
-  const int F = d >> 1;
+// Calibration runs in three steps, all deterministic:
+//  1. a phasor table e^{-i omega_f p_t} per (sample, band), formed in fp64
+//     and stored as fp32 (relative error ~6e-8): the de-rotation angle
+//     depends on the band and the sample only, so one sincos serves every
+//     layer and head;
+//  2. one work-group per (layer, chunk of kCalibChunk samples, 256 words of
+//     a sample row): each thread owns one word (head h, band f) and sums,
+//     over the chunk's samples in order, the de-rotated band (fp32
+//     rotation) and its magnitude (x^2 + y^2 of bf16 values is exact in
+//     fp32) into fp64 sums; a wave reads 256 contiguous bytes of each
+//     sample row;
+//  3. a merge per (layer, head, band) over the chunks in order.
+constexpr int kCalibChunk = 256;
+
+__global__ __launch_bounds__(256) void calib_phasor_kernel(int F, int d, double theta,
+                                                           const int32_t* __restrict__ q_pos,
+                                                           int64_t N, float2* __restrict__ ph) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)L * Hq * F) return;
+  if (idx >= N * F) return;
   const int f = (int)(idx % F);
-  const int h = (int)((idx / F) % Hq);
-  const int l = (int)(idx / ((int64_t)F * Hq));
+  const int64_t t = idx / F;
   const double omega = pow(theta, -2.0 * (double)f / (double)d);
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(q);
-  const int64_t words_per_sample = (int64_t)Hq * F;
-  int64_t off = ((int64_t)l * N * Hq + h) * F + f;
+  double sn, cs;
+  sincos(omega * (double)q_pos[t], &sn, &cs);
+  ph[idx] = make_float2((float)cs, (float)-sn);  // exp(-i omega p)
+}
+
+// grid (chunks, L, ceil(W / 256)), W = Hq * F words per sample row
+__global__ __launch_bounds__(256) void calib_partial_kernel(
+    int W, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
+    const float2* __restrict__ ph, double* __restrict__ partial) {
+  const int c = blockIdx.x, l = blockIdx.y;
+  const int w = blockIdx.z * 256 + threadIdx.x;
+  if (w >= W) return;
+  const int f = w % F;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(q) + (int64_t)l * N * W + w;
+  const int64_t t0 = (int64_t)c * kCalibChunk;
+  const int64_t t1 = min(N, t0 + kCalibChunk);
   double sr = 0.0, si = 0.0, sa = 0.0;
-  for (int64_t t = 0; t < N; ++t, off += words_per_sample) {
-    const uint32_t w = words[off];
-    const double x = (double)bf16_lo(w), y = (double)bf16_hi(w);
-    double re = x, im = y;
-    if (q_pos) {
-      double sn, cs;
-      sincos(omega * (double)q_pos[t], &sn, &cs);
-      re = x * cs + y * sn;   // (x + i y) * exp(-i omega p)
-      im = y * cs - x * sn;
+#pragma unroll 8
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint32_t u = words[t * W];
+    const float x = bf16_lo(u), y = bf16_hi(u);
+    float re = x, im = y;
+    if (ph) {
+      const float2 p = ph[t * F + f];  // (x + i y) * exp(-i omega p)
+      re = fmaf(x, p.x, -y * p.y);
+      im = fmaf(x, p.y, y * p.x);
     }
-    sr += re;
-    si += im;
-    sa += sqrt(x * x + y * y);  // |q_f| is unchanged by the rotation
+    sr += (double)re;
+    si += (double)im;
+    sa += (double)__builtin_amdgcn_sqrtf(fmaf(x, x, y * y));  // |q_f|: unchanged by the rotation
+  }
+  double* out = partial + (((int64_t)l * chunks + c) * W + w) * 3;
+  out[0] = sr;
+  out[1] = si;
+  out[2] = sa;
+}
+
+__global__ __launch_bounds__(256) void calib_merge_kernel(
+    int L, int W, int64_t N, int chunks, const double* __restrict__ partial,
+    float* __restrict__ centre, float* __restrict__ absmean, float* __restrict__ R) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)L * W) return;
+  const int l = (int)(idx / W), w = (int)(idx % W);
+  double sr = 0.0, si = 0.0, sa = 0.0;
+  for (int c = 0; c < chunks; ++c) {
+    const double* p = partial + (((int64_t)l * chunks + c) * W + w) * 3;
+    sr += p[0];
+    si += p[1];
+    sa += p[2];
   }
   const double inv = 1.0 / (double)N;
   const double cr = sr * inv, ci = si * inv, am = sa * inv;
-  const int64_t o = ((int64_t)l * Hq + h) * F + f;
-  centre[2 * o] = (float)cr;
-  centre[2 * o + 1] = (float)ci;
-  absmean[o] = (float)am;
-  R[o] = am > 0.0 ? (float)(sqrt(cr * cr + ci * ci) / am) : 1.0f;
+  centre[2 * idx] = (float)cr;
+  centre[2 * idx + 1] = (float)ci;
+  absmean[idx] = (float)am;
+  R[idx] = am > 0.0 ? (float)(sqrt(cr * cr + ci * ci) / am) : 1.0f;
+}
+
+size_t calibrate_workspace_bytes(int L, int Hq, int d, int64_t n_samples) {
+  const int64_t F = d / 2;
+  const int64_t chunks = (n_samples + kCalibChunk - 1) / kCalibChunk;
+  return (size_t)(n_samples * F * 8) + (size_t)(L * chunks * Hq * F * 3 * 8) + 256;
 }
 
 hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* q,
                             const int32_t* q_pos, int64_t n_samples, float* centre,
-                            float* absmean, float* R, hipStream_t st) {
-  const int64_t total = (int64_t)L * Hq * (d / 2);
-  const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(calibrate_kernel, dim3(blocks), dim3(256), 0, st, L, Hq, d, theta, q,
-                     q_pos, n_samples, centre, absmean, R);
+                            float* absmean, float* R, void* workspace, hipStream_t st) {
+  const int F = d / 2, W = Hq * F;
+  const int chunks = (int)((n_samples + kCalibChunk - 1) / kCalibChunk);
+  float2* ph = nullptr;
+  char* ws = (char*)workspace;
+  double* partial = (double*)(ws + ((n_samples * F * 8 + 255) / 256) * 256);
+  if (q_pos) {
+    ph = (float2*)ws;
+    const int64_t n = n_samples * F;
+    hipLaunchKernelGGL(calib_phasor_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, F,
+                       d, theta, q_pos, n_samples, ph);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(calib_partial_kernel, dim3(chunks, L, (W + 255) / 256), dim3(256), 0, st, W,
+                     F, n_samples, chunks, q, ph, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t m = (int64_t)L * W;
+  hipLaunchKernelGGL(calib_merge_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, L, W,
+                     n_samples, chunks, partial, centre, absmean, R);
   return hipGetLastError();
 }
 

@@ -60,9 +60,11 @@ __device__ __forceinline__ int find_seq_by_out_row(const SeqInfo* seqs, int S, i
 
 // Launchers (defined in the .hip files).  Each returns the hipError_t of the
 // launch.
+// Calibration scratch: the (sample, band) phasor table and per-chunk sums.
+size_t calibrate_workspace_bytes(int L, int Hq, int d, int64_t n_samples);
 hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* q,
                             const int32_t* q_pos, int64_t n_samples, float* centre,
-                            float* absmean, float* R, hipStream_t st);
+                            float* absmean, float* R, void* workspace, hipStream_t st);
 
 // offsets: device array of n_offsets distances, or NULL for the default set
 // {2^0, ..., 2^16}.  fold: P = E[q] * mean_delta exp(i omega delta) when

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_symbols_exported():
     lib = ctypes.CDLL(R.LIB_PATH)
     names = declared_functions()
-    assert set(names) == {"tri_calibrate", "tri_workspace_bytes", "tri_score",
+    assert set(names) == {"tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_bytes", "tri_score",
                           "tri_select_compact", "tri_status_string", "tri_last_error",
                           "tri_workspace_bytes_offsets", "tri_score_offsets",
                           "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
@@ -127,13 +127,20 @@ def test_select_argument_checks():
 def test_calibrate_argument_checks():
     sh = R.make_shape(64, 4, 2, 1)
 
-    def cal(q=_Fake(), n=10, c=_Fake(), a=_Fake(), r=_Fake()):
-        return R.tri_calibrate(sh, q, None, n, c, a, r, stream=0)
+    need = R.tri_calibrate_workspace_bytes(sh, 10)
+    assert need > 0 and R.tri_calibrate_workspace_bytes(sh, 0) == 0
+
+    def cal(q=_Fake(), n=10, c=_Fake(), a=_Fake(), r=_Fake(), ws=_Fake(), wsb=None):
+        return R.tri_calibrate(sh, q, None, n, c, a, r, workspace=ws,
+                               workspace_bytes=need if wsb is None else wsb, stream=0)
 
     assert _status(cal, n=0) == ST["INVALID"]
     assert _status(cal, q=None) == ST["INVALID"]
     assert _status(cal, r=None) == ST["INVALID"]
     assert _status(cal, q=_Fake(FAKE + 2)) == ST["INVALID"]
+    assert _status(cal, ws=None, wsb=0) == ST["WORKSPACE"]
+    assert _status(cal, wsb=need - 1) == ST["WORKSPACE"]
+    assert _status(cal, ws=_Fake(FAKE + 8)) == ST["INVALID"]
 
 
 def test_workspace_grows_with_batch():
