@@ -35,6 +35,9 @@ Sources (cited by page title and the section or equation on that page):
               tokens (e.g. [BOS]).
 * [trigger]   hyper.ai summary, section "方法": scoring and pruning run once
               every 128 generated tokens.
+* [budget]    same tutorial page, budget-setting step: a KV budget B per
+              layer, and pyramid-shaped allocation across layers (PyramidKV):
+              fewer keys for shallow layers, more for deep ones.
 * [recon]     shibing624 blog review, Fig. 1(D) (the trig series built from
               the centres against the real attention logits) and Fig. 7
               (per-head Pearson correlation of that reconstruction).
@@ -58,6 +61,9 @@ again in the design notes):
   correlation over every (sample query, key) pair of the direct post-RoPE
   logit q'.k' and S_trig(k, p_q - p_k) built from the query centre; 0 when
   either side is constant.
+* Pyramid budgets: linear in the layer index, b_l = round(b_0 + (b_{L-1} -
+  b_0) l / (L - 1)) with b_{L-1} = ratio * b_0 and mean (b_0 + b_{L-1}) / 2
+  equal to the requested mean (the pages give the shape, not a formula).
 * Decode loop: a unit is pruned to B when it reaches B + interval keys
   (interval 128), scored at the position of its newest key; the first
   `sink` and the last `recent` keys are kept whatever their score and count
@@ -471,4 +477,33 @@ def trig_reconstruction_r(q_post, q_pos, k_post, k_pos, centre, omega) -> float:
     (query, key) pairs."""
     direct, recon = trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega)
     return pearson(recon, direct)
+
+
+# --------------------------------------------------------------------------
+# Per-layer budgets  [budget]
+# --------------------------------------------------------------------------
+def pyramid_budgets(L: int, mean_budget: float, ratio: float) -> np.ndarray:
+    """Budgets per layer growing linearly from the first layer to the last:
+    the last is `ratio` times the first and the two ends average to
+    mean_budget; each is rounded to the nearest integer (halves up)."""
+    if L == 1:
+        return np.array([int(np.floor(mean_budget + 0.5))])
+    b0 = 2.0 * mean_budget / (1.0 + ratio)
+    b1 = ratio * b0
+    return np.floor(b0 + (b1 - b0) * np.arange(L) / (L - 1) + 0.5).astype(np.int64)
+
+
+def out_rows_layers(cu_len, budgets, L: int, Hkv: int, s: int, l: int, g: int):
+    """Output rows of unit (s, l, g) when each (sequence, layer) has its own
+    budget budgets[s][l]: (sequence, layer) pairs in order, each holding its
+    Hkv units of b = min(budgets[s][l], n_s) rows back to back."""
+    acc = 0
+    for s2 in range(len(cu_len) - 1):
+        n = int(cu_len[s2 + 1] - cu_len[s2])
+        for l2 in range(L):
+            b = max(0, min(int(budgets[s2][l2]), n))
+            if (s2, l2) == (s, l):
+                return acc + g * b, b
+            acc += Hkv * b
+    raise IndexError((s, l, g))
 

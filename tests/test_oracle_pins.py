@@ -605,3 +605,30 @@ def test_reconstruction_degrades_with_query_spread():
     assert rs[0] > 0.99
     assert all(a > b for a, b in zip(rs, rs[1:])), rs
     assert rs[-1] < 0.6
+
+
+# ------------------------------------------------------------ per-layer budgets
+def test_pyramid_budgets():
+    b = O.pyramid_budgets(28, 2048, 3.0)
+    assert len(b) == 28 and np.all(np.diff(b) >= 0)
+    assert b[0] == 1024 and b[-1] == 3072                  # 2*2048/(1+3) and 3x that
+    assert abs(b.mean() - 2048) <= 0.5
+    np.testing.assert_array_equal(O.pyramid_budgets(5, 100, 1.0), [100] * 5)
+    np.testing.assert_array_equal(O.pyramid_budgets(1, 77.5, 4.0), [78])
+    np.testing.assert_array_equal(O.pyramid_budgets(3, 10, 3.0), [5, 10, 15])
+
+
+def test_out_rows_layers_by_hand():
+    """Two sequences of 5 and 3 keys, two layers, two KV heads; budgets
+    [[2, 4], [9, 0]] keep (2, 4) and (3, 0) keys per unit."""
+    cu, bud = [0, 5, 8], [[2, 4], [9, 0]]
+    want = {(0, 0, 0): (0, 2), (0, 0, 1): (2, 2), (0, 1, 0): (4, 4), (0, 1, 1): (8, 4),
+            (1, 0, 0): (12, 3), (1, 0, 1): (15, 3), (1, 1, 0): (18, 0), (1, 1, 1): (18, 0)}
+    for key, val in want.items():
+        assert O.out_rows_layers(cu, bud, 2, 2, *key) == val
+    # with one budget per sequence it is the packed output layout
+    for s in range(2):
+        for l in range(2):
+            for g in range(2):
+                assert O.out_rows_layers(cu, [[3, 3], [2, 2]], 2, 2, s, l, g) == \
+                    O.out_rows(cu, [3, 2], 2, 2, s, l, g)
