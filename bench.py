@@ -225,20 +225,23 @@ def max_mode_flops(case, n_offsets):
     return 2 * G * n_offsets * d, mfma_per_16_keys * 16 * 16 * 32 * 2 // 16
 
 
-def algorithmic_bytes(case):
+def algorithmic_bytes(case, budgets=None):
     """Bytes the method must move (no design intermediates):
     score:   n*d*2 (K read) + n*4 (score write)
     select:  n*4 (score read) + b*4 (index write)
-    compact: 2*b*d*2 (K, V rows read) + 2*b*d*2 (rows written) + 2*b*4 (positions)."""
+    compact: 2*b*d*2 (K, V rows read) + 2*b*d*2 (rows written) + 2*b*4 (positions).
+    budgets: optional [S][L] per-layer budgets (else the sequence's budget)."""
     d = case.shape.head_dim
-    LH = case.shape.num_layers * case.shape.num_kv_heads
+    L, H = case.shape.num_layers, case.shape.num_kv_heads
     score = sel = 0
     keys = 0
     for s in range(case.num_seqs):
-        n, b = case.seq_len(s), case.kept(s)
-        keys += LH * n
-        score += LH * (n * d * 2 + n * 4)
-        sel += LH * (n * 4 + b * 4 + 4 * b * d * 2 + 2 * b * 4)
+        n = case.seq_len(s)
+        for l in range(L):
+            b = case.kept(s) if budgets is None else max(0, min(int(budgets[s][l]), n))
+            keys += H * n
+            score += H * (n * d * 2 + n * 4)
+            sel += H * (n * 4 + b * 4 + 4 * b * d * 2 + 2 * b * 4)
     return keys, score, sel
 
 
@@ -535,6 +538,9 @@ def main():
     ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
     ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
+    ap.add_argument("--pyramid", type=float, default=None, metavar="RATIO",
+                    help="per-layer pyramid budgets (last/first = RATIO, mean = the "
+                         "sequence's budget), selected by tri_select_compact_layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", default=None)
@@ -586,12 +592,23 @@ def main():
     cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
     bu = torch.as_tensor(case.budget).pin_memory().numpy()
     variant = args.offsets != "default" or args.reduce != "mean"
+    budgets = None
+    if args.pyramid is not None:
+        L = case.shape.num_layers
+        budgets = np.stack([R.tri_pyramid_budgets(L, float(b), args.pyramid)
+                            for b in case.budget]).astype(np.int32)
+        out_rows = int(sum(case.shape.num_kv_heads * min(int(budgets[s][l]), case.seq_len(s))
+                           for s in range(case.num_seqs) for l in range(L)))
+        bu = torch.as_tensor(budgets.reshape(-1)).pin_memory().numpy()
+        label = f"{label}+pyramid_ratio_{args.pyramid:g}"
     offs = torch.as_tensor(OFFSET_SETS[args.offsets], dtype=torch.float64).pin_memory().numpy()
     if variant:
         label = f"{label}+{args.reduce}_over_{args.offsets}_offsets"
         wsb = R.tri_workspace_bytes_offsets(sh, cu, len(offs), args.reduce)
     else:
         wsb = R.tri_workspace_bytes(sh, cu)
+    if budgets is not None:
+        wsb = max(wsb, R.tri_workspace_bytes_layers(sh, cu))
     ws = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
     scores = torch.empty(rows, dtype=torch.float32, device=dev)
     kept = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
@@ -609,8 +626,12 @@ def main():
                         scores, workspace=ws, stream=stream)
 
     def select():
-        R.tri_select_compact(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept, k_out, v_out,
-                             pos_out, workspace=ws, stream=stream)
+        if budgets is not None:
+            R.tri_select_compact_layers(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept,
+                                        k_out, v_out, pos_out, workspace=ws, stream=stream)
+        else:
+            R.tri_select_compact(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept, k_out,
+                                 v_out, pos_out, workspace=ws, stream=stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -635,7 +656,7 @@ def main():
     t_step = np.array([a.elapsed_time(c) for a, _, c in ev]) * 1e-3
     print(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
-    keys, b_score, b_sel = algorithmic_bytes(case)
+    keys, b_score, b_sel = algorithmic_bytes(case, budgets)
     step = float(t_step.mean())
     value = keys / step
     gbps = (b_score + b_sel) / step / 1e9
@@ -661,7 +682,9 @@ def main():
         "hbm_frac_of_peak": gbps / PEAK_HBM_GBPS,
         "wall_ms_per_step": wall / args.steps * 1e3,
         "breakdown_ms": {"tri_score": float(t_score.mean()) * 1e3,
-                         "tri_select_compact": float(t_sel.mean()) * 1e3},
+                         ("tri_select_compact_layers" if budgets is not None
+                          else "tri_select_compact"): float(t_sel.mean()) * 1e3},
+        "select_hbm_gbps": b_sel / float(t_sel.mean()) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "tri_score",
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": score_gbps / PEAK_HBM_GBPS,
@@ -670,6 +693,9 @@ def main():
                      "algorithmic_bytes_per_launch": b_score,
                      "launch": "tri_score call: prologue + operand pack + fused score kernel"},
     }
+    if budgets is not None:
+        out["config"]["budget"] = "pyramid"
+        out["config"]["layer_budgets"] = [int(x) for x in budgets[0]]
     if variant:
         out["offsets"] = {"set": args.offsets, "values": OFFSET_SETS[args.offsets],
                           "reduce": args.reduce}

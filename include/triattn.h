@@ -345,6 +345,38 @@ tri_status tri_decode_get_view(const tri_decode* dec, tri_decode_view* view);
 /* Wait for the device, then free everything the driver allocated. */
 tri_status tri_decode_destroy(tri_decode* dec);
 
+/*
+ * Per-layer budgets (tutorial page, budget-setting step: a KV budget per
+ * layer, and PyramidKV's pyramid allocation across layers, fewer keys for
+ * shallow layers and more for deep ones).
+ *
+ * tri_pyramid_budgets -- budgets[num_layers] growing linearly with the
+ * layer index: the last is `ratio` times the first, the two ends average
+ * to mean_budget, each rounded to the nearest integer (the pages give the
+ * shape, not a formula).  ratio > 0; mean_budget in [0, 1e9].
+ *
+ * tri_select_compact_layers -- tri_select_compact with one budget per
+ * (sequence, layer): budget [host][num_seqs][L].  Unit (s, l, g) keeps
+ * b = min(budget[s][l], n_s) keys.  Outputs are packed by (sequence,
+ * layer) in order, each pair holding its Hkv units of b rows back to back.
+ * Workspace: tri_workspace_bytes_layers().  Everything else is as for
+ * tri_select_compact; scores come from tri_score unchanged.
+ */
+tri_status tri_pyramid_budgets(int32_t num_layers, double mean_budget,
+                               double ratio, int32_t* budgets);
+
+size_t tri_workspace_bytes_layers(const tri_shape* shape, int32_t num_seqs,
+                                  const int64_t* cu_len);
+
+tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,
+                                     const int64_t* cu_len, const int32_t* budget,
+                                     const float* scores, const uint16_t* k,
+                                     const uint16_t* v, const int32_t* k_pos,
+                                     int32_t* kept_idx, uint16_t* k_out,
+                                     uint16_t* v_out, int32_t* pos_out,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* tri_status_string(tri_status status);
 

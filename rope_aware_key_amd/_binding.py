@@ -95,11 +95,19 @@ _lib.tri_trig_correlation.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c
                                       ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_trig_correlation.restype = ctypes.c_int
 
+_lib.tri_pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_double, _P]
+_lib.tri_pyramid_budgets.restype = ctypes.c_int
+_lib.tri_workspace_bytes_layers.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P]
+_lib.tri_workspace_bytes_layers.restype = ctypes.c_size_t
+_lib.tri_select_compact_layers.argtypes = _lib.tri_select_compact.argtypes
+_lib.tri_select_compact_layers.restype = ctypes.c_int
+
 EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_bytes", "tri_score", "tri_select_compact",
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
-           "tri_trig_correlation")
+           "tri_trig_correlation", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
+           "tri_select_compact_layers")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -286,4 +294,31 @@ class Decode:
             self.close()
         except Exception:
             pass
+
+
+def tri_pyramid_budgets(num_layers, mean_budget, ratio):
+    out = np.zeros(int(num_layers), dtype=np.int32)
+    _check(_lib.tri_pyramid_budgets(int(num_layers), float(mean_budget), float(ratio),
+                                    ctypes.c_void_p(out.ctypes.data)), "tri_pyramid_budgets")
+    return out
+
+
+def tri_workspace_bytes_layers(shape: TriShape, cu_len) -> int:
+    arr, p = _host(cu_len, np.int64)
+    return int(_lib.tri_workspace_bytes_layers(ctypes.byref(shape), len(arr) - 1, p))
+
+
+def tri_select_compact_layers(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx,
+                              k_out, v_out, pos_out, workspace=None, workspace_bytes=None,
+                              stream=None):
+    """tri_select_compact with budget [num_seqs][L] (one per sequence and layer)."""
+    cu, pcu = _host(cu_len, np.int64)
+    bu, pbu = _host(np.asarray(budget).reshape(-1), np.int32)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_select_compact_layers(ctypes.byref(shape), len(cu) - 1, pcu, pbu, _ptr(scores),
+                                        _ptr(k), _ptr(v), _ptr(k_pos), _ptr(kept_idx), _ptr(k_out),
+                                        _ptr(v_out), _ptr(pos_out), _ptr(workspace), int(wsb),
+                                        _stream(stream))
+    _check(st, "tri_select_compact_layers")
 

@@ -122,13 +122,13 @@ struct OffsetMode {
 
 // Where each unit's rows live.  Packed (stride 0): units of n_s (input) or
 // b_s (output) rows back to back, sequence s from row L*Hkv*cu_len[s] (or
-// its output prefix); this is the public layout.  Strided: every unit of
-// sequence s at row0[s] + (l*Hkv + g)*stride, so units can grow in place
-// (the decode cache).
+// its output prefix) unless row0[s] is given; this is the public layout.
+// Strided: every unit of sequence s at row0[s] + (l*Hkv + g)*stride, so
+// units can grow in place (the decode cache).
 struct PlanLayout {
   int64_t in_stride = 0, out_stride = 0;
-  const int64_t* in_row0 = nullptr;   // [S] host, strided input only
-  const int64_t* out_row0 = nullptr;  // [S] host, strided output only
+  const int64_t* in_row0 = nullptr;   // [S] host: first input row per sequence
+  const int64_t* out_row0 = nullptr;  // [S] host: first output row per sequence
 };
 
 struct Plan {
@@ -203,7 +203,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");
     if (n > (int64_t)0x7fffffff / 2) return fail(TRI_ERR_UNSUPPORTED, "sequence too long");
     SeqInfo& si = p.seqs[s];
-    si.row_base = lay.in_stride ? lay.in_row0[s] : LH * cu_len[s];
+    si.row_base = lay.in_row0 ? lay.in_row0[s] : LH * cu_len[s];
     si.n = (int32_t)n;
     si.in_stride = (int32_t)(lay.in_stride ? lay.in_stride : n);
     if (n > si.in_stride) return fail(TRI_ERR_INVALID_ARGUMENT, "unit longer than its stride");
@@ -215,7 +215,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     si.b = (int32_t)b;
     if (n > p.max_n) p.max_n = (int)n;
     if (b > p.max_b) p.max_b = (int)b;
-    si.out_base = lay.out_stride ? lay.out_row0[s] : LH * out_acc;
+    si.out_base = lay.out_row0 ? lay.out_row0[s] : LH * out_acc;
     si.out_stride = (int32_t)(lay.out_stride ? lay.out_stride : b);
     if (b > si.out_stride) return fail(TRI_ERR_INVALID_ARGUMENT, "budget above the output stride");
     p.total_rows = std::max(p.total_rows, si.row_base + LH * si.in_stride);
@@ -799,3 +799,97 @@ tri_status tri_decode_destroy(tri_decode* dec) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Per-layer budgets.  Select and gather never look at the layer, so each
+// (sequence, layer) becomes a pseudo-sequence of Hkv units with its own
+// budget, reading the units where the packed layout has them.
+// ---------------------------------------------------------------------------
+extern "C" {
+
+tri_status tri_pyramid_budgets(int32_t num_layers, double mean_budget, double ratio,
+                               int32_t* budgets) {
+  if (num_layers < 1 || !budgets) return fail(TRI_ERR_INVALID_ARGUMENT, "num_layers >= 1 and budgets");
+  if (!(mean_budget >= 0.0) || !(ratio > 0.0) || !std::isfinite(mean_budget) ||
+      !std::isfinite(ratio) || mean_budget > 1e9)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "mean_budget must be in [0, 1e9], ratio > 0");
+  if (num_layers == 1) {
+    budgets[0] = (int32_t)std::floor(mean_budget + 0.5);
+    return TRI_OK;
+  }
+  const double b0 = 2.0 * mean_budget / (1.0 + ratio), b1 = ratio * b0;
+  for (int l = 0; l < num_layers; ++l)
+    budgets[l] = (int32_t)std::floor(b0 + (b1 - b0) * l / (double)(num_layers - 1) + 0.5);
+  return TRI_OK;
+}
+
+size_t tri_workspace_bytes_layers(const tri_shape* shape, int32_t num_seqs,
+                                  const int64_t* cu_len) {
+  // pseudo-sequences of one layer each: the plan table grows by L
+  if (check_shape(shape) != TRI_OK || num_seqs < 0 || (num_seqs > 0 && !cu_len)) return 0;
+  const int64_t S2 = (int64_t)num_seqs * shape->num_layers;
+  if ((size_t)S2 * sizeof(SeqInfo) > kSlotBytes) {
+    fail(TRI_ERR_UNSUPPORTED, "too many (sequence, layer) pairs in one call (max 8192)");
+    return 0;
+  }
+  return align_up((size_t)S2 * sizeof(SeqInfo), 256);
+}
+
+tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,
+                                     const int64_t* cu_len, const int32_t* budget,
+                                     const float* scores, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* k_pos, int32_t* kept_idx, uint16_t* k_out,
+                                     uint16_t* v_out, int32_t* pos_out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  tri_status st = check_shape(shape);
+  if (st != TRI_OK) return st;
+  if (num_seqs < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if (num_seqs > 0 && (!cu_len || !budget))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len and budget are required");
+  const int L = shape->num_layers, Hkv = shape->num_kv_heads;
+  const int64_t S2 = (int64_t)num_seqs * L;
+  if ((size_t)S2 * sizeof(SeqInfo) > kSlotBytes)
+    return fail(TRI_ERR_UNSUPPORTED, "too many (sequence, layer) pairs in one call (max 8192)");
+  std::vector<int64_t> cu2(S2 + 1, 0), in0(S2), out0(S2);
+  std::vector<int32_t> bud2(S2);
+  int64_t out_acc = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t n = cu_len[s + 1] - cu_len[s];
+    if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");
+    for (int l = 0; l < L; ++l) {
+      const int64_t i = (int64_t)s * L + l;
+      if (budget[i] < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "budget must be >= 0");
+      cu2[i + 1] = cu2[i] + n;
+      in0[i] = (int64_t)L * Hkv * cu_len[s] + (int64_t)l * Hkv * n;
+      out0[i] = out_acc;
+      bud2[i] = budget[i];
+      out_acc += (int64_t)Hkv * std::min<int64_t>(budget[i], n);
+    }
+  }
+  tri_shape sh1 = *shape;
+  sh1.num_layers = 1;
+  PlanLayout lay;
+  lay.in_row0 = in0.data();
+  lay.out_row0 = out0.data();
+  Plan p;
+  st = make_plan(&sh1, (int32_t)S2, cu2.data(), nullptr, bud2.data(), p, OffsetMode(), lay);
+  if (st != TRI_OK) return st;
+  if ((k == nullptr) != (k_out == nullptr) || (v == nullptr) != (v_out == nullptr) ||
+      (k_pos == nullptr) != (pos_out == nullptr))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "k/k_out, v/v_out and k_pos/pos_out come in pairs");
+  if (p.kept == 0) return TRI_OK;
+  if (!scores || !kept_idx)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "scores and kept_idx must be non-NULL");
+  if ((k && (!aligned16(k) || !aligned16(k_out))) || (v && (!aligned16(v) || !aligned16(v_out))))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "K/V buffers must be 16-byte aligned");
+  if (!workspace || workspace_bytes < p.select_bytes)
+    return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes_layers()");
+  const hipError_t e = run_select_compact(p, scores, k, v, k_pos, kept_idx, k_out, v_out, pos_out,
+                                          (char*)workspace, (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(TRI_ERR_HIP, std::string("select_compact_layers: ") + hipGetErrorString(e));
+  return TRI_OK;
+}
+
+}  // extern "C"
+

@@ -30,7 +30,9 @@ def test_header_symbols_exported():
                           "tri_workspace_bytes_offsets", "tri_score_offsets",
                           "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
                           "tri_decode_get_view", "tri_decode_destroy",
-                          "tri_trig_correlation_workspace_bytes", "tri_trig_correlation"}
+                          "tri_trig_correlation_workspace_bytes", "tri_trig_correlation",
+                          "tri_pyramid_budgets", "tri_workspace_bytes_layers",
+                          "tri_select_compact_layers"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -298,3 +300,39 @@ def test_trig_correlation_argument_checks():
     assert _status(call, k=_Fake(FAKE + 4)) == ST["INVALID"]
     assert _status(call) == ST["WORKSPACE"]
     assert _status(call, ws=_Fake(), wsb=need - 1) == ST["WORKSPACE"]
+
+
+
+def test_pyramid_budgets_match_oracle():
+    """Host arithmetic, no device: the library's pyramid equals the oracle's."""
+    import oracle as O
+    for L, mean, ratio in [(28, 2048, 3.0), (32, 1000, 1.0), (1, 77.5, 4.0), (3, 10, 3.0),
+                           (7, 513.3, 0.5), (40, 4096, 8.0)]:
+        np.testing.assert_array_equal(R.tri_pyramid_budgets(L, mean, ratio),
+                                      O.pyramid_budgets(L, mean, ratio))
+    for bad in [(0, 10, 2.0), (4, -1, 2.0), (4, 10, 0.0), (4, float("nan"), 2.0)]:
+        assert _status(R.tri_pyramid_budgets, *bad) == ST["INVALID"]
+
+
+def test_select_compact_layers_argument_checks():
+    sh = R.make_shape(64, 4, 2, 3)
+    cu = [0, 50, 80]
+    bud = [[10, 20, 30], [5, 5, 5]]
+    need = R.tri_workspace_bytes_layers(sh, cu)
+    assert need == 256                                 # 6 plan entries of 40 bytes
+
+    def sel(budget=bud, **kw):
+        args = dict(scores=_Fake(), k=_Fake(), v=_Fake(), k_pos=_Fake(), kept=_Fake(),
+                    k_out=_Fake(FAKE * 2), v_out=_Fake(FAKE * 3), pos_out=_Fake(FAKE * 4),
+                    workspace=None, workspace_bytes=0)
+        args.update(kw)
+        return R.tri_select_compact_layers(sh, cu, budget, args["scores"], args["k"], args["v"],
+                                           args["k_pos"], args["kept"], args["k_out"],
+                                           args["v_out"], args["pos_out"],
+                                           workspace=args["workspace"],
+                                           workspace_bytes=args["workspace_bytes"], stream=0)
+
+    assert _status(sel, budget=[[10, -1, 3], [5, 5, 5]]) == ST["INVALID"]
+    assert _status(sel, v_out=None) == ST["INVALID"]
+    assert _status(sel) == ST["WORKSPACE"]
+    assert _status(sel, budget=[[0, 0, 0], [0, 0, 0]]) == 0
