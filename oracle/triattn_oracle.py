@@ -38,6 +38,10 @@ Sources (cited by page title and the section or equation on that page):
 * [budget]    same tutorial page, budget-setting step: a KV budget B per
               layer, and pyramid-shaped allocation across layers (PyramidKV):
               fewer keys for shallow layers, more for deep ones.
+* [layout]    same tutorial page, RoPE paragraph: the rotation is applied to
+              queries and keys in LLaMA and Mistral, whose common
+              implementations pair element f with element f + d/2 ("half
+              split") rather than 2f with 2f + 1.
 * [recon]     shibing624 blog review, Fig. 1(D) (the trig series built from
               the centres against the real attention logits) and Fig. 7
               (per-head Pearson correlation of that reconstruction).
@@ -47,7 +51,8 @@ again in the design notes):
 
 * RoPE pairs are interleaved (x_{2f}, x_{2f+1}) as the rotation equation
   writes them; band f is the complex number x_{2f} + i x_{2f+1}, and the
-  printed matrix multiplies it by exp(+i omega_f p).
+  printed matrix multiplies it by exp(+i omega_f p).  layout="half" takes
+  band f as x_f + i x_{f+d/2} instead [layout]; nothing else changes.
 * phi_f in S_trig is arg E[q_f] - arg k_f with k_f the pre-RoPE key.
 * The offsets are averaged (formula page) by default; the blog review's
   maximum over D is available as reduce="max" (a variant, not the default).
@@ -101,43 +106,59 @@ def rope_omega(d: int, theta: float) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * f / d)
 
 
-def rope_rotate(x: np.ndarray, pos, omega: np.ndarray) -> np.ndarray:
+LAYOUTS = ("interleaved", "half")
+
+
+def _pair_slices(d: int, layout: str):
+    """Element positions of (real, imaginary) parts of every band."""
+    if layout == "interleaved":
+        return slice(0, d, 2), slice(1, d, 2)
+    if layout == "half":
+        return slice(0, d // 2), slice(d // 2, d)
+    raise ValueError(layout)
+
+
+def rope_rotate(x: np.ndarray, pos, omega: np.ndarray, layout="interleaved") -> np.ndarray:
     """Apply the printed 2x2 rotation to every band of x at position pos.
 
     x: [..., d] (pre-RoPE).  pos broadcasts against x[..., 0].
-    (x'_{2f}, x'_{2f+1}) = [[cos, -sin], [sin, cos]] (x_{2f}, x_{2f+1}),
-    angle omega_f * pos.
+    (x'_a, x'_b) = [[cos, -sin], [sin, cos]] (x_a, x_b), angle omega_f * pos,
+    with (a, b) = (2f, 2f+1) (interleaved) or (f, f + d/2) (half).
     """
     x = np.asarray(x, dtype=np.float64)
     ang = np.asarray(pos, dtype=np.float64)[..., None] * omega
     c, s = np.cos(ang), np.sin(ang)
-    xe, xo = x[..., 0::2], x[..., 1::2]
+    ra, rb = _pair_slices(x.shape[-1], layout)
+    xe, xo = x[..., ra], x[..., rb]
     out = np.empty_like(x)
-    out[..., 0::2] = c * xe - s * xo
-    out[..., 1::2] = s * xe + c * xo
+    out[..., ra] = c * xe - s * xo
+    out[..., rb] = s * xe + c * xo
     return out
 
 
-def rope_derotate(x: np.ndarray, pos, omega: np.ndarray) -> np.ndarray:
+def rope_derotate(x: np.ndarray, pos, omega: np.ndarray, layout="interleaved") -> np.ndarray:
     """Inverse of rope_rotate (rotation by -omega_f * pos)."""
-    return rope_rotate(x, -np.asarray(pos, dtype=np.float64), omega)
+    return rope_rotate(x, -np.asarray(pos, dtype=np.float64), omega, layout)
 
 
-def bands(x: np.ndarray) -> np.ndarray:
-    """View band f of x as the complex number x_{2f} + i x_{2f+1}."""
+def bands(x: np.ndarray, layout="interleaved") -> np.ndarray:
+    """View band f of x as the complex number x_a + i x_b, (a, b) as in
+    rope_rotate."""
     x = np.asarray(x, dtype=np.float64)
-    return x[..., 0::2] + 1j * x[..., 1::2]
+    ra, rb = _pair_slices(x.shape[-1], layout)
+    return x[..., ra] + 1j * x[..., rb]
 
 
 # --------------------------------------------------------------------------
 # Logit decomposition  [logit-eq]
 # --------------------------------------------------------------------------
-def logit_decomposed(q_pre: np.ndarray, k_pre: np.ndarray, delta, omega) -> np.ndarray:
+def logit_decomposed(q_pre: np.ndarray, k_pre: np.ndarray, delta, omega,
+                     layout="interleaved") -> np.ndarray:
     """sum_f |q_f| |k_f| cos(omega_f * Delta + phi_f), phi_f = arg q_f - arg k_f.
 
     q_pre, k_pre: [..., d] pre-RoPE vectors; delta = p_q - p_k.
     """
-    qf, kf = bands(q_pre), bands(k_pre)
+    qf, kf = bands(q_pre, layout), bands(k_pre, layout)
     phi = np.angle(qf) - np.angle(kf)
     ang = np.asarray(delta, dtype=np.float64)[..., None] * omega + phi
     return np.sum(np.abs(qf) * np.abs(kf) * np.cos(ang), axis=-1)
@@ -146,7 +167,7 @@ def logit_decomposed(q_pre: np.ndarray, k_pre: np.ndarray, delta, omega) -> np.n
 # --------------------------------------------------------------------------
 # Calibration  [calib], [Snorm-eq]
 # --------------------------------------------------------------------------
-def calibrate(q: np.ndarray, q_pos, omega: np.ndarray):
+def calibrate(q: np.ndarray, q_pos, omega: np.ndarray, layout="interleaved"):
     """Per-band query statistics from sample queries of one layer.
 
     q: [N, H, d] fp64 sample queries, post-RoPE at q_pos[N]; pass
@@ -158,8 +179,8 @@ def calibrate(q: np.ndarray, q_pos, omega: np.ndarray):
     q = np.asarray(q, dtype=np.float64)
     if q_pos is not None:
         pos = np.asarray(q_pos, dtype=np.float64)[:, None]       # [N, 1]
-        q = rope_derotate(q, pos, omega)                          # pre-RoPE
-    qf = bands(q)                                                 # [N, H, F]
+        q = rope_derotate(q, pos, omega, layout)                  # pre-RoPE
+    qf = bands(q, layout)                                         # [N, H, F]
     centre = qf.mean(axis=0)
     absmean = np.abs(qf).mean(axis=0)
     R = np.ones_like(absmean)
@@ -173,7 +194,7 @@ def calibrate(q: np.ndarray, q_pos, omega: np.ndarray):
 # --------------------------------------------------------------------------
 def score_terms(k_post: np.ndarray, k_pos, p_q: float,
                 centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
-                omega: np.ndarray, offsets=OFFSETS, reduce="mean"):
+                omega: np.ndarray, offsets=OFFSETS, reduce="mean", layout="interleaved"):
     """Offset-reduced TriAttention score of every key, for each query head.
 
     k_post: [n, d] post-RoPE keys (fp64); k_pos: [n] their positions.
@@ -186,8 +207,8 @@ def score_terms(k_post: np.ndarray, k_pos, p_q: float,
     equations write it; nothing is factored.  S_norm does not depend on the
     offset, so either reduction of S_trig + S_norm leaves it unchanged.
     """
-    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega)
-    kf = bands(k_pre)                                   # [n, F]
+    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega, layout)
+    kf = bands(k_pre, layout)                           # [n, F]
     k_abs = np.abs(kf)
     k_arg = np.angle(kf)
     delta = p_q - np.asarray(k_pos, dtype=np.float64)   # [n]
@@ -223,7 +244,8 @@ def offset_phasor_mean(omega: np.ndarray, offsets=OFFSETS) -> np.ndarray:
 
 def score_factored(k_post: np.ndarray, p_q: float,
                    centre: np.ndarray, absmean: np.ndarray, R: np.ndarray,
-                   omega: np.ndarray, offsets=OFFSETS, reduce="mean") -> np.ndarray:
+                   omega: np.ndarray, offsets=OFFSETS, reduce="mean",
+                   layout="interleaved") -> np.ndarray:
     """The same S_tilde as score_terms, written as one dot product per head.
 
     Band f of a query at p_q + delta contributes
@@ -235,7 +257,7 @@ def score_factored(k_post: np.ndarray, p_q: float,
     offset (A_f = E[q_f] exp(i omega_f (p_q + delta))) and the maximum kept.
     Returns S_tilde [G, n].
     """
-    kf = bands(k_post)                                           # [n, F]
+    kf = bands(k_post, layout)                                   # [n, F]
     if reduce == "mean":
         C = offset_phasor_mean(omega, offsets)                   # [F]
         A = centre * C[None, :] * np.exp(1j * omega * p_q)[None, :]  # [G, F]
@@ -276,15 +298,16 @@ def gqa_max(z: np.ndarray) -> np.ndarray:
 
 
 def unit_scores(k_post, k_pos, p_q, centre, absmean, R, omega,
-                offsets=OFFSETS, factored=False, reduce="mean"):
+                offsets=OFFSETS, factored=False, reduce="mean", layout="interleaved"):
     """Final fp64 score of each key of one unit (one sequence/layer/KV head).
 
     Returns (score [n], S_tilde [G, n], mu [G], sigma [G]).
     """
     if factored:
-        S = score_factored(k_post, p_q, centre, absmean, R, omega, offsets, reduce)
+        S = score_factored(k_post, p_q, centre, absmean, R, omega, offsets, reduce, layout)
     else:
-        S = score_terms(k_post, k_pos, p_q, centre, absmean, R, omega, offsets, reduce)[0]
+        S = score_terms(k_post, k_pos, p_q, centre, absmean, R, omega, offsets, reduce,
+                        layout)[0]
     z, mu, sigma = zscore_rows(S)
     return gqa_max(z), S, mu, sigma
 
@@ -415,12 +438,13 @@ class DecodeUnit:
         self.pos = np.append(self.pos, int(p))
 
     def scores(self, centre, absmean, R, omega, offsets=OFFSETS, reduce="mean",
-               factored=False, p_q=None):
+               factored=False, p_q=None, layout="interleaved"):
         """Final scores of every key, the query at the newest key's position
         (or at p_q)."""
         p = float(self.pos[-1]) if p_q is None else float(p_q)
         return unit_scores(bf16_bits_to_f64(self.k), self.pos.astype(np.float64), p, centre,
-                           absmean, R, omega, offsets, factored=factored, reduce=reduce)[0]
+                           absmean, R, omega, offsets, factored=factored, reduce=reduce,
+                           layout=layout)[0]
 
     def prune(self, kept):
         kept = np.asarray(kept, dtype=np.int64)
@@ -456,7 +480,7 @@ def pearson(x, y) -> float:
     return float(np.sum(dx * dy)) / np.sqrt(sxx * syy)
 
 
-def trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega):
+def trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega, layout="interleaved"):
     """For one (layer, query head): the direct logits [n_q, n_k], q'_j . k'_i
     of the post-RoPE vectors, and the reconstruction S_trig(k_i, p_j - p_i)
     = sum_f |E q_f| |k_f| cos(omega_f Delta + arg E q_f - arg k_f) with k_f
@@ -464,18 +488,20 @@ def trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega):
     q_post = np.asarray(q_post, dtype=np.float64)
     k_post = np.asarray(k_post, dtype=np.float64)
     direct = q_post @ k_post.T
-    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega)
+    k_pre = rope_derotate(k_post, np.asarray(k_pos, dtype=np.float64), omega, layout)
     c_vec = np.empty(2 * len(centre))
-    c_vec[0::2], c_vec[1::2] = np.real(centre), np.imag(centre)
+    ra, rb = _pair_slices(len(c_vec), layout)
+    c_vec[ra], c_vec[rb] = np.real(centre), np.imag(centre)
     delta = np.asarray(q_pos, dtype=np.float64)[:, None] - np.asarray(k_pos, dtype=np.float64)[None, :]
-    recon = logit_decomposed(c_vec[None, None, :], k_pre[None, :, :], delta, omega)
+    recon = logit_decomposed(c_vec[None, None, :], k_pre[None, :, :], delta, omega, layout)
     return direct, recon
 
 
-def trig_reconstruction_r(q_post, q_pos, k_post, k_pos, centre, omega) -> float:
+def trig_reconstruction_r(q_post, q_pos, k_post, k_pos, centre, omega,
+                          layout="interleaved") -> float:
     """Pearson r of the reconstruction against the direct logits, over all
     (query, key) pairs."""
-    direct, recon = trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega)
+    direct, recon = trig_reconstruction(q_post, q_pos, k_post, k_pos, centre, omega, layout)
     return pearson(recon, direct)
 
 

@@ -632,3 +632,92 @@ def test_out_rows_layers_by_hand():
             for g in range(2):
                 assert O.out_rows_layers(cu, [[3, 3], [2, 2]], 2, 2, s, l, g) == \
                     O.out_rows(cu, [3, 2], 2, 2, s, l, g)
+
+
+# --------------------------------------------------------------------------
+# Half-split RoPE layout (band f = x_f + i x_{f+d/2})
+# --------------------------------------------------------------------------
+def _to_half(x):
+    """Column permutation interleaved -> half split: (x0, x2, .., x1, x3, ..)."""
+    x = np.asarray(x)
+    return np.concatenate([x[..., 0::2], x[..., 1::2]], axis=-1)
+
+
+def test_half_split_quarter_turn_by_hand():
+    g = GOLD["rope_quarter_turn_half_split"]
+    om = O.rope_omega(g["d"], g["theta"])
+    x = np.array(g["input"])
+    np.testing.assert_allclose(O.rope_rotate(x, g["pos"], om, layout="half"), g["half"], atol=1e-15)
+    np.testing.assert_allclose(O.rope_rotate(x, g["pos"], om), g["interleaved"], atol=1e-15)
+
+
+def test_half_split_matches_rotate_half_form():
+    """The usual half-split formula, x cos + rotate_half(x) sin with the
+    angles repeated over both halves and rotate_half(x) = (-x2, x1)."""
+    rng = np.random.default_rng(21)
+    d = 64
+    om = O.rope_omega(d, 1e4)
+    x = rng.normal(size=(6, d))
+    pos = rng.integers(0, 40000, size=6).astype(np.float64)
+    ang = pos[:, None] * np.concatenate([om, om])[None, :]
+    rot_half = np.concatenate([-x[:, d // 2:], x[:, :d // 2]], axis=1)
+    want = x * np.cos(ang) + rot_half * np.sin(ang)
+    np.testing.assert_allclose(O.rope_rotate(x, pos[:, None][:, 0], om, layout="half"), want,
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.rope_derotate(want, pos, om, layout="half"), x, atol=1e-12)
+
+
+def test_half_split_relative_position_and_decomposition():
+    rng = np.random.default_rng(22)
+    d = 32
+    om = O.rope_omega(d, 1e4)
+    q, k = rng.normal(size=d), rng.normal(size=d)
+    p1, p2 = 5000.0, 1234.0
+    a = O.rope_rotate(q, p1, om, layout="half") @ O.rope_rotate(k, p2, om, layout="half")
+    b = O.rope_rotate(q, p1 + 777, om, layout="half") @ O.rope_rotate(k, p2 + 777, om, layout="half")
+    np.testing.assert_allclose(a, b, rtol=1e-10)
+    np.testing.assert_allclose(O.logit_decomposed(q, k, p1 - p2, om, layout="half"), a, rtol=1e-10)
+
+
+@pytest.mark.parametrize("reduce", ["mean", "max"])
+@pytest.mark.parametrize("factored", [False, True])
+def test_half_split_scores_equal_permuted_interleaved(reduce, factored):
+    """Storing every vector with its columns permuted to the half layout and
+    scoring with layout="half" reproduces the interleaved scores."""
+    rng = np.random.default_rng(23)
+    d, G, n = 32, 3, 40
+    om = O.rope_omega(d, 1e4)
+    k = rng.normal(size=(n, d))
+    pos = np.sort(rng.choice(10000, size=n, replace=False)).astype(np.float64)
+    centre = rng.normal(size=(G, d // 2)) + 1j * rng.normal(size=(G, d // 2))
+    absmean = np.abs(centre) * 1.3
+    R = np.abs(centre) / absmean
+    offs = O.OFFSETS if reduce == "mean" else (1.0, 8.0, 100.0)
+    a = O.unit_scores(k, pos, 12000.0, centre, absmean, R, om, offs, factored=factored,
+                      reduce=reduce)
+    b = O.unit_scores(_to_half(k), pos, 12000.0, centre, absmean, R, om, offs,
+                      factored=factored, reduce=reduce, layout="half")
+    np.testing.assert_allclose(b[0], a[0], atol=1e-9)
+    np.testing.assert_allclose(b[1], a[1], rtol=1e-10, atol=1e-9)
+    # planted mistake: reading half-split keys as interleaved changes them
+    c = O.unit_scores(_to_half(k), pos, 12000.0, centre, absmean, R, om, offs,
+                      factored=factored, reduce=reduce)
+    assert np.max(np.abs(c[1] - a[1])) > 1e-3
+
+
+def test_half_split_calibration_and_reconstruction():
+    rng = np.random.default_rng(24)
+    d, N, H = 16, 50, 2
+    om = O.rope_omega(d, 1e4)
+    q = rng.normal(size=(N, H, d)) + 2.0
+    qpos = rng.integers(0, 5000, size=N)
+    c1 = O.calibrate(q, qpos, om)
+    c2 = O.calibrate(_to_half(q), qpos, om, layout="half")
+    for x, y in zip(c1, c2):
+        np.testing.assert_allclose(y, x, rtol=1e-12, atol=1e-12)
+    k = rng.normal(size=(30, d))
+    kpos = rng.integers(0, 5000, size=30)
+    r1 = O.trig_reconstruction_r(q[:, 0], qpos, k, kpos, c1[0][0], om)
+    r2 = O.trig_reconstruction_r(_to_half(q[:, 0]), qpos, _to_half(k), kpos, c1[0][0], om,
+                                 layout="half")
+    assert abs(r1 - r2) < 1e-12
