@@ -245,7 +245,7 @@ def algorithmic_bytes(case, budgets=None):
     return keys, score, sel
 
 
-def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean"):
+def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="interleaved"):
     """The oracle as it stands (fp64, term by term) on whole units of the same
     workload, one after another, on one host thread (with the same offset
     set and reduction as the GPU line)."""
@@ -270,7 +270,7 @@ def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean"):
                                   qc[..., 0] + 1j * qc[..., 1],
                                   case.q_absmean[0, g * G:(g + 1) * G].cpu().double().numpy(),
                                   case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy(), om,
-                                  reduce=reduce,
+                                  reduce=reduce, layout=layout,
                                   **({} if offsets is None else {"offsets": offsets}))[0]
             kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
             O.compact_rows(kbits, kept)
@@ -538,6 +538,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
     ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
+    ap.add_argument("--rope-layout", default="interleaved", choices=["interleaved", "half"],
+                    help="store the keys half split (band f = x[f], x[f + d/2])")
     ap.add_argument("--pyramid", type=float, default=None, metavar="RATIO",
                     help="per-layer pyramid budgets (last/first = RATIO, mean = the "
                          "sequence's budget), selected by tri_select_compact_layers")
@@ -585,8 +587,17 @@ def main():
     cid, over, label = WORKLOADS[args.workload]
     print(f"[bench] building workload {label}", file=sys.stderr, flush=True)
     case = synth.config_case(cid, device=dev, **over)
+    if args.rope_layout == "half":
+        # the same keys with their columns permuted to the half-split layout
+        d = case.shape.head_dim
+        perm = torch.as_tensor(np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)]),
+                               device=dev)
+        case.k = case.k[:, perm].contiguous()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        label = f"{label}+half_split_rope"
     sh = R.make_shape(case.shape.head_dim, case.shape.num_q_heads, case.shape.num_kv_heads,
-                      case.shape.num_layers, case.shape.rope_theta)
+                      case.shape.num_layers, case.shape.rope_theta, rope_layout=args.rope_layout)
     rows, out_rows, d = case.total_rows(), case.total_out_rows(), case.shape.head_dim
     cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
     cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
@@ -689,7 +700,7 @@ def main():
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": measured_traffic() if args.workload == "c3" and not variant
-                     else None,
+                     and args.rope_layout == "interleaved" else None,
                      "algorithmic_bytes_per_launch": b_score,
                      "launch": "tri_score call: prologue + operand pack + fused score kernel"},
     }
@@ -721,7 +732,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, offsets=OFFSET_SETS[args.offsets],
-                                           reduce=args.reduce)
+                                           reduce=args.reduce, layout=args.rope_layout)
     print(json.dumps(out), flush=True)
 
 

@@ -63,12 +63,25 @@ typedef enum {
   TRI_ERR_HIP = 4               /* HIP runtime error while queueing work   */
 } tri_status;
 
+/*
+ * RoPE pair layout of every q/k row (TRI_ROPE_*).  Band f is the complex
+ * number (x_{2f}, x_{2f+1}) -- the talk page's rotation equation -- or,
+ * half split, (x_f, x_{f+d/2}), the pairing of the LLaMA/Mistral
+ * implementations the tutorial page's RoPE paragraph names.  The scores
+ * do not depend on the layout; only where the parts are stored.
+ */
+enum { TRI_ROPE_INTERLEAVED = 0, TRI_ROPE_HALF_SPLIT = 1 };
+
 typedef struct {
   int32_t head_dim;     /* d: even, multiple of 8, 8..256                 */
   int32_t num_q_heads;  /* H_q                                            */
   int32_t num_kv_heads; /* H_kv; H_q % H_kv == 0 and G = H_q/H_kv <= 16   */
   int32_t num_layers;   /* L                                              */
   double rope_theta;    /* theta > 0 (10000 in the pages)                 */
+  int32_t rope_layout;  /* TRI_ROPE_INTERLEAVED (0) or TRI_ROPE_HALF_SPLIT.
+                           Half split: every call supports it; the max over
+                           offsets needs d % 64 == 0 there, and tri_score
+                           takes its MFMA kernel only when d % 64 == 0      */
 } tri_shape;
 
 /*

@@ -6,7 +6,7 @@ only marshals arguments to it.  Importing raises if the library is not built.
 """
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, Decode, TriError, TriShape, last_error, make_shape, status_string,
-    TRI_REDUCE_MAX, TRI_REDUCE_MEAN, tri_calibrate, tri_calibrate_workspace_bytes, tri_score, tri_score_offsets,
+    TRI_REDUCE_MAX, TRI_REDUCE_MEAN, TRI_ROPE_HALF_SPLIT, TRI_ROPE_INTERLEAVED, tri_calibrate, tri_calibrate_workspace_bytes, tri_score, tri_score_offsets,
     tri_pyramid_budgets, tri_select_compact, tri_select_compact_layers, tri_trig_correlation,
     tri_trig_correlation_workspace_bytes, tri_workspace_bytes_layers,
     tri_workspace_bytes, tri_workspace_bytes_offsets,

@@ -34,7 +34,7 @@ STATUS = {0: "TRI_OK", 1: "TRI_ERR_INVALID_ARGUMENT", 2: "TRI_ERR_UNSUPPORTED",
 class TriShape(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("num_layers", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double)]
+                ("rope_theta", ctypes.c_double), ("rope_layout", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -126,8 +126,17 @@ def _check(st, where):
         raise TriError(st, where)
 
 
-def make_shape(head_dim, num_q_heads, num_kv_heads, num_layers, rope_theta=10000.0) -> TriShape:
-    return TriShape(head_dim, num_q_heads, num_kv_heads, num_layers, float(rope_theta))
+TRI_ROPE_INTERLEAVED = 0
+TRI_ROPE_HALF_SPLIT = 1
+ROPE_LAYOUT = {"interleaved": TRI_ROPE_INTERLEAVED, "half": TRI_ROPE_HALF_SPLIT}
+
+
+def make_shape(head_dim, num_q_heads, num_kv_heads, num_layers, rope_theta=10000.0,
+               rope_layout="interleaved") -> TriShape:
+    """rope_layout: "interleaved" (band f = x[2f], x[2f+1]), "half"
+    (x[f], x[f + d/2]) or the TRI_ROPE_* value."""
+    lay = ROPE_LAYOUT[rope_layout] if isinstance(rope_layout, str) else int(rope_layout)
+    return TriShape(head_dim, num_q_heads, num_kv_heads, num_layers, float(rope_theta), lay)
 
 
 def _ptr(t):

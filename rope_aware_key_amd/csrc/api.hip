@@ -109,6 +109,8 @@ tri_status check_shape(const tri_shape* sh) {
   if (sh->num_q_heads / sh->num_kv_heads > tri::kMaxGroup)
     return fail(TRI_ERR_UNSUPPORTED, "GQA group size above 16 is not supported");
   if (!(sh->rope_theta > 0.0)) return fail(TRI_ERR_INVALID_ARGUMENT, "rope_theta must be > 0");
+  if (sh->rope_layout != TRI_ROPE_INTERLEAVED && sh->rope_layout != TRI_ROPE_HALF_SPLIT)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "rope_layout must be TRI_ROPE_INTERLEAVED or _HALF_SPLIT");
   return TRI_OK;
 }
 
@@ -144,6 +146,7 @@ struct Plan {
   int64_t n_units = 0, n_stat_slots = 0;
   int chunk = 0;  // keys per score ticket
   bool fused = false;
+  bool half = false;  // half-split RoPE layout
   OffsetMode om;
   tri::MaxOffsetsPlan mp;  // max-over-offsets path
   size_t score_bytes = 0, select_bytes = 0;
@@ -158,6 +161,9 @@ tri_status check_offsets(const tri_shape* sh, const OffsetMode& om) {
       return fail(TRI_ERR_INVALID_ARGUMENT, "offsets must be finite");
   if (om.max && sh->head_dim % 32 != 0)
     return fail(TRI_ERR_UNSUPPORTED, "the max over offsets needs head_dim % 32 == 0");
+  if (om.max && sh->rope_layout == TRI_ROPE_HALF_SPLIT && sh->head_dim % 64 != 0)
+    return fail(TRI_ERR_UNSUPPORTED,
+                "the max over offsets with the half-split layout needs head_dim % 64 == 0");
   return TRI_OK;
 }
 
@@ -180,6 +186,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.G = p.Hq / p.Hkv;
   p.d = sh->head_dim;
   p.F = p.d / 2;
+  p.half = sh->rope_layout == TRI_ROPE_HALF_SPLIT;
   const int64_t LH = (int64_t)p.L * p.Hkv;
   p.seqs.resize(S);
   if (S > 0 && cu_len[0] < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len[0] must be >= 0");
@@ -194,7 +201,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
       return fail(TRI_ERR_UNSUPPORTED,
                   "the max over offsets: one head's offset rows exceed the LDS budget");
   }
-  p.fused = !om.max && tri::fused_supported(p.d) &&
+  p.fused = !om.max && tri::fused_supported(p.d, p.half) &&
             (longest + tri::fused_chunk_keys(p.G) - 1) / tri::fused_chunk_keys(p.G) <=
                 tri::kFusedMaxUnitChunks;
   p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
@@ -333,7 +340,8 @@ tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q, const
     return fail(TRI_ERR_WORKSPACE,
                 "workspace missing or smaller than tri_trig_correlation_workspace_bytes()");
   hipError_t e = tri::launch_trig_corr(shape->num_layers, shape->num_q_heads, shape->num_kv_heads,
-                                       shape->head_dim, n_q, n_k, shape->rope_theta, q, q_pos, k,
+                                       shape->head_dim, n_q, n_k, shape->rope_theta,
+                                       shape->rope_layout == TRI_ROPE_HALF_SPLIT, q, q_pos, k,
                                        k_pos, q_centre, (double*)workspace, r, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("trig_correlation: ") + hipGetErrorString(e));
   return TRI_OK;
@@ -365,7 +373,8 @@ tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_
   if (((uintptr_t)workspace & 15u) != 0)
     return fail(TRI_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   hipError_t e = tri::launch_calibrate(shape->num_layers, shape->num_q_heads, shape->head_dim,
-                                       shape->rope_theta, q, q_pos, n_samples, q_centre,
+                                       shape->rope_theta, shape->rope_layout == TRI_ROPE_HALF_SPLIT,
+                                       q, q_pos, n_samples, q_centre,
                                        q_absmean, q_R, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("calibrate: ") + hipGetErrorString(e));
   return TRI_OK;
@@ -397,17 +406,17 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                                  (int)p.tickets, (const double2*)(ws + p.off_P),
                                  (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E),
                                  doff, ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
-                                 (double*)(ws + p.off_ustats), scores, head_stats, s);
+                                 (double*)(ws + p.off_ustats), scores, head_stats, p.half, s);
   if (p.fused)
     return tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                    (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                                    (const double2*)(ws + p.off_E), ws + p.off_apack, k,
                                    (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
-                                   scores, raw_scores, head_stats, s);
+                                   scores, raw_scores, head_stats, p.half, s);
   return tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                            (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                            (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
-                           (double*)(ws + p.off_ustats), scores, head_stats, s);
+                           (double*)(ws + p.off_ustats), scores, head_stats, p.half, s);
 }
 
 // Queue select (and the gathers asked for) of a ready plan; the sequence

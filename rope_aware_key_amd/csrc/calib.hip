@@ -78,6 +78,51 @@ __global__ __launch_bounds__(256) void calib_partial_kernel(
   out[2] = sa;
 }
 
+// The same sums for the half-split layout (band f = (x_f, x_{f+d/2})):
+// thread w2 owns bands 2 fp and 2 fp + 1 of head h (w2 = h * F/2 + fp) and
+// reads one word of their real parts and one of their imaginary parts, so
+// a wave still reads contiguous words.  Grid (chunks, L, ceil(W/2 / 256)).
+__global__ __launch_bounds__(256) void calib_partial_half_kernel(
+    int W, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
+    const float2* __restrict__ ph, double* __restrict__ partial) {
+  const int c = blockIdx.x, l = blockIdx.y;
+  const int w2 = blockIdx.z * 256 + threadIdx.x;
+  const int hw = F >> 1;  // words per half row of a head
+  if (w2 >= W >> 1) return;
+  const int h = w2 / hw, fp = w2 % hw;
+  const int f0 = 2 * fp;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(q) + (int64_t)l * N * W + h * F + fp;
+  const int64_t t0 = (int64_t)c * kCalibChunk;
+  const int64_t t1 = min(N, t0 + kCalibChunk);
+  double sr[2] = {0.0, 0.0}, si[2] = {0.0, 0.0}, sa[2] = {0.0, 0.0};
+#pragma unroll 4
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint32_t ur = words[t * W], ui = words[t * W + hw];
+    const float xs[2] = {bf16_lo(ur), bf16_hi(ur)};
+    const float ys[2] = {bf16_lo(ui), bf16_hi(ui)};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float x = xs[b], y = ys[b];
+      float re = x, im = y;
+      if (ph) {
+        const float2 p = ph[t * F + f0 + b];
+        re = fmaf(x, p.x, -y * p.y);
+        im = fmaf(x, p.y, y * p.x);
+      }
+      sr[b] += (double)re;
+      si[b] += (double)im;
+      sa[b] += (double)__builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    double* out = partial + (((int64_t)l * chunks + c) * W + h * F + f0 + b) * 3;
+    out[0] = sr[b];
+    out[1] = si[b];
+    out[2] = sa[b];
+  }
+}
+
 __global__ __launch_bounds__(256) void calib_merge_kernel(
     int L, int W, int64_t N, int chunks, const double* __restrict__ partial,
     float* __restrict__ centre, float* __restrict__ absmean, float* __restrict__ R) {
@@ -105,7 +150,7 @@ size_t calibrate_workspace_bytes(int L, int Hq, int d, int64_t n_samples) {
   return (size_t)(n_samples * F * 8) + (size_t)(L * chunks * Hq * F * 3 * 8) + 256;
 }
 
-hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* q,
+hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const uint16_t* q,
                             const int32_t* q_pos, int64_t n_samples, float* centre,
                             float* absmean, float* R, void* workspace, hipStream_t st) {
   const int F = d / 2, W = Hq * F;
@@ -121,8 +166,12 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(calib_partial_kernel, dim3(chunks, L, (W + 255) / 256), dim3(256), 0, st, W,
-                     F, n_samples, chunks, q, ph, partial);
+  if (half)
+    hipLaunchKernelGGL(calib_partial_half_kernel, dim3(chunks, L, (W / 2 + 255) / 256), dim3(256),
+                       0, st, W, F, n_samples, chunks, q, ph, partial);
+  else
+    hipLaunchKernelGGL(calib_partial_kernel, dim3(chunks, L, (W + 255) / 256), dim3(256), 0, st,
+                       W, F, n_samples, chunks, q, ph, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t m = (int64_t)L * W;

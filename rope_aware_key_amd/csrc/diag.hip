@@ -53,7 +53,8 @@ __device__ __forceinline__ uint4 pack8_d(const uint32_t (&v)[8]) {
 // the tile's sums (x, y, xx, yy, xy).
 template <int STEPS>
 __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
-    int Hq, int Hkv, int64_t n_q, int64_t n_k, double theta, const uint16_t* __restrict__ q,
+    int Hq, int Hkv, int64_t n_q, int64_t n_k, double theta, bool half,
+    const uint16_t* __restrict__ q,
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ k_pos, const float* __restrict__ q_centre,
     double* __restrict__ partial) {
@@ -79,16 +80,18 @@ __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
   for (int st = 0; st < STEPS; ++st) {
     ay[st] = qrow[4 * st + qd];
     uint32_t h3[8], m3[8], l3[8];
+    // element j of the lane's eight: the real or imaginary part (by the
+    // RoPE layout) of its band's rotated centre
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = 16 * st + 4 * qd + u;
+    for (int j = 0; j < 8; ++j) {
+      const int e = 32 * st + 8 * qd + j;
+      const int f = elem_band(e, D, half);
       const float* c = q_centre + (((int64_t)l * Hq + h) * F + f) * 2;
       const double omega = pow(theta, -2.0 * (double)f / (double)D);
       double sn, cs;
       sincos(omega * pj, &sn, &cs);
       const double cr = (double)c[0], ci = (double)c[1];
-      split3_d(cr * cs - ci * sn, h3[2 * u], m3[2 * u], l3[2 * u]);
-      split3_d(cr * sn + ci * cs, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+      split3_d(elem_part(e, D, half) ? cr * sn + ci * cs : cr * cs - ci * sn, h3[j], m3[j], l3[j]);
     }
     axh[st] = pack8_d(h3);
     axm[st] = pack8_d(m3);
@@ -170,7 +173,7 @@ size_t trig_corr_workspace_bytes(int L, int Hq, int64_t n_q) {
 }
 
 hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t n_k, double theta,
-                            const uint16_t* q, const int32_t* q_pos, const uint16_t* k,
+                            bool half, const uint16_t* q, const int32_t* q_pos, const uint16_t* k,
                             const int32_t* k_pos, const float* q_centre, double* partial,
                             double* r, hipStream_t st) {
   const int64_t tiles = (n_q + 15) / 16;
@@ -179,7 +182,7 @@ hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t 
 #define TRI_CASE(n)                                                                         \
   case n:                                                                                   \
     hipLaunchKernelGGL(trig_corr_kernel<n>, grid, dim3(64 * kDiagWaves), 0, st, Hq, Hkv,   \
-                       n_q, n_k, theta, q, q_pos, k, k_pos, q_centre, partial);            \
+                       n_q, n_k, theta, half, q, q_pos, k, k_pos, q_centre, partial);      \
     break;
     TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7)
     TRI_CASE(8)

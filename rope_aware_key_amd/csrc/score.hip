@@ -6,8 +6,9 @@
 // with the per-(sequence, head, band) coefficient A_f = E[q_f] C_f
 // exp(i omega_f p_q) prepared by the prologue,
 //   S~_h(i) = sum_f [ Re(A_f) x_f + Im(A_f) y_f ] + sum_f w_f sqrt(x_f^2 + y_f^2)
-// where (x_f, y_f) is band f of the stored post-RoPE key and
-// w_f = (1 - R_f) E|q_f|.  One read of a key serves all G query heads.
+// where (x_f, y_f) is band f of the stored post-RoPE key, (k[2f], k[2f+1])
+// or, half split, (k[f], k[f + d/2]), and w_f = (1 - R_f) E|q_f|.  One read
+// of a key serves all G query heads.
 //
 // Work split: a "ticket" is one chunk of kScoreChunk keys of one unit.
 // Tickets of a unit are consecutive; each records (count, mean, M2) per head
@@ -58,7 +59,7 @@ __device__ __forceinline__ Ticket decode_ticket(const SeqInfo* seqs, int S, int 
 
 template <int GT>
 __global__ __launch_bounds__(256) void score_raw_kernel(
-    const SeqInfo* __restrict__ seqs, int S, int Hkv, int Hq, int G, int d,
+    const SeqInfo* __restrict__ seqs, int S, int Hkv, int Hq, int G, int d, bool half,
     const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
     const uint16_t* __restrict__ k, float* __restrict__ raw, double* __restrict__ chunk_stats) {
   constexpr int KPT = kScoreChunk / 256;
@@ -95,25 +96,36 @@ __global__ __launch_bounds__(256) void score_raw_kernel(
     float acc[GT];
 #pragma unroll
     for (int h = 0; h < GT; ++h) acc[h] = 0.f;
-    if (key < tk.nkeys) {
+    auto band = [&](int f, float x, float y) {
+      const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float a = acc[h];
+        a = fmaf(a_s[h * d + 2 * f], x, a);
+        a = fmaf(a_s[h * d + 2 * f + 1], y, a);
+        a = fmaf(w_s[h * F + f], r, a);
+        acc[h] = a;
+      }
+    };
+    if (key < tk.nkeys && !half) {
       const uint4* rp = reinterpret_cast<const uint4*>(k + (tk.row0 + tk.key0 + key) * d);
       for (int c8 = 0; c8 < (d >> 3); ++c8) {
         const uint4 q = rp[c8];
         const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int f = c8 * 4 + u;
-          const float x = bf16_lo_s(wd[u]), y = bf16_hi_s(wd[u]);
-          const float r = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
-#pragma unroll
-          for (int h = 0; h < GT; ++h) {
-            float a = acc[h];
-            a = fmaf(a_s[h * d + 2 * f], x, a);
-            a = fmaf(a_s[h * d + 2 * f + 1], y, a);
-            a = fmaf(w_s[h * F + f], r, a);
-            acc[h] = a;
-          }
-        }
+        for (int u = 0; u < 4; ++u) band(c8 * 4 + u, bf16_lo_s(wd[u]), bf16_hi_s(wd[u]));
+      }
+    } else if (key < tk.nkeys) {
+      // half split: four bands per step, real parts from the first half of
+      // the row, imaginary parts from the second (8-byte loads: d/2 is a
+      // multiple of 4, not always of 8)
+      const uint2* rp = reinterpret_cast<const uint2*>(k + (tk.row0 + tk.key0 + key) * d);
+      for (int c4 = 0; c4 < (F >> 2); ++c4) {
+        const uint2 re = rp[c4], im = rp[(F >> 2) + c4];
+        band(4 * c4 + 0, bf16_lo_s(re.x), bf16_lo_s(im.x));
+        band(4 * c4 + 1, bf16_hi_s(re.x), bf16_hi_s(im.x));
+        band(4 * c4 + 2, bf16_lo_s(re.y), bf16_lo_s(im.y));
+        band(4 * c4 + 3, bf16_hi_s(re.y), bf16_hi_s(im.y));
       }
     }
 #pragma unroll
@@ -248,28 +260,33 @@ __global__ __launch_bounds__(256) void zmax_kernel(
 
 template <int GT>
 static void launch_raw(int grid, hipStream_t st, const SeqInfo* seqs, int S, int Hkv, int Hq,
-                       int G, int d, const double2* P, const float* W, const double2* E,
-                       const uint16_t* k, float* raw, double* cs) {
+                       int G, int d, bool half, const double2* P, const float* W,
+                       const double2* E, const uint16_t* k, float* raw, double* cs) {
   hipLaunchKernelGGL(score_raw_kernel<GT>, dim3(grid), dim3(256), 0, st, seqs, S, Hkv, Hq, G, d,
-                     P, W, E, k, raw, cs);
+                     half, P, W, E, k, raw, cs);
 }
 
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W, const double2* E,
                         const uint16_t* k, float* raw, double* chunk_stats, double* unit_stats,
-                        float* scores, double* head_stats, hipStream_t st) {
+                        float* scores, double* head_stats, bool half, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const int Hq = Hkv * G;
   if (G <= 1)
-    launch_raw<1>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+    launch_raw<1>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+                  chunk_stats);
   else if (G <= 2)
-    launch_raw<2>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+    launch_raw<2>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+                  chunk_stats);
   else if (G <= 4)
-    launch_raw<4>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+    launch_raw<4>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+                  chunk_stats);
   else if (G <= 8)
-    launch_raw<8>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+    launch_raw<8>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+                  chunk_stats);
   else
-    launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, P, W, E, k, raw, chunk_stats);
+    launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+                  chunk_stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, unit_stats, scores,

@@ -124,8 +124,9 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&v)[8]) {
 // fp64 coefficients of the row the lane feeds at tile position m = lane%16
 // (slot m/4, entry m%4; head and offset from the slot layout above),
 //   a_f = P[l][h][f] E[s][f] exp(i omega_f delta),
-// for the lane's four bands of the step, and stores their bf16 hi/mid/lo
-// splits in MFMA A-operand lane order.  Rows past |D| repeat the first
+// for the lane's eight elements of the step (the real or imaginary part of
+// each element's band, by the RoPE layout), and stores their bf16
+// hi/mid/lo splits in MFMA A-operand lane order.  Rows past |D| repeat the first
 // offset; rows of heads outside the pass are zero.
 //
 // The norm term sum_f w_f |k_f| runs on the same bf16 MFMA: with
@@ -133,13 +134,14 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&v)[8]) {
 // terms, three products per 16 bands,
 //   [w1 w1].[r1 r2] + [w2 w2].[r1 r2] + [w1 w3].[r3 r1],
 // keep every term down to 2^-24 of w r.  Lane (m, q) of step st feeds
-// bands b_u = 16 st + 4q + u as k = 8q + {r(b0) r(b1) r'(b0) r'(b1)
-// r(b2) r(b3) r'(b2) r'(b3)}, the order in which bf16 pairs come out of
-// the key words.  wpack holds the three A operands per (unit, pass, step),
+// the bands of its four norm slots, b_u = slot_band(st, q, u) (16 st + 4q
+// + u when interleaved), as k = 8q + {r(b0) r(b1) r'(b0) r'(b1) r(b2)
+// r(b3) r'(b2) r'(b3)}, the order in which bf16 pairs come out of the
+// split.  wpack holds the three A operands per (unit, pass, step),
 // row r = 4q' + i carrying the pass's local head 4i + q'.
 template <int STEPS>
 __global__ __launch_bounds__(256) void pack_max_operands_kernel(
-    int S, int L, int Hkv, int G, MaxOffsetsPlan mp, int nD, double theta,
+    int S, int L, int Hkv, int G, bool half, MaxOffsetsPlan mp, int nD, double theta,
     const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
     const double* __restrict__ offsets, uint4* __restrict__ apack, uint4* __restrict__ wpack) {
   constexpr int F = STEPS * 16;
@@ -176,11 +178,14 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
     const int h = pass * mp.hp + hl;
     const bool live = hl < mp.hp && h < G;
     const double delta = offsets[j < nD ? j : 0];
+    // element j of the lane's eight: the real or imaginary part (by the
+    // RoPE layout) of its band's coefficient
     uint32_t h3[8], m3[8], l3[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = 4 * (4 * st + q) + u;
-      double re = 0.0, im = 0.0;
+    for (int j = 0; j < 8; ++j) {
+      const int e = 32 * st + 8 * q + j;
+      const int f = elem_band(e, D, half);
+      double x = 0.0;
       if (live) {
         const double2 pv = P[((int64_t)l * Hq + g * G + h) * F + f];
         const double2 ev = E[(int64_t)s * F + f];
@@ -188,11 +193,9 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
         double sn, cs;
         sincos(omega * delta, &sn, &cs);
         const double ar = pv.x * ev.x - pv.y * ev.y, ai = pv.x * ev.y + pv.y * ev.x;
-        re = ar * cs - ai * sn;
-        im = ar * sn + ai * cs;
+        x = elem_part(e, D, half) ? ar * sn + ai * cs : ar * cs - ai * sn;
       }
-      split3_m(re, h3[2 * u], m3[2 * u], l3[2 * u]);
-      split3_m(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+      split3_m(x, h3[j], m3[j], l3[j]);
     }
     uint4* op = apack + (idx >> 6) * 3 * 64 + lane;
     op[0] = pack8(h3);
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
     if (hl < mp.hp && h < G) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        wv[u] = W[((int64_t)l * Hq + g * G + h) * F + 4 * (4 * st + q) + u];
+        wv[u] = W[((int64_t)l * Hq + g * G + h) * F + slot_band(st, q, u, STEPS, half)];
     }
     uint32_t a1, a2, a3, c1, c2, c3;  // splits of (w_b0, w_b1) and (w_b2, w_b3)
     split3_pair(wv[0], wv[1], a1, a2, a3);
@@ -276,7 +279,7 @@ __device__ __forceinline__ void load_item_keys(const SeqInfo* seqs, int S, int L
 // the same GB*NE raw stores per group (rows past the ticket or heads past
 // the pass go to `sink`), so the load/store counter waits for the
 // prefetched keys stay exact.
-template <int STEPS, int GB, int NE>
+template <int STEPS, int GB, int NE, bool HALF>
 __global__ __launch_bounds__(kThreads) void score_max_kernel(
     const SeqInfo* __restrict__ seqs, int S, int LH, int G, MaxOffsetsPlan mp, int total_tickets,
     const uint4* __restrict__ apack, const uint4* __restrict__ wpack,
@@ -413,12 +416,14 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
           __builtin_memcpy(&aw3, &w3, 16);
 #pragma unroll
           for (int bb = 0; bb < GB; ++bb) {
-            const uint4 kw = kb[bb][st];
+            // magnitudes of the bands of the step's four norm slots
             uint32_t r1a, r2a, r3a, r1b, r2b, r3b;
-            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(kw.x)),
-                        __builtin_amdgcn_sqrtf(band_sq_m(kw.y)), r1a, r2a, r3a);
-            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(kw.z)),
-                        __builtin_amdgcn_sqrtf(band_sq_m(kw.w)), r1b, r2b, r3b);
+            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(slot_pair<STEPS, HALF>(kb[bb], st, 0))),
+                        __builtin_amdgcn_sqrtf(band_sq_m(slot_pair<STEPS, HALF>(kb[bb], st, 1))),
+                        r1a, r2a, r3a);
+            split3_pair(__builtin_amdgcn_sqrtf(band_sq_m(slot_pair<STEPS, HALF>(kb[bb], st, 2))),
+                        __builtin_amdgcn_sqrtf(band_sq_m(slot_pair<STEPS, HALF>(kb[bb], st, 3))),
+                        r1b, r2b, r3b);
             const uint4 b12 = make_uint4(r1a, r2a, r1b, r2b);
             const uint4 b31 = make_uint4(r3a, r1a, r3b, r1b);
             bf16x8m_t bx, by;
@@ -546,7 +551,7 @@ size_t max_offsets_operand_bytes(int d, int G, const MaxOffsetsPlan& mp, int64_t
   return ops + (size_t)tickets * kWaves * G * 2 * sizeof(double) + 64 * sizeof(float);
 }
 
-template <int STEPS>
+template <int STEPS, bool HALF>
 static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G, int nD,
                                const MaxOffsetsPlan& mp, double theta, int total_tickets,
                                const double2* P, const float* W, const double2* E,
@@ -558,8 +563,8 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
   double* wsum = reinterpret_cast<double*>(wpack + units * mp.npass * STEPS * 3 * 64);
   const int64_t threads = units * mp.npass * mp.ptiles * STEPS * 64 + units * mp.npass * STEPS * 64;
   hipLaunchKernelGGL(pack_max_operands_kernel<STEPS>, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, st, S, L, Hkv, G, mp, nD, theta, P, W, E, offsets, apack,
-                     wpack);
+                     dim3(256), 0, st, S, L, Hkv, G, HALF, mp, nD, theta, P, W, E, offsets,
+                     apack, wpack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = ((size_t)mp.ptiles + 1) * STEPS * 3 * 64 * sizeof(uint4);
@@ -568,7 +573,8 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
   float* sink = reinterpret_cast<float*>(wsum + (int64_t)total_tickets * kWaves * G * 2);
   const int ne = (mp.hp + 3) / 4;
 #define TRI_LAUNCH(NE)                                                                         \
-  hipLaunchKernelGGL((score_max_kernel<STEPS, GB, NE>), dim3(grid), dim3(kThreads), lds, st,   \
+  hipLaunchKernelGGL((score_max_kernel<STEPS, GB, NE, HALF>), dim3(grid), dim3(kThreads), lds, \
+                     st,                                                                       \
                      seqs, S, L * Hkv, G, mp, total_tickets, apack, wpack, k, raw, wsum, sink)
   if (ne == 1)
     TRI_LAUNCH(1);
@@ -590,22 +596,32 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
                             float* raw, double* chunk_stats, double* unit_stats, float* scores,
-                            double* head_stats, hipStream_t st) {
+                            double* head_stats, bool half, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   if (!mp.ok) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
-  switch (d / 32) {
-#define TRI_CASE(n)                                                                         \
-  case n:                                                                                   \
-    e = launch_max_t<n>(seqs, S, L, Hkv, G, nD, mp, theta, total_tickets, P, W, E, offsets, \
-                        operands, k, raw, chunk_stats, st);                                 \
+#define TRI_CASE(n, h)                                                                         \
+  case n:                                                                                      \
+    e = launch_max_t<n, h>(seqs, S, L, Hkv, G, nD, mp, theta, total_tickets, P, W, E, offsets, \
+                           operands, k, raw, chunk_stats, st);                                 \
     break;
-    TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7)
-    TRI_CASE(8)
-#undef TRI_CASE
-    default:
-      return hipErrorInvalidValue;
+  // half split keeps both parts of a band in one lane only with an even
+  // number of 32-wide steps
+  if (half) {
+    switch (d / 32) {
+      TRI_CASE(2, true) TRI_CASE(4, true) TRI_CASE(6, true) TRI_CASE(8, true)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    switch (d / 32) {
+      TRI_CASE(1, false) TRI_CASE(2, false) TRI_CASE(3, false) TRI_CASE(4, false)
+      TRI_CASE(5, false) TRI_CASE(6, false) TRI_CASE(7, false) TRI_CASE(8, false)
+      default:
+        return hipErrorInvalidValue;
+    }
   }
+#undef TRI_CASE
   if (e != hipSuccess) return e;
   return launch_zmax(seqs, S, L, Hkv, G, total_tickets, raw, chunk_stats, unit_stats, scores,
                      head_stats, st);

@@ -221,7 +221,7 @@ __device__ __forceinline__ void load_operands(const Chunk& ck, const uint4* __re
   }
 }
 
-template <int STEPS>
+template <int STEPS, bool HALF>
 __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
                                           const UnitOperands<STEPS>& op,
                                           const uint16_t* __restrict__ k, float* raw,
@@ -239,11 +239,11 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
           // band magnitudes first (independent VALU work), then the trig
-          // MFMAs, then the norm MFMAs that consume the magnitudes
-          const uint32_t wd[4] = {ring[j][st].x, ring[j][st].y, ring[j][st].z, ring[j][st].w};
+          // MFMAs, then the norm MFMAs that consume the magnitudes; slot
+          // (st, u) of the norm stands for band slot_band(st, q, u)
           float r[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) r[u] = band_sq(wd[u]);
+          for (int u = 0; u < 4; ++u) r[u] = band_sq(slot_pair<STEPS, HALF>(ring[j], st, u));
 #pragma unroll
           for (int u = 0; u < 4; ++u) r[u] = __builtin_amdgcn_sqrtf(r[u]);
           bf16x8_t bk;
@@ -258,7 +258,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           // (left alone, the scheduler funnels them through one register and
           // pads every step with wait states): the dot2s and their operand
           // clears, the trig MFMAs, the square roots, the norm MFMAs.
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, HALF ? 12 : 8, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
           __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
@@ -465,7 +465,7 @@ __device__ __forceinline__ void chunk_store_scores(const Chunk& ck, const float*
 
 // STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
 // tickets.  ch = keys per ticket.
-template <int STEPS>
+template <int STEPS, bool HALF>
 __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
     const uint4* __restrict__ apack, const uint16_t* __restrict__ k,
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
-    if (have) chunk_raw<STEPS>(ck, G, rs, op, k, buf_cur, ring);
+    if (have) chunk_raw<STEPS, HALF>(ck, G, rs, op, k, buf_cur, ring);
     if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
@@ -558,13 +558,14 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
 
 // MFMA operand pack of every unit (s, l, g): thread (unit, st, lane) forms
 // A_f = P[l][h][f] * E[s][f] (fp64) for the lane's head h = g*G + lane%16
-// and its four bands of step st, splits Re/Im into bf16 hi/mid/lo and
-// stores them with the fp32 norm weights W[l][h][f] (zeros for lanes
-// beyond G).
+// and the bands of its eight elements of step st, splits each element's
+// part (Re or Im, by the RoPE layout) into bf16 hi/mid/lo and stores them
+// with the fp32 norm weights W[l][h][f] of the step's four norm slots
+// (zeros for lanes beyond G).
 template <int STEPS>
 __global__ __launch_bounds__(256) void pack_operands_kernel(
-    int S, int L, int Hkv, int G, const double2* __restrict__ P, const float* __restrict__ W,
-    const double2* __restrict__ E, uint4* __restrict__ apack) {
+    int S, int L, int Hkv, int G, bool half, const double2* __restrict__ P,
+    const float* __restrict__ W, const double2* __restrict__ E, uint4* __restrict__ apack) {
   constexpr int F = STEPS * 16;
   const int64_t units = (int64_t)S * L * Hkv;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -577,25 +578,25 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
   const int l = lg / Hkv, g = lg % Hkv;
   const int m = lane & 15, q = lane >> 4;
   const int Hq = Hkv * G;
+  constexpr int D = STEPS * 32;
   uint32_t h3[8], m3[8], l3[8];
   float wv[4];
   const bool live = m < G;
   const int64_t pbase = ((int64_t)l * Hq + g * G + (live ? m : 0)) * F;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int f = 4 * (4 * st + q) + u;
-    double re = 0.0, im = 0.0;
-    wv[u] = 0.f;
+  for (int j = 0; j < 8; ++j) {
+    const int e = 32 * st + 8 * q + j;
+    const int f = elem_band(e, D, half);
+    double x = 0.0;
     if (live) {
       const double2 pv = P[pbase + f];
       const double2 ev = E[(int64_t)s * F + f];
-      re = pv.x * ev.x - pv.y * ev.y;
-      im = pv.x * ev.y + pv.y * ev.x;
-      wv[u] = W[pbase + f];
+      x = elem_part(e, D, half) ? pv.x * ev.y + pv.y * ev.x : pv.x * ev.x - pv.y * ev.y;
     }
-    split3(re, h3[2 * u], m3[2 * u], l3[2 * u]);
-    split3(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+    split3(x, h3[j], m3[j], l3[j]);
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) wv[u] = live ? W[pbase + slot_band(st, q, u, STEPS, half)] : 0.f;
   auto pack8 = [](const uint32_t (&v)[8]) {
     return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
                       v[6] | (v[7] << 16));
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
                                      __float_as_uint(wv[2]), __float_as_uint(wv[3]));
 }
 
-template <int STEPS>
+template <int STEPS, bool HALF>
 static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
                                  const double2* P, const float* W, const double2* E,
@@ -616,10 +617,10 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
                                  float* scores, float* raw, double* hs) {
   const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
   hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
-                     dim3(256), 0, st, S, L, Hkv, G, P, W, E, apack);
+                     dim3(256), 0, st, S, L, Hkv, G, HALF, P, W, E, apack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS>);
+  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF>);
   static const hipError_t attr = hipFuncSetAttribute(
       kern, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds);
   if (attr != hipSuccess) return attr;
@@ -632,12 +633,16 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
   if (per_cu < 1) per_cu = 1;
   int grid = cus * per_cu;
   if (grid > total_tickets) grid = total_tickets;
-  hipLaunchKernelGGL(score_fused_kernel<STEPS>, dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
+  hipLaunchKernelGGL((score_fused_kernel<STEPS, HALF>), dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
                      L, Hkv, G, ch, total_tickets, apack, k, cs, ctrl, scores, raw, hs);
   return hipGetLastError();
 }
 
-bool fused_supported(int d) { return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim; }
+// Half split needs an even number of 32-wide steps (both parts of a band
+// in one lane's words).
+bool fused_supported(int d, bool half) {
+  return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim && (!half || d % 64 == 0);
+}
 
 // Keys per ticket: as many as let three work-groups (two raw buffers of G
 // heads each) share a CU's LDS, in multiples of 64, at most 1024.
@@ -650,28 +655,36 @@ int fused_chunk_keys(int G) {
 }
 
 size_t fused_operand_bytes(int d, int64_t units) {
-  return fused_supported(d) ? (size_t)units * (4 * (d / 32)) * 64 * sizeof(uint4) : 0;
+  return fused_supported(d, false) ? (size_t)units * (4 * (d / 32)) * 64 * sizeof(uint4) : 0;
 }
 
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, hipStream_t st) {
+                              double* head_stats, bool half, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)G * (ch + kRawPad) * sizeof(float);
-  if (lds > (size_t)kFusedMaxLds) return hipErrorInvalidValue;
+  if (lds > (size_t)kFusedMaxLds || !fused_supported(d, half)) return hipErrorInvalidValue;
   uint4* ap = reinterpret_cast<uint4*>(apack);
+#define TRI_CASE(n, h)                                                                        \
+  case n:                                                                                     \
+    return launch_fused_t<n, h>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, \
+                                k, chunk_stats, ctrl, scores, raw, head_stats);
+  if (half) {
+    switch (d / 32) {
+      TRI_CASE(2, true) TRI_CASE(4, true) TRI_CASE(6, true) TRI_CASE(8, true)
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (d / 32) {
-#define TRI_CASE(n)                                                                          \
-  case n:                                                                                    \
-    return launch_fused_t<n>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, k, \
-                             chunk_stats, ctrl, scores, raw, head_stats);
-    TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7) TRI_CASE(8)
-#undef TRI_CASE
+    TRI_CASE(1, false) TRI_CASE(2, false) TRI_CASE(3, false) TRI_CASE(4, false)
+    TRI_CASE(5, false) TRI_CASE(6, false) TRI_CASE(7, false) TRI_CASE(8, false)
     default:
       return hipErrorInvalidValue;
   }
+#undef TRI_CASE
 }
 
 }  // namespace tri

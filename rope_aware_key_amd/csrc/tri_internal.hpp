@@ -37,6 +37,50 @@ constexpr int kMaxOffsets = 4096;
 // the whole 160 KB of a gfx950 CU.
 constexpr size_t kMaxOffsetsLds = 160 * 1024;
 
+// RoPE pair layouts.  Band f of a d-vector is (x_{2f}, x_{2f+1})
+// (interleaved, the talk page's rotation equation) or (x_f, x_{f+d/2})
+// (half split, the layout of the LLaMA/Mistral implementations the
+// tutorial page's RoPE paragraph names).
+__host__ __device__ __forceinline__ int elem_band(int e, int d, bool half) {
+  return half ? (e < (d >> 1) ? e : e - (d >> 1)) : (e >> 1);
+}
+// 0: element e is the real part of its band, 1: the imaginary part.
+__host__ __device__ __forceinline__ int elem_part(int e, int d, bool half) {
+  return half ? (e >= (d >> 1)) : (e & 1);
+}
+
+// The MFMA kernels hand lane (m, q) the key elements 32 st + 8q .. +7 of
+// step st as four 32-bit words.  The norm term needs one magnitude per
+// (step, word) slot; slot_band names the band it stands for.  Interleaved:
+// word u holds band 16 st + 4q + u whole.  Half split (an even number of
+// steps): the band's two parts sit in word u of steps st and st + steps/2,
+// the low halves forming band 32 st + 8q + 2u and the high halves band
+// 32 st + 8q + 2u + 1; slot (st, u) takes the first for st < steps/2 and
+// the second for the rest.
+__host__ __device__ __forceinline__ int slot_band(int st, int q, int u, int steps, bool half) {
+  if (!half) return 16 * st + 4 * q + u;
+  const int h = steps >> 1;
+  return st < h ? 32 * st + 8 * q + 2 * u : 32 * (st - h) + 8 * q + 2 * u + 1;
+}
+
+__device__ __forceinline__ uint32_t uint4_word(const uint4& v, int u) {
+  return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
+}
+
+// The two bf16 parts of slot (st, u)'s band as one bf16 pair (real, imag),
+// from the lane's key words kw[0 .. STEPS-1].
+template <int STEPS, bool HALF>
+__device__ __forceinline__ uint32_t slot_pair(const uint4 (&kw)[STEPS], int st, int u) {
+  if (!HALF) return uint4_word(kw[st], u);
+  constexpr int H = STEPS / 2;
+  if (st < H) {
+    const uint32_t a = uint4_word(kw[st], u), b = uint4_word(kw[st + H], u);
+    return (a & 0xffffu) | (b << 16);
+  }
+  const uint32_t a = uint4_word(kw[st - H], u), b = uint4_word(kw[st], u);
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
 // Largest s with seqs[s].chunk_base <= t (sequences with no tickets share
 // chunk_base with their successor, so the search lands on the owner).
 __device__ __forceinline__ int find_seq_by_ticket(const SeqInfo* seqs, int S, int t) {
@@ -62,7 +106,7 @@ __device__ __forceinline__ int find_seq_by_out_row(const SeqInfo* seqs, int S, i
 // launch.
 // Calibration scratch: the (sample, band) phasor table and per-chunk sums.
 size_t calibrate_workspace_bytes(int L, int Hq, int d, int64_t n_samples);
-hipError_t launch_calibrate(int L, int Hq, int d, double theta, const uint16_t* q,
+hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const uint16_t* q,
                             const int32_t* q_pos, int64_t n_samples, float* centre,
                             float* absmean, float* R, void* workspace, hipStream_t st);
 
@@ -76,7 +120,7 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
                            float* W, double2* E, uint32_t* ctrl, double* stat_slots,
                            int64_t n_stat_slots, hipStream_t st);
 
-bool fused_supported(int d);
+bool fused_supported(int d, bool half);
 // Keys per ticket of the fused path for a GQA group of G heads.
 int fused_chunk_keys(int G);
 // Most chunks one unit may have on the fused path.  Its waits need more
@@ -92,14 +136,14 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, hipStream_t st);
+                              double* head_stats, bool half, hipStream_t st);
 
 // unit_stats: [units][G][2] fp64 scratch for the per-unit (mu, 1/sigma).
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W,
                         const double2* E, const uint16_t* k, float* raw,
                         double* chunk_stats, double* unit_stats, float* scores,
-                        double* head_stats, hipStream_t st);
+                        double* head_stats, bool half, hipStream_t st);
 
 // z pass of the generic path: merges the (count, mean, M2) tickets of each
 // unit into unit_stats ([units][G][2]: mu, 1/sigma; head_stats gets mu,
@@ -132,7 +176,7 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
                             float* raw, double* chunk_stats, double* unit_stats, float* scores,
-                            double* head_stats, hipStream_t st);
+                            double* head_stats, bool half, hipStream_t st);
 
 // Decode-loop driver: where one appended token of sequence s goes (row of
 // unit 0; unit lg at row0 + lg*stride) and its position.
@@ -155,6 +199,7 @@ hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int rece
 // trig_corr_workspace_bytes() of scratch.
 size_t trig_corr_workspace_bytes(int L, int Hq, int64_t n_q);
 hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t n_k, double theta,
+                            bool half,
                             const uint16_t* q, const int32_t* q_pos, const uint16_t* k,
                             const int32_t* k_pos, const float* q_centre, double* partial,
                             double* r, hipStream_t st);

@@ -30,10 +30,29 @@ def dev_read(ptr: int, count: int, dtype) -> np.ndarray:
     return out
 
 
+def layout_of(case: Case) -> str:
+    return case.meta.get("rope_layout", "interleaved")
+
+
 def shape_of(case: Case):
     import rope_aware_key_amd as R
     sh = case.shape
-    return R.make_shape(sh.head_dim, sh.num_q_heads, sh.num_kv_heads, sh.num_layers, sh.rope_theta)
+    return R.make_shape(sh.head_dim, sh.num_q_heads, sh.num_kv_heads, sh.num_layers, sh.rope_theta,
+                        rope_layout=layout_of(case))
+
+
+def half_split(case: Case) -> Case:
+    """The same case stored in the half-split RoPE layout: the columns of
+    every key row and calibration query are permuted from (x0, x1, x2, ..)
+    to (x0, x2, .., x1, x3, ..), so band f moves from (2f, 2f+1) to
+    (f, f + d/2).  Values are not rotated and stay as they are."""
+    import dataclasses
+    d = case.shape.head_dim
+    perm = torch.as_tensor(np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)]),
+                           device=case.k.device)
+    cq = None if case.calib_q is None else case.calib_q[..., perm].contiguous()
+    return dataclasses.replace(case, k=case.k[:, perm].contiguous(), calib_q=cq,
+                               meta=dict(case.meta, rope_layout="half"))
 
 
 def pinned(a, dtype):
@@ -142,7 +161,8 @@ def oracle_unit(case: Case, s, l, g, factored=False, stats=None, offsets=None,
     kpost = O.bf16_bits_to_f64(kbits)
     extra = {} if offsets is None else dict(offsets=np.asarray(offsets, np.float64))
     score, S, mu, sigma = O.unit_scores(kpost, pos, float(case.cur_pos[s]), centre, absmean, Rr,
-                                        om, factored=factored, reduce=reduce, **extra)
+                                        om, factored=factored, reduce=reduce,
+                                        layout=layout_of(case), **extra)
     return start, n, score, S, mu, sigma
 
 

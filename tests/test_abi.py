@@ -336,3 +336,34 @@ def test_select_compact_layers_argument_checks():
     assert _status(sel, v_out=None) == ST["INVALID"]
     assert _status(sel) == ST["WORKSPACE"]
     assert _status(sel, budget=[[0, 0, 0], [0, 0, 0]]) == 0
+
+
+def test_shape_struct_layout_and_rope_layout_field():
+    """tri_shape: four int32, the double at byte 16, rope_layout at byte 24
+    (32 bytes with padding), matching the C declaration."""
+    import ctypes
+    assert ctypes.sizeof(R.TriShape) == 32
+    assert R.TriShape.rope_theta.offset == 16 and R.TriShape.rope_layout.offset == 24
+    assert R.make_shape(64, 4, 2, 1).rope_layout == R.TRI_ROPE_INTERLEAVED
+    assert R.make_shape(64, 4, 2, 1, rope_layout="half").rope_layout == R.TRI_ROPE_HALF_SPLIT
+    bad = R.make_shape(64, 4, 2, 1, rope_layout=2)
+    assert _status(_score, bad, [0, 8], [8]) == ST["INVALID"]
+    assert "rope_layout" in R.last_error()
+    assert R.tri_workspace_bytes(bad, [0, 8]) == 0
+    # half split: every head_dim the interleaved layout takes is accepted
+    for d in (8, 24, 96, 128, 256):
+        sh = R.make_shape(d, 4, 2, 1, rope_layout="half")
+        assert R.tri_workspace_bytes(sh, [0, 8]) > 0
+        assert _status(_score, sh, [0, 8], [8]) == ST["WORKSPACE"]
+
+
+def test_max_offsets_half_split_needs_d_multiple_of_64():
+    offs = np.array([1.0, 2.0, 4.0])
+    for d, ok in ((96, False), (160, False), (64, True), (128, True)):
+        sh = R.make_shape(d, 4, 2, 1, rope_layout="half")
+        got = R.tri_workspace_bytes_offsets(sh, [0, 8], len(offs), "max")
+        assert (got > 0) == ok, (d, got)
+        if not ok:
+            assert "half-split" in R.last_error()
+        # the mean over the same set has no such limit
+        assert R.tri_workspace_bytes_offsets(sh, [0, 8], len(offs), "mean") > 0

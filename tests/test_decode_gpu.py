@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 import synth
-from harness import check_scores, dev_read, shape_of
+from harness import check_scores, dev_read, half_split, layout_of, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -24,11 +24,13 @@ class Stream:
     """One synthetic decode run: sequence s has n_pre[s] prompt keys and
     `steps` generated ones, all drawn at positions 0, 1, 2, ..."""
 
-    def __init__(self, shape, n_pre, steps, seed):
+    def __init__(self, shape, n_pre, steps, seed, layout="interleaved"):
         self.shape, self.n_pre, self.steps = shape, list(n_pre), steps
         lens = tuple(n + steps for n in n_pre)
         self.case = synth.build_case("decode", shape, lens, tuple([1] * len(lens)), device=DEV,
                                      seed=seed)
+        if layout == "half":
+            self.case = half_split(self.case)
         self.S = len(n_pre)
         self.LH = shape.num_layers * shape.num_kv_heads
 
@@ -77,7 +79,8 @@ def _prune_oracle(st, dec, units, s, B, sink, recent, p_q, check=True):
         prot = O.protected_mask(n, sink, recent)
         assert np.all(np.isposinf(gpu[prot]))
         if check:
-            ref = u.scores(*st.stats(lg // H, lg % H), om, factored=True, p_q=p_q)
+            ref = u.scores(*st.stats(lg // H, lg % H), om, factored=True, p_q=p_q,
+                           layout=layout_of(st.case))
             check_scores(gpu[~prot], ref[~prot], f"prune of unit {(s, lg)}")
         u.prune(O.select_protected(gpu, B, sink, recent))
 
@@ -98,9 +101,10 @@ def _check_cache(st, dec, units):
             assert np.array_equal(v, u.v), f"V of unit {(s, lg)}"
 
 
-def _run(shape, n_pre, steps, B, interval, sink, recent, seed, check_every=1, check_scores=True):
+def _run(shape, n_pre, steps, B, interval, sink, recent, seed, check_every=1, check_scores=True,
+         layout="interleaved"):
     import rope_aware_key_amd as R
-    st = Stream(shape, n_pre, steps, seed)
+    st = Stream(shape, n_pre, steps, seed, layout)
     c = st.case
     C = B + interval
     dec = R.Decode(shape_of(c), st.S, B, interval, c.q_centre, c.q_absmean, c.q_R,
@@ -155,6 +159,15 @@ def test_decode_loop_generic_path_and_ragged():
     lengths, an interval of 1 (a prune after every append once full)."""
     shape = synth.Shape(48, 6, 2, 1)
     _run(shape, [0, 5, 19, 20, 33], 12, B=18, interval=1, sink=1, recent=2, seed=11)
+
+
+@pytest.mark.parametrize("d", [128, 48])
+def test_decode_loop_half_split(d):
+    """Keys stored half split (MFMA path at d = 128, VALU path at 48)."""
+    shape = synth.Shape(d, 4, 2, 1)
+    prunes = _run(shape, [20, 45], 24, B=30, interval=6, sink=2, recent=3, seed=17,
+                  layout="half")
+    assert prunes >= 4
 
 
 def test_decode_loop_protected_fill_budget():
