@@ -29,10 +29,10 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_c3.json")
-# The fused score kernel, its operand pack and launch shape (score_mfma.hip)
-# and the prologue (calib.hip): the kernels one tri_score call runs on the
-# 32K->2048 workload.
-KERNEL_SOURCES = ["score_mfma.hip", "calib.hip"]
+# The fused score kernel, its operand pack and launch shape (score_mfma.hip),
+# the prologue (calib.hip) and the shared device helpers (tri_internal.hpp):
+# the kernels one tri_score call runs on the 32K->2048 workload.
+KERNEL_SOURCES = ["score_mfma.hip", "calib.hip", "tri_internal.hpp"]
 
 
 def kernel_source_hash():

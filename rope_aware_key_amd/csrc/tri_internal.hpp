@@ -73,12 +73,11 @@ template <int STEPS, bool HALF>
 __device__ __forceinline__ uint32_t slot_pair(const uint4 (&kw)[STEPS], int st, int u) {
   if (!HALF) return uint4_word(kw[st], u);
   constexpr int H = STEPS / 2;
-  if (st < H) {
-    const uint32_t a = uint4_word(kw[st], u), b = uint4_word(kw[st + H], u);
-    return (a & 0xffffu) | (b << 16);
-  }
-  const uint32_t a = uint4_word(kw[st - H], u), b = uint4_word(kw[st], u);
-  return (a >> 16) | (b & 0xffff0000u);
+  // one v_perm_b32 each: bytes {0,1} of a and b, or bytes {2,3} (selector
+  // bytes 0-3 pick from a, 4-7 from b)
+  if (st < H)
+    return __builtin_amdgcn_perm(uint4_word(kw[st + H], u), uint4_word(kw[st], u), 0x05040100u);
+  return __builtin_amdgcn_perm(uint4_word(kw[st], u), uint4_word(kw[st - H], u), 0x07060302u);
 }
 
 // Largest s with seqs[s].chunk_base <= t (sequences with no tickets share
