@@ -42,6 +42,9 @@ Sources (cited by page title and the section or equation on that page):
               queries and keys in LLaMA and Mistral, whose common
               implementations pair element f with element f + d/2 ("half
               split") rather than 2f with 2f + 1.
+* [paged]     same tutorial page, deployment paragraph: engines keep the KV
+              cache in pages (PagedAttention in vLLM), each sequence's
+              logical blocks mapped to physical pages by a table.
 * [recon]     shibing624 blog review, Fig. 1(D) (the trig series built from
               the centres against the real attention logits) and Fig. 7
               (per-head Pearson correlation of that reconstruction).
@@ -69,6 +72,11 @@ again in the design notes):
 * Pyramid budgets: linear in the layer index, b_l = round(b_0 + (b_{L-1} -
   b_0) l / (L - 1)) with b_{L-1} = ratio * b_0 and mean (b_0 + b_{L-1}) / 2
   equal to the requested mean (the pages give the shape, not a formula).
+* Paged cache: a page holds P consecutive tokens of a sequence for every
+  layer and KV head; one table per sequence (shared by its layers and heads)
+  gives the physical page of each logical page; row strides per page, token,
+  head and layer place every (page, slot, layer, head) row in the pool, so
+  both head-major and token-major pages are described.
 * Decode loop: a unit is pruned to B when it reaches B + interval keys
   (interval 128), scored at the position of its newest key; the first
   `sink` and the last `recent` keys are kept whatever their score and count
@@ -532,4 +540,21 @@ def out_rows_layers(cu_len, budgets, L: int, Hkv: int, s: int, l: int, g: int):
                 return acc + g * b, b
             acc += Hkv * b
     raise IndexError((s, l, g))
+
+
+# --------------------------------------------------------------------------
+# Paged cache addressing  [paged]
+# --------------------------------------------------------------------------
+def paged_row(table, P: int, strides, s: int, l: int, g: int, i: int) -> int:
+    """Pool row of token i of unit (s, l, g): logical page i // P of sequence
+    s is physical page table[s][i // P], slot i % P within it.  strides =
+    (page, token, head, layer) row strides."""
+    page_st, token_st, head_st, layer_st = strides
+    page = int(table[s][i // P])
+    return l * layer_st + g * head_st + page * page_st + (i % P) * token_st
+
+
+def paged_unit_rows(table, P: int, strides, s: int, l: int, g: int, n: int) -> np.ndarray:
+    """Pool rows of the n tokens of unit (s, l, g), in token order."""
+    return np.array([paged_row(table, P, strides, s, l, g, i) for i in range(n)], dtype=np.int64)
 

@@ -721,3 +721,42 @@ def test_half_split_calibration_and_reconstruction():
     r2 = O.trig_reconstruction_r(_to_half(q[:, 0]), qpos, _to_half(k), kpos, c1[0][0], om,
                                  layout="half")
     assert abs(r1 - r2) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Paged cache addressing
+# --------------------------------------------------------------------------
+def test_paged_rows_by_hand():
+    g = GOLD["paged_rows_token_major"]
+    P, H = g["P"], g["Hkv"]
+    strides = (P * H, H, 1, 0)
+    for s, l, h, i, row in g["cases"]:
+        assert O.paged_row(g["table"], P, strides, s, l, h, i) == row
+
+
+def test_paged_rows_reduce_to_packed_layout():
+    """One sequence in one page whose strides are those of the packed layout
+    (unit (l, g) holds n consecutive rows): the same rows as unit_rows."""
+    n, L, H = 48, 3, 2
+    strides = (0, 1, n, H * n)           # page, token, head, layer
+    for l in range(L):
+        for g in range(H):
+            rows = O.paged_unit_rows([[0]], 64, strides, 0, l, g, n)
+            start, nn = O.unit_rows([0, n], L, H, 0, l, g)
+            np.testing.assert_array_equal(rows, np.arange(start, start + nn))
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+def test_paged_rows_cover_the_pool_once(head_major):
+    """Full pages under a permuted table: every pool row is used exactly once
+    (token-major and head-major pages)."""
+    rng = np.random.default_rng(31)
+    P, L, H, S, pages_per_seq = 4, 2, 3, 3, 5
+    npages = S * pages_per_seq
+    table = rng.permutation(npages).reshape(S, pages_per_seq)
+    page_rows = P * H
+    strides = (page_rows, 1, P, npages * page_rows) if head_major else \
+        (page_rows, H, 1, npages * page_rows)
+    rows = np.concatenate([O.paged_unit_rows(table, P, strides, s, l, g, P * pages_per_seq)
+                           for s in range(S) for l in range(L) for g in range(H)])
+    np.testing.assert_array_equal(np.sort(rows), np.arange(L * npages * page_rows))
