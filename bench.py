@@ -540,6 +540,9 @@ def main():
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
     ap.add_argument("--rope-layout", default="interleaved", choices=["interleaved", "half"],
                     help="store the keys half split (band f = x[f], x[f + d/2])")
+    ap.add_argument("--paged", type=int, default=None, metavar="PAGE_SIZE",
+                    help="K, V and positions in a paged pool (token-major pages of PAGE_SIZE "
+                         "tokens, random page order); compaction into a second pool")
     ap.add_argument("--pyramid", type=float, default=None, metavar="RATIO",
                     help="per-layer pyramid budgets (last/first = RATIO, mean = the "
                          "sequence's budget), selected by tri_select_compact_layers")
@@ -621,6 +624,22 @@ def main():
     if budgets is not None:
         wsb = max(wsb, R.tri_workspace_bytes_layers(sh, cu))
     ws = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
+    pool = out_pool = None
+    if args.paged is not None:
+        if budgets is not None or variant:
+            print("--paged runs with the default offsets and one budget per sequence",
+                  file=sys.stderr)
+            sys.exit(2)
+        P = args.paged
+        print(f"[bench] scattering the cache into {P}-token pages", file=sys.stderr, flush=True)
+        pool = synth.paged_from_case(case, P, seed=1)
+        need = [(case.kept(s) + P - 1) // P for s in range(case.num_seqs)]
+        out_pool = synth.empty_pool(case.num_seqs, case.shape.num_layers, case.shape.num_kv_heads,
+                                    d, P, need, spare=0, seed=2, device=dev)
+        pg_in = R.make_pages(pool.table, P, pool.num_pages, *pool.strides())
+        pg_out = R.make_pages(out_pool.table, P, out_pool.num_pages, *out_pool.strides())
+        torch.cuda.synchronize()
+        label = f"{label}+paged_{P}"
     scores = torch.empty(rows, dtype=torch.float32, device=dev)
     kept = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
     k_out = torch.empty(max(1, out_rows), d, dtype=torch.int16, device=dev)
@@ -629,7 +648,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def score():
-        if variant:
+        if pool is not None:
+            R.tri_score_paged(sh, cu, cp, pg_in, pool.k, case.q_centre, case.q_absmean, case.q_R,
+                              scores, workspace=ws, stream=stream)
+        elif variant:
             R.tri_score_offsets(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean,
                                 case.q_R, offs, args.reduce, scores, workspace=ws, stream=stream)
         else:
@@ -637,7 +659,11 @@ def main():
                         scores, workspace=ws, stream=stream)
 
     def select():
-        if budgets is not None:
+        if pool is not None:
+            R.tri_select_compact_paged(sh, cu, bu, scores, pg_in, pool.k, pool.v, pool.pos, kept,
+                                       pg_out, out_pool.k, out_pool.v, out_pool.pos, workspace=ws,
+                                       stream=stream)
+        elif budgets is not None:
             R.tri_select_compact_layers(sh, cu, bu, scores, case.k, case.v, case.k_pos, kept,
                                         k_out, v_out, pos_out, workspace=ws, stream=stream)
         else:

@@ -390,6 +390,77 @@ tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,
                                      void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/*
+ * Paged pools (tutorial page, deployment paragraph: engines keep the KV
+ * cache in pages, as vLLM's PagedAttention does).
+ *
+ * A page holds page_size consecutive tokens of one sequence for every layer
+ * and KV head.  page_table [device][num_seqs][max_pages] int32 gives the
+ * physical page of each logical page of a sequence (one table per sequence,
+ * shared by its layers and heads).  Token i of unit (s, l, g) is pool row
+ *   l*layer_stride + g*head_stride + page*page_stride + (i % page_size)*token_stride,
+ *   page = page_table[s][i / page_size];
+ * a K or V row is head_dim bf16 elements, a position row one int32.  The
+ * strides describe token-major pages ([page][slot][head]: token_stride =
+ * H_kv, head_stride = 1, page_stride = page_size*H_kv) as well as head-major
+ * ones ([page][head][slot]).  Page ids outside [0, num_pages) are clamped
+ * into that range (never an access outside the pool; results for such
+ * tokens are unspecified).  page_size: a power of two in [1, 65536];
+ * max_pages must cover ceil(n / page_size) for every sequence.  The table
+ * is read by the kernels; the caller keeps it alive until the stream has
+ * passed the call.
+ */
+typedef struct {
+  const int32_t* page_table; /* device [num_seqs][max_pages]               */
+  int32_t max_pages;         /* entries per sequence in page_table          */
+  int32_t num_pages;         /* pages in the pool                           */
+  int32_t page_size;         /* tokens per page (power of two)              */
+  int64_t page_stride;       /* rows from one page to the next              */
+  int64_t token_stride;      /* rows from one slot of a page to the next    */
+  int64_t head_stride;       /* rows from one KV head to the next           */
+  int64_t layer_stride;      /* rows from one layer to the next             */
+} tri_kv_pages;
+
+/*
+ * tri_score_paged -- tri_score (offsets == NULL) or tri_score_offsets
+ * (offsets given, reduced by `reduce`) with the keys read from a paged
+ * pool.  scores, raw_scores and head_stats keep the packed layout of
+ * tri_score.  Pages of at least 16 tokens take the fused MFMA kernel
+ * (head_dim % 32 == 0); smaller pages the VALU path, which needs more
+ * workspace: tri_workspace_bytes_paged (n_offsets 0 for the built-in set).
+ */
+size_t tri_workspace_bytes_paged(const tri_shape* shape, int32_t num_seqs,
+                                 const int64_t* cu_len, int32_t page_size,
+                                 int32_t n_offsets, int32_t reduce);
+
+tri_status tri_score_paged(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                           const int32_t* cur_pos, const tri_kv_pages* pages,
+                           const uint16_t* k_pool, const float* q_centre,
+                           const float* q_absmean, const float* q_R, const double* offsets,
+                           int32_t n_offsets, int32_t reduce, float* scores, float* raw_scores,
+                           double* head_stats, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * tri_select_compact_paged -- tri_select_compact with K, V and positions
+ * read from the paged pool in_pages describes and the kept rows written, in
+ * time order, to the pool out_pages describes: kept key j of unit (s, l, g)
+ * goes to that pool's row for token j of (s, l, g).  The two may share a
+ * pool (distinct pages: the call reads and writes at once).  kept_idx keeps
+ * the packed layout (indices are token indices within the unit).  Pools
+ * come in pairs (k_pool/k_out_pool, ...); with none given, in_pages and
+ * out_pages may be NULL and only kept_idx is written.  Workspace:
+ * tri_workspace_bytes.
+ */
+tri_status tri_select_compact_paged(const tri_shape* shape, int32_t num_seqs,
+                                    const int64_t* cu_len, const int32_t* budget,
+                                    const float* scores, const tri_kv_pages* in_pages,
+                                    const uint16_t* k_pool, const uint16_t* v_pool,
+                                    const int32_t* pos_pool, int32_t* kept_idx,
+                                    const tri_kv_pages* out_pages, uint16_t* k_out_pool,
+                                    uint16_t* v_out_pool, int32_t* pos_out_pool,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* tri_status_string(tri_status status);
 

@@ -49,8 +49,7 @@ Sources (cited by page title and the section or equation on that page):
               the centres against the real attention logits) and Fig. 7
               (per-head Pearson correlation of that reconstruction).
 
-Readings where the pages are silent or disagree (each is a choice, listed
-again in the design notes):
+Readings where the pages are silent or disagree (each is a choice):
 
 * RoPE pairs are interleaved (x_{2f}, x_{2f+1}) as the rotation equation
   writes them; band f is the complex number x_{2f} + i x_{2f+1}, and the

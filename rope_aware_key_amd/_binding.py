@@ -102,12 +102,33 @@ _lib.tri_workspace_bytes_layers.restype = ctypes.c_size_t
 _lib.tri_select_compact_layers.argtypes = _lib.tri_select_compact.argtypes
 _lib.tri_select_compact_layers.restype = ctypes.c_int
 
+
+class TriKvPages(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("layer_stride", ctypes.c_int64)]
+
+
+_PG = ctypes.POINTER(TriKvPages)
+_lib.tri_score_paged.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _PG, _P, _P, _P,
+                                 _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                                 ctypes.c_size_t, _P]
+_lib.tri_score_paged.restype = ctypes.c_int
+_lib.tri_select_compact_paged.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _PG,
+                                          _P, _P, _P, _P, _PG, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.tri_select_compact_paged.restype = ctypes.c_int
+_lib.tri_workspace_bytes_paged.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+_lib.tri_workspace_bytes_paged.restype = ctypes.c_size_t
+
 EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_bytes", "tri_score", "tri_select_compact",
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
            "tri_trig_correlation", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
-           "tri_select_compact_layers")
+           "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
+           "tri_workspace_bytes_paged")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -330,4 +351,57 @@ def tri_select_compact_layers(shape: TriShape, cu_len, budget, scores, k, v, k_p
                                         _ptr(v_out), _ptr(pos_out), _ptr(workspace), int(wsb),
                                         _stream(stream))
     _check(st, "tri_select_compact_layers")
+
+
+def make_pages(page_table, page_size, num_pages, page_stride, token_stride, head_stride,
+               layer_stride) -> TriKvPages:
+    """tri_kv_pages for a device page table [num_seqs, max_pages] (int32
+    tensor, kept alive by the caller); strides in rows."""
+    return TriKvPages(ctypes.c_void_p(page_table.data_ptr()), int(page_table.shape[-1]),
+                      int(num_pages), int(page_size), int(page_stride), int(token_stride),
+                      int(head_stride), int(layer_stride))
+
+
+def tri_workspace_bytes_paged(shape: TriShape, cu_len, page_size, n_offsets=0,
+                              reduce="mean") -> int:
+    arr, p = _host(cu_len, np.int64)
+    return int(_lib.tri_workspace_bytes_paged(ctypes.byref(shape), len(arr) - 1, p,
+                                              int(page_size), int(n_offsets), REDUCE[reduce]))
+
+
+def _pages(p):
+    return None if p is None else ctypes.byref(p)
+
+
+def tri_score_paged(shape: TriShape, cu_len, cur_pos, pages: TriKvPages, k_pool, q_centre,
+                    q_absmean, q_R, scores, offsets=None, reduce="mean", raw_scores=None,
+                    head_stats=None, workspace=None, workspace_bytes=None, stream=None):
+    """tri_score (offsets None) or tri_score_offsets with keys in a paged pool."""
+    cu, pcu = _host(cu_len, np.int64)
+    cp, pcp = _host(cur_pos, np.int32)
+    off, poff = _host(offsets, np.float64)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_score_paged(ctypes.byref(shape), len(cu) - 1, pcu, pcp, _pages(pages),
+                              _ptr(k_pool), _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), poff,
+                              0 if off is None else len(off), REDUCE[reduce], _ptr(scores),
+                              _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
+                              _stream(stream))
+    _check(st, "tri_score_paged")
+
+
+def tri_select_compact_paged(shape: TriShape, cu_len, budget, scores, in_pages, k_pool, v_pool,
+                             pos_pool, kept_idx, out_pages, k_out_pool, v_out_pool, pos_out_pool,
+                             workspace=None, workspace_bytes=None, stream=None):
+    """tri_select_compact with K, V, positions read from and written to paged pools."""
+    cu, pcu = _host(cu_len, np.int64)
+    bu, pbu = _host(budget, np.int32)
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    st = _lib.tri_select_compact_paged(ctypes.byref(shape), len(cu) - 1, pcu, pbu, _ptr(scores),
+                                       _pages(in_pages), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(pos_pool), _ptr(kept_idx), _pages(out_pages),
+                                       _ptr(k_out_pool), _ptr(v_out_pool), _ptr(pos_out_pool),
+                                       _ptr(workspace), int(wsb), _stream(stream))
+    _check(st, "tri_select_compact_paged")
 

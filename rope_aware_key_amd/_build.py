@@ -10,7 +10,7 @@ SOURCES = ["api.hip", "calib.hip", "decode.hip", "diag.hip", "score.hip", "score
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # packed-FP32 VALU forms stay off (see the design notes)
+    # no packed-FP32 VALU instructions (v_pk_*_f32): fp32 math stays scalar
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

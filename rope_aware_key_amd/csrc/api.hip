@@ -131,6 +131,8 @@ struct PlanLayout {
   int64_t in_stride = 0, out_stride = 0;
   const int64_t* in_row0 = nullptr;   // [S] host: first input row per sequence
   const int64_t* out_row0 = nullptr;  // [S] host: first output row per sequence
+  const tri::Pages* in_pages = nullptr;   // K/V/positions in a paged pool (scores stay packed)
+  const tri::Pages* out_pages = nullptr;  // compacted rows into a paged pool
 };
 
 struct Plan {
@@ -147,6 +149,7 @@ struct Plan {
   int chunk = 0;  // keys per score ticket
   bool fused = false;
   bool half = false;  // half-split RoPE layout
+  tri::Pages in_pg, out_pg;  // table == NULL: packed
   OffsetMode om;
   tri::MaxOffsetsPlan mp;  // max-over-offsets path
   size_t score_bytes = 0, select_bytes = 0;
@@ -201,7 +204,11 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
       return fail(TRI_ERR_UNSUPPORTED,
                   "the max over offsets: one head's offset rows exceed the LDS budget");
   }
+  if (lay.in_pages) p.in_pg = *lay.in_pages;
+  if (lay.out_pages) p.out_pg = *lay.out_pages;
+  // the fused kernel reads a 16-key block from one page
   p.fused = !om.max && tri::fused_supported(p.d, p.half) &&
+            (!p.in_pg.table || p.in_pg.page_shift >= 4) &&
             (longest + tri::fused_chunk_keys(p.G) - 1) / tri::fused_chunk_keys(p.G) <=
                 tri::kFusedMaxUnitChunks;
   p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
@@ -229,6 +236,11 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     p.total_out = std::max(p.total_out, si.out_base + LH * si.out_stride);
     p.keys += LH * n;
     p.kept += LH * b;
+    if (p.in_pg.table && ((n + (1 << p.in_pg.page_shift) - 1) >> p.in_pg.page_shift) > p.in_pg.max_pages)
+      return fail(TRI_ERR_INVALID_ARGUMENT, "a sequence has more pages than the input page table holds");
+    if (p.out_pg.table &&
+        ((b + (1 << p.out_pg.page_shift) - 1) >> p.out_pg.page_shift) > p.out_pg.max_pages)
+      return fail(TRI_ERR_INVALID_ARGUMENT, "kept keys need more pages than the output page table holds");
     out_acc += b;
     si.p_q = cur_pos ? cur_pos[s] : 0;
     si.chunk_base = (int32_t)ticket_acc;
@@ -406,17 +418,19 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                                  (int)p.tickets, (const double2*)(ws + p.off_P),
                                  (const float*)(ws + p.off_W), (const double2*)(ws + p.off_E),
                                  doff, ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
-                                 (double*)(ws + p.off_ustats), scores, head_stats, p.half, s);
+                                 (double*)(ws + p.off_ustats), scores, head_stats, p.half,
+                                 p.in_pg, s);
   if (p.fused)
     return tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                    (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                                    (const double2*)(ws + p.off_E), ws + p.off_apack, k,
                                    (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
-                                   scores, raw_scores, head_stats, p.half, s);
+                                   scores, raw_scores, head_stats, p.half, p.in_pg, s);
   return tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                            (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                            (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),
-                           (double*)(ws + p.off_ustats), scores, head_stats, p.half, s);
+                           (double*)(ws + p.off_ustats), scores, head_stats, p.half, p.in_pg,
+                           s);
 }
 
 // Queue select (and the gathers asked for) of a ready plan; the sequence
@@ -432,7 +446,7 @@ hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t
   if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, s);
   if (e == hipSuccess && (k_out || v_out || pos_out))
     e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
-                            pos_out, s);
+                            pos_out, p.in_pg, p.out_pg, s);
   return e;
 }
 
@@ -440,9 +454,11 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
                       const int32_t* cur_pos, const uint16_t* k, const float* q_centre,
                       const float* q_absmean, const float* q_R, const OffsetMode& om,
                       float* scores, float* raw_scores, double* head_stats, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, const tri::Pages* pages = nullptr) {
   Plan p;
-  tri_status st = make_plan(shape, num_seqs, cu_len, cur_pos, nullptr, p, om);
+  PlanLayout lay;
+  lay.in_pages = pages;
+  tri_status st = make_plan(shape, num_seqs, cu_len, cur_pos, nullptr, p, om, lay);
   if (st != TRI_OK) return st;
   if (num_seqs > 0 && !cur_pos) return fail(TRI_ERR_INVALID_ARGUMENT, "cur_pos is NULL");
   if (p.keys == 0) return TRI_OK;
@@ -900,5 +916,152 @@ tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,
   return TRI_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Paged pools
+// ---------------------------------------------------------------------------
 }  // extern "C"
 
+namespace {
+
+// A tri_kv_pages descriptor as the kernels take it, after checking it.
+tri_status to_pages(const tri_kv_pages* d, const tri_shape* sh, tri::Pages& pg, const char* what) {
+  const std::string w(what);
+  if (!d) return fail(TRI_ERR_INVALID_ARGUMENT, w + " is NULL");
+  if (!d->page_table) return fail(TRI_ERR_INVALID_ARGUMENT, w + ".page_table is NULL");
+  const int32_t P = d->page_size;
+  if (P < 1 || P > 65536 || (P & (P - 1)) != 0)
+    return fail(TRI_ERR_INVALID_ARGUMENT, w + ".page_size must be a power of two in [1, 65536]");
+  if (d->max_pages < 1 || d->num_pages < 1)
+    return fail(TRI_ERR_INVALID_ARGUMENT, w + ".max_pages and .num_pages must be >= 1");
+  if (d->page_stride < 0 || d->token_stride < 0 || d->head_stride < 0 || d->layer_stride < 0)
+    return fail(TRI_ERR_INVALID_ARGUMENT, w + " strides must be >= 0");
+  // the largest row any (layer, head, page, slot) can name, times d, fits int64
+  const double top = (double)(sh->num_layers - 1) * d->layer_stride +
+                     (double)(sh->num_kv_heads - 1) * d->head_stride +
+                     (double)(d->num_pages - 1) * d->page_stride + (double)(P - 1) * d->token_stride;
+  if ((top + 1.0) * sh->head_dim * 2.0 > 9.0e18)
+    return fail(TRI_ERR_UNSUPPORTED, w + " spans more rows than 64-bit offsets hold");
+  pg.table = d->page_table;
+  pg.max_pages = d->max_pages;
+  pg.num_pages = d->num_pages;
+  int shift = 0;
+  while ((1 << shift) < P) ++shift;
+  pg.page_shift = shift;
+  pg.hkv = sh->num_kv_heads;
+  pg.page_stride = d->page_stride;
+  pg.token_stride = d->token_stride;
+  pg.head_stride = d->head_stride;
+  pg.layer_stride = d->layer_stride;
+  return TRI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tri_workspace_bytes_paged(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                                 int32_t page_size, int32_t n_offsets, int32_t reduce) {
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0) {
+    fail(TRI_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [1, 65536]");
+    return 0;
+  }
+  OffsetMode om;
+  std::vector<double> zeros;  // offsets are only counted here
+  if (n_offsets != 0) {
+    if (reduce != TRI_REDUCE_MEAN && reduce != TRI_REDUCE_MAX) {
+      fail(TRI_ERR_INVALID_ARGUMENT, "reduce must be TRI_REDUCE_MEAN or TRI_REDUCE_MAX");
+      return 0;
+    }
+    if (n_offsets < 1 || n_offsets > tri::kMaxOffsets) {
+      fail(TRI_ERR_INVALID_ARGUMENT, "n_offsets must be 0 (built-in set) or in [1, 4096]");
+      return 0;
+    }
+    zeros.assign(n_offsets, 0.0);
+    om.host = zeros.data();
+    om.n = n_offsets;
+    om.max = reduce == TRI_REDUCE_MAX;
+  }
+  // the path a paged call takes depends only on the page size
+  static const int32_t kNoTable = 0;
+  tri::Pages pg;
+  pg.table = &kNoTable;
+  pg.max_pages = 0x7fffffff;
+  pg.num_pages = 1;
+  while ((1 << pg.page_shift) < page_size) ++pg.page_shift;
+  PlanLayout lay;
+  lay.in_pages = &pg;
+  Plan p;
+  if (make_plan(shape, num_seqs, cu_len, nullptr, nullptr, p, om, lay) != TRI_OK) return 0;
+  return p.score_bytes > p.select_bytes ? p.score_bytes : p.select_bytes;
+}
+
+tri_status tri_score_paged(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                           const int32_t* cur_pos, const tri_kv_pages* pages,
+                           const uint16_t* k_pool, const float* q_centre, const float* q_absmean,
+                           const float* q_R, const double* offsets, int32_t n_offsets,
+                           int32_t reduce, float* scores, float* raw_scores, double* head_stats,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  tri_status st = check_shape(shape);
+  if (st != TRI_OK) return st;
+  tri::Pages pg;
+  st = to_pages(pages, shape, pg, "pages");
+  if (st != TRI_OK) return st;
+  OffsetMode om;
+  if (offsets) {
+    if (reduce != TRI_REDUCE_MEAN && reduce != TRI_REDUCE_MAX)
+      return fail(TRI_ERR_INVALID_ARGUMENT, "reduce must be TRI_REDUCE_MEAN or TRI_REDUCE_MAX");
+    om.host = offsets;
+    om.n = n_offsets;
+    om.max = reduce == TRI_REDUCE_MAX;
+  }
+  return score_impl(shape, num_seqs, cu_len, cur_pos, k_pool, q_centre, q_absmean, q_R, om,
+                    scores, raw_scores, head_stats, workspace, workspace_bytes, stream, &pg);
+}
+
+tri_status tri_select_compact_paged(const tri_shape* shape, int32_t num_seqs,
+                                    const int64_t* cu_len, const int32_t* budget,
+                                    const float* scores, const tri_kv_pages* in_pages,
+                                    const uint16_t* k_pool, const uint16_t* v_pool,
+                                    const int32_t* pos_pool, int32_t* kept_idx,
+                                    const tri_kv_pages* out_pages, uint16_t* k_out_pool,
+                                    uint16_t* v_out_pool, int32_t* pos_out_pool, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  tri_status st = check_shape(shape);
+  if (st != TRI_OK) return st;
+  if (num_seqs > 0 && !budget) return fail(TRI_ERR_INVALID_ARGUMENT, "budget is NULL");
+  if ((k_pool == nullptr) != (k_out_pool == nullptr) ||
+      (v_pool == nullptr) != (v_out_pool == nullptr) ||
+      (pos_pool == nullptr) != (pos_out_pool == nullptr))
+    return fail(TRI_ERR_INVALID_ARGUMENT,
+                "k/k_out, v/v_out and pos/pos_out pools come in pairs");
+  const bool rows = k_pool || v_pool || pos_pool;
+  tri::Pages in_pg, out_pg;
+  PlanLayout lay;
+  if (rows) {
+    st = to_pages(in_pages, shape, in_pg, "in_pages");
+    if (st != TRI_OK) return st;
+    st = to_pages(out_pages, shape, out_pg, "out_pages");
+    if (st != TRI_OK) return st;
+    lay.in_pages = &in_pg;
+    lay.out_pages = &out_pg;
+  }
+  Plan p;
+  st = make_plan(shape, num_seqs, cu_len, nullptr, budget, p, OffsetMode(), lay);
+  if (st != TRI_OK) return st;
+  if (p.kept == 0) return TRI_OK;
+  if (!scores || !kept_idx)
+    return fail(TRI_ERR_INVALID_ARGUMENT, "scores and kept_idx must be non-NULL");
+  if ((k_pool && (!aligned16(k_pool) || !aligned16(k_out_pool))) ||
+      (v_pool && (!aligned16(v_pool) || !aligned16(v_out_pool))))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "K/V pools must be 16-byte aligned");
+  if (!workspace || workspace_bytes < p.select_bytes)
+    return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
+  const hipError_t e = run_select_compact(p, scores, k_pool, v_pool, pos_pool, kept_idx,
+                                          k_out_pool, v_out_pool, pos_out_pool, (char*)workspace,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(TRI_ERR_HIP, std::string("select_compact_paged: ") + hipGetErrorString(e));
+  return TRI_OK;
+}
+
+}  // extern "C"

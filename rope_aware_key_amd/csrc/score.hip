@@ -60,7 +60,7 @@ __device__ __forceinline__ Ticket decode_ticket(const SeqInfo* seqs, int S, int 
 template <int GT>
 __global__ __launch_bounds__(256) void score_raw_kernel(
     const SeqInfo* __restrict__ seqs, int S, int Hkv, int Hq, int G, int d, bool half,
-    const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
+    const Pages pg, const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
     const uint16_t* __restrict__ k, float* __restrict__ raw, double* __restrict__ chunk_stats) {
   constexpr int KPT = kScoreChunk / 256;
   __shared__ float a_s[GT * kMaxHeadDim];
@@ -107,8 +107,12 @@ __global__ __launch_bounds__(256) void score_raw_kernel(
         acc[h] = a;
       }
     };
+    // the key's row: packed, or through the page table
+    const int64_t krow = key >= tk.nkeys ? 0
+                         : pg.table  ? paged_row(pg, tk.s, l, g, tk.key0 + key)
+                                     : tk.row0 + tk.key0 + key;
     if (key < tk.nkeys && !half) {
-      const uint4* rp = reinterpret_cast<const uint4*>(k + (tk.row0 + tk.key0 + key) * d);
+      const uint4* rp = reinterpret_cast<const uint4*>(k + krow * d);
       for (int c8 = 0; c8 < (d >> 3); ++c8) {
         const uint4 q = rp[c8];
         const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256) void score_raw_kernel(
       // half split: four bands per step, real parts from the first half of
       // the row, imaginary parts from the second (8-byte loads: d/2 is a
       // multiple of 4, not always of 8)
-      const uint2* rp = reinterpret_cast<const uint2*>(k + (tk.row0 + tk.key0 + key) * d);
+      const uint2* rp = reinterpret_cast<const uint2*>(k + krow * d);
       for (int c4 = 0; c4 < (F >> 2); ++c4) {
         const uint2 re = rp[c4], im = rp[(F >> 2) + c4];
         band(4 * c4 + 0, bf16_lo_s(re.x), bf16_lo_s(im.x));
@@ -260,32 +264,34 @@ __global__ __launch_bounds__(256) void zmax_kernel(
 
 template <int GT>
 static void launch_raw(int grid, hipStream_t st, const SeqInfo* seqs, int S, int Hkv, int Hq,
-                       int G, int d, bool half, const double2* P, const float* W,
-                       const double2* E, const uint16_t* k, float* raw, double* cs) {
+                       int G, int d, bool half, const Pages& pg, const double2* P,
+                       const float* W, const double2* E, const uint16_t* k, float* raw,
+                       double* cs) {
   hipLaunchKernelGGL(score_raw_kernel<GT>, dim3(grid), dim3(256), 0, st, seqs, S, Hkv, Hq, G, d,
-                     half, P, W, E, k, raw, cs);
+                     half, pg, P, W, E, k, raw, cs);
 }
 
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W, const double2* E,
                         const uint16_t* k, float* raw, double* chunk_stats, double* unit_stats,
-                        float* scores, double* head_stats, bool half, hipStream_t st) {
+                        float* scores, double* head_stats, bool half, const Pages& pg,
+                        hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const int Hq = Hkv * G;
   if (G <= 1)
-    launch_raw<1>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+    launch_raw<1>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, pg, P, W, E, k, raw,
                   chunk_stats);
   else if (G <= 2)
-    launch_raw<2>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+    launch_raw<2>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, pg, P, W, E, k, raw,
                   chunk_stats);
   else if (G <= 4)
-    launch_raw<4>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+    launch_raw<4>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, pg, P, W, E, k, raw,
                   chunk_stats);
   else if (G <= 8)
-    launch_raw<8>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+    launch_raw<8>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, pg, P, W, E, k, raw,
                   chunk_stats);
   else
-    launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, P, W, E, k, raw,
+    launch_raw<16>(total_tickets, st, seqs, S, Hkv, Hq, G, d, half, pg, P, W, E, k, raw,
                   chunk_stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -253,19 +253,22 @@ __device__ __forceinline__ MaxItem first_item(const SeqInfo* seqs, int S, int np
 
 // Key rows of one item into registers: block bb, key 16*bb + m of the
 // group, dims 32*st + 8q .. +7 (the MFMA B-operand layout).  Rows past the
-// ticket's keys re-read its last row.
+// ticket's keys re-read its last row.  Paged pools: each row through the
+// page table.
 template <int STEPS, int GB>
 __device__ __forceinline__ void load_item_keys(const SeqInfo* seqs, int S, int LH,
-                                               const uint16_t* __restrict__ k, const MaxItem& it,
-                                               int m, int q, uint4 (&kb)[GB][STEPS]) {
+                                               const uint16_t* __restrict__ k, const Pages& pg,
+                                               const MaxItem& it, int m, int q,
+                                               uint4 (&kb)[GB][STEPS]) {
   constexpr int D = STEPS * 32;
   const MaxTicket tk = decode_max_ticket(seqs, S, LH, it.t);
-  const uint16_t* base = k + (tk.row0 + tk.key0) * (int64_t)D;
 #pragma unroll
   for (int bb = 0; bb < GB; ++bb) {
     int key = it.grp * 16 * GB + bb * 16 + m;
     key = key < tk.nkeys ? key : tk.nkeys - 1;
-    const uint4* rp = reinterpret_cast<const uint4*>(base + (int64_t)key * D);
+    const int64_t row = pg.table ? paged_row_lg(pg, tk.s, tk.lg, tk.key0 + key)
+                                 : tk.row0 + tk.key0 + key;
+    const uint4* rp = reinterpret_cast<const uint4*>(k + row * D);
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) kb[bb][st] = rp[4 * st + q];
   }
@@ -283,7 +286,8 @@ template <int STEPS, int GB, int NE, bool HALF>
 __global__ __launch_bounds__(kThreads) void score_max_kernel(
     const SeqInfo* __restrict__ seqs, int S, int LH, int G, MaxOffsetsPlan mp, int total_tickets,
     const uint4* __restrict__ apack, const uint4* __restrict__ wpack,
-    const uint16_t* __restrict__ k, float* __restrict__ raw, double* __restrict__ wsum,
+    const uint16_t* __restrict__ k, const Pages pg, float* __restrict__ raw,
+    double* __restrict__ wsum,
     float* __restrict__ sink) {
   constexpr int KG = 16 * GB;  // keys per wave group
   extern __shared__ uint4 lds[];
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
 
   MaxItem cur = first_item(seqs, S, mp.npass, t_begin, t_end, 0, t_begin, wave, KG);
   uint4 kb[GB][STEPS];
-  if (cur.valid) load_item_keys<STEPS, GB>(seqs, S, LH, k, cur, m, q, kb);
+  if (cur.valid) load_item_keys<STEPS, GB>(seqs, S, LH, k, pg, cur, m, q, kb);
 
   // Waves run through the tickets independently; the block meets only
   // where the staged rows change (a new unit or pass).
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
                                ? MaxItem{pass, t, grp + kWaves, true}
                                : first_item(seqs, S, mp.npass, t_begin, t_end, pass, t + 1, wave, KG);
         uint4 kn[GB][STEPS];
-        load_item_keys<STEPS, GB>(seqs, S, LH, k, nx.valid ? nx : cur, m, q, kn);
+        load_item_keys<STEPS, GB>(seqs, S, LH, k, pg, nx.valid ? nx : cur, m, q, kn);
         const int key_g = grp * KG;
         // trig term: running maximum over each head's tiles
         float hm[GB][NE];
@@ -556,7 +560,8 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
                                const MaxOffsetsPlan& mp, double theta, int total_tickets,
                                const double2* P, const float* W, const double2* E,
                                const double* offsets, void* operands, const uint16_t* k,
-                               float* raw, double* chunk_stats, hipStream_t st) {
+                               const Pages& pg, float* raw, double* chunk_stats,
+                               hipStream_t st) {
   const int64_t units = (int64_t)S * L * Hkv;
   uint4* apack = reinterpret_cast<uint4*>(operands);
   uint4* wpack = apack + units * mp.npass * mp.ptiles * STEPS * 3 * 64;
@@ -575,7 +580,7 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
 #define TRI_LAUNCH(NE)                                                                         \
   hipLaunchKernelGGL((score_max_kernel<STEPS, GB, NE, HALF>), dim3(grid), dim3(kThreads), lds, \
                      st,                                                                       \
-                     seqs, S, L * Hkv, G, mp, total_tickets, apack, wpack, k, raw, wsum, sink)
+                     seqs, S, L * Hkv, G, mp, total_tickets, apack, wpack, k, pg, raw, wsum, sink)
   if (ne == 1)
     TRI_LAUNCH(1);
   else if (ne == 2)
@@ -596,14 +601,14 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
                             float* raw, double* chunk_stats, double* unit_stats, float* scores,
-                            double* head_stats, bool half, hipStream_t st) {
+                            double* head_stats, bool half, const Pages& pg, hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   if (!mp.ok) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
 #define TRI_CASE(n, h)                                                                         \
   case n:                                                                                      \
     e = launch_max_t<n, h>(seqs, S, L, Hkv, G, nD, mp, theta, total_tickets, P, W, E, offsets, \
-                           operands, k, raw, chunk_stats, st);                                 \
+                           operands, k, pg, raw, chunk_stats, st);                             \
     break;
   // half split keeps both parts of a band in one lane only with an even
   // number of 32-wide steps

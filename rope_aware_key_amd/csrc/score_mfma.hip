@@ -119,8 +119,8 @@ __device__ __forceinline__ uint64_t ld_agent_u64(const double* p) {
 }
 
 struct Chunk {
-  int t, s, lg, l, g, c, nch, nkeys, nkeys_unit;
-  int64_t row0, unit;
+  int t, s, lg, l, g, c, nch, nkeys, nkeys_unit, key0;
+  int64_t row0, unit;  // row0: first score row of the chunk (and first K row when packed)
 };
 
 __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L, int Hkv, int ch,
@@ -137,6 +137,7 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
   ck.g = ck.lg % Hkv;
   ck.nkeys_unit = si.n;
   const int key0 = ck.c * ch;
+  ck.key0 = key0;
   ck.nkeys = min(ch, si.n - key0);
   ck.row0 = si.row_base + (int64_t)ck.lg * si.in_stride + key0;
   ck.unit = (int64_t)ck.s * L * Hkv + ck.lg;
@@ -162,15 +163,35 @@ __device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ 
 
 // Block b (16 keys) of a chunk into bv: lane (m, q) takes 16 bytes of key
 // b*16 + m per step st (4 lanes cover 64 contiguous bytes of the row).
-template <int STEPS>
+// Paged (pages of at least 16 tokens): the block lies in one page, whose id
+// is one scalar load shared by the wave.
+template <int STEPS, bool PAGED>
 __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __restrict__ k,
+                                           const Pages& pg, const int32_t* __restrict__ ptab,
                                            int b, uint4 (&bv)[STEPS]) {
   constexpr int D = STEPS * 32;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   int key = b * 16 + m;
   key = key < ck.nkeys ? key : ck.nkeys - 1;  // padding lanes re-read a valid row
-  const uint4* rp = reinterpret_cast<const uint4*>(k + (ck.row0 + key) * D);
+  int64_t row;
+  if (PAGED) {
+    // Every operand of the page-table address is wave-uniform and the table
+    // is a restrict (never written) argument: a scalar load, counted apart
+    // from the K loads in flight, so waiting for it does not drain the ring.
+    const int kb = __builtin_amdgcn_readfirstlane(ck.key0 + b * 16);
+    const int j = kb >> pg.page_shift;
+    const int s = __builtin_amdgcn_readfirstlane(ck.s), l = __builtin_amdgcn_readfirstlane(ck.l),
+              g = __builtin_amdgcn_readfirstlane(ck.g);
+    int p = ptab[(int64_t)s * pg.max_pages + j];
+    p = p < 0 ? 0 : (p >= pg.num_pages ? pg.num_pages - 1 : p);
+    row = (int64_t)l * pg.layer_stride + (int64_t)g * pg.head_stride +
+          (int64_t)p * pg.page_stride +
+          (int64_t)(ck.key0 + key - (j << pg.page_shift)) * pg.token_stride;
+  } else {
+    row = ck.row0 + key;
+  }
+  const uint4* rp = reinterpret_cast<const uint4*>(k + row * D);
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
 }
@@ -179,15 +200,16 @@ __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __re
 // blocks w, w + 4, ...).  chunk_raw consumes them.  Unconditional (blocks
 // past the chunk's end re-read its last block) so that no earlier ring
 // contents stay live across the caller's code.
-template <int STEPS>
+template <int STEPS, bool PAGED>
 __device__ __forceinline__ void ring_prime(const Chunk& ck, const uint16_t* __restrict__ k,
+                                           const Pages& pg, const int32_t* __restrict__ ptab,
                                            uint4 (&ring)[kPrefetch][STEPS]) {
   const int wave = threadIdx.x >> 6;
   const int nblk = (ck.nkeys + 15) >> 4;
 #pragma unroll
   for (int j = 0; j < kPrefetch; ++j) {
     const int b = wave + kFusedWaves * j;
-    load_block<STEPS>(ck, k, b < nblk ? b : nblk - 1, ring[j]);
+    load_block<STEPS, PAGED>(ck, k, pg, ptab, b < nblk ? b : nblk - 1, ring[j]);
   }
 }
 
@@ -221,10 +243,11 @@ __device__ __forceinline__ void load_operands(const Chunk& ck, const uint4* __re
   }
 }
 
-template <int STEPS, bool HALF>
+template <int STEPS, bool HALF, bool PAGED>
 __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
                                           const UnitOperands<STEPS>& op,
-                                          const uint16_t* __restrict__ k, float* raw,
+                                          const uint16_t* __restrict__ k, const Pages& pg,
+                                          const int32_t* __restrict__ ptab, float* raw,
                                           uint4 (&ring)[kPrefetch][STEPS]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
@@ -264,7 +287,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         const int bn = b + kFusedWaves * kPrefetch;
-        if (bn < nblk) load_block<STEPS>(ck, k, bn, ring[j]);
+        if (bn < nblk) load_block<STEPS, PAGED>(ck, k, pg, ptab, bn, ring[j]);
         // D layout: lane holds heads 4q..4q+3 of key b*16 + m (rows past
         // the chunk's end land in the buffer's padding and are never read)
 #pragma unroll
@@ -465,10 +488,11 @@ __device__ __forceinline__ void chunk_store_scores(const Chunk& ck, const float*
 
 // STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
 // tickets.  ch = keys per ticket.
-template <int STEPS, bool HALF>
+template <int STEPS, bool HALF, bool PAGED>
 __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
-    const uint4* __restrict__ apack, const uint16_t* __restrict__ k,
+    const uint4* __restrict__ apack, const uint16_t* __restrict__ k, const Pages pg,
+    const int32_t* __restrict__ ptab,
     double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, float* __restrict__ scores,
     float* __restrict__ raw_out, double* __restrict__ head_stats) {
   extern __shared__ float raw_s[];  // 2 buffers of [G][ch + kRawPad]
@@ -495,7 +519,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   int t = __builtin_amdgcn_readfirstlane(sh.ticket);  // uniform: chunk fields in SGPRs
   if (t < total_tickets) {
     ck = decode_chunk(seqs, S, L, Hkv, ch, t);
-    ring_prime<STEPS>(ck, k, ring);
+    ring_prime<STEPS, PAGED>(ck, k, pg, ptab, ring);
     load_operands<STEPS>(ck, apack, op);
   }
   // Each pass streams chunk ck (if any) and finalizes prev (if any).  Every
@@ -514,7 +538,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
-    if (have) chunk_raw<STEPS, HALF>(ck, G, rs, op, k, buf_cur, ring);
+    if (have) chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring);
     if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
@@ -525,7 +549,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
     }
-    if (ahead || !have) ring_prime<STEPS>(nk, k, ring);
+    if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring);
     if (have) {
       chunk_moments(ck, G, rs, buf_cur, sh);
       __syncthreads();
@@ -541,7 +565,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       __syncthreads();
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
-      ring_prime<STEPS>(nk, k, ring);
+      ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring);
     }
     load_operands<STEPS>(nk, apack, op);
     if (have_prev) chunk_store_scores(prev, buf_prev, scores, raw_out);
@@ -609,18 +633,18 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
                                      __float_as_uint(wv[2]), __float_as_uint(wv[3]));
 }
 
-template <int STEPS, bool HALF>
+template <int STEPS, bool HALF, bool PAGED>
 static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
                                  const double2* P, const float* W, const double2* E,
-                                 uint4* apack, const uint16_t* k, double* cs, uint32_t* ctrl,
-                                 float* scores, float* raw, double* hs) {
+                                 uint4* apack, const uint16_t* k, const Pages& pg, double* cs,
+                                 uint32_t* ctrl, float* scores, float* raw, double* hs) {
   const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
   hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
                      dim3(256), 0, st, S, L, Hkv, G, HALF, P, W, E, apack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF>);
+  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF, PAGED>);
   static const hipError_t attr = hipFuncSetAttribute(
       kern, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds);
   if (attr != hipSuccess) return attr;
@@ -633,8 +657,9 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
   if (per_cu < 1) per_cu = 1;
   int grid = cus * per_cu;
   if (grid > total_tickets) grid = total_tickets;
-  hipLaunchKernelGGL((score_fused_kernel<STEPS, HALF>), dim3(grid), dim3(kFusedThreads), lds, st, seqs, S,
-                     L, Hkv, G, ch, total_tickets, apack, k, cs, ctrl, scores, raw, hs);
+  hipLaunchKernelGGL((score_fused_kernel<STEPS, HALF, PAGED>), dim3(grid), dim3(kFusedThreads),
+                     lds, st, seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg, pg.table, cs, ctrl,
+                     scores, raw, hs);
   return hipGetLastError();
 }
 
@@ -662,28 +687,38 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, bool half, hipStream_t st) {
+                              double* head_stats, bool half, const Pages& pg,
+                              hipStream_t st) {
   if (total_tickets == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)G * (ch + kRawPad) * sizeof(float);
   if (lds > (size_t)kFusedMaxLds || !fused_supported(d, half)) return hipErrorInvalidValue;
+  if (pg.table && pg.page_shift < 4) return hipErrorInvalidValue;  // pages of >= 16 tokens
   uint4* ap = reinterpret_cast<uint4*>(apack);
-#define TRI_CASE(n, h)                                                                        \
+#define TRI_CASE(n, h, pgd)                                                                   \
   case n:                                                                                     \
-    return launch_fused_t<n, h>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, ap, \
-                                k, chunk_stats, ctrl, scores, raw, head_stats);
-  if (half) {
-    switch (d / 32) {
-      TRI_CASE(2, true) TRI_CASE(4, true) TRI_CASE(6, true) TRI_CASE(8, true)
-      default:
-        return hipErrorInvalidValue;
-    }
+    return launch_fused_t<n, h, pgd>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, \
+                                     ap, k, pg, chunk_stats, ctrl, scores, raw, head_stats);
+#define TRI_LAYOUTS(pgd)                                                                      \
+  if (half) {                                                                                 \
+    switch (d / 32) {                                                                         \
+      TRI_CASE(2, true, pgd) TRI_CASE(4, true, pgd) TRI_CASE(6, true, pgd)                    \
+      TRI_CASE(8, true, pgd)                                                                  \
+      default:                                                                                \
+        return hipErrorInvalidValue;                                                          \
+    }                                                                                         \
+  }                                                                                           \
+  switch (d / 32) {                                                                           \
+    TRI_CASE(1, false, pgd) TRI_CASE(2, false, pgd) TRI_CASE(3, false, pgd)                   \
+    TRI_CASE(4, false, pgd) TRI_CASE(5, false, pgd) TRI_CASE(6, false, pgd)                   \
+    TRI_CASE(7, false, pgd) TRI_CASE(8, false, pgd)                                           \
+    default:                                                                                  \
+      return hipErrorInvalidValue;                                                            \
   }
-  switch (d / 32) {
-    TRI_CASE(1, false) TRI_CASE(2, false) TRI_CASE(3, false) TRI_CASE(4, false)
-    TRI_CASE(5, false) TRI_CASE(6, false) TRI_CASE(7, false) TRI_CASE(8, false)
-    default:
-      return hipErrorInvalidValue;
+  if (pg.table) {
+    TRI_LAYOUTS(true)
   }
+  TRI_LAYOUTS(false)
+#undef TRI_LAYOUTS
 #undef TRI_CASE
 }
 

@@ -454,11 +454,13 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
 constexpr int kCompactRows = 64;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Rows of K, V and positions: packed, or through the input / output page
+// tables (in_pg, out_pg); kept indices are always packed.
 __global__ __launch_bounds__(256) void compact_kernel(
     const SeqInfo* __restrict__ seqs, int LH, int d, const int32_t* __restrict__ kept,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ k_pos, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
-    int32_t* __restrict__ pos_out) {
+    int32_t* __restrict__ pos_out, const Pages in_pg, const Pages out_pg) {
   const int unit = blockIdx.x;
   const int s = unit / LH, lg = unit % LH;
   const SeqInfo si = seqs[s];
@@ -477,7 +479,8 @@ __global__ __launch_bounds__(256) void compact_kernel(
   for (int r = r0 + sub; r < r1; r += rows_per_pass) {
     const int32_t idx = kept[out0 + r];
     if ((uint32_t)idx >= (uint32_t)si.n) continue;  // never read outside the unit
-    const int64_t src = in0 + idx, dst = out0 + r;
+    const int64_t src = in_pg.table ? paged_row_lg(in_pg, s, lg, idx) : in0 + idx;
+    const int64_t dst = out_pg.table ? paged_row_lg(out_pg, s, lg, r) : out0 + r;
     // rows move whole (d/8 lanes x 16 bytes), read once and written once:
     // non-temporal on both sides
     if (k_out)
@@ -493,12 +496,13 @@ __global__ __launch_bounds__(256) void compact_kernel(
 hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,
                           const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
-                          int32_t* pos_out, hipStream_t st) {
+                          int32_t* pos_out, const Pages& in_pg, const Pages& out_pg,
+                          hipStream_t st) {
   const int64_t units = (int64_t)S * LH;
   if (units == 0 || max_b <= 0) return hipSuccess;
   const dim3 grid((unsigned)units, (unsigned)((max_b + kCompactRows - 1) / kCompactRows));
   hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, seqs, LH, d, kept_idx, k, v, k_pos,
-                     k_out, v_out, pos_out);
+                     k_out, v_out, pos_out, in_pg, out_pg);
   return hipGetLastError();
 }
 

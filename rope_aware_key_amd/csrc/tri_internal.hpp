@@ -37,6 +37,37 @@ constexpr int kMaxOffsets = 4096;
 // the whole 160 KB of a gfx950 CU.
 constexpr size_t kMaxOffsetsLds = 160 * 1024;
 
+// Paged K/V/position pool (tutorial page, deployment paragraph: paged KV
+// management as in vLLM's PagedAttention).  Token i of unit (s, l, g) is
+// pool row
+//   l*layer_stride + g*head_stride + page*page_stride + (i % P)*token_stride,
+// page = table[s*max_pages + i / P], P = 1 << page_shift; a K or V row is d
+// elements, a position row one.  Page ids outside [0, num_pages) are
+// clamped into it, so a bad table never reads or writes outside the pool.
+// table == NULL means the packed layout.
+struct Pages {
+  const int32_t* table = nullptr;
+  int32_t max_pages = 0, num_pages = 0, page_shift = 0;
+  int32_t hkv = 1;  // KV heads: unit lg of a sequence is layer lg / hkv, head lg % hkv
+  int64_t page_stride = 0, token_stride = 0, head_stride = 0, layer_stride = 0;
+};
+
+// Pool row of slot 0 of logical page j of unit (s, l, g).
+__device__ __forceinline__ int64_t page_row0(const Pages& pg, int s, int l, int g, int j) {
+  int p = pg.table[(int64_t)s * pg.max_pages + j];
+  p = p < 0 ? 0 : (p >= pg.num_pages ? pg.num_pages - 1 : p);
+  return (int64_t)l * pg.layer_stride + (int64_t)g * pg.head_stride + (int64_t)p * pg.page_stride;
+}
+
+__device__ __forceinline__ int64_t paged_row(const Pages& pg, int s, int l, int g, int i) {
+  const int j = i >> pg.page_shift;
+  return page_row0(pg, s, l, g, j) + (int64_t)(i - (j << pg.page_shift)) * pg.token_stride;
+}
+
+__device__ __forceinline__ int64_t paged_row_lg(const Pages& pg, int s, int lg, int i) {
+  return paged_row(pg, s, lg / pg.hkv, lg % pg.hkv, i);
+}
+
 // RoPE pair layouts.  Band f of a d-vector is (x_{2f}, x_{2f+1})
 // (interleaved, the talk page's rotation equation) or (x_f, x_{f+d/2})
 // (half split, the layout of the LLaMA/Mistral implementations the
@@ -135,14 +166,14 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
                               int total_tickets, const double2* P, const float* W,
                               const double2* E, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
-                              double* head_stats, bool half, hipStream_t st);
+                              double* head_stats, bool half, const Pages& pg, hipStream_t st);
 
 // unit_stats: [units][G][2] fp64 scratch for the per-unit (mu, 1/sigma).
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
                         int total_tickets, const double2* P, const float* W,
                         const double2* E, const uint16_t* k, float* raw,
                         double* chunk_stats, double* unit_stats, float* scores,
-                        double* head_stats, bool half, hipStream_t st);
+                        double* head_stats, bool half, const Pages& pg, hipStream_t st);
 
 // z pass of the generic path: merges the (count, mean, M2) tickets of each
 // unit into unit_stats ([units][G][2]: mu, 1/sigma; head_stats gets mu,
@@ -175,7 +206,8 @@ hipError_t launch_score_max(const SeqInfo* seqs, int S, int L, int Hkv, int G, i
                             const double2* P, const float* W, const double2* E,
                             const double* offsets, void* operands, const uint16_t* k,
                             float* raw, double* chunk_stats, double* unit_stats, float* scores,
-                            double* head_stats, bool half, hipStream_t st);
+                            double* head_stats, bool half, const Pages& pg,
+                            hipStream_t st);
 
 // Decode-loop driver: where one appended token of sequence s goes (row of
 // unit 0; unit lg at row0 + lg*stride) and its position.
@@ -209,6 +241,7 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
 hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,
                           const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
-                          int32_t* pos_out, hipStream_t st);
+                          int32_t* pos_out, const Pages& in_pg, const Pages& out_pg,
+                          hipStream_t st);
 
 }  // namespace tri

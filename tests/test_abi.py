@@ -32,7 +32,8 @@ def test_header_symbols_exported():
                           "tri_decode_get_view", "tri_decode_destroy",
                           "tri_trig_correlation_workspace_bytes", "tri_trig_correlation",
                           "tri_pyramid_budgets", "tri_workspace_bytes_layers",
-                          "tri_select_compact_layers"}
+                          "tri_select_compact_layers", "tri_score_paged",
+                          "tri_select_compact_paged", "tri_workspace_bytes_paged"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -367,3 +368,89 @@ def test_max_offsets_half_split_needs_d_multiple_of_64():
             assert "half-split" in R.last_error()
         # the mean over the same set has no such limit
         assert R.tri_workspace_bytes_offsets(sh, [0, 8], len(offs), "mean") > 0
+
+
+
+def _pages(**kw):
+    a = dict(page_table=_Fake(FAKE * 5), page_size=16, num_pages=10, page_stride=64,
+             token_stride=4, head_stride=1, layer_stride=640)
+    a.update(kw)
+    pt = a.pop("page_table")
+    p = R.TriKvPages(ctypes.c_void_p(pt.data_ptr()) if pt is not None else None, 4,
+                     a["num_pages"], a["page_size"], a["page_stride"], a["token_stride"],
+                     a["head_stride"], a["layer_stride"])
+    return p
+
+
+def test_kv_pages_struct_layout():
+    """tri_kv_pages: pointer, three int32, then four int64 from byte 24."""
+    assert ctypes.sizeof(R.TriKvPages) == 56
+    assert R.TriKvPages.page_stride.offset == 24 and R.TriKvPages.layer_stride.offset == 48
+
+
+def test_score_paged_argument_checks():
+    sh = R.make_shape(128, 8, 4, 2)
+    cu, cp = [0, 40, 64], [40, 24]
+
+    def call(pages, **kw):
+        a = dict(k=_Fake(), qc=_Fake(), qa=_Fake(), qr=_Fake(), scores=_Fake(), workspace=None,
+                 workspace_bytes=0)
+        a.update(kw)
+        return R.tri_score_paged(sh, cu, cp, pages, a["k"], a["qc"], a["qa"], a["qr"], a["scores"],
+                                 workspace=a["workspace"], workspace_bytes=a["workspace_bytes"],
+                                 stream=0)
+
+    assert _status(call, None) == ST["INVALID"]
+    assert _status(call, _pages(page_table=None)) == ST["INVALID"]
+    for bad in (dict(page_size=0), dict(page_size=24), dict(page_size=1 << 17),
+                dict(num_pages=0), dict(token_stride=-1)):
+        assert _status(call, _pages(**bad)) == ST["INVALID"], bad
+    assert "page" in R.last_error()
+    # 40 keys in pages of 8 need 5 pages; the table holds 4 per sequence
+    assert _status(call, _pages(page_size=8)) == ST["INVALID"]
+    assert "pages" in R.last_error()
+    assert _status(call, _pages(layer_stride=1 << 60)) == ST["UNSUPPORTED"]
+    assert _status(call, _pages()) == ST["WORKSPACE"]
+    assert _status(call, _pages(), k=_Fake(FAKE + 8)) == ST["INVALID"]     # misaligned pool
+
+
+def test_select_compact_paged_argument_checks():
+    sh = R.make_shape(64, 4, 2, 1)
+    cu = [0, 50, 80]
+
+    def call(budget=(10, 10), in_pages=_pages(), out_pages=_pages(), rows=True, **kw):
+        p = FAKE * 2 if rows else None
+        a = dict(k=_Fake(p) if rows else None, v=_Fake(p) if rows else None,
+                 pos=_Fake(p) if rows else None, ko=_Fake(p) if rows else None,
+                 vo=_Fake(p) if rows else None, po=_Fake(p) if rows else None)
+        a.update(kw)
+        return R.tri_select_compact_paged(sh, cu, list(budget), _Fake(), in_pages, a["k"], a["v"],
+                                          a["pos"], _Fake(), out_pages, a["ko"], a["vo"], a["po"],
+                                          workspace=None, workspace_bytes=0, stream=0)
+
+    assert _status(call, vo=None) == ST["INVALID"]                    # unpaired pools
+    assert _status(call, out_pages=None) == ST["INVALID"]
+    assert _status(call, budget=(10, -1)) == ST["INVALID"]
+    # 50 kept keys in output pages of 8 need 7 pages; the table holds 4
+    assert _status(call, budget=(50, 10), out_pages=_pages(page_size=8)) == ST["INVALID"]
+    assert _status(call) == ST["WORKSPACE"]
+    assert _status(call, budget=(0, 0)) == 0                          # nothing kept
+    # indices only: no pools and no page descriptors needed
+    assert _status(call, rows=False, in_pages=None, out_pages=None) == ST["WORKSPACE"]
+
+
+
+def test_workspace_bytes_paged():
+    """Pages of >= 16 tokens take the fused path (its workspace); smaller
+    pages the VALU path, which also holds raw scores in the workspace."""
+    sh = R.make_shape(128, 8, 2, 2)
+    cu = [0, 3000, 5000]
+    fused = R.tri_workspace_bytes(sh, cu)
+    assert R.tri_workspace_bytes_paged(sh, cu, 16) == fused
+    assert R.tri_workspace_bytes_paged(sh, cu, 256) == fused
+    small = R.tri_workspace_bytes_paged(sh, cu, 8)
+    assert small >= fused + 2 * 2 * 5000 * 4 * 4           # raw scores: rows x G floats
+    assert R.tri_workspace_bytes_paged(sh, cu, 16, 3, "max") == \
+        R.tri_workspace_bytes_offsets(sh, cu, 3, "max")
+    assert R.tri_workspace_bytes_paged(sh, cu, 12) == 0
+    assert R.tri_workspace_bytes_paged(sh, cu, 16, 5000) == 0
