@@ -543,6 +543,8 @@ def main():
     ap.add_argument("--paged", type=int, default=None, metavar="PAGE_SIZE",
                     help="K, V and positions in a paged pool (token-major pages of PAGE_SIZE "
                          "tokens, random page order); compaction into a second pool")
+    ap.add_argument("--page-order", default="token", choices=["token", "head"],
+                    help="token-major pages [page][slot][head] or head-major [page][head][slot]")
     ap.add_argument("--pyramid", type=float, default=None, metavar="RATIO",
                     help="per-layer pyramid budgets (last/first = RATIO, mean = the "
                          "sequence's budget), selected by tri_select_compact_layers")
@@ -632,14 +634,15 @@ def main():
             sys.exit(2)
         P = args.paged
         print(f"[bench] scattering the cache into {P}-token pages", file=sys.stderr, flush=True)
-        pool = synth.paged_from_case(case, P, seed=1)
+        hm = args.page_order == "head"
+        pool = synth.paged_from_case(case, P, head_major=hm, seed=1)
         need = [(case.kept(s) + P - 1) // P for s in range(case.num_seqs)]
         out_pool = synth.empty_pool(case.num_seqs, case.shape.num_layers, case.shape.num_kv_heads,
-                                    d, P, need, spare=0, seed=2, device=dev)
+                                    d, P, need, head_major=hm, spare=0, seed=2, device=dev)
         pg_in = R.make_pages(pool.table, P, pool.num_pages, *pool.strides())
         pg_out = R.make_pages(out_pool.table, P, out_pool.num_pages, *out_pool.strides())
         torch.cuda.synchronize()
-        label = f"{label}+paged_{P}"
+        label = f"{label}+paged_{P}_{args.page_order}_major"
     scores = torch.empty(rows, dtype=torch.float32, device=dev)
     kept = torch.empty(max(1, out_rows), dtype=torch.int32, device=dev)
     k_out = torch.empty(max(1, out_rows), d, dtype=torch.int16, device=dev)

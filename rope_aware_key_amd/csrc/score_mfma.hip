@@ -161,14 +161,25 @@ __device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ 
   return apack + unit * (4 * STEPS) * 64;
 }
 
+// Paged pools (pages of at least 16 tokens): block b (16 keys) of a chunk
+// lies in one page, whose table entry this returns.  Every operand of the
+// address is wave-uniform and the table a restrict (never written)
+// argument, so this is a scalar load, counted apart from the K loads in
+// flight: waiting for it does not drain the ring.
+__device__ __forceinline__ int block_page(const Chunk& ck, const Pages& pg,
+                                          const int32_t* __restrict__ ptab, int b) {
+  const int kb = __builtin_amdgcn_readfirstlane(ck.key0 + b * 16);
+  const int s = __builtin_amdgcn_readfirstlane(ck.s);
+  return ptab[(int64_t)s * pg.max_pages + (kb >> pg.page_shift)];
+}
+
 // Block b (16 keys) of a chunk into bv: lane (m, q) takes 16 bytes of key
 // b*16 + m per step st (4 lanes cover 64 contiguous bytes of the row).
-// Paged (pages of at least 16 tokens): the block lies in one page, whose id
-// is one scalar load shared by the wave.
+// Paged: `page` is the block's table entry (block_page), loaded ahead.
 template <int STEPS, bool PAGED>
 __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __restrict__ k,
-                                           const Pages& pg, const int32_t* __restrict__ ptab,
-                                           int b, uint4 (&bv)[STEPS]) {
+                                           const Pages& pg, int page, int b,
+                                           uint4 (&bv)[STEPS]) {
   constexpr int D = STEPS * 32;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
@@ -176,15 +187,10 @@ __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __re
   key = key < ck.nkeys ? key : ck.nkeys - 1;  // padding lanes re-read a valid row
   int64_t row;
   if (PAGED) {
-    // Every operand of the page-table address is wave-uniform and the table
-    // is a restrict (never written) argument: a scalar load, counted apart
-    // from the K loads in flight, so waiting for it does not drain the ring.
     const int kb = __builtin_amdgcn_readfirstlane(ck.key0 + b * 16);
     const int j = kb >> pg.page_shift;
-    const int s = __builtin_amdgcn_readfirstlane(ck.s), l = __builtin_amdgcn_readfirstlane(ck.l),
-              g = __builtin_amdgcn_readfirstlane(ck.g);
-    int p = ptab[(int64_t)s * pg.max_pages + j];
-    p = p < 0 ? 0 : (p >= pg.num_pages ? pg.num_pages - 1 : p);
+    const int l = __builtin_amdgcn_readfirstlane(ck.l), g = __builtin_amdgcn_readfirstlane(ck.g);
+    const int p = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
     row = (int64_t)l * pg.layer_stride + (int64_t)g * pg.head_stride +
           (int64_t)p * pg.page_stride +
           (int64_t)(ck.key0 + key - (j << pg.page_shift)) * pg.token_stride;
@@ -199,17 +205,23 @@ __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __re
 // Request the first kPrefetch blocks of each wave of a chunk (wave w takes
 // blocks w, w + 4, ...).  chunk_raw consumes them.  Unconditional (blocks
 // past the chunk's end re-read its last block) so that no earlier ring
-// contents stay live across the caller's code.
+// contents stay live across the caller's code.  Paged: pid[j] receives the
+// table entry of the block ring slot j loads next (loaded ahead).
 template <int STEPS, bool PAGED>
 __device__ __forceinline__ void ring_prime(const Chunk& ck, const uint16_t* __restrict__ k,
                                            const Pages& pg, const int32_t* __restrict__ ptab,
-                                           uint4 (&ring)[kPrefetch][STEPS]) {
+                                           uint4 (&ring)[kPrefetch][STEPS], int (&pid)[kPrefetch]) {
   const int wave = threadIdx.x >> 6;
   const int nblk = (ck.nkeys + 15) >> 4;
 #pragma unroll
   for (int j = 0; j < kPrefetch; ++j) {
     const int b = wave + kFusedWaves * j;
-    load_block<STEPS, PAGED>(ck, k, pg, ptab, b < nblk ? b : nblk - 1, ring[j]);
+    const int bl = b < nblk ? b : nblk - 1;
+    load_block<STEPS, PAGED>(ck, k, pg, PAGED ? block_page(ck, pg, ptab, bl) : 0, bl, ring[j]);
+    if (PAGED) {
+      const int bp = b + kFusedWaves * kPrefetch;
+      pid[j] = block_page(ck, pg, ptab, bp < nblk ? bp : nblk - 1);
+    }
   }
 }
 
@@ -248,7 +260,8 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
                                           const UnitOperands<STEPS>& op,
                                           const uint16_t* __restrict__ k, const Pages& pg,
                                           const int32_t* __restrict__ ptab, float* raw,
-                                          uint4 (&ring)[kPrefetch][STEPS]) {
+                                          uint4 (&ring)[kPrefetch][STEPS],
+                                          int (&pid)[kPrefetch]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int nblk = (ck.nkeys + 15) >> 4;
@@ -287,7 +300,13 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         const int bn = b + kFusedWaves * kPrefetch;
-        if (bn < nblk) load_block<STEPS, PAGED>(ck, k, pg, ptab, bn, ring[j]);
+        if (bn < nblk) {
+          load_block<STEPS, PAGED>(ck, k, pg, pid[j], bn, ring[j]);
+          if (PAGED) {  // the entry for this slot's following block
+            const int bp = bn + kFusedWaves * kPrefetch;
+            pid[j] = block_page(ck, pg, ptab, bp < nblk ? bp : nblk - 1);
+          }
+        }
         // D layout: lane holds heads 4q..4q+3 of key b*16 + m (rows past
         // the chunk's end land in the buffer's padding and are never read)
 #pragma unroll
@@ -509,6 +528,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   // operands are therefore requested before this chunk's stores (scores,
   // published moments) and the streaming loop never waits on a store.
   uint4 ring[kPrefetch][STEPS];
+  int pid[kPrefetch] = {};  // paged: table entries of the blocks the ring loads next
   UnitOperands<STEPS> op;
   Chunk prev, ck;
   int prev_last = 0;  // last ticket of prev's unit
@@ -519,7 +539,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   int t = __builtin_amdgcn_readfirstlane(sh.ticket);  // uniform: chunk fields in SGPRs
   if (t < total_tickets) {
     ck = decode_chunk(seqs, S, L, Hkv, ch, t);
-    ring_prime<STEPS, PAGED>(ck, k, pg, ptab, ring);
+    ring_prime<STEPS, PAGED>(ck, k, pg, ptab, ring, pid);
     load_operands<STEPS>(ck, apack, op);
   }
   // Each pass streams chunk ck (if any) and finalizes prev (if any).  Every
@@ -538,7 +558,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
-    if (have) chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring);
+    if (have) chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid);
     if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
@@ -549,7 +569,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
     }
-    if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring);
+    if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
     if (have) {
       chunk_moments(ck, G, rs, buf_cur, sh);
       __syncthreads();
@@ -565,7 +585,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       __syncthreads();
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
-      ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring);
+      ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
     }
     load_operands<STEPS>(nk, apack, op);
     if (have_prev) chunk_store_scores(prev, buf_prev, scores, raw_out);
