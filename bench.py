@@ -58,6 +58,27 @@ def measured_traffic():
     return t.get("bytes_per_call")
 
 
+def device_copy_gbps(reps=10):
+    """Read+write rate of a plain 1 GiB device-to-device copy on the current
+    stream (HIP events), the practical ceiling of a gather."""
+    import torch
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * COPY_PROBE_BYTES / t / 1e9
+
+
 def copy_probe(reps=10):
     """A plain device copy of COPY_PROBE_BYTES, for scaling FETCH_SIZE and
     WRITE_SIZE (each copy reads and writes exactly that many bytes)."""
@@ -733,6 +754,9 @@ def main():
                      "algorithmic_bytes_per_launch": b_score,
                      "launch": "tri_score call: prologue + operand pack + fused score kernel"},
     }
+    copy_gbps = device_copy_gbps()
+    out["device_copy_gbps"] = copy_gbps
+    out["hbm_frac_of_device_copy"] = gbps / copy_gbps
     if budgets is not None:
         out["config"]["budget"] = "pyramid"
         out["config"]["layer_budgets"] = [int(x) for x in budgets[0]]

@@ -214,3 +214,20 @@ def check_selection_exact(case: Case, res, units=None, rows_units=None):
             src = src_t[start:start + n].cpu().numpy()
             got = out_t[ostart:ostart + b].cpu().numpy()
             assert np.array_equal(got, O.compact_rows(src, ref)), f"{name} rows of unit {(s, l, g)}"
+
+
+def check_kept_near_threshold(case: Case, res, units, factored=True):
+    """The GPU's kept set of each unit against the oracle's own top-B on its
+    fp64 scores: they may differ only by keys whose oracle score lies within
+    1e-4 * max(1, |s_(b)|) of the oracle's b-th largest score s_(b) (the
+    scores' tolerance decides those keys, not the method)."""
+    kept = res["kept"].cpu().numpy()
+    for (s, l, g) in units:
+        ostart, b = case.unit_out_rows(s, l, g)
+        if b == 0:
+            continue
+        _, n, ref, _, _, _ = oracle_unit(case, s, l, g, factored=factored)
+        thr = np.sort(ref)[::-1][b - 1]
+        diff = set(O.select_topb(ref, b).tolist()) ^ set(kept[ostart:ostart + b].tolist())
+        bad = sorted(i for i in diff if abs(ref[i] - thr) > 1e-4 * max(1.0, abs(thr)))
+        assert not bad, f"unit {(s, l, g)}: keys {bad[:10]} differ away from the threshold {thr}"

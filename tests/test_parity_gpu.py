@@ -13,8 +13,8 @@ import torch
 
 import oracle as O
 import synth
-from harness import (check_raw, check_scores, check_selection_exact, gpu_calibrate, gpu_run,
-                     oracle_unit, units_of)
+from harness import (check_kept_near_threshold, check_raw, check_scores, check_selection_exact,
+                     gpu_calibrate, gpu_run, oracle_unit, units_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,7 @@ def test_reduced_config_parity(name):
     _compare_units(case, res, units, factored=True)
     _compare_units(case, res, units[:1] + units[-1:], factored=False)
     check_selection_exact(case, res)
+    check_kept_near_threshold(case, res, units)
 
 
 @pytest.mark.parametrize("d,G", [(48, 3), (96, 5), (256, 2), (32, 16)])
@@ -132,6 +133,7 @@ def test_other_head_dims(d, G):
     units = units_of(case)
     _compare_units(case, res, units, factored=True)
     check_selection_exact(case, res)
+    check_kept_near_threshold(case, res, units)
 
 
 def test_duplicate_keys_score_bitwise_equal():
@@ -207,6 +209,7 @@ def test_c3_full_size_sampled():
     _compare_units(case, res, samp, factored=True)
     _compare_units(case, res, samp[:1], factored=False)
     check_selection_exact(case, res, units=units, rows_units=samp)
+    check_kept_near_threshold(case, res, samp)
 
 
 @pytest.mark.timeout(600)
@@ -216,6 +219,7 @@ def test_c2_full_size_sampled():
     units = units_of(case)
     samp = _sample(units, 6, seed=2)
     _compare_units(case, res, samp, factored=True)
+    check_kept_near_threshold(case, res, samp)
     check_selection_exact(case, res, units=_sample(units, 2000, seed=5), rows_units=samp)
 
 
@@ -226,6 +230,7 @@ def test_c4_full_layer_sampled():
     units = units_of(case)
     samp = _sample(units, 6, seed=4)
     _compare_units(case, res, samp, factored=True)
+    check_kept_near_threshold(case, res, samp)
     check_selection_exact(case, res, units=units, rows_units=samp)
 
 
@@ -236,6 +241,7 @@ def test_c5_full_size():
     units = units_of(case)
     _compare_units(case, res, units, factored=True)
     check_selection_exact(case, res, units=units, rows_units=units[:2])
+    check_kept_near_threshold(case, res, units)
     sc = res["scores"].cpu().numpy()
     for (s, l, g) in units:
         start, n = case.unit_rows(s, l, g)
