@@ -730,6 +730,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step * 1e3,
+        "ms_per_step_median": float(np.median(t_step)) * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
