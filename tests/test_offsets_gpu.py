@@ -47,8 +47,8 @@ def _compare(case, res, units, offsets, reduce, factored=True):
             check_raw(raw[start:start + n], S, sigma, "raw " + what)
         if hs is not None:
             u = (s * L + l) * H + g
-            np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * np.max(sigma))
-            np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5)
+            np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * max(np.max(sigma), np.max(np.abs(S))))
+            np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5, atol=1e-5 * np.max(np.abs(S)))
 
 
 def _bits(t):

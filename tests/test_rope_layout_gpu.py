@@ -38,8 +38,8 @@ def _compare(case, res, units, factored=True, offsets=None, reduce="mean"):
             check_raw(raw[start:start + n], S, sigma, f"half raw unit {(s, l, g)}")
         if hs is not None:
             u = (s * L + l) * H + g
-            np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * np.max(sigma))
-            np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5)
+            np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * max(np.max(sigma), np.max(np.abs(S))))
+            np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5, atol=1e-5 * np.max(np.abs(S)))
 
 
 @pytest.mark.parametrize("d,G", [(128, 4), (64, 7), (256, 2), (192, 3), (96, 4), (24, 2)])
