@@ -28,7 +28,7 @@ METRIC = "keys scored+compacted/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 COPY_PROBE_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_c3.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_long_reasoning_32k_to_2048.json")
 # The fused score kernel, its operand pack and launch shape (score_mfma.hip),
 # the prologue (calib.hip) and the shared device helpers (tri_internal.hpp):
 # the kernels one tri_score call runs on the 32K->2048 workload.
@@ -174,7 +174,7 @@ def write_traffic(run_root, out):
             raw[name] = {"FETCH_SIZE": f, "WRITE_SIZE": w}
             fetch += f * 1024.0 * fetch_scale
             write += w * 1024.0 * write_scale
-    cfg = synth_config_bytes("c3")
+    cfg = synth_config_bytes("long_reasoning")
     t = {
         "what": "HBM bytes per tri_score call on the 32K->2048 long-reasoning workload (28 layers, "
                 "4 KV heads, 28 q heads, d 128, batch 8): prologue + operand pack + fused score kernel",
@@ -199,16 +199,16 @@ def write_traffic(run_root, out):
 def synth_config_bytes(name):
     """Algorithmic tri_score bytes of a fixed-length workload, from its sizes
     alone (no tensors): units * n * (d*2 + 4)."""
-    sizes = {"c3": dict(S=8, L=28, Hkv=4, n=32768, d=128)}[name]
+    sizes = {"long_reasoning": dict(S=8, L=28, Hkv=4, n=32768, d=128)}[name]
     return sizes["S"] * sizes["L"] * sizes["Hkv"] * sizes["n"] * (sizes["d"] * 2 + 4)
 
 
 WORKLOADS = {
-    # name: (config id, overrides, label)
-    "c3": (3, {}, "long_reasoning_32k_to_2048"),
-    "c2": (2, {}, "decode_window_3200_to_3072"),
-    "c4": (4, {}, "ragged_256seq_one_layer"),
-    "c5": (5, {}, "stress_ties_131072_to_4096"),
+    # name: (overrides, label)
+    "long_reasoning": ({}, "long_reasoning_32k_to_2048"),
+    "decode_window": ({}, "decode_window_3200_to_3072"),
+    "ragged": ({}, "ragged_256seq_one_layer"),
+    "stress_ties": ({}, "stress_ties_131072_to_4096"),
 }
 
 
@@ -370,7 +370,7 @@ def run_decode(args):
     dev = "cuda:0"
     torch.cuda.set_device(0)
     print("[bench] building the decode-window prompts", file=sys.stderr, flush=True)
-    case = synth.config_case(2, device=dev)
+    case = synth.workload_case("decode_window", device=dev)
     sh = case.shape
     S, LH, d = case.num_seqs, sh.num_layers * sh.num_kv_heads, sh.head_dim
     T = warm + steps
@@ -556,7 +556,7 @@ def main():
                     help="time the decode-loop driver at the decode-window shape")
     ap.add_argument("--calib", action="store_true",
                     help="calibration at scale and the reconstruction diagnostic")
-    ap.add_argument("--workload", default="c3", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="long_reasoning", choices=list(WORKLOADS))
     ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
     ap.add_argument("--rope-layout", default="interleaved", choices=["interleaved", "half"],
@@ -610,9 +610,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cid, over, label = WORKLOADS[args.workload]
+    over, label = WORKLOADS[args.workload]
     print(f"[bench] building workload {label}", file=sys.stderr, flush=True)
-    case = synth.config_case(cid, device=dev, **over)
+    case = synth.workload_case(args.workload, device=dev, **over)
     if args.rope_layout == "half":
         # the same keys with their columns permuted to the half-split layout
         d = case.shape.head_dim
@@ -750,7 +750,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "tri_score",
                      "achieved": score_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": score_gbps / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic() if args.workload == "c3" and not variant
+                     "traffic": measured_traffic() if args.workload == "long_reasoning"
+                     and not variant
                      and args.rope_layout == "interleaved" else None,
                      "algorithmic_bytes_per_launch": b_score,
                      "launch": "tri_score call: prologue + operand pack + fused score kernel"},

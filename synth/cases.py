@@ -320,15 +320,24 @@ def build_case(name: str, shape: Shape, seq_lens, budgets, device="cpu", seed=0,
 
 
 # ---------------------------------------------------------------------------
-# The five workloads.  scale < 1 shrinks batch / layers / lengths for tests.
+# The five workloads, by name; keyword overrides shrink batch, layers or
+# lengths for tests.
+#   smallest         1 unit of 4096 keys -> 512, d 128, stats from calibration
+#   decode_window    64 seq x 32 layers x 8 KV heads (G 4), 3200 keys -> 3072
+#   long_reasoning   8 seq x 28 layers x 4 KV heads (G 7), 32768 keys -> 2048
+#   ragged           256 seq of 2048..16384 keys, budgets 1024/2048/3072, G 4
+#   stress_ties      d 64, G 8, 131072 keys -> 4096, weak bands, twin blocks
 # ---------------------------------------------------------------------------
-def config_case(cid: int, device="cpu", seed=0, **over) -> Case:
-    if cid == 1:
+WORKLOAD_NAMES = ("smallest", "decode_window", "long_reasoning", "ragged", "stress_ties")
+
+
+def workload_case(name: str, device="cpu", seed=0, **over) -> Case:
+    if name == "smallest":
         shape = Shape(128, 1, 1, 1)
-        return build_case("c1_smallest", shape, [over.get("n", 4096)], [over.get("B", 512)],
-                          device=device, seed=seed, stats="calibrate",
+        return build_case("smallest_4096_to_512", shape, [over.get("n", 4096)],
+                          [over.get("B", 512)], device=device, seed=seed, stats="calibrate",
                           calib_samples=over.get("calib_samples", 10240))
-    if cid == 2:
+    if name == "decode_window":
         S = over.get("S", 64)
         L = over.get("L", 32)
         shape = Shape(128, 32, 8, L)
@@ -341,16 +350,16 @@ def config_case(cid: int, device="cpu", seed=0, **over) -> Case:
             pos = np.concatenate([old, np.arange(pq - win, pq)])
             positions.append(torch.as_tensor(pos, dtype=torch.int64, device=device))
             cur.append(pq)
-        return build_case("c2_decode_window", shape, [n] * S, [B] * S, device=device, seed=seed,
-                          positions=positions, cur_pos=cur)
-    if cid == 3:
+        return build_case("decode_window_3200_to_3072", shape, [n] * S, [B] * S, device=device,
+                          seed=seed, positions=positions, cur_pos=cur)
+    if name == "long_reasoning":
         S = over.get("S", 8)
         L = over.get("L", 28)
         n = over.get("n", 32768)
         shape = Shape(128, 28, 4, L)
-        return build_case("c3_long_reasoning", shape, [n] * S, [over.get("B", 2048)] * S,
-                          device=device, seed=seed)
-    if cid == 4:
+        return build_case("long_reasoning_32k_to_2048", shape, [n] * S,
+                          [over.get("B", 2048)] * S, device=device, seed=seed)
+    if name == "ragged":
         S = over.get("S", 256)
         L = over.get("L", 1)
         lo, hi = over.get("n_range", (2048, 16384))
@@ -360,10 +369,11 @@ def config_case(cid: int, device="cpu", seed=0, **over) -> Case:
         budgets = g.choice([1024, 2048, 3072], size=S).tolist()
         if "budgets" in over:
             budgets = over["budgets"]
-        return build_case("c4_ragged", shape, lens, budgets, device=device, seed=seed)
-    if cid == 5:
+        return build_case("ragged_256seq", shape, lens, budgets, device=device, seed=seed)
+    if name == "stress_ties":
         n = over.get("n", 131072)
+        S = over.get("S", 1)
         shape = Shape(64, 64, 8, over.get("L", 1))
-        return build_case("c5_stress_ties", shape, [n] * over.get("S", 1), [over.get("B", 4096)] * over.get("S", 1),
+        return build_case("stress_ties_131072_to_4096", shape, [n] * S, [over.get("B", 4096)] * S,
                           device=device, seed=seed, low_band_frac=0.1, dup_blocks=True)
-    raise ValueError(cid)
+    raise ValueError(name)

@@ -104,7 +104,7 @@ def test_ragged_pyramid_budgets(seed):
 
 def test_uniform_layers_equal_tri_select_compact():
     """One budget for every layer reproduces tri_select_compact exactly."""
-    case = synth.config_case(4, device=DEV, S=6, L=3, n_range=(100, 2500))
+    case = synth.workload_case("ragged", device=DEV, S=6, L=3, n_range=(100, 2500))
     res = gpu_run(case, raw=False, stats=False)
     budgets = np.repeat(case.budget[:, None], 3, axis=1).astype(np.int32)
     out = _run_layers(case, res["scores"], budgets)
@@ -128,7 +128,7 @@ def test_scores_only_selection():
 def test_long_reasoning_pyramid_full_size():
     """8 x 32768 keys, 28 layers, pyramid mean 2048 ratio 3: every unit's
     kept set checked; rows checked on sampled units."""
-    case = synth.config_case(3, device=DEV)
+    case = synth.workload_case("long_reasoning", device=DEV)
     L, H = case.shape.num_layers, case.shape.num_kv_heads
     pyr = R.tri_pyramid_budgets(L, 2048, 3.0)
     budgets = np.repeat(pyr[None, :], case.num_seqs, axis=0).astype(np.int32)

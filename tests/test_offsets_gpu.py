@@ -82,10 +82,10 @@ def test_mean_over_other_sets(name, d, G):
 
 # ------------------------------------------------- max over the offsets
 @pytest.mark.parametrize("name", list(SETS))
-def test_max_c3_shape(name):
+def test_max_long_reasoning_shape(name):
     """G = 7, d = 128 (the long-reasoning shape), 5000 keys: five tickets of
     one unit, the last ragged."""
-    case = synth.config_case(3, device=DEV, S=1, L=1, n=5000, B=2048)
+    case = synth.workload_case("long_reasoning", device=DEV, S=1, L=1, n=5000, B=2048)
     res = gpu_score_offsets(case, SETS[name], "max")
     units = units_of(case)
     _compare(case, res, units, SETS[name], "max")
@@ -117,7 +117,7 @@ def test_max_ragged_batch_then_select():
     """Many ragged sequences (tickets of several units share a work-group),
     raw scores spilled to the workspace, then selection and compaction on
     the max-reduced scores."""
-    case = synth.config_case(4, device=DEV, S=6, L=1, n_range=(100, 3000))
+    case = synth.workload_case("ragged", device=DEV, S=6, L=1, n_range=(100, 3000))
     res = gpu_score_offsets(case, DEFAULT, "max", raw_in_ws=True)
     units = units_of(case)
     _compare(case, res, units, DEFAULT, "max")
@@ -127,7 +127,7 @@ def test_max_ragged_batch_then_select():
 
 def test_single_offset_max_equals_mean():
     """With one offset the maximum and the mean are the same score."""
-    case = synth.config_case(3, device=DEV, S=1, L=1, n=3000, B=700)
+    case = synth.workload_case("long_reasoning", device=DEV, S=1, L=1, n=3000, B=700)
     mx = gpu_score_offsets(case, [1024.0], "max")
     mn = gpu_score_offsets(case, [1024.0], "mean")
     a, b = mx["scores"].cpu().numpy(), mn["scores"].cpu().numpy()
@@ -135,7 +135,7 @@ def test_single_offset_max_equals_mean():
 
 
 def test_max_deterministic_bitwise():
-    case = synth.config_case(3, device=DEV, S=1, L=2, n=3000, B=700)
+    case = synth.workload_case("long_reasoning", device=DEV, S=1, L=2, n=3000, B=700)
     a = gpu_score_offsets(case, DEFAULT, "max")
     b = gpu_score_offsets(case, DEFAULT, "max")
     for key in ("scores", "raw", "head_stats"):
@@ -143,10 +143,10 @@ def test_max_deterministic_bitwise():
 
 
 @pytest.mark.timeout(600)
-def test_max_c3_full_size_sampled():
+def test_max_long_reasoning_full_size_sampled():
     """32K -> 2048 workload at full size with the maximum over the default
     set: sampled units against the oracle, selection exact on every unit."""
-    case = synth.config_case(3, device=DEV)
+    case = synth.workload_case("long_reasoning", device=DEV)
     res = gpu_score_offsets(case, DEFAULT, "max", raw=False)
     units = units_of(case)
     g = np.random.default_rng(9)

@@ -184,7 +184,7 @@ def test_long_reasoning_paged_full_size():
     """The 32K -> 2048 workload in 16-token token-major pages: scores equal
     the packed call's on every unit; selection equal; rows of sampled units
     equal in a 64-token output pool."""
-    case = synth.config_case(3, device=DEV)
+    case = synth.workload_case("long_reasoning", device=DEV)
     res = gpu_run(case, raw=False, stats=False)
     pool = synth.paged_from_case(case, 16, seed=21)
     pr = _paged_score(case, pool)

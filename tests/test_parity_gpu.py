@@ -42,8 +42,8 @@ def _compare_units(case, res, units, factored):
 
 
 # ------------------------------------------------------------- calibration
-def test_calibrate_c1_matches_oracle():
-    case = synth.config_case(1, device=DEV)
+def test_calibrate_smallest_matches_oracle():
+    case = synth.workload_case("smallest", device=DEV)
     gpu_calibrate(case)
     q = O.bf16_bits_to_f64(case.calib_q[0].cpu().numpy().view(np.uint16))   # [N, Hq, d]
     om = O.rope_omega(128, 1e4)
@@ -77,19 +77,19 @@ def test_calibrate_pre_rope_and_multi_layer():
         np.testing.assert_allclose(r[l].cpu().numpy(), Rr, rtol=1e-5)
 
 
-# ----------------------------------------------------------- c1 end to end
-def test_c1_end_to_end_term_by_term():
+# ------------------------------------------------------ smallest, end to end
+def test_smallest_end_to_end_term_by_term():
     """Smallest workload in full: GPU calibration -> score -> select/compact,
     against the oracle's own calibration and term-by-term scores."""
-    case = synth.config_case(1, device=DEV)
+    case = synth.workload_case("smallest", device=DEV)
     gpu_calibrate(case)
     res = gpu_run(case)
     q = O.bf16_bits_to_f64(case.calib_q[0].cpu().numpy().view(np.uint16))
     om = O.rope_omega(128, 1e4)
     stats = O.calibrate(q, case.calib_pos.cpu().numpy(), om)
     start, n, ref, S, mu, sigma = oracle_unit(case, 0, 0, 0, factored=False, stats=stats)
-    check_scores(res["scores"].cpu().numpy(), ref, "c1")
-    check_raw(res["raw"].cpu().numpy(), S, sigma, "c1 raw")
+    check_scores(res["scores"].cpu().numpy(), ref, "smallest")
+    check_raw(res["raw"].cpu().numpy(), S, sigma, "smallest raw")
     check_selection_exact(case, res)
     # end-to-end kept set vs the oracle's own selection on fp64 scores
     b = case.kept(0)
@@ -102,18 +102,16 @@ def test_c1_end_to_end_term_by_term():
 
 # ------------------------------------------- reduced configs, many tiles
 REDUCED = {
-    "c2": dict(cid=2, S=2, L=1),                 # 16 units, n = 3200 (3 tiles + tail)
-    "c3": dict(cid=3, S=1, L=1, n=5000, B=2048),  # G = 7, 4 tiles + ragged tail
-    "c4": dict(cid=4, S=6, L=1, n_range=(100, 3000)),  # ragged lengths, some B >= n
-    "c5": dict(cid=5, n=5000, B=1024),           # d = 64, G = 8, duplicated blocks
+    "decode_window": dict(S=2, L=1),                # 16 units, n = 3200 (3 tiles + tail)
+    "long_reasoning": dict(S=1, L=1, n=5000, B=2048),  # G = 7, 4 tiles + ragged tail
+    "ragged": dict(S=6, L=1, n_range=(100, 3000)),  # ragged lengths, some B >= n
+    "stress_ties": dict(n=5000, B=1024),            # d = 64, G = 8, duplicated blocks
 }
 
 
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_reduced_config_parity(name):
-    kw = dict(REDUCED[name])
-    cid = kw.pop("cid")
-    case = synth.config_case(cid, device=DEV, **kw)
+    case = synth.workload_case(name, device=DEV, **REDUCED[name])
     res = gpu_run(case)
     units = units_of(case)
     # every unit against the factored oracle path, two against term-by-term
@@ -137,7 +135,7 @@ def test_other_head_dims(d, G):
 
 
 def test_duplicate_keys_score_bitwise_equal():
-    case = synth.config_case(5, device=DEV, n=4096, B=512)
+    case = synth.workload_case("stress_ties", device=DEV, n=4096, B=512)
     res = gpu_run(case, raw=False, stats=False, compact=False)
     sc = res["scores"].cpu().numpy()
     for (s, l, g) in units_of(case):
@@ -148,7 +146,7 @@ def test_duplicate_keys_score_bitwise_equal():
 
 
 def test_determinism_bitwise():
-    case = synth.config_case(3, device=DEV, S=1, L=2, n=3000, B=700)
+    case = synth.workload_case("long_reasoning", device=DEV, S=1, L=2, n=3000, B=700)
     a = gpu_run(case)
     b = gpu_run(case)
     for key in ("scores", "raw", "head_stats", "kept", "k_out", "v_out", "pos_out"):
@@ -199,10 +197,10 @@ def _sample(units, k, seed=0):
 
 
 @pytest.mark.timeout(600)
-def test_c3_full_size_sampled():
+def test_long_reasoning_full_size_sampled():
     """32K -> 2048 long-reasoning workload at full size: sampled units against
     the oracle, selection bit-exact on every unit, rows on sampled units."""
-    case = synth.config_case(3, device=DEV)
+    case = synth.workload_case("long_reasoning", device=DEV)
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     samp = _sample(units, 6, seed=3)
@@ -213,8 +211,8 @@ def test_c3_full_size_sampled():
 
 
 @pytest.mark.timeout(600)
-def test_c2_full_size_sampled():
-    case = synth.config_case(2, device=DEV)
+def test_decode_window_full_size_sampled():
+    case = synth.workload_case("decode_window", device=DEV)
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     samp = _sample(units, 6, seed=2)
@@ -224,8 +222,8 @@ def test_c2_full_size_sampled():
 
 
 @pytest.mark.timeout(600)
-def test_c4_full_layer_sampled():
-    case = synth.config_case(4, device=DEV)
+def test_ragged_full_layer_sampled():
+    case = synth.workload_case("ragged", device=DEV)
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     samp = _sample(units, 6, seed=4)
@@ -235,8 +233,8 @@ def test_c4_full_layer_sampled():
 
 
 @pytest.mark.timeout(600)
-def test_c5_full_size():
-    case = synth.config_case(5, device=DEV)
+def test_stress_ties_full_size():
+    case = synth.workload_case("stress_ties", device=DEV)
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     _compare_units(case, res, units, factored=True)

@@ -93,7 +93,7 @@ def test_half_split_calibration():
     """Per-band sums do not depend on where the parts are stored: the
     half-split statistics equal the interleaved ones bit for bit, and the
     oracle's within the calibration bar."""
-    base = synth.config_case(1, device=DEV, calib_samples=3000)
+    base = synth.workload_case("smallest", device=DEV, calib_samples=3000)
     case = half_split(base)
     gpu_calibrate(base)
     gpu_calibrate(case)
@@ -147,7 +147,7 @@ def test_half_split_trig_correlation(d, G):
 def test_half_split_long_reasoning_full_size():
     """The 32K -> 2048 workload stored half split: sampled units against the
     oracle, selection bit-exact on every unit."""
-    case = half_split(synth.config_case(3, device=DEV))
+    case = half_split(synth.workload_case("long_reasoning", device=DEV))
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     g = np.random.default_rng(9)
