@@ -454,3 +454,16 @@ def test_workspace_bytes_paged():
         R.tri_workspace_bytes_offsets(sh, cu, 3, "max")
     assert R.tri_workspace_bytes_paged(sh, cu, 12) == 0
     assert R.tri_workspace_bytes_paged(sh, cu, 16, 5000) == 0
+
+
+def test_sequence_count_limit():
+    """One call plans at most 8192 sequences (the plan travels through a
+    fixed pinned staging slot); 8193 is refused before any device work."""
+    sh = R.make_shape(64, 4, 2, 1)
+    ok_cu = np.arange(8193, dtype=np.int64)          # 8192 sequences of one key
+    bad_cu = np.arange(8194, dtype=np.int64)
+    assert R.tri_workspace_bytes(sh, ok_cu) > 0
+    assert R.tri_workspace_bytes(sh, bad_cu) == 0
+    assert _status(_score, sh, bad_cu, np.full(8193, 5, np.int32)) == ST["UNSUPPORTED"]
+    assert "8192" in R.last_error()
+    assert _status(_sel, sh, bad_cu, np.ones(8193, np.int32)) == ST["UNSUPPORTED"]

@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 import synth
-from harness import (check_raw, check_scores, check_selection_exact, gpu_run, gpu_score_offsets,
+from harness import (z_floor, check_raw, check_scores, check_selection_exact, gpu_run, gpu_score_offsets,
                      oracle_unit, units_of)
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +42,7 @@ def _compare(case, res, units, offsets, reduce, factored=True):
         start, n, ref, S, mu, sigma = oracle_unit(case, s, l, g, factored=factored,
                                                   offsets=offsets, reduce=reduce)
         what = f"{reduce} unit {(s, l, g)}"
-        check_scores(scores[start:start + n], ref, what)
+        check_scores(scores[start:start + n], ref, what, z_floor(S, sigma))
         if raw is not None:
             check_raw(raw[start:start + n], S, sigma, "raw " + what)
         if hs is not None:

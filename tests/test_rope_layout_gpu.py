@@ -14,7 +14,7 @@ import torch
 
 import oracle as O
 import synth
-from harness import (check_raw, check_scores, check_selection_exact, gpu_calibrate, gpu_run,
+from harness import (z_floor, check_raw, check_scores, check_selection_exact, gpu_calibrate, gpu_run,
                      gpu_score_offsets, half_split, oracle_unit, shape_of, units_of)
 from synth.cases import _calibration_queries
 
@@ -33,7 +33,7 @@ def _compare(case, res, units, factored=True, offsets=None, reduce="mean"):
             continue
         start, n, ref, S, mu, sigma = oracle_unit(case, s, l, g, factored=factored,
                                                   offsets=offsets, reduce=reduce)
-        check_scores(scores[start:start + n], ref, f"half unit {(s, l, g)}")
+        check_scores(scores[start:start + n], ref, f"half unit {(s, l, g)}", z_floor(S, sigma))
         if raw is not None:
             check_raw(raw[start:start + n], S, sigma, f"half raw unit {(s, l, g)}")
         if hs is not None:
