@@ -84,8 +84,14 @@ class Case:
         return max(0, min(int(self.budget[s]), self.seq_len(s)))
 
     def out_cu(self) -> np.ndarray:
-        b = [self.kept(s) for s in range(self.num_seqs)]
-        return np.concatenate([[0], np.cumsum(b)]).astype(np.int64)
+        key = (np.asarray(self.budget).tobytes(), np.asarray(self.cu_len).tobytes())
+        cached = self.meta.get("_out_cu")
+        if cached is None or cached[0] != key:
+            lens = np.diff(np.asarray(self.cu_len, dtype=np.int64))
+            b = np.clip(np.minimum(np.asarray(self.budget, dtype=np.int64), lens), 0, None)
+            cached = (key, np.concatenate([[0], np.cumsum(b)]).astype(np.int64))
+            self.meta["_out_cu"] = cached
+        return cached[1]
 
     def total_rows(self) -> int:
         return int(self.cu_len[-1]) * self.shape.num_layers * self.shape.num_kv_heads

@@ -216,16 +216,22 @@ def check_selection_exact(case: Case, res, units=None, rows_units=None):
         ref = O.select_topb(scores[start:start + n], int(case.budget[s]))
         assert len(ref) == b
         np.testing.assert_array_equal(kept[ostart:ostart + b], ref, err_msg=f"unit {(s, l, g)}")
+    # small tensors come to the host once; full-size caches unit by unit
+    host = {}
+    for name, src_t in (("k_out", case.k), ("v_out", case.v), ("pos_out", case.k_pos)):
+        out_t = res.get(name)
+        if out_t is None or src_t is None:
+            continue
+        small = src_t.numel() * src_t.element_size() <= (256 << 20)
+        host[name] = (src_t.cpu().numpy() if small else src_t,
+                      out_t.cpu().numpy() if small else out_t, small)
     for (s, l, g) in rows_units:
         start, n = case.unit_rows(s, l, g)
         ostart, b = case.unit_out_rows(s, l, g)
         ref = O.select_topb(scores[start:start + n], int(case.budget[s]))
-        for name, src_t in (("k_out", case.k), ("v_out", case.v), ("pos_out", case.k_pos)):
-            out_t = res.get(name)
-            if out_t is None or src_t is None:
-                continue
-            src = src_t[start:start + n].cpu().numpy()
-            got = out_t[ostart:ostart + b].cpu().numpy()
+        for name, (src_a, out_a, small) in host.items():
+            src = src_a[start:start + n] if small else src_a[start:start + n].cpu().numpy()
+            got = out_a[ostart:ostart + b] if small else out_a[ostart:ostart + b].cpu().numpy()
             assert np.array_equal(got, O.compact_rows(src, ref)), f"{name} rows of unit {(s, l, g)}"
 
 

@@ -260,6 +260,17 @@ def test_unit_past_fused_chunk_cap():
     check_selection_exact(case, res, units=units, rows_units=units)
 
 
+def _to_host(res):
+    return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in res.items()}
+
+
+def _to_device(case):
+    import dataclasses
+    mv = {f: getattr(case, f).to(DEV) for f in ("k", "v", "k_pos", "q_centre", "q_absmean", "q_R")
+          if getattr(case, f) is not None}
+    return dataclasses.replace(case, **mv)
+
+
 @pytest.mark.parametrize("S", [3000, 8192])
 def test_many_tiny_sequences(S):
     """Thousands of sequences of 0..40 keys (up to the 8192 a call takes;
@@ -270,11 +281,12 @@ def test_many_tiny_sequences(S):
     lens[g.choice(S, S // 10, replace=False)] = 0
     budgets = g.integers(0, 51, size=S)
     shape = synth.Shape(64, 4, 2, 1)
-    case = synth.build_case("tiny", shape, lens.tolist(), budgets.tolist(), device=DEV, seed=17)
-    res = gpu_run(case, raw=True, stats=True)
-    units = units_of(case)
-    _compare_units(case, res, units if S <= 3000 else units[::5], factored=True)
-    check_selection_exact(case, res)
+    # the checks read the host copy (thousands of units: no per-unit device reads)
+    host = synth.build_case("tiny", shape, lens.tolist(), budgets.tolist(), seed=17)
+    res = _to_host(gpu_run(_to_device(host), raw=True, stats=True))
+    units = units_of(host)
+    _compare_units(host, res, units if S <= 3000 else units[::5], factored=True)
+    check_selection_exact(host, res)
 
 
 def test_many_tiny_sequences_max_offsets():
@@ -284,9 +296,9 @@ def test_many_tiny_sequences_max_offsets():
     S = 1500
     lens = g.integers(0, 70, size=S)
     shape = synth.Shape(128, 8, 2, 1)
-    case = synth.build_case("tiny_max", shape, lens.tolist(), [1] * S, device=DEV, seed=19)
+    case = synth.build_case("tiny_max", shape, lens.tolist(), [1] * S, seed=19)
     offs = [1.0, 16.0, 256.0, 4096.0]
-    res = gpu_score_offsets(case, offs, "max", raw=True, stats=True)
+    res = _to_host(gpu_score_offsets(_to_device(case), offs, "max", raw=True, stats=True))
     sc = res["scores"].cpu().numpy()
     for (s, l, gg) in units_of(case)[::7]:
         if case.seq_len(s) == 0:
