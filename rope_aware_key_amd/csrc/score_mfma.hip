@@ -144,9 +144,17 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
   return ck;
 }
 
+// Staging tile of one wave: one 128-byte line of each of a block's 16 key
+// rows, padded to 9 16-byte chunks per row (conflict-free reads).
+constexpr int kTileChunks = 16 * 9;
+
 struct Shared {
-  double red1[kStatGroups][kMaxGroup];
-  double red2[kStatGroups][kMaxGroup];
+  // The between-chunk reductions (fp64 sum, sum of squares per head) and
+  // the waves' staging tiles (used only while streaming) share storage.
+  union {
+    double red[2][kStatGroups][kMaxGroup];
+    uint4 tile[kFusedWaves][kTileChunks];
+  };
   double pub[kMaxGroup][2];  // a chunk's moments, summed, until published
   float zmul[kMaxGroup], zadd[kMaxGroup];
   int ticket;
@@ -173,33 +181,78 @@ __device__ __forceinline__ int block_page(const Chunk& ck, const Pages& pg,
   return ptab[(int64_t)s * pg.max_pages + (kb >> pg.page_shift)];
 }
 
-// Block b (16 keys) of a chunk into bv: lane (m, q) takes 16 bytes of key
-// b*16 + m per step st (4 lanes cover 64 contiguous bytes of the row).
-// Paged: `page` is the block's table entry (block_page), loaded ahead.
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+// Whole-line loads and the tile transpose: rows of whole 128-byte lines (an
+// even number of steps), up to d = 192; at d = 256 the transpose's registers
+// would cost a wave per SIMD.
+template <int STEPS>
+constexpr bool whole_lines() { return STEPS % 2 == 0 && STEPS <= 6; }
+
+// Row (within the K array) of key `key` of a chunk's block b.  Paged:
+// `page` is the block's table entry (block_page), loaded ahead.
+template <bool PAGED>
+__device__ __forceinline__ int64_t key_row(const Chunk& ck, const Pages& pg, int page, int b,
+                                           int key) {
+  if (!PAGED) return ck.row0 + key;
+  const int kb = __builtin_amdgcn_readfirstlane(ck.key0 + b * 16);
+  const int j = kb >> pg.page_shift;
+  const int l = __builtin_amdgcn_readfirstlane(ck.l), g = __builtin_amdgcn_readfirstlane(ck.g);
+  const int p = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
+  return (int64_t)l * pg.layer_stride + (int64_t)g * pg.head_stride +
+         (int64_t)p * pg.page_stride +
+         (int64_t)(ck.key0 + key - (j << pg.page_shift)) * pg.token_stride;
+}
+
+// Block b (16 keys) of a chunk into bv.  With whole_lines: load i brings line i/2 of rows 8*(i%2) .. +7,
+// eight lanes per line, non-temporal (each line is read once, whole);
+// transpose_block then puts the data in MFMA layout.  Otherwise lane
+// (m, q) takes 16 bytes of key b*16 + m per step st (4 lanes cover 64
+// contiguous bytes of the row), the MFMA layout directly.  Lanes past the
+// chunk's last key re-read a valid row.
 template <int STEPS, bool PAGED>
 __device__ __forceinline__ void load_block(const Chunk& ck, const uint16_t* __restrict__ k,
                                            const Pages& pg, int page, int b,
                                            uint4 (&bv)[STEPS]) {
   constexpr int D = STEPS * 32;
   const int lane = threadIdx.x & 63;
-  const int m = lane & 15, q = lane >> 4;
-  int key = b * 16 + m;
-  key = key < ck.nkeys ? key : ck.nkeys - 1;  // padding lanes re-read a valid row
-  int64_t row;
-  if (PAGED) {
-    const int kb = __builtin_amdgcn_readfirstlane(ck.key0 + b * 16);
-    const int j = kb >> pg.page_shift;
-    const int l = __builtin_amdgcn_readfirstlane(ck.l), g = __builtin_amdgcn_readfirstlane(ck.g);
-    const int p = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
-    row = (int64_t)l * pg.layer_stride + (int64_t)g * pg.head_stride +
-          (int64_t)p * pg.page_stride +
-          (int64_t)(ck.key0 + key - (j << pg.page_shift)) * pg.token_stride;
-  } else {
-    row = ck.row0 + key;
-  }
-  const uint4* rp = reinterpret_cast<const uint4*>(k + row * D);
+  if constexpr (whole_lines<STEPS>()) {
+    const int r8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
-  for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
+    for (int i = 0; i < STEPS; ++i) {
+      int key = b * 16 + 8 * (i & 1) + r8;
+      key = key < ck.nkeys ? key : ck.nkeys - 1;
+      const v4u_t* rp = reinterpret_cast<const v4u_t*>(k + key_row<PAGED>(ck, pg, page, b, key) * D);
+      const v4u_t w = __builtin_nontemporal_load(rp + 8 * (i >> 1) + c8);
+      __builtin_memcpy(&bv[i], &w, 16);
+    }
+  } else {
+    const int m = lane & 15, q = lane >> 4;
+    int key = b * 16 + m;
+    key = key < ck.nkeys ? key : ck.nkeys - 1;
+    const uint4* rp = reinterpret_cast<const uint4*>(k + key_row<PAGED>(ck, pg, page, b, key) * D);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) bv[st] = rp[4 * st + q];
+  }
+}
+
+// Whole-line loads to MFMA layout, in place, through the wave's tile: for
+// each line h, loads 2h and 2h+1 (rows 0-7, 8-15) go in, and lane (m, q)
+// reads back chunks q and 4 + q of row m (steps 2h and 2h+1).  The wave's
+// LDS accesses complete in order, so no barrier is needed.
+template <int STEPS>
+__device__ __forceinline__ void transpose_block(uint4 (&bv)[STEPS], uint4* __restrict__ tile) {
+  if constexpr (whole_lines<STEPS>()) {
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, q = lane >> 4, r8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+    for (int h = 0; h < STEPS / 2; ++h) {
+      tile[r8 * 9 + c8] = bv[2 * h];
+      tile[(8 + r8) * 9 + c8] = bv[2 * h + 1];
+      bv[2 * h] = tile[m * 9 + q];
+      bv[2 * h + 1] = tile[m * 9 + 4 + q];
+    }
+  }
 }
 
 // Request the first kPrefetch blocks of each wave of a chunk (wave w takes
@@ -261,7 +314,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
                                           const uint16_t* __restrict__ k, const Pages& pg,
                                           const int32_t* __restrict__ ptab, float* raw,
                                           uint4 (&ring)[kPrefetch][STEPS],
-                                          int (&pid)[kPrefetch]) {
+                                          int (&pid)[kPrefetch], uint4* __restrict__ tile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int nblk = (ck.nkeys + 15) >> 4;
@@ -271,6 +324,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
     for (int j = 0; j < kPrefetch; ++j) {
       const int b = base + kFusedWaves * j;
       if (b < nblk) {
+        transpose_block<STEPS>(ring[j], tile);
         f32x4_t acc_t = {0.f, 0.f, 0.f, 0.f}, acc_n = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
@@ -345,8 +399,8 @@ __device__ __forceinline__ void chunk_moments(const Chunk& ck, int G, int rs, co
       b2 = fma(v, v, b2);
     }
   }
-  sh.red1[j][h] = a;
-  sh.red2[j][h] = b2;
+  sh.red[0][j][h] = a;
+  sh.red[1][j][h] = b2;
 }
 
 // Sum the chunk's per-group moments (call after a barrier that follows
@@ -358,8 +412,8 @@ __device__ __forceinline__ void chunk_moment_sums(int G, Shared& sh) {
     double a = 0.0, b2 = 0.0;
 #pragma unroll
     for (int g2 = 0; g2 < kStatGroups; ++g2) {
-      a += sh.red1[g2][tid];
-      b2 += sh.red2[g2][tid];
+      a += sh.red[0][g2][tid];
+      b2 += sh.red[1][g2][tid];
     }
     sh.pub[tid][0] = a;
     sh.pub[tid][1] = b2;
@@ -433,15 +487,15 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
       }
     }
   }
-  sh.red1[j][h] = a;
-  sh.red2[j][h] = b2;
+  sh.red[0][j][h] = a;
+  sh.red[1][j][h] = b2;
   __syncthreads();
   if (tid < G) {
     double sa = 0.0, sb = 0.0;
 #pragma unroll
     for (int g2 = 0; g2 < kStatGroups; ++g2) {
-      sa += sh.red1[g2][tid];
-      sb += sh.red2[g2][tid];
+      sa += sh.red[0][g2][tid];
+      sb += sh.red[1][g2][tid];
     }
     // population moments over the unit's keys; fp64 keeps the cancellation
     // in sum x^2 - n mu^2 far below the fp32 resolution of the raw scores
@@ -558,7 +612,9 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
-    if (have) chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid);
+    if (have)
+      chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid,
+                                    sh.tile[threadIdx.x >> 6]);
     if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
@@ -692,7 +748,8 @@ bool fused_supported(int d, bool half) {
 // Keys per ticket: as many as let three work-groups (two raw buffers of G
 // heads each) share a CU's LDS, in multiples of 64, at most 1024.
 int fused_chunk_keys(int G) {
-  const int per_wg = kFusedLdsPerCu / 3 - 4608;  // leave room for static LDS (Shared)
+  // leave room for the static LDS (Shared)
+  const int per_wg = kFusedLdsPerCu / 3 - (int)((sizeof(Shared) + 255) / 256 * 256);
   int ch = (per_wg / (2 * G * (int)sizeof(float)) - kRawPad) / 64 * 64;
   if (ch > 1024) ch = 1024;
   if (ch < 64) ch = 64;

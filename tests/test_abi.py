@@ -154,11 +154,11 @@ def test_workspace_grows_with_batch():
 
 
 def test_long_units_leave_the_fused_path():
-    """Units of more than 384 fused chunks (832 keys each at G = 7) take the
+    """Units of more than 384 fused chunks (768 keys each at G = 7) take the
     generic path, whose workspace holds the raw per-head scores; one chunk
     fewer stays fused and needs no such spill."""
     sh = R.make_shape(128, 7, 1, 1)
-    ch, cap = 832, 384
+    ch, cap = 768, 384
     fused_n = ch * cap
     long_n = ch * cap + 1
     w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
