@@ -19,9 +19,11 @@
 //  * The norm term sum_f w_f |k_f| uses v_mfma_f32_16x16x4_f32 on the fp32
 //    magnitudes (computed once per key band on the VALU, shared by all G
 //    heads).
-//  * Each lane loads 16 bytes of one key per step (4 lanes cover 64
-//    contiguous bytes of a row); the 4 waves of a work-group take
-//    interleaved blocks so the group streams one contiguous span of K.
+//  * K is read in whole 128-byte lines with non-temporal loads (eight lanes
+//    per line, each line read once) and transposed to the MFMA layout
+//    through a small per-wave LDS tile; the MFMA layout read directly would
+//    touch every line from two instructions.  The 4 waves of a work-group
+//    take interleaved blocks so the group streams one contiguous span of K.
 //  * Work is cut into "tickets": one chunk of `ch` keys of one unit, with ch
 //    chosen per call so that three work-groups fit in a CU's LDS.  The
 //    kernel is persistent: each work-group claims tickets in order from an
