@@ -147,6 +147,11 @@ size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs,
  *  head_stats optional out fp64 [units][G][2]: (mu_h, sigma_h); unit index
  *             = (s*L + l)*Hkv + g.
  *  workspace  device scratch of at least tri_workspace_bytes().
+ *
+ *  Work-groups of the fused kernel wait for each other's per-chunk
+ *  statistics.  The wait provably ends, and it is also bounded: should the
+ *  bound ever be reached, the affected unit's scores and statistics come out
+ *  NaN rather than the kernel hanging.
  */
 tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      const int64_t* cu_len, const int32_t* cur_pos,
