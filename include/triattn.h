@@ -150,8 +150,8 @@ size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs,
  *
  *  Work-groups of the fused kernel wait for each other's per-chunk
  *  statistics.  The wait provably ends, and it is also bounded: should the
- *  bound ever be reached, the affected unit's scores and statistics come out
- *  NaN rather than the kernel hanging.
+ *  bound ever be reached, the kernel does not hang; the affected chunk's
+ *  head_stats mean comes out NaN (sigma 0) and its scores -inf.
  */
 tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      const int64_t* cu_len, const int32_t* cur_pos,
