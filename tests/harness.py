@@ -250,3 +250,28 @@ def check_kept_near_threshold(case: Case, res, units, factored=True):
         diff = set(O.select_topb(ref, b).tolist()) ^ set(kept[ostart:ostart + b].tolist())
         bad = sorted(i for i in diff if abs(ref[i] - thr) > 1e-4 * max(1.0, abs(thr)))
         assert not bad, f"unit {(s, l, g)}: keys {bad[:10]} differ away from the threshold {thr}"
+
+
+def gpu_score_paged(case: Case, pool, offsets=None, reduce="mean", raw=False, stats=False):
+    """tri_score_paged on a case whose K sits in `pool` (synth.paged_from_case)."""
+    import rope_aware_key_amd as R
+    dev = case.k.device
+    sh = shape_of(case)
+    cu = pinned(case.cu_len, np.int64)
+    cp = pinned(case.cur_pos, np.int32)
+    off = None if offsets is None else pinned(offsets, np.float64)
+    wsb = R.tri_workspace_bytes_paged(sh, cu, pool.page_size, 0 if offsets is None else len(off),
+                                      reduce)
+    assert wsb > 0, R.last_error()
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    rows, G = case.total_rows(), case.shape.group
+    scores = torch.full((max(rows, 1),), float("nan"), dtype=torch.float32, device=dev)
+    raw_t = torch.full((max(rows, 1), G), float("nan"), device=dev) if raw else None
+    hs = torch.full((case.num_units, G, 2), float("nan"), dtype=torch.float64,
+                    device=dev) if stats else None
+    pages = R.make_pages(pool.table, pool.page_size, pool.num_pages, *pool.strides())
+    R.tri_score_paged(sh, cu, cp, pages, pool.k, case.q_centre, case.q_absmean, case.q_R, scores,
+                      offsets=off, reduce=reduce, raw_scores=raw_t, head_stats=hs, workspace=ws)
+    torch.cuda.synchronize()
+    return dict(scores=scores[:rows], raw=None if raw_t is None else raw_t[:rows], head_stats=hs)
+

@@ -14,8 +14,8 @@ import torch
 
 import oracle as O
 import synth
-from harness import (check_scores, gpu_run, gpu_score_offsets, half_split, oracle_unit, pinned,
-                     shape_of, units_of)
+from harness import (check_scores, gpu_run, gpu_score_offsets, gpu_score_paged, half_split,
+                     oracle_unit, pinned, shape_of, units_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,24 +23,7 @@ DEV = "cuda"
 
 
 def _paged_score(case, pool, offsets=None, reduce="mean", raw=False, stats=False):
-    import rope_aware_key_amd as R
-    sh = shape_of(case)
-    cu = pinned(case.cu_len, np.int64)
-    cp = pinned(case.cur_pos, np.int32)
-    off = None if offsets is None else pinned(offsets, np.float64)
-    wsb = R.tri_workspace_bytes_paged(sh, cu, pool.page_size,
-                                      0 if offsets is None else len(off), reduce)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
-    rows, G = case.total_rows(), case.shape.group
-    scores = torch.full((max(rows, 1),), float("nan"), dtype=torch.float32, device=DEV)
-    raw_t = torch.full((max(rows, 1), G), float("nan"), device=DEV) if raw else None
-    hs = torch.full((case.num_units, G, 2), float("nan"), dtype=torch.float64,
-                    device=DEV) if stats else None
-    pages = R.make_pages(pool.table, pool.page_size, pool.num_pages, *pool.strides())
-    R.tri_score_paged(sh, cu, cp, pages, pool.k, case.q_centre, case.q_absmean, case.q_R, scores,
-                      offsets=off, reduce=reduce, raw_scores=raw_t, head_stats=hs, workspace=ws)
-    torch.cuda.synchronize()
-    return dict(scores=scores[:rows], raw=None if raw_t is None else raw_t[:rows], head_stats=hs)
+    return gpu_score_paged(case, pool, offsets, reduce, raw, stats)
 
 
 def _paged_select(case, scores, pool, out_page_size, head_major_out=False):

@@ -1,0 +1,81 @@
+"""Seeded random sweep of the whole path against the oracle.
+
+Each case draws a head_dim (any multiple of 8 up to 256), a GQA group (1 to
+16), a small ragged batch, the RoPE layout, the offset set and its
+reduction, and whether K sits in a paged pool (page size and order drawn
+too).  Bars as elsewhere: scores within 1e-4 * max(1, |ref|) (floored at
+the fp32 resolution of the raw scores), raw scores and per-head statistics
+against the oracle, selection bit-exact on the GPU's own scores, compacted
+rows byte-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from harness import (check_raw, check_scores, check_selection_exact, gpu_run, gpu_score_offsets,
+                     gpu_score_paged, half_split, oracle_unit, units_of, z_floor)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def draw(seed):
+    g = np.random.default_rng([91, seed])
+    # half the cases on the MFMA kernels' head dims (multiples of 32)
+    d = int(g.integers(1, 9)) * 32 if g.random() < 0.5 else int(g.integers(1, 33)) * 8
+    G = int(g.integers(1, 17))
+    Hkv = int(g.integers(1, 4))
+    L = int(g.integers(1, 3))
+    S = int(g.integers(1, 5))
+    lens = [int(x) for x in g.integers(0, 2500, size=S)]
+    budgets = [int(x) for x in g.integers(0, 2600, size=S)]
+    half = bool(g.integers(0, 2))
+    reduce = "max" if (d % 32 == 0 and (not half or d % 64 == 0) and g.random() < 0.4) else "mean"
+    offsets = None
+    if reduce == "max" or g.random() < 0.3:
+        n_off = int(g.integers(1, 18))
+        offsets = sorted(float(x) for x in g.choice(70000, size=n_off, replace=False))
+    paged = bool(g.integers(0, 2))
+    page = int(2 ** g.integers(0, 9)) if paged else None
+    head_major = bool(g.integers(0, 2))
+    return dict(d=d, G=G, Hkv=Hkv, L=L, lens=lens, budgets=budgets, half=half, reduce=reduce,
+                offsets=offsets, page=page, head_major=head_major)
+
+
+@pytest.mark.parametrize("seed", range(128))
+def test_random_case(seed):
+    c = draw(seed)
+    print(f"random case {seed}: {c}", flush=True)
+    shape = synth.Shape(c["d"], c["G"] * c["Hkv"], c["Hkv"], c["L"])
+    case = synth.build_case("random", shape, c["lens"], c["budgets"], device=DEV, seed=seed)
+    if c["half"]:
+        case = half_split(case)
+    if c["page"] is not None:
+        pool = synth.paged_from_case(case, c["page"], head_major=c["head_major"], seed=seed)
+        res = gpu_score_paged(case, pool, c["offsets"], c["reduce"], raw=True, stats=True)
+    elif c["offsets"] is not None:
+        res = gpu_score_offsets(case, c["offsets"], c["reduce"], raw=True, stats=True)
+    else:
+        res = gpu_run(case, raw=True, stats=True, compact=False)
+    scores = res["scores"].cpu().numpy()
+    raw = res["raw"].cpu().numpy()
+    hs = res["head_stats"].cpu().numpy()
+    L, H = c["L"], c["Hkv"]
+    for (s, l, g) in units_of(case):
+        if case.seq_len(s) == 0:
+            continue
+        start, n, ref, S, mu, sigma = oracle_unit(case, s, l, g, factored=True,
+                                                  offsets=c["offsets"], reduce=c["reduce"])
+        what = f"case {seed} unit {(s, l, g)}"
+        check_scores(scores[start:start + n], ref, what, z_floor(S, sigma))
+        check_raw(raw[start:start + n], S, sigma, "raw " + what)
+        u = (s * L + l) * H + g
+        top = max(np.max(sigma), np.max(np.abs(S)))
+        np.testing.assert_allclose(hs[u, :, 0], mu, rtol=0, atol=1e-5 * top, err_msg=what)
+        np.testing.assert_allclose(hs[u, :, 1], sigma, rtol=1e-5, atol=1e-5 * np.max(np.abs(S)),
+                                   err_msg=what)
+    sel = gpu_run(case, scores_in=res["scores"])
+    check_selection_exact(case, sel)
