@@ -185,3 +185,24 @@ def test_decode_loop_decode_window_shape():
     shape = synth.Shape(128, 32, 8, 2)
     _run(shape, [3200, 3100], 256, B=3072, interval=128, sink=4, recent=64, seed=2,
          check_every=128)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_loop_random(seed):
+    """Seeded random decode runs: head_dim, group, layers, prompt lengths,
+    budget, interval, protection and RoPE layout drawn per case; caches
+    checked against the oracle after every append."""
+    g = np.random.default_rng([92, seed])
+    d = int(g.integers(1, 9)) * 32 if g.random() < 0.5 else int(g.integers(1, 33)) * 8
+    G, Hkv, L = int(g.integers(1, 9)), int(g.integers(1, 3)), int(g.integers(1, 3))
+    B = int(g.integers(4, 48))
+    interval = int(g.integers(1, 12))
+    sink = int(g.integers(0, 4))
+    recent = int(g.integers(0, max(1, B - sink - 1)))
+    n_pre = [int(x) for x in g.integers(0, B + interval + 10, size=int(g.integers(1, 4)))]
+    layout = "half" if g.random() < 0.5 else "interleaved"
+    print(f"decode case {seed}: d={d} G={G} Hkv={Hkv} L={L} B={B} interval={interval} "
+          f"sink={sink} recent={recent} prompts={n_pre} {layout}", flush=True)
+    shape = synth.Shape(d, G * Hkv, Hkv, L)
+    _run(shape, n_pre, int(g.integers(5, 25)), B=B, interval=interval, sink=sink, recent=recent,
+         seed=seed, layout=layout)
