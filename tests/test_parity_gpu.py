@@ -306,3 +306,35 @@ def test_many_tiny_sequences_max_offsets():
         start, n, ref, S, _, sigma = oracle_unit(case, s, l, gg, factored=True, offsets=offs,
                                                  reduce="max")
         check_scores(sc[start:start + n], ref, f"tiny max unit {(s, l, gg)}", z_floor(S, sigma))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_calibrate_random(seed):
+    """Seeded random calibration shapes: any head_dim multiple of 8, query
+    heads, layers, sample counts (ragged against the 256-sample chunks),
+    post-RoPE or pre-RoPE samples, either RoPE layout."""
+    import rope_aware_key_amd as R
+    g = np.random.default_rng([94, seed])
+    d = int(g.integers(1, 33)) * 8
+    Hq, L, N = int(g.integers(1, 12)), int(g.integers(1, 3)), int(g.integers(1, 1300))
+    layout = "half" if g.random() < 0.5 else "interleaved"
+    post = g.random() < 0.7
+    torch.manual_seed(seed)
+    q = (torch.randn(L, N, Hq, d, device=DEV) * 0.7 + 0.5).to(torch.bfloat16).view(torch.int16)
+    q_pos = torch.as_tensor(g.integers(0, 40000, size=N), dtype=torch.int32, device=DEV) if post else None
+    sh = R.make_shape(d, Hq, 1, L, rope_layout=layout)
+    c = torch.empty(L, Hq, d // 2, 2, device=DEV)
+    a = torch.empty(L, Hq, d // 2, device=DEV)
+    r = torch.empty(L, Hq, d // 2, device=DEV)
+    R.tri_calibrate(sh, q, q_pos, N, c, a, r)
+    torch.cuda.synchronize()
+    qq = O.bf16_bits_to_f64(q.cpu().numpy().view(np.uint16))
+    om = O.rope_omega(d, 1e4)
+    qp = None if q_pos is None else q_pos.cpu().numpy()
+    for l in range(L):
+        centre, absmean, Rr = O.calibrate(qq[l], qp, om, layout=layout)
+        np.testing.assert_allclose(c[l, ..., 0].cpu().numpy(), centre.real, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(c[l, ..., 1].cpu().numpy(), centre.imag, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(a[l].cpu().numpy(), absmean, rtol=1e-5)
+        np.testing.assert_allclose(r[l].cpu().numpy(), Rr, rtol=1e-5, atol=1e-6)
+
