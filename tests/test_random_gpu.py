@@ -79,3 +79,65 @@ def test_random_case(seed):
                                    err_msg=what)
     sel = gpu_run(case, scores_in=res["scores"])
     check_selection_exact(case, sel)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_select_variants(seed):
+    """Per-layer budgets (tri_select_compact_layers) and paged compaction
+    (tri_select_compact_paged, another page size and order for the output)
+    on random batches, against the oracle's selection on the GPU's scores."""
+    import rope_aware_key_amd as R
+    from harness import pinned, shape_of
+    g = np.random.default_rng([95, seed])
+    d = int(g.integers(1, 33)) * 8
+    G, Hkv, L = int(g.integers(1, 9)), int(g.integers(1, 4)), int(g.integers(1, 4))
+    S = int(g.integers(1, 5))
+    lens = [int(x) for x in g.integers(0, 3000, size=S)]
+    budgets = [int(x) for x in g.integers(0, 3100, size=S)]
+    shape = synth.Shape(d, G * Hkv, Hkv, L)
+    case = synth.build_case("random_sel", shape, lens, budgets, device=DEV, seed=seed)
+    scores = gpu_run(case, raw=False, stats=False, compact=False)["scores"]
+    sc = scores.cpu().numpy()
+    sh = shape_of(case)
+    cu = pinned(case.cu_len, np.int64)
+    # per-layer budgets
+    lb = g.integers(0, 3100, size=(S, L)).astype(np.int32)
+    out_rows = int(sum(Hkv * min(int(lb[s, l]), case.seq_len(s)) for s in range(S) for l in range(L)))
+    kept = torch.full((max(out_rows, 1),), -1, dtype=torch.int32, device=DEV)
+    ko = torch.zeros((max(out_rows, 1), d), dtype=torch.int16, device=DEV)
+    ws = torch.empty(max(R.tri_workspace_bytes_layers(sh, cu), 1), dtype=torch.uint8, device=DEV)
+    R.tri_select_compact_layers(sh, cu, pinned(lb.reshape(-1), np.int32), scores, case.k, None,
+                                None, kept, ko, None, None, workspace=ws)
+    torch.cuda.synchronize()
+    kp, kop, kin = kept.cpu().numpy(), ko.cpu().numpy(), case.k.cpu().numpy()
+    for (s, l, gg) in units_of(case):
+        start, n = case.unit_rows(s, l, gg)
+        ostart, b = O.out_rows_layers(case.cu_len, lb, L, Hkv, s, l, gg)
+        ref = O.select_topb(sc[start:start + n], int(lb[s, l]))
+        np.testing.assert_array_equal(kp[ostart:ostart + b], ref, err_msg=f"layers {(s, l, gg)}")
+        assert np.array_equal(kop[ostart:ostart + b], kin[start:start + n][ref])
+    # paged in, paged out
+    P_in, P_out = int(2 ** g.integers(0, 9)), int(2 ** g.integers(0, 9))
+    pool = synth.paged_from_case(case, P_in, head_major=bool(g.integers(0, 2)), seed=seed)
+    need = [(case.kept(s) + P_out - 1) // P_out for s in range(S)]
+    out = synth.empty_pool(S, L, Hkv, d, P_out, need, bool(g.integers(0, 2)), spare=1,
+                           seed=seed + 1, device=DEV)
+    kept2 = torch.full((max(case.total_out_rows(), 1),), -1, dtype=torch.int32, device=DEV)
+    ws2 = torch.empty(max(R.tri_workspace_bytes(sh, cu), 1), dtype=torch.uint8, device=DEV)
+    pin = R.make_pages(pool.table, P_in, pool.num_pages, *pool.strides())
+    pout = R.make_pages(out.table, P_out, out.num_pages, *out.strides())
+    R.tri_select_compact_paged(sh, cu, pinned(case.budget, np.int32), scores, pin, pool.k, pool.v,
+                               pool.pos, kept2, pout, out.k, out.v, out.pos, workspace=ws2)
+    torch.cuda.synchronize()
+    k2 = kept2.cpu().numpy()
+    for (s, l, gg) in units_of(case):
+        start, n = case.unit_rows(s, l, gg)
+        ostart, b = case.unit_out_rows(s, l, gg)
+        ref = O.select_topb(sc[start:start + n], int(case.budget[s]))
+        np.testing.assert_array_equal(k2[ostart:ostart + b], ref, err_msg=f"paged {(s, l, gg)}")
+        if b:
+            rows = torch.as_tensor(out.unit_rows(s, l, gg, b), device=DEV)
+            src = case.k[start:start + n].cpu().numpy()[ref]
+            assert np.array_equal(out.k[rows].cpu().numpy(), src), f"paged K {(s, l, gg)}"
+            srcp = case.k_pos[start:start + n].cpu().numpy()[ref]
+            assert np.array_equal(out.pos[rows].cpu().numpy(), srcp), f"paged pos {(s, l, gg)}"
