@@ -51,10 +51,9 @@ __device__ __forceinline__ uint4 pack8_d(const uint32_t (&v)[8]) {
 // Grid: (L*Hq) x ceil(n_q / 64) work-groups of 4 waves; wave w takes query
 // tile 4*blockIdx.y + w (16 queries).  partial[(lh*tiles + tile)*5 + k]:
 // the tile's sums (x, y, xx, yy, xy).
-template <int STEPS>
+template <int STEPS, bool HALF>
 __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
-    int Hq, int Hkv, int64_t n_q, int64_t n_k, double theta, bool half,
-    const uint16_t* __restrict__ q,
+    int Hq, int Hkv, int64_t n_q, int64_t n_k, double theta, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ k_pos, const float* __restrict__ q_centre,
     double* __restrict__ partial) {
@@ -76,26 +75,74 @@ __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
   const uint4* qrow = reinterpret_cast<const uint4*>(q + (((int64_t)l * n_q + j) * Hq + h) * D);
   const double pj = (double)q_pos[j];
   uint4 ay[STEPS], axh[STEPS], axm[STEPS], axl[STEPS];
+  const float* cbase = q_centre + ((int64_t)l * Hq + h) * F * 2;
+  // rotated centre of band f at the query's position:
+  // E[q_f] exp(i omega_f p_j), omega_f = theta^(-2f/d)
+  auto rotated = [&](int f, double& re, double& im) {
+    const double omega = pow(theta, -2.0 * (double)f / (double)D);
+    double sn, cs;
+    sincos(omega * pj, &sn, &cs);
+    const double cr = (double)cbase[2 * f], ci = (double)cbase[2 * f + 1];
+    re = cr * cs - ci * sn;
+    im = cr * sn + ci * cs;
+  };
 #pragma unroll
-  for (int st = 0; st < STEPS; ++st) {
-    ay[st] = qrow[4 * st + qd];
-    uint32_t h3[8], m3[8], l3[8];
-    // element j of the lane's eight: the real or imaginary part (by the
-    // RoPE layout) of its band's rotated centre
+  for (int st = 0; st < STEPS; ++st) ay[st] = qrow[4 * st + qd];
+  if constexpr (!HALF) {
+    // interleaved pairs: the lane's eight elements of a step are bands
+    // 16st + 4qd + u, real part then imaginary part
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = 32 * st + 8 * qd + j;
-      const int f = elem_band(e, D, half);
-      const float* c = q_centre + (((int64_t)l * Hq + h) * F + f) * 2;
-      const double omega = pow(theta, -2.0 * (double)f / (double)D);
-      double sn, cs;
-      sincos(omega * pj, &sn, &cs);
-      const double cr = (double)c[0], ci = (double)c[1];
-      split3_d(elem_part(e, D, half) ? cr * sn + ci * cs : cr * cs - ci * sn, h3[j], m3[j], l3[j]);
+    for (int st = 0; st < STEPS; ++st) {
+      uint32_t h3[8], m3[8], l3[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        double re, im;
+        rotated(16 * st + 4 * qd + u, re, im);
+        split3_d(re, h3[2 * u], m3[2 * u], l3[2 * u]);
+        split3_d(im, h3[2 * u + 1], m3[2 * u + 1], l3[2 * u + 1]);
+      }
+      axh[st] = pack8_d(h3);
+      axm[st] = pack8_d(m3);
+      axl[st] = pack8_d(l3);
     }
-    axh[st] = pack8_d(h3);
-    axm[st] = pack8_d(m3);
-    axl[st] = pack8_d(l3);
+  } else if constexpr (STEPS % 2 == 0) {
+    // half-split pairs, d a multiple of 64: element e < d/2 is the real part
+    // of band e and element e + d/2, in step st + STEPS/2 of the same lane,
+    // its imaginary part
+#pragma unroll
+    for (int st = 0; st < STEPS / 2; ++st) {
+      uint32_t h3[8], m3[8], l3[8], h4[8], m4[8], l4[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double re, im;
+        rotated(32 * st + 8 * qd + j, re, im);
+        split3_d(re, h3[j], m3[j], l3[j]);
+        split3_d(im, h4[j], m4[j], l4[j]);
+      }
+      axh[st] = pack8_d(h3);
+      axm[st] = pack8_d(m3);
+      axl[st] = pack8_d(l3);
+      axh[st + STEPS / 2] = pack8_d(h4);
+      axm[st + STEPS / 2] = pack8_d(m4);
+      axl[st + STEPS / 2] = pack8_d(l4);
+    }
+  } else {
+    // half-split pairs with an odd number of 32-wide steps: a step straddles
+    // d/2, so each element takes its own band and part
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      uint32_t h3[8], m3[8], l3[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 32 * st + 8 * qd + j;
+        double re, im;
+        rotated(elem_band(e, D, true), re, im);
+        split3_d(elem_part(e, D, true) ? im : re, h3[j], m3[j], l3[j]);
+      }
+      axh[st] = pack8_d(h3);
+      axm[st] = pack8_d(m3);
+      axl[st] = pack8_d(l3);
+    }
   }
   (void)k_pos;  // the key position cancels: keys are stored rotated
 
@@ -181,8 +228,12 @@ hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t 
   switch (d / 32) {
 #define TRI_CASE(n)                                                                         \
   case n:                                                                                   \
-    hipLaunchKernelGGL(trig_corr_kernel<n>, grid, dim3(64 * kDiagWaves), 0, st, Hq, Hkv,   \
-                       n_q, n_k, theta, half, q, q_pos, k, k_pos, q_centre, partial);      \
+    if (half)                                                                               \
+      hipLaunchKernelGGL((trig_corr_kernel<n, true>), grid, dim3(64 * kDiagWaves), 0, st,   \
+                         Hq, Hkv, n_q, n_k, theta, q, q_pos, k, k_pos, q_centre, partial);  \
+    else                                                                                    \
+      hipLaunchKernelGGL((trig_corr_kernel<n, false>), grid, dim3(64 * kDiagWaves), 0, st,  \
+                         Hq, Hkv, n_q, n_k, theta, q, q_pos, k, k_pos, q_centre, partial);  \
     break;
     TRI_CASE(1) TRI_CASE(2) TRI_CASE(3) TRI_CASE(4) TRI_CASE(5) TRI_CASE(6) TRI_CASE(7)
     TRI_CASE(8)
