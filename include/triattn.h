@@ -91,7 +91,8 @@ typedef struct {
  * and the hyper.ai summary, section "方法"; calibration runs once on a small
  * batch (blog review, step 1).
  *
- *  q         [L][n_samples][H_q][d] bf16 sample queries.  If q_pos != NULL
+ *  q         [L][n_samples][H_q][d] bf16 sample queries, 16-byte aligned
+ *            (device).  If q_pos != NULL
  *            they are post-RoPE at positions q_pos[n_samples] (int32,
  *            device) and are de-rotated first; if q_pos == NULL they are
  *            taken as pre-RoPE.

@@ -377,7 +377,7 @@ tri_status tri_calibrate(const tri_shape* shape, const uint16_t* q, const int32_
   if (n_samples < 1) return fail(TRI_ERR_INVALID_ARGUMENT, "n_samples must be >= 1");
   if (!q || !q_centre || !q_absmean || !q_R)
     return fail(TRI_ERR_INVALID_ARGUMENT, "q and every output must be non-NULL");
-  if (((uintptr_t)q & 3u) != 0) return fail(TRI_ERR_INVALID_ARGUMENT, "q must be 4-byte aligned");
+  if (!aligned16(q)) return fail(TRI_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
   const size_t need = tri::calibrate_workspace_bytes(shape->num_layers, shape->num_q_heads,
                                                      shape->head_dim, n_samples);
   if (!workspace || workspace_bytes < need)

@@ -24,14 +24,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //     and stored as fp32 (relative error ~6e-8): the de-rotation angle
 //     depends on the band and the sample only, so one sincos serves every
 //     layer and head;
-//  2. one work-group per (layer, chunk of kCalibChunk samples, 256 words of
-//     a sample row): each thread owns one word (head h, band f) and sums,
-//     over the chunk's samples in order, the de-rotated band (fp32
-//     rotation) and its magnitude (x^2 + y^2 of bf16 values is exact in
-//     fp32) into fp64 sums; a wave reads 256 contiguous bytes of each
-//     sample row;
+//  2. partial sums per (layer, chunk of kCalibChunk samples, band): the
+//     de-rotated band (fp32 rotation) and its magnitude (x^2 + y^2 of bf16
+//     values is exact in fp32), summed in fp64 over the chunk's samples in
+//     order;
 //  3. a merge per (layer, head, band) over the chunks in order.
 constexpr int kCalibChunk = 256;
+constexpr int kCalibWaves = 4;   // waves per work-group, one chunk each
+constexpr int kCalibBatch = 4;  // samples per register batch (two batches in flight)
 
 __global__ __launch_bounds__(256) void calib_phasor_kernel(int F, int d, double theta,
                                                            const int32_t* __restrict__ q_pos,
@@ -46,80 +46,118 @@ __global__ __launch_bounds__(256) void calib_phasor_kernel(int F, int d, double 
   ph[idx] = make_float2((float)cs, (float)-sn);  // exp(-i omega p)
 }
 
-// grid (chunks, L, ceil(W / 256)), W = Hq * F words per sample row
-__global__ __launch_bounds__(256) void calib_partial_kernel(
-    int W, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
-    const float2* __restrict__ ph, double* __restrict__ partial) {
-  const int c = blockIdx.x, l = blockIdx.y;
-  const int w = blockIdx.z * 256 + threadIdx.x;
-  if (w >= W) return;
-  const int f = w % F;
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(q) + (int64_t)l * N * W + w;
-  const int64_t t0 = (int64_t)c * kCalibChunk;
-  const int64_t t1 = min(N, t0 + kCalibChunk);
-  double sr = 0.0, si = 0.0, sa = 0.0;
-#pragma unroll 8
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t u = words[t * W];
-    const float x = bf16_lo(u), y = bf16_hi(u);
-    float re = x, im = y;
-    if (ph) {
-      const float2 p = ph[t * F + f];  // (x + i y) * exp(-i omega p)
-      re = fmaf(x, p.x, -y * p.y);
-      im = fmaf(x, p.y, y * p.x);
-    }
-    sr += (double)re;
-    si += (double)im;
-    sa += (double)__builtin_amdgcn_sqrtf(fmaf(x, x, y * y));  // |q_f|: unchanged by the rotation
-  }
-  double* out = partial + (((int64_t)l * chunks + c) * W + w) * 3;
-  out[0] = sr;
-  out[1] = si;
-  out[2] = sa;
-}
+namespace {
 
-// The same sums for the half-split layout (band f = (x_f, x_{f+d/2})):
-// thread w2 owns bands 2 fp and 2 fp + 1 of head h (w2 = h * F/2 + fp) and
-// reads one word of their real parts and one of their imaginary parts, so
-// a wave still reads contiguous words.  Grid (chunks, L, ceil(W/2 / 256)).
-__global__ __launch_bounds__(256) void calib_partial_half_kernel(
-    int W, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
+// Bands 4j .. 4j+3 of head h in one sample row of W words (one word is two
+// bf16 elements), as (x, y) pairs.  Interleaved: the four words
+// h*F + 4j .. +3, one band each.  Half split: words h*F + 2j, +1 hold the
+// real parts and words h*F + F/2 + 2j, +1 the imaginary parts.
+template <bool HALF>
+struct QuadLoad {
+  uint4 a;
+  __device__ __forceinline__ void load(const uint32_t* row, int h, int F, int j) {
+    if constexpr (!HALF) {
+      a = *reinterpret_cast<const uint4*>(row + h * F + 4 * j);
+    } else {
+      const uint2 re = *reinterpret_cast<const uint2*>(row + h * F + 2 * j);
+      const uint2 im = *reinterpret_cast<const uint2*>(row + h * F + (F >> 1) + 2 * j);
+      a = make_uint4(re.x, re.y, im.x, im.y);
+    }
+  }
+  __device__ __forceinline__ void band(int b, float& x, float& y) const {
+    if constexpr (!HALF) {
+      const uint32_t w = b == 0 ? a.x : b == 1 ? a.y : b == 2 ? a.z : a.w;
+      x = bf16_lo(w);
+      y = bf16_hi(w);
+    } else {
+      const uint32_t wr = b < 2 ? a.x : a.y, wi = b < 2 ? a.z : a.w;
+      x = (b & 1) ? bf16_hi(wr) : bf16_lo(wr);
+      y = (b & 1) ? bf16_hi(wi) : bf16_lo(wi);
+    }
+  }
+};
+
+}  // namespace
+
+// Grid (ceil(chunks / kCalibWaves), L, ceil(Hq*F/4 / 64)), 64 * kCalibWaves
+// threads.  Wave w takes chunk kCalibWaves*blockIdx.x + w; lane i takes band
+// quad blockIdx.z*64 + i (head h = quad / (F/4), bands 4j .. 4j+3 with
+// j = quad mod F/4), so a wave reads one contiguous stretch of each sample
+// row.  Loads are double-buffered: the queries and phasors of the next
+// kCalibBatch samples are in flight while the current ones are summed.
+// partial[((l*chunks + c)*W + h*F + f)*3 + {0,1,2}] = sums of Re, Im, |q_f|.
+template <bool HALF, bool ROTATE>
+__global__ __launch_bounds__(64 * kCalibWaves) void calib_partial_kernel(
+    int Hq, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
     const float2* __restrict__ ph, double* __restrict__ partial) {
-  const int c = blockIdx.x, l = blockIdx.y;
-  const int w2 = blockIdx.z * 256 + threadIdx.x;
-  const int hw = F >> 1;  // words per half row of a head
-  if (w2 >= W >> 1) return;
-  const int h = w2 / hw, fp = w2 % hw;
-  const int f0 = 2 * fp;
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(q) + (int64_t)l * N * W + h * F + fp;
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * kCalibWaves + (threadIdx.x >> 6);
+  const int l = blockIdx.y;
+  const int quads = F >> 2;
+  const int quad = blockIdx.z * 64 + lane;
+  if (c >= chunks || quad >= Hq * quads) return;
+  const int h = quad / quads, j = quad % quads;
+  const int64_t W = (int64_t)Hq * F;
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(q) + (int64_t)l * N * W;
   const int64_t t0 = (int64_t)c * kCalibChunk;
   const int64_t t1 = min(N, t0 + kCalibChunk);
-  double sr[2] = {0.0, 0.0}, si[2] = {0.0, 0.0}, sa[2] = {0.0, 0.0};
-#pragma unroll 4
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t ur = words[t * W], ui = words[t * W + hw];
-    const float xs[2] = {bf16_lo(ur), bf16_hi(ur)};
-    const float ys[2] = {bf16_lo(ui), bf16_hi(ui)};
+  double sr[4] = {0.0, 0.0, 0.0, 0.0}, si[4] = {0.0, 0.0, 0.0, 0.0}, sa[4] = {0.0, 0.0, 0.0, 0.0};
+  auto add = [&](const QuadLoad<HALF>& v, const float4* p) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const float x = xs[b], y = ys[b];
+    for (int b = 0; b < 4; ++b) {
+      float x, y;
+      v.band(b, x, y);
       float re = x, im = y;
-      if (ph) {
-        const float2 p = ph[t * F + f0 + b];
-        re = fmaf(x, p.x, -y * p.y);
-        im = fmaf(x, p.y, y * p.x);
+      if constexpr (ROTATE) {  // (x + i y) * exp(-i omega p)
+        const float4 pp = p[b >> 1];
+        const float px = (b & 1) ? pp.z : pp.x, py = (b & 1) ? pp.w : pp.y;
+        re = fmaf(x, px, -y * py);
+        im = fmaf(x, py, y * px);
       }
       sr[b] += (double)re;
       si[b] += (double)im;
-      sa[b] += (double)__builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
+      sa[b] += (double)__builtin_amdgcn_sqrtf(fmaf(x, x, y * y));  // |q_f|: unchanged by the rotation
     }
-  }
+  };
+  // two batches of NB samples in registers: the loads of batch i+1 are in
+  // flight while batch i is summed (sample indexes past the chunk are
+  // clamped to its last sample and their values dropped)
+  constexpr int NB = kCalibBatch;
+  struct Batch {
+    QuadLoad<HALF> v[NB];
+    float4 p[NB][2];
+  };
+  auto fetch = [&](Batch& bt, int64_t tb) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    double* out = partial + (((int64_t)l * chunks + c) * W + h * F + f0 + b) * 3;
-    out[0] = sr[b];
-    out[1] = si[b];
-    out[2] = sa[b];
+    for (int u = 0; u < NB; ++u) {
+      const int64_t tt = min(tb + u, t1 - 1);
+      bt.v[u].load(rows + tt * W, h, F, j);
+      if constexpr (ROTATE) {
+        const float4* pq = reinterpret_cast<const float4*>(ph + tt * F + 4 * j);
+        bt.p[u][0] = pq[0];
+        bt.p[u][1] = pq[1];
+      }
+    }
+  };
+  auto sum = [&](const Batch& bt, int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (tb + u < t1) add(bt.v[u], bt.p[u]);
+  };
+  Batch A, B;
+  fetch(A, t0);
+  for (int64_t t = t0; t < t1; t += 2 * NB) {
+    fetch(B, t + NB);
+    sum(A, t);
+    fetch(A, t + 2 * NB);
+    sum(B, t + NB);
+  }
+  double* out = partial + (((int64_t)l * chunks + c) * W + (int64_t)h * F + 4 * j) * 3;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    out[3 * b] = sr[b];
+    out[3 * b + 1] = si[b];
+    out[3 * b + 2] = sa[b];
   }
 }
 
@@ -166,12 +204,21 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (half)
-    hipLaunchKernelGGL(calib_partial_half_kernel, dim3(chunks, L, (W / 2 + 255) / 256), dim3(256),
-                       0, st, W, F, n_samples, chunks, q, ph, partial);
+  const dim3 grid((unsigned)((chunks + kCalibWaves - 1) / kCalibWaves), (unsigned)L,
+                  (unsigned)((Hq * (F / 4) + 63) / 64));
+  const dim3 block(64 * kCalibWaves);
+  if (half && ph)
+    hipLaunchKernelGGL((calib_partial_kernel<true, true>), grid, block, 0, st, Hq, F, n_samples,
+                       chunks, q, ph, partial);
+  else if (half)
+    hipLaunchKernelGGL((calib_partial_kernel<true, false>), grid, block, 0, st, Hq, F, n_samples,
+                       chunks, q, ph, partial);
+  else if (ph)
+    hipLaunchKernelGGL((calib_partial_kernel<false, true>), grid, block, 0, st, Hq, F, n_samples,
+                       chunks, q, ph, partial);
   else
-    hipLaunchKernelGGL(calib_partial_kernel, dim3(chunks, L, (W + 255) / 256), dim3(256), 0, st,
-                       W, F, n_samples, chunks, q, ph, partial);
+    hipLaunchKernelGGL((calib_partial_kernel<false, false>), grid, block, 0, st, Hq, F, n_samples,
+                       chunks, q, ph, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t m = (int64_t)L * W;

@@ -141,6 +141,7 @@ def test_calibrate_argument_checks():
     assert _status(cal, q=None) == ST["INVALID"]
     assert _status(cal, r=None) == ST["INVALID"]
     assert _status(cal, q=_Fake(FAKE + 2)) == ST["INVALID"]
+    assert _status(cal, q=_Fake(FAKE + 8)) == ST["INVALID"]
     assert _status(cal, ws=None, wsb=0) == ST["WORKSPACE"]
     assert _status(cal, wsb=need - 1) == ST["WORKSPACE"]
     assert _status(cal, ws=_Fake(FAKE + 8)) == ST["INVALID"]
