@@ -144,7 +144,7 @@ struct Plan {
   int64_t tickets = 0;
   // workspace offsets (bytes)
   size_t off_seq = 0, off_P = 0, off_W = 0, off_E = 0, off_stats = 0, off_ctrl = 0,
-         off_apack = 0, off_raw = 0, off_offsets = 0, off_ustats = 0;
+         off_apack = 0, off_raw = 0, off_offsets = 0, off_ustats = 0, off_split = 0;
   int64_t n_units = 0, n_stat_slots = 0;
   int chunk = 0;  // keys per score ticket
   bool fused = false;
@@ -273,7 +273,10 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.off_ustats = take(p.fused ? 0 : (size_t)p.n_units * p.G * 2 * sizeof(double));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));
   p.score_bytes = off;
-  p.select_bytes = after_seq;
+  // select scratch (split select of long units) reuses the score region:
+  // the two never run at the same time on one workspace
+  p.off_split = after_seq;
+  p.select_bytes = after_seq + tri::split_select_bytes(p.n_units, p.max_n);
   return TRI_OK;
 }
 
@@ -443,7 +446,8 @@ hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t
   hipError_t e = hipSuccess;
   if (upload_seqs) e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   const int LH = p.L * p.Hkv;
-  if (e == hipSuccess) e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, s);
+  if (e == hipSuccess)
+    e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, ws + p.off_split, s);
   if (e == hipSuccess && (k_out || v_out || pos_out))
     e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
                             pos_out, p.in_pg, p.out_pg, s);
@@ -857,7 +861,11 @@ size_t tri_workspace_bytes_layers(const tri_shape* shape, int32_t num_seqs,
     fail(TRI_ERR_UNSUPPORTED, "too many (sequence, layer) pairs in one call (max 8192)");
     return 0;
   }
-  return align_up((size_t)S2 * sizeof(SeqInfo), 256);
+  int64_t max_n = 0;
+  for (int s = 0; s < num_seqs; ++s) max_n = std::max(max_n, cu_len[s + 1] - cu_len[s]);
+  if (max_n > 0x7fffffff) return 0;
+  return align_up((size_t)S2 * sizeof(SeqInfo), 256) +
+         tri::split_select_bytes(S2 * shape->num_kv_heads, (int)max_n);
 }
 
 tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,

@@ -7,10 +7,11 @@
 // the lower index, -0.0 == +0.0, NaN ranks below -inf.
 //
 // Method: scores map to order-preserving 32-bit keys.  A most-significant-
-// digit radix select (4 passes of 8 bits, per-wave LDS histograms) finds the
-// b-th largest key T and how many keys equal to T are kept (the quota).  A
-// final ordered scan keeps every key > T and the first `quota` keys == T,
-// writing their indices by a block-wide ballot prefix sum.
+// digit radix select finds the b-th largest key T and how many keys equal
+// to T are kept (the quota).  A final ordered scan keeps every key > T and
+// the first `quota` keys == T, writing their indices through block-wide
+// prefix sums.  Units up to 35840 keys take one work-group (keys in
+// registers or LDS); longer ones are split over work-groups of 4096 keys.
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -20,112 +21,6 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN: below every number
   if (u == 0x80000000u) u = 0u;                      // -0 ranks as +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-
-__global__ __launch_bounds__(kSelThreads) void select_global_kernel(
-    const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
-    int32_t* __restrict__ kept) {
-  __shared__ uint32_t hist[kSelWaves][256];
-  __shared__ uint32_t sel[2];
-  __shared__ uint32_t wcnt_a[kSelWaves], wcnt_b[kSelWaves];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int unit = blockIdx.x;
-  const int s = unit / LH, lg = unit % LH;
-  const SeqInfo si = seqs[s];
-  const int n = si.n, b = si.b;
-  if (b <= 0) return;
-  const float* in = scores + si.row_base + (int64_t)lg * si.in_stride;
-  int32_t* out = kept + si.out_base + (int64_t)lg * si.out_stride;
-  if (b >= n) {
-    for (int i = tid; i < n; i += kSelThreads) out[i] = i;
-    return;
-  }
-
-  uint32_t prefix = 0u, mask = 0u;
-  uint32_t kk = (uint32_t)b;  // rank of the target within the keys matching prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint32_t key = order_key(in[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
-      uint32_t lane_tot = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t v = 0;
-        for (int w = 0; w < kSelWaves; ++w) v += hist[w][4 * lane + u];
-        c[u] = v;
-        lane_tot += v;
-      }
-      // inclusive suffix sum over lanes (bins above belong to higher lanes)
-      uint32_t suf = lane_tot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      uint32_t above = suf - lane_tot;
-#pragma unroll
-      for (int u = 3; u >= 0; --u) {
-        if (above < kk && kk <= above + c[u]) {
-          sel[0] = (uint32_t)(4 * lane + u);
-          sel[1] = above;
-        }
-        above += c[u];
-      }
-    }
-    __syncthreads();
-    const uint32_t digit = sel[0];
-    kk -= sel[1];
-    prefix |= digit << shift;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t quota = kk;  // keys equal to T that are kept (>= 1)
-
-  uint32_t base_out = 0, base_eq = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int tile = 0; tile < n && base_out < (uint32_t)b; tile += kSelThreads) {
-    const int i = tile + tid;
-    const uint32_t key = i < n ? order_key(in[i]) : 0u;
-    const bool gt = i < n && key > T;
-    const bool eq = i < n && key == T;
-    const uint64_t beq = __ballot(eq);
-    if (lane == 0) wcnt_a[wave] = (uint32_t)__popcll(beq);
-    __syncthreads();
-    uint32_t eq_before = base_eq + (uint32_t)__popcll(beq & lt_mask);
-    uint32_t eq_tile = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t v = wcnt_a[w];
-      if (w < wave) eq_before += v;
-      eq_tile += v;
-    }
-    const bool keep = gt || (eq && eq_before < quota);
-    const uint64_t bk = __ballot(keep);
-    if (lane == 0) wcnt_b[wave] = (uint32_t)__popcll(bk);
-    __syncthreads();
-    uint32_t pos = base_out + (uint32_t)__popcll(bk & lt_mask);
-    uint32_t keep_tile = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t v = wcnt_b[w];
-      if (w < wave) pos += v;
-      keep_tile += v;
-    }
-    if (keep && pos < (uint32_t)b) out[pos] = i;
-    base_out += keep_tile;
-    base_eq += eq_tile;
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -410,6 +305,267 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(
 // Longest unit whose keys the LDS-staged select holds (140 KB of keys next
 // to the 16 KB histogram).
 constexpr int kSelLdsMaxKeys = 35840;
+
+// ---------------------------------------------------------------------------
+// Split select for units longer than the LDS-staged select holds: the unit
+// is cut into tiles of kSplitTile keys, one work-group each, so that a few
+// long units still spread over the chip.  Digits are 8 bits wide (4
+// passes).  In each pass every tile stores its histogram of the keys that
+// match the digits found so far, and a one-work-group-per-unit pick kernel
+// adds the tiles' histograms and picks the digit.  Then a count pass
+// records per tile the keys above the threshold T and equal to it, and a
+// write pass places each tile's kept indices after those of the tiles
+// before it: ahead of tile t sit every key > T of tiles < t and
+// min(quota, keys == T in tiles < t).  Kernel boundaries order the steps;
+// there are no atomics and no fences (a device-wide fence writes back the
+// L2 on this chip, which cost more than the passes themselves).
+// ---------------------------------------------------------------------------
+constexpr int kSplitThreads = 256;
+constexpr int kSplitWaves = kSplitThreads / 64;
+constexpr int kSplitItems = 16;
+constexpr int kSplitTile = kSplitThreads * kSplitItems;  // 4096 keys
+
+// per unit: digits found (prefix, mask) and the rank still to place (kk)
+struct SplitState {
+  uint32_t prefix, mask, kk, pad;
+};
+
+struct SplitBuffers {
+  SplitState* state;  // [units]
+  uint32_t* hist;     // [units][tiles][256], the current pass
+  uint2* counts;      // [units][tiles]: (keys > T, keys == T)
+};
+
+static size_t split_up(int64_t x) { return (size_t)((x + 255) / 256 * 256); }
+
+static SplitBuffers split_buffers(void* ws, int64_t units, int64_t tiles) {
+  char* p = (char*)ws;
+  SplitBuffers sb;
+  sb.state = (SplitState*)p;
+  p += split_up(units * (int64_t)sizeof(SplitState));
+  sb.hist = (uint32_t*)p;
+  p += split_up(units * tiles * 256 * 4);
+  sb.counts = (uint2*)p;
+  return sb;
+}
+
+size_t split_select_bytes(int64_t units, int max_n) {
+  if (max_n <= kSelLdsMaxKeys || units <= 0) return 0;
+  const int64_t tiles = (max_n + kSplitTile - 1) / kSplitTile;
+  return split_up(units * (int64_t)sizeof(SplitState)) + split_up(units * tiles * 256 * 4) +
+         split_up(units * tiles * (int64_t)sizeof(uint2));
+}
+
+// Work-group's tile of one unit (grid units*tiles); false: nothing to do.
+struct SplitTile {
+  int unit, tile, n, b;
+  int64_t t0;
+  const float* in;
+  int32_t* out;
+};
+
+__device__ __forceinline__ SplitTile split_tile(const SeqInfo* seqs, int LH, int tiles,
+                                                const float* scores, int32_t* kept) {
+  SplitTile t;
+  t.unit = blockIdx.x / tiles;
+  t.tile = blockIdx.x % tiles;
+  const SeqInfo si = seqs[t.unit / LH];
+  const int lg = t.unit % LH;
+  t.n = si.n;
+  t.b = si.b;
+  t.t0 = (int64_t)t.tile * kSplitTile;
+  t.in = scores + si.row_base + (int64_t)lg * si.in_stride;
+  t.out = kept ? kept + si.out_base + (int64_t)lg * si.out_stride : nullptr;
+  return t;
+}
+
+// One radix pass (digit bits [24 - 8*pass, 32 - 8*pass)): the tile's
+// histogram of the keys that match the digits found so far.
+__global__ __launch_bounds__(kSplitThreads) void split_hist_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, int tiles, const float* __restrict__ scores,
+    int pass, SplitBuffers sb) {
+  __shared__ uint32_t h[kSplitWaves][256];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const SplitTile t = split_tile(seqs, LH, tiles, scores, nullptr);
+  if (t.b <= 0 || t.b >= t.n || t.t0 >= t.n) return;
+  uint32_t prefix = 0u, mask = 0u;
+  if (pass > 0) {
+    const SplitState st = sb.state[t.unit];
+    prefix = st.prefix;
+    mask = st.mask;
+  }
+  const int shift = 24 - 8 * pass;
+  for (int i = tid; i < kSplitWaves * 256; i += kSplitThreads) (&h[0][0])[i] = 0u;
+  __syncthreads();
+  float v[kSplitItems];  // all loads in flight before the first LDS atomic
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) {
+    const int64_t i = t.t0 + j * kSplitThreads + tid;
+    v[j] = t.in[i < t.n ? i : t.n - 1];
+  }
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) {
+    const uint32_t key = order_key(v[j]);
+    if (t.t0 + j * kSplitThreads + tid < t.n && (key & mask) == prefix)
+      atomicAdd(&h[wave][(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  uint32_t c = 0;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) c += h[w][tid];
+  sb.hist[((int64_t)t.unit * tiles + t.tile) * 256 + tid] = c;
+}
+
+// The digit of one pass per unit: the bin holding rank kk (from the top) of
+// the sum of the tiles' histograms.  Grid units, thread = bin.
+__global__ __launch_bounds__(kSplitThreads) void split_pick_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, int tiles, int pass, SplitBuffers sb) {
+  __shared__ uint32_t wsum[kSplitWaves];
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const SeqInfo si = seqs[unit / LH];
+  const int n = si.n, b = si.b;
+  if (b <= 0 || b >= n) return;
+  const int unit_tiles = (n + kSplitTile - 1) / kSplitTile;
+  SplitState st = {0u, 0u, (uint32_t)b, 0u};
+  if (pass > 0) st = sb.state[unit];
+  const uint32_t* hh = sb.hist + (int64_t)unit * tiles * 256 + tid;
+  uint32_t c = 0;
+#pragma unroll 8
+  for (int t = 0; t < unit_tiles; ++t) c += hh[(int64_t)t * 256];
+  uint32_t all = 0;
+  const uint32_t below = block_excl_scan<kSplitThreads>(c, wsum, &all);
+  const uint32_t above = all - below - c;  // keys in higher bins
+  const int shift = 24 - 8 * pass;
+  if (above < st.kk && st.kk <= above + c)
+    sb.state[unit] = SplitState{st.prefix | ((uint32_t)tid << shift), st.mask | (255u << shift),
+                                st.kk - above, 0u};
+}
+
+// Keys above the threshold and equal to it, per tile.
+__global__ __launch_bounds__(kSplitThreads) void split_count_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, int tiles, const float* __restrict__ scores,
+    SplitBuffers sb) {
+  __shared__ uint32_t wgt[kSplitWaves], weq[kSplitWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SplitTile t = split_tile(seqs, LH, tiles, scores, nullptr);
+  if (t.b <= 0 || t.b >= t.n || t.t0 >= t.n) return;
+  const uint32_t T = sb.state[t.unit].prefix;
+  float v[kSplitItems];
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) {
+    const int64_t i = t.t0 + j * kSplitThreads + tid;
+    v[j] = t.in[i < t.n ? i : t.n - 1];
+  }
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) {
+    const uint32_t key = order_key(v[j]);
+    const bool valid = t.t0 + j * kSplitThreads + tid < t.n;
+    gt += (valid && key > T) ? 1u : 0u;
+    eq += (valid && key == T) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += __shfl_xor(gt, o, 64);
+    eq += __shfl_xor(eq, o, 64);
+  }
+  if (lane == 0) {
+    wgt[wave] = gt;
+    weq[wave] = eq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint2 r = make_uint2(0u, 0u);
+    for (int w = 0; w < kSplitWaves; ++w) {
+      r.x += wgt[w];
+      r.y += weq[w];
+    }
+    sb.counts[(int64_t)t.unit * tiles + t.tile] = r;
+  }
+}
+
+// Kept indices of each tile in index order; thread i takes the tile's keys
+// [i*kSplitItems, (i+1)*kSplitItems).
+__global__ __launch_bounds__(kSplitThreads) void split_write_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, int tiles, const float* __restrict__ scores,
+    SplitBuffers sb, int32_t* __restrict__ kept) {
+  __shared__ uint32_t wsum[kSplitWaves];
+  __shared__ uint32_t wa[kSplitWaves], wb[kSplitWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SplitTile t = split_tile(seqs, LH, tiles, scores, kept);
+  const int n = t.n, b = t.b;
+  if (b <= 0 || t.t0 >= n) return;
+  const int i0 = (int)t.t0 + tid * kSplitItems;
+  if (b >= n) {
+#pragma unroll
+    for (int j = 0; j < kSplitItems; ++j)
+      if (i0 + j < n) t.out[i0 + j] = i0 + j;
+    return;
+  }
+  const SplitState st = sb.state[t.unit];
+  const uint32_t T = st.prefix, quota = st.kk;
+  // keys > T and == T in the tiles before this one
+  uint32_t gt_before = 0, eq_before_tiles = 0;
+  for (int p = tid; p < t.tile; p += kSplitThreads) {
+    const uint2 c = sb.counts[(int64_t)t.unit * tiles + p];
+    gt_before += c.x;
+    eq_before_tiles += c.y;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt_before += __shfl_xor(gt_before, o, 64);
+    eq_before_tiles += __shfl_xor(eq_before_tiles, o, 64);
+  }
+  if (lane == 0) {
+    wa[wave] = gt_before;
+    wb[wave] = eq_before_tiles;
+  }
+  __syncthreads();
+  gt_before = 0;
+  eq_before_tiles = 0;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) {
+    gt_before += wa[w];
+    eq_before_tiles += wb[w];
+  }
+  uint32_t key[kSplitItems];
+  const int mine = max(0, min(kSplitItems, n - i0));
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) key[j] = order_key(t.in[min(i0 + j, n - 1)]);
+  uint32_t neq = 0;
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) neq += (j < mine && key[j] == T) ? 1u : 0u;
+  uint32_t eq_tile = 0;
+  const uint32_t eq_before =
+      eq_before_tiles + block_excl_scan<kSplitThreads>(neq, wsum, &eq_tile);
+  uint32_t nkeep = 0;
+  {
+    uint32_t e = eq_before;
+#pragma unroll
+    for (int j = 0; j < kSplitItems; ++j) {
+      const bool valid = j < mine;
+      const bool eq = valid && key[j] == T;
+      nkeep += ((valid && key[j] > T) || (eq && e < quota)) ? 1u : 0u;
+      e += eq ? 1u : 0u;
+    }
+  }
+  uint32_t keep_tile = 0;
+  uint32_t pos = gt_before + min(quota, eq_before_tiles) +
+                 block_excl_scan<kSplitThreads>(nkeep, wsum, &keep_tile);
+  uint32_t e = eq_before;
+#pragma unroll
+  for (int j = 0; j < kSplitItems; ++j) {
+    const bool valid = j < mine;
+    const bool eq = valid && key[j] == T;
+    if ((valid && key[j] > T) || (eq && e < quota)) {
+      if (pos < (uint32_t)b) t.out[pos] = i0 + j;
+      ++pos;
+    }
+    e += eq ? 1u : 0u;
+  }
+}
+
 constexpr int kSelSmallUnit = 4096;  // up to here 256 threads per unit
 
 template <int NT>
@@ -426,7 +582,7 @@ static hipError_t launch_select_lds(int64_t units, int max_n, hipStream_t st, co
 }
 
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
-                         int32_t* kept_idx, hipStream_t st) {
+                         int32_t* kept_idx, void* split_ws, hipStream_t st) {
   const int64_t units = (int64_t)S * LH;
   if (units == 0) return hipSuccess;
   if (max_n <= kSelSmallUnit)
@@ -443,8 +599,26 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
   }
   if (max_n <= kSelLdsMaxKeys)
     return launch_select_lds<1024>(units, max_n, st, seqs, LH, scores, kept_idx);
-  hipLaunchKernelGGL(select_global_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, st, seqs,
-                     LH, scores, kept_idx);
+  if (!split_ws) return hipErrorInvalidValue;
+  const int tiles = (max_n + kSplitTile - 1) / kSplitTile;
+  if (units * tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const SplitBuffers sb = split_buffers(split_ws, units, tiles);
+  const dim3 grid((unsigned)(units * tiles)), block(kSplitThreads);
+  hipError_t e = hipSuccess;
+  for (int pass = 0; pass < 4 && e == hipSuccess; ++pass) {
+    hipLaunchKernelGGL(split_hist_kernel, grid, block, 0, st, seqs, LH, tiles, scores, pass, sb);
+    e = hipGetLastError();
+    if (e != hipSuccess) break;
+    hipLaunchKernelGGL(split_pick_kernel, dim3((unsigned)units), block, 0, st, seqs, LH, tiles,
+                       pass, sb);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_count_kernel, grid, block, 0, st, seqs, LH, tiles, scores, sb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_write_kernel, grid, block, 0, st, seqs, LH, tiles, scores, sb,
+                     kept_idx);
   return hipGetLastError();
 }
 

@@ -235,8 +235,11 @@ hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t 
                             const int32_t* k_pos, const float* q_centre, double* partial,
                             double* r, hipStream_t st);
 
+// split_ws: split_select_bytes(units, max_n) bytes of device scratch (only
+// read when max_n is above what one work-group's select holds)
+size_t split_select_bytes(int64_t units, int max_n);
 hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const float* scores,
-                         int32_t* kept_idx, hipStream_t st);
+                         int32_t* kept_idx, void* split_ws, hipStream_t st);
 
 hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           const int32_t* kept_idx, const uint16_t* k, const uint16_t* v,

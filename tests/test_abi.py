@@ -147,6 +147,16 @@ def test_calibrate_argument_checks():
     assert _status(cal, ws=_Fake(FAKE + 8)) == ST["INVALID"]
 
 
+def test_split_select_workspace():
+    """Units past 35840 keys take the split select, whose per-tile histograms
+    (1 KB per 4096-key tile) and counts are part of the workspace."""
+    sh = R.make_shape(64, 2, 2, 3)
+    a = R.tri_workspace_bytes_layers(sh, [0, 35840])
+    b = R.tri_workspace_bytes_layers(sh, [0, 35841])
+    units, tiles = 3 * 2, 9
+    assert b - a >= units * tiles * (1024 + 8)
+
+
 def test_workspace_grows_with_batch():
     sh = R.make_shape(128, 28, 4, 28)
     small = R.tri_workspace_bytes(sh, [0, 1024])

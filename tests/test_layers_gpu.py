@@ -125,6 +125,21 @@ def test_scores_only_selection():
     _check(case, scores, budgets, _run_layers(case, scores, budgets, with_rows=False))
 
 
+def test_long_units_split_select():
+    """Units past 35840 keys (split select over 4096-key tiles) with
+    per-layer budgets: a short sequence in the same batch, budgets of 0, 1,
+    n - 1 and above n, ties on a few score values across every tile."""
+    shape = synth.Shape(64, 4, 2, 3)
+    lens = [41000, 900, 70000]
+    case = synth.build_case("layers_long", shape, lens, [1] * len(lens), device=DEV, seed=9)
+    g = np.random.default_rng(9)
+    sc = (g.integers(-4, 5, size=case.total_rows()) * 0.25).astype(np.float32)
+    scores = torch.as_tensor(sc, device=DEV)
+    budgets = np.array([[0, 40999, 50000], [1, 899, 4096], [1, 69999, 12345]], np.int32)
+    _check(case, scores, budgets, _run_layers(case, scores, budgets),
+           rows_units=[(0, 1, 0), (2, 2, 1), (1, 1, 1)])
+
+
 def test_long_reasoning_pyramid_full_size():
     """8 x 32768 keys, 28 layers, pyramid mean 2048 ratio 3: every unit's
     kept set checked; rows checked on sampled units."""

@@ -190,6 +190,43 @@ def test_select_many_ties(n, B):
     check_selection_exact(case, res)
 
 
+def test_select_split_edge_cases_exact():
+    """A batch whose longest unit (70001 keys) is past what one work-group's
+    select holds, so every unit of it takes the split select (tiles of 4096
+    keys): empty, single-key, fully kept and budget-0 units next to long
+    ones; NaN, signed zeros, infinities and denormals; an all-equal unit
+    (ties across every tile boundary) and budgets one below the length."""
+    lens = [0, 1, 5, 4096, 4097, 36000, 50000, 70001]
+    budgets = [4, 0, 9, 4096, 17, 35999, 1, 70000]
+    case = _hand_case(lens, budgets)
+    rows = case.total_rows()
+    g = np.random.default_rng(71)
+    pool = np.array([0.0, -0.0, 1.5, -1.5, np.inf, -np.inf, np.nan, 3.25, 1e-38, -1e-38], np.float32)
+    sc = g.choice(pool, size=rows).astype(np.float32)
+    s0, n0 = case.unit_rows(5, 0, 1)
+    sc[s0:s0 + n0] = 2.0
+    s1, n1 = case.unit_rows(6, 0, 0)
+    sc[s1:s1 + n1] = g.normal(size=n1).astype(np.float32)
+    s2, n2 = case.unit_rows(7, 0, 1)
+    sc[s2:s2 + n2] = g.integers(-3, 4, size=n2).astype(np.float32) * 0.5
+    res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
+    check_selection_exact(case, res)
+    ostart, b = case.unit_out_rows(5, 0, 1)
+    np.testing.assert_array_equal(res["kept"][ostart:ostart + b].cpu().numpy(), np.arange(35999))
+
+
+@pytest.mark.parametrize("n,B", [(35841, 35840), (40000, 1), (131072, 4096), (100000, 50000)])
+def test_select_split_many_ties(n, B):
+    """Split select on 7 distinct score values: the threshold value spans
+    every tile, so each tile's share of the quota comes from the counts of
+    the tiles before it."""
+    case = _hand_case([n], [B], Hkv=1)
+    g = np.random.default_rng(n + B + 1)
+    sc = g.integers(-3, 4, size=n).astype(np.float32) * 0.5
+    res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
+    check_selection_exact(case, res)
+
+
 # ---------------------------------------------- full sizes (bench launch)
 def _sample(units, k, seed=0):
     g = np.random.default_rng(seed)
