@@ -268,7 +268,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.n_units = (int64_t)S * LH;
   p.off_ctrl = take((size_t)tri::kCtrlHeader * sizeof(uint32_t));
   // The fused path keeps raw scores on chip; the generic path spills them.
-  p.off_apack = take(om.max ? tri::max_offsets_operand_bytes(p.d, p.G, p.mp, p.n_units, p.tickets)
+  p.off_apack = take(om.max ? tri::max_offsets_operand_bytes(p.d, p.G, om.n, p.mp, p.n_units, p.tickets)
                             : tri::fused_operand_bytes(p.d, p.n_units));
   p.off_ustats = take(p.fused ? 0 : (size_t)p.n_units * p.G * 2 * sizeof(double));
   p.off_raw = take(p.fused ? 0 : (size_t)p.total_rows * p.G * sizeof(float));

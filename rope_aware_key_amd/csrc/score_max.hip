@@ -120,10 +120,25 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&v)[8]) {
 
 }  // namespace
 
+// Offset phasors exp(i omega_f delta_j) for every (offset, band), fp64: they
+// depend on neither the unit nor the head, so the pack kernel reads them
+// instead of evaluating a sincos per operand element.
+__global__ __launch_bounds__(256) void max_phasor_kernel(int F, int d, int nD, double theta,
+                                                         const double* __restrict__ offsets,
+                                                         double2* __restrict__ ph) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= nD * F) return;
+  const int j = idx / F, f = idx % F;
+  const double omega = pow(theta, -2.0 * (double)f / (double)d);
+  double sn, cs;
+  sincos(omega * offsets[j], &sn, &cs);
+  ph[idx] = make_double2(cs, sn);
+}
+
 // Split coefficient rows: thread (unit, pass, tile, step, lane) forms the
 // fp64 coefficients of the row the lane feeds at tile position m = lane%16
 // (slot m/4, entry m%4; head and offset from the slot layout above),
-//   a_f = P[l][h][f] E[s][f] exp(i omega_f delta),
+//   a_f = P[l][h][f] E[s][f] exp(i omega_f delta)  (the last factor from ph),
 // for the lane's eight elements of the step (the real or imaginary part of
 // each element's band, by the RoPE layout), and stores their bf16
 // hi/mid/lo splits in MFMA A-operand lane order.  Rows past |D| repeat the first
@@ -141,9 +156,9 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&v)[8]) {
 // row r = 4q' + i carrying the pass's local head 4i + q'.
 template <int STEPS>
 __global__ __launch_bounds__(256) void pack_max_operands_kernel(
-    int S, int L, int Hkv, int G, bool half, MaxOffsetsPlan mp, int nD, double theta,
+    int S, int L, int Hkv, int G, bool half, MaxOffsetsPlan mp, int nD,
     const double2* __restrict__ P, const float* __restrict__ W, const double2* __restrict__ E,
-    const double* __restrict__ offsets, uint4* __restrict__ apack, uint4* __restrict__ wpack) {
+    const double2* __restrict__ ph, uint4* __restrict__ apack, uint4* __restrict__ wpack) {
   constexpr int F = STEPS * 16;
   constexpr int D = STEPS * 32;
   const int64_t units = (int64_t)S * L * Hkv;
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
     }
     const int h = pass * mp.hp + hl;
     const bool live = hl < mp.hp && h < G;
-    const double delta = offsets[j < nD ? j : 0];
+    const double2* phj = ph + (int64_t)(j < nD ? j : 0) * F;
     // element j of the lane's eight: the real or imaginary part (by the
     // RoPE layout) of its band's coefficient
     uint32_t h3[8], m3[8], l3[8];
@@ -189,9 +204,8 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
       if (live) {
         const double2 pv = P[((int64_t)l * Hq + g * G + h) * F + f];
         const double2 ev = E[(int64_t)s * F + f];
-        const double omega = pow(theta, -2.0 * (double)f / (double)D);
-        double sn, cs;
-        sincos(omega * delta, &sn, &cs);
+        const double2 pd = phj[f];
+        const double cs = pd.x, sn = pd.y;
         const double ar = pv.x * ev.x - pv.y * ev.y, ai = pv.x * ev.y + pv.y * ev.x;
         x = elem_part(e, D, half) ? ar * sn + ai * cs : ar * cs - ai * sn;
       }
@@ -546,13 +560,14 @@ MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets) {
   return mp;
 }
 
-size_t max_offsets_operand_bytes(int d, int G, const MaxOffsetsPlan& mp, int64_t units,
+size_t max_offsets_operand_bytes(int d, int G, int nD, const MaxOffsetsPlan& mp, int64_t units,
                                  int64_t tickets) {
   if (!mp.ok) return 0;
   const int steps = d / 32;
   const size_t ops = (size_t)units * mp.npass *
                      ((size_t)mp.ptiles * steps * 3 * 64 + (size_t)steps * 3 * 64) * sizeof(uint4);
-  return ops + (size_t)tickets * kWaves * G * 2 * sizeof(double) + 64 * sizeof(float);
+  return ops + (size_t)tickets * kWaves * G * 2 * sizeof(double) + 64 * sizeof(float) +
+         (size_t)nD * (d / 2) * sizeof(double2);
 }
 
 template <int STEPS, bool HALF>
@@ -566,16 +581,21 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
   uint4* apack = reinterpret_cast<uint4*>(operands);
   uint4* wpack = apack + units * mp.npass * mp.ptiles * STEPS * 3 * 64;
   double* wsum = reinterpret_cast<double*>(wpack + units * mp.npass * STEPS * 3 * 64);
+  float* sink = reinterpret_cast<float*>(wsum + (int64_t)total_tickets * kWaves * G * 2);
+  double2* ph = reinterpret_cast<double2*>(sink + 64);
+  constexpr int F = STEPS * 16;
+  hipLaunchKernelGGL(max_phasor_kernel, dim3((unsigned)((nD * F + 255) / 256)), dim3(256), 0, st,
+                     F, STEPS * 32, nD, theta, offsets, ph);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t threads = units * mp.npass * mp.ptiles * STEPS * 64 + units * mp.npass * STEPS * 64;
   hipLaunchKernelGGL(pack_max_operands_kernel<STEPS>, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, st, S, L, Hkv, G, HALF, mp, nD, theta, P, W, E, offsets,
-                     apack, wpack);
-  hipError_t e = hipGetLastError();
+                     dim3(256), 0, st, S, L, Hkv, G, HALF, mp, nD, P, W, E, ph, apack, wpack);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = ((size_t)mp.ptiles + 1) * STEPS * 3 * 64 * sizeof(uint4);
   const int grid = (total_tickets + kTicketsPerGroup - 1) / kTicketsPerGroup;
   constexpr int GB = STEPS <= 4 ? 4 : 2;
-  float* sink = reinterpret_cast<float*>(wsum + (int64_t)total_tickets * kWaves * G * 2);
   const int ne = (mp.hp + 3) / 4;
 #define TRI_LAUNCH(NE)                                                                         \
   hipLaunchKernelGGL((score_max_kernel<STEPS, GB, NE, HALF>), dim3(grid), dim3(kThreads), lds, \

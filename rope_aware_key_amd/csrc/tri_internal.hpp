@@ -197,7 +197,7 @@ struct MaxOffsetsPlan {
 };
 MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets);
 // Operand rows, norm weights and per-wave moment sums of the max path.
-size_t max_offsets_operand_bytes(int d, int G, const MaxOffsetsPlan& mp, int64_t units,
+size_t max_offsets_operand_bytes(int d, int G, int nD, const MaxOffsetsPlan& mp, int64_t units,
                                  int64_t tickets);
 // Generic tickets (kScoreChunk keys); raw: [rows][G] fp32 spill; chunk_stats
 // as the generic path; P from the prologue with fold = false.
