@@ -151,8 +151,11 @@ size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs,
  *
  *  Work-groups of the fused kernel wait for each other's per-chunk
  *  statistics.  The wait provably ends, and it is also bounded: should the
- *  bound ever be reached, the kernel does not hang; the affected chunk's
- *  head_stats mean comes out NaN (sigma 0) and its scores -inf.
+ *  bound ever be reached, the kernel does not hang.  A head whose
+ *  statistics a finalizing work-group gave up on gets mean NaN and sigma 0
+ *  there, so its z-scores drop out of that chunk's maximum (scores -inf
+ *  where every head of the group is affected), and head_stats, written
+ *  with the unit's first chunk, show (NaN, 0) for it.
  */
 tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      const int64_t* cu_len, const int32_t* cur_pos,
@@ -161,6 +164,16 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      const float* q_R, float* scores, float* raw_scores,
                      double* head_stats, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * tri_debug_set_wait_limit -- test hook: the number of polls of one
+ * chunk-statistics slot after which a finalizing work-group of the fused
+ * score kernel gives up on it (default 4194304, far beyond any real wait).
+ * Applies to launches queued after it returns; returns the previous value.
+ * A small bound forces the outcome described at tri_score from the host,
+ * with every kernel still exiting normally.  Not for production use.
+ */
+uint32_t tri_debug_set_wait_limit(uint32_t polls);
 
 /*
  * Offset-set variants of tri_score.

@@ -7,7 +7,8 @@ only marshals arguments to it.  Importing raises if the library is not built.
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, Decode, TriError, TriKvPages, TriShape, last_error, make_pages,
     make_shape, status_string, TRI_REDUCE_MAX, TRI_REDUCE_MEAN, TRI_ROPE_HALF_SPLIT,
-    TRI_ROPE_INTERLEAVED, tri_calibrate, tri_calibrate_workspace_bytes, tri_pyramid_budgets,
+    TRI_ROPE_INTERLEAVED, tri_calibrate, tri_calibrate_workspace_bytes, tri_debug_set_wait_limit,
+    tri_pyramid_budgets,
     tri_score, tri_score_offsets, tri_score_paged, tri_select_compact, tri_select_compact_layers,
     tri_select_compact_paged, tri_trig_correlation, tri_trig_correlation_workspace_bytes,
     tri_workspace_bytes, tri_workspace_bytes_layers, tri_workspace_bytes_offsets,

@@ -62,6 +62,8 @@ _lib.tri_status_string.argtypes = [ctypes.c_int]
 _lib.tri_status_string.restype = ctypes.c_char_p
 _lib.tri_last_error.argtypes = []
 _lib.tri_last_error.restype = ctypes.c_char_p
+_lib.tri_debug_set_wait_limit.argtypes = [ctypes.c_uint32]
+_lib.tri_debug_set_wait_limit.restype = ctypes.c_uint32
 
 class TriDecodeConfig(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_int32), ("interval", ctypes.c_int32),
@@ -128,7 +130,7 @@ EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_byte
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
            "tri_trig_correlation", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
            "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
-           "tri_workspace_bytes_paged")
+           "tri_workspace_bytes_paged", "tri_debug_set_wait_limit")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -324,6 +326,11 @@ class Decode:
             self.close()
         except Exception:
             pass
+
+
+def tri_debug_set_wait_limit(polls: int) -> int:
+    """Test hook: bound on the fused score kernel's wait (see triattn.h)."""
+    return int(_lib.tri_debug_set_wait_limit(int(polls)))
 
 
 def tri_pyramid_budgets(num_layers, mean_budget, ratio):

@@ -299,6 +299,8 @@ const char* tri_status_string(tri_status s) {
 
 const char* tri_last_error(void) { return g_last_error.c_str(); }
 
+uint32_t tri_debug_set_wait_limit(uint32_t polls) { return tri::set_fused_wait_limit(polls); }
+
 size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len) {
   Plan p;
   if (make_plan(shape, num_seqs, cu_len, nullptr, nullptr, p) != TRI_OK) return 0;

@@ -59,6 +59,8 @@
 //    more than the unit's chunks.  The planner caps chunks per unit well
 //    below that.  A spin bound turns a broken invariant into an error flag
 //    instead of a hang.
+#include <atomic>
+
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -85,7 +87,6 @@ __device__ __forceinline__ void split3(double x, uint32_t& hi, uint32_t& mid, ui
 constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kRawPad = 4;  // LDS row stride (floats) per head = ch + kRawPad
-constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kPrefetch = 2;  // blocks of 16 keys in flight per wave
 constexpr int kStatGroups = kFusedThreads / kMaxGroup;  // finalize reduction fan-in
 constexpr int kPollBatch = 4;  // chunk-stat slots a finalizing thread loads at once
@@ -448,6 +449,7 @@ __device__ __forceinline__ bool vector_scores(const Chunk& ck, const float* scor
 __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, const float* raw,
                                                Shared& sh, const double* __restrict__ chunk_stats,
                                                uint32_t* __restrict__ err_flag,
+                                               uint32_t wait_limit,
                                                float* __restrict__ scores,
                                                float* __restrict__ raw_out,
                                                double* __restrict__ head_stats, int unit_n) {
@@ -478,8 +480,11 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
             __builtin_amdgcn_s_sleep(2);
             u[r][0] = ld_agent_u64(cs);
             u[r][1] = ld_agent_u64(cs + 1);
-            if (++spins > kSpinLimit) {
+            if (++spins > wait_limit) {
+              // give up on the whole slot (one half may have landed): the
+              // head's moments become NaN, never a finite mean with sigma 0
               __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              u[r][0] = u[r][1] = kStatSentinel;
               break;
             }
           }
@@ -568,8 +573,8 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
     const uint4* __restrict__ apack, const uint16_t* __restrict__ k, const Pages pg,
     const int32_t* __restrict__ ptab,
-    double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, float* __restrict__ scores,
-    float* __restrict__ raw_out, double* __restrict__ head_stats) {
+    double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, uint32_t wait_limit,
+    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats) {
   extern __shared__ float raw_s[];  // 2 buffers of [G][ch + kRawPad]
   __shared__ Shared sh;
   uint32_t* ticket_ctr = ctrl;
@@ -636,7 +641,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       __syncthreads();  // sh.red1/red2 are free again
     }
     if (have_prev)
-      chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, scores, raw_out,
+      chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, wait_limit, scores, raw_out,
                      head_stats, prev.nkeys_unit);
     if (have && !ahead) {
       if (threadIdx.x == 0) sh.ticket = (int)claim();
@@ -711,6 +716,12 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
                                      __float_as_uint(wv[2]), __float_as_uint(wv[3]));
 }
 
+// Polls of a chunk-statistics slot before a finalizing work-group gives up
+// on it (the wait ends by construction; this only bounds a broken one).
+static std::atomic<uint32_t> g_wait_limit{1u << 22};
+
+uint32_t set_fused_wait_limit(uint32_t polls) { return g_wait_limit.exchange(polls); }
+
 template <int STEPS, bool HALF, bool PAGED>
 static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
@@ -737,7 +748,7 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
   if (grid > total_tickets) grid = total_tickets;
   hipLaunchKernelGGL((score_fused_kernel<STEPS, HALF, PAGED>), dim3(grid), dim3(kFusedThreads),
                      lds, st, seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg, pg.table, cs, ctrl,
-                     scores, raw, hs);
+                     g_wait_limit.load(std::memory_order_relaxed), scores, raw, hs);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ def test_header_symbols_exported():
                           "tri_trig_correlation_workspace_bytes", "tri_trig_correlation",
                           "tri_pyramid_budgets", "tri_workspace_bytes_layers",
                           "tri_select_compact_layers", "tri_score_paged",
-                          "tri_select_compact_paged", "tri_workspace_bytes_paged"}
+                          "tri_select_compact_paged", "tri_workspace_bytes_paged",
+                          "tri_debug_set_wait_limit"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -145,6 +146,18 @@ def test_calibrate_argument_checks():
     assert _status(cal, ws=None, wsb=0) == ST["WORKSPACE"]
     assert _status(cal, wsb=need - 1) == ST["WORKSPACE"]
     assert _status(cal, ws=_Fake(FAKE + 8)) == ST["INVALID"]
+
+
+def test_wait_limit_hook_round_trip():
+    """The test hook swaps the fused kernel's wait bound on the host side
+    only (no device work) and hands back the previous value."""
+    prev = R.tri_debug_set_wait_limit(7)
+    try:
+        assert prev == 1 << 22
+        assert R.tri_debug_set_wait_limit(9) == 7
+    finally:
+        R.tri_debug_set_wait_limit(prev)
+    assert R.tri_debug_set_wait_limit(prev) == prev
 
 
 def test_split_select_workspace():
