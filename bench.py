@@ -6,6 +6,9 @@ head_dim 128, batch 8, 32768 keys per head pruned to 2048, K and V bf16),
 inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py --workload {smallest,decode_window,ragged,stress_ties}
+                                        # other workloads; those that fit in the
+                                        # Infinity Cache are also timed cold
   python bench.py --offsets linear --reduce max   # offset-set variant (tri_score_offsets)
   python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
   python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
@@ -206,11 +209,14 @@ def synth_config_bytes(name):
 WORKLOADS = {
     # name: (overrides, label)
     "long_reasoning": ({}, "long_reasoning_32k_to_2048"),
+    "smallest": ({}, "smallest_4096_to_512"),
     "decode_window": ({}, "decode_window_3200_to_3072"),
     "ragged": ({}, "ragged_256seq_one_layer"),
     "stress_ties": ({}, "stress_ties_131072_to_4096"),
 }
 
+
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level cache
 
 OFFSET_SETS = {
     "default": [2.0 ** j for j in range(17)],           # {2^0..2^16}
@@ -624,6 +630,15 @@ def main():
         label = f"{label}+half_split_rope"
     sh = R.make_shape(case.shape.head_dim, case.shape.num_q_heads, case.shape.num_kv_heads,
                       case.shape.num_layers, case.shape.rope_theta, rope_layout=args.rope_layout)
+    if case.calib_q is not None:
+        # statistics from the workload's own calibration queries (not timed)
+        if args.rope_layout == "half":
+            print("--rope-layout half runs on workloads with synthesised statistics",
+                  file=sys.stderr)
+            sys.exit(2)
+        R.tri_calibrate(sh, case.calib_q, case.calib_pos, case.calib_q.shape[1], case.q_centre,
+                        case.q_absmean, case.q_R)
+        torch.cuda.synchronize()
     rows, out_rows, d = case.total_rows(), case.total_out_rows(), case.shape.head_dim
     cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
     cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
@@ -759,6 +774,31 @@ def main():
     copy_gbps = device_copy_gbps()
     out["device_copy_gbps"] = copy_gbps
     out["hbm_frac_of_device_copy"] = gbps / copy_gbps
+    if b_score + b_sel < INFINITY_CACHE_BYTES:
+        # The working set fits in the Infinity Cache, so the steps above run
+        # warm.  Cold: a 1 GiB scratch write before each step (outside the
+        # timed region, ahead of it on the same stream) evicts it.
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                 torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i, (e0, e1, e2) in enumerate(cold):
+            scratch.fill_(i & 255)
+            e0.record(stream)
+            score()
+            e1.record(stream)
+            select()
+            e2.record(stream)
+        torch.cuda.synchronize()
+        del scratch
+        c_score = np.array([a.elapsed_time(b) for a, b, _ in cold])
+        c_sel = np.array([b.elapsed_time(c) for _, b, c in cold])
+        c_step = np.array([a.elapsed_time(c) for a, _, c in cold])
+        out["cold_cache"] = {
+            "flush": "1 GiB scratch write before each step, outside the timed region",
+            "ms_per_step": float(c_step.mean()), "ms_per_step_median": float(np.median(c_step)),
+            "keys_per_s": keys / (float(c_step.mean()) * 1e-3),
+            "breakdown_ms": {"tri_score": float(c_score.mean()),
+                             "tri_select_compact": float(c_sel.mean())}}
     if budgets is not None:
         out["config"]["budget"] = "pyramid"
         out["config"]["layer_budgets"] = [int(x) for x in budgets[0]]
