@@ -10,6 +10,7 @@ inputs resident in HBM.  Prints one JSON line.
                                         # other workloads; those that fit in the
                                         # Infinity Cache are also timed cold
   python bench.py --offsets linear --reduce max   # offset-set variant (tri_score_offsets)
+  python bench.py --compare-reductions  # kept-set overlap of the mean and max readings
   python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
   python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
   python bench.py --traffic DIR --out FILE   # counter runs (DIR/fetch, write, copy_fetch,
@@ -461,6 +462,72 @@ def run_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def run_compare_reductions(args):
+    """How far the two offset readings disagree: the averaged score (the talk
+    page's formula) against the maximum over offsets (the blog review's
+    reading), each z-scored, maxed over the group and cut to the top B, on
+    the long-reasoning synthetic cache.  Per unit: the fraction of the B
+    kept keys the two readings share, for the pages' budgets."""
+    import numpy as np
+    import torch
+
+    import rope_aware_key_amd as R
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    case = synth.workload_case("long_reasoning", device=dev)
+    sh = R.make_shape(case.shape.head_dim, case.shape.num_q_heads, case.shape.num_kv_heads,
+                      case.shape.num_layers, case.shape.rope_theta)
+    cu = torch.as_tensor(case.cu_len).pin_memory().numpy()
+    cp = torch.as_tensor(case.cur_pos).pin_memory().numpy()
+    offs = torch.as_tensor(OFFSET_SETS["default"], dtype=torch.float64).pin_memory().numpy()
+    rows, n = case.total_rows(), case.seq_len(0)
+    units = case.num_units
+    ws = torch.empty(max(R.tri_workspace_bytes(sh, cu),
+                         R.tri_workspace_bytes_offsets(sh, cu, len(offs), "max")),
+                     dtype=torch.uint8, device=dev)
+    sc = {}
+    for red in ("mean", "max"):
+        sc[red] = torch.empty(rows, dtype=torch.float32, device=dev)
+        R.tri_score_offsets(sh, cu, cp, case.k, case.k_pos, case.q_centre, case.q_absmean,
+                            case.q_R, offs, red, sc[red], workspace=ws)
+    corr = []
+    for u in range(units):
+        a = sc["mean"][u * n:(u + 1) * n].double()
+        b = sc["max"][u * n:(u + 1) * n].double()
+        corr.append(float(torch.corrcoef(torch.stack([a, b]))[0, 1]))
+    by_budget = {}
+    for B in (512, 1024, 2048, 4096):
+        bu = torch.full((case.num_seqs,), B, dtype=torch.int32).pin_memory().numpy()
+        masks = {}
+        for red in ("mean", "max"):
+            kept = torch.empty(units * B, dtype=torch.int32, device=dev)
+            R.tri_select_compact(sh, cu, bu, sc[red], None, None, None, kept, None, None, None,
+                                 workspace=ws)
+            m = torch.zeros(rows, dtype=torch.bool, device=dev)
+            base = torch.arange(units, device=dev, dtype=torch.int64).repeat_interleave(B) * n
+            m[base + kept.long()] = True
+            masks[red] = m
+        both = (masks["mean"] & masks["max"]).view(units, n).sum(dim=1).double() / B
+        q = both.cpu().numpy()
+        by_budget[str(B)] = {"mean": float(q.mean()), "min": float(q.min()),
+                             "p10": float(np.percentile(q, 10)), "max": float(q.max())}
+    torch.cuda.synchronize()
+    corr = np.array(corr)
+    out = {
+        "metric": "kept-set overlap between the mean and the max over the 17 offsets",
+        "value": by_budget["2048"]["mean"], "unit": "fraction of B shared (B = 2048)",
+        "n_gpus": 1, "higher_is_better": True, "vs_baseline": None,
+        "data": "synthetic (seeded concentrated bf16 K cache, synthesised query statistics)",
+        "config": {"workload": "long_reasoning_32k_to_2048", "units": units,
+                   "keys_per_head": n, "offsets": "2^0..2^16"},
+        "overlap_by_budget": by_budget,
+        "score_pearson_per_unit": {"mean": float(corr.mean()), "min": float(corr.min())},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run_calib(args):
     """Calibration at scale and the reconstruction diagnostic at the
     long-reasoning model shape (28 layers, 28 query heads, 4 KV heads,
@@ -562,6 +629,8 @@ def main():
                     help="time the decode-loop driver at the decode-window shape")
     ap.add_argument("--calib", action="store_true",
                     help="calibration at scale and the reconstruction diagnostic")
+    ap.add_argument("--compare-reductions", action="store_true",
+                    help="kept-set overlap of the mean and the max over offsets")
     ap.add_argument("--workload", default="long_reasoning", choices=list(WORKLOADS))
     ap.add_argument("--offsets", default="default", choices=list(OFFSET_SETS))
     ap.add_argument("--reduce", default="mean", choices=["mean", "max"])
@@ -606,6 +675,9 @@ def main():
         return
     if args.calib:
         run_calib(args)
+        return
+    if args.compare_reductions:
+        run_compare_reductions(args)
         return
 
     import numpy as np
