@@ -14,8 +14,8 @@ import torch
 
 import oracle as O
 import synth
-from harness import (check_scores, gpu_run, gpu_score_offsets, gpu_score_paged, half_split,
-                     oracle_unit, pinned, shape_of, units_of)
+from harness import (check_scores, check_selection_exact, gpu_run, gpu_score_offsets,
+                     gpu_score_paged, half_split, oracle_unit, pinned, shape_of, units_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,23 @@ def test_paged_equals_packed_bitwise(d, G, P, head_major, P_out):
     kept, out = _paged_select(case, res["scores"], pool, P_out)
     assert torch.equal(kept, res["kept"])
     _check_rows(case, res, out, units_of(case))
+
+
+def test_paged_long_units_split_select():
+    """Units past 35840 keys in a paged pool: the split select on the scores
+    and the compaction through both page tables give the packed call's kept
+    indices and rows; a short sequence shares the batch."""
+    shape = synth.Shape(64, 8, 2, 1)
+    case = synth.build_case("paged_long", shape, [40000, 700, 65536], [20000, 699, 4096],
+                            device=DEV, seed=23)
+    res = gpu_run(case, raw=False, stats=False)
+    pool = synth.paged_from_case(case, 64, head_major=True, seed=23)
+    pr = _paged_score(case, pool)
+    assert torch.equal(_bits(pr["scores"]), _bits(res["scores"]))
+    kept, out = _paged_select(case, res["scores"], pool, 128)
+    assert torch.equal(kept, res["kept"])
+    _check_rows(case, res, out, units_of(case))
+    check_selection_exact(case, res, rows_units=[])
 
 
 @pytest.mark.parametrize("P", [1, 4, 8])
