@@ -187,6 +187,17 @@ def test_decode_loop_decode_window_shape():
          check_every=128)
 
 
+@pytest.mark.timeout(600)
+def test_decode_loop_long_context_split_select():
+    """Prompts of 40000 and 36100 keys with a budget of 36000: every prune
+    selects over units past 35840 keys, so the split select runs inside the
+    loop (at prefill and after 64 appends), with sinks and a recent window."""
+    shape = synth.Shape(64, 2, 1, 1)
+    prunes = _run(shape, [40000, 36100], 70, B=36000, interval=64, sink=4, recent=32, seed=29,
+                  check_every=35)
+    assert prunes == 4
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_decode_loop_random(seed):
     """Seeded random decode runs: head_dim, group, layers, prompt lengths,
