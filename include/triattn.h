@@ -44,6 +44,12 @@
  *  - Argument errors return before any device work is queued.  A HIP error
  *    during launch returns TRI_ERR_HIP.  tri_last_error() gives a message
  *    for the last failing call of the calling thread.
+ *  - Host arrays reach the device through a pinned staging ring the library
+ *    allocates once per device: each call copies its per-sequence plan into
+ *    a ring slot and queues an asynchronous copy from it, and a slot is
+ *    reused only once that copy has completed.  Calls are therefore not
+ *    meant to be captured into a HIP graph: a replay would copy whatever a
+ *    later call left in the slot.
  */
 #ifndef TRIATTN_H
 #define TRIATTN_H
