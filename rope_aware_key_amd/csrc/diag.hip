@@ -14,7 +14,8 @@
 // exact MFMA per 32-wide step; the rotated centres are formed per query in
 // fp64 and split into three bf16 terms (fp32-accurate, as in the score
 // kernels).  A wave owns 16 queries of one (layer, head) and streams the
-// KV head's keys in blocks of 16; each lane sums x, y, x^2, y^2, xy over
+// KV head's keys in blocks of 16, the next block's loads in flight while
+// the current one is multiplied; each lane sums x, y, x^2, y^2, xy over
 // its valid pairs in fp64, the wave reduces them and a merge kernel adds
 // the waves of a head in order (deterministic).
 #include "tri_internal.hpp"
@@ -149,13 +150,23 @@ __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
   double sx = 0.0, sy = 0.0, sxx = 0.0, syy = 0.0, sxy = 0.0;
   const uint16_t* kunit = k + ((int64_t)l * Hkv + g) * n_k * D;
   const int64_t blocks = (n_k + 15) / 16;
+  // B operands of block blk (key 16*blk + m, clamped), one block ahead
+  auto load_keys = [&](int64_t blk, uint4 (&kb)[STEPS]) {
+    const uint4* krow =
+        reinterpret_cast<const uint4*>(kunit + min<int64_t>(blk * 16 + m, n_k - 1) * D);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) kb[st] = krow[4 * st + qd];
+  };
+  uint4 kcur[STEPS];
+  load_keys(0, kcur);
   for (int64_t blk = 0; blk < blocks; ++blk) {
     const int64_t key = blk * 16 + m;
-    const uint4* krow = reinterpret_cast<const uint4*>(kunit + min<int64_t>(key, n_k - 1) * D);
+    uint4 knext[STEPS];
+    load_keys(blk + 1 < blocks ? blk + 1 : blk, knext);
     f32x4d_t accx = {0.f, 0.f, 0.f, 0.f}, accy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-      const uint4 kb = krow[4 * st + qd];
+      const uint4 kb = kcur[st];
       bf16x8d_t bk, a0, a1, a2, a3;
       __builtin_memcpy(&bk, &kb, 16);
       __builtin_memcpy(&a0, &ay[st], 16);
@@ -179,6 +190,8 @@ __global__ __launch_bounds__(64 * kDiagWaves) void trig_corr_kernel(
       syy = fma(y, y, syy);
       sxy = fma(x, y, sxy);
     }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) kcur[st] = knext[st];
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
