@@ -273,10 +273,14 @@ def algorithmic_bytes(case, budgets=None):
     return keys, score, sel
 
 
-def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="interleaved"):
-    """The oracle as it stands (fp64, term by term) on whole units of the same
-    workload, one after another, on one host thread (with the same offset
-    set and reduction as the GPU line)."""
+def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="interleaved",
+                 factored=False):
+    """The oracle as it stands (fp64) on whole units of the same workload,
+    one after another in (layer, KV head) order of sequence 0, on one host
+    thread (with the same offset set and reduction as the GPU line), until
+    max_seconds.  factored=False: the term-by-term definition (the
+    baseline); factored=True: the oracle's factored form of the same score
+    (one dot product per head), the faster CPU reference."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -286,32 +290,42 @@ def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="in
     keys = 0
     units = 0
     t0 = time.perf_counter()
+    done = False
     with threadpool_limits(limits=1):
-        for g in range(case.shape.num_kv_heads):
-            start, n = case.unit_rows(0, 0, g)
-            kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
-            pos = case.k_pos[start:start + n].cpu().numpy().astype(np.float64)
-            vrows = case.v[start:start + n].cpu().numpy()
-            qc = case.q_centre[0, g * G:(g + 1) * G].cpu().double().numpy()
-            t_unit = time.perf_counter()
-            score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, float(case.cur_pos[0]),
-                                  qc[..., 0] + 1j * qc[..., 1],
-                                  case.q_absmean[0, g * G:(g + 1) * G].cpu().double().numpy(),
-                                  case.q_R[0, g * G:(g + 1) * G].cpu().double().numpy(), om,
-                                  reduce=reduce, layout=layout,
-                                  **({} if offsets is None else {"offsets": offsets}))[0]
-            kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
-            O.compact_rows(kbits, kept)
-            O.compact_rows(vrows, kept)
-            O.compact_rows(pos, kept)
-            keys += n
-            units += 1
-            if time.perf_counter() - t0 > max_seconds or time.perf_counter() - t_unit > max_seconds / 2:
+        for l in range(case.shape.num_layers):
+            for g in range(case.shape.num_kv_heads):
+                start, n = case.unit_rows(0, l, g)
+                kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
+                pos = case.k_pos[start:start + n].cpu().numpy().astype(np.float64)
+                vrows = case.v[start:start + n].cpu().numpy()
+                hs = slice(g * G, (g + 1) * G)
+                qc = case.q_centre[l, hs].cpu().double().numpy()
+                t_unit = time.perf_counter()
+                score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, float(case.cur_pos[0]),
+                                      qc[..., 0] + 1j * qc[..., 1],
+                                      case.q_absmean[l, hs].cpu().double().numpy(),
+                                      case.q_R[l, hs].cpu().double().numpy(), om,
+                                      reduce=reduce, layout=layout, factored=factored,
+                                      **({} if offsets is None else {"offsets": offsets}))[0]
+                kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
+                O.compact_rows(kbits, kept)
+                O.compact_rows(vrows, kept)
+                O.compact_rows(pos, kept)
+                keys += n
+                units += 1
+                now = time.perf_counter()
+                if now - t0 > max_seconds or now - t_unit > max_seconds / 2:
+                    done = True
+                    break
+            if done:
                 break
     dt = time.perf_counter() - t0
-    return {"value": keys / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} unit(s) (sequence 0, layer 0, KV heads 0..{units - 1}) of "
-                      f"{n} keys, G={G}: term-by-term fp64 score ({reduce} over "
+    how = ("factored fp64 score (one dot product per head)" if factored
+           else "term-by-term fp64 score")
+    return {"value": keys / dt, "unit": "keys/s", "cores": 1,
+            "kind": "oracle (factored)" if factored else "oracle",
+            "sample": f"{units} unit(s) of sequence 0 in (layer, KV head) order, {n} keys each, "
+                      f"G={G}: {how} ({reduce} over "
                       f"{len(offsets) if offsets is not None else 17} offsets), z-score, max, "
                       f"top-B, gather; "
                       f"{dt:.1f} s"}
@@ -900,6 +914,10 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, offsets=OFFSET_SETS[args.offsets],
                                            reduce=args.reduce, layout=args.rope_layout)
+        if not variant and budgets is None and pool is None:
+            print("[bench] cpu factored baseline", file=sys.stderr, flush=True)
+            out["cpu_factored_baseline"] = cpu_baseline(case, max_seconds=20.0,
+                                                        layout=args.rope_layout, factored=True)
     print(json.dumps(out), flush=True)
 
 
