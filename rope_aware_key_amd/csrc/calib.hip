@@ -32,6 +32,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 constexpr int kCalibChunk = 256;
 constexpr int kCalibWaves = 4;   // waves per work-group, one chunk each
 constexpr int kCalibBatch = 4;  // samples per register batch (two batches in flight)
+constexpr int kXcds = 8;        // XCDs of the chip, each with its own L2
 
 __global__ __launch_bounds__(256) void calib_phasor_kernel(int F, int d, double theta,
                                                            const int32_t* __restrict__ q_pos,
@@ -79,22 +80,30 @@ struct QuadLoad {
 
 }  // namespace
 
-// Grid (ceil(chunks / kCalibWaves), L, ceil(Hq*F/4 / 64)), 64 * kCalibWaves
-// threads.  Wave w takes chunk kCalibWaves*blockIdx.x + w; lane i takes band
-// quad blockIdx.z*64 + i (head h = quad / (F/4), bands 4j .. 4j+3 with
-// j = quad mod F/4), so a wave reads one contiguous stretch of each sample
-// row.  Loads are double-buffered: the queries and phasors of the next
+// Work item (chunk group cg, layer l, slab zq), zq fastest; 64 * kCalibWaves
+// threads.  Wave w takes chunk kCalibWaves*cg + w; lane i takes band quad
+// zq*64 + i (head h = quad / (F/4), bands 4j .. 4j+3 with j = quad mod F/4),
+// so a wave reads one contiguous stretch of each sample row.  Work-groups
+// are dealt to the chip's 8 XCDs in turn (block b on XCD b mod 8, each XCD
+// with its own L2); block b takes item (b mod 8)*per + b/8, so an XCD walks
+// a contiguous run of items and the phasors of its few chunk groups stay in
+// its L2 (1.4% faster than the plain 3-D grid at 10240 samples, 28 x 28).  Loads are double-buffered: the queries and phasors of the next
 // kCalibBatch samples are in flight while the current ones are summed.
 // partial[((l*chunks + c)*W + h*F + f)*3 + {0,1,2}] = sums of Re, Im, |q_f|.
 template <bool HALF, bool ROTATE>
 __global__ __launch_bounds__(64 * kCalibWaves) void calib_partial_kernel(
     int Hq, int F, int64_t N, int chunks, const uint16_t* __restrict__ q,
-    const float2* __restrict__ ph, double* __restrict__ partial) {
+    const float2* __restrict__ ph, double* __restrict__ partial, int L, int nz, int64_t items,
+    int64_t per) {
   const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * kCalibWaves + (threadIdx.x >> 6);
-  const int l = blockIdx.y;
+  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (item >= items) return;
+  const int zq = (int)(item % nz);
+  const int64_t rr = item / nz;
+  const int l = (int)(rr % L);
+  const int c = (int)(rr / L) * kCalibWaves + (threadIdx.x >> 6);
   const int quads = F >> 2;
-  const int quad = blockIdx.z * 64 + lane;
+  const int quad = zq * 64 + lane;
   if (c >= chunks || quad >= Hq * quads) return;
   const int h = quad / quads, j = quad % quads;
   const int64_t W = (int64_t)Hq * F;
@@ -204,21 +213,24 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)((chunks + kCalibWaves - 1) / kCalibWaves), (unsigned)L,
-                  (unsigned)((Hq * (F / 4) + 63) / 64));
+  const int nz = (Hq * (F / 4) + 63) / 64;
+  const int64_t items = (int64_t)((chunks + kCalibWaves - 1) / kCalibWaves) * L * nz;
+  const int64_t per = (items + kXcds - 1) / kXcds;
+  if (per * kXcds > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(per * kXcds));
   const dim3 block(64 * kCalibWaves);
   if (half && ph)
     hipLaunchKernelGGL((calib_partial_kernel<true, true>), grid, block, 0, st, Hq, F, n_samples,
-                       chunks, q, ph, partial);
+                       chunks, q, ph, partial, L, nz, items, per);
   else if (half)
     hipLaunchKernelGGL((calib_partial_kernel<true, false>), grid, block, 0, st, Hq, F, n_samples,
-                       chunks, q, ph, partial);
+                       chunks, q, ph, partial, L, nz, items, per);
   else if (ph)
     hipLaunchKernelGGL((calib_partial_kernel<false, true>), grid, block, 0, st, Hq, F, n_samples,
-                       chunks, q, ph, partial);
+                       chunks, q, ph, partial, L, nz, items, per);
   else
     hipLaunchKernelGGL((calib_partial_kernel<false, false>), grid, block, 0, st, Hq, F, n_samples,
-                       chunks, q, ph, partial);
+                       chunks, q, ph, partial, L, nz, items, per);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t m = (int64_t)L * W;
