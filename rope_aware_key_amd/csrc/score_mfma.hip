@@ -481,10 +481,12 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
             u[r][0] = ld_agent_u64(cs);
             u[r][1] = ld_agent_u64(cs + 1);
             if (++spins > wait_limit) {
-              // give up on the whole slot (one half may have landed): the
-              // head's moments become NaN, never a finite mean with sigma 0
+              // give up on the whole slot, even if its second half landed:
+              // a NaN sum makes the head's mean NaN and its sigma 0, never a
+              // finite mean with sigma 0 (one store; the second half's
+              // value no longer matters)
               __hip_atomic_store(err_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              u[r][0] = u[r][1] = kStatSentinel;
+              u[r][0] = kStatSentinel;
               break;
             }
           }
