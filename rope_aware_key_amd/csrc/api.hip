@@ -751,10 +751,17 @@ tri_status tri_decode_append(tri_decode* dec, const uint16_t* k_new, const uint1
     if (dec->len[s] + 1 == dec->C) hit.push_back(s);
   }
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = upload(dec->items, it.data(), it.size() * sizeof(tri::DecodeItem), st);
-  if (e == hipSuccess)
-    e = tri::launch_append(dec->items, S, dec->LH, dec->d, dec->C, k_new, v_new, dec->k, dec->v,
-                           dec->pos, st);
+  hipError_t e = hipSuccess;
+  if (S <= tri::kAppendInline) {
+    // the items ride in the launch: no staging copy per decode step
+    e = tri::launch_append_inline(it.data(), S, dec->LH, dec->d, dec->C, k_new, v_new, dec->k,
+                                  dec->v, dec->pos, st);
+  } else {
+    e = upload(dec->items, it.data(), it.size() * sizeof(tri::DecodeItem), st);
+    if (e == hipSuccess)
+      e = tri::launch_append(dec->items, S, dec->LH, dec->d, dec->C, k_new, v_new, dec->k,
+                             dec->v, dec->pos, st);
+  }
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("decode append: ") + hipGetErrorString(e));
   for (int s = 0; s < S; ++s) ++dec->len[s];
   if (hit.empty()) return TRI_OK;

@@ -220,6 +220,12 @@ struct DecodeItem {
   int32_t pad;
 };
 static_assert(sizeof(DecodeItem) == 16, "DecodeItem layout");
+// Sequences whose append items travel in the kernel arguments (16 bytes each).
+constexpr int kAppendInline = 128;
+// host_items: host memory, copied into the launch (S <= kAppendInline).
+hipError_t launch_append_inline(const DecodeItem* host_items, int S, int LH, int d,
+                                int64_t stride, const uint16_t* k_new, const uint16_t* v_new,
+                                uint16_t* k, uint16_t* v, int32_t* pos, hipStream_t st);
 hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t stride,
                          const uint16_t* k_new, const uint16_t* v_new, uint16_t* k, uint16_t* v,
                          int32_t* pos, hipStream_t st);

@@ -187,6 +187,17 @@ def test_decode_loop_decode_window_shape():
          check_every=128)
 
 
+def test_decode_loop_many_sequences_staged_append():
+    """130 sequences, past the 128 whose append items ride in the kernel
+    arguments: the items go through the staging copy instead.  Short
+    prompts of different lengths, a prune every 4 appends."""
+    shape = synth.Shape(64, 2, 1, 1)
+    g = np.random.default_rng(41)
+    n_pre = [int(x) for x in g.integers(0, 14, size=130)]
+    prunes = _run(shape, n_pre, 9, B=8, interval=4, sink=1, recent=2, seed=41, check_every=3)
+    assert prunes >= 130
+
+
 @pytest.mark.timeout(600)
 def test_decode_loop_long_context_split_select():
     """Prompts of 40000 and 36100 keys with a budget of 36000: every prune
