@@ -209,9 +209,9 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   // the fused kernel reads a 16-key block from one page
   p.fused = !om.max && tri::fused_supported(p.d, p.half) &&
             (!p.in_pg.table || p.in_pg.page_shift >= 4) &&
-            (longest + tri::fused_chunk_keys(p.G) - 1) / tri::fused_chunk_keys(p.G) <=
+            (longest + tri::fused_chunk_keys(p.G, p.d) - 1) / tri::fused_chunk_keys(p.G, p.d) <=
                 tri::kFusedMaxUnitChunks;
-  p.chunk = p.fused ? tri::fused_chunk_keys(p.G) : tri::kScoreChunk;
+  p.chunk = p.fused ? tri::fused_chunk_keys(p.G, p.d) : tri::kScoreChunk;
   for (int s = 0; s < S; ++s) {
     const int64_t n = cu_len[s + 1] - cu_len[s];
     if (n < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len must be non-decreasing");

@@ -760,11 +760,15 @@ bool fused_supported(int d, bool half) {
   return d % 32 == 0 && d >= 32 && d <= kMaxHeadDim && (!half || d % 64 == 0);
 }
 
-// Keys per ticket: as many as let three work-groups (two raw buffers of G
-// heads each) share a CU's LDS, in multiples of 64, at most 1024.
-int fused_chunk_keys(int G) {
+// Keys per ticket: as many as let the work-groups a CU holds (two raw
+// buffers of G heads each) share its LDS, in multiples of 64, at most 1024.
+// Up to d = 128 the kernel's registers allow three work-groups per CU; from
+// d = 160 (five or more 32-wide steps) only two fit, and chunks sized for
+// two cut the chunk boundaries by a third (3% on a d = 256 cache).
+int fused_chunk_keys(int G, int d) {
+  const int wgs = d / 32 >= 5 ? 2 : 3;
   // leave room for the static LDS (Shared)
-  const int per_wg = kFusedLdsPerCu / 3 - (int)((sizeof(Shared) + 255) / 256 * 256);
+  const int per_wg = kFusedLdsPerCu / wgs - (int)((sizeof(Shared) + 255) / 256 * 256);
   int ch = (per_wg / (2 * G * (int)sizeof(float)) - kRawPad) / 64 * 64;
   if (ch > 1024) ch = 1024;
   if (ch < 64) ch = 64;

@@ -152,7 +152,7 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
 
 bool fused_supported(int d, bool half);
 // Keys per ticket of the fused path for a GQA group of G heads.
-int fused_chunk_keys(int G);
+int fused_chunk_keys(int G, int d);
 // Bound on the fused kernel's wait for another work-group's chunk statistics
 // (polls per slot; default 2^22); returns the previous bound.
 uint32_t set_fused_wait_limit(uint32_t polls);
