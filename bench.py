@@ -12,6 +12,7 @@ inputs resident in HBM.  Prints one JSON line.
   python bench.py --offsets linear --reduce max   # offset-set variant (tri_score_offsets)
   python bench.py --compare-reductions  # kept-set overlap of the mean and max readings
   python bench.py --copy-probe          # 1 GiB device copy, for counter scaling
+  python bench.py --stream-probe        # 4 GiB streaming read: the practical read ceiling
   python bench.py --summarize DIR --out FILE --cmd "..."   # rocprofv3 CSV -> text
   python bench.py --traffic DIR --out FILE   # counter runs (DIR/fetch, write, copy_fetch,
                                              # copy_write) -> HBM bytes per tri_score call
@@ -32,6 +33,7 @@ METRIC = "keys scored+compacted/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 COPY_PROBE_BYTES = 1 << 30
+STREAM_PROBE_BYTES = 4 << 30  # well past the 256 MB Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_long_reasoning_32k_to_2048.json")
 # The fused score kernel, its operand pack and launch shape (score_mfma.hip),
 # the prologue (calib.hip) and the shared device helpers (tri_internal.hpp):
@@ -81,6 +83,31 @@ def device_copy_gbps(reps=10):
     del a, b
     torch.cuda.empty_cache()
     return 2 * COPY_PROBE_BYTES / t / 1e9
+
+
+def stream_probe_gbps(reps=10):
+    """Rate of a plain streaming read (tri_stream_probe: 16-byte
+    non-temporal loads over every CU) of STREAM_PROBE_BYTES, timed with HIP
+    events on the stream it runs on: the practical ceiling of the score
+    kernel's K stream."""
+    import torch
+    import rope_aware_key_amd as R
+    a = torch.empty(STREAM_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    a.fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    R.tri_stream_probe(a, sink, stream=st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        R.tri_stream_probe(a, sink, stream=st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del a
+    torch.cuda.empty_cache()
+    return STREAM_PROBE_BYTES / t / 1e9
 
 
 def copy_probe(reps=10):
@@ -660,6 +687,8 @@ def main():
                          "sequence's budget), selected by tri_select_compact_layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="time the read-bandwidth probe alone (4 GiB, 20 reads) and print its rate")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--cmd", default="")
@@ -677,6 +706,11 @@ def main():
         return
     if args.copy_probe:
         copy_probe()
+        return
+    if args.stream_probe:
+        g = stream_probe_gbps(reps=20)
+        print(json.dumps({"stream_probe_bytes": STREAM_PROBE_BYTES, "reps": 20,
+                          "stream_probe_gbps": g, "frac_of_peak": g / PEAK_HBM_GBPS}))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path shards over (sequence, layer, KV head) "
@@ -860,6 +894,9 @@ def main():
     copy_gbps = device_copy_gbps()
     out["device_copy_gbps"] = copy_gbps
     out["hbm_frac_of_device_copy"] = gbps / copy_gbps
+    probe_gbps = stream_probe_gbps()
+    out["stream_probe_gbps"] = probe_gbps
+    out["roofline"]["frac_of_stream_probe"] = score_gbps / probe_gbps
     if b_score + b_sel < INFINITY_CACHE_BYTES:
         # The working set fits in the Infinity Cache, so the steps above run
         # warm.  Cold: a 1 GiB scratch write before each step (outside the

@@ -294,6 +294,22 @@ tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q,
                                 void* stream);
 
 /*
+ * tri_stream_probe -- read-bandwidth probe (a measurement aid, not part of
+ * the method): reads `bytes` of device memory at src once, with 16-byte
+ * non-temporal loads spread over every compute unit, and XORs all its
+ * 32-bit words into *sink (so no read can be skipped).  Timing it on a
+ * buffer the size of a K cache gives the rate a plain streaming read
+ * reaches on the device, the practical ceiling of tri_score's K stream.
+ *
+ *  src    device, 16-byte aligned; bytes a multiple of 16 (else
+ *         TRI_ERR_INVALID_ARGUMENT).  Read only.
+ *  sink   one device uint32, owned and initialised by the caller; the
+ *         probe XORs into it (it is not cleared).
+ * bytes == 0 is a no-op.  Asynchronous on `stream`.
+ */
+tri_status tri_stream_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Decode-loop driver.
  *
  * Keeps the pruned K/V cache of a batch across decode steps.

@@ -97,6 +97,8 @@ _lib.tri_trig_correlation.argtypes = [ctypes.POINTER(TriShape), _P, _P, ctypes.c
                                       ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_trig_correlation.restype = ctypes.c_int
 
+_lib.tri_stream_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.tri_stream_probe.restype = ctypes.c_int
 _lib.tri_pyramid_budgets.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_double, _P]
 _lib.tri_pyramid_budgets.restype = ctypes.c_int
 _lib.tri_workspace_bytes_layers.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P]
@@ -128,7 +130,7 @@ EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_byte
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
-           "tri_trig_correlation", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
+           "tri_trig_correlation", "tri_stream_probe", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
            "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
            "tri_workspace_bytes_paged", "tri_debug_set_wait_limit")
 
@@ -267,6 +269,14 @@ def tri_trig_correlation(shape: TriShape, q, q_pos, n_q, k, k_pos, n_k, q_centre
                                    _ptr(k_pos), int(n_k), _ptr(q_centre), _ptr(r), _ptr(workspace),
                                    int(wsb), _stream(stream))
     _check(st, "tri_trig_correlation")
+
+
+def tri_stream_probe(src, sink, nbytes=None, stream=None):
+    """Read-bandwidth probe: reads src (device, 16-byte aligned) once and
+    XORs its 32-bit words into sink (one device uint32/int32, not cleared)."""
+    n = nbytes if nbytes is not None else src.numel() * src.element_size()
+    st = _lib.tri_stream_probe(_ptr(src), int(n), _ptr(sink), _stream(stream))
+    _check(st, "tri_stream_probe")
 
 
 def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx, k_out,

@@ -364,6 +364,17 @@ tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q, const
   return TRI_OK;
 }
 
+tri_status tri_stream_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return TRI_OK;
+  if (!src || !sink) return fail(TRI_ERR_INVALID_ARGUMENT, "src and sink must be non-NULL");
+  if (bytes % 16 != 0 || !aligned16(src))
+    return fail(TRI_ERR_INVALID_ARGUMENT, "src must be 16-byte aligned and bytes a multiple of 16");
+  if (bytes > ((size_t)1 << 62)) return fail(TRI_ERR_INVALID_ARGUMENT, "bytes out of range");
+  const hipError_t e = tri::launch_stream_probe(src, (int64_t)bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("stream_probe: ") + hipGetErrorString(e));
+  return TRI_OK;
+}
+
 size_t tri_calibrate_workspace_bytes(const tri_shape* shape, int64_t n_samples) {
   if (check_shape(shape) != TRI_OK) return 0;
   if (n_samples < 1) {
@@ -415,7 +426,7 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
     e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq, q_centre, q_absmean, q_R, doff,
                              om.n, !om.max, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
                              (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl),
-                             (double*)(ws + p.off_stats), p.n_stat_slots, s);
+                             tri::kCtrlHeader, (double*)(ws + p.off_stats), p.n_stat_slots, s);
   if (e != hipSuccess) return e;
   float* raw = raw_scores ? raw_scores : (float*)(ws + p.off_raw);
   if (om.max)

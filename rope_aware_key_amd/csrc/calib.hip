@@ -249,16 +249,19 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const float* __restrict__ q_centre, const float* __restrict__ q_absmean,
     const float* __restrict__ q_R, const double* __restrict__ offsets, int nD, int fold,
     double2* __restrict__ P, float* __restrict__ W, double2* __restrict__ E,
-    uint32_t* __restrict__ ctrl, double* __restrict__ stat_slots, int64_t n_stat_slots) {
+    uint32_t* __restrict__ ctrl, int64_t n_ctrl, double* __restrict__ stat_slots,
+    int64_t n_stat_slots) {
   const int F = d >> 1;
   const int64_t n_stat = (int64_t)L * Hq * F;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // score control block and published-statistics slots of this call
-  if (idx < kCtrlHeader) ctrl[idx] = 0u;
+  // score control words and published-statistics slots of this call
+  if (idx < n_ctrl) ctrl[idx] = 0u;
   if (idx < n_stat_slots)
     reinterpret_cast<unsigned long long*>(stat_slots)[idx] = kStatSentinel;
-  if (idx < n_stat) {
-    const int f = (int)(idx % F);
+  // C_f = mean over the offsets of exp(i omega_f delta), once per band per
+  // block (F <= 128)
+  __shared__ double2 cf[kMaxHeadDim / 2];
+  for (int f = threadIdx.x; f < F; f += blockDim.x) {
     const double omega = pow(theta, -2.0 * (double)f / (double)d);
     double cr = 1.0, ci = 0.0;
     if (fold) {
@@ -274,6 +277,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(
       cr *= inv;
       ci *= inv;
     }
+    cf[f] = make_double2(cr, ci);
+  }
+  __syncthreads();
+  if (idx < n_stat) {
+    const int f = (int)(idx % F);
+    const double cr = cf[f].x, ci = cf[f].y;
     const double qr = (double)q_centre[2 * idx], qi = (double)q_centre[2 * idx + 1];
     P[idx] = make_double2(qr * cr - qi * ci, qr * ci + qi * cr);
     W[idx] = (float)((1.0 - (double)q_R[idx]) * (double)q_absmean[idx]);
@@ -290,16 +299,16 @@ __global__ __launch_bounds__(256) void prologue_kernel(
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqInfo* seqs,
                            const float* q_centre, const float* q_absmean, const float* q_R,
                            const double* offsets, int n_offsets, bool fold, double2* P,
-                           float* W, double2* E, uint32_t* ctrl, double* stat_slots,
-                           int64_t n_stat_slots, hipStream_t st) {
+                           float* W, double2* E, uint32_t* ctrl, int64_t n_ctrl,
+                           double* stat_slots, int64_t n_stat_slots, hipStream_t st) {
   int64_t total = (int64_t)L * Hq * (d / 2) + (int64_t)S * (d / 2);
   if (n_stat_slots > total) total = n_stat_slots;
-  if (kCtrlHeader > total) total = kCtrlHeader;
+  if (n_ctrl > total) total = n_ctrl;
   const int nD = offsets ? n_offsets : 17;
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, st, L, Hq, d, theta, S,
                      seqs, q_centre, q_absmean, q_R, offsets, nD, fold ? 1 : 0, P, W, E, ctrl,
-                     stat_slots, n_stat_slots);
+                     n_ctrl, stat_slots, n_stat_slots);
   return hipGetLastError();
 }
 

@@ -261,4 +261,49 @@ hipError_t launch_trig_corr(int L, int Hq, int Hkv, int d, int64_t n_q, int64_t 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Read-bandwidth probe: the rate a plain streaming read reaches on this
+// device, the practical ceiling of the score kernel's K stream.  Each thread
+// reads a grid-strided share of src with 16-byte non-temporal loads, four in
+// flight, and XORs the words; one atomic per wave folds them into *sink (so
+// no load can be dropped).
+// ---------------------------------------------------------------------------
+typedef uint32_t v4u_probe_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_probe_kernel(const v4u_probe_t* __restrict__ src,
+                                                           int64_t n16, uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  v4u_probe_t x = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const v4u_probe_t a = __builtin_nontemporal_load(src + i);
+    const v4u_probe_t b = __builtin_nontemporal_load(src + i + stride);
+    const v4u_probe_t c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const v4u_probe_t d = __builtin_nontemporal_load(src + i + 3 * stride);
+    x ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
+  uint32_t w = x.x ^ x.y ^ x.z ^ x.w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) w ^= __shfl_xor(w, o, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, w);
+}
+
+hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(&stream_probe_kernel), 256, 0);
+  if (e != hipSuccess) return e;
+  const int64_t n16 = bytes / 16;
+  int64_t grid = (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
+  if (grid > (n16 + 255) / 256) grid = (n16 + 255) / 256;
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)grid), dim3(256), 0, st,
+                     reinterpret_cast<const v4u_probe_t*>(src), n16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace tri

@@ -33,22 +33,26 @@
 //    wait for the rest of chunk i's unit overlaps useful streaming.
 //  * No work-group idles between chunks: while streaming chunk i+1 it has
 //    already claimed chunk i+2 (an atomic whose result it reads afterwards),
-//    so it requests chunk i+2's first K blocks and operands, then finalizes
-//    chunk i and publishes chunk i+1 while they land.  This holds whenever
-//    chunk i+1 starts past the end of chunk i's unit; otherwise (rare: one
-//    group took two chunks of a unit) it publishes chunk i+1, finalizes
-//    chunk i, and only then claims and requests the next chunk.
+//    so it requests chunk i+2's first K blocks, then publishes chunk i+1
+//    and finalizes chunk i while they land.  This holds whenever chunk i+1
+//    starts past the end of chunk i's unit; otherwise (rare: one group took
+//    two chunks of a unit) it publishes chunk i+1, finalizes chunk i, and
+//    only then claims and requests the next chunk.
+//  * The steps between chunks work per head on a group of lanes inside one
+//    wave (the moments of a chunk, the sums of a unit's published slots)
+//    and reduce it with DPP lane moves, so a head's total forms in one lane
+//    without a work-group barrier.
 //  * Publishing needs no flag and no ordering wait: every published slot
 //    holds a sentinel NaN (set by the prologue) until its value lands, and
 //    values are written once with coherent (agent-scope) stores.  A
 //    finalizing work-group reads all chunk slots of its unit (re-reading any
-//    that still hold the sentinel), sums them in chunk order and derives
+//    that still hold the sentinel), sums them in one fixed order and derives
 //    (mu, sigma); every chunk of the unit does the same arithmetic on the
 //    same numbers, so results are deterministic and equal keys score
 //    equally.
 //  * Waits cannot deadlock.  A work-group waits only to finalize, and then
-//    holds claimed, unpublished chunks (at most two) only of later units
-//    than the one it waits on.  Following "waits on a chunk held by" from
+//    holds a claimed, unpublished chunk (at most one, claimed ahead) only of
+//    a later unit than the one it waits on.  Following "waits on a chunk held by" from
 //    any waiter therefore passes through strictly earlier units and ends at
 //    a work-group that is streaming (and will publish) or at an unclaimed
 //    chunk.  Tickets are claimed in order, so an unclaimed chunk a waiter
@@ -88,14 +92,56 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kRawPad = 4;  // LDS row stride (floats) per head = ch + kRawPad
 constexpr int kPrefetch = 2;  // blocks of 16 keys in flight per wave
-constexpr int kStatGroups = kFusedThreads / kMaxGroup;  // finalize reduction fan-in
-constexpr int kPollBatch = 4;  // chunk-stat slots a finalizing thread loads at once
+constexpr int kPollBatch = 4;  // chunk-stat slots a finalizing lane loads at once
 constexpr int kFusedLdsPerCu = 160 * 1024;
 constexpr int kFusedMaxLds = 96 * 1024;  // dynamic LDS ceiling of one work-group
 
 __device__ __forceinline__ double wave_sum_f(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// threadIdx.x through an opaque move: per-lane values derived from it in the
+// once-per-chunk steps are then recomputed where used instead of being
+// hoisted out of the persistent loop, where they would stay live (and hold
+// registers) through the streaming loop.
+__device__ __forceinline__ int local_tid() {
+  int v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"((int)threadIdx.x));
+  return v;
+}
+
+// The per-head steps between chunks give head h the lanes [h << sh, (h + 1)
+// << sh) of the work-group, a group inside one wave: 64 lanes for G <= 4,
+// 32 for G <= 8, else 16.
+__device__ __forceinline__ int head_shift(int G) { return G <= 4 ? 6 : (G <= 8 ? 5 : 4); }
+
+// An fp64 value moved across lanes by a DPP pattern (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Sum over a head's group of lanes: swaps within quads, rotations by 4 and 8
+// within rows of 16 (DPP, no LDS), then the row pair (swizzle, xor 16) and
+// the wave halves (xor 32) as the group needs.  The group's first lane
+// forms its total in the same order in every work-group.
+__device__ __forceinline__ double head_sum(double v, int shift) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x124>(v);  // row_ror:4
+  v += dpp_f64<0x128>(v);  // row_ror:8
+  if (shift >= 5) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_ds_swizzle((int)b, 0x401F);  // xor 16 within 32 lanes
+    const int hi = __builtin_amdgcn_ds_swizzle((int)(b >> 32), 0x401F);
+    v += __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+  }
+  if (shift >= 6) v += __shfl_xor(v, 32, 64);
   return v;
 }
 
@@ -126,12 +172,25 @@ struct Chunk {
   int64_t row0, unit;  // row0: first score row of the chunk (and first K row when packed)
 };
 
+// Tickets a work-group claims only grow, so the sequence of a new ticket is
+// found from that of the group's last one (s_from): usually it is the same
+// or the next, two loads issued together; past that, a binary search.
 __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L, int Hkv, int ch,
-                                              int t) {
+                                              int t, int s_from) {
   Chunk ck;
   ck.t = t;
-  ck.s = find_seq_by_ticket(seqs, S, t);
-  const SeqInfo si = seqs[ck.s];
+  int s = s_from;
+  SeqInfo si = seqs[s];
+  if (s + 1 < S && seqs[s + 1].chunk_base <= t) {
+    int lo = s + 1, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seqs[mid].chunk_base <= t) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    si = seqs[s];
+  }
+  ck.s = s;
   ck.nch = (si.n + ch - 1) / ch;
   const int local = t - si.chunk_base;
   ck.lg = local / ck.nch;
@@ -152,14 +211,8 @@ __device__ __forceinline__ Chunk decode_chunk(const SeqInfo* seqs, int S, int L,
 constexpr int kTileChunks = 16 * 9;
 
 struct Shared {
-  // The between-chunk reductions (fp64 sum, sum of squares per head) and
-  // the waves' staging tiles (used only while streaming) share storage.
-  union {
-    double red[2][kStatGroups][kMaxGroup];
-    uint4 tile[kFusedWaves][kTileChunks];
-  };
-  double pub[kMaxGroup][2];  // a chunk's moments, summed, until published
-  float zmul[kMaxGroup], zadd[kMaxGroup];
+  uint4 tile[kFusedWaves][kTileChunks];  // the waves' staging tiles (streaming only)
+  float2 zm[kMaxGroup];                  // per head: z = raw * zm.x + zm.y
   int ticket;
 };
 
@@ -281,10 +334,6 @@ __device__ __forceinline__ void ring_prime(const Chunk& ck, const uint16_t* __re
   }
 }
 
-// Raw scores of one chunk into raw (LDS, [G][ch + kRawPad]) and the per-wave,
-// per-head fp64 sum and sum of squares of them into sh.red1/red2.  The ring
-// holds the chunk's first blocks (ring_prime); a ring of kPrefetch register
-// buffers keeps that many blocks in flight per wave.
 template <int STEPS>
 struct UnitOperands {
   bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];  // trig coefficients, bf16 split
@@ -311,6 +360,9 @@ __device__ __forceinline__ void load_operands(const Chunk& ck, const uint4* __re
   }
 }
 
+// Raw scores of one chunk into raw (LDS, [G][ch + kRawPad]).  The ring holds
+// the chunk's first blocks (ring_prime); a ring of kPrefetch register buffers
+// keeps that many blocks in flight per wave.
 template <int STEPS, bool HALF, bool PAGED>
 __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
                                           const UnitOperands<STEPS>& op,
@@ -377,17 +429,20 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
 }
 
 // Per-head fp64 sum and sum of squares of a chunk's raw scores, read back
-// from LDS (call after a barrier that follows chunk_raw): thread (h, j)
-// takes keys 4j.. of every 64, then the tail, into sh.red1/red2[j][h].
-__device__ __forceinline__ void chunk_moments(const Chunk& ck, int G, int rs, const float* raw,
-                                              Shared& sh) {
-  const int tid = threadIdx.x;
-  const int h = tid % kMaxGroup, j = tid / kMaxGroup;
+// from LDS (after a barrier that follows chunk_raw), published with
+// coherent stores by the first lane of each head's group.  No wait: readers
+// recognise slots not yet written by their sentinel.
+__device__ __forceinline__ void chunk_moments_publish(const Chunk& ck, int G, int rs,
+                                                      const float* raw,
+                                                      double* __restrict__ chunk_stats) {
+  const int tid = local_tid();
+  const int hs = head_shift(G), lph = 1 << hs;
+  const int h = tid >> hs, k = tid & (lph - 1);
   double a = 0.0, b2 = 0.0;
   if (h < G) {
     const float* row = raw + h * rs;
     const int nk4 = ck.nkeys & ~3;
-    for (int i = 4 * j; i < nk4; i += 4 * kStatGroups) {
+    for (int i = 4 * k; i < nk4; i += 4 * lph) {
       const f32x4_t r = *reinterpret_cast<const f32x4_t*>(row + i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -396,42 +451,18 @@ __device__ __forceinline__ void chunk_moments(const Chunk& ck, int G, int rs, co
         b2 = fma(v, v, b2);
       }
     }
-    for (int i = nk4 + j; i < ck.nkeys; i += kStatGroups) {
+    for (int i = nk4 + k; i < ck.nkeys; i += lph) {
       const double v = (double)row[i];
       a += v;
       b2 = fma(v, v, b2);
     }
   }
-  sh.red[0][j][h] = a;
-  sh.red[1][j][h] = b2;
-}
-
-// Sum the chunk's per-group moments (call after a barrier that follows
-// chunk_moments); thread h < G keeps head h's (sum, sum of squares) in
-// sh.pub for chunk_publish.
-__device__ __forceinline__ void chunk_moment_sums(int G, Shared& sh) {
-  const int tid = threadIdx.x;
-  if (tid < G) {
-    double a = 0.0, b2 = 0.0;
-#pragma unroll
-    for (int g2 = 0; g2 < kStatGroups; ++g2) {
-      a += sh.red[0][g2][tid];
-      b2 += sh.red[1][g2][tid];
-    }
-    sh.pub[tid][0] = a;
-    sh.pub[tid][1] = b2;
-  }
-}
-
-// Publish the sums with coherent stores, by the threads that formed them.
-// No wait: readers recognise slots not yet written by their sentinel.
-__device__ __forceinline__ void chunk_publish(const Chunk& ck, int G, const Shared& sh,
-                                              double* __restrict__ chunk_stats) {
-  const int tid = threadIdx.x;
-  if (tid < G) {
-    double* cs = chunk_stats + ((int64_t)ck.t * G + tid) * 2;
-    st_agent(cs, sh.pub[tid][0]);
-    st_agent(cs + 1, sh.pub[tid][1]);
+  a = head_sum(a, hs);
+  b2 = head_sum(b2, hs);
+  if (h < G && k == 0) {
+    double* cs = chunk_stats + ((int64_t)ck.t * G + h) * 2;
+    st_agent(cs, a);
+    st_agent(cs + 1, b2);
   }
 }
 
@@ -453,26 +484,27 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
                                                float* __restrict__ scores,
                                                float* __restrict__ raw_out,
                                                double* __restrict__ head_stats, int unit_n) {
-  const int tid = threadIdx.x;
-  const int h = tid % kMaxGroup, j = tid / kMaxGroup;  // head, reduction group
+  const int tid = local_tid();
+  const int hs = head_shift(G), lph = 1 << hs;
+  const int h = tid >> hs, k = tid & (lph - 1);
   double a = 0.0, b2 = 0.0;
   if (h < G) {
-    // Thread (h, j) sums chunks j, j + kStatGroups, ... in that order.  The
-    // loads of a batch are all issued before any is examined, so a unit of
-    // up to kStatGroups * kPollBatch chunks costs one round trip.
+    // Lane k of head h's group sums chunks k, k + lph, ... in that order.
+    // The loads of a batch are all issued before any is examined, so a unit
+    // of up to lph * kPollBatch chunks costs one round trip.
     const int t0 = ck.t - ck.c;
-    for (int cc0 = j; cc0 < ck.nch; cc0 += kStatGroups * kPollBatch) {
+    for (int cc0 = k; cc0 < ck.nch; cc0 += lph * kPollBatch) {
       uint64_t u[kPollBatch][2];
 #pragma unroll
       for (int r = 0; r < kPollBatch; ++r) {
-        const int cc = min(cc0 + r * kStatGroups, ck.nch - 1);
+        const int cc = min(cc0 + r * lph, ck.nch - 1);
         const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
         u[r][0] = ld_agent_u64(cs);
         u[r][1] = ld_agent_u64(cs + 1);
       }
 #pragma unroll
       for (int r = 0; r < kPollBatch; ++r) {
-        const int cc = cc0 + r * kStatGroups;
+        const int cc = cc0 + r * lph;
         if (cc < ck.nch) {
           const double* cs = chunk_stats + ((int64_t)(t0 + cc) * G + h) * 2;
           uint32_t spins = 0;
@@ -496,16 +528,8 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
       }
     }
   }
-  sh.red[0][j][h] = a;
-  sh.red[1][j][h] = b2;
-  __syncthreads();
-  if (tid < G) {
-    double sa = 0.0, sb = 0.0;
-#pragma unroll
-    for (int g2 = 0; g2 < kStatGroups; ++g2) {
-      sa += sh.red[0][g2][tid];
-      sb += sh.red[1][g2][tid];
-    }
+  const double sa = head_sum(a, hs), sb = head_sum(b2, hs);
+  if (h < G && k == 0) {
     // population moments over the unit's keys; fp64 keeps the cancellation
     // in sum x^2 - n mu^2 far below the fp32 resolution of the raw scores
     const double n = (double)unit_n;
@@ -513,11 +537,10 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
     const double var = fmax(sb / n - mu * mu, 0.0);
     const double sigma = sqrt(var);
     const double inv = sigma > 0.0 ? 1.0 / sigma : 0.0;
-    sh.zmul[tid] = (float)inv;
-    sh.zadd[tid] = (float)(-mu * inv);
+    sh.zm[h] = make_float2((float)inv, (float)(-mu * inv));
     if (ck.c == 0 && head_stats) {
-      head_stats[(ck.unit * G + tid) * 2] = mu;
-      head_stats[(ck.unit * G + tid) * 2 + 1] = sigma;
+      head_stats[(ck.unit * G + h) * 2] = mu;
+      head_stats[(ck.unit * G + h) * 2 + 1] = sigma;
     }
   }
   __syncthreads();
@@ -531,11 +554,12 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
     const int nk4 = ck.nkeys & ~3;
     for (int i = 4 * tid; i < nk4; i += 4 * kFusedThreads) {
       f32x4_t best = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll 4
       for (int hh = 0; hh < G; ++hh) {
         const f32x4_t r = *reinterpret_cast<const f32x4_t*>(raw + hh * rs + i);
-        const float zm = sh.zmul[hh], za = sh.zadd[hh];
+        const float2 z = sh.zm[hh];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) best[e] = fmaxf(best[e], fmaf(r[e], zm, za));
+        for (int e = 0; e < 4; ++e) best[e] = fmaxf(best[e], fmaf(r[e], z.x, z.y));
       }
       *reinterpret_cast<f32x4_t*>(out + i) = best;
     }
@@ -543,8 +567,10 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
   }
   for (int i = i0 + tid; i < ck.nkeys; i += kFusedThreads) {
     float best = -__builtin_inff();
-    for (int hh = 0; hh < G; ++hh)
-      best = fmaxf(best, fmaf(raw[hh * rs + i], sh.zmul[hh], sh.zadd[hh]));
+    for (int hh = 0; hh < G; ++hh) {
+      const float2 z = sh.zm[hh];
+      best = fmaxf(best, fmaf(raw[hh * rs + i], z.x, z.y));
+    }
     if (raw_out)
       for (int hh = 0; hh < G; ++hh) raw_out[(ck.row0 + i) * G + hh] = raw[hh * rs + i];
     out[i] = best;
@@ -556,7 +582,7 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
 __device__ __forceinline__ void chunk_store_scores(const Chunk& ck, const float* raw,
                                                    float* __restrict__ scores,
                                                    const float* raw_out) {
-  const int tid = threadIdx.x;
+  const int tid = local_tid();
   int i0 = 0;
   if (vector_scores(ck, scores, raw_out)) {
     const int nk4 = ck.nkeys & ~3;
@@ -601,7 +627,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   __syncthreads();
   int t = __builtin_amdgcn_readfirstlane(sh.ticket);  // uniform: chunk fields in SGPRs
   if (t < total_tickets) {
-    ck = decode_chunk(seqs, S, L, Hkv, ch, t);
+    ck = decode_chunk(seqs, S, L, Hkv, ch, t, 0);
     ring_prime<STEPS, PAGED>(ck, k, pg, ptab, ring, pid);
     load_operands<STEPS>(ck, apack, op);
   }
@@ -613,11 +639,11 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     float* buf_cur = raw_s + cur * G * rs;
     float* buf_prev = raw_s + (cur ^ 1) * G * rs;
     // Claim the next ticket now (its result is read after streaming) when it
-    // is bound to lie in a later unit than prev.  Then prev's finalize and
-    // this chunk's publish both run under the next chunk's first loads with
-    // this chunk and the next held unpublished, both of later units than the
-    // one waited on.  Otherwise this chunk is published before prev's
-    // finalize and the next ticket claimed after it.
+    // is bound to lie in a later unit than prev.  Then prev's finalize runs
+    // under the next chunk's first loads with the next chunk held
+    // unclaimed-by-others and unpublished, of a later unit than the one
+    // waited on.  Otherwise the next ticket is claimed after prev's
+    // finalize.  This chunk is published before prev's finalize either way.
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
@@ -632,16 +658,10 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     Chunk nk = ck;
     if (ahead) {
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
-      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
+      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t, ck.s);
     }
     if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
-    if (have) {
-      chunk_moments(ck, G, rs, buf_cur, sh);
-      __syncthreads();
-      chunk_moment_sums(G, sh);
-      if (!ahead) chunk_publish(ck, G, sh, chunk_stats);
-      __syncthreads();  // sh.red1/red2 are free again
-    }
+    if (have) chunk_moments_publish(ck, G, rs, buf_cur, chunk_stats);
     if (have_prev)
       chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, wait_limit, scores, raw_out,
                      head_stats, prev.nkeys_unit);
@@ -649,12 +669,11 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       if (threadIdx.x == 0) sh.ticket = (int)claim();
       __syncthreads();
       t = __builtin_amdgcn_readfirstlane(sh.ticket);
-      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t);
+      if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t, ck.s);
       ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
     }
     load_operands<STEPS>(nk, apack, op);
     if (have_prev) chunk_store_scores(prev, buf_prev, scores, raw_out);
-    if (ahead) chunk_publish(ck, G, sh, chunk_stats);
     __syncthreads();
     if (!have) break;
     prev = ck;

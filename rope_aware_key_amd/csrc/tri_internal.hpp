@@ -147,8 +147,8 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
                            const SeqInfo* seqs, const float* q_centre,
                            const float* q_absmean, const float* q_R,
                            const double* offsets, int n_offsets, bool fold, double2* P,
-                           float* W, double2* E, uint32_t* ctrl, double* stat_slots,
-                           int64_t n_stat_slots, hipStream_t st);
+                           float* W, double2* E, uint32_t* ctrl, int64_t n_ctrl,
+                           double* stat_slots, int64_t n_stat_slots, hipStream_t st);
 
 bool fused_supported(int d, bool half);
 // Keys per ticket of the fused path for a GQA group of G heads.
@@ -233,6 +233,9 @@ hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t 
 // (b < n) of the plan's sequences -> +inf.
 hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
                           float* scores, hipStream_t st);
+
+// Read-bandwidth probe over bytes (a multiple of 16) of src; XORs into *sink.
+hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);
 
 // Reconstruction diagnostic (d % 32 == 0): per-(layer, query head) Pearson
 // r of the trig series against the direct logits; partial is

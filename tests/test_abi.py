@@ -34,7 +34,7 @@ def test_header_symbols_exported():
                           "tri_pyramid_budgets", "tri_workspace_bytes_layers",
                           "tri_select_compact_layers", "tri_score_paged",
                           "tri_select_compact_paged", "tri_workspace_bytes_paged",
-                          "tri_debug_set_wait_limit"}
+                          "tri_debug_set_wait_limit", "tri_stream_probe"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -178,16 +178,21 @@ def test_workspace_grows_with_batch():
 
 
 def test_long_units_leave_the_fused_path():
-    """Units of more than 384 fused chunks (768 keys each at G = 7) take the
-    generic path, whose workspace holds the raw per-head scores; one chunk
-    fewer stays fused and needs no such spill."""
-    sh = R.make_shape(128, 7, 1, 1)
-    ch, cap = 768, 384
-    fused_n = ch * cap
-    long_n = ch * cap + 1
-    w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
-    w_long = R.tri_workspace_bytes(sh, [0, long_n])
-    assert w_long >= long_n * 7 * 4 > w_fused
+    """Units of more than 384 fused chunks take the generic path, whose
+    workspace holds the raw per-head scores; one chunk fewer stays fused and
+    needs no such spill.  The chunk size (a multiple of 64 keys, at most
+    1024) depends on the group and head size, so the step is searched for:
+    exactly one candidate chunk size shows it."""
+    sh = R.make_shape(128, 16, 1, 1)
+    G = 16
+    jumps = []
+    for ch in range(64, 1025, 64):
+        fused_n = ch * 384
+        w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
+        w_long = R.tri_workspace_bytes(sh, [0, fused_n + 1])
+        if w_long >= (fused_n + 1) * G * 4 and w_long - w_fused >= (fused_n + 1) * G * 2:
+            jumps.append(ch)
+    assert len(jumps) == 1, jumps
 
 
 DEFAULT_OFFSETS = [2.0 ** j for j in range(17)]
@@ -491,3 +496,14 @@ def test_sequence_count_limit():
     assert _status(_score, sh, bad_cu, np.full(8193, 5, np.int32)) == ST["UNSUPPORTED"]
     assert "8192" in R.last_error()
     assert _status(_sel, sh, bad_cu, np.ones(8193, np.int32)) == ST["UNSUPPORTED"]
+
+
+def test_stream_probe_rejects_bad_arguments():
+    sink = _Fake(FAKE + 64)
+    with pytest.raises(R.TriError, match="INVALID"):
+        R.tri_stream_probe(_Fake(FAKE + 4), sink, nbytes=64, stream=0)   # misaligned
+    with pytest.raises(R.TriError, match="INVALID"):
+        R.tri_stream_probe(_Fake(), sink, nbytes=40, stream=0)   # not a multiple of 16
+    with pytest.raises(R.TriError, match="INVALID"):
+        R.tri_stream_probe(_Fake(0), sink, nbytes=64, stream=0)   # NULL src
+    R.tri_stream_probe(_Fake(0), _Fake(0), nbytes=0, stream=0)   # empty: a no-op

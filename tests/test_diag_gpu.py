@@ -93,3 +93,19 @@ def test_trig_correlation_random(seed):
     r, ref = _run(shape, n_q, n_k, float(g.uniform(0.5, 0.99)), seed=100 + seed, layout=layout)
     np.testing.assert_allclose(r, ref, rtol=0, atol=2e-5)
 
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 20) + 16 * 37, 64 << 20])
+def test_stream_probe_reads_every_word(nbytes):
+    """The read probe folds every 32-bit word of the buffer into the sink:
+    its XOR equals the host's over the same bytes, for sizes that end in a
+    partial grid stride."""
+    import rope_aware_key_amd as R
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.as_tensor(words.view(np.int32), device=DEV)
+    sink = torch.tensor([0x1234567], dtype=torch.int32, device=DEV)
+    R.tri_stream_probe(src, sink)
+    torch.cuda.synchronize()
+    expect = np.bitwise_xor.reduce(words) ^ np.uint32(0x1234567)
+    assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == expect

@@ -287,10 +287,11 @@ def test_stress_ties_full_size():
 
 @pytest.mark.timeout(600)
 def test_unit_past_fused_chunk_cap():
-    """A unit of more than 384 fused chunks (here 320488 keys at G = 7) is
-    scored by the generic path; scores against the oracle, selection exact."""
+    """A unit of more than 384 fused chunks (here 394216 keys at G = 7, chunks
+    of at most 1024 keys) is scored by the generic path; scores against the
+    oracle, selection exact."""
     shape = synth.Shape(128, 7, 1, 1)
-    case = synth.build_case("long_unit", shape, [832 * 384 + 1000], [4096], device=DEV, seed=11)
+    case = synth.build_case("long_unit", shape, [1024 * 384 + 1000], [4096], device=DEV, seed=11)
     res = gpu_run(case, raw=False, stats=True)
     units = units_of(case)
     _compare_units(case, res, units, factored=True)
