@@ -172,6 +172,31 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * tri_score_noalloc -- tri_score for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as tri_score,
+ * without the workspace: the scratch tri_score would take from the
+ * workspace lives in a device array of the library, 64 MiB, that each GPU
+ * the library runs on holds until the process ends, and the per-call
+ * sequence table travels in kernel arguments (one small launch per 64
+ * sequences) instead of a pinned staging copy.  No hipMalloc, hipFree or
+ * host-pinned allocation is made.
+ *
+ * Limit: a call whose tri_workspace_bytes() exceeds 64 MiB (about 3,900
+ * units of head_dim 128 on the fused path) returns TRI_ERR_WORKSPACE and
+ * queues nothing.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, or two host threads) race and must
+ * be serialised by the caller; calls in order on one stream are safe (each
+ * call reinitialises what it reads).
+ */
+tri_status tri_score_noalloc(const tri_shape* shape, int32_t num_seqs,
+                             const int64_t* cu_len, const int32_t* cur_pos,
+                             const uint16_t* k, const int32_t* k_pos,
+                             const float* q_centre, const float* q_absmean,
+                             const float* q_R, float* scores, float* raw_scores,
+                             double* head_stats, void* stream);
+
+/*
  * tri_debug_set_wait_limit -- test hook: the number of polls of one
  * chunk-statistics slot after which a finalizing work-group of the fused
  * score kernel gives up on it (default 4194304, far beyond any real wait).

@@ -48,6 +48,9 @@ _lib.tri_workspace_bytes.restype = ctypes.c_size_t
 _lib.tri_score.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                            _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.tri_score.restype = ctypes.c_int
+_lib.tri_score_noalloc.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P]
+_lib.tri_score_noalloc.restype = ctypes.c_int
 _lib.tri_workspace_bytes_offsets.argtypes = [ctypes.POINTER(TriShape), ctypes.c_int32, _P,
                                              ctypes.c_int32, ctypes.c_int32]
 _lib.tri_workspace_bytes_offsets.restype = ctypes.c_size_t
@@ -130,7 +133,7 @@ EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_byte
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
-           "tri_trig_correlation", "tri_stream_probe", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
+           "tri_trig_correlation", "tri_stream_probe", "tri_score_noalloc", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
            "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
            "tri_workspace_bytes_paged", "tri_debug_set_wait_limit")
 
@@ -230,6 +233,18 @@ def tri_score(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_absmean, q
                         _ptr(raw_scores), _ptr(head_stats), _ptr(workspace), int(wsb),
                         _stream(stream))
     _check(st, "tri_score")
+
+
+def tri_score_noalloc(shape: TriShape, cu_len, cur_pos, k, k_pos, q_centre, q_absmean, q_R,
+                      scores, raw_scores=None, head_stats=None, stream=None):
+    """tri_score without a workspace (the library's device scratch; see
+    include/triattn.h for its limit and sharing rules)."""
+    cu, pcu = _host(cu_len, np.int64)
+    cp, pcp = _host(cur_pos, np.int32)
+    st = _lib.tri_score_noalloc(ctypes.byref(shape), len(cu) - 1, pcu, pcp, _ptr(k), _ptr(k_pos),
+                                _ptr(q_centre), _ptr(q_absmean), _ptr(q_R), _ptr(scores),
+                                _ptr(raw_scores), _ptr(head_stats), _stream(stream))
+    _check(st, "tri_score_noalloc")
 
 
 def tri_workspace_bytes_offsets(shape: TriShape, cu_len, n_offsets, reduce="mean") -> int:

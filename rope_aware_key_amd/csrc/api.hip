@@ -417,10 +417,12 @@ namespace {
 hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const uint16_t* k,
                      const float* q_centre, const float* q_absmean, const float* q_R,
                      float* scores, float* raw_scores, double* head_stats, char* ws,
-                     hipStream_t s) {
+                     hipStream_t s, bool inline_plan = false) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
   double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
-  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  hipError_t e = inline_plan
+                     ? tri::launch_write_plan(p.seqs.data(), (int)p.seqs.size(), dseq, s)
+                     : upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
   if (e == hipSuccess)
     e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq, q_centre, q_absmean, q_R, doff,
@@ -467,11 +469,44 @@ hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t
   return e;
 }
 
+// ---------------------------------------------------------------------------
+// Scoring without allocation (tri_score_noalloc): the workspace is a
+// file-scope device array, one copy per device for the life of the process.
+// Host code reaches a device's copy only through the address
+// hipGetSymbolAddress gives on that device, taken once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_addr.find(dev);
+  if (it != g_scratch_addr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_addr[dev] = ptr;
+  *out = ptr;
+  return hipSuccess;
+}
+
+// workspace == nullptr with noalloc: the device's scratch array, the plan
+// table written through kernel arguments (no pinned staging either).
 tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
                       const int32_t* cur_pos, const uint16_t* k, const float* q_centre,
                       const float* q_absmean, const float* q_R, const OffsetMode& om,
                       float* scores, float* raw_scores, double* head_stats, void* workspace,
-                      size_t workspace_bytes, void* stream, const tri::Pages* pages = nullptr) {
+                      size_t workspace_bytes, void* stream, const tri::Pages* pages = nullptr,
+                      bool noalloc = false) {
   Plan p;
   PlanLayout lay;
   lay.in_pages = pages;
@@ -483,10 +518,21 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
     return fail(TRI_ERR_INVALID_ARGUMENT, "k, statistics and scores must be non-NULL");
   if (!aligned16(k)) return fail(TRI_ERR_INVALID_ARGUMENT, "k must be 16-byte aligned");
   const size_t need = (raw_scores || p.fused) ? p.off_raw : p.score_bytes;
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes)
+      return fail(TRI_ERR_WORKSPACE, "this call needs " + std::to_string(need) +
+                                         " bytes of scratch; tri_score_noalloc holds " +
+                                         std::to_string(kNoAllocScratchBytes));
+    const hipError_t e = scratch_address(&workspace);
+    if (e != hipSuccess)
+      return fail(TRI_ERR_HIP, std::string("score scratch: ") + hipGetErrorString(e));
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
   const hipError_t e = run_score(p, shape->rope_theta, om, k, q_centre, q_absmean, q_R, scores,
-                                 raw_scores, head_stats, (char*)workspace, (hipStream_t)stream);
+                                 raw_scores, head_stats, (char*)workspace, (hipStream_t)stream,
+                                 noalloc);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score: ") + hipGetErrorString(e));
   return TRI_OK;
 }
@@ -504,6 +550,16 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs, const int64_t* cu
   return score_impl(shape, num_seqs, cu_len, cur_pos, k, q_centre, q_absmean, q_R,
                     OffsetMode(), scores, raw_scores, head_stats, workspace, workspace_bytes,
                     stream);
+}
+
+tri_status tri_score_noalloc(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
+                             const int32_t* cur_pos, const uint16_t* k, const int32_t* k_pos,
+                             const float* q_centre, const float* q_absmean, const float* q_R,
+                             float* scores, float* raw_scores, double* head_stats, void* stream) {
+  (void)k_pos;
+  return score_impl(shape, num_seqs, cu_len, cur_pos, k, q_centre, q_absmean, q_R,
+                    OffsetMode(), scores, raw_scores, head_stats, nullptr, 0, stream, nullptr,
+                    true);
 }
 
 tri_status tri_score_offsets(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,

@@ -312,4 +312,28 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqI
   return hipGetLastError();
 }
 
+// A launch's sequence table written from the kernel arguments (64 entries
+// per launch), for callers that pass no host staging: the entries travel
+// with the launch, so nothing on the host has to outlive the call.
+struct PlanArgs {
+  SeqInfo e[kPlanInline];
+};
+
+__global__ __launch_bounds__(64) void write_plan_kernel(PlanArgs a, int n, SeqInfo* __restrict__ dst) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = a.e[i];
+}
+
+hipError_t launch_write_plan(const SeqInfo* host, int S, SeqInfo* dst, hipStream_t st) {
+  for (int s0 = 0; s0 < S; s0 += kPlanInline) {
+    const int n = S - s0 < kPlanInline ? S - s0 : kPlanInline;
+    PlanArgs a = {};
+    for (int i = 0; i < n; ++i) a.e[i] = host[s0 + i];
+    hipLaunchKernelGGL(write_plan_kernel, dim3(1), dim3(kPlanInline), 0, st, a, n, dst + s0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace tri

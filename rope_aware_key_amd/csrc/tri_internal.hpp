@@ -234,6 +234,11 @@ hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t 
 hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
                           float* scores, hipStream_t st);
 
+// Sequence-table entries one write_plan launch carries in its arguments.
+constexpr int kPlanInline = 64;
+// Writes host[0, S) to dst (device) through kernel arguments, no staging.
+hipError_t launch_write_plan(const SeqInfo* host, int S, SeqInfo* dst, hipStream_t st);
+
 // Read-bandwidth probe over bytes (a multiple of 16) of src; XORs into *sink.
 hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);
 

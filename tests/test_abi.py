@@ -34,7 +34,8 @@ def test_header_symbols_exported():
                           "tri_pyramid_budgets", "tri_workspace_bytes_layers",
                           "tri_select_compact_layers", "tri_score_paged",
                           "tri_select_compact_paged", "tri_workspace_bytes_paged",
-                          "tri_debug_set_wait_limit", "tri_stream_probe"}
+                          "tri_debug_set_wait_limit", "tri_stream_probe",
+                          "tri_score_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -507,3 +508,19 @@ def test_stream_probe_rejects_bad_arguments():
     with pytest.raises(R.TriError, match="INVALID"):
         R.tri_stream_probe(_Fake(0), sink, nbytes=64, stream=0)   # NULL src
     R.tri_stream_probe(_Fake(0), _Fake(0), nbytes=0, stream=0)   # empty: a no-op
+
+
+def test_noalloc_rejects_calls_past_its_scratch():
+    """tri_score_noalloc holds 64 MiB of device scratch: a call needing more
+    (4096 units: 64 MiB of packed operands alone) fails with
+    TRI_ERR_WORKSPACE before queueing anything; one that fits gets past that
+    check (and fails here only on the fake K pointer's alignment)."""
+    big = R.make_shape(128, 64, 64, 64)
+    cu, cp = np.array([0, 16], np.int64), np.array([16], np.int32)
+    assert R.tri_workspace_bytes(big, cu) > 64 << 20
+    a = (_Fake(), None, _Fake(), _Fake(), _Fake(), _Fake())
+    assert _status(R.tri_score_noalloc, big, cu, cp, *a, stream=0) == ST["WORKSPACE"]
+    assert "tri_score_noalloc holds 67108864" in R.last_error()
+    small = R.make_shape(128, 7, 1, 1)
+    a = (_Fake(FAKE + 4), None, _Fake(), _Fake(), _Fake(), _Fake())
+    assert _status(R.tri_score_noalloc, small, cu, cp, *a, stream=0) == ST["INVALID"]
