@@ -72,9 +72,10 @@ typedef enum {
 /*
  * RoPE pair layout of every q/k row (TRI_ROPE_*).  Band f is the complex
  * number (x_{2f}, x_{2f+1}) -- the talk page's rotation equation -- or,
- * half split, (x_f, x_{f+d/2}), the pairing of the LLaMA/Mistral
- * implementations the tutorial page's RoPE paragraph names.  The scores
- * do not depend on the layout; only where the parts are stored.
+ * half split, (x_f, x_{f+d/2}).  The pages print only the interleaved
+ * pairing; the half split is a storage layout supported as a reading (the
+ * rotation of each pair is the printed matrix either way).  The scores do
+ * not depend on the layout; only where the parts are stored.
  */
 enum { TRI_ROPE_INTERLEAVED = 0, TRI_ROPE_HALF_SPLIT = 1 };
 
@@ -161,7 +162,12 @@ size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs,
  *  statistics a finalizing work-group gave up on gets mean NaN and sigma 0
  *  there, so its z-scores drop out of that chunk's maximum (scores -inf
  *  where every head of the group is affected), and head_stats, written
- *  with the unit's first chunk, show (NaN, 0) for it.
+ *  with the unit's first chunk, show (NaN, 0) for it.  The call also raises
+ *  a flag in the workspace that tri_score_status reports.  The planner
+ *  keeps that case out of reach: a unit takes the fused path only if its
+ *  chunks number at most the work-groups the device holds at once
+ *  (occupancy x CUs, twice what the wait needs); longer units take the
+ *  generic path, which never waits on other work-groups.
  */
 tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
                      const int64_t* cu_len, const int32_t* cur_pos,
@@ -195,6 +201,28 @@ tri_status tri_score_noalloc(const tri_shape* shape, int32_t num_seqs,
                              const float* q_centre, const float* q_absmean,
                              const float* q_R, float* scores, float* raw_scores,
                              double* head_stats, void* stream);
+
+/*
+ * tri_score_status -- whether the last tri_score (or tri_score_offsets,
+ * tri_score_paged) call queued on `workspace` gave up a bounded wait (see
+ * tri_score): *flags gets TRI_SCORE_WAIT_GAVE_UP if it did, else 0.
+ * workspace == NULL reads tri_score_noalloc's scratch on the current device.
+ * Blocks the host until `stream` has finished its queued work, then reads
+ * the flag: word 1 (a uint32 at byte offset 4) of the workspace, which
+ * every score call resets when it starts and select never writes.
+ */
+#define TRI_SCORE_WAIT_GAVE_UP 1u
+tri_status tri_score_status(const void* workspace, uint32_t* flags, void* stream);
+
+/*
+ * tri_debug_set_resident_groups -- test hook: replaces the device query of
+ * how many fused-kernel work-groups run at once (used by the planner's
+ * per-unit chunk cap, see tri_score) with `groups`; 0 restores the query.
+ * Returns the previous override.  Lets a test on any host (also without a
+ * GPU) check where the planner routes long units on a smaller device.  Not
+ * for production use.
+ */
+int32_t tri_debug_set_resident_groups(int32_t groups);
 
 /*
  * tri_debug_set_wait_limit -- test hook: the number of polls of one

@@ -38,10 +38,11 @@ Sources (cited by page title and the section or equation on that page):
 * [budget]    same tutorial page, budget-setting step: a KV budget B per
               layer, and pyramid-shaped allocation across layers (PyramidKV):
               fewer keys for shallow layers, more for deep ones.
-* [layout]    same tutorial page, RoPE paragraph: the rotation is applied to
-              queries and keys in LLaMA and Mistral, whose common
-              implementations pair element f with element f + d/2 ("half
-              split") rather than 2f with 2f + 1.
+* [layout]    the pages print only the interleaved pairing (x_2f, x_2f+1)
+              of the talk page's rotation equation.  Pairing element f with
+              element f + d/2 ("half split") is a storage layout the pages
+              give no formula for; it is supported as a reading, each pair
+              rotating by the printed matrix.
 * [paged]     same tutorial page, deployment paragraph: engines keep the KV
               cache in pages (PagedAttention in vLLM), each sequence's
               logical blocks mapped to physical pages by a table.

@@ -67,6 +67,10 @@ _lib.tri_last_error.argtypes = []
 _lib.tri_last_error.restype = ctypes.c_char_p
 _lib.tri_debug_set_wait_limit.argtypes = [ctypes.c_uint32]
 _lib.tri_debug_set_wait_limit.restype = ctypes.c_uint32
+_lib.tri_debug_set_resident_groups.argtypes = [ctypes.c_int32]
+_lib.tri_debug_set_resident_groups.restype = ctypes.c_int32
+_lib.tri_score_status.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
+_lib.tri_score_status.restype = ctypes.c_int
 
 class TriDecodeConfig(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_int32), ("interval", ctypes.c_int32),
@@ -133,7 +137,8 @@ EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_byte
            "tri_status_string", "tri_last_error", "tri_workspace_bytes_offsets",
            "tri_score_offsets", "tri_decode_create", "tri_decode_prefill", "tri_decode_append",
            "tri_decode_get_view", "tri_decode_destroy", "tri_trig_correlation_workspace_bytes",
-           "tri_trig_correlation", "tri_stream_probe", "tri_score_noalloc", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
+           "tri_trig_correlation", "tri_stream_probe", "tri_score_noalloc", "tri_score_status",
+           "tri_debug_set_resident_groups", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
            "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
            "tri_workspace_bytes_paged", "tri_debug_set_wait_limit")
 
@@ -292,6 +297,24 @@ def tri_stream_probe(src, sink, nbytes=None, stream=None):
     n = nbytes if nbytes is not None else src.numel() * src.element_size()
     st = _lib.tri_stream_probe(_ptr(src), int(n), _ptr(sink), _stream(stream))
     _check(st, "tri_stream_probe")
+
+
+TRI_SCORE_WAIT_GAVE_UP = 1
+
+
+def tri_score_status(workspace=None, stream=None) -> int:
+    """Flags of the last score call on `workspace` (None: tri_score_noalloc's
+    scratch): TRI_SCORE_WAIT_GAVE_UP if it gave up a bounded wait.  Waits for
+    the stream's queued work."""
+    flags = ctypes.c_uint32(0)
+    st = _lib.tri_score_status(_ptr(workspace), ctypes.byref(flags), _stream(stream))
+    _check(st, "tri_score_status")
+    return int(flags.value)
+
+
+def tri_debug_set_resident_groups(groups: int) -> int:
+    """Test hook: the planner's resident work-group count (0 = query the device)."""
+    return int(_lib.tri_debug_set_resident_groups(int(groups)))
 
 
 def tri_select_compact(shape: TriShape, cu_len, budget, scores, k, v, k_pos, kept_idx, k_out,

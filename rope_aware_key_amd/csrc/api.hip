@@ -27,70 +27,21 @@ tri_status fail(tri_status st, const std::string& msg) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// ---------------------------------------------------------------------------
-// Pinned staging for the per-call sequence plan.  One ring per device,
-// allocated on first use; a slot is reused only after the copy that last
-// read it has completed (its event).
-// ---------------------------------------------------------------------------
-constexpr int kSlots = 16;
-constexpr size_t kSlotBytes = 320 * 1024;  // 8192 sequences of 40-byte plan entries
-
-struct Staging {
-  std::mutex mu;
-  char* host = nullptr;
-  hipEvent_t ev[kSlots] = {};
-  bool used[kSlots] = {};
-  int next = 0;
-};
-
-std::mutex g_staging_mu;
-std::map<int, Staging*> g_staging;
-
-hipError_t get_staging(Staging** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(g_staging_mu);
-  auto it = g_staging.find(dev);
-  if (it != g_staging.end()) {
-    *out = it->second;
-    return hipSuccess;
-  }
-  Staging* st = new Staging();
-  e = hipHostMalloc((void**)&st->host, kSlots * kSlotBytes, hipHostMallocDefault);
-  if (e != hipSuccess) {
-    delete st;
-    return e;
-  }
-  for (int i = 0; i < kSlots; ++i) {
-    e = hipEventCreateWithFlags(&st->ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-  }
-  g_staging[dev] = st;
-  *out = st;
-  return hipSuccess;
+// Host tables of a call reach the device through kernel arguments (no
+// pinned staging, no process-wide ring; a call can be stream-captured).
+// Sequences (or (sequence, layer) pairs) one call may plan: 320 KB of
+// plan entries, 128 small write launches.
+constexpr int64_t kMaxSeqsPerCall = 8192;
+// Whether `stream` is being captured into a HIP graph.
+bool capturing(void* stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess &&
+         cs != hipStreamCaptureStatusNone;
 }
 
-// Copy `bytes` of host data to `dst` on `stream` through a pinned slot.
 hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;
-  Staging* st = nullptr;
-  hipError_t e = get_staging(&st);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(st->mu);
-  const int slot = st->next;
-  st->next = (st->next + 1) % kSlots;
-  if (st->used[slot]) {
-    e = hipEventSynchronize(st->ev[slot]);
-    if (e != hipSuccess) return e;
-  }
-  char* h = st->host + (size_t)slot * kSlotBytes;
-  std::memcpy(h, src, bytes);
-  e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(st->ev[slot], stream);
-  st->used[slot] = true;
-  return e;
+  return tri::launch_write_args(dst, src, bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -180,7 +131,7 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.om = om;
   if (S < 0) return fail(TRI_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
   if (S > 0 && !cu_len) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len is NULL");
-  if ((size_t)S * sizeof(SeqInfo) > kSlotBytes)
+  if ((int64_t)S > kMaxSeqsPerCall)
     return fail(TRI_ERR_UNSUPPORTED, "too many sequences in one call (max 8192)");
   p.S = S;
   p.L = sh->num_layers;
@@ -206,11 +157,20 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   }
   if (lay.in_pages) p.in_pg = *lay.in_pages;
   if (lay.out_pages) p.out_pg = *lay.out_pages;
-  // the fused kernel reads a 16-key block from one page
+  // The fused kernel reads a 16-key block from one page.  A unit's chunks
+  // must also stay within the work-groups the device holds at once: its
+  // waits need more than half that many resident, and capping a unit at
+  // the resident count (occupancy x CUs, when a device answers) keeps twice
+  // that margin, also on a partitioned or smaller device.
   p.fused = !om.max && tri::fused_supported(p.d, p.half) &&
-            (!p.in_pg.table || p.in_pg.page_shift >= 4) &&
-            (longest + tri::fused_chunk_keys(p.G, p.d) - 1) / tri::fused_chunk_keys(p.G, p.d) <=
-                tri::kFusedMaxUnitChunks;
+            (!p.in_pg.table || p.in_pg.page_shift >= 4);
+  if (p.fused) {
+    const int64_t ch = tri::fused_chunk_keys(p.G, p.d);
+    int64_t cap = tri::kFusedMaxUnitChunks;
+    const int resident = tri::fused_resident_groups(p.d, p.half, p.in_pg.table != nullptr, p.G);
+    if (resident > 0 && resident < cap) cap = resident;
+    p.fused = (longest + ch - 1) / ch <= cap;
+  }
   p.chunk = p.fused ? tri::fused_chunk_keys(p.G, p.d) : tri::kScoreChunk;
   for (int s = 0; s < S; ++s) {
     const int64_t n = cu_len[s + 1] - cu_len[s];
@@ -255,6 +215,9 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
     off = align_up(off + bytes, 256);
     return o;
   };
+  // the control words first, at a fixed place (word 1: the fused kernel's
+  // wait-bound flag, read by tri_score_status; select never writes there)
+  p.off_ctrl = take((size_t)tri::kCtrlHeader * sizeof(uint32_t));
   p.off_seq = take((size_t)S * sizeof(SeqInfo));
   const size_t after_seq = off;
   p.off_offsets = take(om.host ? (size_t)om.n * sizeof(double) : 0);
@@ -266,7 +229,6 @@ tri_status make_plan(const tri_shape* sh, int32_t S, const int64_t* cu_len,
   p.n_stat_slots = p.fused ? p.tickets * p.G * 2 : 0;
   p.off_stats = take((size_t)p.tickets * tri::kMaxGroup * 3 * sizeof(double));
   p.n_units = (int64_t)S * LH;
-  p.off_ctrl = take((size_t)tri::kCtrlHeader * sizeof(uint32_t));
   // The fused path keeps raw scores on chip; the generic path spills them.
   p.off_apack = take(om.max ? tri::max_offsets_operand_bytes(p.d, p.G, om.n, p.mp, p.n_units, p.tickets)
                             : tri::fused_operand_bytes(p.d, p.n_units));
@@ -300,6 +262,10 @@ const char* tri_status_string(tri_status s) {
 const char* tri_last_error(void) { return g_last_error.c_str(); }
 
 uint32_t tri_debug_set_wait_limit(uint32_t polls) { return tri::set_fused_wait_limit(polls); }
+
+int32_t tri_debug_set_resident_groups(int32_t groups) {
+  return tri::set_fused_resident_override(groups > 0 ? groups : 0);
+}
 
 size_t tri_workspace_bytes(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len) {
   Plan p;
@@ -417,12 +383,10 @@ namespace {
 hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const uint16_t* k,
                      const float* q_centre, const float* q_absmean, const float* q_R,
                      float* scores, float* raw_scores, double* head_stats, char* ws,
-                     hipStream_t s, bool inline_plan = false) {
+                     hipStream_t s) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
   double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
-  hipError_t e = inline_plan
-                     ? tri::launch_write_plan(p.seqs.data(), (int)p.seqs.size(), dseq, s)
-                     : upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
   if (e == hipSuccess)
     e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq, q_centre, q_absmean, q_R, doff,
@@ -499,8 +463,7 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 
-// workspace == nullptr with noalloc: the device's scratch array, the plan
-// table written through kernel arguments (no pinned staging either).
+// noalloc: the workspace is the device's scratch array.
 tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
                       const int32_t* cur_pos, const uint16_t* k, const float* q_centre,
                       const float* q_absmean, const float* q_R, const OffsetMode& om,
@@ -531,8 +494,7 @@ tri_status score_impl(const tri_shape* shape, int32_t num_seqs, const int64_t* c
   if (!workspace || workspace_bytes < need)
     return fail(TRI_ERR_WORKSPACE, "workspace missing or smaller than tri_workspace_bytes()");
   const hipError_t e = run_score(p, shape->rope_theta, om, k, q_centre, q_absmean, q_R, scores,
-                                 raw_scores, head_stats, (char*)workspace, (hipStream_t)stream,
-                                 noalloc);
+                                 raw_scores, head_stats, (char*)workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score: ") + hipGetErrorString(e));
   return TRI_OK;
 }
@@ -560,6 +522,24 @@ tri_status tri_score_noalloc(const tri_shape* shape, int32_t num_seqs, const int
   return score_impl(shape, num_seqs, cu_len, cur_pos, k, q_centre, q_absmean, q_R,
                     OffsetMode(), scores, raw_scores, head_stats, nullptr, 0, stream, nullptr,
                     true);
+}
+
+tri_status tri_score_status(const void* workspace, uint32_t* flags, void* stream) {
+  if (!flags) return fail(TRI_ERR_INVALID_ARGUMENT, "flags is NULL");
+  void* ws = const_cast<void*>(workspace);
+  if (!ws) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score status: ") + hipGetErrorString(e));
+  }
+  uint32_t word = 0;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(&word, (const char*)ws + sizeof(uint32_t), sizeof(word),
+                       hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, std::string("score status: ") + hipGetErrorString(e));
+  *flags = word ? TRI_SCORE_WAIT_GAVE_UP : 0u;
+  return TRI_OK;
 }
 
 tri_status tri_score_offsets(const tri_shape* shape, int32_t num_seqs, const int64_t* cu_len,
@@ -746,6 +726,9 @@ tri_status tri_decode_prefill(tri_decode* dec, const int64_t* cu_len, const int3
                               const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
                               void* stream) {
   if (!dec) return fail(TRI_ERR_INVALID_ARGUMENT, "driver is NULL");
+  if (capturing(stream))
+    return fail(TRI_ERR_UNSUPPORTED,
+                "the decode-loop driver may allocate and cannot be stream-captured");
   if (!cu_len || !cur_pos) return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len and cur_pos are required");
   const int S = dec->S;
   std::vector<int32_t> bud(S);
@@ -804,6 +787,9 @@ tri_status tri_decode_prefill(tri_decode* dec, const int64_t* cu_len, const int3
 tri_status tri_decode_append(tri_decode* dec, const uint16_t* k_new, const uint16_t* v_new,
                              const int32_t* pos_new, void* stream) {
   if (!dec) return fail(TRI_ERR_INVALID_ARGUMENT, "driver is NULL");
+  if (capturing(stream))
+    return fail(TRI_ERR_UNSUPPORTED,
+                "the decode-loop driver may allocate and cannot be stream-captured");
   if (!k_new || !v_new || !pos_new)
     return fail(TRI_ERR_INVALID_ARGUMENT, "k_new, v_new and pos_new are required");
   if (!aligned16(k_new) || !aligned16(v_new))
@@ -933,14 +919,15 @@ size_t tri_workspace_bytes_layers(const tri_shape* shape, int32_t num_seqs,
   // pseudo-sequences of one layer each: the plan table grows by L
   if (check_shape(shape) != TRI_OK || num_seqs < 0 || (num_seqs > 0 && !cu_len)) return 0;
   const int64_t S2 = (int64_t)num_seqs * shape->num_layers;
-  if ((size_t)S2 * sizeof(SeqInfo) > kSlotBytes) {
+  if (S2 > kMaxSeqsPerCall) {
     fail(TRI_ERR_UNSUPPORTED, "too many (sequence, layer) pairs in one call (max 8192)");
     return 0;
   }
   int64_t max_n = 0;
   for (int s = 0; s < num_seqs; ++s) max_n = std::max(max_n, cu_len[s + 1] - cu_len[s]);
   if (max_n > 0x7fffffff) return 0;
-  return align_up((size_t)S2 * sizeof(SeqInfo), 256) +
+  return align_up((size_t)tri::kCtrlHeader * sizeof(uint32_t), 256) +
+         align_up((size_t)S2 * sizeof(SeqInfo), 256) +
          tri::split_select_bytes(S2 * shape->num_kv_heads, (int)max_n);
 }
 
@@ -957,7 +944,7 @@ tri_status tri_select_compact_layers(const tri_shape* shape, int32_t num_seqs,
     return fail(TRI_ERR_INVALID_ARGUMENT, "cu_len and budget are required");
   const int L = shape->num_layers, Hkv = shape->num_kv_heads;
   const int64_t S2 = (int64_t)num_seqs * L;
-  if ((size_t)S2 * sizeof(SeqInfo) > kSlotBytes)
+  if (S2 > kMaxSeqsPerCall)
     return fail(TRI_ERR_UNSUPPORTED, "too many (sequence, layer) pairs in one call (max 8192)");
   std::vector<int64_t> cu2(S2 + 1, 0), in0(S2), out0(S2);
   std::vector<int32_t> bud2(S2);

@@ -12,6 +12,8 @@
 //   Re(E[q_f] C_f exp(i omega_f p_q) conj(k'_f)),  C_f = mean_delta exp(i omega_f delta),
 // so one complex coefficient per (sequence, query head, band) carries the
 // whole offset mean and the key position drops out.
+#include <cstring>
+
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -312,24 +314,30 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqI
   return hipGetLastError();
 }
 
-// A launch's sequence table written from the kernel arguments (64 entries
-// per launch), for callers that pass no host staging: the entries travel
-// with the launch, so nothing on the host has to outlive the call.
-struct PlanArgs {
-  SeqInfo e[kPlanInline];
+// Host tables of a call (the sequence plan, an offset set, decode items)
+// written to device memory from kernel arguments, 2560 bytes per launch:
+// the data travels with the launch, so nothing on the host has to outlive
+// the call, no staging memory is held, and the copy is an ordinary kernel
+// node under stream capture.
+struct ArgWords {
+  uint32_t w[kArgWords];
 };
 
-__global__ __launch_bounds__(64) void write_plan_kernel(PlanArgs a, int n, SeqInfo* __restrict__ dst) {
-  const int i = threadIdx.x;
-  if (i < n) dst[i] = a.e[i];
+__global__ __launch_bounds__(256) void write_args_kernel(ArgWords a, int n,
+                                                         uint32_t* __restrict__ dst) {
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = a.w[i];
 }
 
-hipError_t launch_write_plan(const SeqInfo* host, int S, SeqInfo* dst, hipStream_t st) {
-  for (int s0 = 0; s0 < S; s0 += kPlanInline) {
-    const int n = S - s0 < kPlanInline ? S - s0 : kPlanInline;
-    PlanArgs a = {};
-    for (int i = 0; i < n; ++i) a.e[i] = host[s0 + i];
-    hipLaunchKernelGGL(write_plan_kernel, dim3(1), dim3(kPlanInline), 0, st, a, n, dst + s0);
+hipError_t launch_write_args(void* dst, const void* host, size_t bytes, hipStream_t st) {
+  if (bytes % 4 != 0) return hipErrorInvalidValue;
+  const size_t words = bytes / 4;
+  const uint32_t* src = static_cast<const uint32_t*>(host);
+  uint32_t* out = static_cast<uint32_t*>(dst);
+  for (size_t w0 = 0; w0 < words; w0 += kArgWords) {
+    const int n = (int)(words - w0 < (size_t)kArgWords ? words - w0 : kArgWords);
+    ArgWords a;
+    std::memcpy(a.w, src + w0, (size_t)n * 4);
+    hipLaunchKernelGGL(write_args_kernel, dim3(1), dim3(256), 0, st, a, n, out + w0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

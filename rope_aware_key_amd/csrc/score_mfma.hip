@@ -64,6 +64,9 @@
 //    below that.  A spin bound turns a broken invariant into an error flag
 //    instead of a hang.
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "tri_internal.hpp"
 
@@ -213,7 +216,9 @@ constexpr int kTileChunks = 16 * 9;
 struct Shared {
   uint4 tile[kFusedWaves][kTileChunks];  // the waves' staging tiles (streaming only)
   float2 zm[kMaxGroup];                  // per head: z = raw * zm.x + zm.y
-  int ticket;
+  int ticket;       // a ticket claimed between chunks, for the work-group
+  int next_ticket;  // the ticket claimed ahead, posted after streaming (its
+                    // own slot: waves may still be reading `ticket` then)
 };
 
 // MFMA operands of one unit, packed by pack_operands_kernel in lane order:
@@ -650,14 +655,14 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     if (have)
       chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid,
                                     sh.tile[threadIdx.x >> 6]);
-    if (ahead && threadIdx.x == 0) sh.ticket = (int)next;
+    if (ahead && threadIdx.x == 0) sh.next_ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
     // go unused.  The ring and operands are reloaded on every path so their
     // old contents are dead from here on.
     Chunk nk = ck;
     if (ahead) {
-      t = __builtin_amdgcn_readfirstlane(sh.ticket);
+      t = __builtin_amdgcn_readfirstlane(sh.next_ticket);
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t, ck.s);
     }
     if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
@@ -771,6 +776,71 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
                      lds, st, seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg, pg.table, cs, ctrl,
                      g_wait_limit.load(std::memory_order_relaxed), scores, raw, hs);
   return hipGetLastError();
+}
+
+// Work-groups of the fused kernel the current device holds at once for a
+// shape (occupancy at the shape's LDS size x CUs), cached per device and
+// shape; -1 when no device answers.  A test hook may override the value.
+static std::atomic<int> g_resident_override{0};
+
+int set_fused_resident_override(int groups) { return g_resident_override.exchange(groups); }
+
+template <int STEPS, bool HALF, bool PAGED>
+static int resident_t(size_t lds) {
+  const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF, PAGED>);
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds) !=
+      hipSuccess)
+    return -1;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds) !=
+          hipSuccess)
+    return -1;
+  return cus * (per_cu < 1 ? 1 : per_cu);
+}
+
+int fused_resident_groups(int d, bool half, bool paged, int G) {
+  const int forced = g_resident_override.load();
+  if (forced > 0) return forced;
+  int count = 0, dev = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1 || hipGetDevice(&dev) != hipSuccess)
+    return -1;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, bool, bool, int>, int> cache;
+  const auto key = std::make_tuple(dev, d, half, paged, G);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const size_t lds = 2 * (size_t)G * (fused_chunk_keys(G, d) + kRawPad) * sizeof(float);
+  int r = -1;
+#define TRI_RES(n, h, pgd) \
+  case n:                  \
+    r = resident_t<n, h, pgd>(lds); \
+    break;
+#define TRI_RES_ALL(pgd)                                                                  \
+  if (half) {                                                                             \
+    switch (d / 32) { TRI_RES(2, true, pgd) TRI_RES(4, true, pgd) TRI_RES(6, true, pgd)   \
+                      TRI_RES(8, true, pgd) default: break; }                             \
+  } else {                                                                                \
+    switch (d / 32) { TRI_RES(1, false, pgd) TRI_RES(2, false, pgd) TRI_RES(3, false, pgd) \
+                      TRI_RES(4, false, pgd) TRI_RES(5, false, pgd) TRI_RES(6, false, pgd) \
+                      TRI_RES(7, false, pgd) TRI_RES(8, false, pgd) default: break; }     \
+  }
+  if (paged) {
+    TRI_RES_ALL(true)
+  } else {
+    TRI_RES_ALL(false)
+  }
+#undef TRI_RES_ALL
+#undef TRI_RES
+  if (r > 0) {
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = r;
+  }
+  return r;
 }
 
 // Half split needs an even number of 32-wide steps (both parts of a band

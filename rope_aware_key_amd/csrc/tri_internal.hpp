@@ -70,8 +70,8 @@ __device__ __forceinline__ int64_t paged_row_lg(const Pages& pg, int s, int lg, 
 
 // RoPE pair layouts.  Band f of a d-vector is (x_{2f}, x_{2f+1})
 // (interleaved, the talk page's rotation equation) or (x_f, x_{f+d/2})
-// (half split, the layout of the LLaMA/Mistral implementations the
-// tutorial page's RoPE paragraph names).
+// (half split: a storage layout the pages print no formula for, supported
+// as a reading; each pair still rotates by the printed matrix).
 __host__ __device__ __forceinline__ int elem_band(int e, int d, bool half) {
   return half ? (e < (d >> 1) ? e : e - (d >> 1)) : (e >> 1);
 }
@@ -157,8 +157,15 @@ int fused_chunk_keys(int G, int d);
 // (polls per slot; default 2^22); returns the previous bound.
 uint32_t set_fused_wait_limit(uint32_t polls);
 // Most chunks one unit may have on the fused path.  Its waits need more
-// than half that many work-groups resident (every CU holds at least one).
+// than half that many work-groups resident; the planner also caps a unit at
+// the device's resident work-groups (fused_resident_groups), twice that
+// margin.
 constexpr int kFusedMaxUnitChunks = 384;
+// Fused-kernel work-groups the current device holds at once for a shape
+// (occupancy x CUs), or -1 when no device answers; a positive override
+// (test hook) replaces the query.  Returns / sets process-wide values.
+int fused_resident_groups(int d, bool half, bool paged, int G);
+int set_fused_resident_override(int groups);
 // Workspace bytes of the fused path's packed MFMA operands.
 size_t fused_operand_bytes(int d, int64_t units);
 
@@ -234,10 +241,11 @@ hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t 
 hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
                           float* scores, hipStream_t st);
 
-// Sequence-table entries one write_plan launch carries in its arguments.
-constexpr int kPlanInline = 64;
-// Writes host[0, S) to dst (device) through kernel arguments, no staging.
-hipError_t launch_write_plan(const SeqInfo* host, int S, SeqInfo* dst, hipStream_t st);
+// 32-bit words one write_args launch carries in its arguments (2560 bytes).
+constexpr int kArgWords = 640;
+// Writes `bytes` (a multiple of 4) of host memory to dst (device) through
+// kernel arguments: no staging memory, host data free once this returns.
+hipError_t launch_write_args(void* dst, const void* host, size_t bytes, hipStream_t st);
 
 // Read-bandwidth probe over bytes (a multiple of 16) of src; XORs into *sink.
 hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);

@@ -105,6 +105,7 @@ def gpu_run(case: Case, raw=True, stats=True, compact=True, scores_in=None):
                          case.v if compact else None, case.k_pos if compact else None, kept,
                          k_out, v_out, pos_out, workspace=ws)
     torch.cuda.synchronize()
+    res["workspace"] = ws
     res.update(kept=kept[:out_rows], k_out=None if k_out is None else k_out[:out_rows],
                v_out=None if v_out is None else v_out[:out_rows],
                pos_out=None if pos_out is None else pos_out[:out_rows])

@@ -35,7 +35,8 @@ def test_header_symbols_exported():
                           "tri_select_compact_layers", "tri_score_paged",
                           "tri_select_compact_paged", "tri_workspace_bytes_paged",
                           "tri_debug_set_wait_limit", "tri_stream_probe",
-                          "tri_score_noalloc"}
+                          "tri_score_noalloc", "tri_score_status",
+                          "tri_debug_set_resident_groups"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
@@ -350,7 +351,7 @@ def test_select_compact_layers_argument_checks():
     cu = [0, 50, 80]
     bud = [[10, 20, 30], [5, 5, 5]]
     need = R.tri_workspace_bytes_layers(sh, cu)
-    assert need == 256                                 # 6 plan entries of 40 bytes
+    assert need == 512                 # control words, then 6 plan entries of 40 bytes
 
     def sel(budget=bud, **kw):
         args = dict(scores=_Fake(), k=_Fake(), v=_Fake(), k_pos=_Fake(), kept=_Fake(),
@@ -524,3 +525,31 @@ def test_noalloc_rejects_calls_past_its_scratch():
     small = R.make_shape(128, 7, 1, 1)
     a = (_Fake(FAKE + 4), None, _Fake(), _Fake(), _Fake(), _Fake())
     assert _status(R.tri_score_noalloc, small, cu, cp, *a, stream=0) == ST["INVALID"]
+
+
+def test_fused_routing_follows_resident_work_groups():
+    """The planner keeps a unit on the fused path only while its chunks
+    number at most the work-groups the device holds at once.  With 96
+    resident (a 32-CU partition, three per CU) a unit of 97 chunks moves to
+    the generic path, whose workspace spills the raw scores; 96 chunks stay
+    fused.  The device's own count (three per CU on 256 CUs, or no device
+    here) leaves both fused."""
+    sh = R.make_shape(128, 7, 1, 1)
+    G = 7
+    ch = None
+    for c in range(64, 1025, 64):   # the fused chunk size: where 384 chunks stop fitting
+        if R.tri_workspace_bytes(sh, [0, c * 384 + 1]) >= (c * 384 + 1) * G * 4:
+            if R.tri_workspace_bytes(sh, [0, c * 384]) < c * 384 * G * 4:
+                ch = c
+    assert ch is not None
+    n96, n97 = 96 * ch, 96 * ch + 1
+    base96, base97 = R.tri_workspace_bytes(sh, [0, n96]), R.tri_workspace_bytes(sh, [0, n97])
+    assert base97 < n97 * G * 4                      # fused at the device's count
+    prev = R.tri_debug_set_resident_groups(96)
+    try:
+        assert R.tri_workspace_bytes(sh, [0, n96]) == base96
+        assert R.tri_workspace_bytes(sh, [0, n97]) >= n97 * G * 4   # generic: raw spill
+    finally:
+        R.tri_debug_set_resident_groups(prev)
+    assert prev == 0
+    assert R.tri_workspace_bytes(sh, [0, n97]) == base97

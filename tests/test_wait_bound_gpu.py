@@ -7,8 +7,9 @@ finalizer give up on a slot still unpublished at its second look, so the
 outcome tri_score documents for a reached bound can be checked while every
 kernel exits normally: raw scores unchanged, heads given up on read
 (NaN, 0) in head_stats and drop out of the group maximum (-inf where all
-of them do), every other statistic bit-identical, and the default bound
-restoring exact results on the next call.
+of them do), every other statistic bit-identical, the call's status word
+raised (tri_score_status), and the default bound restoring exact results
+and a clear status on the next call.
 """
 import numpy as np
 import pytest
@@ -28,13 +29,17 @@ def test_forced_wait_bound_outcome():
     # other chunks of their unit are still streaming
     case = synth.workload_case("long_reasoning", device=DEV, S=2, L=2, n=32768, B=2048)
     ref = gpu_run(case, raw=True, stats=True, compact=False)
+    assert R.tri_score_status(ref["workspace"]) == 0
     prev = R.tri_debug_set_wait_limit(0)
     try:
         res = gpu_run(case, raw=True, stats=True, compact=False)
     finally:
         R.tri_debug_set_wait_limit(prev)
     assert prev == 1 << 22
+    # the call reports the wait it gave up (the status word of its workspace)
+    assert R.tri_score_status(res["workspace"]) == R.TRI_SCORE_WAIT_GAVE_UP
     again = gpu_run(case, raw=True, stats=True, compact=False)
+    assert R.tri_score_status(again["workspace"]) == 0
     for key in ("scores", "raw", "head_stats"):
         assert torch.equal(again[key], ref[key]), key
 
