@@ -2,10 +2,13 @@
 library (via the binding) and evaluate units with the CPU oracle."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
 import oracle as O
+from checks import check_raw, check_scores, head_stat_errors, score_error, z_floor  # noqa: F401
 from synth import Case
 
 
@@ -167,36 +170,6 @@ def oracle_unit(case: Case, s, l, g, factored=False, stats=None, offsets=None,
     return start, n, score, S, mu, sigma
 
 
-def z_floor(S_ref: np.ndarray, sigma_ref: np.ndarray) -> float:
-    """Resolution of a z-score computed from fp32 raw scores: the raw values
-    carry a few ulps of |S~|, so z = (S~ - mu) / sigma carries about
-    eps * |S~| / sigma.  64 ulps (2^-18) of the unit's largest |S~_h| / sigma_h;
-    0 for a head with sigma = 0 (its z is 0 on both sides)."""
-    ratios = [np.max(np.abs(S_ref[h])) / sigma_ref[h] for h in range(len(sigma_ref))
-              if sigma_ref[h] > 0 and S_ref.shape[1] > 0]
-    return 2.0 ** -18 * max(ratios) if ratios else 0.0
-
-
-def check_scores(gpu_scores: np.ndarray, ref: np.ndarray, what="", floor=0.0):
-    """|gpu - ref| <= max(1e-4 * max(1, |ref|), floor): z-scores are in units
-    of sigma; floor (z_floor) covers units whose spread is below the fp32
-    resolution of their raw scores."""
-    err = np.abs(gpu_scores.astype(np.float64) - ref) / np.maximum(1.0, np.abs(ref))
-    bar = np.maximum(1e-4, floor / np.maximum(1.0, np.abs(ref)))
-    worst = float(np.max(err / bar)) * 1e-4 if err.size else 0.0
-    assert worst <= 1e-4, f"{what}: worst scaled score error {worst:.3e} (of the 1e-4 bar)"
-    return worst
-
-
-def check_raw(gpu_raw: np.ndarray, S_ref: np.ndarray, sigma_ref: np.ndarray, what=""):
-    """Raw S~_h(i): |gpu - ref| <= 1e-4 * max(|ref|, sigma_h)."""
-    scale = np.maximum(np.abs(S_ref), sigma_ref[:, None])
-    err = np.abs(gpu_raw.T.astype(np.float64) - S_ref) / scale
-    worst = float(np.max(err)) if err.size else 0.0
-    assert worst <= 1e-4, f"{what}: worst scaled raw error {worst:.3e}"
-    return worst
-
-
 def units_of(case: Case):
     L, H = case.shape.num_layers, case.shape.num_kv_heads
     return [(s, l, g) for s in range(case.num_seqs) for l in range(L) for g in range(H)]
@@ -276,3 +249,75 @@ def gpu_score_paged(case: Case, pool, offsets=None, reduce="mean", raw=False, st
     torch.cuda.synchronize()
     return dict(scores=scores[:rows], raw=None if raw_t is None else raw_t[:rows], head_stats=hs)
 
+
+
+def compare_units_pool(case: Case, res, units, min_bytes_free=None):
+    """Every unit in `units` against the factored oracle, in worker processes
+    (tests/oracle_pool.py): scores (with the z_floor bar) and (mu, sigma).
+    The case and the GPU's results go to memory-mapped files the workers
+    read.  Returns (worst score error, list of floors); asserts per unit."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import checks
+    import oracle_pool
+
+    L, H, G = case.shape.num_layers, case.shape.num_kv_heads, case.shape.group
+    arrays = {
+        "k_pos": case.k_pos, "scores": res["scores"], "head_stats": res["head_stats"],
+        "q_centre": case.q_centre, "q_absmean": case.q_absmean, "q_R": case.q_R,
+    }
+    need = case.k.numel() * 2 + sum(t.numel() * t.element_size() for t in arrays.values())
+    base = "/dev/shm" if shutil.disk_usage("/dev/shm").free > 1.2 * need else None
+    tmp = tempfile.mkdtemp(prefix="tri_oracle_", dir=base)
+    try:
+        files = {}
+        path = os.path.join(tmp, "k.bin")
+        mm = np.memmap(path, dtype=np.uint16, mode="w+", shape=tuple(case.k.shape))
+        step = max(1, (256 << 20) // max(1, case.k.shape[1] * 2))
+        for a in range(0, case.k.shape[0], step):
+            mm[a:a + step] = case.k[a:a + step].cpu().numpy().view(np.uint16)
+        mm.flush()
+        del mm
+        files["k"] = (path, "uint16", list(case.k.shape))
+        for name, t in arrays.items():
+            a = t.cpu().numpy()
+            path = os.path.join(tmp, name + ".bin")
+            m = np.memmap(path, dtype=a.dtype, mode="w+", shape=a.shape)
+            m[...] = a
+            m.flush()
+            files[name] = (path, a.dtype.str, list(a.shape))
+        cp = np.asarray(case.cur_pos, np.int64)
+        path = os.path.join(tmp, "cur_pos.bin")
+        m = np.memmap(path, dtype=np.int64, mode="w+", shape=cp.shape)
+        m[...] = cp
+        m.flush()
+        files["cur_pos"] = (path, "<i8", list(cp.shape))
+        meta = dict(G=G, d=case.shape.head_dim, theta=case.shape.rope_theta, layout=layout_of(case))
+        tasks = []
+        for (s, l, g) in units:
+            start, n = case.unit_rows(s, l, g)
+            tasks.append(((s * L + l) * H + g, s, l, g, start, n))
+        nw = oracle_pool.workers()
+        batch = max(1, len(tasks) // (nw * 8))
+        chunks = [tasks[i:i + batch] for i in range(0, len(tasks), batch)]
+        results = []
+        with cf.ProcessPoolExecutor(nw, mp_context=mp.get_context("spawn"),
+                                    initializer=oracle_pool.attach,
+                                    initargs=(files, meta)) as ex:
+            for part in ex.map(oracle_pool.score_units, chunks):
+                results.extend(part)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    worst, floors = 0.0, []
+    for (u, err, floor, e_mu, e_sig) in results:
+        checks.note_floor(floor)
+        floors.append(floor)
+        assert err <= 1e-4, f"unit {u}: worst scaled score error {err:.3e} (of the 1e-4 bar)"
+        assert e_mu <= 1.0 and e_sig <= 1.0, f"unit {u}: head stats off ({e_mu:.2f}, {e_sig:.2f} of their bars)"
+        worst = max(worst, err)
+    print(f"{len(results)} units against the oracle on {oracle_pool.workers()} processes: "
+          f"worst {worst:.2e}, floors above 1e-4: {sum(f > 1e-4 for f in floors)}", flush=True)
+    return worst, floors
