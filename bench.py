@@ -127,7 +127,9 @@ def copy_probe(reps=10):
 def summarize(prof_dir, out, cmd):
     """Turn a rocprofv3 --stats / --pmc CSV directory into a short text summary."""
     import csv
-    lines = [f"# rocprofv3 summary: {os.path.basename(out)}", "", f"command: `{cmd}`", ""]
+    lines = [f"# rocprofv3 summary: {os.path.basename(out)}", "", f"command: `{cmd}`", "",
+             f"kernel_source_hash: `{kernel_source_hash()}` (score_mfma.hip, calib.hip, "
+             f"tri_internal.hpp as built for this run)", ""]
     for path in sorted(glob.glob(os.path.join(prof_dir, "**", "*kernel_stats.csv"), recursive=True)):
         lines += ["kernel stats (durations in microseconds):", "",
                   "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
@@ -169,8 +171,32 @@ TRAFFIC_RUNS = {
                                  "python3 bench.py --copy-probe"),
     "copy_write": ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- "
                                  "python3 bench.py --copy-probe"),
+    "probe_fetch": ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- "
+                                  "python3 bench.py --stream-probe"),
 }
-SCORE_KERNELS = ("tri::prologue_kernel", "tri::pack_operands_kernel", "tri::score_fused_kernel")
+SCORE_KERNELS = ("tri::write_args_kernel", "tri::prologue_kernel", "tri::pack_operands_kernel",
+                 "tri::score_fused_kernel")
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_long_reasoning_32k_to_2048.md")
+
+
+def trace_avg_us(kernel_prefix):
+    """Average duration (us) of a kernel in the committed rocprofv3 trace of
+    the 32K->2048 bench run, if that trace was taken on the current kernel
+    sources; else None."""
+    try:
+        text = open(TRACE_FILE).read()
+    except OSError:
+        return None
+    if f"kernel_source_hash: `{kernel_source_hash()}`" not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0].startswith(kernel_prefix):
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
 
 
 def counter_means(run_dir, counter):
@@ -188,14 +214,18 @@ def counter_means(run_dir, counter):
 
 
 def write_traffic(run_root, out):
-    """HBM bytes per tri_score call from the four counter runs of
-    TRAFFIC_RUNS under run_root.  FETCH_SIZE and WRITE_SIZE are scaled by
-    what they read for the copy probe, which moves exactly COPY_PROBE_BYTES
-    each way per dispatch."""
+    """HBM bytes per tri_score call from the counter runs of TRAFFIC_RUNS
+    under run_root.  FETCH_SIZE is scaled by what it reads for the stream
+    probe, which reads exactly STREAM_PROBE_BYTES per dispatch with the
+    score kernel's load pattern (16-byte non-temporal loads covering whole
+    128-byte lines); WRITE_SIZE by what it reads for the copy probe, which
+    writes exactly COPY_PROBE_BYTES per dispatch.  The copy probe's fetch
+    factor is kept beside it as a cross-check."""
     means = {sub: counter_means(os.path.join(run_root, sub), c) for sub, (c, _) in TRAFFIC_RUNS.items()}
     true_kib = COPY_PROBE_BYTES / 1024.0
-    # the copy probe's copies are the dispatches with the largest reading
-    fetch_scale = true_kib / max(means["copy_fetch"].values())
+    # the probes' own kernels are the dispatches with the largest reading
+    copy_fetch_scale = true_kib / max(means["copy_fetch"].values())
+    fetch_scale = (STREAM_PROBE_BYTES / 1024.0) / max(means["probe_fetch"].values())
     write_scale = true_kib / max(means["copy_write"].values())
     raw = {}
     fetch = write = 0.0
@@ -211,7 +241,11 @@ def write_traffic(run_root, out):
                 "4 KV heads, 28 q heads, d 128, batch 8): prologue + operand pack + fused score kernel",
         "kernel_source_hash": kernel_source_hash(),
         "fetch_scale": fetch_scale,
+        "fetch_scale_from": "stream probe (read-only, the score kernel's load pattern)",
+        "copy_fetch_scale": copy_fetch_scale,
         "write_scale": write_scale,
+        "stream_probe_kib": {"FETCH_SIZE": max(means["probe_fetch"].values()),
+                             "true": STREAM_PROBE_BYTES / 1024.0},
         "copy_probe_kib": {"FETCH_SIZE": max(means["copy_fetch"].values()),
                            "WRITE_SIZE": max(means["copy_write"].values()), "true_each": true_kib},
         "raw_kib_per_dispatch": raw,
@@ -300,62 +334,106 @@ def algorithmic_bytes(case, budgets=None):
     return keys, score, sel
 
 
-def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="interleaved",
-                 factored=False):
-    """The oracle as it stands (fp64) on whole units of the same workload,
-    one after another in (layer, KV head) order of sequence 0, on one host
-    thread (with the same offset set and reduction as the GPU line), until
-    max_seconds.  factored=False: the term-by-term definition (the
-    baseline); factored=True: the oracle's factored form of the same score
-    (one dot product per head), the faster CPU reference."""
+def _oracle_unit_job(job):
+    """One unit through the oracle as it stands (fp64 score, z-score, max,
+    top-B, gather), on one thread; runs in a worker process of cpu_baseline.
+    Returns (keys, seconds)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
-    om = O.rope_omega(case.shape.head_dim, case.shape.rope_theta)
-    G = case.shape.group
-    keys = 0
-    units = 0
+    (kbits, vrows, pos, p_q, centre, absmean, Rr, d, theta, budget, reduce, layout, factored,
+     offsets) = job
+    om = O.rope_omega(d, theta)
     t0 = time.perf_counter()
-    done = False
     with threadpool_limits(limits=1):
-        for l in range(case.shape.num_layers):
-            for g in range(case.shape.num_kv_heads):
-                start, n = case.unit_rows(0, l, g)
-                kbits = case.k[start:start + n].cpu().numpy().view(np.uint16)
-                pos = case.k_pos[start:start + n].cpu().numpy().astype(np.float64)
-                vrows = case.v[start:start + n].cpu().numpy()
-                hs = slice(g * G, (g + 1) * G)
-                qc = case.q_centre[l, hs].cpu().double().numpy()
-                t_unit = time.perf_counter()
-                score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, float(case.cur_pos[0]),
-                                      qc[..., 0] + 1j * qc[..., 1],
-                                      case.q_absmean[l, hs].cpu().double().numpy(),
-                                      case.q_R[l, hs].cpu().double().numpy(), om,
-                                      reduce=reduce, layout=layout, factored=factored,
-                                      **({} if offsets is None else {"offsets": offsets}))[0]
-                kept = O.select_topb(score.astype(np.float32), int(case.budget[0]))
-                O.compact_rows(kbits, kept)
-                O.compact_rows(vrows, kept)
-                O.compact_rows(pos, kept)
-                keys += n
+        score = O.unit_scores(O.bf16_bits_to_f64(kbits), pos, p_q, centre, absmean, Rr, om,
+                              reduce=reduce, layout=layout, factored=factored,
+                              **({} if offsets is None else {"offsets": offsets}))[0]
+        kept = O.select_topb(score.astype(np.float32), budget)
+        O.compact_rows(kbits, kept)
+        O.compact_rows(vrows, kept)
+        O.compact_rows(pos, kept)
+    return kbits.shape[0], time.perf_counter() - t0
+
+
+def oracle_workers():
+    """Worker processes for the oracle baseline: the host cores this process
+    may run on, at most 16 (one GPU's CPU share on a shared host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(case, max_seconds=30.0, offsets=None, reduce="mean", layout="interleaved",
+                 factored=False):
+    """The oracle as it stands (fp64) on whole units of the same workload, in
+    (sequence, layer, KV head) order, one unit per worker process at a time
+    over oracle_workers() processes (one thread each), with the same offset
+    set and reduction as the GPU line, until max_seconds of wall time.
+    Returns the aggregate keys/s over that wall time and the time the whole
+    workload would take at that rate.  factored=False: the term-by-term
+    definition (the baseline); factored=True: the oracle's factored form of
+    the same score (one dot product per head), the faster CPU reference."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    G = case.shape.group
+    L, H = case.shape.num_layers, case.shape.num_kv_heads
+    order = [(s, l, g) for s in range(case.num_seqs) for l in range(L) for g in range(H)]
+    nw = oracle_workers()
+
+    def job(s, l, g):
+        start, n = case.unit_rows(s, l, g)
+        hs = slice(g * G, (g + 1) * G)
+        qc = case.q_centre[l, hs].cpu().double().numpy()
+        return (case.k[start:start + n].cpu().numpy().view(np.uint16),
+                case.v[start:start + n].cpu().numpy(),
+                case.k_pos[start:start + n].cpu().numpy().astype(np.float64),
+                float(case.cur_pos[s]), qc[..., 0] + 1j * qc[..., 1],
+                case.q_absmean[l, hs].cpu().double().numpy(),
+                case.q_R[l, hs].cpu().double().numpy(), case.shape.head_dim,
+                case.shape.rope_theta, int(case.budget[s]), reduce, layout, factored,
+                None if offsets is None else np.asarray(offsets, np.float64))
+
+    keys = units = 0
+    nxt = 0
+    with cf.ProcessPoolExecutor(nw, mp_context=mp.get_context("spawn")) as ex:
+        ex.submit(time.sleep, 0).result()    # workers up before the clock starts
+        t0 = time.perf_counter()
+        pending = set()
+        while nxt < len(order) and len(pending) < 2 * nw:
+            pending.add(ex.submit(_oracle_unit_job, job(*order[nxt])))
+            nxt += 1
+        while pending:
+            done, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            for f in done:
+                k, _ = f.result()
+                keys += k
                 units += 1
-                now = time.perf_counter()
-                if now - t0 > max_seconds or now - t_unit > max_seconds / 2:
-                    done = True
-                    break
-            if done:
-                break
-    dt = time.perf_counter() - t0
+            if time.perf_counter() - t0 < max_seconds:
+                while nxt < len(order) and len(pending) < 2 * nw:
+                    pending.add(ex.submit(_oracle_unit_job, job(*order[nxt])))
+                    nxt += 1
+            elif pending:
+                # past the budget: count only what is already running, drop the rest
+                for f in pending:
+                    f.cancel()
+                pending = {f for f in pending if not f.cancelled()}
+        dt = time.perf_counter() - t0
+    rate = keys / dt
+    total_keys = case.total_rows()
     how = ("factored fp64 score (one dot product per head)" if factored
            else "term-by-term fp64 score")
-    return {"value": keys / dt, "unit": "keys/s", "cores": 1,
+    return {"value": rate, "unit": "keys/s", "cores": nw,
             "kind": "oracle (factored)" if factored else "oracle",
-            "sample": f"{units} unit(s) of sequence 0 in (layer, KV head) order, {n} keys each, "
-                      f"G={G}: {how} ({reduce} over "
+            "extrapolated_s": total_keys / rate,
+            "sample": f"{units} whole unit(s) in (sequence, layer, KV head) order on {nw} worker "
+                      f"processes, one thread each ({len(os.sched_getaffinity(0))} host cores "
+                      f"visible), G={G}: {how} ({reduce} over "
                       f"{len(offsets) if offsets is not None else 17} offsets), z-score, max, "
-                      f"top-B, gather; "
-                      f"{dt:.1f} s"}
+                      f"top-B, gather; {dt:.1f} s wall; extrapolated_s = the whole workload "
+                      f"({total_keys} keys) at this rate"}
 
 
 def decode_cpu_baseline(case, tokens_k, tokens_v, B, interval, sink, recent, max_seconds=30.0):
@@ -889,8 +967,18 @@ def main():
                      and not variant
                      and args.rope_layout == "interleaved" else None,
                      "algorithmic_bytes_per_launch": b_score,
-                     "launch": "tri_score call: prologue + operand pack + fused score kernel"},
+                     "launch": "tri_score call: plan write, prologue, operand pack, fused score "
+                               "kernel",
+                     "timing": "achieved: HIP events around each tri_score call in the timed "
+                               "steps, on the stream the kernels run on; frac_trace: the fused "
+                               "kernel's average duration in the committed rocprofv3 trace of "
+                               "this build (profiles/), null if that trace is of other sources"},
     }
+    if args.workload == "long_reasoning" and not variant and args.rope_layout == "interleaved":
+        t_us = trace_avg_us("tri::score_fused_kernel")
+        out["roofline"]["trace_avg_us"] = t_us
+        out["roofline"]["frac_trace"] = (b_score / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBPS
+                                         if t_us else None)
     copy_gbps = device_copy_gbps()
     out["device_copy_gbps"] = copy_gbps
     out["hbm_frac_of_device_copy"] = gbps / copy_gbps

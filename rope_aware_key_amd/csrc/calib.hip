@@ -261,9 +261,11 @@ __global__ __launch_bounds__(256) void prologue_kernel(
   if (idx < n_stat_slots)
     reinterpret_cast<unsigned long long*>(stat_slots)[idx] = kStatSentinel;
   // C_f = mean over the offsets of exp(i omega_f delta), once per band per
-  // block (F <= 128)
+  // block (F <= 128), in the blocks that form P (the others only reset the
+  // statistics slots)
   __shared__ double2 cf[kMaxHeadDim / 2];
-  for (int f = threadIdx.x; f < F; f += blockDim.x) {
+  const bool forms_p = (int64_t)blockIdx.x * blockDim.x < n_stat;
+  for (int f = threadIdx.x; forms_p && f < F; f += blockDim.x) {
     const double omega = pow(theta, -2.0 * (double)f / (double)d);
     double cr = 1.0, ci = 0.0;
     if (fold) {
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     }
     cf[f] = make_double2(cr, ci);
   }
-  __syncthreads();
+  if (forms_p) __syncthreads();  // block-uniform
   if (idx < n_stat) {
     const int f = (int)(idx % F);
     const double cr = cf[f].x, ci = cf[f].y;
