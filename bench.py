@@ -291,13 +291,14 @@ def max_mode_flops(case, n_offsets):
     """Per-key MFMA work of the max-over-offsets kernel: the method's dot
     products (2*G*|D|*d flops, fp32-equivalent) and the bf16 MFMA flops the
     kernel issues for them.  Issued work follows the library's plan: per 16
-    keys and pass, tiles*d/32*3 trig MFMAs (three bf16 terms per
+    keys and pass, tiles*d/32*2 trig MFMAs (two bf16 terms per
     coefficient) and d/32*3 norm MFMAs, 16*16*32*2 flops each; tiles hold the
     (head, offset) rows with each head's rows rounded up to 4 (one lane
-    slot) or, when one head exceeds the LDS budget, to 16 (all four)."""
+    slot) or, when one head exceeds the LDS budget, to 16 (all four).  The
+    LDS budget holds the norm operands (three terms per step) and the tiles."""
     G, d = case.shape.group, case.shape.head_dim
     steps = d // 32
-    max_tiles = (160 * 1024) // (steps * 3 * 64 * 16) - 1
+    max_tiles = (160 * 1024 - steps * 3 * 64 * 16) // (steps * 2 * 64 * 16)
     tph = (n_offsets + 3) // 4
     if tph <= max_tiles:
         hp_max = min(G, 4 * (max_tiles // tph))
@@ -310,7 +311,7 @@ def max_mode_flops(case, n_offsets):
         npass = -(-G // hp_max)
         hp = -(-G // npass)
         tiles = hp * tph
-    mfma_per_16_keys = npass * (tiles * steps * 3 + steps * 3)
+    mfma_per_16_keys = npass * (tiles * steps * 2 + steps * 3)
     return 2 * G * n_offsets * d, mfma_per_16_keys * 16 * 16 * 32 * 2 // 16
 
 
@@ -970,11 +971,12 @@ def main():
                      "launch": "tri_score call: plan write, prologue, operand pack, fused score "
                                "kernel",
                      "timing": "achieved: HIP events around each tri_score call in the timed "
-                               "steps, on the stream the kernels run on; frac_trace: the fused "
-                               "kernel's average duration in the committed rocprofv3 trace of "
-                               "this build (profiles/), null if that trace is of other sources"},
+                               "steps, on the stream the kernels run on"},
     }
     if args.workload == "long_reasoning" and not variant and args.rope_layout == "interleaved":
+        out["roofline"]["timing"] += ("; frac_trace: the fused kernel's average duration in the "
+                                      "committed rocprofv3 trace of this build (profiles/), null "
+                                      "if that trace is of other sources")
         t_us = trace_avg_us("tri::score_fused_kernel")
         out["roofline"]["trace_avg_us"] = t_us
         out["roofline"]["frac_trace"] = (b_score / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBPS

@@ -271,8 +271,8 @@ size_t tri_workspace_bytes_offsets(const tri_shape* shape, int32_t num_seqs,
  * Every other argument is as for tri_score.
  *
  * TRI_REDUCE_MAX needs head_dim % 32 == 0, and one head's offset rows
- * must fit the kernel's LDS budget: up to 400 offsets at d = 64, 192 at
- * d = 128, 80 at d = 256.  Heads are processed in as many
+ * must fit the kernel's LDS budget: up to 608 offsets at d = 64, 288 at
+ * d = 128, 128 at d = 256.  Heads are processed in as many
  * passes over the keys as that budget needs.  Shapes outside this return
  * TRI_ERR_UNSUPPORTED.  TRI_REDUCE_MAX spills raw scores to the workspace
  * (or to raw_scores when given).

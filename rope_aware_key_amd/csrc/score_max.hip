@@ -8,10 +8,10 @@
 // own, so per unit the trig term is a (G*|D| x d) by (d x n) product.
 //
 // Mapping onto CDNA4:
-//  * v_mfma_f32_16x16x32_bf16 with each fp64 coefficient split into three
-//    bf16 terms (hi, mid, lo), the same fp32-accurate scheme as the averaged
-//    path.  The split rows of one unit live in LDS; each A-operand read
-//    serves GB blocks of 16 keys held in registers.
+//  * v_mfma_f32_16x16x32_bf16 with each fp64 coefficient split into two
+//    bf16 terms (hi, mid; kTrigTerms says why two suffice here, where the
+//    averaged path keeps three).  The split rows of one unit live in LDS;
+//    each A-operand read serves GB blocks of 16 keys held in registers.
 //  * Lane (m, q) of an MFMA holds accumulator rows 4q..4q+3 of key m, so the
 //    rows are dealt to the four lane slots q.  Normally head h of a pass
 //    owns slot h % 4: its Dp rows (|D| rounded up to 4) fill Dp/4
@@ -52,6 +52,13 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTicketsPerGroup = 8;
+// bf16 terms of each trig coefficient (hi + mid, ~17 significant bits).  The
+// split error of a coefficient is at most 2^-17 of it, so a raw score moves
+// by at most 2^-17 of sum_j |a_j k_j|, a few 2^-17 of the raw scores' own
+// spread: on the five workload shapes the z-scores move by at most 2e-5
+// (fp64 check of 2 against 3 terms), a fifth of the 1e-4 bar; the third
+// term would add a third more MFMAs for 3e-8.
+constexpr int kTrigTerms = 2;
 
 __device__ __forceinline__ uint32_t bf16_rne_m(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -211,10 +218,10 @@ __global__ __launch_bounds__(256) void pack_max_operands_kernel(
       }
       split3_m(x, h3[j], m3[j], l3[j]);
     }
-    uint4* op = apack + (idx >> 6) * 3 * 64 + lane;
+    uint4* op = apack + (idx >> 6) * kTrigTerms * 64 + lane;
     op[0] = pack8(h3);
     op[64] = pack8(m3);
-    op[128] = pack8(l3);
+    if (kTrigTerms > 2) op[128] = pack8(l3);
   } else {
     const int64_t j = idx - n_a;
     const int st = (int)((j >> 6) % STEPS);
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
   // wave index as a scalar: the work list and ticket lookups stay uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, q = lane >> 4;
-  const int n_a = mp.ptiles * STEPS * 3 * 64;
+  const int n_a = mp.ptiles * STEPS * kTrigTerms * 64;
   const int t_begin = blockIdx.x * kTicketsPerGroup;
   const int t_end = min(t_begin + kTicketsPerGroup, total_tickets);
   const bool spread = mp.spread != 1;
@@ -359,7 +366,9 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
         // A operands run one MFMA step ahead of their use (tiles in order
         // over all rounds); past the last tile the last step is re-read.
         const uint4* ap = a_s + lane;
-        uint4 va[3] = {ap[0], ap[64], ap[128]};
+        uint4 va[kTrigTerms];
+#pragma unroll
+        for (int tt = 0; tt < kTrigTerms; ++tt) va[tt] = ap[64 * tt];
         for (int kk = 0; kk < mp.nk; ++kk) {
           float run[GB];
 #pragma unroll
@@ -372,25 +381,25 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
             const bool more = tile + 1 < mp.ptiles;
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
-              const uint4* np = ap + ((st + 1 < STEPS || more) ? 192 : 0);
-              const uint4 vn[3] = {np[0], np[64], np[128]};
-              bf16x8m_t ah, am, al;
-              __builtin_memcpy(&ah, &va[0], 16);
-              __builtin_memcpy(&am, &va[1], 16);
-              __builtin_memcpy(&al, &va[2], 16);
+              const uint4* np = ap + ((st + 1 < STEPS || more) ? 64 * kTrigTerms : 0);
+              uint4 vn[kTrigTerms];
+#pragma unroll
+              for (int tt = 0; tt < kTrigTerms; ++tt) vn[tt] = np[64 * tt];
+              bf16x8m_t at[kTrigTerms];
+#pragma unroll
+              for (int tt = 0; tt < kTrigTerms; ++tt) __builtin_memcpy(&at[tt], &va[tt], 16);
 #pragma unroll
               for (int bb = 0; bb < GB; ++bb) {
                 bf16x8m_t bk;
                 __builtin_memcpy(&bk, &kb[bb][st], 16);
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bk, acc[bb], 0, 0, 0);
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bk, acc[bb], 0, 0, 0);
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bk, acc[bb], 0, 0, 0);
+#pragma unroll
+                for (int tt = 0; tt < kTrigTerms; ++tt)
+                  acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[tt], bk, acc[bb], 0, 0, 0);
               }
-              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);       // next operands
-              __builtin_amdgcn_sched_group_barrier(0x008, 3 * GB, 0);  // this step
-              va[0] = vn[0];
-              va[1] = vn[1];
-              va[2] = vn[2];
+              __builtin_amdgcn_sched_group_barrier(0x100, kTrigTerms, 0);       // next operands
+              __builtin_amdgcn_sched_group_barrier(0x008, kTrigTerms * GB, 0);  // this step
+#pragma unroll
+              for (int tt = 0; tt < kTrigTerms; ++tt) va[tt] = vn[tt];
               ap = np;
             }
 #pragma unroll
@@ -531,9 +540,10 @@ MaxOffsetsPlan plan_max_offsets(int d, int G, int n_offsets) {
       n_offsets > kMaxOffsets)
     return mp;
   const int steps = d / 32;
-  const size_t tile_bytes = (size_t)steps * 3 * 64 * sizeof(uint4);
-  // the norm operands take one tile's worth of the LDS budget
-  const int max_tiles = (int)(kMaxOffsetsLds / tile_bytes) - 1;
+  const size_t tile_bytes = (size_t)steps * kTrigTerms * 64 * sizeof(uint4);
+  // the norm operands (three terms per step) take their share of the budget
+  const size_t norm_bytes = (size_t)steps * 3 * 64 * sizeof(uint4);
+  const int max_tiles = (int)((kMaxOffsetsLds - norm_bytes) / tile_bytes);
   // one slot per head: Dp/4 tiles per head, four heads per round of tiles
   int tph = (n_offsets + 3) / 4;
   if (tph <= max_tiles) {
@@ -565,7 +575,8 @@ size_t max_offsets_operand_bytes(int d, int G, int nD, const MaxOffsetsPlan& mp,
   if (!mp.ok) return 0;
   const int steps = d / 32;
   const size_t ops = (size_t)units * mp.npass *
-                     ((size_t)mp.ptiles * steps * 3 * 64 + (size_t)steps * 3 * 64) * sizeof(uint4);
+                     ((size_t)mp.ptiles * steps * kTrigTerms * 64 + (size_t)steps * 3 * 64) *
+                     sizeof(uint4);
   return ops + (size_t)tickets * kWaves * G * 2 * sizeof(double) + 64 * sizeof(float) +
          (size_t)nD * (d / 2) * sizeof(double2);
 }
@@ -579,7 +590,7 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
                                hipStream_t st) {
   const int64_t units = (int64_t)S * L * Hkv;
   uint4* apack = reinterpret_cast<uint4*>(operands);
-  uint4* wpack = apack + units * mp.npass * mp.ptiles * STEPS * 3 * 64;
+  uint4* wpack = apack + units * mp.npass * mp.ptiles * STEPS * kTrigTerms * 64;
   double* wsum = reinterpret_cast<double*>(wpack + units * mp.npass * STEPS * 3 * 64);
   float* sink = reinterpret_cast<float*>(wsum + (int64_t)total_tickets * kWaves * G * 2);
   double2* ph = reinterpret_cast<double2*>(sink + 64);
@@ -593,7 +604,7 @@ static hipError_t launch_max_t(const SeqInfo* seqs, int S, int L, int Hkv, int G
                      dim3(256), 0, st, S, L, Hkv, G, HALF, mp, nD, P, W, E, ph, apack, wpack);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = ((size_t)mp.ptiles + 1) * STEPS * 3 * 64 * sizeof(uint4);
+  const size_t lds = ((size_t)mp.ptiles * kTrigTerms + 3) * STEPS * 64 * sizeof(uint4);
   const int grid = (total_tickets + kTicketsPerGroup - 1) / kTicketsPerGroup;
   constexpr int GB = STEPS <= 4 ? 4 : 2;
   const int ne = (mp.hp + 3) / 4;

@@ -249,19 +249,20 @@ def test_max_over_offsets_shape_limits():
     assert _status(_score_off, sh, cu, cp, reduce="max") == ST["UNSUPPORTED"]
     assert R.tri_workspace_bytes_offsets(sh, cu, 17, "max") == 0
     assert R.tri_workspace_bytes_offsets(sh, cu, 17, "mean") > 0
-    # one head's rows must fit the LDS budget: 400 offsets at d = 64, 192 at
-    # d = 128, 80 at d = 256
+    # one head's rows (two bf16 terms per coefficient) must fit the LDS
+    # budget beside the norm operands: 608 offsets at d = 64, 288 at d = 128,
+    # 128 at d = 256
     sh = R.make_shape(128, 8, 2, 1)
-    assert R.tri_workspace_bytes_offsets(sh, cu, 192, "max") > 0
-    assert R.tri_workspace_bytes_offsets(sh, cu, 193, "max") == 0
-    assert _status(_score_off, sh, cu, cp, offsets=np.arange(1.0, 194.0),
+    assert R.tri_workspace_bytes_offsets(sh, cu, 288, "max") > 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 289, "max") == 0
+    assert _status(_score_off, sh, cu, cp, offsets=np.arange(1.0, 290.0),
                    reduce="max") == ST["UNSUPPORTED"]
     sh = R.make_shape(256, 8, 2, 1)
-    assert R.tri_workspace_bytes_offsets(sh, cu, 80, "max") > 0
-    assert R.tri_workspace_bytes_offsets(sh, cu, 81, "max") == 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 128, "max") > 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 129, "max") == 0
     sh = R.make_shape(64, 8, 2, 1)
-    assert R.tri_workspace_bytes_offsets(sh, cu, 400, "max") > 0
-    assert R.tri_workspace_bytes_offsets(sh, cu, 401, "max") == 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 608, "max") > 0
+    assert R.tri_workspace_bytes_offsets(sh, cu, 609, "max") == 0
 
 
 def test_offset_workspaces():
