@@ -44,12 +44,14 @@
  *  - Argument errors return before any device work is queued.  A HIP error
  *    during launch returns TRI_ERR_HIP.  tri_last_error() gives a message
  *    for the last failing call of the calling thread.
- *  - Host arrays reach the device through a pinned staging ring the library
- *    allocates once per device: each call copies its per-sequence plan into
- *    a ring slot and queues an asynchronous copy from it, and a slot is
- *    reused only once that copy has completed.  Calls are therefore not
- *    meant to be captured into a HIP graph: a replay would copy whatever a
- *    later call left in the slot.
+ *  - Host arrays reach the device in the arguments of small copy launches
+ *    (2560 bytes each): nothing on the host outlives the call and no
+ *    staging memory is held.  A call's device work is kernel launches
+ *    only, so tri_score, tri_score_offsets, tri_score_paged,
+ *    tri_select_compact* and tri_score_noalloc may be captured into a HIP
+ *    graph and replayed (the plan is fixed at capture).  The decode-loop
+ *    calls may allocate and return TRI_ERR_UNSUPPORTED on a capturing
+ *    stream.
  */
 #ifndef TRIATTN_H
 #define TRIATTN_H
@@ -183,10 +185,9 @@ tri_status tri_score(const tri_shape* shape, int32_t num_seqs,
  * forbid allocation).  Same arguments, results and errors as tri_score,
  * without the workspace: the scratch tri_score would take from the
  * workspace lives in a device array of the library, 64 MiB, that each GPU
- * the library runs on holds until the process ends, and the per-call
- * sequence table travels in kernel arguments (one small launch per 64
- * sequences) instead of a pinned staging copy.  No hipMalloc, hipFree or
- * host-pinned allocation is made.
+ * the library runs on holds until the process ends; the per-call sequence
+ * table travels in kernel arguments (one small launch per 64 sequences) as
+ * for every call.  No hipMalloc, hipFree or host-pinned allocation is made.
  *
  * Limit: a call whose tri_workspace_bytes() exceeds 64 MiB (about 3,900
  * units of head_dim 128 on the fused path) returns TRI_ERR_WORKSPACE and
