@@ -188,7 +188,7 @@ def test_long_units_leave_the_fused_path():
     sh = R.make_shape(128, 16, 1, 1)
     G = 16
     jumps = []
-    for ch in range(64, 1025, 64):
+    for ch in range(64, 2049, 64):
         fused_n = ch * 384
         w_fused = R.tri_workspace_bytes(sh, [0, fused_n])
         w_long = R.tri_workspace_bytes(sh, [0, fused_n + 1])
@@ -538,7 +538,7 @@ def test_fused_routing_follows_resident_work_groups():
     sh = R.make_shape(128, 7, 1, 1)
     G = 7
     ch = None
-    for c in range(64, 1025, 64):   # the fused chunk size: where 384 chunks stop fitting
+    for c in range(64, 2049, 64):   # the fused chunk size: where 384 chunks stop fitting
         if R.tri_workspace_bytes(sh, [0, c * 384 + 1]) >= (c * 384 + 1) * G * 4:
             if R.tri_workspace_bytes(sh, [0, c * 384]) < c * 384 * G * 4:
                 ch = c
