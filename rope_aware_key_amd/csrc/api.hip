@@ -426,10 +426,9 @@ hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t
   if (upload_seqs) e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   const int LH = p.L * p.Hkv;
   if (e == hipSuccess)
-    e = tri::launch_select(dseq, p.S, LH, p.max_n, scores, kept_idx, ws + p.off_split, s);
-  if (e == hipSuccess && (k_out || v_out || pos_out))
-    e = tri::launch_compact(dseq, p.S, LH, p.d, p.max_b, kept_idx, k, v, k_pos, k_out, v_out,
-                            pos_out, p.in_pg, p.out_pg, s);
+    e = tri::launch_select_compact(dseq, p.S, LH, p.d, p.max_n, p.max_b, scores, kept_idx,
+                                   ws + p.off_split, k, v, k_pos, k_out, v_out, pos_out, p.in_pg,
+                                   p.out_pg, s);
   return e;
 }
 

@@ -8,10 +8,13 @@
 //
 // Method: scores map to order-preserving 32-bit keys.  A most-significant-
 // digit radix select finds the b-th largest key T and how many keys equal
-// to T are kept (the quota).  A final ordered scan keeps every key > T and
-// the first `quota` keys == T, writing their indices through block-wide
-// prefix sums.  Units up to 35840 keys take one work-group (keys in
-// registers or LDS); longer ones are split over work-groups of 4096 keys.
+// to T are kept (the quota).  A final ordered pass keeps every key > T and
+// the first `quota` keys == T, writing their indices in index order.  By
+// unit length: up to 4096 keys, one work-group of 256 threads with the
+// keys in LDS; up to 32768, one work-group of 1024 threads with the keys
+// in registers (and, when rows are gathered, the gathers in the same
+// kernel); up to 35840, one work-group of 512 threads reading the scores
+// three times; longer units are split over work-groups of 4096 keys.
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -28,17 +31,21 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // LDS; the radix passes and the ordered scan then run on LDS.  Digits are
 // 12, 12 and 8 bits wide: z-scores crowd a few exponent values, and 12-bit
 // first digits (sign, exponent, 3 mantissa bits) spread them over enough
-// bins that LDS atomics rarely collide.  NT threads per unit: 1024 for long
-// units, 256 so that many short units share a CU.
+// bins that LDS atomics rarely collide.  256 threads per unit (units of up
+// to 4096 keys), so that many short units share a CU.
 // ---------------------------------------------------------------------------
 constexpr int kHistBins = 4096;
 constexpr int kScanItems = 8;  // consecutive keys per thread in the ordered scan
 
 // Exclusive prefix sum over a block of NT threads; *total gets the sum.
+// The wave totals are scanned across the lanes of every wave (one total
+// per lane) and read back with readlane, so the scan holds few registers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(NW <= 64, "one wave total per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -47,13 +54,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  uint32_t before = 0, all = 0;
+  uint32_t ws = lane < NW ? wsum[lane] : 0u;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t t = wsum[w];
-    if (w < wave) before += t;
-    all += t;
+  for (int o = 1; o < NW; o <<= 1) {
+    const uint32_t y = __shfl_up(ws, o, 64);
+    if (lane >= o) ws += y;
   }
+  const uint32_t before = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
+  const uint32_t all = __builtin_amdgcn_readlane(ws, NW - 1);
   __syncthreads();
   *total = all;
   return before + x - v;
@@ -201,24 +209,95 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* hist, uint32_t kk, 
   return bin;
 }
 
+// Longest unit one work-group selects (the streaming select); longer units
+// take the split select.
+constexpr int kSelLdsMaxKeys = 35840;
+
 // ---------------------------------------------------------------------------
-// Register-resident select for units of up to NT*KPT keys: thread t holds
-// keys [t*KPT, (t+1)*KPT) in registers, so LDS holds only the histogram and
-// two work-groups share a CU.  Same digits and passes as select_lds_kernel;
-// since each thread's keys are one contiguous index range, the ordered
-// emission needs a single pair of block scans over per-thread counts.
+// Streaming select for units of 4096 < n <= kSelLdsMaxKeys.  The keys stay
+// in neither registers nor LDS (32 KB per work-group), so four work-groups
+// share a CU and one group's reads overlap another's arithmetic.  Wave w
+// owns the contiguous index segment [w*seg, w*seg + seg) and reads it 64
+// consecutive keys at a time: counts per wave are counts per segment, and
+// the ordered emission needs one scan over the NW wave totals.
+//   sweep 1: histogram of the top 12 key bits; pick that digit (bin0).
+//   sweep 2: keys above bin0 are counted per wave, the indices of keys in
+//            bin0 go to an LDS list; the 12- and 8-bit lower digits are
+//            found over the listed keys alone.  If the list overflows
+//            (heavy ties), two more sweeps find them over the whole unit.
+//   sweep 3: each wave writes its kept indices in index order; ballots
+//            give each lane its rank among the wave's equal and kept keys.
+// Sweeps 2 and 3 compare the scores as floats against thresholds derived
+// from key bounds (key_floor), which costs one compare per bound instead of
+// a key conversion.  Sweep 1 reads HBM; sweeps 2 and 3 mostly hit the
+// caches.
 // ---------------------------------------------------------------------------
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void select_reg_kernel(
+constexpr int kStreamThreads = 512;
+constexpr int kStreamCand = 4096;  // candidate indices (16 KB)
+constexpr int kStreamBatch = 8;    // loads in flight per lane
+
+// For K in [1, 2^32): order_key(x) >= K  <=>  x >= key_floor(K) (float
+// compare, false for NaN).  Keys at or above 2^31 are the non-negative
+// floats (and -0) in bit order; keys below it the negative floats in
+// reverse bit order, so the bound is the float whose key is K.  Keys in
+// [1, 0x007fffff) belong to NaN bit patterns, which key to 0, so such K
+// are raised to the key of -inf; K above the key of +inf give a NaN bound,
+// which nothing reaches.  K == 0 (every key, NaN included) is the caller's.
+__device__ __forceinline__ float key_floor(uint32_t K) {
+  K = K < 0x007fffffu ? 0x007fffffu : K;
+  return __uint_as_float((K & 0x80000000u) ? (K & 0x7fffffffu) : ~K);
+}
+
+// number of set bits of mask held by lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Calls f(i, valid, x) for each score of the wave's segment [s0, s0 + seg)
+// (seg a multiple of 64; scores at i >= s1 invalid), kStreamBatch loads in
+// flight per lane.  Every lane of the wave makes every call.
+template <class F>
+__device__ __forceinline__ void sweep_segment(const float* __restrict__ in, int s0, int seg, int s1,
+                                              F&& f) {
+  const int lane = threadIdx.x & 63;
+  int base = s0;
+  for (; base + 64 * kStreamBatch <= s1; base += 64 * kStreamBatch) {
+    float v[kStreamBatch];
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) v[u] = in[base + u * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) f(base + u * 64 + lane, true, v[u]);
+  }
+  for (; base < s1; base += 64 * kStreamBatch) {
+    float v[kStreamBatch];
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) {
+      const int i = base + u * 64 + lane;
+      v[u] = i < s1 ? in[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) {
+      const int i = base + u * 64 + lane;
+      f(i, i < s1, v[u]);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_stream_kernel(
     const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
     int32_t* __restrict__ kept) {
   constexpr int NW = NT / 64;
-  static_assert(KPT % 4 == 0, "keys load as float4");
   __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t cand[kStreamCand];
   __shared__ uint32_t sel[2];
   __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t wgt[NW], weq[NW];
+  __shared__ uint32_t ncand;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x;
   const int s = unit / LH, lg = unit % LH;
   const SeqInfo si = seqs[s];
@@ -230,36 +309,226 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(
     for (int i = tid; i < n; i += NT) out[i] = i;
     return;
   }
-  const int i0 = tid * KPT;
-  uint32_t key[KPT];
-  if ((reinterpret_cast<uintptr_t>(in) & 15u) == 0 && i0 + KPT <= n) {
-#pragma unroll
-    for (int j = 0; j < KPT; j += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(in + i0 + j);
-      key[j] = order_key(f.x);
-      key[j + 1] = order_key(f.y);
-      key[j + 2] = order_key(f.z);
-      key[j + 3] = order_key(f.w);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? order_key(in[i0 + j]) : 0u;
-  }
-  // keys past n are 0 (the NaN key) and are excluded by index below
-  const int mine = max(0, min(KPT, n - i0));
+  const int seg = (n + NW * 64 - 1) / (NW * 64) * 64;
+  const int s0 = wave * seg, s1 = min(n, s0 + seg);
 
-  uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)b;
+  // sweep 1: top digit
+  for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
+  if (tid < NW) {
+    wgt[tid] = 0u;
+    weq[tid] = 0u;
+  }
+  if (tid == 0) ncand = 0u;
+  __syncthreads();
+  sweep_segment(in, s0, seg, s1, [&](int, bool valid, float x) {
+    if (valid) atomicAdd(&hist[order_key(x) >> 20], 1u);
+  });
+  __syncthreads();
+  uint32_t above = 0;
+  const uint32_t bin0 = pick_bin<NT>(hist, (uint32_t)b, sel, wsum, &above);
+  uint32_t kk = (uint32_t)b - above;
+
+  // sweep 2: keys above bin0 counted, keys in bin0 listed.  bin0 holds the
+  // b-th largest key, so bin0 << 20 > 0 unless that key is a NaN's.
+  const float lo_f = key_floor(bin0 << 20), hi_f = key_floor((bin0 + 1u) << 20);
+  const bool lo_all = bin0 == 0u;
+  uint32_t hi = 0;  // wave-uniform
+  sweep_segment(in, s0, seg, s1, [&](int i, bool valid, float x) {
+    const bool up = valid && x >= hi_f;
+    hi += (uint32_t)__popcll(__ballot(up));
+    const bool c = valid && !up && (lo_all || x >= lo_f);
+    const uint64_t cm = __ballot(c);
+    if (cm != 0) {
+      uint32_t first = 0;
+      if (lane == 0) first = atomicAdd(&ncand, (uint32_t)__popcll(cm));
+      const uint32_t slot = (uint32_t)__shfl(first, 0, 64) + lanes_below(cm);
+      if (c && slot < (uint32_t)kStreamCand) cand[slot] = (uint32_t)i;
+    }
+  });
+  __syncthreads();
+  const uint32_t nc = ncand;
+  const bool listed = nc <= (uint32_t)kStreamCand;
+  uint32_t prefix = bin0 << 20, mask = 0xfff00000u;
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const uint32_t dmask = pass == 2 ? 0xffu : 0xfffu;
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 8 : 0;
+    const uint32_t dmask = pass == 1 ? 0xfffu : 0xffu;
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (j < mine && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+    if (listed) {
+      for (uint32_t c = tid; c < nc; c += NT) {
+        const uint32_t key = order_key(in[cand[c]]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      }
+    } else {
+      sweep_segment(in, s0, seg, s1, [&](int, bool valid, float x) {
+        const uint32_t key = order_key(x);
+        if (valid && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      });
+    }
     __syncthreads();
-    uint32_t above = 0;
+    const uint32_t bin = pick_bin<NT>(hist, kk, sel, wsum, &above);
+    kk -= above;
+    prefix |= bin << shift;
+    mask |= dmask << shift;
+  }
+  const uint32_t T = prefix, quota = kk;
+  // key > T <=> x >= gt_f (T is a present key, at most that of +inf, so
+  // T + 1 does not wrap); key == T <=> eq_all or x >= eq_f, and not above
+  const float gt_f = key_floor(T + 1u), eq_f = key_floor(T);
+  const bool eq_all = T == 0u;
+
+  // keys > T and == T per segment
+  if (listed) {
+    if (lane == 0) atomicAdd(&wgt[wave], hi);
+    for (uint32_t c = tid; c < nc; c += NT) {
+      const uint32_t i = cand[c];
+      const float x = in[i];
+      if (x >= gt_f) atomicAdd(&wgt[i / (uint32_t)seg], 1u);
+      else if (eq_all || x >= eq_f) atomicAdd(&weq[i / (uint32_t)seg], 1u);
+    }
+  } else {
+    uint32_t gt = 0, eq = 0;
+    sweep_segment(in, s0, seg, s1, [&](int, bool valid, float x) {
+      const bool up = valid && x >= gt_f;
+      gt += (uint32_t)__popcll(__ballot(up));
+      eq += (uint32_t)__popcll(__ballot(valid && !up && (eq_all || x >= eq_f)));
+    });
+    if (lane == 0) {
+      wgt[wave] = gt;
+      weq[wave] = eq;
+    }
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {  // wave-uniform trip count
+    gt_before += wgt[w];
+    eq_before += weq[w];
+  }
+  const uint32_t eq_left = quota > eq_before ? quota - eq_before : 0u;
+  if (wgt[wave] + min(eq_left, weq[wave]) == 0u) return;  // nothing kept in this segment
+
+  // sweep 3: ordered emission
+  uint32_t pos0 = gt_before + min(quota, eq_before), eq_run = eq_before;
+  sweep_segment(in, s0, seg, s1, [&](int i, bool valid, float x) {
+    const bool up = valid && x >= gt_f;
+    const uint64_t em = __ballot(valid && !up && (eq_all || x >= eq_f));
+    bool keep = up;
+    if (em != 0) {  // keys equal to T: the first `quota` of the unit are kept
+      const bool eq = (em >> lane) & 1u;
+      keep = up || (eq && eq_run + lanes_below(em) < quota);
+      eq_run += (uint32_t)__popcll(em);
+    }
+    const uint64_t km = __ballot(keep);
+    const uint32_t pos = pos0 + lanes_below(km);
+    if (keep && pos < (uint32_t)b) out[pos] = i;
+    pos0 += (uint32_t)__popcll(km);
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Register-held select for units of 4096 < n <= NT*KPT: the streaming
+// select's steps with the unit's order keys read once into registers (KPT
+// per lane; lane l of wave w holds indices w*64*KPT + 64*j + l), so no
+// score is read twice and every bound is an integer compare.  Keys in the
+// top-digit bin are listed with their index, so the lower digits cost one
+// pass over the list; if the list overflows, over the held keys.  At most
+// 64 VGPRs, so that two work-groups of 1024 threads share a CU.
+// ---------------------------------------------------------------------------
+constexpr int kHeldCand = 4096;  // listed keys and their indices (32 KB)
+
+// A copy of x the compiler cannot see through: per-lane values derived from
+// it in a later phase are recomputed there instead of being kept live from
+// an earlier one.
+__device__ __forceinline__ int fresh(int x) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// One unit's selection by one work-group of NT threads, 0 < b < n; writes
+// the b kept indices to out.  Every thread calls it (it holds barriers).
+template <int NT, int KPT>
+__device__ __forceinline__ void held_select(const float* __restrict__ in, int32_t* __restrict__ out,
+                                            int n, int b) {
+  constexpr int NW = NT / 64, SEG = 64 * KPT;
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t cand_key[kHeldCand], cand_idx[kHeldCand];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t wgt[NW], weq[NW];
+  __shared__ uint32_t ncand;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Places past n hold key 0 (a NaN's): they join the histograms and the
+  // list as NaNs whose indices follow every real key, so they rank after
+  // every real NaN, and the b < n real keys fill the budget before them.
+  const int s0 = wave * SEG + lane;
+  uint32_t key[KPT];
+  if (wave * SEG + SEG <= n) {  // the whole range real: unconditional loads, all in flight
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = order_key(in[s0 + 64 * j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = s0 + 64 * j < n ? order_key(in[s0 + 64 * j]) : 0u;
+  }
+
+  for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
+  if (tid < NW) {
+    wgt[tid] = 0u;
+    weq[tid] = 0u;
+  }
+  if (tid == 0) ncand = 0u;
+  __syncthreads();
+  // top digit
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) atomicAdd(&hist[key[j] >> 20], 1u);
+  __syncthreads();
+  uint32_t above = 0;
+  const uint32_t bin0 = pick_bin<NT>(hist, (uint32_t)b, sel, wsum, &above);
+  uint32_t kk = (uint32_t)b - above;
+
+  // keys above bin0 counted per wave, keys in bin0 listed
+  const uint32_t lo = bin0 << 20, hi_k = (bin0 + 1u) << 20;  // bin0 <= 0xff8: no wrap
+  uint32_t hi = 0;  // wave-uniform
+  const int s0c = fresh(s0);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    hi += (uint32_t)__popcll(__ballot(key[j] >= hi_k));
+    const bool c = key[j] >= lo && key[j] < hi_k;
+    const uint64_t cm = __ballot(c);
+    if (cm != 0) {
+      uint32_t first = 0;
+      if (lane == 0) first = atomicAdd(&ncand, (uint32_t)__popcll(cm));
+      const uint32_t slot = __builtin_amdgcn_readfirstlane(first) + lanes_below(cm);
+      if (c && slot < (uint32_t)kHeldCand) {
+        cand_key[slot] = key[j];
+        cand_idx[slot] = (uint32_t)(s0c + 64 * j);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nc = ncand;
+  const bool listed = nc <= (uint32_t)kHeldCand;
+  uint32_t prefix = lo, mask = 0xfff00000u;
+#pragma unroll 1
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 8 : 0;
+    const uint32_t dmask = pass == 1 ? 0xfffu : 0xffu;
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    if (listed) {
+      for (uint32_t c = tid; c < nc; c += NT) {
+        const uint32_t k = cand_key[c];
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if ((key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
     const uint32_t bin = pick_bin<NT>(hist, kk, sel, wsum, &above);
     kk -= above;
     prefix |= bin << shift;
@@ -267,44 +536,123 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(
   }
   const uint32_t T = prefix, quota = kk;
 
-  // Keys are blocked per thread, so a thread's counts cover a contiguous
-  // index range: one scan of the per-thread totals orders the whole unit.
-  uint32_t neq = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) neq += (j < mine && key[j] == T) ? 1u : 0u;
-  uint32_t eq_all = 0;
-  const uint32_t eq_before = block_excl_scan<NT>(neq, wsum, &eq_all);
-  uint32_t nkeep = 0;
-  {
-    uint32_t e = eq_before;
+  // keys > T and == T per wave
+  if (listed) {
+    if (lane == 0) atomicAdd(&wgt[wave], hi);
+    for (uint32_t c = tid; c < nc; c += NT) {
+      const uint32_t k = cand_key[c], w = cand_idx[c] / (uint32_t)SEG;
+      if (k > T) atomicAdd(&wgt[w], 1u);
+      else if (k == T) atomicAdd(&weq[w], 1u);
+    }
+  } else {
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool valid = j < mine;
-      const bool gt = valid && key[j] > T;
-      const bool eq = valid && key[j] == T;
-      nkeep += (gt || (eq && e < quota)) ? 1u : 0u;
-      e += eq ? 1u : 0u;
+      gt += (uint32_t)__popcll(__ballot(key[j] > T));
+      eq += (uint32_t)__popcll(__ballot(key[j] == T));
+    }
+    if (lane == 0) {
+      wgt[wave] = gt;
+      weq[wave] = eq;
     }
   }
-  uint32_t keep_all = 0;
-  uint32_t pos = block_excl_scan<NT>(nkeep, wsum, &keep_all);
-  uint32_t e = eq_before;
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {  // wave-uniform trip count
+    gt_before += wgt[w];
+    eq_before += weq[w];
+  }
+  const uint32_t eq_left = quota > eq_before ? quota - eq_before : 0u;
+  if (wgt[wave] + min(eq_left, weq[wave]) == 0u) return;  // nothing kept in this wave's range
+
+  // ordered emission
+  uint32_t pos0 = gt_before + min(quota, eq_before), eq_run = eq_before;
+  const int s0e = fresh(s0);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool valid = j < mine;
-    const bool gt = valid && key[j] > T;
-    const bool eq = valid && key[j] == T;
-    if (gt || (eq && e < quota)) {
-      if (pos < (uint32_t)b) out[pos] = i0 + j;
-      ++pos;
+    const uint64_t em = __ballot(key[j] == T);
+    bool keep = key[j] > T;
+    if (em != 0) {  // keys equal to T: the first `quota` of the unit are kept
+      keep = keep || (key[j] == T && eq_run + lanes_below(em) < quota);
+      eq_run += (uint32_t)__popcll(em);
     }
-    e += eq ? 1u : 0u;
+    const uint64_t km = __ballot(keep);
+    const uint32_t pos = pos0 + lanes_below(km);
+    if (keep && pos < (uint32_t)b) out[pos] = s0e + 64 * j;
+    pos0 += (uint32_t)__popcll(km);
   }
 }
 
-// Longest unit whose keys the LDS-staged select holds (140 KB of keys next
-// to the 16 KB histogram).
-constexpr int kSelLdsMaxKeys = 35840;
+// Rows of the gathers (K, V, positions), packed or through page tables.
+struct CompactArgs {
+  int d;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* k_pos;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int32_t* pos_out;
+  Pages in_pg, out_pg;
+};
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Moves part `part` (16 bytes) of kept row r (input row idx of unit
+// (s, lg)) of K and V, and its position from part 0.  Rows move whole,
+// read once and written once: non-temporal on both sides.
+__device__ __forceinline__ void copy_row_part(const CompactArgs& ca, int s, int lg, int64_t in0,
+                                              int64_t out0, int idx, int r, int part) {
+  const int64_t src = ca.in_pg.table ? paged_row_lg(ca.in_pg, s, lg, idx) : in0 + idx;
+  const int64_t dst = ca.out_pg.table ? paged_row_lg(ca.out_pg, s, lg, r) : out0 + r;
+  if (ca.k_out)
+    __builtin_nontemporal_store(
+        __builtin_nontemporal_load(reinterpret_cast<const v4u*>(ca.k + src * ca.d) + part),
+        reinterpret_cast<v4u*>(ca.k_out + dst * ca.d) + part);
+  if (ca.v_out)
+    __builtin_nontemporal_store(
+        __builtin_nontemporal_load(reinterpret_cast<const v4u*>(ca.v + src * ca.d) + part),
+        reinterpret_cast<v4u*>(ca.v_out + dst * ca.d) + part);
+  if (ca.pos_out && part == 0) ca.pos_out[dst] = ca.k_pos[src];
+}
+
+// Register-held select of one unit per work-group; with COPY the same
+// work-group then gathers the unit's kept rows (the kept indices it just
+// wrote, read back after a barrier), so that one work-group's selection
+// overlaps another's copy on the same CU.
+template <int NT, int KPT, bool COPY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void select_held_kernel(
+    const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
+    int32_t* __restrict__ kept, const CompactArgs ca) {
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int s = unit / LH, lg = unit % LH;
+  const SeqInfo si = seqs[s];
+  const int n = si.n, b = si.b;
+  if (b <= 0) return;
+  const int64_t in0 = si.row_base + (int64_t)lg * si.in_stride;
+  const int64_t out0 = si.out_base + (int64_t)lg * si.out_stride;
+  int32_t* out = kept + out0;
+  if (b >= n) {
+    for (int i = tid; i < n; i += NT) out[i] = i;
+  } else {
+    held_select<NT, KPT>(scores + in0, out, n, b);
+  }
+  if constexpr (COPY) {
+    // The unit's kept indices, written by this work-group: complete in L2
+    // after the barrier, and read from there (agent-scope loads skip the
+    // CU's L1, which may hold a line shared with a neighbouring unit's
+    // indices from before they were written).
+    __syncthreads();
+    const int lpr = ca.d >> 3;  // lanes per row, 16 bytes each
+    const int rows_per_pass = NT / lpr;
+    const int sub = tid / lpr, part = tid - sub * lpr;
+#pragma unroll 2
+    for (int r = sub < rows_per_pass ? sub : b; r < b; r += rows_per_pass) {
+      const int idx = __hip_atomic_load(out + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)idx < (uint32_t)n) copy_row_part(ca, s, lg, in0, out0, idx, r, part);
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Split select for units longer than the LDS-staged select holds: the unit
@@ -571,10 +919,8 @@ constexpr int kSelSmallUnit = 4096;  // up to here 256 threads per unit
 template <int NT>
 static hipError_t launch_select_lds(int64_t units, int max_n, hipStream_t st, const SeqInfo* seqs,
                                     int LH, const float* scores, int32_t* kept_idx) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&select_lds_kernel<NT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMaxKeys * (int)sizeof(uint32_t));
-  if (attr != hipSuccess) return attr;
+  // at most kSelSmallUnit keys (16 KB) beside the 16 KB histogram: within
+  // the default dynamic LDS limit
   const size_t lds = (size_t)(max_n > 0 ? max_n : 1) * sizeof(uint32_t);
   hipLaunchKernelGGL(select_lds_kernel<NT>, dim3((unsigned)units), dim3(NT), lds, st, seqs, LH,
                      scores, kept_idx);
@@ -588,17 +934,20 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
   if (max_n <= kSelSmallUnit)
     return launch_select_lds<256>(units, max_n, st, seqs, LH, scores, kept_idx);
   if (max_n <= 1024 * 16) {
-    hipLaunchKernelGGL((select_reg_kernel<1024, 16>), dim3((unsigned)units), dim3(1024), 0, st,
-                       seqs, LH, scores, kept_idx);
+    hipLaunchKernelGGL((select_held_kernel<1024, 16, false>), dim3((unsigned)units), dim3(1024), 0,
+                       st, seqs, LH, scores, kept_idx, CompactArgs{});
     return hipGetLastError();
   }
   if (max_n <= 1024 * 32) {
-    hipLaunchKernelGGL((select_reg_kernel<1024, 32>), dim3((unsigned)units), dim3(1024), 0, st,
-                       seqs, LH, scores, kept_idx);
+    hipLaunchKernelGGL((select_held_kernel<1024, 32, false>), dim3((unsigned)units), dim3(1024), 0,
+                       st, seqs, LH, scores, kept_idx, CompactArgs{});
     return hipGetLastError();
   }
-  if (max_n <= kSelLdsMaxKeys)
-    return launch_select_lds<1024>(units, max_n, st, seqs, LH, scores, kept_idx);
+  if (max_n <= kSelLdsMaxKeys) {
+    hipLaunchKernelGGL(select_stream_kernel<kStreamThreads>, dim3((unsigned)units),
+                       dim3(kStreamThreads), 0, st, seqs, LH, scores, kept_idx);
+    return hipGetLastError();
+  }
   if (!split_ws) return hipErrorInvalidValue;
   const int tiles = (max_n + kSplitTile - 1) / kSplitTile;
   if (units * tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -624,17 +973,12 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
 
 // Gather kept rows.  Work-group (unit, tile) copies kCompactRows output rows;
 // a group of d/8 lanes moves one row (16 bytes per lane) of K and of V, the
-// first lane of the group the position.
+// first lane of the group the position.  Kept indices are always packed.
 constexpr int kCompactRows = 64;
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Rows of K, V and positions: packed, or through the input / output page
-// tables (in_pg, out_pg); kept indices are always packed.
-__global__ __launch_bounds__(256) void compact_kernel(
-    const SeqInfo* __restrict__ seqs, int LH, int d, const int32_t* __restrict__ kept,
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ k_pos, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
-    int32_t* __restrict__ pos_out, const Pages in_pg, const Pages out_pg) {
+__global__ __launch_bounds__(256) void compact_kernel(const SeqInfo* __restrict__ seqs, int LH,
+                                                      const int32_t* __restrict__ kept,
+                                                      const CompactArgs ca) {
   const int unit = blockIdx.x;
   const int s = unit / LH, lg = unit % LH;
   const SeqInfo si = seqs[s];
@@ -642,7 +986,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
   const int r0 = blockIdx.y * kCompactRows;
   if (r0 >= b) return;
   const int r1 = min(b, r0 + kCompactRows);
-  const int lpr = d >> 3;
+  const int lpr = ca.d >> 3;
   const int rows_per_pass = 256 / lpr;
   const int tid = threadIdx.x;
   const int sub = tid / lpr, part = tid - sub * lpr;
@@ -653,17 +997,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
   for (int r = r0 + sub; r < r1; r += rows_per_pass) {
     const int32_t idx = kept[out0 + r];
     if ((uint32_t)idx >= (uint32_t)si.n) continue;  // never read outside the unit
-    const int64_t src = in_pg.table ? paged_row_lg(in_pg, s, lg, idx) : in0 + idx;
-    const int64_t dst = out_pg.table ? paged_row_lg(out_pg, s, lg, r) : out0 + r;
-    // rows move whole (d/8 lanes x 16 bytes), read once and written once:
-    // non-temporal on both sides
-    if (k_out)
-      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(k + src * d) + part),
-                                  reinterpret_cast<v4u*>(k_out + dst * d) + part);
-    if (v_out)
-      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(v + src * d) + part),
-                                  reinterpret_cast<v4u*>(v_out + dst * d) + part);
-    if (pos_out && part == 0) pos_out[dst] = k_pos[src];
+    copy_row_part(ca, s, lg, in0, out0, idx, r, part);
   }
 }
 
@@ -675,9 +1009,33 @@ hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
   const int64_t units = (int64_t)S * LH;
   if (units == 0 || max_b <= 0) return hipSuccess;
   const dim3 grid((unsigned)units, (unsigned)((max_b + kCompactRows - 1) / kCompactRows));
-  hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, seqs, LH, d, kept_idx, k, v, k_pos,
-                     k_out, v_out, pos_out, in_pg, out_pg);
+  const CompactArgs ca{d, k, v, k_pos, k_out, v_out, pos_out, in_pg, out_pg};
+  hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, seqs, LH, kept_idx, ca);
   return hipGetLastError();
+}
+
+hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int max_n, int max_b,
+                                 const float* scores, int32_t* kept_idx, void* split_ws,
+                                 const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
+                                 uint16_t* k_out, uint16_t* v_out, int32_t* pos_out,
+                                 const Pages& in_pg, const Pages& out_pg, hipStream_t st) {
+  const int64_t units = (int64_t)S * LH;
+  const bool copy = k_out || v_out || pos_out;
+  if (units > 0 && copy && max_n > kSelSmallUnit && max_n <= 1024 * 32) {
+    // register-held select and the gathers in one kernel
+    const CompactArgs ca{d, k, v, k_pos, k_out, v_out, pos_out, in_pg, out_pg};
+    if (max_n <= 1024 * 16)
+      hipLaunchKernelGGL((select_held_kernel<1024, 16, true>), dim3((unsigned)units), dim3(1024),
+                         0, st, seqs, LH, scores, kept_idx, ca);
+    else
+      hipLaunchKernelGGL((select_held_kernel<1024, 32, true>), dim3((unsigned)units), dim3(1024),
+                         0, st, seqs, LH, scores, kept_idx, ca);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_select(seqs, S, LH, max_n, scores, kept_idx, split_ws, st);
+  if (e != hipSuccess || !copy) return e;
+  return launch_compact(seqs, S, LH, d, max_b, kept_idx, k, v, k_pos, k_out, v_out, pos_out, in_pg,
+                        out_pg, st);
 }
 
 }  // namespace tri

@@ -272,4 +272,13 @@ hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
                           int32_t* pos_out, const Pages& in_pg, const Pages& out_pg,
                           hipStream_t st);
 
+// Select, then the gathers asked for (any of k_out, v_out, pos_out); for
+// units of 4096 < n <= 32768 keys one kernel does both, one work-group per
+// unit, so that selections overlap other units' copies.
+hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int max_n, int max_b,
+                                 const float* scores, int32_t* kept_idx, void* split_ws,
+                                 const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
+                                 uint16_t* k_out, uint16_t* v_out, int32_t* pos_out,
+                                 const Pages& in_pg, const Pages& out_pg, hipStream_t st);
+
 }  // namespace tri

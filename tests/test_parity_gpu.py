@@ -184,13 +184,72 @@ def test_select_edge_cases_exact():
     np.testing.assert_array_equal(res["kept"][ostart:ostart + b].cpu().numpy(), np.arange(17))
 
 
-@pytest.mark.parametrize("n,B", [(4096, 4095), (4096, 1), (20000, 10000), (33000, 2048)])
+@pytest.mark.parametrize("n,B", [(4096, 4095), (4096, 1), (20000, 10000), (33000, 2048),
+                                 (4097, 4096), (35840, 1)])
 def test_select_many_ties(n, B):
     case = _hand_case([n], [B], Hkv=1)
     g = np.random.default_rng(n + B)
     sc = g.integers(-3, 4, size=n).astype(np.float32) * 0.5    # 7 distinct values
     res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
     check_selection_exact(case, res)
+
+
+def test_select_held_edge_cases_exact():
+    """A batch whose longest unit (32768 keys) takes the register-held
+    select (16384 < n <= 32768: 32 keys per lane, places past n padded with
+    the NaN key): empty, single-key, fully kept and budget-0 units, lengths
+    that leave waves partly or wholly past n; NaN, signed zeros, infinities
+    and denormals; an all-equal unit (the top-digit list overflows, so the
+    lower digits come from the held keys); a unit whose threshold is the
+    NaN key itself, so that the kept NaNs come first in index order and no
+    padding place may be taken; and normal scores."""
+    lens = [0, 1, 5, 64, 4097, 32768, 20000, 9999, 16385, 20001]
+    budgets = [4, 0, 9, 64, 1, 32767, 2, 9998, 6000, 5000]
+    case = _hand_case(lens, budgets)
+    rows = case.total_rows()
+    g = np.random.default_rng(31)
+    pool = np.array([0.0, -0.0, 1.5, -1.5, np.inf, -np.inf, np.nan, 3.25, 1e-38, -1e-38], np.float32)
+    sc = g.choice(pool, size=rows).astype(np.float32)
+    s0, n0 = case.unit_rows(5, 0, 1)
+    sc[s0:s0 + n0] = 2.0
+    for seq, h in ((6, 0), (8, 1)):
+        s1, n1 = case.unit_rows(seq, 0, h)
+        sc[s1:s1 + n1] = g.normal(size=n1).astype(np.float32)
+    s2, n2 = case.unit_rows(9, 0, 0)
+    sc[s2:s2 + n2] = np.nan
+    sc[s2 + g.choice(n2, size=1000, replace=False)] = g.normal(size=1000).astype(np.float32)
+    res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
+    check_selection_exact(case, res)
+    ostart, b = case.unit_out_rows(5, 0, 1)
+    np.testing.assert_array_equal(res["kept"][ostart:ostart + b].cpu().numpy(), np.arange(32767))
+    ostart, b = case.unit_out_rows(9, 0, 0)
+    assert int(res["kept"][ostart + b - 1]) < n2
+
+
+def test_select_stream_edge_cases_exact():
+    """A batch whose longest unit (35840 keys) takes the streaming select
+    (4096 < n <= 35840, keys in per-wave segments): empty, single-key, fully
+    kept and budget-0 units, lengths that are not multiples of 64, units far
+    shorter than the segments of 8 waves; NaN, signed zeros, infinities and
+    denormals; an all-equal unit (the candidate list of the top digit
+    overflows, so the lower digits come from sweeps over the unit) and
+    normal scores (the lower digits come from the candidate list)."""
+    lens = [0, 1, 5, 64, 4097, 35840, 20000, 9999, 12345, 513]
+    budgets = [4, 0, 9, 64, 1, 35839, 2, 9998, 6000, 100]
+    case = _hand_case(lens, budgets)
+    rows = case.total_rows()
+    g = np.random.default_rng(29)
+    pool = np.array([0.0, -0.0, 1.5, -1.5, np.inf, -np.inf, np.nan, 3.25, 1e-38, -1e-38], np.float32)
+    sc = g.choice(pool, size=rows).astype(np.float32)
+    s0, n0 = case.unit_rows(5, 0, 1)
+    sc[s0:s0 + n0] = 2.0
+    for seq, h in ((6, 0), (8, 1), (9, 0)):
+        s1, n1 = case.unit_rows(seq, 0, h)
+        sc[s1:s1 + n1] = g.normal(size=n1).astype(np.float32)
+    res = gpu_run(case, scores_in=torch.as_tensor(sc, device=DEV))
+    check_selection_exact(case, res)
+    ostart, b = case.unit_out_rows(5, 0, 1)
+    np.testing.assert_array_equal(res["kept"][ostart:ostart + b].cpu().numpy(), np.arange(35839))
 
 
 def test_select_split_edge_cases_exact():
