@@ -19,11 +19,17 @@
 
 namespace tri {
 
+// Order-preserving key of a score: non-negative floats map to their bits
+// with the top bit set, negative ones to their complemented bits; -0 keys
+// as +0 and NaN as 0, below every number.  x + 0.0f turns -0 into +0 and
+// leaves every other value's bits as they are (these kernels keep fp32
+// denormals, and the sum is exact), so one add replaces a compare and a
+// select.
 __device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN: below every number
-  if (u == 0x80000000u) u = 0u;                      // -0 ranks as +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const float y = x + 0.0f;
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return y != y ? 0u : k;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,6 +260,19 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// sum over the wave's 64 lanes, in every lane
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// a[0] + ... + a[w - 1] for a wave-uniform w <= 64, one entry per lane
+__device__ __forceinline__ uint32_t sum_below(const uint32_t* a, int w) {
+  const int lane = threadIdx.x & 63;
+  return __builtin_amdgcn_readfirstlane(wave_sum(lane < w ? a[lane] : 0u));
+}
+
 // Calls f(i, valid, x) for each score of the wave's segment [s0, s0 + seg)
 // (seg a multiple of 64; scores at i >= s1 invalid), kStreamBatch loads in
 // flight per lane.  Every lane of the wave makes every call.
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(
 // pass over the list; if the list overflows, over the held keys.  At most
 // 64 VGPRs, so that two work-groups of 1024 threads share a CU.
 // ---------------------------------------------------------------------------
-constexpr int kHeldCand = 4096;  // listed keys and their indices (32 KB)
+constexpr int kHeldCand = 4096;  // listed keys and their indices (32 KB), split over the waves
 
 // A copy of x the compiler cannot see through: per-lane values derived from
 // it in a later phase are recomputed there instead of being kept live from
@@ -456,8 +475,8 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
   __shared__ uint32_t cand_key[kHeldCand], cand_idx[kHeldCand];
   __shared__ uint32_t sel[2];
   __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t wgt[NW], weq[NW];
-  __shared__ uint32_t ncand;
+  __shared__ uint32_t wgt[NW], weq[NW], wcnt[NW];
+  constexpr int kHeldWaveCand = kHeldCand / NW;  // list entries per wave
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -469,17 +488,20 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
   if (wave * SEG + SEG <= n) {  // the whole range real: unconditional loads, all in flight
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = order_key(in[s0 + 64 * j]);
-  } else {
+  } else {  // the wave holding the unit's end: per 64-key step, whole, partial or past n
+    const int w0 = wave * SEG;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = s0 + 64 * j < n ? order_key(in[s0 + 64 * j]) : 0u;
+    for (int j = 0; j < KPT; ++j) {
+      if (w0 + 64 * j + 64 <= n)
+        key[j] = order_key(in[s0 + 64 * j]);
+      else if (w0 + 64 * j < n)
+        key[j] = s0 + 64 * j < n ? order_key(in[s0 + 64 * j]) : 0u;
+      else
+        key[j] = 0u;
+    }
   }
 
   for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
-  if (tid < NW) {
-    wgt[tid] = 0u;
-    weq[tid] = 0u;
-  }
-  if (tid == 0) ncand = 0u;
   __syncthreads();
   // top digit
 #pragma unroll
@@ -489,28 +511,32 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
   const uint32_t bin0 = pick_bin<NT>(hist, (uint32_t)b, sel, wsum, &above);
   uint32_t kk = (uint32_t)b - above;
 
-  // keys above bin0 counted per wave, keys in bin0 listed
+  // keys above bin0 counted per wave; keys in bin0 listed, each wave in its
+  // own part of the list (no atomics: the wave keeps its count in a scalar)
   const uint32_t lo = bin0 << 20, hi_k = (bin0 + 1u) << 20;  // bin0 <= 0xff8: no wrap
-  uint32_t hi = 0;  // wave-uniform
+  uint32_t hi = 0, cnt = 0;  // wave-uniform
   const int s0c = fresh(s0);
+  uint32_t* const my_key = cand_key + wave * kHeldWaveCand;
+  uint32_t* const my_idx = cand_idx + wave * kHeldWaveCand;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     hi += (uint32_t)__popcll(__ballot(key[j] >= hi_k));
+    asm volatile("" : "+s"(hi));  // count now: a deferred count holds its mask in SGPRs
     const bool c = key[j] >= lo && key[j] < hi_k;
     const uint64_t cm = __ballot(c);
     if (cm != 0) {
-      uint32_t first = 0;
-      if (lane == 0) first = atomicAdd(&ncand, (uint32_t)__popcll(cm));
-      const uint32_t slot = __builtin_amdgcn_readfirstlane(first) + lanes_below(cm);
-      if (c && slot < (uint32_t)kHeldCand) {
-        cand_key[slot] = key[j];
-        cand_idx[slot] = (uint32_t)(s0c + 64 * j);
+      const uint32_t slot = cnt + lanes_below(cm);
+      if (c && slot < (uint32_t)kHeldWaveCand) {
+        my_key[slot] = key[j];
+        my_idx[slot] = (uint32_t)(s0c + 64 * j);
       }
+      cnt += (uint32_t)__popcll(cm);
     }
   }
+  if (lane == 0) wcnt[wave] = cnt;
   __syncthreads();
-  const uint32_t nc = ncand;
-  const bool listed = nc <= (uint32_t)kHeldCand;
+  const bool listed =
+      __ballot(lane < NW && wcnt[lane < NW ? lane : 0] > (uint32_t)kHeldWaveCand) == 0;
   uint32_t prefix = lo, mask = 0xfff00000u;
 #pragma unroll 1
   for (int pass = 1; pass < 3; ++pass) {
@@ -519,9 +545,11 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     __syncthreads();
     if (listed) {
-      for (uint32_t c = tid; c < nc; c += NT) {
-        const uint32_t k = cand_key[c];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+      for (int c = tid; c < kHeldCand; c += NT) {
+        if ((uint32_t)(c % kHeldWaveCand) < wcnt[c / kHeldWaveCand]) {
+          const uint32_t k = cand_key[c];
+          if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+        }
       }
     } else {
 #pragma unroll
@@ -536,34 +564,31 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
   }
   const uint32_t T = prefix, quota = kk;
 
-  // keys > T and == T per wave
+  // keys > T and == T per wave: from the wave's own list, or its held keys
+  uint32_t gt = 0, eq = 0;
   if (listed) {
-    if (lane == 0) atomicAdd(&wgt[wave], hi);
-    for (uint32_t c = tid; c < nc; c += NT) {
-      const uint32_t k = cand_key[c], w = cand_idx[c] / (uint32_t)SEG;
-      if (k > T) atomicAdd(&wgt[w], 1u);
-      else if (k == T) atomicAdd(&weq[w], 1u);
+    for (uint32_t c = lane; c < cnt; c += 64) {
+      const uint32_t k = my_key[c];
+      gt += k > T ? 1u : 0u;
+      eq += k == T ? 1u : 0u;
     }
+    gt = hi + __builtin_amdgcn_readfirstlane(wave_sum(gt));  // listed keys above T, and above bin0
+    eq = __builtin_amdgcn_readfirstlane(wave_sum(eq));
   } else {
-    uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       gt += (uint32_t)__popcll(__ballot(key[j] > T));
       eq += (uint32_t)__popcll(__ballot(key[j] == T));
     }
-    if (lane == 0) {
-      wgt[wave] = gt;
-      weq[wave] = eq;
-    }
+  }
+  if (lane == 0) {
+    wgt[wave] = gt;
+    weq[wave] = eq;
   }
   __syncthreads();
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {  // wave-uniform trip count
-    gt_before += wgt[w];
-    eq_before += weq[w];
-  }
+  const uint32_t gt_before = sum_below(wgt, wave), eq_before = sum_below(weq, wave);
   const uint32_t eq_left = quota > eq_before ? quota - eq_before : 0u;
-  if (wgt[wave] + min(eq_left, weq[wave]) == 0u) return;  // nothing kept in this wave's range
+  if (gt + min(eq_left, eq) == 0u) return;  // nothing kept in this wave's range
 
   // ordered emission
   uint32_t pos0 = gt_before + min(quota, eq_before), eq_run = eq_before;
