@@ -386,11 +386,15 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                      hipStream_t s) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
   double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
-  hipError_t e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
+  // a plan that fits one launch's arguments travels with the prologue
+  const size_t plan_bytes = p.seqs.size() * sizeof(SeqInfo);
+  const bool inline_plan = plan_bytes <= sizeof(tri::ArgWords);
+  hipError_t e = inline_plan ? hipSuccess : upload(dseq, p.seqs.data(), plan_bytes, s);
   if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
   if (e == hipSuccess)
-    e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq, q_centre, q_absmean, q_R, doff,
-                             om.n, !om.max, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
+    e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq,
+                             inline_plan ? p.seqs.data() : nullptr, q_centre, q_absmean, q_R,
+                             doff, om.n, !om.max, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
                              (double2*)(ws + p.off_E), (uint32_t*)(ws + p.off_ctrl),
                              tri::kCtrlHeader, (double*)(ws + p.off_stats), p.n_stat_slots, s);
   if (e != hipSuccess) return e;

@@ -246,9 +246,12 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const
 // C_f is the mean of exp(i omega_f delta) over the offsets, summed in their
 // order (the default set is {2^0, ..., 2^16}); without folding C_f = 1.
 // All in fp64 (W is stored as fp32: it multiplies fp32 magnitudes).
+// With plan_words > 0 the call's sequence plan arrives in the arguments:
+// block 0 writes it to seqs (for the kernels after this one) and the
+// query positions are read from the arguments.
 __global__ __launch_bounds__(256) void prologue_kernel(
-    int L, int Hq, int d, double theta, int S, const SeqInfo* __restrict__ seqs,
-    const float* __restrict__ q_centre, const float* __restrict__ q_absmean,
+    int L, int Hq, int d, double theta, int S, SeqInfo* __restrict__ seqs, const ArgWords plan,
+    int plan_words, const float* __restrict__ q_centre, const float* __restrict__ q_absmean,
     const float* __restrict__ q_R, const double* __restrict__ offsets, int nD, int fold,
     double2* __restrict__ P, float* __restrict__ W, double2* __restrict__ E,
     uint32_t* __restrict__ ctrl, int64_t n_ctrl, double* __restrict__ stat_slots,
@@ -256,6 +259,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(
   const int F = d >> 1;
   const int64_t n_stat = (int64_t)L * Hq * F;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < plan_words; i += blockDim.x)
+      reinterpret_cast<uint32_t*>(seqs)[i] = plan.w[i];
   // score control words and published-statistics slots of this call
   if (idx < n_ctrl) ctrl[idx] = 0u;
   if (idx < n_stat_slots)
@@ -295,24 +301,35 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const int s = (int)(j / F), f = (int)(j % F);
     const double omega = pow(theta, -2.0 * (double)f / (double)d);
     double sn, cs;
-    sincos(omega * (double)seqs[s].p_q, &sn, &cs);
+    const int32_t p_q =
+        plan_words ? reinterpret_cast<const SeqInfo*>(plan.w)[s].p_q : seqs[s].p_q;
+    sincos(omega * (double)p_q, &sn, &cs);
     E[j] = make_double2(cs, sn);
   }
 }
 
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqInfo* seqs,
-                           const float* q_centre, const float* q_absmean, const float* q_R,
-                           const double* offsets, int n_offsets, bool fold, double2* P,
-                           float* W, double2* E, uint32_t* ctrl, int64_t n_ctrl,
-                           double* stat_slots, int64_t n_stat_slots, hipStream_t st) {
+                           const SeqInfo* plan_host, const float* q_centre,
+                           const float* q_absmean, const float* q_R, const double* offsets,
+                           int n_offsets, bool fold, double2* P, float* W, double2* E,
+                           uint32_t* ctrl, int64_t n_ctrl, double* stat_slots,
+                           int64_t n_stat_slots, hipStream_t st) {
   int64_t total = (int64_t)L * Hq * (d / 2) + (int64_t)S * (d / 2);
   if (n_stat_slots > total) total = n_stat_slots;
   if (n_ctrl > total) total = n_ctrl;
   const int nD = offsets ? n_offsets : 17;
   const int blocks = (int)((total + 255) / 256);
+  ArgWords plan;
+  int plan_words = 0;
+  if (plan_host) {
+    const size_t bytes = (size_t)S * sizeof(SeqInfo);
+    if (bytes > sizeof(plan.w)) return hipErrorInvalidValue;
+    std::memcpy(plan.w, plan_host, bytes);
+    plan_words = (int)(bytes / 4);
+  }
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, st, L, Hq, d, theta, S,
-                     seqs, q_centre, q_absmean, q_R, offsets, nD, fold ? 1 : 0, P, W, E, ctrl,
-                     n_ctrl, stat_slots, n_stat_slots);
+                     const_cast<SeqInfo*>(seqs), plan, plan_words, q_centre, q_absmean, q_R,
+                     offsets, nD, fold ? 1 : 0, P, W, E, ctrl, n_ctrl, stat_slots, n_stat_slots);
   return hipGetLastError();
 }
 
@@ -321,9 +338,6 @@ hipError_t launch_prologue(int L, int Hq, int d, double theta, int S, const SeqI
 // the data travels with the launch, so nothing on the host has to outlive
 // the call, no staging memory is held, and the copy is an ordinary kernel
 // node under stream capture.
-struct ArgWords {
-  uint32_t w[kArgWords];
-};
 
 __global__ __launch_bounds__(256) void write_args_kernel(ArgWords a, int n,
                                                          uint32_t* __restrict__ dst) {

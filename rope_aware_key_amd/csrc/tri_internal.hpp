@@ -140,12 +140,22 @@ hipError_t launch_calibrate(int L, int Hq, int d, double theta, bool half, const
                             const int32_t* q_pos, int64_t n_samples, float* centre,
                             float* absmean, float* R, void* workspace, hipStream_t st);
 
+// 32-bit words one launch carries in its arguments (2560 bytes).
+constexpr int kArgWords = 640;
+struct ArgWords {
+  uint32_t w[kArgWords];
+};
+
 // offsets: device array of n_offsets distances, or NULL for the default set
 // {2^0, ..., 2^16}.  fold: P = E[q] * mean_delta exp(i omega delta) when
 // true, P = E[q] when false (the offsets are applied later, per row).
+// plan_host: the S sequences' host plan when it fits one launch's argument
+// words (S * 40 <= 2560 bytes): the prologue then writes it to seqs itself
+// and reads the query positions from its arguments; NULL when the plan was
+// uploaded to seqs before.
 hipError_t launch_prologue(int L, int Hq, int d, double theta, int S,
-                           const SeqInfo* seqs, const float* q_centre,
-                           const float* q_absmean, const float* q_R,
+                           const SeqInfo* seqs, const SeqInfo* plan_host,
+                           const float* q_centre, const float* q_absmean, const float* q_R,
                            const double* offsets, int n_offsets, bool fold, double2* P,
                            float* W, double2* E, uint32_t* ctrl, int64_t n_ctrl,
                            double* stat_slots, int64_t n_stat_slots, hipStream_t st);
@@ -241,8 +251,6 @@ hipError_t launch_append(const DecodeItem* items, int S, int LH, int d, int64_t 
 hipError_t launch_protect(const SeqInfo* seqs, int S, int LH, int sink, int recent,
                           float* scores, hipStream_t st);
 
-// 32-bit words one write_args launch carries in its arguments (2560 bytes).
-constexpr int kArgWords = 640;
 // Writes `bytes` (a multiple of 4) of host memory to dst (device) through
 // kernel arguments: no staging memory, host data free once this returns.
 hipError_t launch_write_args(void* dst, const void* host, size_t bytes, hipStream_t st);
