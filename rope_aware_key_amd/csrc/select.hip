@@ -469,10 +469,12 @@ __device__ __forceinline__ int fresh(int x) {
 // the b kept indices to out.  Every thread calls it (it holds barriers).
 template <int NT, int KPT>
 __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_t* __restrict__ out,
-                                            int n, int b) {
+                                            int n, int b, uint32_t* __restrict__ buf,
+                                            bool keep_in_lds) {
   constexpr int NW = NT / 64, SEG = 64 * KPT;
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t cand_key[kHeldCand], cand_idx[kHeldCand];
+  uint32_t* const hist = buf;                            // kHistBins
+  uint32_t* const cand_key = buf + kHistBins;            // kHeldCand
+  uint32_t* const cand_idx = buf + kHistBins + kHeldCand;  // kHeldCand
   __shared__ uint32_t sel[2];
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t wgt[NW], weq[NW], wcnt[NW];
@@ -603,7 +605,10 @@ __device__ __forceinline__ void held_select(const float* __restrict__ in, int32_
     }
     const uint64_t km = __ballot(keep);
     const uint32_t pos = pos0 + lanes_below(km);
-    if (keep && pos < (uint32_t)b) out[pos] = s0e + 64 * j;
+    if (keep && pos < (uint32_t)b) {
+      out[pos] = s0e + 64 * j;
+      if (keep_in_lds) buf[pos] = s0e + 64 * j;  // the lists are dead by now
+    }
     pos0 += (uint32_t)__popcll(km);
   }
 }
@@ -657,14 +662,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
   const int64_t in0 = si.row_base + (int64_t)lg * si.in_stride;
   const int64_t out0 = si.out_base + (int64_t)lg * si.out_stride;
   int32_t* out = kept + out0;
+  // histogram and lists of the selection; afterwards, when the gathers
+  // follow and b fits, the kept indices
+  __shared__ uint32_t buf[kHistBins + 2 * kHeldCand];
+  const bool in_lds = COPY && b <= kHistBins + 2 * kHeldCand;
   if (b >= n) {
-    for (int i = tid; i < n; i += NT) out[i] = i;
+    for (int i = tid; i < n; i += NT) {
+      out[i] = i;
+      if (in_lds) buf[i] = i;
+    }
   } else {
-    held_select<NT, KPT>(scores + in0, out, n, b);
+    held_select<NT, KPT>(scores + in0, out, n, b, buf, in_lds);
   }
   if constexpr (COPY) {
-    // The unit's kept indices, written by this work-group: complete in L2
-    // after the barrier, and read from there (agent-scope loads skip the
+    // The unit's kept indices, written by this work-group: from LDS when
+    // they fit, else from L2 after the barrier (agent-scope loads skip the
     // CU's L1, which may hold a line shared with a neighbouring unit's
     // indices from before they were written).
     __syncthreads();
@@ -673,7 +685,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
     const int sub = tid / lpr, part = tid - sub * lpr;
 #pragma unroll 2
     for (int r = sub < rows_per_pass ? sub : b; r < b; r += rows_per_pass) {
-      const int idx = __hip_atomic_load(out + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int idx = in_lds ? (int)buf[r]
+                             : __hip_atomic_load(out + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((uint32_t)idx < (uint32_t)n) copy_row_part(ca, s, lg, in0, out0, idx, r, part);
     }
   }
