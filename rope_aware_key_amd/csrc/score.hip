@@ -285,7 +285,8 @@ __global__ __launch_bounds__(256) void zmax_kernel(
 #pragma unroll
     for (int h = 0; h < GT; ++h)
       if (h < G) best = fmax(best, ((double)blk[key * GP + h] - mu_s[h]) * inv_s[h]);
-    scores[tk.row0 + tk.key0 + key] = (float)best;
+    // non-temporal: written once here, read once by the select kernel
+    __builtin_nontemporal_store((float)best, scores + tk.row0 + tk.key0 + key);
   }
 }
 
