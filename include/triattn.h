@@ -18,9 +18,9 @@
  *    generated tokens.
  *  - shibing624 blog review of TriAttention, section "具体操作分三步",
  *    step 1: statistics are calibrated offline, once, from ~10K tokens.
- *  - jaedaily.cn KV-cache compression tutorial, eviction step: the
- *    evict_kv_cache snippet keeps the top-k indices, sorts them to keep the
- *    time order, and gathers keys and values with them.
+ *  - jaedaily.cn KV-cache compression tutorial, eviction step: the top-k
+ *    indices are kept, sorted to keep the time order, and keys and values
+ *    are gathered with them.
  *
  * Conventions shared by every call
  *  - d = head_dim, F = d/2 RoPE bands.  Band f of a vector x is the pair
@@ -295,8 +295,8 @@ tri_status tri_score_offsets(const tri_shape* shape, int32_t num_seqs,
  * Per unit, b_s = min(budget[s], n_s) keys are kept: the highest scores,
  * equal scores resolved toward the lower index (= lower position); -0.0
  * equals +0.0 and NaN ranks below every number (talk page, closing top-B
- * step; tutorial page, evict_kv_cache snippet, which sorts the kept indices
- * to keep the time order).
+ * step; tutorial page, eviction step, which sorts the kept indices to keep
+ * the time order).
  *
  *  budget    [host][num_seqs] B_s >= 0.
  *  scores    fp32 per row (as tri_score writes them).

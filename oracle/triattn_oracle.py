@@ -19,15 +19,15 @@ Sources (cited by page title and the section or equation on that page):
 * [topB]      same page -- the closing step: rank keys by the averaged score
               and keep the top B.
 * [gqa]       hyper.ai summary of arXiv 2604.04921, section "方法": average over
-              future query positions, then for grouped-query attention
-              "normalise then aggregate": z-score per query head, max over the
-              group.
+              future query positions, then for grouped-query attention the
+              scores are normalised before they are aggregated: z-score per
+              query head, max over the group.
 * [calib]     hyper.ai summary, section "方法" (R = |E[q]| / E[|q|]) and the
               shibing624 blog review, section "具体操作分三步" step 1 (offline
               calibration on ~10K tokens, done once).
-* [evict]     jaedaily.cn KV-cache compression tutorial, eviction step: the
-              ``evict_kv_cache`` snippet (top-k, then sort the kept indices so
-              the time order is preserved, then gather keys and values).
+* [evict]     jaedaily.cn KV-cache compression tutorial, eviction step
+              (top-k, then the kept indices sorted so the time order is
+              preserved, then keys and values gathered).
 * [stream]    same tutorial page, streaming-generation paragraph: each decode
               step appends the new token's K and V, eviction runs when the
               cache exceeds the budget, and the most recent r tokens are
