@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void score_max_kernel(
               run[bb] = fmaxf(run[bb], fmaxf(fmaxf(acc[bb][0], acc[bb][1]),
                                              fmaxf(acc[bb][2], acc[bb][3])));
           }
-          // head of this round: 4*kk + q (own slot), or kk spread over all
+          // head of this kk step: 4*kk + q (own slot), or kk spread over all
           // slots (merge the four, lane kk % 4 keeps it as entry kk / 4)
           int ent = kk;
           bool own = true;

@@ -57,6 +57,6 @@ def score_units(tasks):
 
 
 def workers():
-    """Worker processes: the host cores this process may use, at most 16 (a
-    GPU machine's CPU share)."""
+    """Worker processes: the host cores this process may use, at most 16 (one
+    GPU's share of the host's cores on a shared machine)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
