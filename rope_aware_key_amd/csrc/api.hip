@@ -386,12 +386,14 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                      hipStream_t s) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
   double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
-  // a plan that fits one launch's arguments travels with the prologue
+  // a plan that fits one launch's arguments travels with the first kernel
   const size_t plan_bytes = p.seqs.size() * sizeof(SeqInfo);
   const bool inline_plan = plan_bytes <= sizeof(tri::ArgWords);
+  // the fused averaged path prepares in one kernel of its own (no prologue)
+  const bool prep_fused = p.fused && !om.max;
   hipError_t e = inline_plan ? hipSuccess : upload(dseq, p.seqs.data(), plan_bytes, s);
   if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !prep_fused)
     e = tri::launch_prologue(p.L, p.Hq, p.d, theta, p.S, dseq,
                              inline_plan ? p.seqs.data() : nullptr, q_centre, q_absmean, q_R,
                              doff, om.n, !om.max, (double2*)(ws + p.off_P), (float*)(ws + p.off_W),
@@ -406,12 +408,17 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                                  doff, ws + p.off_apack, k, raw, (double*)(ws + p.off_stats),
                                  (double*)(ws + p.off_ustats), scores, head_stats, p.half,
                                  p.in_pg, s);
-  if (p.fused)
+  if (p.fused) {
+    const tri::PrepArgs pa{theta, p.Hq, q_centre, q_absmean, q_R, doff, om.n,
+                           inline_plan ? p.seqs.data() : nullptr, tri::kCtrlHeader,
+                           p.n_stat_slots};
     return tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
                                    (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                                    (const double2*)(ws + p.off_E), ws + p.off_apack, k,
                                    (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
-                                   scores, raw_scores, head_stats, p.half, p.in_pg, s);
+                                   scores, raw_scores, head_stats, p.half, p.in_pg,
+                                   prep_fused ? &pa : nullptr, s);
+  }
   return tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                            (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
                            (const double2*)(ws + p.off_E), k, raw, (double*)(ws + p.off_stats),

@@ -68,6 +68,8 @@
 #include <mutex>
 #include <tuple>
 
+#include <cstring>
+
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -745,6 +747,125 @@ __global__ __launch_bounds__(256) void pack_operands_kernel(
                                      __float_as_uint(wv[2]), __float_as_uint(wv[3]));
 }
 
+// The fused averaged path's preparation in one launch, in place of the
+// prologue and the operand pack: block 0 writes the plan carried in the
+// arguments (plan_words > 0); every thread resets its share of the control
+// words and the published-statistics slots; the blocks that pack operands
+// first form, in LDS, C_f for every band (the offsets dealt over the
+// block's threads, the partial sums added in a fixed order) and E for the
+// sequences their units belong to, then pack each unit's operands as
+// pack_operands_kernel does from P = E[q] * C_f, W and E.
+template <int STEPS>
+__global__ __launch_bounds__(256) void prep_fused_kernel(
+    int S, int L, int Hkv, int G, int Hq, bool half, double theta, SeqInfo* __restrict__ seqs,
+    const ArgWords plan, int plan_words, const float* __restrict__ q_centre,
+    const float* __restrict__ q_absmean, const float* __restrict__ q_R,
+    const double* __restrict__ offsets, int nD, uint32_t* __restrict__ ctrl, int64_t n_ctrl,
+    double* __restrict__ stat_slots, int64_t n_stat_slots, uint4* __restrict__ apack) {
+  constexpr int F = STEPS * 16, D = STEPS * 32;
+  constexpr int R = 256 / F;  // threads per band for C_f (F <= 128)
+  const int tid = threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + tid;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < plan_words; i += 256) reinterpret_cast<uint32_t*>(seqs)[i] = plan.w[i];
+  if (idx < n_ctrl) ctrl[idx] = 0u;
+  if (idx < n_stat_slots)
+    reinterpret_cast<unsigned long long*>(stat_slots)[idx] = kStatSentinel;
+  const int64_t units = (int64_t)S * L * Hkv;
+  const int64_t pack_threads = units * STEPS * 64;
+  if ((int64_t)blockIdx.x * 256 >= pack_threads) return;  // block-uniform
+
+  __shared__ double2 part[R][F];
+  __shared__ double2 cf[F];
+  __shared__ double2 es[256];  // E of the block's sequences: at most 256 (sequence, band)
+  {
+    const int f = tid % F, r = tid / F;
+    if (r < R) {
+      const double omega = pow(theta, -2.0 * (double)f / (double)D);
+      double cr = 0.0, ci = 0.0;
+      for (int j = r; j < nD; j += R) {
+        const double delta = offsets ? offsets[j] : ldexp(1.0, j);
+        double sn, cs;
+        sincos(omega * delta, &sn, &cs);
+        cr += cs;
+        ci += sn;
+      }
+      part[r][f] = make_double2(cr, ci);
+    }
+  }
+  const int LH = L * Hkv;
+  const int64_t u_lo = (int64_t)blockIdx.x * 256 / (64 * STEPS);
+  const int64_t u_hi = ((int64_t)blockIdx.x * 256 + 255) / (64 * STEPS);
+  const int s_lo = (int)(u_lo / LH);
+  const int s_hi = (int)((u_hi < units ? u_hi : units - 1) / LH);
+  const int ns = s_hi - s_lo + 1;
+  for (int e = tid; e < ns * F; e += 256) {
+    const int s = s_lo + e / F, f = e % F;
+    const int32_t p_q =
+        plan_words ? reinterpret_cast<const SeqInfo*>(plan.w)[s].p_q : seqs[s].p_q;
+    const double omega = pow(theta, -2.0 * (double)f / (double)D);
+    double sn, cs;
+    sincos(omega * (double)p_q, &sn, &cs);
+    es[e] = make_double2(cs, sn);
+  }
+  __syncthreads();
+  if (tid < F) {
+    double cr = 0.0, ci = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      cr += part[r][tid].x;
+      ci += part[r][tid].y;
+    }
+    const double inv = 1.0 / (double)nD;
+    cf[tid] = make_double2(cr * inv, ci * inv);
+  }
+  __syncthreads();
+  if (idx >= pack_threads) return;
+
+  const int lane = (int)(idx & 63);
+  const int st = (int)((idx >> 6) % STEPS);
+  const int64_t unit = idx / (64 * STEPS);
+  const int lg = (int)(unit % LH);
+  const int s = (int)(unit / LH);
+  const int l = lg / Hkv, g = lg % Hkv;
+  const int m = lane & 15, q = lane >> 4;
+  uint32_t h3[8], m3[8], l3[8];
+  float wv[4];
+  const bool live = m < G;
+  const int64_t pbase = ((int64_t)l * Hq + g * G + (live ? m : 0)) * F;
+  const double2* ev_s = es + (s - s_lo) * F;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = 32 * st + 8 * q + j;
+    const int f = elem_band(e, D, half);
+    double x = 0.0;
+    if (live) {
+      const double qr = (double)q_centre[2 * (pbase + f)];
+      const double qi = (double)q_centre[2 * (pbase + f) + 1];
+      const double2 c = cf[f];
+      const double2 pv = make_double2(qr * c.x - qi * c.y, qr * c.y + qi * c.x);
+      const double2 ev = ev_s[f];
+      x = elem_part(e, D, half) ? pv.x * ev.y + pv.y * ev.x : pv.x * ev.x - pv.y * ev.y;
+    }
+    split3(x, h3[j], m3[j], l3[j]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t wi = pbase + slot_band(st, q, u, STEPS, half);
+    wv[u] = live ? (float)((1.0 - (double)q_R[wi]) * (double)q_absmean[wi]) : 0.f;
+  }
+  auto pack8 = [](const uint32_t (&v)[8]) {
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                      v[6] | (v[7] << 16));
+  };
+  uint4* op = apack + unit * (4 * STEPS) * 64 + lane;
+  op[(4 * st + 0) * 64] = pack8(h3);
+  op[(4 * st + 1) * 64] = pack8(m3);
+  op[(4 * st + 2) * 64] = pack8(l3);
+  op[(4 * st + 3) * 64] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
+                                     __float_as_uint(wv[2]), __float_as_uint(wv[3]));
+}
+
 // Polls of a chunk-statistics slot before a finalizing work-group gives up
 // on it (the wait ends by construction; this only bounds a broken one).
 static std::atomic<uint32_t> g_wait_limit{1u << 22};
@@ -756,12 +877,34 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G,
                                  const double2* P, const float* W, const double2* E,
                                  uint4* apack, const uint16_t* k, const Pages& pg, double* cs,
-                                 uint32_t* ctrl, float* scores, float* raw, double* hs) {
+                                 uint32_t* ctrl, float* scores, float* raw, double* hs,
+                                 const PrepArgs* prep) {
   const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
-  hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
-                     dim3(256), 0, st, S, L, Hkv, G, HALF, P, W, E, apack);
+  if (prep) {
+    ArgWords plan;
+    int plan_words = 0;
+    if (prep->plan_host) {
+      const size_t bytes = (size_t)S * sizeof(SeqInfo);
+      if (bytes > sizeof(plan.w)) return hipErrorInvalidValue;
+      std::memcpy(plan.w, prep->plan_host, bytes);
+      plan_words = (int)(bytes / 4);
+    }
+    int64_t total = pack_threads;
+    if (prep->n_stat_slots > total) total = prep->n_stat_slots;
+    if (prep->n_ctrl > total) total = prep->n_ctrl;
+    if (total < 1) total = 1;  // block 0 writes the plan
+    const int nD = prep->offsets ? prep->n_offsets : 17;
+    hipLaunchKernelGGL(prep_fused_kernel<STEPS>, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, st, S, L, Hkv, G, prep->Hq, HALF, prep->theta,
+                       const_cast<SeqInfo*>(seqs), plan, plan_words, prep->q_centre,
+                       prep->q_absmean, prep->q_R, prep->offsets, nD, ctrl, prep->n_ctrl, cs,
+                       prep->n_stat_slots, apack);
+  } else {
+    hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
+                       dim3(256), 0, st, S, L, Hkv, G, HALF, P, W, E, apack);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || total_tickets == 0) return e;
   const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF, PAGED>);
   static const hipError_t attr = hipFuncSetAttribute(
       kern, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds);
@@ -876,8 +1019,8 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
                               const double2* E, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
                               double* head_stats, bool half, const Pages& pg,
-                              hipStream_t st) {
-  if (total_tickets == 0) return hipSuccess;
+                              const PrepArgs* prep, hipStream_t st) {
+  if (total_tickets == 0 && !prep) return hipSuccess;
   const size_t lds = 2 * (size_t)G * (ch + kRawPad) * sizeof(float);
   if (lds > (size_t)kFusedMaxLds || !fused_supported(d, half)) return hipErrorInvalidValue;
   if (pg.table && pg.page_shift < 4) return hipErrorInvalidValue;  // pages of >= 16 tokens
@@ -885,7 +1028,8 @@ hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G,
 #define TRI_CASE(n, h, pgd)                                                                   \
   case n:                                                                                     \
     return launch_fused_t<n, h, pgd>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, \
-                                     ap, k, pg, chunk_stats, ctrl, scores, raw, head_stats);
+                                     ap, k, pg, chunk_stats, ctrl, scores, raw, head_stats,   \
+                                     prep);
 #define TRI_LAYOUTS(pgd)                                                                      \
   if (half) {                                                                                 \
     switch (d / 32) {                                                                         \
