@@ -35,9 +35,10 @@ PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 COPY_PROBE_BYTES = 1 << 30
 STREAM_PROBE_BYTES = 4 << 30  # well past the 256 MB Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_score_long_reasoning_32k_to_2048.json")
-# The fused score kernel, its operand pack and launch shape (score_mfma.hip),
-# the prologue (calib.hip) and the shared device helpers (tri_internal.hpp):
-# the kernels one tri_score call runs on the 32K->2048 workload.
+# The fused score kernel, its preparation kernel and launch shape
+# (score_mfma.hip), the prologue of the other paths (calib.hip) and the
+# shared device helpers (tri_internal.hpp): the kernels one tri_score call
+# runs on the 32K->2048 workload.
 KERNEL_SOURCES = ["score_mfma.hip", "calib.hip", "tri_internal.hpp"]
 
 
@@ -175,8 +176,8 @@ TRAFFIC_RUNS = {
                                   "python3 bench.py --stream-probe"),
 }
 # kernels of one tri_score call on the 32K->2048 workload (its plan travels
-# in the prologue's arguments)
-SCORE_KERNELS = ("tri::prologue_kernel", "tri::pack_operands_kernel", "tri::score_fused_kernel")
+# in the preparation kernel's arguments)
+SCORE_KERNELS = ("tri::prep_fused_kernel", "tri::score_fused_kernel")
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_long_reasoning_32k_to_2048.md")
 
 
@@ -239,7 +240,7 @@ def write_traffic(run_root, out):
     cfg = synth_config_bytes("long_reasoning")
     t = {
         "what": "HBM bytes per tri_score call on the 32K->2048 long-reasoning workload (28 layers, "
-                "4 KV heads, 28 q heads, d 128, batch 8): prologue + operand pack + fused score kernel",
+                "4 KV heads, 28 q heads, d 128, batch 8): preparation kernel + fused score kernel",
         "kernel_source_hash": kernel_source_hash(),
         "fetch_scale": fetch_scale,
         "fetch_scale_from": "stream probe (read-only, the score kernel's load pattern)",
@@ -980,8 +981,8 @@ def main():
                      and not variant
                      and args.rope_layout == "interleaved" else None,
                      "algorithmic_bytes_per_launch": b_score,
-                     "launch": "tri_score call: prologue (carrying the plan), operand pack, "
-                               "fused score kernel",
+                     "launch": "tri_score call: preparation kernel (plan, resets, operand "
+                               "pack), fused score kernel",
                      "timing": "achieved: HIP events around as many back-to-back tri_score "
                                "calls as timed steps, right after them, on the stream the "
                                "kernels run on"},
@@ -1032,9 +1033,9 @@ def main():
         out["offsets"] = {"set": args.offsets, "values": OFFSET_SETS[args.offsets],
                           "reduce": args.reduce}
         out["roofline"]["kernel"] = "tri_score_offsets"
-        out["roofline"]["launch"] = "tri_score_offsets call: prologue + " + (
-            "operand pack + max-over-offsets MFMA kernel + z pass" if args.reduce == "max"
-            else "operand pack + score kernels")
+        out["roofline"]["launch"] = "tri_score_offsets call: " + (
+            "prologue + operand pack + max-over-offsets MFMA kernel + z pass"
+            if args.reduce == "max" else "preparation kernel + score kernels")
         if args.reduce == "max":
             # One row per (head, offset): a dense contraction on the bf16
             # MFMA.  `achieved` counts the method's dot products once
