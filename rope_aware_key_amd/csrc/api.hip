@@ -385,7 +385,14 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                      float* scores, float* raw_scores, double* head_stats, char* ws,
                      hipStream_t s) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
-  double* doff = om.host ? (double*)(ws + p.off_offsets) : nullptr;
+  // a given set equal to the built-in {2^0..2^16} under the mean takes the
+  // built-in path, so the two give the same bits
+  bool builtin = !om.host;
+  if (om.host && !om.max && om.n == 17) {
+    builtin = true;
+    for (int j = 0; j < 17; ++j) builtin = builtin && om.host[j] == std::ldexp(1.0, j);
+  }
+  double* doff = builtin ? nullptr : (double*)(ws + p.off_offsets);
   // a plan that fits one launch's arguments travels with the first kernel
   const size_t plan_bytes = p.seqs.size() * sizeof(SeqInfo);
   const bool inline_plan = plan_bytes <= sizeof(tri::ArgWords);
