@@ -350,7 +350,8 @@ tri_status tri_trig_correlation(const tri_shape* shape, const uint16_t* q,
 /*
  * tri_stream_probe -- read-bandwidth probe (a measurement aid, not part of
  * the method): reads `bytes` of device memory at src once, with 16-byte
- * non-temporal loads spread over every compute unit, and XORs all its
+ * non-temporal loads, one contiguous span per work-group over every
+ * compute unit, and XORs all its
  * 32-bit words into *sink (so no read can be skipped).  Timing it on a
  * buffer the size of a K cache gives the rate a plain streaming read
  * reaches on the device, the practical ceiling of tri_score's K stream.
