@@ -648,11 +648,14 @@ __device__ __forceinline__ void copy_row_part(const CompactArgs& ca, int s, int 
 // Register-held select of one unit per work-group; with COPY the same
 // work-group then gathers the unit's kept rows (the kept indices it just
 // wrote, read back after a barrier), so that one work-group's selection
-// overlaps another's copy on the same CU.
+// overlaps another's copy on the same CU.  Units below `presel` were
+// selected by an earlier launch: their work-groups only gather, so the
+// kernel starts with copies under way instead of every resident
+// work-group selecting at once.
 template <int NT, int KPT, bool COPY>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void select_held_kernel(
     const SeqInfo* __restrict__ seqs, int LH, const float* __restrict__ scores,
-    int32_t* __restrict__ kept, const CompactArgs ca) {
+    int32_t* __restrict__ kept, const CompactArgs ca, int presel) {
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
   const int s = unit / LH, lg = unit % LH;
@@ -665,8 +668,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
   // histogram and lists of the selection; afterwards, when the gathers
   // follow and b fits, the kept indices
   __shared__ uint32_t buf[kHistBins + 2 * kHeldCand];
-  const bool in_lds = COPY && b <= kHistBins + 2 * kHeldCand;
-  if (b >= n) {
+  const bool in_lds = COPY && unit >= presel && b <= kHistBins + 2 * kHeldCand;
+  if (unit < presel) {
+    // kept indices already written
+  } else if (b >= n) {
     for (int i = tid; i < n; i += NT) {
       out[i] = i;
       if (in_lds) buf[i] = i;
@@ -973,12 +978,12 @@ hipError_t launch_select(const SeqInfo* seqs, int S, int LH, int max_n, const fl
     return launch_select_lds<256>(units, max_n, st, seqs, LH, scores, kept_idx);
   if (max_n <= 1024 * 16) {
     hipLaunchKernelGGL((select_held_kernel<1024, 16, false>), dim3((unsigned)units), dim3(1024), 0,
-                       st, seqs, LH, scores, kept_idx, CompactArgs{});
+                       st, seqs, LH, scores, kept_idx, CompactArgs{}, 0);
     return hipGetLastError();
   }
   if (max_n <= 1024 * 32) {
     hipLaunchKernelGGL((select_held_kernel<1024, 32, false>), dim3((unsigned)units), dim3(1024), 0,
-                       st, seqs, LH, scores, kept_idx, CompactArgs{});
+                       st, seqs, LH, scores, kept_idx, CompactArgs{}, 0);
     return hipGetLastError();
   }
   if (max_n <= kSelLdsMaxKeys) {
@@ -1060,14 +1065,37 @@ hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int 
   const int64_t units = (int64_t)S * LH;
   const bool copy = k_out || v_out || pos_out;
   if (units > 0 && copy && max_n > kSelSmallUnit && max_n <= 1024 * 32) {
-    // register-held select and the gathers in one kernel
+    // register-held select and the gathers in one kernel.  With more units
+    // than two rounds of resident work-groups, one unit per CU is selected
+    // first by a select-only launch (a fraction of the gathers' time), so
+    // the gathering kernel starts with one work-group per CU copying while
+    // the other selects.
     const CompactArgs ca{d, k, v, k_pos, k_out, v_out, pos_out, in_pg, out_pg};
-    if (max_n <= 1024 * 16)
-      hipLaunchKernelGGL((select_held_kernel<1024, 16, true>), dim3((unsigned)units), dim3(1024),
-                         0, st, seqs, LH, scores, kept_idx, ca);
-    else
+    int presel = 0;
+    {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+          cus > 0 && units > 2 * (int64_t)cus)
+        presel = cus;
+    }
+    const bool wide = max_n > 1024 * 16;
+    if (presel > 0) {
+      if (wide)
+        hipLaunchKernelGGL((select_held_kernel<1024, 32, false>), dim3((unsigned)presel),
+                           dim3(1024), 0, st, seqs, LH, scores, kept_idx, CompactArgs{}, 0);
+      else
+        hipLaunchKernelGGL((select_held_kernel<1024, 16, false>), dim3((unsigned)presel),
+                           dim3(1024), 0, st, seqs, LH, scores, kept_idx, CompactArgs{}, 0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (wide)
       hipLaunchKernelGGL((select_held_kernel<1024, 32, true>), dim3((unsigned)units), dim3(1024),
-                         0, st, seqs, LH, scores, kept_idx, ca);
+                         0, st, seqs, LH, scores, kept_idx, ca, presel);
+    else
+      hipLaunchKernelGGL((select_held_kernel<1024, 16, true>), dim3((unsigned)units), dim3(1024),
+                         0, st, seqs, LH, scores, kept_idx, ca, presel);
     return hipGetLastError();
   }
   hipError_t e = launch_select(seqs, S, LH, max_n, scores, kept_idx, split_ws, st);
