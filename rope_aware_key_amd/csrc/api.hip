@@ -396,8 +396,8 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
   // a plan that fits one launch's arguments travels with the first kernel
   const size_t plan_bytes = p.seqs.size() * sizeof(SeqInfo);
   const bool inline_plan = plan_bytes <= sizeof(tri::ArgWords);
-  // the fused averaged path prepares in one kernel of its own (no prologue)
-  const bool prep_fused = p.fused && !om.max;
+  // the fused path (the averaged score) prepares in one kernel of its own
+  const bool prep_fused = p.fused;
   hipError_t e = inline_plan ? hipSuccess : upload(dseq, p.seqs.data(), plan_bytes, s);
   if (e == hipSuccess && doff) e = upload(doff, om.host, (size_t)om.n * sizeof(double), s);
   if (e == hipSuccess && !prep_fused)
@@ -420,11 +420,9 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
                            inline_plan ? p.seqs.data() : nullptr, tri::kCtrlHeader,
                            p.n_stat_slots};
     return tri::launch_score_fused(dseq, p.S, p.L, p.Hkv, p.G, p.d, p.chunk, (int)p.tickets,
-                                   (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),
-                                   (const double2*)(ws + p.off_E), ws + p.off_apack, k,
-                                   (double*)(ws + p.off_stats), (uint32_t*)(ws + p.off_ctrl),
-                                   scores, raw_scores, head_stats, p.half, p.in_pg,
-                                   prep_fused ? &pa : nullptr, s);
+                                   ws + p.off_apack, k, (double*)(ws + p.off_stats),
+                                   (uint32_t*)(ws + p.off_ctrl), scores, raw_scores, head_stats,
+                                   p.half, p.in_pg, pa, s);
   }
   return tri::launch_score(dseq, p.S, p.L, p.Hkv, p.G, p.d, (int)p.tickets,
                            (const double2*)(ws + p.off_P), (const float*)(ws + p.off_W),

@@ -15,7 +15,7 @@
 //    terms (hi + mid + lo, ~25 significant bits), so three MFMAs per 32-wide
 //    step reproduce an fp32-accurate dot product with exact bf16 x bf16
 //    products and fp32 accumulation.  The split operands of every unit are
-//    packed once per call, in MFMA lane order, by pack_operands_kernel.
+//    packed once per call, in MFMA lane order, by prep_fused_kernel.
 //  * The norm term sum_f w_f |k_f| uses v_mfma_f32_16x16x4_f32 on the fp32
 //    magnitudes (computed once per key band on the VALU, shared by all G
 //    heads).
@@ -223,7 +223,7 @@ struct Shared {
                     // own slot: waves may still be reading `ticket` then)
 };
 
-// MFMA operands of one unit, packed by pack_operands_kernel in lane order:
+// MFMA operands of one unit, packed by prep_fused_kernel in lane order:
 // vector 4*st + 0/1/2 is the bf16 hi/mid/lo split of a_h over the lane's
 // eight d-elements of step st, vector 4*st + 3 the four fp32 norm weights.
 template <int STEPS>
@@ -694,68 +694,18 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   }
 }
 
-// MFMA operand pack of every unit (s, l, g): thread (unit, st, lane) forms
-// A_f = P[l][h][f] * E[s][f] (fp64) for the lane's head h = g*G + lane%16
-// and the bands of its eight elements of step st, splits each element's
-// part (Re or Im, by the RoPE layout) into bf16 hi/mid/lo and stores them
-// with the fp32 norm weights W[l][h][f] of the step's four norm slots
-// (zeros for lanes beyond G).
-template <int STEPS>
-__global__ __launch_bounds__(256) void pack_operands_kernel(
-    int S, int L, int Hkv, int G, bool half, const double2* __restrict__ P,
-    const float* __restrict__ W, const double2* __restrict__ E, uint4* __restrict__ apack) {
-  constexpr int F = STEPS * 16;
-  const int64_t units = (int64_t)S * L * Hkv;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= units * STEPS * 64) return;
-  const int lane = (int)(idx & 63);
-  const int st = (int)((idx >> 6) % STEPS);
-  const int64_t unit = idx / (64 * STEPS);
-  const int lg = (int)(unit % ((int64_t)L * Hkv));
-  const int s = (int)(unit / ((int64_t)L * Hkv));
-  const int l = lg / Hkv, g = lg % Hkv;
-  const int m = lane & 15, q = lane >> 4;
-  const int Hq = Hkv * G;
-  constexpr int D = STEPS * 32;
-  uint32_t h3[8], m3[8], l3[8];
-  float wv[4];
-  const bool live = m < G;
-  const int64_t pbase = ((int64_t)l * Hq + g * G + (live ? m : 0)) * F;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = 32 * st + 8 * q + j;
-    const int f = elem_band(e, D, half);
-    double x = 0.0;
-    if (live) {
-      const double2 pv = P[pbase + f];
-      const double2 ev = E[(int64_t)s * F + f];
-      x = elem_part(e, D, half) ? pv.x * ev.y + pv.y * ev.x : pv.x * ev.x - pv.y * ev.y;
-    }
-    split3(x, h3[j], m3[j], l3[j]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) wv[u] = live ? W[pbase + slot_band(st, q, u, STEPS, half)] : 0.f;
-  auto pack8 = [](const uint32_t (&v)[8]) {
-    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                      v[6] | (v[7] << 16));
-  };
-  uint4* op = apack + unit * (4 * STEPS) * 64 + lane;
-  op[(4 * st + 0) * 64] = pack8(h3);
-  op[(4 * st + 1) * 64] = pack8(m3);
-  op[(4 * st + 2) * 64] = pack8(l3);
-  op[(4 * st + 3) * 64] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
-                                     __float_as_uint(wv[2]), __float_as_uint(wv[3]));
-}
-
-// The fused averaged path's preparation in one launch, in place of the
-// prologue and the operand pack: block 0 writes the plan carried in the
-// arguments (plan_words > 0); every thread resets its share of the control
-// words and the published-statistics slots; the blocks that pack operands
-// first form, in LDS, C_f for every band (built-in offsets by repeated
-// squaring; a given set dealt over the block's threads, the partial sums
-// added in a fixed order) and E for the sequences their units belong to,
-// then pack each unit's operands as pack_operands_kernel does from
-// P = E[q] * C_f, W and E.
+// The fused path's preparation of a call, one launch: block 0 writes the
+// plan carried in the arguments (plan_words > 0); every thread resets its
+// share of the control words and the published-statistics slots; the blocks
+// that pack operands first form, in LDS, C_f for every band (built-in
+// offsets by repeated squaring; a given set dealt over the block's threads,
+// the partial sums added in a fixed order) and E for the sequences their
+// units belong to.  Then thread (unit, st, lane) forms A_f = P * E (fp64,
+// P = E[q_f] * C_f) for the lane's head h = g*G + lane%16 and the bands of
+// its eight elements of step st, splits each element's part (Re or Im, by
+// the RoPE layout) into bf16 hi/mid/lo and stores them with the fp32 norm
+// weights W = (1 - R) E|q| of the step's four norm slots (zeros for lanes
+// beyond G).
 template <int STEPS>
 __global__ __launch_bounds__(256) void prep_fused_kernel(
     int S, int L, int Hkv, int G, int Hq, bool half, double theta, SeqInfo* __restrict__ seqs,
@@ -892,35 +842,27 @@ uint32_t set_fused_wait_limit(uint32_t polls) { return g_wait_limit.exchange(pol
 
 template <int STEPS, bool HALF, bool PAGED>
 static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
-                                 const SeqInfo* seqs, int S, int L, int Hkv, int G,
-                                 const double2* P, const float* W, const double2* E,
-                                 uint4* apack, const uint16_t* k, const Pages& pg, double* cs,
-                                 uint32_t* ctrl, float* scores, float* raw, double* hs,
-                                 const PrepArgs* prep) {
+                                 const SeqInfo* seqs, int S, int L, int Hkv, int G, uint4* apack,
+                                 const uint16_t* k, const Pages& pg, double* cs, uint32_t* ctrl,
+                                 float* scores, float* raw, double* hs, const PrepArgs& prep) {
   const int64_t pack_threads = (int64_t)S * L * Hkv * STEPS * 64;
-  if (prep) {
-    ArgWords plan;
-    int plan_words = 0;
-    if (prep->plan_host) {
-      const size_t bytes = (size_t)S * sizeof(SeqInfo);
-      if (bytes > sizeof(plan.w)) return hipErrorInvalidValue;
-      std::memcpy(plan.w, prep->plan_host, bytes);
-      plan_words = (int)(bytes / 4);
-    }
-    int64_t total = pack_threads;
-    if (prep->n_stat_slots > total) total = prep->n_stat_slots;
-    if (prep->n_ctrl > total) total = prep->n_ctrl;
-    if (total < 1) total = 1;  // block 0 writes the plan
-    const int nD = prep->offsets ? prep->n_offsets : 17;
-    hipLaunchKernelGGL(prep_fused_kernel<STEPS>, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                       0, st, S, L, Hkv, G, prep->Hq, HALF, prep->theta,
-                       const_cast<SeqInfo*>(seqs), plan, plan_words, prep->q_centre,
-                       prep->q_absmean, prep->q_R, prep->offsets, nD, ctrl, prep->n_ctrl, cs,
-                       prep->n_stat_slots, apack);
-  } else {
-    hipLaunchKernelGGL(pack_operands_kernel<STEPS>, dim3((unsigned)((pack_threads + 255) / 256)),
-                       dim3(256), 0, st, S, L, Hkv, G, HALF, P, W, E, apack);
+  ArgWords plan;
+  int plan_words = 0;
+  if (prep.plan_host) {
+    const size_t bytes = (size_t)S * sizeof(SeqInfo);
+    if (bytes > sizeof(plan.w)) return hipErrorInvalidValue;
+    std::memcpy(plan.w, prep.plan_host, bytes);
+    plan_words = (int)(bytes / 4);
   }
+  int64_t total = pack_threads;
+  if (prep.n_stat_slots > total) total = prep.n_stat_slots;
+  if (prep.n_ctrl > total) total = prep.n_ctrl;
+  if (total < 1) total = 1;  // block 0 writes the plan
+  const int nD = prep.offsets ? prep.n_offsets : 17;
+  hipLaunchKernelGGL(prep_fused_kernel<STEPS>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     st, S, L, Hkv, G, prep.Hq, HALF, prep.theta, const_cast<SeqInfo*>(seqs),
+                     plan, plan_words, prep.q_centre, prep.q_absmean, prep.q_R, prep.offsets, nD,
+                     ctrl, prep.n_ctrl, cs, prep.n_stat_slots, apack);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || total_tickets == 0) return e;
   const void* kern = reinterpret_cast<const void*>(&score_fused_kernel<STEPS, HALF, PAGED>);
@@ -1033,21 +975,18 @@ size_t fused_operand_bytes(int d, int64_t units) {
 }
 
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,
-                              int total_tickets, const double2* P, const float* W,
-                              const double2* E, void* apack, const uint16_t* k,
+                              int total_tickets, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
                               double* head_stats, bool half, const Pages& pg,
-                              const PrepArgs* prep, hipStream_t st) {
-  if (total_tickets == 0 && !prep) return hipSuccess;
+                              const PrepArgs& prep, hipStream_t st) {
   const size_t lds = 2 * (size_t)G * (ch + kRawPad) * sizeof(float);
   if (lds > (size_t)kFusedMaxLds || !fused_supported(d, half)) return hipErrorInvalidValue;
   if (pg.table && pg.page_shift < 4) return hipErrorInvalidValue;  // pages of >= 16 tokens
   uint4* ap = reinterpret_cast<uint4*>(apack);
 #define TRI_CASE(n, h, pgd)                                                                   \
   case n:                                                                                     \
-    return launch_fused_t<n, h, pgd>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, P, W, E, \
-                                     ap, k, pg, chunk_stats, ctrl, scores, raw, head_stats,   \
-                                     prep);
+    return launch_fused_t<n, h, pgd>(total_tickets, ch, lds, st, seqs, S, L, Hkv, G, ap, k, pg, \
+                                     chunk_stats, ctrl, scores, raw, head_stats, prep);
 #define TRI_LAYOUTS(pgd)                                                                      \
   if (half) {                                                                                 \
     switch (d / 32) {                                                                         \

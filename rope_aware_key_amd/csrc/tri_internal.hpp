@@ -179,11 +179,11 @@ int set_fused_resident_override(int groups);
 // Workspace bytes of the fused path's packed MFMA operands.
 size_t fused_operand_bytes(int d, int64_t units);
 
-// What the fused path's preparation kernel needs when it replaces the
-// prologue (the averaged score: offsets folded into C_f): the calibration
-// tables, the offsets (NULL: {2^0..2^16}), the plan (plan_host: carried in
-// the launch's arguments and written to seqs; NULL: already in seqs), and
-// the control words and statistics slots to reset.
+// What the fused path's preparation kernel needs (it stands in for the
+// prologue there: the averaged score, offsets folded into C_f): the
+// calibration tables, the offsets (NULL: {2^0..2^16}), the plan (plan_host:
+// carried in the launch's arguments and written to seqs; NULL: already in
+// seqs), and the control words and statistics slots to reset.
 struct PrepArgs {
   double theta;
   int Hq;
@@ -197,17 +197,15 @@ struct PrepArgs {
   int64_t n_stat_slots;
 };
 
-// Fused MFMA score path (head_dim % 32 == 0).  ctrl as above, zeroed by the
-// prologue; chunk_stats: [tickets][G][2] fp64 (sum, sum of squares), reset
-// to kStatSentinel by the prologue.  With prep non-NULL the prologue is not
-// run: one preparation kernel resets ctrl and chunk_stats, writes the plan
-// and packs the operands from the calibration tables (P, W, E unused).
+// Fused MFMA score path (head_dim % 32 == 0, the averaged score), with no
+// prologue: one preparation kernel zeroes ctrl, resets chunk_stats ([tickets]
+// [G][2] fp64 sum and sum of squares) to kStatSentinel, writes the plan and
+// packs the operands into apack; then the fused kernel.
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,
-                              int total_tickets, const double2* P, const float* W,
-                              const double2* E, void* apack, const uint16_t* k,
+                              int total_tickets, void* apack, const uint16_t* k,
                               double* chunk_stats, uint32_t* ctrl, float* scores, float* raw,
                               double* head_stats, bool half, const Pages& pg,
-                              const PrepArgs* prep, hipStream_t st);
+                              const PrepArgs& prep, hipStream_t st);
 
 // unit_stats: [units][G][2] fp64 scratch for the per-unit (mu, 1/sigma).
 hipError_t launch_score(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d,
