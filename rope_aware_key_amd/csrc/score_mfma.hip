@@ -11,11 +11,15 @@
 // Mapping onto CDNA4:
 //  * The dot product with the post-RoPE key is a (16 heads x d) x (d x 16
 //    keys) product per block of 16 keys: v_mfma_f32_16x16x32_bf16.  The keys
-//    are bf16 already; the fp64 coefficient a_h is split into three bf16
-//    terms (hi + mid + lo, ~25 significant bits), so three MFMAs per 32-wide
-//    step reproduce an fp32-accurate dot product with exact bf16 x bf16
-//    products and fp32 accumulation.  The split operands of every unit are
-//    packed once per call, in MFMA lane order, by prep_fused_kernel.
+//    are bf16 already; the fp64 coefficient a_h is split into two bf16 terms
+//    (hi + mid, ~17 significant bits: the split moves a coefficient by at
+//    most 2^-17 of itself), so two MFMAs per 32-wide step give the dot
+//    product with exact bf16 x bf16 products and fp32 accumulation.  On the
+//    workload shapes this moves z-scores by at most 1.5e-5 against exact
+//    coefficients (fp64 check), well inside the 1e-4 score bar; a third term
+//    (3e-8) costs a third more trig MFMAs and 16 registers, about 4% of the
+//    kernel's time.  The split operands of every unit are packed once per
+//    call, in MFMA lane order, by prep_fused_kernel.
 //  * The norm term sum_f w_f |k_f| uses v_mfma_f32_16x16x4_f32 on the fp32
 //    magnitudes (computed once per key band on the VALU, shared by all G
 //    heads).
@@ -84,14 +88,20 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// x ~= hi + mid + lo with each term a bf16 (relative residual ~2^-25).
-__device__ __forceinline__ void split3(double x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+// x ~= hi + mid with each term a bf16 (relative residual at most ~2^-17).
+__device__ __forceinline__ void split2(double x, uint32_t& hi, uint32_t& mid) {
   hi = bf16_rne((float)x);
   const double r1 = x - (double)__uint_as_float(hi << 16);
   mid = bf16_rne((float)r1);
-  const double r2 = r1 - (double)__uint_as_float(mid << 16);
-  lo = bf16_rne((float)r2);
 }
+
+// 16-byte vectors per 32-wide step of a unit's packed operands: the bf16 hi
+// and mid terms of the trig coefficients, one unused slot, the fp32 norm
+// weights.  With the unused slot a unit's operands start on a 16 KB
+// boundary at d = 128 (12 KB without it), and the score kernel measured
+// about 1% faster that way.
+constexpr int kOpVecs = 4;
+constexpr int kOpNorm = 3;  // slot of the norm weights
 
 constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / 64;
@@ -224,12 +234,12 @@ struct Shared {
 };
 
 // MFMA operands of one unit, packed by prep_fused_kernel in lane order:
-// vector 4*st + 0/1/2 is the bf16 hi/mid/lo split of a_h over the lane's
-// eight d-elements of step st, vector 4*st + 3 the four fp32 norm weights.
+// vector 4*st + 0/1 is the bf16 hi/mid split of a_h over the lane's eight
+// d-elements of step st, vector 4*st + 3 the four fp32 norm weights.
 template <int STEPS>
 __device__ __forceinline__ const uint4* unit_operands(const uint4* __restrict__ apack,
                                                       int64_t unit) {
-  return apack + unit * (4 * STEPS) * 64;
+  return apack + unit * (kOpVecs * STEPS) * 64;
 }
 
 // Paged pools (pages of at least 16 tokens): block b (16 keys) of a chunk
@@ -343,7 +353,7 @@ __device__ __forceinline__ void ring_prime(const Chunk& ck, const uint16_t* __re
 
 template <int STEPS>
 struct UnitOperands {
-  bf16x8_t a_hi[STEPS], a_mid[STEPS], a_lo[STEPS];  // trig coefficients, bf16 split
+  bf16x8_t a_hi[STEPS], a_mid[STEPS];  // trig coefficients, bf16 split
   float wn[STEPS][4];                                // norm weights
 };
 
@@ -355,11 +365,10 @@ __device__ __forceinline__ void load_operands(const Chunk& ck, const uint4* __re
   const uint4* src = unit_operands<STEPS>(apack, ck.unit) + (threadIdx.x & 63);
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
-    const uint4 vh = src[(4 * st + 0) * 64], vm = src[(4 * st + 1) * 64];
-    const uint4 vl = src[(4 * st + 2) * 64], vw = src[(4 * st + 3) * 64];
+    const uint4 vh = src[(kOpVecs * st + 0) * 64], vm = src[(kOpVecs * st + 1) * 64];
+    const uint4 vw = src[(kOpVecs * st + kOpNorm) * 64];
     __builtin_memcpy(&op.a_hi[st], &vh, 16);
     __builtin_memcpy(&op.a_mid[st], &vm, 16);
-    __builtin_memcpy(&op.a_lo[st], &vl, 16);
     op.wn[st][0] = __uint_as_float(vw.x);
     op.wn[st][1] = __uint_as_float(vw.y);
     op.wn[st][2] = __uint_as_float(vw.z);
@@ -402,7 +411,6 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           __builtin_memcpy(&bk, &ring[j][st], 16);
           acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_hi[st], bk, acc_t, 0, 0, 0);
           acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_mid[st], bk, acc_t, 0, 0, 0);
-          acc_t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.a_lo[st], bk, acc_t, 0, 0, 0);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             acc_n = __builtin_amdgcn_mfma_f32_16x16x4f32(op.wn[st][u], r[u], acc_n, 0, 0, 0);
@@ -411,7 +419,7 @@ __device__ __forceinline__ void chunk_raw(const Chunk& ck, int G, int rs,
           // pads every step with wait states): the dot2s and their operand
           // clears, the trig MFMAs, the square roots, the norm MFMAs.
           __builtin_amdgcn_sched_group_barrier(0x002, HALF ? 12 : 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
 // units belong to.  Then thread (unit, st, lane) forms A_f = P * E (fp64,
 // P = E[q_f] * C_f) for the lane's head h = g*G + lane%16 and the bands of
 // its eight elements of step st, splits each element's part (Re or Im, by
-// the RoPE layout) into bf16 hi/mid/lo and stores them with the fp32 norm
+// the RoPE layout) into bf16 hi and mid terms and stores them with the fp32 norm
 // weights W = (1 - R) E|q| of the step's four norm slots (zeros for lanes
 // beyond G).
 template <int STEPS>
@@ -797,7 +805,7 @@ __global__ __launch_bounds__(256) void prep_fused_kernel(
   const int s = (int)(unit / LH);
   const int l = lg / Hkv, g = lg % Hkv;
   const int m = lane & 15, q = lane >> 4;
-  uint32_t h3[8], m3[8], l3[8];
+  uint32_t h2[8], m2[8];
   float wv[4];
   const bool live = m < G;
   const int64_t pbase = ((int64_t)l * Hq + g * G + (live ? m : 0)) * F;
@@ -815,7 +823,7 @@ __global__ __launch_bounds__(256) void prep_fused_kernel(
       const double2 ev = ev_s[f];
       x = elem_part(e, D, half) ? pv.x * ev.y + pv.y * ev.x : pv.x * ev.x - pv.y * ev.y;
     }
-    split3(x, h3[j], m3[j], l3[j]);
+    split2(x, h2[j], m2[j]);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -826,11 +834,10 @@ __global__ __launch_bounds__(256) void prep_fused_kernel(
     return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
                       v[6] | (v[7] << 16));
   };
-  uint4* op = apack + unit * (4 * STEPS) * 64 + lane;
-  op[(4 * st + 0) * 64] = pack8(h3);
-  op[(4 * st + 1) * 64] = pack8(m3);
-  op[(4 * st + 2) * 64] = pack8(l3);
-  op[(4 * st + 3) * 64] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
+  uint4* op = apack + unit * (kOpVecs * STEPS) * 64 + lane;
+  op[(kOpVecs * st + 0) * 64] = pack8(h2);
+  op[(kOpVecs * st + 1) * 64] = pack8(m2);
+  op[(kOpVecs * st + kOpNorm) * 64] = make_uint4(__float_as_uint(wv[0]), __float_as_uint(wv[1]),
                                      __float_as_uint(wv[2]), __float_as_uint(wv[3]));
 }
 
@@ -957,11 +964,11 @@ bool fused_supported(int d, bool half) {
 
 // Keys per ticket: as many as let the work-groups a CU holds (two raw
 // buffers of G heads each) share its LDS, in multiples of 64, at most 1024.
-// Up to d = 128 the kernel's registers allow three work-groups per CU; from
-// d = 160 (five or more 32-wide steps) only two fit, and chunks sized for
+// Up to d = 160 the kernel's registers allow three work-groups per CU; from
+// d = 192 (six or more 32-wide steps) only two fit, and chunks sized for
 // two cut the chunk boundaries by a third (3% on a d = 256 cache).
 int fused_chunk_keys(int G, int d) {
-  const int wgs = d / 32 >= 5 ? 2 : 3;
+  const int wgs = d / 32 >= 6 ? 2 : 3;
   // leave room for the static LDS (Shared)
   const int per_wg = kFusedLdsPerCu / wgs - (int)((sizeof(Shared) + 255) / 256 * 256);
   int ch = (per_wg / (2 * G * (int)sizeof(float)) - kRawPad) / 64 * 64;
@@ -971,7 +978,7 @@ int fused_chunk_keys(int G, int d) {
 }
 
 size_t fused_operand_bytes(int d, int64_t units) {
-  return fused_supported(d, false) ? (size_t)units * (4 * (d / 32)) * 64 * sizeof(uint4) : 0;
+  return fused_supported(d, false) ? (size_t)units * (kOpVecs * (d / 32)) * 64 * sizeof(uint4) : 0;
 }
 
 hipError_t launch_score_fused(const SeqInfo* seqs, int S, int L, int Hkv, int G, int d, int ch,

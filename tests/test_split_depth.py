@@ -1,10 +1,10 @@
-"""Why the max-over-offsets path splits each trig coefficient into two
-bf16 terms (hi + mid) while the averaged path keeps three: in fp64, the
-z-scores of the maximum over the default offset set computed with
-coefficients rounded to two bf16 terms stay within 5e-5 of the exact ones
-(half the 1e-4 score bar) on synthetic units of the workloads' kind, and
-three terms stay below 1e-7.  A split error of at most 2^-17 per
-coefficient moves a raw score by a few 2^-17 of the raw scores' own spread.
+"""Why both MFMA score paths split each fp64 trig coefficient into two bf16
+terms (hi + mid): in fp64, the z-scores computed with coefficients rounded
+to two bf16 terms stay within 3e-5 (the averaged score, over units of the
+five workload kinds) and 5e-5 (the maximum over the default offset set) of
+the exact ones, well inside the 1e-4 score bar, while three terms stay
+below 1e-7.  A split error of at most 2^-17 per coefficient moves a raw
+score by a few 2^-17 of the raw scores' own spread.
 """
 import numpy as np
 import pytest
@@ -54,3 +54,41 @@ def test_two_bf16_terms_suffice_for_the_max_over_offsets(shape, n, seed):
     dz3 = np.max(np.abs(raw(_split(a, 3)) - exact) / sigma)
     assert dz2 < 5e-5, dz2
     assert dz3 < 1e-7, dz3
+
+
+@pytest.mark.parametrize("name,over,units", [
+    ("decode_window", dict(S=2, L=2), 8),
+    ("long_reasoning", dict(S=1, L=2, n=8192), 8),
+    ("ragged", dict(S=4, L=1), 6),
+    ("stress_ties", dict(n=16384), 4),
+])
+def test_two_bf16_terms_suffice_for_the_averaged_score(name, over, units):
+    # the averaged score's coefficients a_h = E[q_f] C_f exp(i omega_f p_q),
+    # C_f the mean of exp(i omega_f delta) over the default offsets
+    case = synth.workload_case(name, **over)
+    shape = case.shape
+    d, G = shape.head_dim, shape.group
+    om = O.rope_omega(d, shape.rope_theta)
+    offs = np.array([2.0 ** j for j in range(17)])
+    C = np.exp(1j * om[None, :] * offs[:, None]).mean(axis=0)
+    worst2 = worst3 = 0.0
+    done = 0
+    for s in range(case.num_seqs):
+        for l in range(shape.num_layers):
+            for g in range(shape.num_kv_heads):
+                if done == units:
+                    break
+                done += 1
+                _, _, kbits, _, centre, absmean, Rr = unit_inputs(case, s, l, g)
+                kp = O.bf16_bits_to_f64(kbits)
+                A = centre * C[None, :] * np.exp(1j * om[None, :] * float(case.cur_pos[s]))
+                a = np.zeros((G, d))
+                a[:, 0::2], a[:, 1::2] = A.real, A.imag
+                norm = np.abs(kp[:, 0::2] + 1j * kp[:, 1::2]) @ ((1 - Rr) * absmean).T
+                exact = kp @ a.T + norm
+                sigma = exact.std(axis=0)
+                worst2 = max(worst2, np.max(np.abs(kp @ _split(a, 2).T + norm - exact) / sigma))
+                worst3 = max(worst3, np.max(np.abs(kp @ _split(a, 3).T + norm - exact) / sigma))
+    assert done == units
+    assert worst2 < 3e-5, worst2
+    assert worst3 < 1e-7, worst3
