@@ -432,20 +432,17 @@ hipError_t run_score(const Plan& p, double theta, const OffsetMode& om, const ui
 }
 
 // Queue select (and the gathers asked for) of a ready plan; the sequence
-// table is uploaded unless the caller already did on this stream.
+// table is written to the workspace first (by the first kernel, or a copy
+// kernel of its own) unless the caller already wrote it on this stream.
 hipError_t run_select_compact(const Plan& p, const float* scores, const uint16_t* k,
                               const uint16_t* v, const int32_t* k_pos, int32_t* kept_idx,
                               uint16_t* k_out, uint16_t* v_out, int32_t* pos_out, char* ws,
                               hipStream_t s, bool upload_seqs = true) {
   SeqInfo* dseq = (SeqInfo*)(ws + p.off_seq);
-  hipError_t e = hipSuccess;
-  if (upload_seqs) e = upload(dseq, p.seqs.data(), p.seqs.size() * sizeof(SeqInfo), s);
   const int LH = p.L * p.Hkv;
-  if (e == hipSuccess)
-    e = tri::launch_select_compact(dseq, p.S, LH, p.d, p.max_n, p.max_b, scores, kept_idx,
-                                   ws + p.off_split, k, v, k_pos, k_out, v_out, pos_out, p.in_pg,
-                                   p.out_pg, s);
-  return e;
+  return tri::launch_select_compact(dseq, upload_seqs ? p.seqs.data() : nullptr, p.S, LH, p.d,
+                                    p.max_n, p.max_b, scores, kept_idx, ws + p.off_split, k, v,
+                                    k_pos, k_out, v_out, pos_out, p.in_pg, p.out_pg, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -15,6 +15,8 @@
 // in registers (and, when rows are gathered, the gathers in the same
 // kernel); up to 35840, one work-group of 512 threads reading the scores
 // three times; longer units are split over work-groups of 4096 keys.
+#include <cstring>
+
 #include "tri_internal.hpp"
 
 namespace tri {
@@ -697,6 +699,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
   }
 }
 
+// The selection of the first units of a call whose plan travels in the
+// launch's arguments: block 0 also writes the plan to seqs, where the
+// gathering kernel that follows reads it.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void select_first_kernel(
+    SeqInfo* __restrict__ seqs, const ArgWords plan, int plan_words, int LH,
+    const float* __restrict__ scores, int32_t* __restrict__ kept) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < plan_words; i += NT)
+      reinterpret_cast<uint32_t*>(seqs)[i] = plan.w[i];
+  const int unit = blockIdx.x;
+  const int s = unit / LH, lg = unit % LH;
+  const SeqInfo si = reinterpret_cast<const SeqInfo*>(plan.w)[s];
+  const int n = si.n, b = si.b;
+  if (b <= 0) return;
+  const int64_t in0 = si.row_base + (int64_t)lg * si.in_stride;
+  int32_t* out = kept + si.out_base + (int64_t)lg * si.out_stride;
+  __shared__ uint32_t buf[kHistBins + 2 * kHeldCand];
+  if (b >= n) {
+    for (int i = threadIdx.x; i < n; i += NT) out[i] = i;
+  } else {
+    held_select<NT, KPT>(scores + in0, out, n, b, buf, false);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split select for units longer than the LDS-staged select holds: the unit
 // is cut into tiles of kSplitTile keys, one work-group each, so that a few
@@ -1057,13 +1084,21 @@ hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
   return hipGetLastError();
 }
 
-hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int max_n, int max_b,
-                                 const float* scores, int32_t* kept_idx, void* split_ws,
-                                 const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
-                                 uint16_t* k_out, uint16_t* v_out, int32_t* pos_out,
-                                 const Pages& in_pg, const Pages& out_pg, hipStream_t st) {
+hipError_t launch_select_compact(SeqInfo* seqs, const SeqInfo* plan_host, int S, int LH, int d,
+                                 int max_n, int max_b, const float* scores, int32_t* kept_idx,
+                                 void* split_ws, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
+                                 int32_t* pos_out, const Pages& in_pg, const Pages& out_pg,
+                                 hipStream_t st) {
   const int64_t units = (int64_t)S * LH;
   const bool copy = k_out || v_out || pos_out;
+  const size_t plan_bytes = (size_t)S * sizeof(SeqInfo);
+  // the plan goes to the workspace by a copy kernel unless a first launch
+  // below carries it
+  auto write_plan = [&]() -> hipError_t {
+    return plan_host && plan_bytes ? launch_write_args(seqs, plan_host, plan_bytes, st)
+                                   : hipSuccess;
+  };
   if (units > 0 && copy && max_n > kSelSmallUnit && max_n <= 1024 * 32) {
     // register-held select and the gathers in one kernel.  With more units
     // than two rounds of resident work-groups, one unit per CU is selected
@@ -1080,7 +1115,24 @@ hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int 
         presel = cus;
     }
     const bool wide = max_n > 1024 * 16;
-    if (presel > 0) {
+    ArgWords plan;
+    const bool carry = presel > 0 && plan_host && plan_bytes <= sizeof(plan.w);
+    if (!carry) {
+      const hipError_t e = write_plan();
+      if (e != hipSuccess) return e;
+    }
+    if (carry) {
+      std::memcpy(plan.w, plan_host, plan_bytes);
+      const int words = (int)(plan_bytes / 4);
+      if (wide)
+        hipLaunchKernelGGL((select_first_kernel<1024, 32>), dim3((unsigned)presel), dim3(1024), 0,
+                           st, seqs, plan, words, LH, scores, kept_idx);
+      else
+        hipLaunchKernelGGL((select_first_kernel<1024, 16>), dim3((unsigned)presel), dim3(1024), 0,
+                           st, seqs, plan, words, LH, scores, kept_idx);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else if (presel > 0) {
       if (wide)
         hipLaunchKernelGGL((select_held_kernel<1024, 32, false>), dim3((unsigned)presel),
                            dim3(1024), 0, st, seqs, LH, scores, kept_idx, CompactArgs{}, 0);
@@ -1098,7 +1150,8 @@ hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int 
                          0, st, seqs, LH, scores, kept_idx, ca, presel);
     return hipGetLastError();
   }
-  hipError_t e = launch_select(seqs, S, LH, max_n, scores, kept_idx, split_ws, st);
+  hipError_t e = write_plan();
+  if (e == hipSuccess) e = launch_select(seqs, S, LH, max_n, scores, kept_idx, split_ws, st);
   if (e != hipSuccess || !copy) return e;
   return launch_compact(seqs, S, LH, d, max_b, kept_idx, k, v, k_pos, k_out, v_out, pos_out, in_pg,
                         out_pg, st);

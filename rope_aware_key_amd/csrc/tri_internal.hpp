@@ -301,11 +301,16 @@ hipError_t launch_compact(const SeqInfo* seqs, int S, int LH, int d, int max_b,
 
 // Select, then the gathers asked for (any of k_out, v_out, pos_out); for
 // units of 4096 < n <= 32768 keys one kernel does both, one work-group per
-// unit, so that selections overlap other units' copies.
-hipError_t launch_select_compact(const SeqInfo* seqs, int S, int LH, int d, int max_n, int max_b,
-                                 const float* scores, int32_t* kept_idx, void* split_ws,
-                                 const uint16_t* k, const uint16_t* v, const int32_t* k_pos,
-                                 uint16_t* k_out, uint16_t* v_out, int32_t* pos_out,
-                                 const Pages& in_pg, const Pages& out_pg, hipStream_t st);
+// unit, so that selections overlap other units' copies.  plan_host: the
+// host copy of the S-entry plan, written to seqs first (when the first
+// units are selected by a launch of their own and the plan fits its
+// arguments, that launch carries and writes it); NULL when seqs already
+// holds the plan.
+hipError_t launch_select_compact(SeqInfo* seqs, const SeqInfo* plan_host, int S, int LH, int d,
+                                 int max_n, int max_b, const float* scores, int32_t* kept_idx,
+                                 void* split_ws, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* k_pos, uint16_t* k_out, uint16_t* v_out,
+                                 int32_t* pos_out, const Pages& in_pg, const Pages& out_pg,
+                                 hipStream_t st);
 
 }  // namespace tri
