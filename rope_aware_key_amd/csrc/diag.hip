@@ -12,8 +12,8 @@
 // Both are 16 x 16 tiles of (query x key) products on
 // v_mfma_f32_16x16x32_bf16: queries and keys are bf16 already, so y is one
 // exact MFMA per 32-wide step; the rotated centres are formed per query in
-// fp64 and split into three bf16 terms (fp32-accurate, as in the score
-// kernels).  A wave owns 16 queries of one (layer, head) and streams the
+// fp64 and split into three bf16 terms (fp32-accurate; the score kernels
+// keep two, which their 1e-4 score bar allows).  A wave owns 16 queries of one (layer, head) and streams the
 // KV head's keys in blocks of 16, the next block's loads in flight while
 // the current one is multiplied; each lane sums x, y, x^2, y^2, xy over
 // its valid pairs in fp64, the wave reduces them and a merge kernel adds
