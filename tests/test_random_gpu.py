@@ -45,7 +45,7 @@ def draw(seed):
                 offsets=offsets, page=page, head_major=head_major)
 
 
-@pytest.mark.parametrize("seed", range(128))
+@pytest.mark.parametrize("seed", range(512))
 def test_random_case(seed):
     c = draw(seed)
     print(f"random case {seed}: {c}", flush=True)
