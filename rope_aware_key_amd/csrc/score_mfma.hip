@@ -665,9 +665,15 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     const bool ahead = have && (!have_prev || prev_last < t);
     uint32_t next = 0;  // thread 0
     if (ahead && threadIdx.x == 0) next = claim();
+    // The stream runs at the lowest wave priority and the chunk boundary
+    // (moments, finalize, score stores, next operands) at a higher one, so
+    // that a wave at its boundary takes the SIMD's issue slots ahead of the
+    // other work-groups' streaming waves, which mostly wait on memory.
+    __builtin_amdgcn_s_setprio(0);
     if (have)
       chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid,
                                     sh.tile[threadIdx.x >> 6]);
+    __builtin_amdgcn_s_setprio(2);
     if (ahead && threadIdx.x == 0) sh.next_ticket = (int)next;
     __syncthreads();
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
