@@ -742,6 +742,40 @@ def run_calib(args):
     print(json.dumps(out), flush=True)
 
 
+def phase_profile(args, label, score, scores, stream):
+    """tri_score calls with the phase-counting copy of the fused kernel
+    (tri_debug_set_phase_buffer): cycles of wave 0 of a work-group per pass
+    and phase, averaged over every pass of every work-group; the scores are
+    checked bit for bit against a plain call."""
+    import torch
+    import rope_aware_key_amd as R
+    plain = scores.clone()
+    buf = torch.zeros(8, dtype=torch.int64, device=scores.device)
+    R.tri_debug_set_phase_buffer(buf)
+    try:
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            score()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        R.tri_debug_set_phase_buffer(None)
+    same = bool(torch.equal(scores.view(torch.int32), plain.view(torch.int32)))
+    c = buf.cpu().tolist()
+    passes = c[7]
+    cyc = {name: c[i] / passes for i, name in enumerate(R.PHASE_NAMES)}
+    total = sum(cyc.values())
+    print(json.dumps({"phase_profile": label, "calls": args.steps, "passes_per_call": passes / args.steps,
+                      "cycles_per_pass": {k: round(v, 1) for k, v in cyc.items()},
+                      "share": {k: round(v / total, 4) for k, v in cyc.items()},
+                      "tri_score_ms_with_counters": ev0.elapsed_time(ev1) / args.steps,
+                      "scores_bit_identical": same,
+                      "clock": "s_memtime (core clock) on wave 0 of every work-group"}))
+    if not same:
+        sys.exit(1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -770,6 +804,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--stream-probe", action="store_true",
                     help="time the read-bandwidth probe alone (4 GiB, 20 reads) and print its rate")
+    ap.add_argument("--phase-profile", action="store_true",
+                    help="cycles per phase of the fused score kernel's passes (tri_score only)")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--cmd", default="")
@@ -915,6 +951,9 @@ def main():
         score()
         select()
     torch.cuda.synchronize()
+    if args.phase_profile:
+        phase_profile(args, label, score, scores, stream)
+        return
 
     # The timed steps run back to back between one pair of events: an event
     # recorded between two kernels costs about 5 us of GPU time on this

@@ -8,7 +8,8 @@ from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, Decode, TriError, TriKvPages, TriShape, last_error, make_pages,
     make_shape, status_string, TRI_REDUCE_MAX, TRI_REDUCE_MEAN, TRI_ROPE_HALF_SPLIT,
     TRI_ROPE_INTERLEAVED, TRI_SCORE_WAIT_GAVE_UP, tri_calibrate, tri_calibrate_workspace_bytes,
-    tri_debug_set_resident_groups, tri_debug_set_wait_limit,
+    tri_debug_set_resident_groups, tri_debug_set_wait_limit, tri_debug_set_phase_buffer,
+    PHASE_NAMES,
     tri_pyramid_budgets,
     tri_score, tri_score_noalloc, tri_score_offsets, tri_score_paged, tri_score_status,
     tri_select_compact,

@@ -67,6 +67,8 @@ _lib.tri_last_error.argtypes = []
 _lib.tri_last_error.restype = ctypes.c_char_p
 _lib.tri_debug_set_wait_limit.argtypes = [ctypes.c_uint32]
 _lib.tri_debug_set_wait_limit.restype = ctypes.c_uint32
+_lib.tri_debug_set_phase_buffer.argtypes = [_P]
+_lib.tri_debug_set_phase_buffer.restype = _P
 _lib.tri_debug_set_resident_groups.argtypes = [ctypes.c_int32]
 _lib.tri_debug_set_resident_groups.restype = ctypes.c_int32
 _lib.tri_score_status.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
@@ -140,7 +142,7 @@ EXPORTS = ("tri_calibrate", "tri_calibrate_workspace_bytes", "tri_workspace_byte
            "tri_trig_correlation", "tri_stream_probe", "tri_score_noalloc", "tri_score_status",
            "tri_debug_set_resident_groups", "tri_pyramid_budgets", "tri_workspace_bytes_layers",
            "tri_select_compact_layers", "tri_score_paged", "tri_select_compact_paged",
-           "tri_workspace_bytes_paged", "tri_debug_set_wait_limit")
+           "tri_workspace_bytes_paged", "tri_debug_set_wait_limit", "tri_debug_set_phase_buffer")
 
 TRI_REDUCE_MEAN = 0
 TRI_REDUCE_MAX = 1
@@ -379,6 +381,20 @@ class Decode:
 def tri_debug_set_wait_limit(polls: int) -> int:
     """Test hook: bound on the fused score kernel's wait (see triattn.h)."""
     return int(_lib.tri_debug_set_wait_limit(int(polls)))
+
+
+PHASE_NAMES = ("stream", "other_waves", "next_ticket", "moments", "stats_wait", "zscore_max",
+               "operands_stores")
+
+
+def tri_debug_set_phase_buffer(buf) -> int:
+    """Measurement hook: a device tensor of 8 int64 counters (zeroed by the
+    caller) for the fused score kernel's phase cycles, or None to turn it
+    off (see triattn.h).  Returns the previous buffer's address (0 if none)."""
+    if buf is not None and (buf.device.type != "cuda" or buf.numel() < 8 or buf.element_size() != 8
+                            or not buf.is_contiguous()):
+        raise ValueError("phase buffer: 8 contiguous 64-bit counters in device memory")
+    return int(_lib.tri_debug_set_phase_buffer(None if buf is None else buf.data_ptr()) or 0)
 
 
 def tri_pyramid_budgets(num_layers, mean_budget, ratio):

@@ -263,6 +263,10 @@ const char* tri_last_error(void) { return g_last_error.c_str(); }
 
 uint32_t tri_debug_set_wait_limit(uint32_t polls) { return tri::set_fused_wait_limit(polls); }
 
+unsigned long long* tri_debug_set_phase_buffer(unsigned long long* device_buf) {
+  return tri::set_fused_phase_buffer(device_buf);
+}
+
 int32_t tri_debug_set_resident_groups(int32_t groups) {
   return tri::set_fused_resident_override(groups > 0 ? groups : 0);
 }

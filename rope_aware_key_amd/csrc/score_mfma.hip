@@ -492,13 +492,15 @@ __device__ __forceinline__ bool vector_scores(const Chunk& ck, const float* scor
   return (reinterpret_cast<uintptr_t>(scores + ck.row0) & 15u) == 0 && !raw_out;
 }
 
+template <bool PHASES>
 __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, const float* raw,
                                                Shared& sh, const double* __restrict__ chunk_stats,
                                                uint32_t* __restrict__ err_flag,
                                                uint32_t wait_limit,
                                                float* __restrict__ scores,
                                                float* __restrict__ raw_out,
-                                               double* __restrict__ head_stats, int unit_n) {
+                                               double* __restrict__ head_stats, int unit_n,
+                                               uint64_t& t_stats) {
   const int tid = local_tid();
   const int hs = head_shift(G), lph = 1 << hs;
   const int h = tid >> hs, k = tid & (lph - 1);
@@ -559,6 +561,7 @@ __device__ __forceinline__ void chunk_finalize(const Chunk& ck, int G, int rs, c
     }
   }
   __syncthreads();
+  if constexpr (PHASES) t_stats = __builtin_amdgcn_s_memtime();
   // Four keys per thread with 16-byte LDS accesses where the chunk's first
   // score is 16-byte aligned in global memory (rs and the buffers are
   // multiples of four floats); the same fmaf/fmaxf per key as the scalar
@@ -612,15 +615,31 @@ __device__ __forceinline__ void chunk_store_scores(const Chunk& ck, const float*
     __builtin_nontemporal_store(raw[i], scores + ck.row0 + i);
 }
 
+// Cycle counters of the phase-profiling build of the kernel: per pass, the
+// cycles wave 0 of a work-group spends in each phase, summed over passes.
+enum FusedPhase {
+  kPhStream,    // streaming its blocks of the chunk
+  kPhWaves,     // waiting for the work-group's other waves to finish streaming
+  kPhNext,      // decoding the next ticket, requesting its first K blocks
+  kPhMoments,   // chunk moments: LDS read-back, fp64 sums, publication
+  kPhStats,     // waiting for the unit's published statistics, mu and sigma
+  kPhZ,         // z-score and group max of the finalized chunk
+  kPhTail,      // ticket claim if not ahead, next operands, score stores, barrier
+  kPhCount,
+};
+
 // STEPS = head_dim / 32.  Persistent: gridDim.x work-groups loop over the
-// tickets.  ch = keys per ticket.
-template <int STEPS, bool HALF, bool PAGED>
-__global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
+// tickets.  ch = keys per ticket.  With PHASES, wave 0 of every work-group
+// adds its per-phase cycle counts (s_memtime) to phases[0 .. kPhCount) and
+// its number of passes to phases[kPhCount]; the arithmetic is unchanged.
+template <int STEPS, bool HALF, bool PAGED, bool PHASES>
+__device__ __forceinline__ void score_fused_body(
     const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
     const uint4* __restrict__ apack, const uint16_t* __restrict__ k, const Pages pg,
     const int32_t* __restrict__ ptab,
     double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, uint32_t wait_limit,
-    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats) {
+    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats,
+    unsigned long long* __restrict__ phases) {
   extern __shared__ float raw_s[];  // 2 buffers of [G][ch + kRawPad]
   __shared__ Shared sh;
   uint32_t* ticket_ctr = ctrl;
@@ -641,6 +660,15 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
   int prev_last = 0;  // last ticket of prev's unit
   bool have_prev = false;
   int cur = 0;
+  uint64_t ph[kPhCount] = {};
+  uint64_t passes = 0, t_prev = 0, t_stats = 0;
+  auto mark = [&](int phase) {
+    if constexpr (PHASES) {
+      const uint64_t now = __builtin_amdgcn_s_memtime();
+      ph[phase] += now - t_prev;
+      t_prev = now;
+    }
+  };
   if (threadIdx.x == 0) sh.ticket = (int)claim();
   __syncthreads();
   int t = __builtin_amdgcn_readfirstlane(sh.ticket);  // uniform: chunk fields in SGPRs
@@ -670,12 +698,18 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     // that a wave at its boundary takes the SIMD's issue slots ahead of the
     // other work-groups' streaming waves, which mostly wait on memory.
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (PHASES) {
+      t_prev = __builtin_amdgcn_s_memtime();
+      ++passes;
+    }
     if (have)
       chunk_raw<STEPS, HALF, PAGED>(ck, G, rs, op, k, pg, ptab, buf_cur, ring, pid,
                                     sh.tile[threadIdx.x >> 6]);
     __builtin_amdgcn_s_setprio(2);
+    mark(kPhStream);
     if (ahead && threadIdx.x == 0) sh.next_ticket = (int)next;
     __syncthreads();
+    mark(kPhWaves);
     // nk: the next chunk, or (past the last ticket) a valid chunk whose loads
     // go unused.  The ring and operands are reloaded on every path so their
     // old contents are dead from here on.
@@ -685,10 +719,18 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
       if (t < total_tickets) nk = decode_chunk(seqs, S, L, Hkv, ch, t, ck.s);
     }
     if (ahead || !have) ring_prime<STEPS, PAGED>(nk, k, pg, ptab, ring, pid);
+    mark(kPhNext);
     if (have) chunk_moments_publish(ck, G, rs, buf_cur, chunk_stats);
-    if (have_prev)
-      chunk_finalize(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, wait_limit, scores, raw_out,
-                     head_stats, prev.nkeys_unit);
+    mark(kPhMoments);
+    if (have_prev) {
+      chunk_finalize<PHASES>(prev, G, rs, buf_prev, sh, chunk_stats, err_flag, wait_limit, scores,
+                             raw_out, head_stats, prev.nkeys_unit, t_stats);
+      if constexpr (PHASES) {
+        ph[kPhStats] += t_stats - t_prev;
+        t_prev = t_stats;
+      }
+    }
+    mark(kPhZ);
     if (have && !ahead) {
       if (threadIdx.x == 0) sh.ticket = (int)claim();
       __syncthreads();
@@ -699,6 +741,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     load_operands<STEPS>(nk, apack, op);
     if (have_prev) chunk_store_scores(prev, buf_prev, scores, raw_out);
     __syncthreads();
+    mark(kPhTail);
     if (!have) break;
     prev = ck;
     prev_last = ck.t - ck.c + ck.nch - 1;
@@ -706,6 +749,39 @@ __global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
     ck = nk;
     cur ^= 1;
   }
+  if constexpr (PHASES) {
+    if (threadIdx.x == 0) {
+      for (int i = 0; i < kPhCount; ++i) atomicAdd(phases + i, (unsigned long long)ph[i]);
+      atomicAdd(phases + kPhCount, (unsigned long long)passes);
+    }
+  }
+}
+
+template <int STEPS, bool HALF, bool PAGED>
+__global__ __launch_bounds__(kFusedThreads) void score_fused_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
+    const uint4* __restrict__ apack, const uint16_t* __restrict__ k, const Pages pg,
+    const int32_t* __restrict__ ptab,
+    double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, uint32_t wait_limit,
+    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats) {
+  score_fused_body<STEPS, HALF, PAGED, false>(seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg,
+                                              ptab, chunk_stats, ctrl, wait_limit, scores, raw_out,
+                                              head_stats, nullptr);
+}
+
+// The same kernel with per-phase cycle counters (interleaved layout, packed
+// cache); launched only while a phase buffer is set.
+template <int STEPS>
+__global__ __launch_bounds__(kFusedThreads) void score_phase_kernel(
+    const SeqInfo* __restrict__ seqs, int S, int L, int Hkv, int G, int ch, int total_tickets,
+    const uint4* __restrict__ apack, const uint16_t* __restrict__ k, const Pages pg,
+    const int32_t* __restrict__ ptab,
+    double* __restrict__ chunk_stats, uint32_t* __restrict__ ctrl, uint32_t wait_limit,
+    float* __restrict__ scores, float* __restrict__ raw_out, double* __restrict__ head_stats,
+    unsigned long long* __restrict__ phases) {
+  score_fused_body<STEPS, false, false, true>(seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg,
+                                              ptab, chunk_stats, ctrl, wait_limit, scores, raw_out,
+                                              head_stats, phases);
 }
 
 // The fused path's preparation of a call, one launch: block 0 writes the
@@ -853,6 +929,14 @@ static std::atomic<uint32_t> g_wait_limit{1u << 22};
 
 uint32_t set_fused_wait_limit(uint32_t polls) { return g_wait_limit.exchange(polls); }
 
+// Device buffer of kPhCount + 1 counters for the phase-profiling kernel;
+// null (the default) runs the plain kernel.
+static std::atomic<unsigned long long*> g_phase_buf{nullptr};
+
+unsigned long long* set_fused_phase_buffer(unsigned long long* buf) {
+  return g_phase_buf.exchange(buf);
+}
+
 template <int STEPS, bool HALF, bool PAGED>
 static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStream_t st,
                                  const SeqInfo* seqs, int S, int L, int Hkv, int G, uint4* apack,
@@ -891,6 +975,24 @@ static hipError_t launch_fused_t(int total_tickets, int ch, size_t lds, hipStrea
   if (per_cu < 1) per_cu = 1;
   int grid = cus * per_cu;
   if (grid > total_tickets) grid = total_tickets;
+  if constexpr (STEPS == 4 && !HALF && !PAGED) {
+    unsigned long long* phases = g_phase_buf.load(std::memory_order_relaxed);
+    if (phases) {
+      // same grid as the plain kernel; refused if the counters cost occupancy
+      const void* pk = reinterpret_cast<const void*>(&score_phase_kernel<STEPS>);
+      static const hipError_t pattr = hipFuncSetAttribute(
+          pk, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedMaxLds);
+      if (pattr != hipSuccess) return pattr;
+      int pcu = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pcu, pk, kFusedThreads, lds);
+      if (e != hipSuccess) return e;
+      if (pcu < per_cu) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((score_phase_kernel<STEPS>), dim3(grid), dim3(kFusedThreads), lds, st,
+                         seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg, pg.table, cs, ctrl,
+                         g_wait_limit.load(std::memory_order_relaxed), scores, raw, hs, phases);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((score_fused_kernel<STEPS, HALF, PAGED>), dim3(grid), dim3(kFusedThreads),
                      lds, st, seqs, S, L, Hkv, G, ch, total_tickets, apack, k, pg, pg.table, cs, ctrl,
                      g_wait_limit.load(std::memory_order_relaxed), scores, raw, hs);

@@ -166,6 +166,7 @@ int fused_chunk_keys(int G, int d);
 // Bound on the fused kernel's wait for another work-group's chunk statistics
 // (polls per slot; default 2^22); returns the previous bound.
 uint32_t set_fused_wait_limit(uint32_t polls);
+unsigned long long* set_fused_phase_buffer(unsigned long long* buf);
 // Most chunks one unit may have on the fused path.  Its waits need more
 // than half that many work-groups resident; the planner also caps a unit at
 // the device's resident work-groups (fused_resident_groups), twice that

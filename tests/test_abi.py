@@ -36,7 +36,7 @@ def test_header_symbols_exported():
                           "tri_select_compact_paged", "tri_workspace_bytes_paged",
                           "tri_debug_set_wait_limit", "tri_stream_probe",
                           "tri_score_noalloc", "tri_score_status",
-                          "tri_debug_set_resident_groups"}
+                          "tri_debug_set_resident_groups", "tri_debug_set_phase_buffer"}
     for name in names:
         assert hasattr(lib, name), name
     assert set(R.EXPORTS) == set(names)
