@@ -239,17 +239,19 @@ uint32_t tri_debug_set_wait_limit(uint32_t polls);
  * tri_debug_set_phase_buffer -- measurement hook: where the cycles of the
  * fused score kernel's passes go.  device_buf is device memory of 8
  * unsigned 64-bit counters, owned and zeroed by the caller; NULL (the
- * default) turns the hook off.  While it is set, tri_score and
- * tri_score_noalloc calls on head_dim 128 with the interleaved layout and a
- * packed cache run a copy of the fused kernel in which wave 0 of every
- * work-group adds the core-clock cycles (s_memtime) of each phase of its
- * passes to counters 0..6 -- streaming its blocks of the chunk; waiting
+ * default) turns the hook off.  While it is set, every launch of the fused
+ * score kernel (tri_score, tri_score_noalloc, tri_score_offsets with the
+ * mean, the decode calls' pruning steps) on head_dim 128 with the
+ * interleaved layout and a packed cache runs a copy of the kernel in which
+ * wave 0 of every work-group adds the core-clock cycles (s_memtime) of
+ * each phase of its passes to counters 0..6 -- streaming its blocks of the
+ * chunk; waiting
  * for the work-group's other waves; decoding the next ticket and
  * requesting its first K blocks; the chunk's moments and their
  * publication; waiting for the unit's published statistics; z-score and
  * group max; ticket claim, next operands, score stores and the closing
  * barrier -- and its number of passes to counter 7.  Scores are the
- * same bits as without the hook.  Other shapes ignore it.  The call
+ * same bits as without the hook.  Other shapes ignore it.  A scoring call
  * returns TRI_ERR_HIP if the counting kernel would hold fewer work-groups
  * per CU than the plain one.  Applies to launches queued after it returns;
  * returns the previous buffer.  Not for production use.
